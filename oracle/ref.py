@@ -1,0 +1,97 @@
+"""Float64 reference results and the per-element tolerance.  TEST INFRASTRUCTURE.
+
+The projection (cera `wgpu_gemm_bench.rs`, Shape: dst[n, m] = src0[m, k] *
+src1[n, k], dst column-major with y_stride = m):
+
+    ref[j, i] = sum_c W[i, c] * x[j, c],    S[j, i] = sum_c |W[i, c] * x[j, c]|
+
+with W decoded exactly (``oracle.formats``) and the sum taken in float64 by a
+plain matmul.  A device result g passes when it is finite and
+|g - ref| <= tau * S element by element (tau = 2e-3 when activations and
+weights are rounded to f16 for the matrix cores, 1e-5 on the f32 path).
+
+The MoE gate/up (memra `moe_rows_ceiling_bench.rs`: gate and up planes over
+in_f -> n_ff, n_used experts per token, a per-pair f32 scale indexed
+plane*n_pairs + pair, as the pointer table is):
+
+    out_P[p, r] = scale[P*n_pairs + p] * sum_c W_P[e_p][r, c] * x[tau_p, c]
+
+for pair p = tau*n_used + s with expert e_p = ids[tau, s].
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import decode
+
+
+def gemm_ref(name: str, w, x, m: int, k: int, n: int):
+    """(ref, S) as float64 [n, m]."""
+    W = decode(name, w, m, k)
+    X = np.asarray(x, dtype=np.float32).reshape(n, k).astype(np.float64)
+    return X @ W.T, np.abs(X) @ np.abs(W).T
+
+
+def gemm_ref_rows(name: str, w, x, m: int, k: int, rows, cols, row_bytes: int):
+    """(ref, S) for the sampled outputs dst[cols[t], rows[t]] only.
+
+    Decodes just the sampled weight rows, so full-size shapes stay cheap.
+    ``row_bytes`` is the packed size of one row (bytes; 4*k for f32)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    buf = np.asarray(w).reshape(-1).view(np.uint8)
+    uniq, inv = np.unique(rows, return_inverse=True)
+    sel = np.stack([buf[r * row_bytes:(r + 1) * row_bytes] for r in uniq])
+    W = decode(name, sel, len(uniq), k)[inv]                      # [T, k]
+    X = np.asarray(x, dtype=np.float32).reshape(-1, k)[cols].astype(np.float64)
+    return np.einsum("tk,tk->t", W, X), np.einsum("tk,tk->t", np.abs(W), np.abs(X))
+
+
+def moe_ref(name: str, w_gate, w_up, ids, scales, x, n_expert: int, in_f: int, n_ff: int):
+    """(gate, up, S_gate, S_up) as float64 [n_pairs, n_ff]."""
+    ids = np.asarray(ids, dtype=np.int64)
+    t, n_used = ids.shape
+    n_pairs = t * n_used
+    X = np.asarray(x, dtype=np.float32).reshape(t, in_f).astype(np.float64)
+    sc = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    outs = []
+    for plane, wp in enumerate((w_gate, w_up)):
+        buf = np.asarray(wp).reshape(-1).view(np.uint8)
+        per = buf.size // n_expert
+        val = np.empty((n_pairs, n_ff))
+        tol = np.empty((n_pairs, n_ff))
+        cache = {}
+        for tau in range(t):
+            for s in range(n_used):
+                e = int(ids[tau, s])
+                if e not in cache:
+                    cache[e] = decode(name, buf[e * per:(e + 1) * per], n_ff, in_f)
+                W = cache[e]
+                p = tau * n_used + s
+                f = sc[plane * n_pairs + p]
+                val[p] = f * (W @ X[tau])
+                tol[p] = abs(f) * (np.abs(W) @ np.abs(X[tau]))
+        outs.append((val, tol))
+    return outs[0][0], outs[1][0], outs[0][1], outs[1][1]
+
+
+def tolerance_check(got, ref, S, tau: float):
+    """(ok, worst) where worst = max |got - ref| / (tau * S) over the outputs
+    (a ratio <= 1 passes).  Any non-finite value in ``got`` fails outright:
+    a max over NaN would otherwise hide every mismatch (cera
+    `wgpu_gemm_bench.rs`, the non-finite guard before the relative error)."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    s = np.asarray(S, dtype=np.float64)
+    if g.shape != r.shape:
+        raise ValueError(f"shape mismatch {g.shape} vs {r.shape}")
+    if not np.all(np.isfinite(g)):
+        return False, float("inf")
+    err = np.abs(g - r)
+    bound = tau * s
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0),
+                         np.where(err > 0, np.inf, 0.0))
+    worst = float(ratio.max()) if ratio.size else 0.0
+    return bool(worst <= 1.0), worst

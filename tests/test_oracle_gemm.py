@@ -1,0 +1,179 @@
+"""Pins for the oracle's reference GEMM / MoE and the tolerance check.
+
+- identity activations reduce the GEMM to the decoder: ref[j, i] = W[i, j]
+- tiny shapes: brute force with exactly rounded sums (math.fsum) over the
+  literal decoder
+- invariants: row permutation of x, linearity, S >= |ref|
+- MoE: brute force per pair; renaming experts together with their weights
+  leaves the outputs unchanged
+- planted mistakes (in the oracle, on the CPU) are caught by these pins
+"""
+
+import numpy as np
+import pytest
+
+import encoders as enc
+from oracle import formats, ref, scalar
+from synth import gen
+
+QTS = ["f32", "q4_0", "q8_0", "q4_k", "q6_k", "nvfp4"]
+
+
+def _weights(qt, m, k, seed):
+    if qt == "f32":
+        return gen.unit_f32(m * k, seed)
+    if qt == "nvfp4":
+        return gen.nvfp4_rows(m, k, seed)
+    return gen.quant_bytes(m * formats.row_bytes(qt, k), seed)
+
+
+@pytest.mark.parametrize("qt", QTS)
+def test_identity_activations_return_weights(qt):
+    m, k = 5, formats.block_elems(qt) if qt != "f32" else 64
+    k = max(k, 64)
+    w = _weights(qt, m, k, 3)
+    x = np.eye(k, dtype=np.float32)
+    r, S = ref.gemm_ref(qt, w, x, m, k, k)
+    W = formats.decode(qt, w, m, k)
+    assert np.array_equal(r, W.T)
+    assert np.array_equal(S, np.abs(W.T))
+
+
+@pytest.mark.parametrize("qt", QTS)
+def test_tiny_shapes_brute_force(qt):
+    k = max(formats.block_elems(qt), 32)
+    for m in (1, 2, 3):
+        for n in (1, 2, 3):
+            w = _weights(qt, m, k, 17 + m)
+            x = gen.unit_f32(n * k, 23 + n).reshape(n, k)
+            r, S = ref.gemm_ref(qt, w, x, m, k, n)
+            bf = np.array(scalar.gemm(qt, bytes(np.asarray(w).view(np.uint8)), x.tolist(), m, k, n))
+            # f64 matmul vs exactly rounded sum: differ by f64 rounding only
+            assert np.all(np.abs(r - bf) <= 1e-12 * S + 1e-300)
+
+
+def test_invariants_permutation_linearity():
+    qt, m, k, n = "q4_k", 16, 512, 6
+    w = _weights(qt, m, k, 5)
+    x = gen.unit_f32(n * k, 6).reshape(n, k)
+    r, S = ref.gemm_ref(qt, w, x, m, k, n)
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    rp, _ = ref.gemm_ref(qt, w, x[perm], m, k, n)
+    assert np.array_equal(rp, r[perm])
+    y = gen.unit_f32(n * k, 7).reshape(n, k)
+    ry, _ = ref.gemm_ref(qt, w, y, m, k, n)
+    rs, _ = ref.gemm_ref(qt, w, (x + y).astype(np.float64).astype(np.float32), m, k, n)
+    # x + y is exact in f32 here (both on a 2^-15 grid in [-1, 1))
+    assert np.allclose(rs, r + ry, rtol=0, atol=1e-9)
+    assert np.all(S >= np.abs(r))
+
+
+def test_sampled_rows_equal_full():
+    qt, m, k, n = "q6_k", 40, 512, 9
+    w = _weights(qt, m, k, 8)
+    x = gen.unit_f32(n * k, 9).reshape(n, k)
+    r, S = ref.gemm_ref(qt, w, x, m, k, n)
+    rng = np.random.default_rng(0)
+    rows = rng.integers(0, m, 50)
+    cols = rng.integers(0, n, 50)
+    rr, ss = ref.gemm_ref_rows(qt, w, x, m, k, rows, cols, formats.row_bytes(qt, k))
+    assert np.allclose(rr, r[cols, rows], rtol=1e-14, atol=0)
+    assert np.allclose(ss, S[cols, rows], rtol=1e-14, atol=0)
+
+
+def test_moe_ref_brute_force_and_expert_renaming():
+    n_expert, in_f, n_ff, t, n_used = 6, 128, 8, 3, 2
+    wg = np.concatenate([gen.nvfp4_rows(n_ff, in_f, 0x8181 + 2 * e) for e in range(n_expert)])
+    wu = np.concatenate([gen.nvfp4_rows(n_ff, in_f, 0x8181 + 2 * e + 1) for e in range(n_expert)])
+    ids = gen.expert_ids(t, n_used, n_expert, 5)
+    sc = gen.pair_scales(2 * t * n_used)
+    x = gen.xorshift_f32(t * in_f, 91)
+    g, u, Sg, Su = ref.moe_ref("nvfp4", wg, wu, ids, sc, x, n_expert, in_f, n_ff)
+    per = n_ff * formats.row_bytes("nvfp4", in_f)
+    n_pairs = t * n_used
+    for tau in range(t):
+        for s in range(n_used):
+            p = tau * n_used + s
+            e = ids[tau, s]
+            for plane, wp, out in ((0, wg, g), (1, wu, u)):
+                blk = bytes(wp[e * per:(e + 1) * per])
+                bf = scalar.gemm("nvfp4", blk, [x[tau * in_f:(tau + 1) * in_f].tolist()], n_ff, in_f, 1)[0]
+                assert np.allclose(out[p], np.float64(sc[plane * n_pairs + p]) * np.array(bf),
+                                   rtol=1e-13, atol=1e-13)
+    # rename experts: permute the weight slabs and map the ids through the same permutation
+    perm = np.array([4, 2, 0, 5, 1, 3])          # new slot of old expert e is perm[e]
+    inv = np.argsort(perm)
+    wg2 = np.concatenate([wg[inv[s] * per:(inv[s] + 1) * per] for s in range(n_expert)])
+    wu2 = np.concatenate([wu[inv[s] * per:(inv[s] + 1) * per] for s in range(n_expert)])
+    g2, u2, _, _ = ref.moe_ref("nvfp4", wg2, wu2, perm[ids], sc, x, n_expert, in_f, n_ff)
+    assert np.array_equal(g2, g) and np.array_equal(u2, u)
+
+
+def test_tolerance_check_semantics():
+    r = np.array([[1.0, -2.0]])
+    S = np.array([[1.0, 2.0]])
+    assert ref.tolerance_check(r, r, S, 1e-5) == (True, 0.0)
+    ok, worst = ref.tolerance_check(r + np.array([[0.9e-5, 0]]), r, S, 1e-5)
+    assert ok and 0.89 < worst < 0.91
+    ok, _ = ref.tolerance_check(r + np.array([[2e-5, 0]]), r, S, 1e-5)
+    assert not ok
+    ok, worst = ref.tolerance_check(np.array([[np.nan, -2.0]]), r, S, 1e-5)
+    assert not ok and worst == float("inf")
+    # zero tolerance scale: only an exact match passes
+    assert ref.tolerance_check(np.array([0.0]), np.array([0.0]), np.array([0.0]), 1e-5)[0]
+    assert not ref.tolerance_check(np.array([1e-30]), np.array([0.0]), np.array([0.0]), 1e-5)[0]
+
+
+# ------------------------------------------------------------ planted mistakes
+
+
+def _q4k_roundtrip_ok(decode_fn):
+    rng = np.random.default_rng(1)
+    for _ in range(5):
+        d, dmin = 0x3C00, 0x3800
+        sc = rng.integers(0, 64, 8)
+        mn = rng.integers(0, 64, 8)
+        q = rng.integers(0, 16, 256)
+        blk = np.frombuffer(enc.q4_k(d, dmin, sc, mn, q), np.uint8)
+        j = np.arange(256) // 32
+        want = 1.0 * sc[j] * q - 0.5 * mn[j]
+        if not np.array_equal(decode_fn("q4_k", blk, 1, 256)[0], want):
+            return False
+    return True
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    assert _q4k_roundtrip_ok(formats.decode)
+    orig = formats._q4k_scale_min
+
+    def swapped(sc):                       # min and scale swapped for j >= 4
+        s, m = orig(sc)
+        s2, m2 = s.copy(), m.copy()
+        s2[..., 4:], m2[..., 4:] = m[..., 4:], s[..., 4:]
+        return s2, m2
+    monkeypatch.setattr(formats, "_q4k_scale_min", swapped)
+    assert not _q4k_roundtrip_ok(formats.decode)
+    monkeypatch.setattr(formats, "_q4k_scale_min", orig)
+
+    # Q6_K with the qh bit pair of quarter 1 and 2 exchanged
+    orig_codes = formats._q6k_codes
+
+    def bad_codes(ql, qh):
+        q = orig_codes(ql, qh)
+        q2 = q.copy()
+        q2[..., 32:64], q2[..., 64:96] = q[..., 64:96], q[..., 32:64]
+        return q2
+    monkeypatch.setattr(formats, "_q6k_codes", bad_codes)
+    rng = np.random.default_rng(3)
+    sc = rng.integers(-128, 128, 16)
+    q = rng.integers(0, 64, 256)
+    got = formats.decode("q6_k", np.frombuffer(enc.q6_k(0x3C00, sc, q), np.uint8), 1, 256)[0]
+    assert not np.array_equal(got, sc[np.arange(256) // 16] * (q - 32.0))
+    monkeypatch.setattr(formats, "_q6k_codes", orig_codes)
+
+    # f16 decoder that drops the sign: the golden -1.0 code no longer matches
+    orig_f16 = formats.f16_bits_to_f64
+    monkeypatch.setattr(formats, "f16_bits_to_f64", lambda b: np.abs(orig_f16(b)))
+    data = np.frombuffer(enc.q4_0(0xBC00, list(range(16)) * 2), np.uint8)
+    got = formats.decode("q4_0", data, 1, 32)[0]
+    assert not np.array_equal(got, -1.0 * (np.array(list(range(16)) * 2) - 8.0))
