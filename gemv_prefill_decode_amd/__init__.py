@@ -1,0 +1,196 @@
+"""gemv_prefill_decode_amd - dequant-fused projection matmul for MI355X (gfx950).
+
+A thin ctypes binding over ``libqmm.so`` (the C-ABI declared in
+``include/qmm.h``).  Every step of the computation runs in the library's HIP
+kernels; this module only checks tensor dtypes/devices and passes data
+pointers and the current HIP stream.  PyTorch is used for device memory and
+streams.
+
+    out = gemm(w, x, m, "q4_k")            # dst[n, m] = x[n, k] @ deq(w)[m, k]^T
+    g, u = moe_gateup(wg, wu, ids, scales, x, n_expert, n_ff, "nvfp4")
+
+If the library has not been built, every call raises RuntimeError: there is
+no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "QTYPES", "PATHS", "QmmError", "lib_path", "load", "gemm", "moe_gateup", "stream_loadonly",
+    "row_bytes", "block_elems", "gemv_max_n", "status_str", "abi_version",
+]
+
+QTYPES = {"f32": 0, "q4_0": 1, "q8_0": 2, "q4_k": 3, "q6_k": 4, "nvfp4": 5}
+PATHS = {"auto": 0, "gemv": 1, "mfma": 2}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+_LOCK = threading.Lock()
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: qmm status {status} ({status_str(status)})")
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libqmm.so")
+
+
+def load() -> ctypes.CDLL:
+    """Load libqmm.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _LIB
+    with _LOCK:
+        if _LIB is not None:
+            return _LIB
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is not built: run `python -m gemv_prefill_decode_amd.build` "
+                "(or __graft_entry__.build()); there is no non-HIP fallback")
+        lib = ctypes.CDLL(path)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        lib.qmm_gemm.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp]
+        lib.qmm_gemm.restype = i32
+        lib.qmm_gemm_path.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, vp]
+        lib.qmm_gemm_path.restype = i32
+        lib.qmm_moe_gateup.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+        lib.qmm_moe_gateup.restype = i32
+        lib.qmm_stream_loadonly.argtypes = [vp, vp, i64, i64, i32, vp]
+        lib.qmm_stream_loadonly.restype = i32
+        lib.qmm_row_bytes.argtypes = [i32, i64]
+        lib.qmm_row_bytes.restype = i64
+        lib.qmm_block_elems.argtypes = [i32]
+        lib.qmm_block_elems.restype = i32
+        lib.qmm_gemv_max_n.argtypes = []
+        lib.qmm_gemv_max_n.restype = i32
+        lib.qmm_status_str.argtypes = [i32]
+        lib.qmm_status_str.restype = ctypes.c_char_p
+        lib.qmm_abi_version.argtypes = []
+        lib.qmm_abi_version.restype = i32
+        _LIB = lib
+        return lib
+
+
+def _qt(qtype) -> int:
+    if isinstance(qtype, str):
+        if qtype not in QTYPES:
+            raise ValueError(f"unknown qtype {qtype!r}")
+        return QTYPES[qtype]
+    return int(qtype)
+
+
+def status_str(status: int) -> str:
+    return load().qmm_status_str(int(status)).decode()
+
+
+def abi_version() -> int:
+    return load().qmm_abi_version()
+
+
+def row_bytes(qtype, k: int) -> int:
+    r = load().qmm_row_bytes(_qt(qtype), int(k))
+    if r < 0:
+        raise QmmError(-r, "qmm_row_bytes")
+    return r
+
+
+def block_elems(qtype) -> int:
+    r = load().qmm_block_elems(_qt(qtype))
+    if r < 0:
+        raise QmmError(-r, "qmm_block_elems")
+    return r
+
+
+def gemv_max_n() -> int:
+    return load().qmm_gemv_max_n()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, what, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a device (cuda/hip) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def gemm(w, x, m: int, qtype, out=None, path: str = "auto", stream=None):
+    """dst[n, m] with dst[j, i] = sum_c deq(w)[i, c] * x[j, c].
+
+    w: packed weights (uint8, m*row_bytes(qtype, k) bytes; float32 [m, k] for
+    "f32"); x: float32 [n, k]; out: optional float32 [n, m]."""
+    import torch
+    lib = load()
+    qt = _qt(qtype)
+    if x.dim() != 2:
+        raise ValueError("x must be [n, k]")
+    n, k = x.shape
+    if out is None:
+        out = torch.empty((n, m), dtype=torch.float32, device=x.device)
+    if tuple(out.shape) != (n, m):
+        raise ValueError(f"out must be [{n}, {m}]")
+    need = m * row_bytes(qt, k)
+    if w.numel() * w.element_size() != need:
+        raise ValueError(f"w holds {w.numel() * w.element_size()} bytes, expected {need}")
+    st = lib.qmm_gemm_path(_dev(out, "out", torch.float32), _dev(w, "w"),
+                           _dev(x, "x", torch.float32), m, k, n, qt, PATHS[path], _stream(stream))
+    if st != 0:
+        raise QmmError(st, "qmm_gemm_path")
+    return out
+
+
+def moe_gateup(w_gate, w_up, expert_ids, pair_scale, x, n_expert: int, n_ff: int,
+               qtype="nvfp4", gate_out=None, up_out=None, stream=None):
+    """Gate and up projections over routed experts; returns (gate, up), each
+    float32 [t*n_used, n_ff].  expert_ids: int32 [t, n_used]; pair_scale:
+    float32 [2*t*n_used] (gate plane then up plane); x: float32 [t, in_f]."""
+    import torch
+    lib = load()
+    qt = _qt(qtype)
+    t, n_used = expert_ids.shape
+    t2, in_f = x.shape
+    if t2 != t:
+        raise ValueError("x and expert_ids disagree on t")
+    n_pairs = t * n_used
+    if pair_scale.numel() != 2 * n_pairs:
+        raise ValueError("pair_scale must hold 2*t*n_used floats")
+    if gate_out is None:
+        gate_out = torch.empty((n_pairs, n_ff), dtype=torch.float32, device=x.device)
+    if up_out is None:
+        up_out = torch.empty((n_pairs, n_ff), dtype=torch.float32, device=x.device)
+    st = lib.qmm_moe_gateup(_dev(gate_out, "gate_out", torch.float32),
+                            _dev(up_out, "up_out", torch.float32), _dev(w_gate, "w_gate"),
+                            _dev(w_up, "w_up"), _dev(expert_ids, "expert_ids", torch.int32),
+                            _dev(pair_scale, "pair_scale", torch.float32),
+                            _dev(x, "x", torch.float32), t, n_used, n_expert, in_f, n_ff, qt,
+                            _stream(stream))
+    if st != 0:
+        raise QmmError(st, "qmm_moe_gateup")
+    return gate_out, up_out
+
+
+def stream_loadonly(w, m: int, k: int, qtype, sink=None, stream=None):
+    """Load-only twin of the GEMV: reads all of w, writes one checksum per row."""
+    import torch
+    lib = load()
+    if sink is None:
+        sink = torch.empty(m, dtype=torch.int32, device=w.device)
+    st = lib.qmm_stream_loadonly(_dev(sink, "sink"), _dev(w, "w"), m, k, _qt(qtype), _stream(stream))
+    if st != 0:
+        raise QmmError(st, "qmm_stream_loadonly")
+    return sink

@@ -1,0 +1,132 @@
+// Device helpers shared by the qmm kernels (gfx950 / CDNA4).
+//
+// Packed weights are read through buffer resource descriptors: every load is
+// range-checked by the hardware against the descriptor's byte count, and a
+// load past it returns zero instead of faulting.  Blocks of 18, 34 and 210
+// bytes start at 2-byte-aligned offsets, so the kernels load the enclosing
+// dword-aligned span and shift bytes into place in registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+enum : int { QT_F32 = 0, QT_Q4_0 = 1, QT_Q8_0 = 2, QT_Q4_K = 3, QT_Q6_K = 4, QT_NVFP4 = 5 };
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Raw (stride 0) buffer descriptor over [base, base + nbytes).  Word 3 is
+// the gfx9-family default (32-bit data format, no swizzle).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ uint32_t ld32(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 ld64(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x4 ld128(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// Load N dwords starting at the dword-aligned offset (off & ~3).
+template <int N>
+__device__ __forceinline__ void ld_span(rsrc_t r, uint32_t off, uint32_t (&v)[N]) {
+    const uint32_t a = off & ~3u;
+#pragma unroll
+    for (int i = 0; i + 4 <= N; i += 4) {
+        u32x4 t = ld128(r, a + 4 * i);
+        v[i] = t.x; v[i + 1] = t.y; v[i + 2] = t.z; v[i + 3] = t.w;
+    }
+    if constexpr (N % 4 >= 2) {
+        u32x2 t = ld64(r, a + 4 * (N / 4 * 4));
+        v[N / 4 * 4] = t.x;
+        v[N / 4 * 4 + 1] = t.y;
+    }
+    if constexpr (N % 2 == 1) {
+        v[N - 1] = ld32(r, a + 4 * (N - 1));
+    }
+}
+
+// Bytes [sh, sh+4) of the 8-byte little-endian pair (lo, hi), sh in 0..4.
+__device__ __forceinline__ uint32_t shr64(uint32_t lo, uint32_t hi, uint32_t sh) {
+    return (uint32_t)((((uint64_t)hi << 32) | lo) >> (8u * sh));
+}
+
+__device__ __forceinline__ float h2f(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
+}
+
+__device__ __forceinline__ _Float16 bits_h(uint32_t bits) {
+    return __builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
+}
+
+__device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
+    f16x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint32_t pack_f2h(float a, float b) {
+    return pack_h2((_Float16)a, (_Float16)b);
+}
+
+__device__ __forceinline__ uint32_t byte_of(uint32_t v, int b) { return (v >> (8 * b)) & 0xFFu; }
+
+// OCP FP8 E4M3FN byte -> f32 (exact): sign, 4-bit exponent bias 7, 3-bit
+// mantissa, exponent 0 subnormal, S.1111.111 NaN, no infinities.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, mt = b & 7u;
+    float mag;
+    if (e == 0) {
+        mag = (float)mt * 0x1p-9f;
+    } else {
+        mag = __builtin_bit_cast(float, ((e + 120u) << 23) | (mt << 20));
+    }
+    if ((b & 0x7Fu) == 0x7Fu) mag = __builtin_nanf("");
+    return (b & 0x80u) ? -mag : mag;
+}
+
+// Two OCP FP4 E2M1 codes in byte `sel` of v -> f32 (low nibble first), exact.
+__device__ __forceinline__ f32x2 e2m1x2_to_f32(uint32_t v, int sel) {
+    switch (sel) {
+        case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 0);
+        case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 1);
+        case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 2);
+        default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 3);
+    }
+}
+
+// E2M1 code (4 bits) -> f16 bit pattern of the code placed so that the f16
+// value times 2^14 is the E2M1 value: magnitude bits land in f16 bits 9..11
+// (a 2-bit exponent field whose bias differs from binary16's by 14, with
+// exponent 0 landing in the binary16 subnormal range), sign in bit 15.
+__device__ __forceinline__ uint32_t e2m1_f16_bits_unscaled(uint32_t c) {
+    return ((c & 7u) << 9) | ((c & 8u) << 12);
+}
+
+__device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+// Descriptor over the packed rows [row0, row0+rows) clipped to m, based at the
+// 16-byte boundary at or below the first row (returned in `base`); its byte
+// count is rounded up to 16, so a dword-aligned span that ends inside the
+// last row's final bytes never has its covering dword range-checked away.
+// (Reads past the end of w stay within its last 16-byte granule.)
+__device__ __forceinline__ rsrc_t row_window(const uint8_t* w, int64_t row0, int64_t rows,
+                                             int64_t m, int64_t rb, int64_t& base) {
+    base = (row0 * rb) & ~(int64_t)15;
+    const int64_t end = imin64(m, row0 + rows) * rb;
+    const int64_t bytes = end > base ? ((end - base + 15) & ~(int64_t)15) : 0;
+    return make_rsrc(w + base, (uint32_t)bytes);
+}
+
+}  // namespace qmm

@@ -1,0 +1,414 @@
+// Prefill path: dequant-fused GEMM on the gfx950 matrix cores.
+//
+// One work group (256 threads, 4 waves in a 2x2 grid) computes a 128 x 128
+// tile of dst (128 weight rows x 128 tokens) over k in steps of 64.  Per step
+// every thread loads the packed bytes of half a row of the weight tile and
+// half a row of the activation tile into registers, decodes the weights to
+// f16 (round to nearest even, once) and rounds the activations to f16, and
+// stores both into LDS.  The waves then run v_mfma_f32_16x16x32_f16 on 64 x 64
+// sub-tiles with f32 accumulators.  LDS is double buffered and the next
+// step's global loads are issued before the current step's MFMAs, so the
+// loads, the decode and the matrix-core work overlap.
+//
+// k order inside an LDS row.  The contraction is over k, so any permutation
+// of the 64 k values of a step gives the same result, provided the weight
+// and activation tiles use the same one.  Each format uses the permutation
+// under which one thread's 4 packed bytes expand into 8 consecutive LDS
+// slots: slot 8s+i holds k = g*2H + 4s' + i (i<4) or g*2H + H + 4s' + i-4
+// (i>=4), where s = g*H/4 + s' and H is the distance between the two weights
+// that share a packed byte (16 for Q4_0 and NVFP4, 32 for Q4_K, 64 for Q6_K;
+// 4, the identity, for F32 and Q8_0).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qmm {
+
+constexpr int BM = MFMA_BM, BN = MFMA_BN, BK = 64;
+constexpr int LDK = BK + 8;  // LDS row stride in halves (16-byte pad: conflict-free b128 reads)
+
+template <int QT> struct Perm { static constexpr int H = 4; };
+template <> struct Perm<QT_Q4_0> { static constexpr int H = 16; };
+template <> struct Perm<QT_Q4_K> { static constexpr int H = 32; };
+template <> struct Perm<QT_Q6_K> { static constexpr int H = 64; };
+template <> struct Perm<QT_NVFP4> { static constexpr int H = 16; };
+
+// f16x2 from two bytes (lo, hi) of v at byte positions b0, b0+1, each given
+// as 1024 + byte by the binary16 pattern 0x6400 | byte.
+__device__ __forceinline__ f16x2 magic_pair(uint32_t v, int b0) {
+    const uint32_t bits = ((v >> (8 * b0)) & 0xFFu) | (((v >> (8 * b0 + 8)) & 0xFFu) << 16) | 0x64006400u;
+    return __builtin_bit_cast(f16x2, bits);
+}
+
+// ------------------------------------------------------------ weight tiles
+// Thread (row, p) covers the 32 slots [32p, 32p+32) of its row's k-step kt.
+// decode() fills o[4u..4u+3] with the 8 halves of slot unit u (slot order).
+
+template <int QT> struct ALoad;
+
+template <> struct ALoad<QT_F32> {
+    u32x4 r[8];
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int k) {
+        const int e = kt * 64 + 32 * p;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            r[i] = ld128(wr, row_off + 4u * (uint32_t)(e + 4 * i));
+            if (e + 4 * i >= k) r[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void decode(uint32_t (&o)[16]) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const f32x4 v = __builtin_bit_cast(f32x4, r[i]);
+            o[2 * i] = pack_f2h(v.x, v.y);
+            o[2 * i + 1] = pack_f2h(v.z, v.w);
+        }
+    }
+};
+
+template <> struct ALoad<QT_Q4_0> {
+    uint32_t r[5], sh;
+    bool valid;
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int k) {
+        const int b = 2 * kt + p;
+        const uint32_t o = row_off + (uint32_t)b * 18u;
+        sh = o & 3u;
+        valid = b * 32 < k;
+        ld_span<5>(wr, o, r);
+    }
+    __device__ __forceinline__ void decode(uint32_t (&o)[16]) const {
+        const _Float16 d = bits_h(r[0] >> (8u * sh));
+        const f16x2 dd = {d, d}, off = {(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t q = shr64(r[u], r[u + 1], sh + 2u);
+            const uint32_t lo = q & 0x0F0F0F0Fu, hi = (q >> 4) & 0x0F0F0F0Fu;
+            // (1024 + q) - 1032 = q - 8 exactly; one f16 rounding in the product
+            o[4 * u + 0] = __builtin_bit_cast(uint32_t, (magic_pair(lo, 0) - off) * dd);
+            o[4 * u + 1] = __builtin_bit_cast(uint32_t, (magic_pair(lo, 2) - off) * dd);
+            o[4 * u + 2] = __builtin_bit_cast(uint32_t, (magic_pair(hi, 0) - off) * dd);
+            o[4 * u + 3] = __builtin_bit_cast(uint32_t, (magic_pair(hi, 2) - off) * dd);
+        }
+        if (!valid)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[i] = 0u;
+    }
+};
+
+template <> struct ALoad<QT_Q8_0> {
+    uint32_t r[9], sh;
+    bool valid;
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int k) {
+        const int b = 2 * kt + p;
+        const uint32_t o = row_off + (uint32_t)b * 34u;
+        sh = o & 3u;
+        valid = b * 32 < k;
+        ld_span<9>(wr, o, r);
+    }
+    __device__ __forceinline__ void decode(uint32_t (&o)[16]) const {
+        const _Float16 d = bits_h(r[0] >> (8u * sh));
+        const f16x2 dd = {d, d}, off = {(_Float16)1152.0f, (_Float16)1152.0f};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            // int8 q -> byte q+128 -> 1024 + q + 128 in f16, minus 1152 = q exactly
+            const uint32_t qa = shr64(r[2 * u], r[2 * u + 1], sh + 2u) ^ 0x80808080u;
+            const uint32_t qb = shr64(r[2 * u + 1], r[2 * u + 2], sh + 2u) ^ 0x80808080u;
+            o[4 * u + 0] = __builtin_bit_cast(uint32_t, (magic_pair(qa, 0) - off) * dd);
+            o[4 * u + 1] = __builtin_bit_cast(uint32_t, (magic_pair(qa, 2) - off) * dd);
+            o[4 * u + 2] = __builtin_bit_cast(uint32_t, (magic_pair(qb, 0) - off) * dd);
+            o[4 * u + 3] = __builtin_bit_cast(uint32_t, (magic_pair(qb, 2) - off) * dd);
+        }
+        if (!valid)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[i] = 0u;
+    }
+};
+
+template <> struct ALoad<QT_Q4_K> {
+    u32x4 hdr, qs;
+    int c;
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int) {
+        const uint32_t sb = (uint32_t)kt >> 2;
+        c = kt & 3;
+        const uint32_t o = row_off + sb * 144u;
+        hdr = ld128(wr, o);
+        qs = ld128(wr, o + 16u + 32u * (uint32_t)c + 16u * (uint32_t)p);
+    }
+    __device__ __forceinline__ static uint32_t scb(u32x4 h, int i) {
+        const uint32_t v = i < 4 ? h.y : (i < 8 ? h.z : h.w);
+        return (v >> (8 * (i & 3))) & 0xFFu;
+    }
+    __device__ __forceinline__ void decode(uint32_t (&o)[16]) const {
+        const float d = h2f(hdr.x), dmin = h2f(hdr.x >> 16);
+        uint32_t s0, m0, s1, m1;
+        if (c < 2) {
+            s0 = scb(hdr, 2 * c) & 63u;     m0 = scb(hdr, 2 * c + 4) & 63u;
+            s1 = scb(hdr, 2 * c + 1) & 63u; m1 = scb(hdr, 2 * c + 5) & 63u;
+        } else {
+            const int j0 = 2 * c, j1 = 2 * c + 1;
+            s0 = (scb(hdr, j0 + 4) & 15u) | ((scb(hdr, j0 - 4) >> 6) << 4);
+            m0 = (scb(hdr, j0 + 4) >> 4) | ((scb(hdr, j0) >> 6) << 4);
+            s1 = (scb(hdr, j1 + 4) & 15u) | ((scb(hdr, j1 - 4) >> 6) << 4);
+            m1 = (scb(hdr, j1 + 4) >> 4) | ((scb(hdr, j1) >> 6) << 4);
+        }
+        const float D0 = d * (float)s0, M0 = dmin * (float)m0;
+        const float D1 = d * (float)s1, M1 = dmin * (float)m1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t q = u == 0 ? qs.x : (u == 1 ? qs.y : (u == 2 ? qs.z : qs.w));
+            float lo[4], hi[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                lo[b] = __builtin_fmaf(D0, (float)((q >> (8 * b)) & 15u), -M0);
+                hi[b] = __builtin_fmaf(D1, (float)((q >> (8 * b + 4)) & 15u), -M1);
+            }
+            o[4 * u + 0] = pack_f2h(lo[0], lo[1]);
+            o[4 * u + 1] = pack_f2h(lo[2], lo[3]);
+            o[4 * u + 2] = pack_f2h(hi[0], hi[1]);
+            o[4 * u + 3] = pack_f2h(hi[2], hi[3]);
+        }
+    }
+};
+
+// Q6_K step kt: superblock kt/4, half (kt/2)&1, L bytes [32*(kt&1) + 16p, +16)
+// of the half's 64 ql bytes, qh bytes [16p, +16) of the half's 32, two scales.
+template <> struct ALoad<QT_Q6_K> {
+    uint32_t ra[5], rh[5], rs0, rs1, rd, sh;
+    int kh;
+    uint32_t pos0, pos1;
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int) {
+        const uint32_t sb = (uint32_t)kt >> 2;
+        const uint32_t hh = ((uint32_t)kt >> 1) & 1u;
+        kh = kt & 1;
+        const uint32_t o = row_off + sb * 210u;
+        sh = o & 3u;
+        ld_span<5>(wr, o + 64u * hh + 32u * (uint32_t)kh + 16u * (uint32_t)p, ra);
+        ld_span<5>(wr, o + 128u + 32u * hh + 16u * (uint32_t)p, rh);
+        const uint32_t i0 = 8u * hh + 2u * (uint32_t)kh + (uint32_t)p;
+        const uint32_t a0 = o + 192u + i0, a1 = a0 + 4u;
+        pos0 = a0 & 3u;
+        pos1 = a1 & 3u;
+        rs0 = ld32(wr, a0 & ~3u);
+        rs1 = ld32(wr, a1 & ~3u);
+        rd = ld32(wr, (o + 208u) & ~3u);
+    }
+    __device__ __forceinline__ void decode(uint32_t (&o)[16]) const {
+        const float d = h2f(rd >> (8u * sh));
+        const float Dl = d * (float)(int8_t)(rs0 >> (8u * pos0));
+        const float Dh = d * (float)(int8_t)(rs1 >> (8u * pos1));
+        const float Dl32 = -32.0f * Dl, Dh32 = -32.0f * Dh;
+        const int hs = 2 * kh;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t L = shr64(ra[u], ra[u + 1], sh);
+            const uint32_t H = shr64(rh[u], rh[u + 1], sh);
+            const uint32_t ql = (L & 0x0F0F0F0Fu) | (((H >> hs) & 0x03030303u) << 4);
+            const uint32_t qhv = ((L >> 4) & 0x0F0F0F0Fu) | (((H >> (hs + 4)) & 0x03030303u) << 4);
+            float lo[4], hi[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                lo[b] = __builtin_fmaf(Dl, (float)((ql >> (8 * b)) & 0xFFu), Dl32);
+                hi[b] = __builtin_fmaf(Dh, (float)((qhv >> (8 * b)) & 0xFFu), Dh32);
+            }
+            o[4 * u + 0] = pack_f2h(lo[0], lo[1]);
+            o[4 * u + 1] = pack_f2h(lo[2], lo[3]);
+            o[4 * u + 2] = pack_f2h(hi[0], hi[1]);
+            o[4 * u + 3] = pack_f2h(hi[2], hi[3]);
+        }
+    }
+};
+
+template <> struct ALoad<QT_NVFP4> {
+    uint32_t sd;
+    u32x4 qs;
+    int p_;
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int) {
+        const uint32_t o = row_off + (uint32_t)kt * 36u;
+        p_ = p;
+        sd = ld32(wr, o);
+        qs = ld128(wr, o + 4u + 16u * (uint32_t)p);
+    }
+    __device__ __forceinline__ void decode(uint32_t (&o)[16]) const {
+        const float sl = e4m3_to_f32((sd >> (16 * p_)) & 0xFFu);
+        const float sh_ = e4m3_to_f32((sd >> (16 * p_ + 8)) & 0xFFu);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t q = u == 0 ? qs.x : (u == 1 ? qs.y : (u == 2 ? qs.z : qs.w));
+            float lo[4], hi[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const f32x2 v = e2m1x2_to_f32(q, b);
+                lo[b] = v.x * sl;   // exact: at most 5 significant bits, within f16 range
+                hi[b] = v.y * sh_;
+            }
+            o[4 * u + 0] = pack_f2h(lo[0], lo[1]);
+            o[4 * u + 1] = pack_f2h(lo[2], lo[3]);
+            o[4 * u + 2] = pack_f2h(hi[0], hi[1]);
+            o[4 * u + 3] = pack_f2h(hi[2], hi[3]);
+        }
+    }
+};
+
+// ------------------------------------------------------------ activation tiles
+// Thread (token, p): slot units u=0..3 of [32p, 32p+32) of step kt, each two
+// runs of 4 activations placed by the format's permutation.
+template <int H> struct XLoad {
+    u32x4 r[8];
+    __device__ __forceinline__ void load(rsrc_t xr, uint32_t xrow_off, int kt, int p, int k) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int U8 = 8 * kt + 4 * p + u;
+            const int g = U8 / (H / 4), sp = U8 % (H / 4);
+            const int e0 = g * 2 * H + 4 * sp, e1 = e0 + H;
+            r[2 * u] = ld128(xr, xrow_off + 4u * (uint32_t)e0);
+            r[2 * u + 1] = ld128(xr, xrow_off + 4u * (uint32_t)e1);
+            if (e0 >= k) r[2 * u] = u32x4{0u, 0u, 0u, 0u};
+            if (e1 >= k) r[2 * u + 1] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void convert(uint32_t (&o)[16]) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const f32x4 v = __builtin_bit_cast(f32x4, r[i]);
+            o[2 * i] = pack_f2h(v.x, v.y);
+            o[2 * i + 1] = pack_f2h(v.z, v.w);
+        }
+    }
+};
+
+// ------------------------------------------------------------ kernel
+
+template <int QT>
+__global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(float* __restrict__ dst,
+                                                           const uint8_t* __restrict__ w,
+                                                           const float* __restrict__ x, int m,
+                                                           int k, int n, int rb, int n_mb,
+                                                           int n_nb) {
+    __shared__ __attribute__((aligned(16))) _Float16 sA[2][BM * LDK];
+    __shared__ __attribute__((aligned(16))) _Float16 sB[2][BN * LDK];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    // Work groups are dealt round-robin to the 8 XCDs (id % 8); give each XCD
+    // a contiguous run of tiles so the tiles that share weight rows share an L2.
+    const int T = n_mb * n_nb, L = blockIdx.x;
+    const int xcd = L & 7, idx = L >> 3, per = T >> 3, rem = T & 7;
+    const int tile = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    const int mb = tile / n_nb, nb = tile - mb * n_nb;
+    const int64_t m0 = (int64_t)mb * BM, n0 = (int64_t)nb * BN;
+
+    int64_t base;
+    const rsrc_t wr = row_window(w, m0, BM, m, rb, base);
+    const int ntok = (int)imin64(BN, n - n0);
+    const rsrc_t xr = make_rsrc(x + n0 * k, (uint32_t)ntok * (uint32_t)k * 4u);
+    const int arow = tid >> 1, part = tid & 1;
+    const uint32_t roff = (uint32_t)((m0 + arow) * rb - base);
+    const uint32_t xoff = (uint32_t)arow * (uint32_t)k * 4u;
+    const int nk = (k + BK - 1) / BK;
+
+    ALoad<QT> al;
+    XLoad<Perm<QT>::H> xl;
+    uint32_t tmp[16];
+    const int lds_off = arow * LDK + part * 32;
+
+    al.load(wr, roff, 0, part, k);
+    xl.load(xr, xoff, 0, part, k);
+    al.decode(tmp);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        *(u32x4*)&sA[0][lds_off + 8 * u] = u32x4{tmp[4 * u], tmp[4 * u + 1], tmp[4 * u + 2], tmp[4 * u + 3]};
+    xl.convert(tmp);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        *(u32x4*)&sB[0][lds_off + 8 * u] = u32x4{tmp[4 * u], tmp[4 * u + 1], tmp[4 * u + 2], tmp[4 * u + 3]};
+    __syncthreads();
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int wm = wave >> 1, wn = wave & 1;
+    const int frag = (lane & 15) * LDK + (lane >> 4) * 8;
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            al.load(wr, roff, kt + 1, part, k);
+            xl.load(xr, xoff, kt + 1, part, k);
+        }
+        const _Float16* A = &sA[cur][wm * 64 * LDK + frag];
+        const _Float16* B = &sB[cur][wn * 64 * LDK + frag];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            f16x8 a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = *(const f16x8*)(A + i * 16 * LDK + ks * 32);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = *(const f16x8*)(B + j * 16 * LDK + ks * 32);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        if (more) {
+            al.decode(tmp);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                *(u32x4*)&sA[cur ^ 1][lds_off + 8 * u] =
+                    u32x4{tmp[4 * u], tmp[4 * u + 1], tmp[4 * u + 2], tmp[4 * u + 3]};
+            xl.convert(tmp);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                *(u32x4*)&sB[cur ^ 1][lds_off + 8 * u] =
+                    u32x4{tmp[4 * u], tmp[4 * u + 1], tmp[4 * u + 2], tmp[4 * u + 3]};
+        }
+        __syncthreads();
+    }
+
+    // D[row][col] of a 16x16 tile sits in lane (row/4)*16 + col, element row%4:
+    // rows are weight rows (contiguous in dst), cols are tokens.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t mrow = m0 + wm * 64 + i * 16 + (lane >> 4) * 4;
+            const int64_t tok = n0 + wn * 64 + j * 16 + (lane & 15);
+            if (tok < n) {
+                float* p = dst + tok * m + mrow;
+                const f32x4 v = acc[i][j];
+                if ((m & 3) == 0 && mrow + 4 <= m) {
+                    *(f32x4*)p = v;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (mrow + r < m) p[r] = v[r];
+                }
+            }
+        }
+    }
+}
+
+template <int QT>
+static void launch_qt(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k, int64_t n,
+                      int64_t rb, hipStream_t st) {
+    const int n_mb = (int)((m + BM - 1) / BM), n_nb = (int)((n + BN - 1) / BN);
+    gemm_mfma_kernel<QT><<<dim3((unsigned)(n_mb * n_nb)), 256, 0, st>>>(
+        dst, w, x, (int)m, (int)k, (int)n, (int)rb, n_mb, n_nb);
+}
+
+void launch_gemm_mfma(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
+                      int qt, int64_t rb, hipStream_t st) {
+    const uint8_t* wb = (const uint8_t*)w;
+    switch (qt) {
+        case QT_F32: launch_qt<QT_F32>(dst, wb, x, m, k, n, rb, st); break;
+        case QT_Q4_0: launch_qt<QT_Q4_0>(dst, wb, x, m, k, n, rb, st); break;
+        case QT_Q8_0: launch_qt<QT_Q8_0>(dst, wb, x, m, k, n, rb, st); break;
+        case QT_Q4_K: launch_qt<QT_Q4_K>(dst, wb, x, m, k, n, rb, st); break;
+        case QT_Q6_K: launch_qt<QT_Q6_K>(dst, wb, x, m, k, n, rb, st); break;
+        case QT_NVFP4: launch_qt<QT_NVFP4>(dst, wb, x, m, k, n, rb, st); break;
+    }
+}
+
+}  // namespace qmm

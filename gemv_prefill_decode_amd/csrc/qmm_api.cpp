@@ -1,0 +1,189 @@
+// C-ABI entry points of libqmm: argument validation, path dispatch, launch
+// error reporting.  Declarations and the contract are in include/qmm.h.
+#include "qmm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cerrno>
+#include <climits>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "kernels.hpp"
+
+namespace {
+
+struct Fmt {
+    int qk;  // elements per block
+    int bb;  // bytes per block
+};
+
+// Packed sizes: cera wgpu_gemm_bench.rs VARIANTS (f32 e*4, q4_0 e/32*18,
+// q8_0 e/32*34, q4_k e/256*144, q6_k e/256*210); memra synth_rows (NVFP4 36
+// bytes per 64 weights).
+constexpr Fmt kFmt[] = {{1, 4}, {32, 18}, {32, 34}, {256, 144}, {256, 210}, {64, 36}};
+constexpr int kNumQt = 6;
+
+bool valid_qt(int qt) { return qt >= 0 && qt < kNumQt; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// a*b without int64 overflow (both >= 0)
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+int g_gemv_max_n = 32;
+std::once_flag g_env_once;
+
+void parse_env() {
+    const char* v = std::getenv("QMM_GEMV_MAX_N");
+    if (!v) return;
+    char* end = nullptr;
+    errno = 0;
+    const long val = std::strtol(v, &end, 10);
+    while (end && *end == ' ') ++end;
+    if (errno != 0 || end == v || (end && *end != '\0') || val < 1 || val > INT_MAX)
+        g_gemv_max_n = -QMM_ERR_RANGE;  // set but unusable: AUTO calls fail loudly
+    else
+        g_gemv_max_n = (int)val;
+}
+
+int launch_status() {
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
+}
+
+// Common checks for a weight matrix of m rows x k.  On success *rb is the row
+// stride in bytes.
+int check_weights(const void* w, int64_t m, int64_t k, int qt, int64_t* rb) {
+    if (!w) return QMM_ERR_NULL;
+    if (!valid_qt(qt)) return QMM_ERR_QTYPE;
+    if (m < 1 || k < 1) return QMM_ERR_SHAPE;
+    if (k % kFmt[qt].qk != 0 || k % 4 != 0) return QMM_ERR_K_ALIGN;
+    if (!aligned(w, 16)) return QMM_ERR_ALIGN;
+    if (m > INT_MAX || k > INT_MAX) return QMM_ERR_RANGE;
+    *rb = k / kFmt[qt].qk * kFmt[qt].bb;
+    int64_t total;
+    if (!mul_ok(m, *rb, &total)) return QMM_ERR_SHAPE;
+    return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmm_abi_version(void) { return 1; }
+
+int64_t qmm_row_bytes(int qtype, int64_t k) {
+    if (!valid_qt(qtype)) return -QMM_ERR_QTYPE;
+    if (k < 1) return -QMM_ERR_SHAPE;
+    if (k % kFmt[qtype].qk != 0) return -QMM_ERR_K_ALIGN;
+    int64_t r;
+    if (!mul_ok(k / kFmt[qtype].qk, kFmt[qtype].bb, &r)) return -QMM_ERR_SHAPE;
+    return r;
+}
+
+int qmm_block_elems(int qtype) { return valid_qt(qtype) ? kFmt[qtype].qk : -QMM_ERR_QTYPE; }
+
+int qmm_gemv_max_n(void) {
+    std::call_once(g_env_once, parse_env);
+    return g_gemv_max_n;
+}
+
+const char* qmm_status_str(int s) {
+    switch (s) {
+        case QMM_OK: return "ok";
+        case QMM_ERR_NULL: return "null pointer argument";
+        case QMM_ERR_SHAPE: return "invalid shape (a size < 1 or an int64 overflow)";
+        case QMM_ERR_K_ALIGN: return "k is not a multiple of the block size (and of 4)";
+        case QMM_ERR_QTYPE: return "unknown or unsupported qtype";
+        case QMM_ERR_ALIGN: return "misaligned pointer (w, x and outputs must be 16-byte aligned)";
+        case QMM_ERR_LAUNCH: return "kernel launch failed";
+        case QMM_ERR_PATH: return "unknown kernel path";
+        case QMM_ERR_RANGE: return "size outside the kernels' index range (or bad QMM_GEMV_MAX_N)";
+    }
+    return "unknown status";
+}
+
+int qmm_gemm_path(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
+                  int qtype, int path, hipStream_t stream) {
+    if (!dst || !x) return QMM_ERR_NULL;
+    int64_t rb;
+    int st = check_weights(w, m, k, qtype, &rb);
+    if (st) return st;
+    if (n < 1) return QMM_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(dst, 16)) return QMM_ERR_ALIGN;
+    if (n > INT_MAX) return QMM_ERR_RANGE;
+    int64_t t1, t2;
+    if (!mul_ok(n, k, &t1) || !mul_ok(n, m, &t2)) return QMM_ERR_SHAPE;
+    if (path == QMM_PATH_AUTO) {
+        const int lim = qmm_gemv_max_n();
+        if (lim < 0) return QMM_ERR_RANGE;
+        path = n <= lim ? QMM_PATH_GEMV : QMM_PATH_MFMA;
+    }
+    if (path == QMM_PATH_GEMV) {
+        // one work group addresses at most this window of w, and 8 token rows of x
+        if (qmm::gemv_max_window_bytes(qtype, k, rb) >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
+        if (8 * k * 4 >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
+        qmm::launch_gemv(dst, w, x, m, k, n, qtype, rb, stream);
+        return launch_status();
+    }
+    if (path == QMM_PATH_MFMA) {
+        if ((int64_t)qmm::MFMA_BM * rb + 16 >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
+        if ((int64_t)qmm::MFMA_BN * k * 4 >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
+        const int64_t tiles = ((m + qmm::MFMA_BM - 1) / qmm::MFMA_BM) * ((n + qmm::MFMA_BN - 1) / qmm::MFMA_BN);
+        if (tiles > INT_MAX) return QMM_ERR_RANGE;
+        qmm::launch_gemm_mfma(dst, w, x, m, k, n, qtype, rb, stream);
+        return launch_status();
+    }
+    return QMM_ERR_PATH;
+}
+
+int qmm_gemm(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qtype,
+             hipStream_t stream) {
+    return qmm_gemm_path(dst, w, x, m, k, n, qtype, QMM_PATH_AUTO, stream);
+}
+
+int qmm_moe_gateup(float* gate_out, float* up_out, const void* w_gate, const void* w_up,
+                   const int32_t* expert_ids, const float* pair_scale, const float* x, int64_t t,
+                   int64_t n_used, int64_t n_expert, int64_t in_f, int64_t n_ff, int qtype,
+                   hipStream_t stream) {
+    if (!gate_out || !up_out || !w_gate || !w_up || !expert_ids || !pair_scale || !x)
+        return QMM_ERR_NULL;
+    if (t < 1 || n_used < 1 || n_expert < 1 || n_used > n_expert) return QMM_ERR_SHAPE;
+    int64_t rb;
+    int64_t rows;
+    if (!mul_ok(n_expert, n_ff, &rows)) return QMM_ERR_SHAPE;
+    int st = check_weights(w_gate, rows, in_f, qtype, &rb);
+    if (st) return st;
+    st = check_weights(w_up, rows, in_f, qtype, &rb);
+    if (st) return st;
+    if (!aligned(x, 16) || !aligned(gate_out, 4) || !aligned(up_out, 4) || !aligned(pair_scale, 4) ||
+        !aligned(expert_ids, 4))
+        return QMM_ERR_ALIGN;
+    int64_t n_pairs;
+    if (!mul_ok(t, n_used, &n_pairs)) return QMM_ERR_SHAPE;
+    if (n_pairs > 65535 || n_ff > INT_MAX || t * in_f * 4 >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
+    if (qmm::gemv_max_window_bytes(qtype, in_f, rb) >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
+    qmm::launch_moe(gate_out, up_out, w_gate, w_up, expert_ids, pair_scale, x, t, n_used, n_expert,
+                    in_f, n_ff, qtype, rb, stream);
+    return launch_status();
+}
+
+int qmm_stream_loadonly(uint32_t* sink, const void* w, int64_t m, int64_t k, int qtype,
+                        hipStream_t stream) {
+    if (!sink) return QMM_ERR_NULL;
+    int64_t rb;
+    int st = check_weights(w, m, k, qtype, &rb);
+    if (st) return st;
+    if (!aligned(sink, 4)) return QMM_ERR_ALIGN;
+    if (qmm::gemv_max_window_bytes(qtype, k, rb) >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
+    qmm::launch_loadonly(sink, w, m, k, qtype, rb, stream);
+    return launch_status();
+}
+
+}  // extern "C"

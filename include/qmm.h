@@ -1,0 +1,156 @@
+/*
+ * qmm.h - dequant-fused projection matmul on block-quantized weights (gfx950).
+ *
+ * The operation (cera 0.4.0 examples/wgpu_gemm_bench.rs, the Shape doc
+ * comment and the SHADER diff comment):
+ *
+ *     dst[j*m + i] = sum_{c<k} deq(W)[i][c] * x[j*k + c]     0<=i<m, 0<=j<n
+ *
+ * i.e. dst[n, m] = src0[m, k] * src1[n, k] with dst column-major, stride m.
+ * W is m rows of row_bytes(qtype, k) bytes, blocks along k, rows contiguous,
+ * no padding (the packed sizes of the VARIANTS table on the same page;
+ * NVFP4 from memra-engine moe_rows_ceiling_bench.rs, synth_rows).
+ *
+ * Conventions for every entry point below:
+ *  - Pointers marked DEVICE are device (HBM) pointers owned by the caller;
+ *    the library never frees or retains them.
+ *  - Work is enqueued asynchronously on `stream` (0 = the null stream).  No
+ *    call allocates device memory, synchronizes, or keeps state beyond a
+ *    lazily cached device property and the parsed QMM_GEMV_MAX_N knob, so the
+ *    calls can be recorded into a hipGraph.
+ *  - Arguments are validated on the host before anything is launched; a
+ *    rejected call returns a non-zero qmm_status and launches nothing.  A
+ *    launch failure reported by the runtime returns QMM_ERR_LAUNCH.
+ *  - Outputs are a pure function of the inputs: kernels read only the bytes
+ *    the shapes define (loads past the end are bounds-checked by the buffer
+ *    descriptors and return zero) and use no float atomics, so two identical
+ *    calls produce bit-identical results.
+ *  - dst must not alias w or x.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight formats.  Block sizes (elements / bytes): F32 1/4, Q4_0 32/18,
+ * Q8_0 32/34, Q4_K 256/144, Q6_K 256/210, NVFP4 64/36 (the packed-size
+ * formulas of cera wgpu_gemm_bench.rs VARIANTS and memra synth_rows). */
+typedef enum {
+    QMM_F32 = 0,
+    QMM_Q4_0 = 1,
+    QMM_Q8_0 = 2,
+    QMM_Q4_K = 3,
+    QMM_Q6_K = 4,
+    QMM_NVFP4 = 5
+} qmm_qtype;
+
+typedef enum {
+    QMM_OK = 0,
+    QMM_ERR_NULL = 1,      /* a required pointer is null                      */
+    QMM_ERR_SHAPE = 2,     /* a size is < 1, or a product overflows int64      */
+    QMM_ERR_K_ALIGN = 3,   /* k is not a multiple of the block size (and of 4) */
+    QMM_ERR_QTYPE = 4,     /* unknown qtype, or not valid for this entry point */
+    QMM_ERR_ALIGN = 5,     /* w not 16-byte aligned, or x/dst not 16-byte aligned */
+    QMM_ERR_LAUNCH = 6,    /* the runtime reported a launch error              */
+    QMM_ERR_PATH = 7,      /* unknown path selector                            */
+    QMM_ERR_RANGE = 8      /* a size exceeds what the kernels index (see below) */
+} qmm_status;
+
+/* Kernel path selector for qmm_gemm_path. */
+typedef enum {
+    QMM_PATH_AUTO = 0,     /* n <= qmm_gemv_max_n() -> GEMV, else MFMA        */
+    QMM_PATH_GEMV = 1,     /* f32 FMA, any n (decode path)                     */
+    QMM_PATH_MFMA = 2      /* f16 MFMA tiles, f32 accumulation, any n (prefill) */
+} qmm_path;
+
+/*
+ * qmm_gemm: the projection above.
+ *   dst   DEVICE float[n*m], written (every element), column-major stride m.
+ *   w     DEVICE packed weights, m*row_bytes(qtype,k) bytes, 16-byte aligned.
+ *         For QMM_F32, float[m*k].
+ *   x     DEVICE float[n*k] activations, row-major, 16-byte aligned.
+ *   m,k,n >= 1; k % block_elems(qtype) == 0 and k % 4 == 0.
+ *   qtype one of QMM_F32..QMM_NVFP4.
+ * Dispatch (the GEMV-vs-GEMM crossover of aprender-serve cublas_prefill,
+ * cublas_gemm_threshold): n <= qmm_gemv_max_n() runs the f32 GEMV (results
+ * within 1e-5 * sum|w*x| of the exact value), otherwise the MFMA kernel,
+ * which rounds W and x to f16 (RNE) and accumulates in f32 (within
+ * 2e-3 * sum|w*x|).
+ * Limits: m*row_bytes and n*k*4 each below 2^31 per 128-row / 128-token tile
+ * window; m, n, k below 2^31.  Larger values return QMM_ERR_RANGE.
+ */
+int qmm_gemm(float* dst, const void* w, const float* x,
+             int64_t m, int64_t k, int64_t n, int qtype, hipStream_t stream);
+
+/* qmm_gemm with an explicit kernel path (QMM_PATH_*).  Same arguments and
+ * errors as qmm_gemm; QMM_ERR_PATH for an unknown path. */
+int qmm_gemm_path(float* dst, const void* w, const float* x,
+                  int64_t m, int64_t k, int64_t n, int qtype, int path,
+                  hipStream_t stream);
+
+/*
+ * qmm_moe_gateup: the MoE gate and up projections over the routed experts
+ * (memra-engine moe_rows_ceiling_bench.rs: gate/up planes, in_f -> n_ff,
+ * n_used experts per token, per-pair f32 scales indexed plane*n_pairs+pair as
+ * the pointer table is).  With n_pairs = t*n_used, pair p = tau*n_used + s and
+ * expert e = expert_ids[p]:
+ *     gate_out[p*n_ff + r] = pair_scale[p]           * sum_c Wg[e][r][c] * x[tau*in_f + c]
+ *     up_out  [p*n_ff + r] = pair_scale[n_pairs + p] * sum_c Wu[e][r][c] * x[tau*in_f + c]
+ *   gate_out, up_out  DEVICE float[n_pairs*n_ff], written.
+ *   w_gate, w_up      DEVICE, each n_expert*n_ff rows of row_bytes(qtype,in_f)
+ *                     bytes (expert-major), 16-byte aligned.
+ *   expert_ids        DEVICE int32[n_pairs]; an id outside [0, n_expert) makes
+ *                     that pair's outputs NaN (no out-of-range read).
+ *   pair_scale        DEVICE float[2*n_pairs] (gate plane, then up plane).
+ *   x                 DEVICE float[t*in_f], 16-byte aligned.
+ *   qtype             QMM_NVFP4 (the other formats are accepted too).
+ * Each selected expert's rows are read once per call and applied to every
+ * token that chose it.  f32 arithmetic; results within 1e-5*|scale|*sum|w*x|.
+ */
+int qmm_moe_gateup(float* gate_out, float* up_out,
+                   const void* w_gate, const void* w_up,
+                   const int32_t* expert_ids, const float* pair_scale,
+                   const float* x, int64_t t, int64_t n_used, int64_t n_expert,
+                   int64_t in_f, int64_t n_ff, int qtype, hipStream_t stream);
+
+/*
+ * qmm_stream_loadonly: the load-only twin of the GEMV (memra-engine
+ * moe_rows_ceiling_bench.rs, the "loadonly" ceiling-probe arm: the same
+ * addresses with the arithmetic deleted).  Reads every byte of the m packed
+ * rows with the GEMV's access pattern and writes one checksum word per row to
+ * sink (DEVICE uint32[m]) so the loads stay live.  Used only to measure the
+ * access-pattern ceiling.
+ */
+int qmm_stream_loadonly(uint32_t* sink, const void* w, int64_t m, int64_t k,
+                        int qtype, hipStream_t stream);
+
+/* Packed bytes of one row of k weights; < 0 is -qmm_status on error.
+ * (Sizes per the VARIANTS table of cera wgpu_gemm_bench.rs and memra
+ * synth_rows.) */
+int64_t qmm_row_bytes(int qtype, int64_t k);
+
+/* Elements per block of qtype, or -QMM_ERR_QTYPE. */
+int qmm_block_elems(int qtype);
+
+/* The n at or below which QMM_PATH_AUTO uses the GEMV (default 32; the
+ * environment variable QMM_GEMV_MAX_N overrides it; a set but unparseable or
+ * non-positive value makes this return -QMM_ERR_RANGE and every AUTO call
+ * fail with QMM_ERR_RANGE, never a silent default). */
+int qmm_gemv_max_n(void);
+
+/* Static string for a status code. */
+const char* qmm_status_str(int status);
+
+/* Library ABI version (incremented on incompatible changes). */
+int qmm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

@@ -1,0 +1,102 @@
+"""Shared helpers for the GPU parity tests: seeded inputs, device transfer,
+oracle comparison.  Inputs come from ``synth`` (shared with nothing else);
+expected values come only from ``oracle``."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import encoders as enc
+from oracle import formats, ref
+from synth import gen
+
+TAU_F16 = 2e-3     # MFMA path: W and x rounded to f16, f32 accumulation
+TAU_F32 = 1e-5     # GEMV and MoE: f32 arithmetic
+
+
+def note(msg: str) -> None:
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def weights(qt: str, m: int, k: int, buf_id: int = 0) -> np.ndarray:
+    """Seeded weights: f32 values, NVFP4 rows, or the page's packed byte stream."""
+    if qt == "f32":
+        return gen.dense_weights(m * k, True, buf_id)
+    if qt == "nvfp4":
+        return gen.nvfp4_rows(m, k, gen.SEED_MOE_W + buf_id)
+    return gen.dense_weights(m * formats.row_bytes(qt, k), False, buf_id)
+
+
+def acts(n: int, k: int, seed_off: int = 0) -> np.ndarray:
+    return gen.unit_f32(n * k, gen.SEED_X + 0x9E37 * seed_off).reshape(n, k)
+
+
+def exact_weights(qt: str, m: int, k: int, seed: int) -> np.ndarray:
+    """Blocks whose every weight and every product with a grid_f32 activation
+    is exact in f16 and f32 (power-of-two scales, small integers)."""
+    rng = np.random.default_rng(seed)
+    if qt == "f32":
+        return (rng.integers(-64, 65, m * k) / 16.0).astype(np.float32)
+    qk = formats.block_elems(qt)
+    nb = m * k // qk
+    # largest d exponent per format so that every weight is a multiple of 1/16
+    # below 128 in magnitude (11 significant bits: exact in f16)
+    e_hi = {"q4_0": 16, "q8_0": 16, "q4_k": 15, "q6_k": 14, "nvfp4": 0}[qt]
+    out = []
+    for _ in range(nb):
+        e = int(rng.integers(11, e_hi + 1)) if e_hi else 0   # d = 2^(e-15) >= 1/16
+        d = (int(rng.integers(0, 2)) << 15) | (e << 10)
+        if qt == "q4_0":
+            out.append(enc.q4_0(d, rng.integers(0, 16, 32)))
+        elif qt == "q8_0":
+            out.append(enc.q8_0(d, rng.integers(-16, 17, 32)))
+        elif qt == "q4_k":
+            dmin = (int(rng.integers(0, 2)) << 15) | (int(rng.integers(11, 15)) << 10)
+            out.append(enc.q4_k(d, dmin, rng.integers(0, 8, 8), rng.integers(0, 8, 8),
+                                rng.integers(0, 16, 256)))
+        elif qt == "q6_k":
+            out.append(enc.q6_k(d, rng.integers(-4, 5, 16), rng.integers(0, 64, 256)))
+        elif qt == "nvfp4":
+            out.append(enc.nvfp4(rng.integers(0, 8, 4) | 0x38, rng.integers(0, 16, 64)))
+        else:
+            raise ValueError(qt)
+    return np.frombuffer(b"".join(out), dtype=np.uint8).copy()
+
+
+def to_dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def gpu_gemm(qt: str, w: np.ndarray, x: np.ndarray, m: int, path: str) -> np.ndarray:
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    out = qmm.gemm(to_dev(w), to_dev(x), m, qt, path=path)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_full(qt, w, x, m, k, n, got, tau, what=""):
+    r, S = ref.gemm_ref(qt, w, x, m, k, n)
+    ok, worst = ref.tolerance_check(got, r, S, tau)
+    assert ok, f"{what}: worst |gpu-ref|/(tau*S) = {worst:.3g}"
+    return worst
+
+
+def check_sampled(qt, w, x, m, k, got, tau, n_samples=4000, seed=0, what=""):
+    """Compare sampled outputs got[j, i] with the oracle computed one by one,
+    always including the four corners (tile edges and ragged tails)."""
+    n = got.shape[0]
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([rng.integers(0, m, n_samples), [0, m - 1, 0, m - 1]])
+    cols = np.concatenate([rng.integers(0, n, n_samples), [0, 0, n - 1, n - 1]])
+    rb = formats.row_bytes(qt, k)
+    r, S = ref.gemm_ref_rows(qt, w, x, m, k, rows, cols, rb)
+    g = got[cols, rows]
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    ok, worst = ref.tolerance_check(g, r, S, tau)
+    assert ok, f"{what}: worst |gpu-ref|/(tau*S) = {worst:.3g}"
+    return worst

@@ -1,0 +1,127 @@
+"""The C-ABI boundary, on the CPU: the library loads, exports every function
+include/qmm.h declares, reports the pages' packed sizes, and rejects bad
+arguments with a status before anything is launched (no GPU needed)."""
+
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+
+
+def _lib():
+    from gemv_prefill_decode_amd import load, lib_path
+    if not os.path.exists(lib_path()):
+        pytest.skip("libqmm.so not built")
+    return load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_entry_points():
+    names = _declared()
+    for want in ("qmm_gemm", "qmm_gemm_path", "qmm_moe_gateup", "qmm_row_bytes",
+                 "qmm_block_elems", "qmm_status_str", "qmm_stream_loadonly"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True)
+    if out.returncode == 0:
+        exported = set(re.findall(r"\bT (qmm_\w+)", out.stdout))
+        assert set(_declared()) <= exported
+
+
+def test_row_bytes_match_pages_and_oracle():
+    from gemv_prefill_decode_amd import row_bytes, block_elems, QTYPES
+    from oracle import formats
+    _lib()
+    for name in QTYPES:
+        qk = formats.block_elems(name)
+        assert block_elems(name) == qk
+        for k in (qk * 4, qk * 32, 4096 if 4096 % qk == 0 else qk):
+            assert row_bytes(name, k) == formats.row_bytes(name, k)
+    lib = _lib()
+    assert lib.qmm_row_bytes(3, 1000) == -3        # Q4_K, k % 256 != 0 -> -QMM_ERR_K_ALIGN
+    assert lib.qmm_row_bytes(9, 256) == -4         # unknown qtype
+    assert lib.qmm_row_bytes(1, 0) == -2           # k < 1
+    assert lib.qmm_block_elems(7) == -4
+
+
+def test_status_strings():
+    lib = _lib()
+    for s in range(9):
+        assert lib.qmm_status_str(s).decode() not in ("", "unknown status")
+    assert lib.qmm_status_str(99).decode() == "unknown status"
+    assert lib.qmm_abi_version() == 1
+
+
+def test_validation_rejects_before_launch():
+    """Every call here fails validation on the host; none reaches a launch, so
+    this runs without a GPU."""
+    lib = _lib()
+    A = ctypes.c_void_p(1 << 20)        # 16-byte aligned fake device pointers
+    B = ctypes.c_void_p((1 << 20) + 4)  # misaligned
+    z = ctypes.c_void_p(0)
+    s0 = ctypes.c_void_p(0)
+    g = lib.qmm_gemm_path
+    assert g(z, A, A, 64, 256, 4, 3, 0, s0) == 1          # null dst
+    assert g(A, z, A, 64, 256, 4, 3, 0, s0) == 1          # null w
+    assert g(A, A, z, 64, 256, 4, 3, 0, s0) == 1          # null x
+    assert g(A, A, A, 0, 256, 4, 3, 0, s0) == 2           # m < 1
+    assert g(A, A, A, 64, 256, 0, 3, 0, s0) == 2          # n < 1
+    assert g(A, A, A, 64, 0, 4, 3, 0, s0) == 2            # k < 1
+    assert g(A, A, A, 64, 128, 4, 3, 0, s0) == 3          # Q4_K needs k % 256
+    assert g(A, A, A, 64, 48, 4, 1, 0, s0) == 3           # Q4_0 needs k % 32
+    assert g(A, A, A, 64, 6, 4, 0, 0, s0) == 3            # f32 needs k % 4
+    assert g(A, A, A, 64, 256, 4, 6, 0, s0) == 4          # unknown qtype
+    assert g(A, B, A, 64, 256, 4, 3, 0, s0) == 5          # misaligned w
+    assert g(A, A, B, 64, 256, 4, 3, 0, s0) == 5          # misaligned x
+    assert g(B, A, A, 64, 256, 4, 3, 0, s0) == 5          # misaligned dst
+    assert g(A, A, A, 64, 256, 4, 3, 9, s0) == 7          # unknown path
+    assert g(A, A, A, 1 << 40, 256, 4, 3, 0, s0) == 8     # m beyond int range
+    m = lib.qmm_moe_gateup
+    assert m(A, A, A, A, z, A, A, 1, 8, 64, 4096, 2048, 5, s0) == 1   # null ids
+    assert m(A, A, A, A, A, A, A, 1, 9, 8, 4096, 2048, 5, s0) == 2    # n_used > n_expert
+    assert m(A, A, A, A, A, A, A, 1, 8, 64, 4000, 2048, 5, s0) == 3   # in_f % 64
+    assert m(A, A, A, A, A, A, A, 1, 8, 64, 4096, 2048, 8, s0) == 4   # qtype
+    lo = lib.qmm_stream_loadonly
+    assert lo(z, A, 64, 256, 3, s0) == 1
+    assert lo(A, A, 64, 255, 3, s0) == 3
+
+
+@pytest.mark.parametrize("value,expect", [("16", 16), ("1", 1), ("abc", -8), ("0", -8), ("-3", -8)])
+def test_gemv_max_n_env_is_strict(value, expect):
+    _lib()
+    code = ("import sys; sys.path.insert(0, %r); from gemv_prefill_decode_amd import load; "
+            "print(load().qmm_gemv_max_n())" % ROOT)
+    env = dict(os.environ, QMM_GEMV_MAX_N=value)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env)
+    assert out.returncode == 0, out.stderr
+    assert int(out.stdout.strip()) == expect
+    if expect < 0:
+        # an AUTO call with a bad knob fails loudly (before any launch)
+        code2 = ("import sys, ctypes; sys.path.insert(0, %r); from gemv_prefill_decode_amd import load; "
+                 "A = ctypes.c_void_p(1 << 20); "
+                 "print(load().qmm_gemm(A, A, A, 64, 256, 4, 3, ctypes.c_void_p(0)))" % ROOT)
+        out = subprocess.run([sys.executable, "-c", code2], capture_output=True, text=True, env=env)
+        assert int(out.stdout.strip()) == 8
+
+
+def test_default_gemv_max_n():
+    lib = _lib()
+    if "QMM_GEMV_MAX_N" in os.environ:
+        pytest.skip("QMM_GEMV_MAX_N set in the environment")
+    assert lib.qmm_gemv_max_n() == 32

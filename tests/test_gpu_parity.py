@@ -1,0 +1,224 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C-ABI.
+
+Small shapes that span several tiles and ragged tails are compared element
+by element over the whole output; exact-structured inputs must match bit for
+bit on both paths; identity activations pin the output layout; repeated runs
+must be bit-identical; guard bands around dst must stay untouched.
+"""
+
+import numpy as np
+import pytest
+
+from gpu_helpers import (TAU_F16, TAU_F32, acts, check_full, exact_weights, gpu_gemm, note,
+                         to_dev, weights)
+from oracle import formats, ref
+from synth import gen
+
+pytestmark = pytest.mark.gpu
+
+QTS = ["f32", "q4_0", "q8_0", "q4_k", "q6_k", "nvfp4"]
+
+# (m, k) per format: ragged m, several units per row, odd unit counts / tails
+GEMV_SHAPES = {
+    "f32": [(67, 292), (300, 1024)],
+    "q4_0": [(67, 1184), (300, 1024)],
+    "q8_0": [(67, 1184), (300, 1024)],
+    "q4_k": [(67, 1280), (300, 1024)],
+    "q6_k": [(67, 1280), (300, 1024)],
+    "nvfp4": [(67, 1216), (300, 1024)],
+}
+
+
+@pytest.mark.parametrize("qt", QTS)
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8, 13, 32])
+def test_gemv_parity(qt, n):
+    for si, (m, k) in enumerate(GEMV_SHAPES[qt]):
+        note(f"gemv {qt} m={m} k={k} n={n}")
+        w = weights(qt, m, k, si)
+        x = acts(n, k, si)
+        got = gpu_gemm(qt, w, x, m, "gemv")
+        check_full(qt, w, x, m, k, n, got, TAU_F32, f"gemv {qt} {m}x{k} n={n}")
+
+
+MFMA_SHAPES = {
+    "f32": [(300, 292, 33), (128, 1024, 200)],
+    "q4_0": [(300, 1184, 33), (129, 1024, 257)],
+    "q8_0": [(300, 1184, 33), (129, 1024, 257)],
+    "q4_k": [(300, 1280, 33), (129, 1024, 257)],
+    "q6_k": [(300, 1280, 33), (129, 1024, 257)],
+    "nvfp4": [(300, 1216, 33), (129, 1024, 257)],
+}
+
+
+@pytest.mark.parametrize("qt", QTS)
+def test_mfma_parity(qt):
+    for si, (m, k, n) in enumerate(MFMA_SHAPES[qt]):
+        note(f"mfma {qt} m={m} k={k} n={n}")
+        w = weights(qt, m, k, 10 + si)
+        x = acts(n, k, 10 + si)
+        got = gpu_gemm(qt, w, x, m, "mfma")
+        check_full(qt, w, x, m, k, n, got, TAU_F16, f"mfma {qt} {m}x{k} n={n}")
+
+
+@pytest.mark.parametrize("qt", QTS)
+def test_auto_dispatch_threshold(qt):
+    m, k = 130, 512 if qt != "f32" else 512
+    for n in (32, 33):
+        note(f"auto {qt} n={n}")
+        w = weights(qt, m, k, 3)
+        x = acts(n, k, 3)
+        got = gpu_gemm(qt, w, x, m, "auto")
+        gv = gpu_gemm(qt, w, x, m, "gemv" if n <= 32 else "mfma")
+        assert np.array_equal(got, gv)
+
+
+@pytest.mark.parametrize("qt", QTS)
+@pytest.mark.parametrize("path", ["gemv", "mfma"])
+def test_exact_structured_inputs(qt, path):
+    """Power-of-two scales, small integer codes, x on a 1/16 grid: every
+    product and partial sum is exact, so the GPU must equal the oracle bit
+    for bit on both paths (f16 rounding included)."""
+    m, k = 150, 512
+    n = 8 if path == "gemv" else 70
+    note(f"exact {qt} {path}")
+    w = exact_weights(qt, m, k, 7)
+    x = gen.structured_exact(n * k, 11).reshape(n, k)
+    got = gpu_gemm(qt, w, x, m, path)
+    r, _ = ref.gemm_ref(qt, w, x, m, k, n)
+    assert np.array_equal(got.astype(np.float64), r)
+
+
+@pytest.mark.parametrize("qt", QTS)
+def test_identity_activations_mfma(qt):
+    """x = I_k (n = k): dst[j, i] = f16(f32(W[i, j])) exactly (the weight is
+    decoded to f32 and rounded once more to f16 for the matrix cores; both
+    roundings are to nearest even).  Pins the tile mapping of every weight row
+    and k index into dst."""
+    m, k = 130, 256
+    note(f"identity mfma {qt}")
+    w = weights(qt, m, k, 21)
+    x = np.eye(k, dtype=np.float32)
+    got = gpu_gemm(qt, w, x, m, "mfma")
+    W = formats.decode(qt, w, m, k)
+    want = W.T.astype(np.float32).astype(np.float16).astype(np.float64)
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+@pytest.mark.parametrize("qt", QTS)
+def test_identity_windows_gemv(qt):
+    """Sliding one-hot windows (n = 32 tokens, token j selects k index
+    c0 + j): dst[j, i] = f32(W[i, c0 + j]) exactly on the f32 path."""
+    m, k = 70, 512
+    note(f"identity gemv {qt}")
+    w = weights(qt, m, k, 22)
+    W = formats.decode(qt, w, m, k)
+    for c0 in range(0, k, 32):
+        x = np.zeros((32, k), dtype=np.float32)
+        x[np.arange(32), c0 + np.arange(32)] = 1.0
+        got = gpu_gemm(qt, w, x, m, "gemv")
+        want = W[:, c0:c0 + 32].T.astype(np.float32)
+        assert np.array_equal(got, want), c0
+
+
+@pytest.mark.parametrize("path", ["gemv", "mfma"])
+def test_deterministic_and_guard_bands(path):
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    qt, m, k = "q6_k", 260, 1024
+    n = 5 if path == "gemv" else 90
+    note(f"determinism {path}")
+    w, x = to_dev(weights(qt, m, k, 4)), to_dev(acts(n, k, 4))
+    pad = 1024
+    buf = torch.full((2 * pad + n * m,), 12345.0, dtype=torch.float32, device="cuda")
+    out = buf[pad:pad + n * m].view(n, m)
+    qmm.gemm(w, x, m, qt, out=out, path=path)
+    first = out.clone()
+    qmm.gemm(w, x, m, qt, out=out, path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(first, out)
+    assert bool((buf[:pad] == 12345.0).all()) and bool((buf[pad + n * m:] == 12345.0).all())
+
+
+def test_gemv_and_mfma_agree_within_tolerance():
+    m, k, n = 200, 1024, 16
+    for qt in QTS:
+        note(f"cross-path {qt}")
+        w = weights(qt, m, k, 30)
+        x = acts(n, k, 30)
+        a = gpu_gemm(qt, w, x, m, "gemv")
+        b = gpu_gemm(qt, w, x, m, "mfma")
+        _, S = ref.gemm_ref(qt, w, x, m, k, n)
+        assert np.all(np.abs(a - b) <= (TAU_F16 + TAU_F32) * S)
+
+
+# ------------------------------------------------------------------ MoE
+
+
+def _moe_inputs(n_expert, in_f, n_ff, t, n_used, seed=0):
+    wg = np.concatenate([gen.nvfp4_rows(n_ff, in_f, gen.SEED_MOE_W + 2 * e + 0) for e in range(n_expert)])
+    wu = np.concatenate([gen.nvfp4_rows(n_ff, in_f, gen.SEED_MOE_W + 2 * e + 1) for e in range(n_expert)])
+    ids = gen.expert_ids(t, n_used, n_expert, gen.SEED_EXPERTS + seed)
+    sc = gen.pair_scales(2 * t * n_used)
+    x = gen.xorshift_f32(t * in_f, gen.SEED_MOE_X + seed).reshape(t, in_f)
+    return wg, wu, ids, sc, x
+
+
+def _gpu_moe(wg, wu, ids, sc, x, n_expert, n_ff):
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    g, u = qmm.moe_gateup(to_dev(wg), to_dev(wu), to_dev(ids.astype(np.int32)), to_dev(sc),
+                          to_dev(x), n_expert, n_ff, "nvfp4")
+    torch.cuda.synchronize()
+    return g.cpu().numpy(), u.cpu().numpy()
+
+
+@pytest.mark.parametrize("t,n_used", [(1, 4), (3, 2), (5, 4), (16, 3)])
+def test_moe_parity_small(t, n_used):
+    n_expert, in_f, n_ff = 6, 256, 80
+    note(f"moe small t={t} n_used={n_used}")
+    wg, wu, ids, sc, x = _moe_inputs(n_expert, in_f, n_ff, t, n_used, seed=t)
+    g, u = _gpu_moe(wg, wu, ids, sc, x, n_expert, n_ff)
+    rg, ru, Sg, Su = ref.moe_ref("nvfp4", wg, wu, ids, sc, x, n_expert, in_f, n_ff)
+    for got, r, S in ((g, rg, Sg), (u, ru, Su)):
+        ok, worst = ref.tolerance_check(got, r, S, TAU_F32)
+        assert ok, worst
+
+
+def test_moe_repeated_expert_many_tokens():
+    """One expert chosen by 70 tokens (more than one gather chunk)."""
+    n_expert, in_f, n_ff, t, n_used = 4, 128, 40, 70, 2
+    note("moe repeated expert")
+    wg, wu, _, sc, x = _moe_inputs(n_expert, in_f, n_ff, t, n_used)
+    ids = np.zeros((t, n_used), dtype=np.int32)
+    ids[:, 0] = 2
+    ids[:, 1] = np.arange(t) % 2 * 3  # experts 0 and 3 alternate
+    g, u = _gpu_moe(wg, wu, ids, sc, x, n_expert, n_ff)
+    rg, ru, Sg, Su = ref.moe_ref("nvfp4", wg, wu, ids, sc, x, n_expert, in_f, n_ff)
+    assert ref.tolerance_check(g, rg, Sg, TAU_F32)[0]
+    assert ref.tolerance_check(u, ru, Su, TAU_F32)[0]
+
+
+def test_moe_invalid_expert_id_gives_nan():
+    n_expert, in_f, n_ff, t, n_used = 4, 128, 40, 2, 2
+    note("moe invalid id")
+    wg, wu, ids, sc, x = _moe_inputs(n_expert, in_f, n_ff, t, n_used)
+    ids = np.array([[1, 7], [2, -1]], dtype=np.int32)
+    g, u = _gpu_moe(wg, wu, ids, sc, x, n_expert, n_ff)
+    for out in (g, u):
+        assert np.all(np.isnan(out[1])) and np.all(np.isnan(out[3]))
+        assert np.all(np.isfinite(out[0])) and np.all(np.isfinite(out[2]))
+    rg, ru, Sg, Su = ref.moe_ref("nvfp4", wg, wu, np.array([[1, 0], [2, 0]]), sc, x, n_expert, in_f, n_ff)
+    assert ref.tolerance_check(g[[0, 2]], rg[[0, 2]], Sg[[0, 2]], TAU_F32)[0]
+
+
+def test_loadonly_twin_runs_and_is_deterministic():
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    for qt in QTS:
+        m, k = 300, 1024
+        note(f"loadonly {qt}")
+        w = to_dev(weights(qt, m, k, 5))
+        a = qmm.stream_loadonly(w, m, k, qt).clone()
+        b = qmm.stream_loadonly(w, m, k, qt)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
