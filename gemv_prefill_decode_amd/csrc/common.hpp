@@ -82,6 +82,36 @@ __device__ __forceinline__ uint32_t pack_f2h(float a, float b) {
 
 __device__ __forceinline__ uint32_t byte_of(uint32_t v, int b) { return (v >> (8 * b)) & 0xFFu; }
 
+// Byte b of v as f32 (v_cvt_f32_ubyte{0..3}: select and convert in one
+// instruction; the compiler's own pattern is lost once the byte is known to
+// hold a nibble).
+template <int B>
+__device__ __forceinline__ float ubyte_f32(uint32_t v) {
+    float r;
+    if constexpr (B == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(v));
+    else if constexpr (B == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(v));
+    else if constexpr (B == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(v));
+    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
+__device__ __forceinline__ float ubyte_f32(uint32_t v, int b) {
+    switch (b) {
+        case 0: return ubyte_f32<0>(v);
+        case 1: return ubyte_f32<1>(v);
+        case 2: return ubyte_f32<2>(v);
+        default: return ubyte_f32<3>(v);
+    }
+}
+
+// Index of the calling wave in its work group, as a wave-uniform (scalar)
+// value: buffer descriptors derived from it stay in SGPRs.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+__device__ __forceinline__ int uniform_i32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // OCP FP8 E4M3FN byte -> f32 (exact): sign, 4-bit exponent bias 7, 3-bit
 // mantissa, exponent 0 subnormal, S.1111.111 NaN, no infinities.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {

@@ -4,445 +4,708 @@
 // lanes that share a row reduce with cross-lane shuffles.
 //
 // Work split.  A row of k weights is cut into "units" (16..64 weights each,
-// per format).  The LPR lanes of a lane group take units gl, gl+LPR, ... of
-// the same R rows, so one wave load instruction reads LPR consecutive units
-// of a row (coalesced), and the activations a lane loads for its units are
-// reused for all R rows.  Each unit's products are summed in a fresh partial
-// (at most 64 terms) before joining the lane's running sum, and the LPR lane
-// partials are combined by a butterfly, which keeps every f32 rounding chain
-// short (64 + k/(UE*LPR) + log2(LPR) terms).
+// per format).  The LPR lanes of a lane group take units gl + LPR*uu
+// (uu = 0, 1, ...) of the same R rows, so one wave load instruction reads LPR
+// consecutive units of a row, and the activations a lane reads for a unit are
+// reused for its R rows.  Because LPR is a power of two no smaller than the
+// number of units per block-format period, the position of a lane's unit
+// inside its block is the same for every uu: byte and k offsets are a
+// per-lane constant plus uu times a uniform step, and the decode parameters
+// that depend on that position are per-lane constants.
+//
+// Rounding chains.  Each unit's products are summed in a fresh partial (at
+// most 64 terms) before joining the lane's running sum, and the LPR lane sums
+// are combined by a butterfly: every f32 chain has at most
+// 64 + k/(UE*LPR) + log2(LPR) terms.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace qmm {
 
 // ------------------------------------------------------------------ units
-// load(): fetch one unit of one row (row_off = byte offset of the row inside
-// the weight descriptor).  prep(): per-unit scales.  sub(s): weights of
-// sub-unit s (8 weights) plus the k indices e0, e1 of the two runs of 4
-// consecutive weights they are (w[0..3] <-> k e0..e0+3, w[4..7] <-> e1..e1+3).
+// Per format:
+//   UE, S        weights per unit, sub-units of 8 weights
+//   MIN_LPR      smallest lane-group size for which the unit position within
+//                its block is the same for all uu
+//   Lane         per-lane constants: boff (byte offset of unit gl in its row),
+//                e (k index of the unit's first run)
+//   ustep(lpr)   byte offset added per uu
+//   load(), prep(), sub(s, w, f0, f1)
+//                sub-unit s: 8 weights w[0..7]; w[0..3] pair with the 4
+//                activations at k = e + rel0(s), w[4..7] with k = e + rel1(s).
+//                SCALED units return unscaled weights and the factors f0, f1
+//                of the two runs (the factor is common to each run).
+//   prel0(s), prel1(s)
+//                rel0/rel1 in the padded LDS activation layout.
 
 template <int QT> struct GUnit;
 
+struct LaneBase {
+    uint32_t boff;
+    int e;
+};
+
 template <> struct GUnit<QT_F32> {  // 16 weights, 64 bytes
-    static constexpr int UE = 16, S = 2;
+    static constexpr int UE = 16, S = 2, MIN_LPR = 1;
+    static constexpr bool SCALED = false;
+    struct Lane : LaneBase {};
+    __device__ static Lane lane(int gl) { return Lane{{(uint32_t)gl * 64u, gl * 16}}; }
+    __host__ __device__ static uint32_t ustep(int lpr) { return (uint32_t)lpr * 64u; }
+    static constexpr int rel0(int s) { return 8 * s; }
+    static constexpr int rel1(int s) { return 8 * s + 4; }
+    static constexpr int prel0(int s) { return rel0(s); }
+    static constexpr int prel1(int s) { return rel1(s); }
     uint32_t r[16];
-    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int u, int k) {
-        ld_span<16>(wr, row_off + (uint32_t)u * 64u, r);
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t off, int e, int k, const Lane&) {
+        ld_span<16>(wr, off, r);
 #pragma unroll
         for (int i = 0; i < 4; ++i)  // k % 4 == 0: a run of 4 is wholly in or out
-            if (u * 16 + 4 * i >= k) r[4 * i] = r[4 * i + 1] = r[4 * i + 2] = r[4 * i + 3] = 0u;
+            if (e + 4 * i >= k) r[4 * i] = r[4 * i + 1] = r[4 * i + 2] = r[4 * i + 3] = 0u;
     }
-    __device__ __forceinline__ void prep() {}
-    __device__ __forceinline__ void sub(int s, int u, float (&w)[8], int& e0, int& e1) const {
+    __device__ __forceinline__ void prep(const Lane&) {}
+    __device__ __forceinline__ void sub(int s, float (&w)[8], float&, float&) const {
 #pragma unroll
         for (int i = 0; i < 8; ++i) w[i] = __builtin_bit_cast(float, r[8 * s + i]);
-        e0 = u * 16 + 8 * s;
-        e1 = e0 + 4;
     }
 };
 
 template <> struct GUnit<QT_Q4_0> {  // one 18-byte block of 32 weights
-    static constexpr int UE = 32, S = 4;
+    static constexpr int UE = 32, S = 4, MIN_LPR = 1;
+    static constexpr bool SCALED = false;
+    struct Lane : LaneBase {};
+    __device__ static Lane lane(int gl) { return Lane{{(uint32_t)gl * 18u, gl * 32}}; }
+    __host__ __device__ static uint32_t ustep(int lpr) { return (uint32_t)lpr * 18u; }
+    static constexpr int rel0(int s) { return 4 * s; }
+    static constexpr int rel1(int s) { return 16 + 4 * s; }
+    static constexpr int prel0(int s) { return rel0(s); }
+    static constexpr int prel1(int s) { return rel1(s); }
     uint32_t r[5], sh;
     float d, d8;
-    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int u, int) {
-        const uint32_t o = row_off + (uint32_t)u * 18u;
-        sh = o & 3u;
-        ld_span<5>(wr, o, r);
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t off, int, int, const Lane&) {
+        sh = off & 3u;
+        ld_span<5>(wr, off, r);
     }
-    __device__ __forceinline__ void prep() {
+    __device__ __forceinline__ void prep(const Lane&) {
         d = h2f(r[0] >> (8u * sh));
         d8 = -8.0f * d;
     }
-    __device__ __forceinline__ void sub(int s, int u, float (&w)[8], int& e0, int& e1) const {
+    __device__ __forceinline__ void sub(int s, float (&w)[8], float&, float&) const {
         const uint32_t q = shr64(r[s], r[s + 1], sh + 2u);  // qs[4s..4s+3]
+        const uint32_t lo = q & 0x0F0F0F0Fu, hi = (q >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            w[b] = __builtin_fmaf(d, (float)((q >> (8 * b)) & 15u), d8);
-            w[4 + b] = __builtin_fmaf(d, (float)((q >> (8 * b + 4)) & 15u), d8);
+            w[b] = __builtin_fmaf(d, ubyte_f32(lo, b), d8);  // d*(q-8), exact
+            w[4 + b] = __builtin_fmaf(d, ubyte_f32(hi, b), d8);
         }
-        e0 = u * 32 + 4 * s;
-        e1 = e0 + 16;
     }
 };
 
 template <> struct GUnit<QT_Q8_0> {  // one 34-byte block of 32 weights
-    static constexpr int UE = 32, S = 4;
+    static constexpr int UE = 32, S = 4, MIN_LPR = 1;
+    static constexpr bool SCALED = true;  // d is common to the whole block
+    struct Lane : LaneBase {};
+    __device__ static Lane lane(int gl) { return Lane{{(uint32_t)gl * 34u, gl * 32}}; }
+    __host__ __device__ static uint32_t ustep(int lpr) { return (uint32_t)lpr * 34u; }
+    static constexpr int rel0(int s) { return 8 * s; }
+    static constexpr int rel1(int s) { return 8 * s + 4; }
+    static constexpr int prel0(int s) { return rel0(s); }
+    static constexpr int prel1(int s) { return rel1(s); }
     uint32_t r[9], sh;
     float d;
-    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int u, int) {
-        const uint32_t o = row_off + (uint32_t)u * 34u;
-        sh = o & 3u;
-        ld_span<9>(wr, o, r);
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t off, int, int, const Lane&) {
+        sh = off & 3u;
+        ld_span<9>(wr, off, r);
     }
-    __device__ __forceinline__ void prep() { d = h2f(r[0] >> (8u * sh)); }
-    __device__ __forceinline__ void sub(int s, int u, float (&w)[8], int& e0, int& e1) const {
-        const uint32_t qa = shr64(r[2 * s], r[2 * s + 1], sh + 2u);
-        const uint32_t qb = shr64(r[2 * s + 1], r[2 * s + 2], sh + 2u);
+    __device__ __forceinline__ void prep(const Lane&) { d = h2f(r[0] >> (8u * sh)); }
+    __device__ __forceinline__ void sub(int s, float (&w)[8], float& f0, float& f1) const {
+        // int8 q as (q + 128) - 128: both exact in f32
+        const uint32_t qa = shr64(r[2 * s], r[2 * s + 1], sh + 2u) ^ 0x80808080u;
+        const uint32_t qb = shr64(r[2 * s + 1], r[2 * s + 2], sh + 2u) ^ 0x80808080u;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            w[b] = d * (float)(int8_t)(qa >> (8 * b));
-            w[4 + b] = d * (float)(int8_t)(qb >> (8 * b));
+            w[b] = ubyte_f32(qa, b) - 128.0f;
+            w[4 + b] = ubyte_f32(qb, b) - 128.0f;
         }
-        e0 = u * 32 + 8 * s;
-        e1 = e0 + 4;
+        f0 = d;
+        f1 = d;
     }
 };
 
-// Q4_K: 16 bytes of nibbles (32 weights) of one 144-byte superblock, plus the
-// superblock's 16-byte header (d, dmin, 12 bytes of 6-bit scales/mins).
+// Q4_K: 16 bytes of nibbles (32 weights: 16 of sub-block 2c, 16 of 2c+1) of
+// a 144-byte superblock, plus the superblock's 16-byte header.  The lane's
+// nibble-chunk index c8 = gl & 7 is the same for every uu (LPR >= 8).
 template <> struct GUnit<QT_Q4_K> {
-    static constexpr int UE = 32, S = 4;
+    static constexpr int UE = 32, S = 4, MIN_LPR = 8;
+    static constexpr bool SCALED = false;
+    struct Lane : LaneBase {
+        uint32_t qoff;   // byte offset of the lane's 16 nibble bytes in the superblock
+        int lo6;         // c < 2: the (scale, min) pairs are 6-bit fields of sc[j], sc[j+4]
+        uint32_t bsh;    // bit offset of the byte of sub-block j = 2c in its dword
+    };
+    __device__ static Lane lane(int gl) {
+        const int c8 = gl & 7, c = c8 >> 1, hh = c8 & 1;
+        Lane l;
+        l.boff = (uint32_t)(gl >> 3) * 144u;
+        l.e = (gl >> 3) * 256 + 64 * c + 16 * hh;
+        l.qoff = 16u + 16u * (uint32_t)c8;
+        l.lo6 = c < 2;
+        l.bsh = 16u * (uint32_t)(c & 1);
+        return l;
+    }
+    __host__ __device__ static uint32_t ustep(int lpr) { return (uint32_t)(lpr / 8) * 144u; }
+    static constexpr int rel0(int s) { return 4 * s; }
+    static constexpr int rel1(int s) { return 32 + 4 * s; }
+    static constexpr int prel0(int s) { return rel0(s); }
+    static constexpr int prel1(int s) { return rel1(s); }
     u32x4 hdr, qs;
     float D0, M0, D1, M1;
-    int c8;
-    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int u, int) {
-        const uint32_t sb = (uint32_t)u >> 3;
-        c8 = u & 7;
-        const uint32_t o = row_off + sb * 144u;
-        hdr = ld128(wr, o);
-        qs = ld128(wr, o + 16u + 16u * (uint32_t)c8);
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t off, int, int, const Lane& l) {
+        hdr = ld128(wr, off);
+        qs = ld128(wr, off + l.qoff);
     }
-    __device__ __forceinline__ static uint32_t scb(u32x4 h, int i) {  // scale byte i (0..11)
-        const uint32_t v = i < 4 ? h.y : (i < 8 ? h.z : h.w);
-        return (v >> (8 * (i & 3))) & 0xFFu;
-    }
-    __device__ __forceinline__ void prep() {
+    // (scale, min) of sub-blocks j = 2c (field at bit b) and 2c+1 (b + 8):
+    // j < 4: scale = sc[j] & 63, min = sc[j+4] & 63;
+    // j >= 4: scale = (sc[j+4] & 15) | (sc[j-4] >> 6) << 4,
+    //         min   = (sc[j+4] >> 4) | (sc[j]   >> 6) << 4.
+    // sc[0..3] = hdr.y, sc[4..7] = hdr.z, sc[8..11] = hdr.w.
+    __device__ __forceinline__ void prep(const Lane& l) {
         const float d = h2f(hdr.x), dmin = h2f(hdr.x >> 16);
-        const int c = c8 >> 1;
-        uint32_t s0, m0, s1, m1;
-        if (c < 2) {  // pairs j = 2c, 2c+1 < 4
-            s0 = scb(hdr, 2 * c) & 63u;     m0 = scb(hdr, 2 * c + 4) & 63u;
-            s1 = scb(hdr, 2 * c + 1) & 63u; m1 = scb(hdr, 2 * c + 5) & 63u;
-        } else {      // j >= 4: low 4 bits in sc[j+4], high 2 bits in sc[j-4] / sc[j]
-            const int j0 = 2 * c, j1 = 2 * c + 1;
-            s0 = (scb(hdr, j0 + 4) & 15u) | ((scb(hdr, j0 - 4) >> 6) << 4);
-            m0 = (scb(hdr, j0 + 4) >> 4) | ((scb(hdr, j0) >> 6) << 4);
-            s1 = (scb(hdr, j1 + 4) & 15u) | ((scb(hdr, j1 - 4) >> 6) << 4);
-            m1 = (scb(hdr, j1 + 4) >> 4) | ((scb(hdr, j1) >> 6) << 4);
+        const uint32_t sa = l.lo6 ? hdr.y : hdr.w;  // holds the low 4 bits of the scale
+        const uint32_t ma = l.lo6 ? hdr.z : hdr.w;  // holds the low 4 bits of the min
+        const uint32_t mas = l.lo6 ? 0u : 4u;
+        const uint32_t hs = l.lo6 ? 4u : 6u;        // position of the 2 high bits
+        float Dv[2], Mv[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t b = l.bsh + 8u * t;
+            const uint32_t sc = __builtin_amdgcn_ubfe(sa, b, 4) | (__builtin_amdgcn_ubfe(hdr.y, b + hs, 2) << 4);
+            const uint32_t mn = __builtin_amdgcn_ubfe(ma, b + mas, 4) | (__builtin_amdgcn_ubfe(hdr.z, b + hs, 2) << 4);
+            Dv[t] = d * (float)sc;
+            Mv[t] = dmin * (float)mn;
         }
-        D0 = d * (float)s0; M0 = dmin * (float)m0;
-        D1 = d * (float)s1; M1 = dmin * (float)m1;
+        D0 = Dv[0]; M0 = Mv[0]; D1 = Dv[1]; M1 = Mv[1];
     }
-    __device__ __forceinline__ void sub(int s, int u, float (&w)[8], int& e0, int& e1) const {
+    __device__ __forceinline__ void sub(int s, float (&w)[8], float&, float&) const {
         const uint32_t q = s == 0 ? qs.x : (s == 1 ? qs.y : (s == 2 ? qs.z : qs.w));
+        const uint32_t lo = q & 0x0F0F0F0Fu, hi = (q >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            w[b] = __builtin_fmaf(D0, (float)((q >> (8 * b)) & 15u), -M0);
-            w[4 + b] = __builtin_fmaf(D1, (float)((q >> (8 * b + 4)) & 15u), -M1);
+            w[b] = __builtin_fmaf(D0, ubyte_f32(lo, b), -M0);
+            w[4 + b] = __builtin_fmaf(D1, ubyte_f32(hi, b), -M1);
         }
-        const int sb = u >> 3, c = c8 >> 1, hh = c8 & 1;
-        e0 = sb * 256 + 64 * c + 16 * hh + 4 * s;
-        e1 = e0 + 32;
     }
 };
 
-// Q6_K: 64 weights of one 210-byte superblock: half h, l in [l0, l0+16) of
-// the four quarters.  Needs 16 bytes of ql for quarters 0/2, 16 for 1/3, 16
-// bytes of qh, the half's 8 scale bytes and d.
+// Q6_K: 64 weights of a 210-byte superblock: half h, l in [l0, l0+16) of the
+// half's four quarters.  Reads 16 bytes of ql for quarters 0/2, 16 for 1/3,
+// 16 bytes of qh, the 8 scale bytes of the half and d.  (gl & 3 fixes h and
+// l0 for every uu, LPR >= 4.)
 template <> struct GUnit<QT_Q6_K> {
-    static constexpr int UE = 64, S = 8;
-    uint32_t ra[5], rb[5], rh[5], rs[3], rd, sh;
-    int h, l0;
-    float D[4];
-    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int u, int) {
-        const uint32_t sb = (uint32_t)u >> 2;
-        h = (u >> 1) & 1;
-        l0 = 16 * (u & 1);
-        const uint32_t o = row_off + sb * 210u;
-        sh = o & 3u;
-        ld_span<5>(wr, o + 64u * h + l0, ra);
-        ld_span<5>(wr, o + 64u * h + 32u + l0, rb);
-        ld_span<5>(wr, o + 128u + 32u * h + l0, rh);
-        ld_span<3>(wr, o + 192u + 8u * h, rs);
-        rd = ld32(wr, (o + 208u) & ~3u);
+    static constexpr int UE = 64, S = 8, MIN_LPR = 4;
+    static constexpr bool SCALED = true;  // d * scale is common to each 16-run
+    struct Lane : LaneBase {
+        uint32_t oa, ob, oh, os;  // byte offsets (in the superblock) of the four spans
+        uint32_t so;              // bit offset of the half's first used scale byte
+    };
+    __device__ static Lane lane(int gl) {
+        const int h = (gl >> 1) & 1, l0 = 16 * (gl & 1);
+        Lane l;
+        l.boff = (uint32_t)(gl >> 2) * 210u;
+        l.e = (gl >> 2) * 256 + 128 * h + l0;
+        l.oa = 64u * h + l0;
+        l.ob = 64u * h + 32u + l0;
+        l.oh = 128u + 32u * h + l0;
+        l.os = 192u + 8u * h;
+        l.so = 8u * (uint32_t)(l0 >> 4);
+        return l;
     }
-    __device__ __forceinline__ void prep() {
+    __host__ __device__ static uint32_t ustep(int lpr) { return (uint32_t)(lpr / 4) * 210u; }
+    // sub-unit s: quarter g = s/2, 8 weights at l0 + 8*(s&1) of the quarter
+    static constexpr int rel0(int s) { return 32 * (s >> 1) + 8 * (s & 1); }
+    static constexpr int rel1(int s) { return rel0(s) + 4; }
+    static constexpr int prel0(int s) { return rel0(s) + ((s >> 1) >= 2 ? 4 : 0); }
+    static constexpr int prel1(int s) { return rel1(s) + ((s >> 1) >= 2 ? 4 : 0); }
+    uint32_t ra[5], rb[5], rh[5], rs[3], rd, sh;
+    float D[4];
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t off, int, int, const Lane& l) {
+        sh = off & 3u;
+        ld_span<5>(wr, off + l.oa, ra);
+        ld_span<5>(wr, off + l.ob, rb);
+        ld_span<5>(wr, off + l.oh, rh);
+        ld_span<3>(wr, off + l.os, rs);
+        rd = ld32(wr, (off + 208u) & ~3u);
+    }
+    __device__ __forceinline__ void prep(const Lane& l) {
         const float d = h2f(rd >> (8u * sh));
         const uint32_t sc0 = shr64(rs[0], rs[1], sh), sc1 = shr64(rs[1], rs[2], sh);
-        const int add = l0 >> 4;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int i = 2 * g + add;  // scale byte index within the half
-            const uint32_t v = i < 4 ? sc0 : sc1;
-            D[g] = d * (float)(int8_t)(v >> (8 * (i & 3)));
-        }
+        // quarter g uses scale byte 2g + l0/16 of the half
+        D[0] = d * (float)(int8_t)(sc0 >> l.so);
+        D[1] = d * (float)(int8_t)(sc0 >> (l.so + 16u));
+        D[2] = d * (float)(int8_t)(sc1 >> l.so);
+        D[3] = d * (float)(int8_t)(sc1 >> (l.so + 16u));
     }
-    __device__ __forceinline__ void sub(int s, int u, float (&w)[8], int& e0, int& e1) const {
+    __device__ __forceinline__ void sub(int s, float (&w)[8], float& f0, float& f1) const {
         const int g = s >> 1, i8 = s & 1;
         const uint32_t L0 = (g & 1) ? rb[2 * i8] : ra[2 * i8];
         const uint32_t L1 = (g & 1) ? rb[2 * i8 + 1] : ra[2 * i8 + 1];
         const uint32_t L2 = (g & 1) ? rb[2 * i8 + 2] : ra[2 * i8 + 2];
-        const uint32_t l_a = shr64(L0, L1, sh);
-        const uint32_t l_b = shr64(L1, L2, sh);
+        const uint32_t l_a = shr64(L0, L1, sh), l_b = shr64(L1, L2, sh);
         const uint32_t h_a = shr64(rh[2 * i8], rh[2 * i8 + 1], sh);
         const uint32_t h_b = shr64(rh[2 * i8 + 1], rh[2 * i8 + 2], sh);
         const int nsh = g >= 2 ? 4 : 0;
         const uint32_t qa = ((l_a >> nsh) & 0x0F0F0F0Fu) | (((h_a >> (2 * g)) & 0x03030303u) << 4);
         const uint32_t qb = ((l_b >> nsh) & 0x0F0F0F0Fu) | (((h_b >> (2 * g)) & 0x03030303u) << 4);
-        const float Dg = D[g], D32 = -32.0f * D[g];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            w[b] = __builtin_fmaf(Dg, (float)((qa >> (8 * b)) & 0xFFu), D32);
-            w[4 + b] = __builtin_fmaf(Dg, (float)((qb >> (8 * b)) & 0xFFu), D32);
+            w[b] = ubyte_f32(qa, b) - 32.0f;  // q - 32, exact
+            w[4 + b] = ubyte_f32(qb, b) - 32.0f;
         }
-        const int sb = u >> 2;
-        e0 = sb * 256 + 128 * h + 32 * g + l0 + 8 * i8;
-        e1 = e0 + 4;
+        f0 = D[g];
+        f1 = D[g];
     }
 };
 
 // NVFP4: one half (32 weights) of a 36-byte group: the group's scale dword
-// and 16 bytes of E2M1 nibbles.
+// and 16 bytes of E2M1 nibbles.  (gl & 1 fixes the half, LPR >= 2.)
 template <> struct GUnit<QT_NVFP4> {
-    static constexpr int UE = 32, S = 4;
+    static constexpr int UE = 32, S = 4, MIN_LPR = 2;
+    static constexpr bool SCALED = true;  // one E4M3 factor per 16-weight run
+    struct Lane : LaneBase {
+        uint32_t hsh;  // 16 * h: the half's two scale bytes
+        uint32_t qoff;
+    };
+    __device__ static Lane lane(int gl) {
+        const int h = gl & 1;
+        Lane l;
+        l.boff = (uint32_t)(gl >> 1) * 36u;
+        l.e = (gl >> 1) * 64 + 32 * h;
+        l.hsh = 16u * (uint32_t)h;
+        l.qoff = 4u + 16u * (uint32_t)h;
+        return l;
+    }
+    __host__ __device__ static uint32_t ustep(int lpr) { return (uint32_t)(lpr / 2) * 36u; }
+    static constexpr int rel0(int s) { return 4 * s; }
+    static constexpr int rel1(int s) { return 16 + 4 * s; }
+    static constexpr int prel0(int s) { return rel0(s); }
+    static constexpr int prel1(int s) { return rel1(s); }
     uint32_t sd;
     u32x4 qs;
-    int h;
     float s_lo, s_hi;
-    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int u, int) {
-        const uint32_t gi = (uint32_t)u >> 1;
-        h = u & 1;
-        const uint32_t o = row_off + gi * 36u;
-        sd = ld32(wr, o);
-        qs = ld128(wr, o + 4u + 16u * (uint32_t)h);
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t off, int, int, const Lane& l) {
+        sd = ld32(wr, off);
+        qs = ld128(wr, off + l.qoff);
     }
-    __device__ __forceinline__ void prep() {
-        s_lo = e4m3_to_f32((sd >> (16 * h)) & 0xFFu);
-        s_hi = e4m3_to_f32((sd >> (16 * h + 8)) & 0xFFu);
+    __device__ __forceinline__ void prep(const Lane& l) {
+        s_lo = e4m3_to_f32((sd >> l.hsh) & 0xFFu);
+        s_hi = e4m3_to_f32((sd >> (l.hsh + 8u)) & 0xFFu);
     }
-    __device__ __forceinline__ void sub(int s, int u, float (&w)[8], int& e0, int& e1) const {
+    __device__ __forceinline__ void sub(int s, float (&w)[8], float& f0, float& f1) const {
         const uint32_t q = s == 0 ? qs.x : (s == 1 ? qs.y : (s == 2 ? qs.z : qs.w));
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const f32x2 v = e2m1x2_to_f32(q, b);
-            w[b] = v.x * s_lo;
-            w[4 + b] = v.y * s_hi;
+            w[b] = v.x;
+            w[4 + b] = v.y;
         }
-        const int gi = u >> 1;
-        e0 = gi * 64 + 32 * h + 4 * s;
-        e1 = e0 + 16;
+        f0 = s_lo;
+        f1 = s_hi;
     }
 };
 
+// ------------------------------------------------------------------ activations
+// NT activation rows, either staged in LDS (4 floats of padding after every
+// 64 so that the lanes of a wave, which read 16 bytes at unit-strided k
+// offsets, fall on distinct banks) or read from global memory.
+__device__ __forceinline__ int xpad(int e) { return e + ((e >> 6) << 2); }
+__host__ __device__ constexpr int xpad_len(int k) { return k + ((k + 63) / 64) * 4; }
+
+template <int NT>
+struct XLds {
+    const float* s;  // [NT][xpad_len(k)]
+    int ld;
+    struct Base { const float* p[NT]; };
+    __device__ __forceinline__ Base base(int e) const {
+        Base b;
+        const int pe = xpad(e);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) b.p[j] = s + j * ld + pe;
+        return b;
+    }
+    template <int REL, int PREL>
+    __device__ __forceinline__ f32x4 get(const Base& b, int j) const {
+        return *(const f32x4*)(b.p[j] + PREL);
+    }
+};
+
+template <int NT>
+struct XGlobal {
+    rsrc_t xr;
+    uint32_t xoff[NT];
+    struct Base { uint32_t o[NT]; };
+    __device__ __forceinline__ Base base(int e) const {
+        Base b;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) b.o[j] = xoff[j] + 4u * (uint32_t)e;
+        return b;
+    }
+    template <int REL, int PREL>
+    __device__ __forceinline__ f32x4 get(const Base& b, int j) const {
+        return __builtin_bit_cast(f32x4, ld128(xr, b.o[j] + 4u * REL));
+    }
+};
+
+// Stage rows xoff[j] (j < NT) of x (row length k) into LDS in the padded
+// layout.  All threads of the work group take part; ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void stage_x(float* sx, rsrc_t xr, const uint32_t (&xoff)[NT], int k) {
+    const int ld = xpad_len(k);
+    const int per = k >> 2;  // float4 per row
+    for (int i = threadIdx.x; i < NT * per; i += 256) {
+        const int j = i / per, e = (i - j * per) << 2;
+        const f32x4 v = __builtin_bit_cast(f32x4, ld128(xr, xoff[j] + 4u * (uint32_t)e));
+        *(f32x4*)(sx + j * ld + xpad(e)) = v;
+    }
+    __syncthreads();
+}
+
 // ------------------------------------------------------------------ core
 
-template <int QT>
-__device__ __host__ constexpr int UT_elems() { return GUnit<QT>::UE; }
+struct StreamGeom {
+    const uint8_t* w;  // packed rows
+    int64_t m;         // rows
+    int64_t rb;        // bytes per row
+    int k;             // weights per row
+    int lpr_log2;      // lanes per lane group = 1 << lpr_log2
+};
 
-template <int QT, int NT, int R>
-__device__ __forceinline__ void gemv_rows(rsrc_t wr, const uint32_t (&roff)[R], rsrc_t xr,
-                                          const uint32_t (&xoff)[NT], int k, int gl,
-                                          int lpr, float (&acc)[R][NT]) {
-    const int n_units = (k + UT_elems<QT>() - 1) / UT_elems<QT>();
+template <int QT, int NT, int R, typename XS, int S_>
+__device__ __forceinline__ void sub_fma(const GUnit<QT> (&un)[R], const XS& xs,
+                                        const typename XS::Base& xb, int k, int e,
+                                        float (&part)[R][NT]) {
     using UT = GUnit<QT>;
+    float wv[R][8], f0[R], f1[R];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) un[rr].sub(S_, wv[rr], f0[rr], f1[rr]);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        f32x4 xa = xs.template get<UT::rel0(S_), UT::prel0(S_)>(xb, j);
+        f32x4 xb4 = xs.template get<UT::rel1(S_), UT::prel1(S_)>(xb, j);
+        if constexpr (QT == QT_F32) {  // runs past k belong to the next row
+            if (e + UT::rel0(S_) >= k) xa = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (e + UT::rel1(S_) >= k) xb4 = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+            if constexpr (UT::SCALED) {
+                float p0 = wv[rr][0] * xa.x;
+                p0 = __builtin_fmaf(wv[rr][1], xa.y, p0);
+                p0 = __builtin_fmaf(wv[rr][2], xa.z, p0);
+                p0 = __builtin_fmaf(wv[rr][3], xa.w, p0);
+                float p1 = wv[rr][4] * xb4.x;
+                p1 = __builtin_fmaf(wv[rr][5], xb4.y, p1);
+                p1 = __builtin_fmaf(wv[rr][6], xb4.z, p1);
+                p1 = __builtin_fmaf(wv[rr][7], xb4.w, p1);
+                const float p = __builtin_fmaf(f0[rr], p0, part[rr][j]);
+                part[rr][j] = __builtin_fmaf(f1[rr], p1, p);
+            } else {
+                float p = part[rr][j];
+                p = __builtin_fmaf(wv[rr][0], xa.x, p);
+                p = __builtin_fmaf(wv[rr][1], xa.y, p);
+                p = __builtin_fmaf(wv[rr][2], xa.z, p);
+                p = __builtin_fmaf(wv[rr][3], xa.w, p);
+                p = __builtin_fmaf(wv[rr][4], xb4.x, p);
+                p = __builtin_fmaf(wv[rr][5], xb4.y, p);
+                p = __builtin_fmaf(wv[rr][6], xb4.z, p);
+                p = __builtin_fmaf(wv[rr][7], xb4.w, p);
+                part[rr][j] = p;
+            }
+        }
+    }
+}
+
+template <int QT, int NT, int R, typename XS, int S_ = 0>
+__device__ __forceinline__ void sub_all(const GUnit<QT> (&un)[R], const XS& xs,
+                                        const typename XS::Base& xb, int k, int e,
+                                        float (&part)[R][NT]) {
+    if constexpr (S_ < GUnit<QT>::S) {
+        sub_fma<QT, NT, R, XS, S_>(un, xs, xb, k, e, part);
+        sub_all<QT, NT, R, XS, S_ + 1>(un, xs, xb, k, e, part);
+    }
+}
+
+template <int QT, int NT, int R, typename XS>
+__device__ __forceinline__ void compute_item(GUnit<QT> (&un)[R], const typename GUnit<QT>::Lane& ln,
+                                             int e, int k, const XS& xs, float (&acc)[R][NT]) {
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) un[rr].prep(ln);
+    float part[R][NT];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) part[rr][j] = 0.0f;
+    const typename XS::Base xb = xs.base(e);
+    sub_all<QT, NT, R, XS>(un, xs, xb, k, e, part);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[rr][j] += part[rr][j];
+}
+
+// Issue the loads of item (row group rg, unit iteration uu) into un[].
+// The descriptor covers the row group's rows from the 16-byte boundary at or
+// below its first byte (wave-uniform, scalar registers); a lane's offset is
+// its per-lane row/unit constant plus the group's sub-16 remainder and uu
+// times the format's step.
+template <int QT, int R>
+__device__ __forceinline__ void issue_item(GUnit<QT> (&un)[R], const StreamGeom& g, int RG,
+                                           uint32_t lane_row_off, const typename GUnit<QT>::Lane& ln,
+                                           int rg, int uu, int e) {
+    const int64_t row0 = (int64_t)rg * RG;
+    const int64_t byte0 = row0 * g.rb;
+    const int64_t base = byte0 & ~(int64_t)15;
+    const int64_t end = imin64(g.m, row0 + RG) * g.rb;
+    const rsrc_t wr = make_rsrc(g.w + base, (uint32_t)((end - base + 15) & ~(int64_t)15));
+    const uint32_t off0 = lane_row_off + (uint32_t)(byte0 & 15) + ln.boff +
+                          (uint32_t)uu * GUnit<QT>::ustep(1 << g.lpr_log2);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) un[rr].load(wr, off0 + (uint32_t)(rr * g.rb), e, g.k, ln);
+}
+
+// Row groups first_rg, first_rg + rg_stride, ... < n_rg.  A row group is the
+// RG = (64/LPR)*R rows that the wave's lane groups cover at once.  Items are
+// numbered it = 0, 1, ...: row group first_rg + (it / upl) * rg_stride, unit
+// iteration it % upl.  D items of weight loads are kept in flight in a ring
+// of register sets (slot it % D, indexed at compile time); a slot is refilled
+// with item it + D right after item it is consumed.  store(row, j, value) is
+// called by lane gl == 0 of each lane group for every row (rows >= m too).
+template <int QT, int NT, int R, int D, typename XS, typename Store>
+__device__ __forceinline__ void gemv_stream(const StreamGeom& g, int first_rg, int rg_stride,
+                                            int n_rg, const XS& xs, Store store) {
+    using UT = GUnit<QT>;
+    const int lane = threadIdx.x & 63;
+    const int lpr = 1 << g.lpr_log2;
+    const int gl = lane & (lpr - 1), slot = lane >> g.lpr_log2;
+    const int RG = (64 >> g.lpr_log2) * R;
+    const int U = (g.k + UT::UE - 1) / UT::UE;
+    const int upl = (U + lpr - 1) >> g.lpr_log2;
+    if (first_rg >= n_rg) return;
+    const int n_items = (n_rg - first_rg + rg_stride - 1) / rg_stride * upl;
+    const typename UT::Lane ln = UT::lane(gl);
+    const uint32_t lane_row_off = (uint32_t)(slot * R) * (uint32_t)g.rb;
+    const int e_step = lpr * UT::UE;
+
+    float acc[R][NT];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr)
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[rr][j] = 0.0f;
 
-    for (int u = gl; u < n_units; u += lpr) {
-        UT un[R];
+    UT ring[D][R];
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) un[rr].load(wr, roff[rr], u, k);
+    for (int d = 0; d < D; ++d) {
+        if (d < n_items) {
+            const int q = d / upl, uu = d - q * upl;
+            issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q * rg_stride, uu,
+                              ln.e + uu * e_step);
+        }
+    }
+    for (int base = 0; base < n_items; base += D) {
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) un[rr].prep();
-        float part[R][NT];
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-            for (int j = 0; j < NT; ++j) part[rr][j] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < UT::S; ++s) {
-            float wv[R][8];
-            int e0 = 0, e1 = 0;
-#pragma unroll
-            for (int rr = 0; rr < R; ++rr) un[rr].sub(s, u, wv[rr], e0, e1);
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                f32x4 xa = __builtin_bit_cast(f32x4, ld128(xr, xoff[j] + 4u * (uint32_t)e0));
-                f32x4 xb = __builtin_bit_cast(f32x4, ld128(xr, xoff[j] + 4u * (uint32_t)e1));
-                if constexpr (QT == QT_F32) {  // runs past k belong to the next row
-                    if (e0 >= k) xa = f32x4{0.f, 0.f, 0.f, 0.f};
-                    if (e1 >= k) xb = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int d = 0; d < D; ++d) {
+            const int it = base + d;
+            if (it < n_items) {  // wave-uniform
+                const int q = it / upl, uu = it - q * upl;
+                if (gl + lpr * uu < U)
+                    compute_item<QT, NT, R>(ring[d], ln, ln.e + uu * e_step, g.k, xs, acc);
+                const int nx = it + D;
+                if (nx < n_items) {
+                    const int q2 = nx / upl, uu2 = nx - q2 * upl;
+                    issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q2 * rg_stride,
+                                      uu2, ln.e + uu2 * e_step);
                 }
+                if (uu == upl - 1) {  // row group complete: reduce, store, reset
+                    for (int off = lpr >> 1; off > 0; off >>= 1)
 #pragma unroll
-                for (int rr = 0; rr < R; ++rr) {
-                    float p = part[rr][j];
-                    p = __builtin_fmaf(wv[rr][0], xa.x, p);
-                    p = __builtin_fmaf(wv[rr][1], xa.y, p);
-                    p = __builtin_fmaf(wv[rr][2], xa.z, p);
-                    p = __builtin_fmaf(wv[rr][3], xa.w, p);
-                    p = __builtin_fmaf(wv[rr][4], xb.x, p);
-                    p = __builtin_fmaf(wv[rr][5], xb.y, p);
-                    p = __builtin_fmaf(wv[rr][6], xb.z, p);
-                    p = __builtin_fmaf(wv[rr][7], xb.w, p);
-                    part[rr][j] = p;
+                        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                            for (int j = 0; j < NT; ++j) acc[rr][j] += __shfl_xor(acc[rr][j], off, 64);
+                    if (gl == 0) {
+                        const int64_t r0 = (int64_t)(first_rg + q * rg_stride) * RG + slot * R;
+#pragma unroll
+                        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                            for (int j = 0; j < NT; ++j) store(r0 + rr, j, acc[rr][j]);
+                    }
+#pragma unroll
+                    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                        for (int j = 0; j < NT; ++j) acc[rr][j] = 0.0f;
                 }
             }
         }
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-            for (int j = 0; j < NT; ++j) acc[rr][j] += part[rr][j];
-    }
-    for (int off = lpr >> 1; off > 0; off >>= 1) {
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-            for (int j = 0; j < NT; ++j) acc[rr][j] += __shfl_xor(acc[rr][j], off, 64);
     }
 }
 
-// grid: x = row blocks of 4 * (64/LPR) * R rows, y = token groups of NT.
-template <int QT, int NT, int R>
+extern __shared__ __attribute__((aligned(16))) float qmm_dyn_lds[];
+
+// grid: x = work groups (their 4 waves stride over the row groups), y = token
+// groups of NT.  XL: activations staged in LDS (dynamic shared memory of
+// NT * xpad_len(k) floats).
+template <int QT, int NT, int R, int D, bool XL>
 __global__ __launch_bounds__(256) void gemv_kernel(float* __restrict__ dst,
                                                    const uint8_t* __restrict__ w,
                                                    const float* __restrict__ x, int m, int k,
-                                                   int n, int rb, int lpr_log2) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int lpr = 1 << lpr_log2;
-    const int gl = lane & (lpr - 1), slot = lane >> lpr_log2;
-    const int rows_per_wave = (64 >> lpr_log2) * R;
-    const int64_t row0 = (int64_t)blockIdx.x * 4 * rows_per_wave;
-    int64_t base;
-    const rsrc_t wr = row_window(w, row0, 4 * rows_per_wave, m, rb, base);
+                                                   int n, int rb, int lpr_log2, int n_rg) {
+    const int wave = wave_id();
     const int tok0 = blockIdx.y * NT;
     const int ntok = min(NT, n - tok0);
     const rsrc_t xr = make_rsrc(x + (int64_t)tok0 * k, (uint32_t)ntok * (uint32_t)k * 4u);
-    const int64_t myrow0 = row0 + wave * rows_per_wave + slot * R;
-    uint32_t roff[R];
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) roff[rr] = (uint32_t)((myrow0 + rr) * rb - base);
     uint32_t xoff[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) xoff[j] = (uint32_t)j * (uint32_t)k * 4u;
-
-    float acc[R][NT];
-    gemv_rows<QT, NT, R>(wr, roff, xr, xoff, k, gl, lpr, acc);
-    if (gl == 0) {
+    const StreamGeom g{w, m, rb, k, lpr_log2};
+    float* out = dst + (int64_t)tok0 * m;
+    auto store = [&](int64_t row, int j, float v) {
+        if (row < m && j < ntok) out[(int64_t)j * m + row] = v;
+    };
+    if constexpr (XL) {
+        stage_x<NT>(qmm_dyn_lds, xr, xoff, k);
+        const XLds<NT> xs{qmm_dyn_lds, xpad_len(k)};
+        gemv_stream<QT, NT, R, D>(g, blockIdx.x * 4 + wave, gridDim.x * 4, n_rg, xs, store);
+    } else {
+        XGlobal<NT> xs;
+        xs.xr = xr;
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) {
-            const int64_t row = myrow0 + rr;
-            if (row < m) {
-#pragma unroll
-                for (int j = 0; j < NT; ++j)
-                    if (j < ntok) dst[(int64_t)(tok0 + j) * m + row] = acc[rr][j];
-            }
-        }
+        for (int j = 0; j < NT; ++j) xs.xoff[j] = xoff[j];
+        gemv_stream<QT, NT, R, D>(g, blockIdx.x * 4 + wave, gridDim.x * 4, n_rg, xs, store);
     }
 }
 
 // ------------------------------------------------------------------ MoE gate/up
-// grid: x = row blocks of one expert's n_ff rows, y = pair p, z = plane.
-// The work group of the FIRST pair that routes to expert e gathers every pair
-// routed to e and applies e's rows to all their tokens, so each selected
-// expert's rows are read once per call; work groups of later pairs of the same
-// expert exit at once.  The decision uses only expert_ids, so it is the same
-// in every work group.
-constexpr int MOE_MAXP = 64;  // pairs gathered per chunk (more are looped)
+// grid: x = work groups per (pair, plane) (their waves stride over the row
+// groups of one expert's n_ff rows), y = pair p, z = plane.
+// The work groups of the FIRST pair routed to expert e gather every pair
+// routed to e and apply e's rows to all their tokens, so each selected
+// expert's rows are read once per call when it has at most MOE_NT tokens (in
+// chunks of MOE_NT tokens otherwise), with the chunk's activations staged in
+// LDS; the work groups of later pairs of the same expert exit after the
+// check.  The decision depends on expert_ids only.
+constexpr int MOE_CHUNK = 256;  // pairs examined (and gathered) per pass
+constexpr int MOE_NT = 3;       // token rows staged in LDS at a time
 
-template <int QT, int NT, int R>
-__device__ void moe_tokens(float* __restrict__ out, const float* __restrict__ scale, rsrc_t wr,
-                           const uint32_t (&roff)[R], rsrc_t xr, const int* plist,
-                           const int* tlist, int cnt, int in_f, int n_ff, int gl,
-                           int lpr, int64_t myrow0) {
-    for (int c0 = 0; c0 < cnt; c0 += NT) {
-        uint32_t xoff[NT];
+template <int QT, int NT, int R, int D, bool XL>
+__device__ __forceinline__ void moe_tokens(float* __restrict__ out, const float* __restrict__ scale,
+                                           const StreamGeom& g, int n_rg, rsrc_t xr,
+                                           const int* plist, const int* tlist, int c0, int cnt,
+                                           int in_f, int n_ff) {
+    const int wave = wave_id();
+    uint32_t xoff[NT];
+    int pj[NT];
+    float fj[NT];
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-            xoff[j] = (uint32_t)tlist[(c0 + j < cnt) ? c0 + j : c0] * (uint32_t)in_f * 4u;
-        float acc[R][NT];
-        gemv_rows<QT, NT, R>(wr, roff, xr, xoff, in_f, gl, lpr, acc);
-        if (gl == 0) {
+    for (int j = 0; j < NT; ++j) {
+        const int c = (c0 + j < cnt) ? c0 + j : c0;  // absent slots repeat a real token
+        xoff[j] = (uint32_t)tlist[c] * (uint32_t)in_f * 4u;
+        pj[j] = (c0 + j < cnt) ? plist[c] : -1;
+        fj[j] = scale[plist[c]];
+    }
+    auto store = [&](int64_t row, int j, float v) {
+        if (row < n_ff && pj[j] >= 0) out[(int64_t)pj[j] * n_ff + row] = fj[j] * v;
+    };
+    if constexpr (XL) {
+        __syncthreads();  // the previous chunk's waves are done with the staged x
+        stage_x<NT>(qmm_dyn_lds, xr, xoff, in_f);
+        const XLds<NT> xs{qmm_dyn_lds, xpad_len(in_f)};
+        gemv_stream<QT, NT, R, D>(g, blockIdx.x * 4 + wave, gridDim.x * 4, n_rg, xs, store);
+    } else {
+        XGlobal<NT> xs;
+        xs.xr = xr;
 #pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                if (c0 + j < cnt) {
-                    const int p = plist[c0 + j];
-                    const float f = scale[p];
-#pragma unroll
-                    for (int rr = 0; rr < R; ++rr) {
-                        const int64_t row = myrow0 + rr;
-                        if (row < n_ff) out[(int64_t)p * n_ff + row] = f * acc[rr][j];
-                    }
+        for (int j = 0; j < NT; ++j) xs.xoff[j] = xoff[j];
+        gemv_stream<QT, NT, R, D>(g, blockIdx.x * 4 + wave, gridDim.x * 4, n_rg, xs, store);
+    }
+}
+
+template <int QT, int R, int D>
+__global__ __launch_bounds__(256) void moe_gateup_kernel(
+    float* __restrict__ gate_out, float* __restrict__ up_out, const uint8_t* __restrict__ w_gate,
+    const uint8_t* __restrict__ w_up, const int* __restrict__ ids, const float* __restrict__ pscale,
+    const float* __restrict__ x, int t, int n_used, int n_expert, int in_f, int n_ff, int rb,
+    int lpr_log2, int n_rg, int xl) {
+    __shared__ int plist[MOE_CHUNK];
+    __shared__ int tlist[MOE_CHUNK];
+    __shared__ int wcnt[4];
+    __shared__ int s_seen;
+    const int n_pairs = t * n_used;
+    const int p = blockIdx.y, plane = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int e = uniform_i32(ids[p]);
+    float* out = plane == 0 ? gate_out : up_out;
+    const float* scale = pscale + (int64_t)plane * n_pairs;
+
+    // Is p the first pair routed to e?
+    if (tid == 0) s_seen = 0;
+    __syncthreads();
+    for (int q0 = 0; q0 < p; q0 += MOE_CHUNK) {
+        const int q = q0 + tid;
+        if (q < p && ids[q] == e) s_seen = 1;
+    }
+    __syncthreads();
+    if (s_seen) return;
+
+    const int RG = (64 >> lpr_log2) * R;
+    if (e < 0 || e >= n_expert) {  // invalid id: poison every pair that carries it
+        for (int q = p; q < n_pairs; ++q) {
+            if (ids[q] != e) continue;
+            for (int rg = blockIdx.x; rg < n_rg; rg += gridDim.x)
+                for (int r = tid; r < RG; r += 256) {
+                    const int64_t row = (int64_t)rg * RG + r;
+                    if (row < n_ff) out[(int64_t)q * n_ff + row] = __builtin_nanf("");
                 }
+        }
+        return;
+    }
+
+    const StreamGeom g{(plane == 0 ? w_gate : w_up) + (int64_t)e * n_ff * rb, n_ff, rb, in_f,
+                       lpr_log2};
+    const rsrc_t xr = make_rsrc(x, (uint32_t)t * (uint32_t)in_f * 4u);
+    for (int q0 = p; q0 < n_pairs; q0 += MOE_CHUNK) {
+        // gather the pairs of this chunk routed to e, in pair order
+        const int q = q0 + tid;
+        const bool hit = q < n_pairs && ids[q] == e;
+        const uint64_t bal = __ballot(hit);
+        const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        __syncthreads();
+        if (lane == 0) wcnt[wave] = __builtin_popcountll(bal);
+        __syncthreads();
+        int off = 0;
+        for (int wv = 0; wv < wave; ++wv) off += wcnt[wv];
+        if (hit) {
+            plist[off + before] = q;
+            tlist[off + before] = q / n_used;
+        }
+        const int cnt = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+        __syncthreads();
+        for (int c0 = 0; c0 < cnt; c0 += MOE_NT) {
+            const int left = cnt - c0;
+            if (xl) {
+                if (left == 1)
+                    moe_tokens<QT, 1, R, D, true>(out, scale, g, n_rg, xr, plist, tlist, c0, cnt, in_f, n_ff);
+                else if (left == 2)
+                    moe_tokens<QT, 2, R, D, true>(out, scale, g, n_rg, xr, plist, tlist, c0, cnt, in_f, n_ff);
+                else
+                    moe_tokens<QT, 3, R, D, true>(out, scale, g, n_rg, xr, plist, tlist, c0, cnt, in_f, n_ff);
+            } else {
+                moe_tokens<QT, MOE_NT, R, 2, false>(out, scale, g, n_rg, xr, plist, tlist, c0, cnt, in_f, n_ff);
             }
         }
     }
 }
 
-template <int QT, int R>
-__global__ __launch_bounds__(256) void moe_gateup_kernel(
-    float* __restrict__ gate_out, float* __restrict__ up_out, const uint8_t* __restrict__ w_gate,
-    const uint8_t* __restrict__ w_up, const int* __restrict__ ids, const float* __restrict__ pscale,
-    const float* __restrict__ x, int t, int n_used, int n_expert, int in_f, int n_ff, int rb,
-    int lpr_log2) {
-    __shared__ int plist[MOE_MAXP];
-    __shared__ int tlist[MOE_MAXP];
-    __shared__ int s_cnt, s_first;
-    const int n_pairs = t * n_used;
-    const int p = blockIdx.y, plane = blockIdx.z;
-    const int e = ids[p];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int lpr = 1 << lpr_log2;
-    const int gl = lane & (lpr - 1), slot = lane >> lpr_log2;
-    const int rows_per_wave = (64 >> lpr_log2) * R;
-    const int64_t row0 = (int64_t)blockIdx.x * 4 * rows_per_wave;
-    const int64_t myrow0 = row0 + wave * rows_per_wave + slot * R;
-    float* out = plane == 0 ? gate_out : up_out;
-    const float* scale = pscale + (int64_t)plane * n_pairs;
-
-    if (threadIdx.x == 0) {
-        int first = 1;
-        for (int q = 0; q < p; ++q)
-            if (ids[q] == e) { first = 0; break; }
-        s_first = first;
-    }
-    __syncthreads();
-    if (!s_first) return;
-
-    if (e < 0 || e >= n_expert) {  // invalid id: poison every pair that carries it
-        for (int q = p; q < n_pairs; ++q) {
-            if (ids[q] != e) continue;
-            for (int64_t r = myrow0; r < myrow0 + R; ++r)
-                if (gl == 0 && r < n_ff && r < row0 + 4 * rows_per_wave)
-                    out[(int64_t)q * n_ff + r] = __builtin_nanf("");
-        }
-        return;
-    }
-
-    const uint8_t* wp = (plane == 0 ? w_gate : w_up) + (int64_t)e * n_ff * rb;
-    int64_t base;
-    const rsrc_t wr = row_window(wp, row0, 4 * rows_per_wave, n_ff, rb, base);
-    const rsrc_t xr = make_rsrc(x, (uint32_t)t * (uint32_t)in_f * 4u);
-    uint32_t roff[R];
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) roff[rr] = (uint32_t)((myrow0 + rr) * rb - base);
-    for (int q0 = p; q0 < n_pairs;) {
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            int cnt = 0, q = q0;
-            for (; q < n_pairs && cnt < MOE_MAXP; ++q)
-                if (ids[q] == e) { plist[cnt] = q; tlist[cnt] = q / n_used; ++cnt; }
-            s_cnt = cnt;
-            s_first = q;  // resume point
-        }
-        __syncthreads();
-        const int cnt = s_cnt;
-        q0 = s_first;
-        if (cnt == 1)
-            moe_tokens<QT, 1, R>(out, scale, wr, roff, xr, plist, tlist, cnt, in_f, n_ff, gl, lpr, myrow0);
-        else if (cnt == 2)
-            moe_tokens<QT, 2, R>(out, scale, wr, roff, xr, plist, tlist, cnt, in_f, n_ff, gl, lpr, myrow0);
-        else if (cnt > 0)
-            moe_tokens<QT, 4, R>(out, scale, wr, roff, xr, plist, tlist, cnt, in_f, n_ff, gl, lpr, myrow0);
-    }
-}
-
 // ------------------------------------------------------------------ load-only twin
-// Same grid, descriptors and unit loads as gemv_kernel<QT, 1, R>; the decode
-// and FMAs are replaced by an XOR of the raw words.
+// The GEMV's streaming loop with the decode and FMAs replaced by an XOR of
+// the raw words: the same descriptors, unit loads and item order.
 template <typename UT>
 __device__ __forceinline__ uint32_t raw_xor(const UT& un);
 
@@ -471,48 +734,70 @@ template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_NVFP4>& u
     return u.sd ^ u.qs.x ^ u.qs.y ^ u.qs.z ^ u.qs.w;
 }
 
-template <int QT, int R>
+template <int QT, int R, int D>
 __global__ __launch_bounds__(256) void loadonly_kernel(uint32_t* __restrict__ sink,
                                                        const uint8_t* __restrict__ w, int m, int k,
-                                                       int rb, int lpr_log2) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+                                                       int rb, int lpr_log2, int n_rg) {
+    using UT = GUnit<QT>;
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const StreamGeom g{w, m, rb, k, lpr_log2};
     const int lpr = 1 << lpr_log2;
     const int gl = lane & (lpr - 1), slot = lane >> lpr_log2;
-    const int rows_per_wave = (64 >> lpr_log2) * R;
-    const int64_t row0 = (int64_t)blockIdx.x * 4 * rows_per_wave;
-    int64_t base;
-    const rsrc_t wr = row_window(w, row0, 4 * rows_per_wave, m, rb, base);
-    const int64_t myrow0 = row0 + wave * rows_per_wave + slot * R;
-    uint32_t roff[R], acc[R];
+    const int RG = (64 >> lpr_log2) * R;
+    const int U = (k + UT::UE - 1) / UT::UE;
+    const int upl = (U + lpr - 1) >> lpr_log2;
+    const int first_rg = blockIdx.x * 4 + wave, rg_stride = gridDim.x * 4;
+    if (first_rg >= n_rg) return;
+    const int n_items = (n_rg - first_rg + rg_stride - 1) / rg_stride * upl;
+    const typename UT::Lane ln = UT::lane(gl);
+    const uint32_t lane_row_off = (uint32_t)(slot * R) * (uint32_t)rb;
+    const int e_step = lpr * UT::UE;
+    uint32_t acc[R];
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-        roff[rr] = (uint32_t)((myrow0 + rr) * rb - base);
-        acc[rr] = 0;
+    for (int rr = 0; rr < R; ++rr) acc[rr] = 0;
+    UT ring[D][R];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        if (d < n_items) {
+            const int q = d / upl, uu = d - q * upl;
+            issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q * rg_stride, uu,
+                              ln.e + uu * e_step);
+        }
     }
-    const int n_units = (k + GUnit<QT>::UE - 1) / GUnit<QT>::UE;
-    for (int u = gl; u < n_units; u += lpr) {
-        GUnit<QT> un[R];
+    for (int base = 0; base < n_items; base += D) {
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) un[rr].load(wr, roff[rr], u, k);
+        for (int d = 0; d < D; ++d) {
+            const int it = base + d;
+            if (it < n_items) {
+                const int q = it / upl, uu = it - q * upl;
+                if (gl + lpr * uu < U)
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) acc[rr] ^= raw_xor(un[rr]);
+                    for (int rr = 0; rr < R; ++rr) acc[rr] ^= raw_xor(ring[d][rr]);
+                const int nx = it + D;
+                if (nx < n_items) {
+                    const int q2 = nx / upl, uu2 = nx - q2 * upl;
+                    issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q2 * rg_stride,
+                                      uu2, ln.e + uu2 * e_step);
+                }
+                if (uu == upl - 1) {
+                    for (int off = lpr >> 1; off > 0; off >>= 1)
+#pragma unroll
+                        for (int rr = 0; rr < R; ++rr) acc[rr] ^= __shfl_xor(acc[rr], off, 64);
+                    if (gl == 0)
+#pragma unroll
+                        for (int rr = 0; rr < R; ++rr) {
+                            const int64_t row = (int64_t)(first_rg + q * rg_stride) * RG + slot * R + rr;
+                            if (row < m) sink[row] = acc[rr];
+                        }
+#pragma unroll
+                    for (int rr = 0; rr < R; ++rr) acc[rr] = 0;
+                }
+            }
+        }
     }
-    for (int off = lpr >> 1; off > 0; off >>= 1)
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr) acc[rr] ^= __shfl_xor(acc[rr], off, 64);
-    if (gl == 0)
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr)
-            if (myrow0 + rr < m) sink[myrow0 + rr] = acc[rr];
 }
 
 // ------------------------------------------------------------------ launchers
-
-static int lpr_log2_for(int64_t n_units) {
-    int l = 0;
-    while (l < 6 && (int64_t(2) << l) <= n_units) ++l;
-    return l;  // largest power of two <= min(n_units, 64)
-}
 
 int gemv_unit_elems(int qt) {
     switch (qt) {
@@ -526,117 +811,154 @@ int gemv_unit_elems(int qt) {
     return 0;
 }
 
-// Rows per work group for a given R (host mirror of the kernels' mapping).
-static int64_t rows_per_wg(int lpr_log2, int R) { return 4 * (64 >> lpr_log2) * R; }
-
-static int pick_R(int64_t m, int lpr_log2, int64_t groups_y) {
-    for (int R : {4, 2}) {
-        const int64_t wgs = (m + rows_per_wg(lpr_log2, R) - 1) / rows_per_wg(lpr_log2, R) * groups_y;
-        if (wgs >= 1024) return R;
+static int min_lpr(int qt) {
+    switch (qt) {
+        case QT_Q4_K: return GUnit<QT_Q4_K>::MIN_LPR;
+        case QT_Q6_K: return GUnit<QT_Q6_K>::MIN_LPR;
+        case QT_NVFP4: return GUnit<QT_NVFP4>::MIN_LPR;
     }
     return 1;
 }
 
+// log2 of the lane-group size: the largest power of two <= min(units, 64),
+// and at least the format's MIN_LPR (a row then leaves lanes of its group
+// idle rather than breaking the per-lane constant unit position).
+static int lpr_for(int qt, int64_t k) {
+    const int ue = gemv_unit_elems(qt);
+    const int64_t units = (k + ue - 1) / ue;
+    int l = 0;
+    while (l < 6 && (int64_t(2) << l) <= units) ++l;
+    while ((1 << l) < min_lpr(qt)) ++l;
+    return l;
+}
+
+// Row-group size in rows for R rows per lane group.
+static int64_t rg_rows(int lpr_log2, int R) { return (int64_t)(64 >> lpr_log2) * R; }
+
 int64_t gemv_max_window_bytes(int qt, int64_t k, int64_t rb) {
-    const int l = lpr_log2_for((k + gemv_unit_elems(qt) - 1) / gemv_unit_elems(qt));
-    return rows_per_wg(l, 4) * rb + 16;
+    return rg_rows(lpr_for(qt, k), 2) * rb + 16;
+}
+
+// Work groups for a stream of n_rg row groups shared by `sets` independent
+// streams: about num_cu * wg_per_cu work groups in total, never more than one
+// wave per row group.
+static unsigned stream_grid(int64_t n_rg, int64_t sets, const GemvTuning& tune) {
+    int64_t target = ((int64_t)tune.num_cu * tune.wg_per_cu + sets - 1) / (sets > 0 ? sets : 1);
+    if (target < 1) target = 1;
+    const int64_t need = (n_rg + 3) / 4;
+    return (unsigned)(need < target ? need : target);
+}
+
+// Activations are staged in LDS when NT rows of them fit this budget.
+constexpr int64_t XLDS_MAX_BYTES = 64 * 1024;
+
+// (R, D) variants compiled: NT <= 2: (1,4) (1,8) (2,2) (2,4); NT >= 4: (1,2) (1,4) (2,2).
+template <int NT, typename F>
+static void with_rd(const GemvTuning& t, F&& f) {
+    if constexpr (NT <= 2) {
+        if (t.rows >= 2) {
+            if (t.depth >= 4) f(std::integral_constant<int, 2>{}, std::integral_constant<int, 4>{});
+            else f(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
+        } else {
+            if (t.depth >= 8) f(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{});
+            else f(std::integral_constant<int, 1>{}, std::integral_constant<int, 4>{});
+        }
+    } else {
+        if (t.rows >= 2) f(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
+        else if (t.depth >= 4) f(std::integral_constant<int, 1>{}, std::integral_constant<int, 4>{});
+        else f(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+    }
 }
 
 template <int QT, int NT>
 static void launch_gemv_nt(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k,
-                           int64_t n, int64_t rb, hipStream_t st) {
-    const int l = lpr_log2_for((k + GUnit<QT>::UE - 1) / GUnit<QT>::UE);
-    const int64_t gy = (n + NT - 1) / NT;
-    const int R = pick_R(m, l, gy);
-    const dim3 grid((unsigned)((m + rows_per_wg(l, R) - 1) / rows_per_wg(l, R)), (unsigned)gy);
-    if (R == 4)
-        gemv_kernel<QT, NT, 4><<<grid, 256, 0, st>>>(dst, w, x, (int)m, (int)k, (int)n, (int)rb, l);
-    else if (R == 2)
-        gemv_kernel<QT, NT, 2><<<grid, 256, 0, st>>>(dst, w, x, (int)m, (int)k, (int)n, (int)rb, l);
-    else
-        gemv_kernel<QT, NT, 1><<<grid, 256, 0, st>>>(dst, w, x, (int)m, (int)k, (int)n, (int)rb, l);
+                           int64_t n, int64_t rb, const GemvTuning& tune, hipStream_t st) {
+    with_rd<NT>(tune, [&](auto Rc, auto Dc) {
+        constexpr int R = decltype(Rc)::value, D = decltype(Dc)::value;
+        const int l = lpr_for(QT, k);
+        const int64_t n_rg = (m + rg_rows(l, R) - 1) / rg_rows(l, R);
+        const int64_t gy = (n + NT - 1) / NT;
+        const dim3 grid(stream_grid(n_rg, gy, tune), (unsigned)gy);
+        const int64_t lds = (int64_t)NT * xpad_len((int)k) * 4;
+        if (lds <= XLDS_MAX_BYTES)
+            gemv_kernel<QT, NT, R, D, true><<<grid, 256, (size_t)lds, st>>>(
+                dst, w, x, (int)m, (int)k, (int)n, (int)rb, l, (int)n_rg);
+        else
+            gemv_kernel<QT, NT, R, D, false><<<grid, 256, 0, st>>>(
+                dst, w, x, (int)m, (int)k, (int)n, (int)rb, l, (int)n_rg);
+    });
 }
 
 template <int QT>
 static void launch_gemv_qt(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k,
-                           int64_t n, int64_t rb, hipStream_t st) {
-    if (n == 1) launch_gemv_nt<QT, 1>(dst, w, x, m, k, n, rb, st);
-    else if (n == 2) launch_gemv_nt<QT, 2>(dst, w, x, m, k, n, rb, st);
-    else if (n <= 4) launch_gemv_nt<QT, 4>(dst, w, x, m, k, n, rb, st);
-    else launch_gemv_nt<QT, 8>(dst, w, x, m, k, n, rb, st);
+                           int64_t n, int64_t rb, const GemvTuning& tune, hipStream_t st) {
+    if (n == 1) launch_gemv_nt<QT, 1>(dst, w, x, m, k, n, rb, tune, st);
+    else if (n == 2) launch_gemv_nt<QT, 2>(dst, w, x, m, k, n, rb, tune, st);
+    else if (n <= 4) launch_gemv_nt<QT, 4>(dst, w, x, m, k, n, rb, tune, st);
+    else launch_gemv_nt<QT, 8>(dst, w, x, m, k, n, rb, tune, st);
 }
 
-void launch_gemv(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
-                 int qt, int64_t rb, hipStream_t st) {
-    const uint8_t* wb = (const uint8_t*)w;
-    switch (qt) {
-        case QT_F32: launch_gemv_qt<QT_F32>(dst, wb, x, m, k, n, rb, st); break;
-        case QT_Q4_0: launch_gemv_qt<QT_Q4_0>(dst, wb, x, m, k, n, rb, st); break;
-        case QT_Q8_0: launch_gemv_qt<QT_Q8_0>(dst, wb, x, m, k, n, rb, st); break;
-        case QT_Q4_K: launch_gemv_qt<QT_Q4_K>(dst, wb, x, m, k, n, rb, st); break;
-        case QT_Q6_K: launch_gemv_qt<QT_Q6_K>(dst, wb, x, m, k, n, rb, st); break;
-        case QT_NVFP4: launch_gemv_qt<QT_NVFP4>(dst, wb, x, m, k, n, rb, st); break;
+#define QMM_QT_SWITCH(qt, CALL)                                     \
+    switch (qt) {                                                   \
+        case QT_F32: { constexpr int Q = QT_F32; CALL; break; }     \
+        case QT_Q4_0: { constexpr int Q = QT_Q4_0; CALL; break; }   \
+        case QT_Q8_0: { constexpr int Q = QT_Q8_0; CALL; break; }   \
+        case QT_Q4_K: { constexpr int Q = QT_Q4_K; CALL; break; }   \
+        case QT_Q6_K: { constexpr int Q = QT_Q6_K; CALL; break; }   \
+        case QT_NVFP4: { constexpr int Q = QT_NVFP4; CALL; break; } \
     }
+
+void launch_gemv(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
+                 int qt, int64_t rb, const GemvTuning& tune, hipStream_t st) {
+    const uint8_t* wb = (const uint8_t*)w;
+    QMM_QT_SWITCH(qt, (launch_gemv_qt<Q>(dst, wb, x, m, k, n, rb, tune, st)))
 }
 
 template <int QT>
 static void launch_moe_qt(float* g, float* u, const uint8_t* wg, const uint8_t* wu, const int* ids,
                           const float* sc, const float* x, int64_t t, int64_t n_used,
                           int64_t n_expert, int64_t in_f, int64_t n_ff, int64_t rb,
-                          hipStream_t st) {
-    const int l = lpr_log2_for(in_f / GUnit<QT>::UE);
-    const int64_t n_pairs = t * n_used;
-    const int R = pick_R(n_ff, l, n_pairs * 2);
-    const dim3 grid((unsigned)((n_ff + rows_per_wg(l, R) - 1) / rows_per_wg(l, R)),
-                    (unsigned)n_pairs, 2);
-    if (R == 4)
-        moe_gateup_kernel<QT, 4><<<grid, 256, 0, st>>>(g, u, wg, wu, ids, sc, x, (int)t, (int)n_used,
-                                                       (int)n_expert, (int)in_f, (int)n_ff, (int)rb, l);
-    else if (R == 2)
-        moe_gateup_kernel<QT, 2><<<grid, 256, 0, st>>>(g, u, wg, wu, ids, sc, x, (int)t, (int)n_used,
-                                                       (int)n_expert, (int)in_f, (int)n_ff, (int)rb, l);
-    else
-        moe_gateup_kernel<QT, 1><<<grid, 256, 0, st>>>(g, u, wg, wu, ids, sc, x, (int)t, (int)n_used,
-                                                       (int)n_expert, (int)in_f, (int)n_ff, (int)rb, l);
+                          const GemvTuning& tune, hipStream_t st) {
+    with_rd<1>(tune, [&](auto Rc, auto Dc) {
+        constexpr int R = decltype(Rc)::value, D = decltype(Dc)::value;
+        const int l = lpr_for(QT, in_f);
+        const int64_t n_pairs = t * n_used;
+        const int64_t n_rg = (n_ff + rg_rows(l, R) - 1) / rg_rows(l, R);
+        // at most one set of work groups per distinct expert and plane is active
+        const int64_t active = 2 * (n_pairs < n_expert ? n_pairs : n_expert);
+        const dim3 grid(stream_grid(n_rg, active, tune), (unsigned)n_pairs, 2);
+        const int64_t lds = (int64_t)MOE_NT * xpad_len((int)in_f) * 4;
+        const int xl = lds <= XLDS_MAX_BYTES;
+        moe_gateup_kernel<QT, R, D><<<grid, 256, (size_t)(xl ? lds : 0), st>>>(
+            g, u, wg, wu, ids, sc, x, (int)t, (int)n_used, (int)n_expert, (int)in_f, (int)n_ff,
+            (int)rb, l, (int)n_rg, xl);
+    });
 }
 
 void launch_moe(float* g, float* u, const void* wg, const void* wu, const int* ids, const float* sc,
                 const float* x, int64_t t, int64_t n_used, int64_t n_expert, int64_t in_f,
-                int64_t n_ff, int qt, int64_t rb, hipStream_t st) {
+                int64_t n_ff, int qt, int64_t rb, const GemvTuning& tune, hipStream_t st) {
     const uint8_t* a = (const uint8_t*)wg;
     const uint8_t* b = (const uint8_t*)wu;
-    switch (qt) {
-        case QT_F32: launch_moe_qt<QT_F32>(g, u, a, b, ids, sc, x, t, n_used, n_expert, in_f, n_ff, rb, st); break;
-        case QT_Q4_0: launch_moe_qt<QT_Q4_0>(g, u, a, b, ids, sc, x, t, n_used, n_expert, in_f, n_ff, rb, st); break;
-        case QT_Q8_0: launch_moe_qt<QT_Q8_0>(g, u, a, b, ids, sc, x, t, n_used, n_expert, in_f, n_ff, rb, st); break;
-        case QT_Q4_K: launch_moe_qt<QT_Q4_K>(g, u, a, b, ids, sc, x, t, n_used, n_expert, in_f, n_ff, rb, st); break;
-        case QT_Q6_K: launch_moe_qt<QT_Q6_K>(g, u, a, b, ids, sc, x, t, n_used, n_expert, in_f, n_ff, rb, st); break;
-        case QT_NVFP4: launch_moe_qt<QT_NVFP4>(g, u, a, b, ids, sc, x, t, n_used, n_expert, in_f, n_ff, rb, st); break;
-    }
+    QMM_QT_SWITCH(qt, (launch_moe_qt<Q>(g, u, a, b, ids, sc, x, t, n_used, n_expert, in_f, n_ff, rb, tune, st)))
 }
 
 template <int QT>
 static void launch_lo_qt(uint32_t* sink, const uint8_t* w, int64_t m, int64_t k, int64_t rb,
-                         hipStream_t st) {
-    const int l = lpr_log2_for((k + GUnit<QT>::UE - 1) / GUnit<QT>::UE);
-    const int R = pick_R(m, l, 1);
-    const dim3 grid((unsigned)((m + rows_per_wg(l, R) - 1) / rows_per_wg(l, R)));
-    if (R == 4) loadonly_kernel<QT, 4><<<grid, 256, 0, st>>>(sink, w, (int)m, (int)k, (int)rb, l);
-    else if (R == 2) loadonly_kernel<QT, 2><<<grid, 256, 0, st>>>(sink, w, (int)m, (int)k, (int)rb, l);
-    else loadonly_kernel<QT, 1><<<grid, 256, 0, st>>>(sink, w, (int)m, (int)k, (int)rb, l);
+                         const GemvTuning& tune, hipStream_t st) {
+    with_rd<1>(tune, [&](auto Rc, auto Dc) {
+        constexpr int R = decltype(Rc)::value, D = decltype(Dc)::value;
+        const int l = lpr_for(QT, k);
+        const int64_t n_rg = (m + rg_rows(l, R) - 1) / rg_rows(l, R);
+        loadonly_kernel<QT, R, D><<<dim3(stream_grid(n_rg, 1, tune)), 256, 0, st>>>(
+            sink, w, (int)m, (int)k, (int)rb, l, (int)n_rg);
+    });
 }
 
 void launch_loadonly(uint32_t* sink, const void* w, int64_t m, int64_t k, int qt, int64_t rb,
-                     hipStream_t st) {
+                     const GemvTuning& tune, hipStream_t st) {
     const uint8_t* wb = (const uint8_t*)w;
-    switch (qt) {
-        case QT_F32: launch_lo_qt<QT_F32>(sink, wb, m, k, rb, st); break;
-        case QT_Q4_0: launch_lo_qt<QT_Q4_0>(sink, wb, m, k, rb, st); break;
-        case QT_Q8_0: launch_lo_qt<QT_Q8_0>(sink, wb, m, k, rb, st); break;
-        case QT_Q4_K: launch_lo_qt<QT_Q4_K>(sink, wb, m, k, rb, st); break;
-        case QT_Q6_K: launch_lo_qt<QT_Q6_K>(sink, wb, m, k, rb, st); break;
-        case QT_NVFP4: launch_lo_qt<QT_NVFP4>(sink, wb, m, k, rb, st); break;
-    }
+    QMM_QT_SWITCH(qt, (launch_lo_qt<Q>(sink, wb, m, k, rb, tune, st)))
 }
 
 }  // namespace qmm

@@ -52,6 +52,69 @@ void parse_env() {
         g_gemv_max_n = (int)val;
 }
 
+// Strict integer from the environment: absent -> dflt; set but not an
+// integer in [lo, hi] -> -1 (the caller reports QMM_ERR_RANGE).
+int env_int(const char* name, int dflt, int lo, int hi) {
+    const char* v = std::getenv(name);
+    if (!v) return dflt;
+    char* end = nullptr;
+    errno = 0;
+    const long val = std::strtol(v, &end, 10);
+    while (end && *end == ' ') ++end;
+    if (errno != 0 || end == v || (end && *end != '\0') || val < lo || val > hi) return -1;
+    return (int)val;
+}
+
+struct TuneState {
+    int wg_per_cu = 4;
+    int rows = 1;
+    int depth = 8;
+    bool bad = false;
+};
+TuneState g_tune;
+std::once_flag g_tune_once;
+std::mutex g_cu_mu;
+int g_cu[64] = {0};
+
+void parse_tune() {
+    const int w = env_int("QMM_GEMV_WG_PER_CU", g_tune.wg_per_cu, 1, 64);
+    const int r = env_int("QMM_GEMV_ROWS", g_tune.rows, 1, 2);
+    const int d = env_int("QMM_GEMV_DEPTH", g_tune.depth, 2, 8);
+    if (w < 0 || r < 0 || d < 0 || (d & (d - 1)) != 0) {
+        g_tune.bad = true;
+        return;
+    }
+    g_tune.wg_per_cu = w;
+    g_tune.rows = r;
+    g_tune.depth = d;
+}
+
+// Tuning for the current device; false if a tuning variable is malformed.
+bool gemv_tuning(qmm::GemvTuning* t) {
+    std::call_once(g_tune_once, parse_tune);
+    if (g_tune.bad) return false;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    int cu = 0;
+    {
+        std::lock_guard<std::mutex> lk(g_cu_mu);
+        if (dev >= 0 && dev < 64) cu = g_cu[dev];
+    }
+    if (cu <= 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cu = v;
+        std::lock_guard<std::mutex> lk(g_cu_mu);
+        if (dev >= 0 && dev < 64) g_cu[dev] = cu;
+    }
+    t->num_cu = cu;
+    t->wg_per_cu = g_tune.wg_per_cu;
+    t->rows = g_tune.rows;
+    t->depth = g_tune.depth;
+    return true;
+}
+
 int launch_status() {
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
@@ -129,7 +192,9 @@ int qmm_gemm_path(float* dst, const void* w, const float* x, int64_t m, int64_t 
         // one work group addresses at most this window of w, and 8 token rows of x
         if (qmm::gemv_max_window_bytes(qtype, k, rb) >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
         if (8 * k * 4 >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
-        qmm::launch_gemv(dst, w, x, m, k, n, qtype, rb, stream);
+        qmm::GemvTuning tune;
+        if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
+        qmm::launch_gemv(dst, w, x, m, k, n, qtype, rb, tune, stream);
         return launch_status();
     }
     if (path == QMM_PATH_MFMA) {
@@ -169,8 +234,10 @@ int qmm_moe_gateup(float* gate_out, float* up_out, const void* w_gate, const voi
     if (!mul_ok(t, n_used, &n_pairs)) return QMM_ERR_SHAPE;
     if (n_pairs > 65535 || n_ff > INT_MAX || t * in_f * 4 >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
     if (qmm::gemv_max_window_bytes(qtype, in_f, rb) >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
+    qmm::GemvTuning tune;
+    if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
     qmm::launch_moe(gate_out, up_out, w_gate, w_up, expert_ids, pair_scale, x, t, n_used, n_expert,
-                    in_f, n_ff, qtype, rb, stream);
+                    in_f, n_ff, qtype, rb, tune, stream);
     return launch_status();
 }
 
@@ -182,7 +249,9 @@ int qmm_stream_loadonly(uint32_t* sink, const void* w, int64_t m, int64_t k, int
     if (st) return st;
     if (!aligned(sink, 4)) return QMM_ERR_ALIGN;
     if (qmm::gemv_max_window_bytes(qtype, k, rb) >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
-    qmm::launch_loadonly(sink, w, m, k, qtype, rb, stream);
+    qmm::GemvTuning tune;
+    if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
+    qmm::launch_loadonly(sink, w, m, k, qtype, rb, tune, stream);
     return launch_status();
 }
 

@@ -34,4 +34,4 @@ from .formats import (  # noqa: F401
     e2m1_bits_to_f64,
     decode,
 )
-from .ref import gemm_ref, gemm_ref_rows, moe_ref, tolerance_check  # noqa: F401
+from .ref import gemm_ref, gemm_ref_rows, gemm_value, moe_ref, tolerance_check  # noqa: F401

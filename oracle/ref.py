@@ -26,6 +26,13 @@ import numpy as np
 from .formats import decode
 
 
+def gemm_value(name: str, w, x, m: int, k: int, n: int):
+    """ref as float64 [n, m] (decode, then one f64 matmul)."""
+    W = decode(name, w, m, k)
+    X = np.asarray(x, dtype=np.float32).reshape(n, k).astype(np.float64)
+    return X @ W.T
+
+
 def gemm_ref(name: str, w, x, m: int, k: int, n: int):
     """(ref, S) as float64 [n, m]."""
     W = decode(name, w, m, k)
