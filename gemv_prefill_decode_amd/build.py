@@ -43,6 +43,10 @@ def _flags():
         "-Wall",
         "-Wno-unused-function",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in VGPRs: with the default AGPR form the register
+        # allocator shuffles the prefill kernel's 64 accumulators between the
+        # two unrolled halves of its k loop on every iteration
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", INCLUDE,
         "-I", CSRC,
     ]

@@ -39,6 +39,13 @@ __device__ __forceinline__ u32x4 ld128(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// An offset no descriptor reaches: every descriptor the kernels build covers
+// fewer than 2^31 bytes (checked on the host), so a load at OOB_OFF (plus a
+// small immediate) returns zero.  Masking an address this way, instead of
+// zeroing the loaded value, keeps the load asynchronous: a select on the
+// loaded data would make the wave wait for it right after issuing it.
+constexpr uint32_t OOB_OFF = 0x80000000u;
+
 // Load N dwords starting at the dword-aligned offset (off & ~3).
 template <int N>
 __device__ __forceinline__ void ld_span(rsrc_t r, uint32_t off, uint32_t (&v)[N]) {
@@ -58,9 +65,12 @@ __device__ __forceinline__ void ld_span(rsrc_t r, uint32_t off, uint32_t (&v)[N]
     }
 }
 
-// Bytes [sh, sh+4) of the 8-byte little-endian pair (lo, hi), sh in 0..4.
+// Bytes [sh, sh+4) of the 8-byte little-endian pair (lo, hi), sh in 0..4
+// (v_alignbyte_b32 for 0..3; a 64-bit shift of adjacent array elements would
+// be turned into an unaligned 64-bit load and push the array to scratch).
 __device__ __forceinline__ uint32_t shr64(uint32_t lo, uint32_t hi, uint32_t sh) {
-    return (uint32_t)((((uint64_t)hi << 32) | lo) >> (8u * sh));
+    const uint32_t a = __builtin_amdgcn_alignbyte(hi, lo, sh & 3u);
+    return sh >= 4u ? hi : a;
 }
 
 __device__ __forceinline__ float h2f(uint32_t bits) {

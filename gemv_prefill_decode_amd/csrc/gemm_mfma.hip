@@ -47,13 +47,11 @@ template <int QT> struct ALoad;
 
 template <> struct ALoad<QT_F32> {
     u32x4 r[8];
-    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int k) {
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int k, int) {
         const int e = kt * 64 + 32 * p;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            r[i] = ld128(wr, row_off + 4u * (uint32_t)(e + 4 * i));
-            if (e + 4 * i >= k) r[i] = u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int i = 0; i < 8; ++i)  // runs past k read zeros (out-of-range offset)
+            r[i] = ld128(wr, e + 4 * i < k ? row_off + 4u * (uint32_t)(e + 4 * i) : OOB_OFF);
     }
     __device__ __forceinline__ void decode(uint32_t (&o)[16]) const {
 #pragma unroll
@@ -68,9 +66,9 @@ template <> struct ALoad<QT_F32> {
 template <> struct ALoad<QT_Q4_0> {
     uint32_t r[5], sh;
     bool valid;
-    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int k) {
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int k, int) {
         const int b = 2 * kt + p;
-        const uint32_t o = row_off + (uint32_t)b * 18u;
+        const uint32_t o = b * 32 < k ? row_off + (uint32_t)b * 18u : OOB_OFF;
         sh = o & 3u;
         valid = b * 32 < k;
         ld_span<5>(wr, o, r);
@@ -97,9 +95,9 @@ template <> struct ALoad<QT_Q4_0> {
 template <> struct ALoad<QT_Q8_0> {
     uint32_t r[9], sh;
     bool valid;
-    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int k) {
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int k, int) {
         const int b = 2 * kt + p;
-        const uint32_t o = row_off + (uint32_t)b * 34u;
+        const uint32_t o = b * 32 < k ? row_off + (uint32_t)b * 34u : OOB_OFF;
         sh = o & 3u;
         valid = b * 32 < k;
         ld_span<9>(wr, o, r);
@@ -126,10 +124,10 @@ template <> struct ALoad<QT_Q8_0> {
 template <> struct ALoad<QT_Q4_K> {
     u32x4 hdr, qs;
     int c;
-    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int) {
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int, int nk) {
         const uint32_t sb = (uint32_t)kt >> 2;
         c = kt & 3;
-        const uint32_t o = row_off + sb * 144u;
+        const uint32_t o = kt < nk ? row_off + sb * 144u : OOB_OFF;
         hdr = ld128(wr, o);
         qs = ld128(wr, o + 16u + 32u * (uint32_t)c + 16u * (uint32_t)p);
     }
@@ -156,10 +154,11 @@ template <> struct ALoad<QT_Q4_K> {
         for (int u = 0; u < 4; ++u) {
             const uint32_t q = u == 0 ? qs.x : (u == 1 ? qs.y : (u == 2 ? qs.z : qs.w));
             float lo[4], hi[4];
+            const uint32_t ql = q & 0x0F0F0F0Fu, qh = (q >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                lo[b] = __builtin_fmaf(D0, (float)((q >> (8 * b)) & 15u), -M0);
-                hi[b] = __builtin_fmaf(D1, (float)((q >> (8 * b + 4)) & 15u), -M1);
+                lo[b] = __builtin_fmaf(D0, ubyte_f32(ql, b), -M0);
+                hi[b] = __builtin_fmaf(D1, ubyte_f32(qh, b), -M1);
             }
             o[4 * u + 0] = pack_f2h(lo[0], lo[1]);
             o[4 * u + 1] = pack_f2h(lo[2], lo[3]);
@@ -175,11 +174,11 @@ template <> struct ALoad<QT_Q6_K> {
     uint32_t ra[5], rh[5], rs0, rs1, rd, sh;
     int kh;
     uint32_t pos0, pos1;
-    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int) {
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int, int nk) {
         const uint32_t sb = (uint32_t)kt >> 2;
         const uint32_t hh = ((uint32_t)kt >> 1) & 1u;
         kh = kt & 1;
-        const uint32_t o = row_off + sb * 210u;
+        const uint32_t o = kt < nk ? row_off + sb * 210u : OOB_OFF;
         sh = o & 3u;
         ld_span<5>(wr, o + 64u * hh + 32u * (uint32_t)kh + 16u * (uint32_t)p, ra);
         ld_span<5>(wr, o + 128u + 32u * hh + 16u * (uint32_t)p, rh);
@@ -206,8 +205,8 @@ template <> struct ALoad<QT_Q6_K> {
             float lo[4], hi[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                lo[b] = __builtin_fmaf(Dl, (float)((ql >> (8 * b)) & 0xFFu), Dl32);
-                hi[b] = __builtin_fmaf(Dh, (float)((qhv >> (8 * b)) & 0xFFu), Dh32);
+                lo[b] = __builtin_fmaf(Dl, ubyte_f32(ql, b), Dl32);
+                hi[b] = __builtin_fmaf(Dh, ubyte_f32(qhv, b), Dh32);
             }
             o[4 * u + 0] = pack_f2h(lo[0], lo[1]);
             o[4 * u + 1] = pack_f2h(lo[2], lo[3]);
@@ -221,8 +220,8 @@ template <> struct ALoad<QT_NVFP4> {
     uint32_t sd;
     u32x4 qs;
     int p_;
-    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int) {
-        const uint32_t o = row_off + (uint32_t)kt * 36u;
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int kt, int p, int, int nk) {
+        const uint32_t o = kt < nk ? row_off + (uint32_t)kt * 36u : OOB_OFF;
         p_ = p;
         sd = ld32(wr, o);
         qs = ld128(wr, o + 4u + 16u * (uint32_t)p);
@@ -249,28 +248,33 @@ template <> struct ALoad<QT_NVFP4> {
 };
 
 // ------------------------------------------------------------ activation tiles
-// Thread (token, p): slot units u=0..3 of [32p, 32p+32) of step kt, each two
-// runs of 4 activations placed by the format's permutation.
-template <int H> struct XLoad {
+// Thread t loads 16 bytes (a run of 4 consecutive k) of token row
+// 16*i + t/16 (i = 0..7): lane chunk c = t % 16 is run c & 1 of slot unit
+// c / 2 of the step, i.e. k = g*2H + 4s' + (c & 1)*H for the step's global
+// slot unit U = 8*kt + c/2, g = U / (H/4), s' = U % (H/4).  The 16 lanes of a
+// token together read whole 128-byte segments of its row.  Each run is
+// rounded to f16 and stored at slots 8*(c/2) + 4*(c&1) .. +3.
+struct XLoad {
     u32x4 r[8];
-    __device__ __forceinline__ void load(rsrc_t xr, uint32_t xrow_off, int kt, int p, int k) {
+    template <int H>
+    __device__ __forceinline__ void load(rsrc_t xr, int k, int kt, int tid) {
+        const int c = tid & 15, row = tid >> 4;
+        const int U = 8 * kt + (c >> 1);
+        const int g = U / (H / 4), sp = U % (H / 4);
+        const int e = g * 2 * H + 4 * sp + (c & 1) * H;
+        const uint32_t off = 4u * ((uint32_t)row * (uint32_t)k + (uint32_t)e);
+        const bool in = e < k;  // past k lies the next token's row: read zeros instead
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int U8 = 8 * kt + 4 * p + u;
-            const int g = U8 / (H / 4), sp = U8 % (H / 4);
-            const int e0 = g * 2 * H + 4 * sp, e1 = e0 + H;
-            r[2 * u] = ld128(xr, xrow_off + 4u * (uint32_t)e0);
-            r[2 * u + 1] = ld128(xr, xrow_off + 4u * (uint32_t)e1);
-            if (e0 >= k) r[2 * u] = u32x4{0u, 0u, 0u, 0u};
-            if (e1 >= k) r[2 * u + 1] = u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int i = 0; i < 8; ++i)
+            r[i] = ld128(xr, in ? off + 4u * 16u * (uint32_t)i * (uint32_t)k : OOB_OFF);
     }
-    __device__ __forceinline__ void convert(uint32_t (&o)[16]) const {
+    __device__ __forceinline__ void store(_Float16* sB, int tid) const {
+        const int c = tid & 15, row = tid >> 4;
+        const int slot = 8 * (c >> 1) + 4 * (c & 1);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const f32x4 v = __builtin_bit_cast(f32x4, r[i]);
-            o[2 * i] = pack_f2h(v.x, v.y);
-            o[2 * i + 1] = pack_f2h(v.z, v.w);
+            *(u32x2*)&sB[(16 * i + row) * LDK + slot] = u32x2{pack_f2h(v.x, v.y), pack_f2h(v.z, v.w)};
         }
     }
 };
@@ -278,7 +282,7 @@ template <int H> struct XLoad {
 // ------------------------------------------------------------ kernel
 
 template <int QT>
-__global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(float* __restrict__ dst,
+__global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(float* __restrict__ dst,
                                                            const uint8_t* __restrict__ w,
                                                            const float* __restrict__ x, int m,
                                                            int k, int n, int rb, int n_mb,
@@ -301,24 +305,32 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(float* __restrict__ d
     const rsrc_t xr = make_rsrc(x + n0 * k, (uint32_t)ntok * (uint32_t)k * 4u);
     const int arow = tid >> 1, part = tid & 1;
     const uint32_t roff = (uint32_t)((m0 + arow) * rb - base);
-    const uint32_t xoff = (uint32_t)arow * (uint32_t)k * 4u;
     const int nk = (k + BK - 1) / BK;
+    const int lds_a = arow * LDK + part * 32;
+    constexpr int H = Perm<QT>::H;
 
-    ALoad<QT> al;
-    XLoad<Perm<QT>::H> xl;
+    // Two register sets of raw step data: while the matrix cores work on step
+    // kt, the loads of step kt+2 are in flight and step kt+1 is decoded.
+    ALoad<QT> al0, al1;
+    XLoad xl0, xl1;
     uint32_t tmp[16];
-    const int lds_off = arow * LDK + part * 32;
+    auto stage = [&](const ALoad<QT>& al, const XLoad& xl, int buf) {
+        al.decode(tmp);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            *(u32x4*)&sA[buf][lds_a + 8 * u] = u32x4{tmp[4 * u], tmp[4 * u + 1], tmp[4 * u + 2], tmp[4 * u + 3]};
+        xl.store(sB[buf], tid);
+    };
 
-    al.load(wr, roff, 0, part, k);
-    xl.load(xr, xoff, 0, part, k);
-    al.decode(tmp);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-        *(u32x4*)&sA[0][lds_off + 8 * u] = u32x4{tmp[4 * u], tmp[4 * u + 1], tmp[4 * u + 2], tmp[4 * u + 3]};
-    xl.convert(tmp);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-        *(u32x4*)&sB[0][lds_off + 8 * u] = u32x4{tmp[4 * u], tmp[4 * u + 1], tmp[4 * u + 2], tmp[4 * u + 3]};
+    // Every load is unconditional (steps at or past nk read zeros through
+    // out-of-range offsets, and their staged tiles are never used), so the
+    // loop body is straight-line and the compiler's load counters let the
+    // loads of step kt+2 stay in flight while step kt computes.
+    al0.load(wr, roff, 0, part, k, nk);
+    xl0.template load<H>(xr, k, 0, tid);
+    al1.load(wr, roff, 1, part, k, nk);
+    xl1.template load<H>(xr, k, 1, tid);
+    stage(al0, xl0, 0);
     __syncthreads();
 
     f32x4 acc[4][4];
@@ -329,16 +341,9 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(float* __restrict__ d
 
     const int wm = wave >> 1, wn = wave & 1;
     const int frag = (lane & 15) * LDK + (lane >> 4) * 8;
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            al.load(wr, roff, kt + 1, part, k);
-            xl.load(xr, xoff, kt + 1, part, k);
-        }
-        const _Float16* A = &sA[cur][wm * 64 * LDK + frag];
-        const _Float16* B = &sB[cur][wn * 64 * LDK + frag];
+    auto mfma_step = [&](int buf) {
+        const _Float16* A = &sA[buf][wm * 64 * LDK + frag];
+        const _Float16* B = &sB[buf][wn * 64 * LDK + frag];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             f16x8 a[4], b[4];
@@ -352,18 +357,24 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(float* __restrict__ d
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
-        if (more) {
-            al.decode(tmp);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                *(u32x4*)&sA[cur ^ 1][lds_off + 8 * u] =
-                    u32x4{tmp[4 * u], tmp[4 * u + 1], tmp[4 * u + 2], tmp[4 * u + 3]};
-            xl.convert(tmp);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                *(u32x4*)&sB[cur ^ 1][lds_off + 8 * u] =
-                    u32x4{tmp[4 * u], tmp[4 * u + 1], tmp[4 * u + 2], tmp[4 * u + 3]};
-        }
+    };
+
+    // An odd step count runs one extra step whose weight and activation tiles
+    // are all zeros (out-of-range loads): it adds exactly 0 to every sum and
+    // keeps a single loop exit, so the accumulators stay in place.
+    const int nk2 = (nk + 1) & ~1;
+    for (int kt = 0; kt < nk2; kt += 2) {
+        // step kt: buffer 0; set 1 holds step kt+1, set 0 takes kt+2
+        al0.load(wr, roff, kt + 2, part, k, nk);
+        xl0.template load<H>(xr, k, kt + 2, tid);
+        mfma_step(0);
+        stage(al1, xl1, 1);
+        __syncthreads();
+        // step kt+1: buffer 1; set 0 holds step kt+2, set 1 takes kt+3
+        al1.load(wr, roff, kt + 3, part, k, nk);
+        xl1.template load<H>(xr, k, kt + 3, tid);
+        mfma_step(1);
+        stage(al0, xl0, 0);
         __syncthreads();
     }
 

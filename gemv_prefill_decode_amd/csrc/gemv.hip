@@ -57,10 +57,11 @@ template <> struct GUnit<QT_F32> {  // 16 weights, 64 bytes
     static constexpr int prel1(int s) { return rel1(s); }
     uint32_t r[16];
     __device__ __forceinline__ void load(rsrc_t wr, uint32_t off, int e, int k, const Lane&) {
-        ld_span<16>(wr, off, r);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)  // k % 4 == 0: a run of 4 is wholly in or out
-            if (e + 4 * i >= k) r[4 * i] = r[4 * i + 1] = r[4 * i + 2] = r[4 * i + 3] = 0u;
+        for (int i = 0; i < 4; ++i) {  // k % 4 == 0: a run of 4 is wholly in or out
+            const u32x4 v = ld128(wr, e + 4 * i < k ? off + 16u * i : OOB_OFF);
+            r[4 * i] = v.x; r[4 * i + 1] = v.y; r[4 * i + 2] = v.z; r[4 * i + 3] = v.w;
+        }
     }
     __device__ __forceinline__ void prep(const Lane&) {}
     __device__ __forceinline__ void sub(int s, float (&w)[8], float&, float&) const {

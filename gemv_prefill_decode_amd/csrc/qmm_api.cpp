@@ -190,16 +190,16 @@ int qmm_gemm_path(float* dst, const void* w, const float* x, int64_t m, int64_t 
     }
     if (path == QMM_PATH_GEMV) {
         // one work group addresses at most this window of w, and 8 token rows of x
-        if (qmm::gemv_max_window_bytes(qtype, k, rb) >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
-        if (8 * k * 4 >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
+        if (qmm::gemv_max_window_bytes(qtype, k, rb) >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+        if (8 * k * 4 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
         qmm::GemvTuning tune;
         if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
         qmm::launch_gemv(dst, w, x, m, k, n, qtype, rb, tune, stream);
         return launch_status();
     }
     if (path == QMM_PATH_MFMA) {
-        if ((int64_t)qmm::MFMA_BM * rb + 16 >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
-        if ((int64_t)qmm::MFMA_BN * k * 4 >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
+        if ((int64_t)qmm::MFMA_BM * rb + 16 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+        if ((int64_t)qmm::MFMA_BN * k * 4 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
         const int64_t tiles = ((m + qmm::MFMA_BM - 1) / qmm::MFMA_BM) * ((n + qmm::MFMA_BN - 1) / qmm::MFMA_BN);
         if (tiles > INT_MAX) return QMM_ERR_RANGE;
         qmm::launch_gemm_mfma(dst, w, x, m, k, n, qtype, rb, stream);
@@ -232,8 +232,8 @@ int qmm_moe_gateup(float* gate_out, float* up_out, const void* w_gate, const voi
         return QMM_ERR_ALIGN;
     int64_t n_pairs;
     if (!mul_ok(t, n_used, &n_pairs)) return QMM_ERR_SHAPE;
-    if (n_pairs > 65535 || n_ff > INT_MAX || t * in_f * 4 >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
-    if (qmm::gemv_max_window_bytes(qtype, in_f, rb) >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
+    if (n_pairs > 65535 || n_ff > INT_MAX || t * in_f * 4 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+    if (qmm::gemv_max_window_bytes(qtype, in_f, rb) >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
     qmm::GemvTuning tune;
     if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
     qmm::launch_moe(gate_out, up_out, w_gate, w_up, expert_ids, pair_scale, x, t, n_used, n_expert,
@@ -248,7 +248,7 @@ int qmm_stream_loadonly(uint32_t* sink, const void* w, int64_t m, int64_t k, int
     int st = check_weights(w, m, k, qtype, &rb);
     if (st) return st;
     if (!aligned(sink, 4)) return QMM_ERR_ALIGN;
-    if (qmm::gemv_max_window_bytes(qtype, k, rb) >= ((int64_t)1 << 32)) return QMM_ERR_RANGE;
+    if (qmm::gemv_max_window_bytes(qtype, k, rb) >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
     qmm::GemvTuning tune;
     if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
     qmm::launch_loadonly(sink, w, m, k, qtype, rb, tune, stream);
