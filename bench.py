@@ -3,19 +3,26 @@
 
 A step is one pass of the LFM2.5-350M-shaped 512-token prefill: the four
 projection shapes (ffn_gate 4608x1024, ffn_down 1024x4608, conv_in 3072x1024,
-attn_out 1024x1024; shapes of cera wgpu_gemm_bench.rs, SHAPES) in each of the
+attn_out 1024x1024; the SHAPES of cera wgpu_gemm_bench.rs) in each of the
 five weight formats (f32, q4_0, q8_0, q4_k, q6_k) = 20 GEMMs with n = 512,
-all on the f16 matrix-core path.  `value` is TFLOP/s (2*m*k*n per GEMM) over
-the K timed steps, inputs resident in HBM.
+all on the f16 matrix-core path.  Each format's four launches are captured
+once in a HIP graph; a timed step replays the five graphs back to back on
+one stream, with HIP events between them.  `value` is TFLOP/s (2*m*k*n per
+GEMM) over the K timed steps, inputs resident in HBM.
 
-The same JSON line also carries the other half of the metric, decode GEMV
-HBM GB/s at n = 1 (q4_k and q6_k, 14336x4096 and 4608x1024, weight copies
-rotated over >= 1 GiB so every read comes from HBM), the NVFP4 MoE gate/up at
-t = 1 and t = 16, the load-only twin's GB/s on the decode shapes, the roofline
-of the dominant kernel (HIP events around every launch in the timed region)
-and the CPU oracle timed on the host cores.
+The same JSON line also carries the other half of the metric:
+  decode   the GEMV sweep n in {1,4,8,16,32}, q4_k and q6_k at 14336x4096 and
+           4608x1024, weight copies rotated over >= 1 GiB so that every read
+           comes from HBM; GB/s of algorithmic bytes (packed W + x + dst) and
+           TFLOP/s, each against its roof; the load-only twin at n = 1.
+  moe      the NVFP4 gate/up rows at t = 1 and t = 16 (64 experts, 8 used,
+           in_f 4096, n_ff 2048), rotated over 4 weight copies x 8 id draws.
+  roofline the dominant prefill kernel instance: algorithmic flops per launch
+           over its average launch time from the events of the timed region.
+  cpu_baseline  the CPU oracle over the whole prefill step on the host cores.
+Decode and MoE launches are graph-replayed too (32+ launches per graph).
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras] [--quick]
 """
 
 from __future__ import annotations
@@ -32,11 +39,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_F16_TFLOPS = 2516.6   # MI355X dense f16 MFMA
+PEAK_F32_TFLOPS = 157.3    # MI355X f32 vector FMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 SHAPES = [("ffn_gate", 4608, 1024), ("ffn_down", 1024, 4608), ("conv_in", 3072, 1024),
           ("attn_out", 1024, 1024)]
 QTS = ["f32", "q4_0", "q8_0", "q4_k", "q6_k"]
-KERNEL_NAME = {"gemm": "gemm_mfma_kernel", "gemv": "gemv_kernel", "moe": "moe_gateup_kernel"}
+QT_ENUM = {"f32": 0, "q4_0": 1, "q8_0": 2, "q4_k": 3, "q6_k": 4, "nvfp4": 5}
+DECODE_SHAPES = [(14336, 4096), (4608, 1024)]
+DECODE_NS = [1, 4, 8, 16, 32]
 
 
 def log(msg):
@@ -44,6 +54,8 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources; profiles/traffic.json is used only when it
+    was measured on the same sources."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gemv_prefill_decode_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
@@ -53,18 +65,18 @@ def kernel_source_hash() -> str:
 
 
 def traffic_from_profiles(kernel: str):
-    """HBM bytes per launch from committed rocprofv3 PMC summaries, only if
-    they were taken on the current kernel sources."""
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
+    calibration) from profiles/traffic.json, or None if absent or stale."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             tab = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = tab.get(kernel)
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    if tab.get("source_hash") != kernel_source_hash():
         return None
-    return ent.get("bytes_per_launch")
+    ent = tab.get("kernels", {}).get(kernel)
+    return None if not ent else ent.get("bytes_per_launch")
 
 
 def gen_weights(qt, m, k, buf_id):
@@ -83,139 +95,168 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
 
 
+def capture(fns):
+    """Capture the calls in fns (in order) into one HIP graph."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):          # first calls outside capture (library load, lazy state)
+        for f in fns[:2]:
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, launches, rounds):
+    """Median seconds per launch over `rounds` replays of g (events on the
+    replay stream)."""
+    import torch
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(rounds):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3 / launches)
+    return statistics.median(ts)
+
+
 # ---------------------------------------------------------------- prefill step
 
-def prefill_setup(n):
-    from synth import gen
+def run_prefill(args, n):
     import torch
-    bufs = []
-    xs = {}
-    outs = {}
-    for si, (label, m, k) in enumerate(SHAPES):
+    import gemv_prefill_decode_amd as qmm
+    from synth import gen
+    xs, outs, bufs = {}, {}, []
+    for label, m, k in SHAPES:
         if k not in xs:
             xs[k] = to_dev(gen.unit_f32(n * k, gen.SEED_X + k).reshape(n, k))
         outs[label] = torch.empty((n, m), dtype=torch.float32, device="cuda")
     for qi, qt in enumerate(QTS):
         for si, (label, m, k) in enumerate(SHAPES):
-            w = to_dev(gen_weights(qt, m, k, 16 * qi + si))
-            bufs.append((qt, label, m, k, w))
-    return bufs, xs, outs
+            bufs.append((qt, label, m, k, to_dev(gen_weights(qt, m, k, 16 * qi + si))))
 
+    def call(b):
+        qt, label, m, k, w = b
+        return lambda: qmm.gemm(w, xs[k], m, qt, out=outs[label], path="mfma")
 
-def prefill_step(bufs, xs, outs, events=None):
-    import gemv_prefill_decode_amd as qmm
-    for i, (qt, label, m, k, w) in enumerate(bufs):
-        if events is not None:
-            events[i][0].record()
-        qmm.gemm(w, xs[k], m, qt, out=outs[label], path="mfma")
-        if events is not None:
-            events[i][1].record()
-
-
-def run_prefill(args, n):
-    import torch
-    bufs, xs, outs = prefill_setup(n)
-    flops = [2.0 * m * k * n for (_, _, m, k, _) in bufs]
-    step_flops = sum(flops)
+    graphs = {qt: capture([call(b) for b in bufs if b[0] == qt]) for qt in QTS}
+    flops = {qt: sum(2.0 * m * k * n for (q, _, m, k, _) in bufs if q == qt) for qt in QTS}
+    step_flops = sum(flops.values())
     for _ in range(args.warmup):
-        prefill_step(bufs, xs, outs)
+        for qt in QTS:
+            graphs[qt].replay()
     torch.cuda.synchronize()
-    # timed region: K steps, events around every launch on the launch stream
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in bufs] for _ in range(args.steps)]
+    ev = [{qt: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for qt in QTS} for _ in range(args.steps)]
+    # timed region: K steps, each the five per-format graphs on the current stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        prefill_step(bufs, xs, outs, ev[s])
+        for qt in QTS:
+            ev[s][qt][0].record()
+            graphs[qt].replay()
+            ev[s][qt][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_launch = [[ev[s][i][0].elapsed_time(ev[s][i][1]) * 1e-3 for s in range(args.steps)]
-                  for i in range(len(bufs))]
-    # per-qtype aggregates
     per_qt = {}
-    for i, (qt, label, m, k, _) in enumerate(bufs):
-        d = per_qt.setdefault(qt, {"flops": 0.0, "sec": 0.0, "launches": 0, "shapes": {}})
-        t = statistics.median(per_launch[i])
-        d["flops"] += flops[i]
-        d["sec"] += sum(per_launch[i]) / args.steps
-        d["launches"] += 1
-        d["shapes"][label] = {"us": round(t * 1e6, 2), "TFLOP/s": round(flops[i] / t / 1e12, 1)}
-    for qt, d in per_qt.items():
-        d["TFLOP/s"] = round(d["flops"] / d["sec"] / 1e12, 1)
-        d["frac_mfma_peak"] = round(d["flops"] / d["sec"] / 1e12 / PEAK_F16_TFLOPS, 4)
-    dom = max(per_qt, key=lambda q: per_qt[q]["sec"])
-    d = per_qt[dom]
-    avg_launch = d["sec"] / d["launches"]
-    flops_per_launch = d["flops"] / d["launches"]
-    ach = flops_per_launch / avg_launch / 1e12
+    for qt in QTS:
+        sec = [ev[s][qt][0].elapsed_time(ev[s][qt][1]) * 1e-3 for s in range(args.steps)]
+        mean = sum(sec) / len(sec)
+        per_qt[qt] = {"us_per_step": round(mean * 1e6, 2),
+                      "TFLOP/s": round(flops[qt] / mean / 1e12, 1),
+                      "frac_mfma_peak": round(flops[qt] / mean / 1e12 / PEAK_F16_TFLOPS, 4)}
+    # per-shape times (outside the timed region): each launch graph-replayed alone
+    for (qt, label, m, k, w) in bufs:
+        g = capture([call((qt, label, m, k, w))] * 8)
+        t = time_graph(g, 8, 5)
+        per_qt[qt].setdefault("shapes", {})[label] = {
+            "us": round(t * 1e6, 2), "TFLOP/s": round(2.0 * m * k * n / t / 1e12, 1)}
+        del g
+    dom = max(QTS, key=lambda q: per_qt[q]["us_per_step"])
+    launches = sum(1 for b in bufs if b[0] == dom)
+    avg_launch = per_qt[dom]["us_per_step"] * 1e-6 / launches
+    fpl = flops[dom] / launches
+    ach = fpl / avg_launch / 1e12
     roofline = {
-        "kernel": f"{KERNEL_NAME['gemm']}<{dom}>",
+        "kernel": f"qmm::gemm_mfma_kernel<{QT_ENUM[dom]}> ({dom} weights)",
         "bound": "mfma",
         "achieved": round(ach, 2),
         "peak": PEAK_F16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(ach / PEAK_F16_TFLOPS, 4),
+        "traffic": traffic_from_profiles(f"gemm_mfma_kernel<{QT_ENUM[dom]}>"),
         "avg_launch_us": round(avg_launch * 1e6, 3),
-        "algorithmic_flops_per_launch": flops_per_launch,
-        "traffic": traffic_from_profiles(f"gemm_mfma<{dom}>"),
+        "launches_per_step": launches,
+        "algorithmic_flops_per_launch": fpl,
+        "algorithmic_bytes_per_launch": sum(
+            (m * qmm.row_bytes(q, k) + 4 * n * k + 4 * n * m) for (q, _, m, k, _) in bufs
+            if q == dom) / launches,
     }
-    for qt in per_qt:
-        per_qt[qt].pop("flops"); per_qt[qt].pop("sec"); per_qt[qt].pop("launches")
-    return step_flops, wall, per_qt, roofline, bufs, xs
+    return step_flops, wall, per_qt, roofline
 
 
 # ---------------------------------------------------------------- decode GEMV
+
+def rotated_copies(base, copies):
+    """copies of base, each with one payload byte perturbed (distinct buffers)."""
+    ws = []
+    for c in range(copies):
+        w = base.clone()
+        w[5] ^= (c * 16 + 1) & 0xFF
+        ws.append(w)
+    return ws
+
 
 def run_decode(args):
     import torch
     import gemv_prefill_decode_amd as qmm
     from synth import gen
     res = {}
-    shapes = [(14336, 4096), (4608, 1024)]
     for qt in ("q4_k", "q6_k"):
-        for (m, k) in shapes:
+        for (m, k) in DECODE_SHAPES:
             wbytes = m * qmm.row_bytes(qt, k)
             copies = max(4, -(-(1 << 30) // wbytes))
             if args.quick:
                 copies = max(4, copies // 8)
-            base = to_dev(gen_weights(qt, m, k, 99))
-            ws = []
-            for c in range(copies):       # clone-and-perturb one payload byte per copy
-                w = base.clone()
-                w[5] ^= (c * 16 + 1) & 0xFF
-                ws.append(w)
-            x = to_dev(gen.unit_f32(k, gen.SEED_X))
-            x = x.view(1, k)
-            out = torch.empty((1, m), dtype=torch.float32, device="cuda")
+            ws = rotated_copies(to_dev(gen_weights(qt, m, k, 99)), copies)
+            L = max(copies, 32)
+            ent = {"copies": copies, "footprint_MiB": round(copies * wbytes / 2**20),
+                   "weight_bytes": wbytes}
+            for n in DECODE_NS:
+                x = to_dev(gen.unit_f32(n * k, gen.SEED_X).reshape(n, k))
+                out = torch.empty((n, m), dtype=torch.float32, device="cuda")
+                g = capture([(lambda w=ws[i % copies]: qmm.gemm(w, x, m, qt, out=out, path="gemv"))
+                             for i in range(L)])
+                t = time_graph(g, L, 5)
+                del g
+                alg = wbytes + 4 * n * k + 4 * n * m
+                ent[f"n{n}"] = {"us": round(t * 1e6, 2),
+                                "GB/s": round(alg / t / 1e9, 1),
+                                "frac_hbm_peak": round(alg / t / 1e9 / PEAK_HBM_GBS, 4),
+                                "TFLOP/s": round(2.0 * m * k * n / t / 1e12, 2),
+                                "frac_f32_peak": round(2.0 * m * k * n / t / 1e12 / PEAK_F32_TFLOPS, 4)}
             sink = torch.empty(m, dtype=torch.int32, device="cuda")
-            reps = args.decode_reps
-            for i in range(min(copies, 20)):
-                qmm.gemm(ws[i], x, m, qt, out=out, path="gemv")
-            torch.cuda.synchronize()
-
-            def timed(fn):
-                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                       for _ in range(reps)]
-                for r in range(reps):
-                    evs[r][0].record()
-                    fn(ws[r % copies])
-                    evs[r][1].record()
-                torch.cuda.synchronize()
-                return statistics.median(a.elapsed_time(b) * 1e-3 for a, b in evs)
-            t = timed(lambda w: qmm.gemm(w, x, m, qt, out=out, path="gemv"))
-            tl = timed(lambda w: qmm.stream_loadonly(w, m, k, qt, sink=sink))
-            alg = wbytes + 4 * k + 4 * m
-            res[f"{qt}_{m}x{k}"] = {
-                "us": round(t * 1e6, 2),
-                "GB/s": round(alg / t / 1e9, 1),
-                "frac_hbm_peak": round(alg / t / 1e9 / PEAK_HBM_GBS, 4),
-                "weight_GB/s": round(wbytes / t / 1e9, 1),
-                "loadonly_us": round(tl * 1e6, 2),
-                "loadonly_GB/s": round(wbytes / tl / 1e9, 1),
-                "copies": copies,
-                "footprint_MiB": round(copies * wbytes / 2**20),
-            }
-            del ws, base
+            g = capture([(lambda w=ws[i % copies]: qmm.stream_loadonly(w, m, k, qt, sink=sink))
+                         for i in range(L)])
+            tl = time_graph(g, L, 5)
+            del g
+            ent["loadonly_us"] = round(tl * 1e6, 2)
+            ent["loadonly_GB/s"] = round(wbytes / tl / 1e9, 1)
+            res[f"{qt}_{m}x{k}"] = ent
+            log(f"decode {qt} {m}x{k}: n=1 {ent['n1']['us']} us {ent['n1']['GB/s']} GB/s; "
+                f"load-only {ent['loadonly_us']} us")
+            del ws
             torch.cuda.empty_cache()
     return res
 
@@ -239,49 +280,110 @@ def run_moe(args):
     copies = 2 if args.quick else 4
     sets = []
     for c in range(copies):
-        g = planes[0].clone(); u = planes[1].clone()
+        g = planes[0].clone()
+        u = planes[1].clone()
         for e in range(n_expert):           # perturb one payload byte of every expert slab
             g[e * per_e + 5] ^= (c * 16 + 1) & 0xFF
             u[e * per_e + 5] ^= (c * 16 + 2) & 0xFF
         sets.append((g, u))
     del planes
     res = {}
+    L = 32
     for t in (1, 16):
         n_pairs = t * n_used
-        draws = [to_dev(gen.expert_ids(t, n_used, n_expert, gen.SEED_EXPERTS + d)) for d in range(8)]
+        draws_h = [gen.expert_ids(t, n_used, n_expert, gen.SEED_EXPERTS + d) for d in range(8)]
+        draws = [to_dev(d) for d in draws_h]
+        uniq = [len(np.unique(d)) for d in draws_h]
         sc = to_dev(gen.pair_scales(2 * n_pairs))
         x = to_dev(gen.xorshift_f32(t * in_f, gen.SEED_MOE_X).reshape(t, in_f))
         go = torch.empty((n_pairs, n_ff), dtype=torch.float32, device="cuda")
         uo = torch.empty((n_pairs, n_ff), dtype=torch.float32, device="cuda")
-        uniq = [len(np.unique(gen.expert_ids(t, n_used, n_expert, gen.SEED_EXPERTS + d))) for d in range(8)]
-        for i in range(10):
-            qmm.moe_gateup(sets[i % copies][0], sets[i % copies][1], draws[i % 8], sc, x, n_expert,
-                           n_ff, gate_out=go, up_out=uo)
-        torch.cuda.synchronize()
-        reps = args.moe_reps
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for r in range(reps):
-            evs[r][0].record()
-            qmm.moe_gateup(sets[r % copies][0], sets[r % copies][1], draws[r % 8], sc, x, n_expert, n_ff,
-                           gate_out=go, up_out=uo)
-            evs[r][1].record()
-        torch.cuda.synchronize()
-        times = [a.elapsed_time(b) * 1e-3 for a, b in evs]
-        byts = [2 * uniq[r % 8] * per_e + 4 * t * in_f + 2 * 4 * n_pairs * n_ff for r in range(reps)]
-        gbs = statistics.median(b / s / 1e9 for b, s in zip(byts, times))
-        res[f"t{t}"] = {
-            "us": round(statistics.median(times) * 1e6, 2),
-            "GB/s": round(gbs, 1),
-            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "unique_experts_mean": round(sum(uniq) / len(uniq), 2),
-        }
+        g = capture([(lambda c=sets[i % copies], d=draws[i % 8]:
+                      qmm.moe_gateup(c[0], c[1], d, sc, x, n_expert, n_ff, gate_out=go, up_out=uo))
+                     for i in range(L)])
+        tt = time_graph(g, L, 5)
+        del g
+        byts = statistics.mean(2 * uniq[i % 8] * per_e + 4 * t * in_f + 2 * 4 * n_pairs * n_ff
+                               for i in range(L))
+        res[f"t{t}"] = {"us": round(tt * 1e6, 2),
+                        "GB/s": round(byts / tt / 1e9, 1),
+                        "frac_hbm_peak": round(byts / tt / 1e9 / PEAK_HBM_GBS, 4),
+                        "unique_experts_mean": round(statistics.mean(uniq), 2),
+                        "algorithmic_bytes_mean": round(byts)}
+        log(f"moe t={t}: {res[f't{t}']['us']} us {res[f't{t}']['GB/s']} GB/s")
     return res
+
+
+# ---------------------------------------------------------------- HBM traffic
+
+COPY_PROBE_BYTES = 1 << 30
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def copy_probe():
+    """Three device-to-device copies of 1 GiB (the runtime's copy kernel): the
+    calibration for the FETCH_SIZE / WRITE_SIZE counters.  The largest copies
+    in the run, so the summary can find them."""
+    import torch
+    a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
+
+
+def pmc_summary(fetch_csv, write_csv, out_path):
+    """profiles/traffic.json from two rocprofv3 --pmc counter_collection.csv
+    files (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  Each counter is
+    scaled by what it reads for the copy probe (COPY_PROBE_BYTES read and
+    written per copy)."""
+    import csv
+    import collections
+
+    def read(path, counter):
+        per = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "").strip()
+            per[name].append(float(r["Counter_Value"]) * 1024.0)
+        return per
+
+    fetch, write = read(fetch_csv, "FETCH_SIZE"), read(write_csv, "WRITE_SIZE")
+    fac = {}
+    for lab, per in (("fetch", fetch), ("write", write)):
+        vals = per.get(COPY_KERNEL, [])
+        if not vals:
+            raise SystemExit(f"no {COPY_KERNEL} dispatches in the {lab} counters")
+        top = max(vals)
+        probe = [v for v in vals if v >= 0.5 * top]
+        fac[lab] = COPY_PROBE_BYTES / statistics.mean(probe)
+    kernels = {}
+    for name in sorted(set(fetch) & set(write)):
+        if not name.startswith("qmm::"):
+            continue
+        f = statistics.mean(fetch[name]) * fac["fetch"]
+        w = statistics.mean(write[name]) * fac["write"]
+        short = name.replace("qmm::", "")
+        kernels[short] = {"fetch_bytes": round(f), "write_bytes": round(w),
+                          "bytes_per_launch": round(f + w), "dispatches": len(fetch[name])}
+    tab = {"source_hash": kernel_source_hash(),
+           "calibration": {"copy_bytes": COPY_PROBE_BYTES, "fetch_scale": round(fac["fetch"], 4),
+                           "write_scale": round(fac["write"], 4)},
+           "kernels": kernels}
+    with open(out_path, "w") as f:
+        json.dump(tab, f, indent=1)
+    print(json.dumps(tab["calibration"]))
+    for k, v in kernels.items():
+        print(f"{k:70s} {v['bytes_per_launch'] / 1e6:10.3f} MB/launch  (n={v['dispatches']})")
 
 
 # ---------------------------------------------------------------- CPU oracle
 
 def run_cpu_baseline(args, n):
-    import numpy as np
     from oracle import ref
     from synth import gen
     try:
@@ -289,7 +391,6 @@ def run_cpu_baseline(args, n):
         cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
         cores = os.cpu_count() or 1
-    import gemv_prefill_decode_amd as qmm
     work = []
     for qi, qt in enumerate(QTS):
         for si, (label, m, k) in enumerate(SHAPES):
@@ -304,15 +405,14 @@ def run_cpu_baseline(args, n):
             ref.gemm_value(qt, w, x, m, k, n)
         return time.perf_counter() - t0
     once()
-    ts = [once() for _ in range(3)]
-    t = statistics.median(ts)
+    t = statistics.median([once() for _ in range(3)])
     return {
         "value": round(flops / t / 1e12, 5),
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"the full 20-GEMM prefill step (4 shapes x 5 formats, n={n}): numpy decode to "
-                  f"f64 + f64 matmul (OpenBLAS); median of 3 after 1 warm-up, {t:.2f} s per step",
+        "sample": f"the whole 20-GEMM prefill step (4 shapes x 5 formats, n={n}): numpy decode to "
+                  f"f64 + f64 matmul (BLAS); median of 3 after 1 warm-up, {t:.2f} s per step",
     }
 
 
@@ -322,14 +422,19 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--n", type=int, default=512, help="prefill tokens (default 512)")
-    ap.add_argument("--decode-reps", type=int, default=200)
-    ap.add_argument("--moe-reps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode and MoE measurements")
     ap.add_argument("--quick", action="store_true", help="fewer rotation copies")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run the 1 GiB copy that calibrates the HBM byte counters")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], os.path.join(ROOT, "profiles", "traffic.json"))
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+        print(f"bench.py measures one GPU; there is no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
@@ -341,15 +446,18 @@ def main():
         sys.exit(2)
     import gemv_prefill_decode_amd as qmm
     qmm.load()
+    if args.copy_probe:
+        log("copy probe: 3 x 1 GiB device copies")
+        copy_probe()
     n = args.n
     log(f"prefill step: {len(SHAPES)} shapes x {len(QTS)} formats, n={n}, warmup={args.warmup} steps={args.steps}")
-    step_flops, wall, per_qt, roofline, _, _ = run_prefill(args, n)
+    step_flops, wall, per_qt, roofline = run_prefill(args, n)
     value = step_flops * args.steps / wall / 1e12
     log(f"prefill: {value:.1f} TFLOP/s, {wall / args.steps * 1e3:.3f} ms/step")
     extras = {}
     if not args.no_extras:
-        log("decode GEMV n=1 with rotation")
-        extras["decode_n1"] = run_decode(args)
+        log("decode GEMV sweep with rotation")
+        extras["decode"] = run_decode(args)
         log("MoE gate/up NVFP4")
         extras["moe_gateup"] = run_moe(args)
     cpu = None
@@ -367,10 +475,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16-mfma/f32-acc",
-        "data": "synthetic (seeded LCG packed weights and uniform[-1,1) activations)",
-        "config": {"workload": "LFM2.5-350M-shaped prefill n=512: ffn_gate 4608x1024, ffn_down 1024x4608, "
-                               "conv_in 3072x1024, attn_out 1024x1024 in f32/q4_0/q8_0/q4_k/q6_k",
+        "dtype": "f16",
+        "data": "synthetic (seeded LCG packed weights, uniform[-1,1) activations)",
+        "config": {"workload": "LFM2.5-350M-shaped prefill, n=512: ffn_gate 4608x1024, ffn_down 1024x4608, "
+                               "conv_in 3072x1024, attn_out 1024x1024, each in f32/q4_0/q8_0/q4_k/q6_k "
+                               "(f16 MFMA operands, f32 accumulation)",
                    "n": n, "gemms_per_step": len(SHAPES) * len(QTS)},
         "per_qtype": per_qt,
         "roofline": roofline,

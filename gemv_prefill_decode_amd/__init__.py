@@ -20,7 +20,8 @@ import os
 import threading
 
 __all__ = [
-    "QTYPES", "PATHS", "QmmError", "lib_path", "load", "gemm", "moe_gateup", "stream_loadonly",
+    "QTYPES", "PATHS", "QmmError", "lib_path", "load", "gemm", "workspace_bytes", "moe_gateup",
+    "stream_loadonly",
     "row_bytes", "block_elems", "gemv_max_n", "status_str", "abi_version",
 ]
 
@@ -59,6 +60,10 @@ def load() -> ctypes.CDLL:
         lib.qmm_gemm.restype = i32
         lib.qmm_gemm_path.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, vp]
         lib.qmm_gemm_path.restype = i32
+        lib.qmm_gemm_ws.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, vp, i64, vp]
+        lib.qmm_gemm_ws.restype = i32
+        lib.qmm_gemm_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+        lib.qmm_gemm_workspace_bytes.restype = i64
         lib.qmm_moe_gateup.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
         lib.qmm_moe_gateup.restype = i32
         lib.qmm_stream_loadonly.argtypes = [vp, vp, i64, i64, i32, vp]
@@ -129,11 +134,40 @@ def _dev(t, what, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def gemm(w, x, m: int, qtype, out=None, path: str = "auto", stream=None):
+def workspace_bytes(m: int, k: int, n: int, qtype, path: str = "auto") -> int:
+    """Bytes of workspace qmm_gemm_ws uses for this product (0: none)."""
+    v = load().qmm_gemm_workspace_bytes(m, k, n, _qt(qtype), PATHS[path])
+    if v < 0:
+        raise QmmError(-v, "qmm_gemm_workspace_bytes")
+    return v
+
+
+# Workspaces handed to qmm_gemm_ws by gemm(workspace="auto"): one buffer per
+# (device, stream), grown when a product needs more.  Buffers are never
+# freed, so a call captured in a graph keeps a valid workspace.
+_WS = {}
+_WS_ALL = []
+
+
+def _auto_workspace(device, stream_handle: int, nbytes: int):
+    import torch
+    key = (device.index, stream_handle)
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _WS[key] = buf
+        _WS_ALL.append(buf)
+    return buf
+
+
+def gemm(w, x, m: int, qtype, out=None, path: str = "auto", stream=None, workspace="auto"):
     """dst[n, m] with dst[j, i] = sum_c deq(w)[i, c] * x[j, c].
 
     w: packed weights (uint8, m*row_bytes(qtype, k) bytes; float32 [m, k] for
-    "f32"); x: float32 [n, k]; out: optional float32 [n, m]."""
+    "f32"); x: float32 [n, k]; out: optional float32 [n, m].
+    workspace: "auto" (a buffer kept per device and stream), None (no k split
+    on the matrix-core path), or a device tensor of at least
+    workspace_bytes() bytes."""
     import torch
     lib = load()
     qt = _qt(qtype)
@@ -147,10 +181,21 @@ def gemm(w, x, m: int, qtype, out=None, path: str = "auto", stream=None):
     need = m * row_bytes(qt, k)
     if w.numel() * w.element_size() != need:
         raise ValueError(f"w holds {w.numel() * w.element_size()} bytes, expected {need}")
-    st = lib.qmm_gemm_path(_dev(out, "out", torch.float32), _dev(w, "w"),
-                           _dev(x, "x", torch.float32), m, k, n, qt, PATHS[path], _stream(stream))
+    sh = _stream(stream)
+    ws_ptr, ws_len = None, 0
+    if workspace is not None:
+        nbytes = workspace_bytes(m, k, n, qt, path)
+        if nbytes > 0:
+            if isinstance(workspace, str):
+                if workspace != "auto":
+                    raise ValueError("workspace must be 'auto', None or a tensor")
+                workspace = _auto_workspace(x.device, sh.value or 0, nbytes)
+            ws_ptr = _dev(workspace, "workspace")
+            ws_len = workspace.numel() * workspace.element_size()
+    st = lib.qmm_gemm_ws(_dev(out, "out", torch.float32), _dev(w, "w"), _dev(x, "x", torch.float32),
+                         m, k, n, qt, PATHS[path], ws_ptr, ws_len, sh)
     if st != 0:
-        raise QmmError(st, "qmm_gemm_path")
+        raise QmmError(st, "qmm_gemm_ws")
     return out
 
 

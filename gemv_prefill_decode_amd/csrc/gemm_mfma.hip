@@ -256,14 +256,15 @@ template <> struct ALoad<QT_NVFP4> {
 // rounded to f16 and stored at slots 8*(c/2) + 4*(c&1) .. +3.
 struct XLoad {
     u32x4 r[8];
+    // k: row length (stride); kend: loads at k positions >= kend read zeros
     template <int H>
-    __device__ __forceinline__ void load(rsrc_t xr, int k, int kt, int tid) {
+    __device__ __forceinline__ void load(rsrc_t xr, int k, int kend, int kt, int tid) {
         const int c = tid & 15, row = tid >> 4;
         const int U = 8 * kt + (c >> 1);
         const int g = U / (H / 4), sp = U % (H / 4);
         const int e = g * 2 * H + 4 * sp + (c & 1) * H;
         const uint32_t off = 4u * ((uint32_t)row * (uint32_t)k + (uint32_t)e);
-        const bool in = e < k;  // past k lies the next token's row: read zeros instead
+        const bool in = e < kend;  // past k lies the next token's row: read zeros instead
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             r[i] = ld128(xr, in ? off + 4u * 16u * (uint32_t)i * (uint32_t)k : OOB_OFF);
@@ -281,21 +282,30 @@ struct XLoad {
 
 // ------------------------------------------------------------ kernel
 
+// Split k (n_split > 1): work item (z, tile) covers the k steps
+// [z*sps, min(nk, (z+1)*sps)) of one tile (sps even) and writes its partial
+// tile to partial + z*splitk_stride(n, m) in dst's layout.  splitk_sum_kernel
+// then adds the n_split partials in the order z = 0, 1, ... into dst; it is a
+// second launch on the same stream, so the partials are visible to it without
+// any fence, and the sum does not depend on the order the work items ran in.
 template <int QT>
 __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(float* __restrict__ dst,
                                                            const uint8_t* __restrict__ w,
                                                            const float* __restrict__ x, int m,
                                                            int k, int n, int rb, int n_mb,
-                                                           int n_nb) {
+                                                           int n_nb, int n_split, int sps,
+                                                           float* __restrict__ partial) {
     __shared__ __attribute__((aligned(16))) _Float16 sA[2][BM * LDK];
     __shared__ __attribute__((aligned(16))) _Float16 sB[2][BN * LDK];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // Work groups are dealt round-robin to the 8 XCDs (id % 8); give each XCD
-    // a contiguous run of tiles so the tiles that share weight rows share an L2.
-    const int T = n_mb * n_nb, L = blockIdx.x;
-    const int xcd = L & 7, idx = L >> 3, per = T >> 3, rem = T & 7;
-    const int tile = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    // a contiguous run of work items so the tiles that share weight rows (and
+    // the same k range) share an L2.
+    const int T = n_mb * n_nb, NI = T * n_split, L = blockIdx.x;
+    const int xcd = L & 7, idx = L >> 3, per = NI >> 3, rem = NI & 7;
+    const int item = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    const int z = item / T, tile = item - z * T;
     const int mb = tile / n_nb, nb = tile - mb * n_nb;
     const int64_t m0 = (int64_t)mb * BM, n0 = (int64_t)nb * BN;
 
@@ -305,7 +315,10 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(float* __restrict__ d
     const rsrc_t xr = make_rsrc(x + n0 * k, (uint32_t)ntok * (uint32_t)k * 4u);
     const int arow = tid >> 1, part = tid & 1;
     const uint32_t roff = (uint32_t)((m0 + arow) * rb - base);
-    const int nk = (k + BK - 1) / BK;
+    const int nk_all = (k + BK - 1) / BK;
+    const int s0 = z * sps;
+    const int nk = min(nk_all, s0 + sps);     // steps at or past nk read zeros
+    const int kend = min(k, nk * BK);         // so do k positions at or past kend
     const int lds_a = arow * LDK + part * 32;
     constexpr int H = Perm<QT>::H;
 
@@ -326,10 +339,10 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(float* __restrict__ d
     // out-of-range offsets, and their staged tiles are never used), so the
     // loop body is straight-line and the compiler's load counters let the
     // loads of step kt+2 stay in flight while step kt computes.
-    al0.load(wr, roff, 0, part, k, nk);
-    xl0.template load<H>(xr, k, 0, tid);
-    al1.load(wr, roff, 1, part, k, nk);
-    xl1.template load<H>(xr, k, 1, tid);
+    al0.load(wr, roff, s0, part, kend, nk);
+    xl0.template load<H>(xr, k, kend, s0, tid);
+    al1.load(wr, roff, s0 + 1, part, kend, nk);
+    xl1.template load<H>(xr, k, kend, s0 + 1, tid);
     stage(al0, xl0, 0);
     __syncthreads();
 
@@ -362,24 +375,26 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(float* __restrict__ d
     // An odd step count runs one extra step whose weight and activation tiles
     // are all zeros (out-of-range loads): it adds exactly 0 to every sum and
     // keeps a single loop exit, so the accumulators stay in place.
-    const int nk2 = (nk + 1) & ~1;
-    for (int kt = 0; kt < nk2; kt += 2) {
+    const int nk2 = s0 + ((nk - s0 + 1) & ~1);
+    for (int kt = s0; kt < nk2; kt += 2) {
         // step kt: buffer 0; set 1 holds step kt+1, set 0 takes kt+2
-        al0.load(wr, roff, kt + 2, part, k, nk);
-        xl0.template load<H>(xr, k, kt + 2, tid);
+        al0.load(wr, roff, kt + 2, part, kend, nk);
+        xl0.template load<H>(xr, k, kend, kt + 2, tid);
         mfma_step(0);
         stage(al1, xl1, 1);
         __syncthreads();
         // step kt+1: buffer 1; set 0 holds step kt+2, set 1 takes kt+3
-        al1.load(wr, roff, kt + 3, part, k, nk);
-        xl1.template load<H>(xr, k, kt + 3, tid);
+        al1.load(wr, roff, kt + 3, part, kend, nk);
+        xl1.template load<H>(xr, k, kend, kt + 3, tid);
         mfma_step(1);
         stage(al0, xl0, 0);
         __syncthreads();
     }
 
+
     // D[row][col] of a 16x16 tile sits in lane (row/4)*16 + col, element row%4:
     // rows are weight rows (contiguous in dst), cols are tokens.
+    float* out = n_split > 1 ? partial + (int64_t)z * splitk_stride(n, m) : dst;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -387,7 +402,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(float* __restrict__ d
             const int64_t mrow = m0 + wm * 64 + i * 16 + (lane >> 4) * 4;
             const int64_t tok = n0 + wn * 64 + j * 16 + (lane & 15);
             if (tok < n) {
-                float* p = dst + tok * m + mrow;
+                float* p = out + tok * m + mrow;
                 const f32x4 v = acc[i][j];
                 if ((m & 3) == 0 && mrow + 4 <= m) {
                     *(f32x4*)p = v;
@@ -401,24 +416,85 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(float* __restrict__ d
     }
 }
 
+// dst[i] = part[0][i] + part[1][i] + ... + part[n_split-1][i], in that
+// order, for i < count; part[z] starts at z * splitk_stride (16-byte aligned).
+__global__ __launch_bounds__(256) void splitk_sum_kernel(float* __restrict__ dst,
+                                                         const float* __restrict__ part,
+                                                         int64_t count, int64_t zstride, int n_split) {
+    const int64_t n4 = count >> 2;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+        f32x4 v = reinterpret_cast<const f32x4*>(part)[i];
+        for (int z = 1; z < n_split; ++z) v += reinterpret_cast<const f32x4*>(part + z * zstride)[i];
+        reinterpret_cast<f32x4*>(dst)[i] = v;
+    }
+    for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += stride) {
+        float v = part[i];
+        for (int z = 1; z < n_split; ++z) v += part[z * zstride + i];
+        dst[i] = v;
+    }
+}
+
 template <int QT>
 static void launch_qt(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k, int64_t n,
-                      int64_t rb, hipStream_t st) {
+                      int64_t rb, const MfmaPlan& pl, void* ws, hipStream_t st) {
     const int n_mb = (int)((m + BM - 1) / BM), n_nb = (int)((n + BN - 1) / BN);
-    gemm_mfma_kernel<QT><<<dim3((unsigned)(n_mb * n_nb)), 256, 0, st>>>(
-        dst, w, x, (int)m, (int)k, (int)n, (int)rb, n_mb, n_nb);
+    gemm_mfma_kernel<QT><<<dim3((unsigned)(n_mb * n_nb * pl.n_split)), 256, 0, st>>>(
+        dst, w, x, (int)m, (int)k, (int)n, (int)rb, n_mb, n_nb, pl.n_split, pl.sps, (float*)ws);
+    if (pl.n_split > 1) {
+        const int64_t count = n * m;
+        int64_t blocks = (count / 4 + 255) / 256;
+        if (blocks > 4096) blocks = 4096;
+        if (blocks < 1) blocks = 1;
+        splitk_sum_kernel<<<dim3((unsigned)blocks), 256, 0, st>>>(dst, (const float*)ws, count,
+                                                                 splitk_stride(n, m), pl.n_split);
+    }
+}
+
+MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int num_cu) {
+    MfmaPlan best;
+    const int64_t T = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+    const int nk = (int)((k + BK - 1) / BK);
+    best.n_split = 1;
+    best.sps = nk + (nk & 1);
+    best.ws_bytes = 0;
+    if (T >= num_cu || nk < 4) return best;
+    // Estimated time in k steps of one work group: (rounds of work groups
+    // over the CUs) x (steps per item), plus for a split the second launch
+    // and the partials' traffic (written once, read once; dst written once).
+    constexpr double STEP_US = 1.3, LAUNCH_US = 2.0, BYTES_PER_US = 4.0e6;
+    const double out_bytes = 4.0 * (double)n * (double)m;
+    double best_cost = 1e30;
+    for (int S = 1; S <= 16 && S <= nk / 2; ++S) {
+        const int sps = ((nk + S - 1) / S + 1) & ~1;
+        const int se = (nk + sps - 1) / sps;
+        if (S > 1 && se < 2) continue;
+        const int64_t rounds = (T * se + num_cu - 1) / num_cu;
+        const double extra = se > 1 ? (LAUNCH_US + (2.0 * se + 1.0) * out_bytes / BYTES_PER_US) / STEP_US : 0.0;
+        const double cost = (double)rounds * sps + extra;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best.n_split = se;
+            best.sps = sps;
+        }
+    }
+    if (best.n_split > 1)
+        best.ws_bytes = (int64_t)best.n_split * splitk_stride(n, m) * 4;
+    else
+        best.sps = nk + (nk & 1);
+    return best;
 }
 
 void launch_gemm_mfma(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
-                      int qt, int64_t rb, hipStream_t st) {
+                      int qt, int64_t rb, const MfmaPlan& pl, void* ws, hipStream_t st) {
     const uint8_t* wb = (const uint8_t*)w;
     switch (qt) {
-        case QT_F32: launch_qt<QT_F32>(dst, wb, x, m, k, n, rb, st); break;
-        case QT_Q4_0: launch_qt<QT_Q4_0>(dst, wb, x, m, k, n, rb, st); break;
-        case QT_Q8_0: launch_qt<QT_Q8_0>(dst, wb, x, m, k, n, rb, st); break;
-        case QT_Q4_K: launch_qt<QT_Q4_K>(dst, wb, x, m, k, n, rb, st); break;
-        case QT_Q6_K: launch_qt<QT_Q6_K>(dst, wb, x, m, k, n, rb, st); break;
-        case QT_NVFP4: launch_qt<QT_NVFP4>(dst, wb, x, m, k, n, rb, st); break;
+        case QT_F32: launch_qt<QT_F32>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
+        case QT_Q4_0: launch_qt<QT_Q4_0>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
+        case QT_Q8_0: launch_qt<QT_Q8_0>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
+        case QT_Q4_K: launch_qt<QT_Q4_K>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
+        case QT_Q6_K: launch_qt<QT_Q6_K>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
+        case QT_NVFP4: launch_qt<QT_NVFP4>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
     }
 }
 

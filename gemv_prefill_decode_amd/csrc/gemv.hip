@@ -356,15 +356,30 @@ struct XGlobal {
 };
 
 // Stage rows xoff[j] (j < NT) of x (row length k) into LDS in the padded
-// layout.  All threads of the work group take part; ends with a barrier.
+// layout.  All threads of the work group take part, each with at least 8
+// independent 16-byte loads in flight per batch; ends with a barrier.
 template <int NT>
 __device__ __forceinline__ void stage_x(float* sx, rsrc_t xr, const uint32_t (&xoff)[NT], int k) {
+    constexpr int U = NT >= 8 ? 1 : 8 / NT;  // float4 columns per thread per batch
     const int ld = xpad_len(k);
     const int per = k >> 2;  // float4 per row
-    for (int i = threadIdx.x; i < NT * per; i += 256) {
-        const int j = i / per, e = (i - j * per) << 2;
-        const f32x4 v = __builtin_bit_cast(f32x4, ld128(xr, xoff[j] + 4u * (uint32_t)e));
-        *(f32x4*)(sx + j * ld + xpad(e)) = v;
+    for (int c0 = threadIdx.x; c0 < per; c0 += 256 * U) {
+        f32x4 v[NT][U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + 256 * u;
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                v[j][u] = __builtin_bit_cast(
+                    f32x4, ld128(xr, c < per ? xoff[j] + 16u * (uint32_t)c : OOB_OFF));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + 256 * u;
+            if (c < per)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) *(f32x4*)(sx + j * ld + xpad(4 * c)) = v[j][u];
+        }
     }
     __syncthreads();
 }
@@ -453,6 +468,10 @@ __device__ __forceinline__ void compute_item(GUnit<QT> (&un)[R], const typename 
 }
 
 // Issue the loads of item (row group rg, unit iteration uu) into un[].
+// Callers issue every ring refill, also for items past the end (live =
+// false), so that the number of loads issued after any item is the same on
+// every path and the compiler's wait before an item counts only that item's
+// loads, not all of those in flight.
 // The descriptor covers the row group's rows from the 16-byte boundary at or
 // below its first byte (wave-uniform, scalar registers); a lane's offset is
 // its per-lane row/unit constant plus the group's sub-16 remainder and uu
@@ -460,11 +479,12 @@ __device__ __forceinline__ void compute_item(GUnit<QT> (&un)[R], const typename 
 template <int QT, int R>
 __device__ __forceinline__ void issue_item(GUnit<QT> (&un)[R], const StreamGeom& g, int RG,
                                            uint32_t lane_row_off, const typename GUnit<QT>::Lane& ln,
-                                           int rg, int uu, int e) {
+                                           int rg, int uu, int e, bool live) {
     const int64_t row0 = (int64_t)rg * RG;
     const int64_t byte0 = row0 * g.rb;
-    const int64_t base = byte0 & ~(int64_t)15;
-    const int64_t end = imin64(g.m, row0 + RG) * g.rb;
+    // an item past the end gets an empty descriptor: its loads return zeros
+    const int64_t base = live ? byte0 & ~(int64_t)15 : 0;
+    const int64_t end = live ? imin64(g.m, row0 + RG) * g.rb : 0;
     const rsrc_t wr = make_rsrc(g.w + base, (uint32_t)((end - base + 15) & ~(int64_t)15));
     const uint32_t off0 = lane_row_off + (uint32_t)(byte0 & 15) + ln.boff +
                           (uint32_t)uu * GUnit<QT>::ustep(1 << g.lpr_log2);
@@ -479,9 +499,16 @@ __device__ __forceinline__ void issue_item(GUnit<QT> (&un)[R], const StreamGeom&
 // of register sets (slot it % D, indexed at compile time); a slot is refilled
 // with item it + D right after item it is consumed.  store(row, j, value) is
 // called by lane gl == 0 of each lane group for every row (rows >= m too).
-template <int QT, int NT, int R, int D, typename XS, typename Store>
+struct NoPre {
+    __device__ void operator()() const {}
+};
+
+// pre() is called by every wave once the ring's first loads are issued (the
+// work group's activation staging, with its barrier, goes there so that it
+// overlaps the first weight loads).
+template <int QT, int NT, int R, int D, typename XS, typename Store, typename Pre = NoPre>
 __device__ __forceinline__ void gemv_stream(const StreamGeom& g, int first_rg, int rg_stride,
-                                            int n_rg, const XS& xs, Store store) {
+                                            int n_rg, const XS& xs, Store store, Pre pre = {}) {
     using UT = GUnit<QT>;
     const int lane = threadIdx.x & 63;
     const int lpr = 1 << g.lpr_log2;
@@ -489,8 +516,7 @@ __device__ __forceinline__ void gemv_stream(const StreamGeom& g, int first_rg, i
     const int RG = (64 >> g.lpr_log2) * R;
     const int U = (g.k + UT::UE - 1) / UT::UE;
     const int upl = (U + lpr - 1) >> g.lpr_log2;
-    if (first_rg >= n_rg) return;
-    const int n_items = (n_rg - first_rg + rg_stride - 1) / rg_stride * upl;
+    const int n_items = first_rg < n_rg ? (n_rg - first_rg + rg_stride - 1) / rg_stride * upl : 0;
     const typename UT::Lane ln = UT::lane(gl);
     const uint32_t lane_row_off = (uint32_t)(slot * R) * (uint32_t)g.rb;
     const int e_step = lpr * UT::UE;
@@ -501,48 +527,73 @@ __device__ __forceinline__ void gemv_stream(const StreamGeom& g, int first_rg, i
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[rr][j] = 0.0f;
 
+    // row group of item it complete: lane-group reduction, store, reset
+    auto finish = [&](int q) {
+        for (int off = lpr >> 1; off > 0; off >>= 1)
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) acc[rr][j] += __shfl_xor(acc[rr][j], off, 64);
+        if (gl == 0) {
+            const int64_t r0 = (int64_t)(first_rg + q * rg_stride) * RG + slot * R;
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) store(r0 + rr, j, acc[rr][j]);
+        }
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) acc[rr][j] = 0.0f;
+    };
+
     UT ring[D][R];
+    if (n_items <= D) {
+        // Short stream: every item's loads are in flight before the first
+        // is consumed.
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (d < n_items) {
+                const int q = d / upl, uu = d - q * upl;
+                issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q * rg_stride, uu,
+                                  ln.e + uu * e_step, true);
+            }
+        }
+        pre();
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (d < n_items) {
+                const int q = d / upl, uu = d - q * upl;
+                if (gl + lpr * uu < U)
+                    compute_item<QT, NT, R>(ring[d], ln, ln.e + uu * e_step, g.k, xs, acc);
+                if (uu == upl - 1) finish(q);
+            }
+        }
+        return;
+    }
+    // Long stream: a ring of D items.  Every refill is issued, also for items
+    // past the end (they read nothing), so the wait before an item counts
+    // only the loads issued after it on every path.
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        if (d < n_items) {
-            const int q = d / upl, uu = d - q * upl;
-            issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q * rg_stride, uu,
-                              ln.e + uu * e_step);
-        }
+        const int q = d / upl, uu = d - q * upl;
+        issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q * rg_stride, uu,
+                          ln.e + uu * e_step, true);
     }
+    pre();
     for (int base = 0; base < n_items; base += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int it = base + d;
-            if (it < n_items) {  // wave-uniform
-                const int q = it / upl, uu = it - q * upl;
-                if (gl + lpr * uu < U)
-                    compute_item<QT, NT, R>(ring[d], ln, ln.e + uu * e_step, g.k, xs, acc);
-                const int nx = it + D;
-                if (nx < n_items) {
-                    const int q2 = nx / upl, uu2 = nx - q2 * upl;
-                    issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q2 * rg_stride,
-                                      uu2, ln.e + uu2 * e_step);
-                }
-                if (uu == upl - 1) {  // row group complete: reduce, store, reset
-                    for (int off = lpr >> 1; off > 0; off >>= 1)
-#pragma unroll
-                        for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-                            for (int j = 0; j < NT; ++j) acc[rr][j] += __shfl_xor(acc[rr][j], off, 64);
-                    if (gl == 0) {
-                        const int64_t r0 = (int64_t)(first_rg + q * rg_stride) * RG + slot * R;
-#pragma unroll
-                        for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-                            for (int j = 0; j < NT; ++j) store(r0 + rr, j, acc[rr][j]);
-                    }
-#pragma unroll
-                    for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-                        for (int j = 0; j < NT; ++j) acc[rr][j] = 0.0f;
-                }
-            }
+            const bool live = it < n_items;  // wave-uniform
+            const int q = it / upl, uu = it - q * upl;
+            if (live && gl + lpr * uu < U)
+                compute_item<QT, NT, R>(ring[d], ln, ln.e + uu * e_step, g.k, xs, acc);
+            const int nx = it + D;
+            const int q2 = nx / upl, uu2 = nx - q2 * upl;
+            issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q2 * rg_stride, uu2,
+                              ln.e + uu2 * e_step, nx < n_items);
+            if (live && uu == upl - 1) finish(q);
         }
     }
 }
@@ -570,9 +621,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(float* __restrict__ dst,
         if (row < m && j < ntok) out[(int64_t)j * m + row] = v;
     };
     if constexpr (XL) {
-        stage_x<NT>(qmm_dyn_lds, xr, xoff, k);
         const XLds<NT> xs{qmm_dyn_lds, xpad_len(k)};
-        gemv_stream<QT, NT, R, D>(g, blockIdx.x * 4 + wave, gridDim.x * 4, n_rg, xs, store);
+        gemv_stream<QT, NT, R, D>(g, blockIdx.x * 4 + wave, gridDim.x * 4, n_rg, xs, store,
+                                  [&]() { stage_x<NT>(qmm_dyn_lds, xr, xoff, k); });
     } else {
         XGlobal<NT> xs;
         xs.xr = xr;
@@ -593,6 +644,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(float* __restrict__ dst,
 // check.  The decision depends on expert_ids only.
 constexpr int MOE_CHUNK = 256;  // pairs examined (and gathered) per pass
 constexpr int MOE_NT = 3;       // token rows staged in LDS at a time
+constexpr unsigned MOE_MIN_WG = 32;  // work groups per (pair, plane) at least
 
 template <int QT, int NT, int R, int D, bool XL>
 __device__ __forceinline__ void moe_tokens(float* __restrict__ out, const float* __restrict__ scale,
@@ -615,9 +667,9 @@ __device__ __forceinline__ void moe_tokens(float* __restrict__ out, const float*
     };
     if constexpr (XL) {
         __syncthreads();  // the previous chunk's waves are done with the staged x
-        stage_x<NT>(qmm_dyn_lds, xr, xoff, in_f);
         const XLds<NT> xs{qmm_dyn_lds, xpad_len(in_f)};
-        gemv_stream<QT, NT, R, D>(g, blockIdx.x * 4 + wave, gridDim.x * 4, n_rg, xs, store);
+        gemv_stream<QT, NT, R, D>(g, blockIdx.x * 4 + wave, gridDim.x * 4, n_rg, xs, store,
+                                  [&]() { stage_x<NT>(qmm_dyn_lds, xr, xoff, in_f); });
     } else {
         XGlobal<NT> xs;
         xs.xr = xr;
@@ -748,52 +800,68 @@ __global__ __launch_bounds__(256) void loadonly_kernel(uint32_t* __restrict__ si
     const int U = (k + UT::UE - 1) / UT::UE;
     const int upl = (U + lpr - 1) >> lpr_log2;
     const int first_rg = blockIdx.x * 4 + wave, rg_stride = gridDim.x * 4;
-    if (first_rg >= n_rg) return;
-    const int n_items = (n_rg - first_rg + rg_stride - 1) / rg_stride * upl;
+    const int n_items = first_rg < n_rg ? (n_rg - first_rg + rg_stride - 1) / rg_stride * upl : 0;
     const typename UT::Lane ln = UT::lane(gl);
     const uint32_t lane_row_off = (uint32_t)(slot * R) * (uint32_t)rb;
     const int e_step = lpr * UT::UE;
     uint32_t acc[R];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) acc[rr] = 0;
+    auto finish = [&](int q) {
+        for (int off = lpr >> 1; off > 0; off >>= 1)
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) acc[rr] ^= __shfl_xor(acc[rr], off, 64);
+        if (gl == 0)
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) {
+                const int64_t row = (int64_t)(first_rg + q * rg_stride) * RG + slot * R + rr;
+                if (row < m) sink[row] = acc[rr];
+            }
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) acc[rr] = 0;
+    };
     UT ring[D][R];
+    if (n_items <= D) {  // short stream, as in gemv_stream
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (d < n_items) {
+                const int q = d / upl, uu = d - q * upl;
+                issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q * rg_stride, uu,
+                                  ln.e + uu * e_step, true);
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (d < n_items) {
+                const int q = d / upl, uu = d - q * upl;
+                if (gl + lpr * uu < U)
+#pragma unroll
+                    for (int rr = 0; rr < R; ++rr) acc[rr] ^= raw_xor(ring[d][rr]);
+                if (uu == upl - 1) finish(q);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        if (d < n_items) {
-            const int q = d / upl, uu = d - q * upl;
-            issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q * rg_stride, uu,
-                              ln.e + uu * e_step);
-        }
+        const int q = d / upl, uu = d - q * upl;
+        issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q * rg_stride, uu,
+                          ln.e + uu * e_step, true);
     }
     for (int base = 0; base < n_items; base += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int it = base + d;
-            if (it < n_items) {
-                const int q = it / upl, uu = it - q * upl;
-                if (gl + lpr * uu < U)
+            const bool live = it < n_items;
+            const int q = it / upl, uu = it - q * upl;
+            if (live && gl + lpr * uu < U)
 #pragma unroll
-                    for (int rr = 0; rr < R; ++rr) acc[rr] ^= raw_xor(ring[d][rr]);
-                const int nx = it + D;
-                if (nx < n_items) {
-                    const int q2 = nx / upl, uu2 = nx - q2 * upl;
-                    issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q2 * rg_stride,
-                                      uu2, ln.e + uu2 * e_step);
-                }
-                if (uu == upl - 1) {
-                    for (int off = lpr >> 1; off > 0; off >>= 1)
-#pragma unroll
-                        for (int rr = 0; rr < R; ++rr) acc[rr] ^= __shfl_xor(acc[rr], off, 64);
-                    if (gl == 0)
-#pragma unroll
-                        for (int rr = 0; rr < R; ++rr) {
-                            const int64_t row = (int64_t)(first_rg + q * rg_stride) * RG + slot * R + rr;
-                            if (row < m) sink[row] = acc[rr];
-                        }
-#pragma unroll
-                    for (int rr = 0; rr < R; ++rr) acc[rr] = 0;
-                }
-            }
+                for (int rr = 0; rr < R; ++rr) acc[rr] ^= raw_xor(ring[d][rr]);
+            const int nx = it + D;
+            const int q2 = nx / upl, uu2 = nx - q2 * upl;
+            issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q2 * rg_stride, uu2,
+                              ln.e + uu2 * e_step, nx < n_items);
+            if (live && uu == upl - 1) finish(q);
         }
     }
 }
@@ -850,8 +918,20 @@ static unsigned stream_grid(int64_t n_rg, int64_t sets, const GemvTuning& tune) 
     return (unsigned)(need < target ? need : target);
 }
 
-// Activations are staged in LDS when NT rows of them fit this budget.
+// Activations are staged in LDS when NT rows of them fit what one work group
+// may allocate; the MoE kernel keeps to 64 KB.
 constexpr int64_t XLDS_MAX_BYTES = 64 * 1024;
+
+// The tuning with wg_per_cu lowered to the work groups of `lds` bytes each
+// that fit in one CU's LDS at once.
+static GemvTuning lds_limited(const GemvTuning& t, int64_t lds) {
+    GemvTuning r = t;
+    if (lds > 0) {
+        const int64_t fit = t.lds_per_cu / lds;
+        r.wg_per_cu = (int)(fit < 1 ? 1 : (fit < t.wg_per_cu ? fit : t.wg_per_cu));
+    }
+    return r;
+}
 
 // (R, D) variants compiled: NT <= 2: (1,4) (1,8) (2,2) (2,4); NT >= 4: (1,2) (1,4) (2,2).
 template <int NT, typename F>
@@ -879,14 +959,16 @@ static void launch_gemv_nt(float* dst, const uint8_t* w, const float* x, int64_t
         const int l = lpr_for(QT, k);
         const int64_t n_rg = (m + rg_rows(l, R) - 1) / rg_rows(l, R);
         const int64_t gy = (n + NT - 1) / NT;
-        const dim3 grid(stream_grid(n_rg, gy, tune), (unsigned)gy);
         const int64_t lds = (int64_t)NT * xpad_len((int)k) * 4;
-        if (lds <= XLDS_MAX_BYTES)
+        if (lds <= tune.lds_per_wg) {
+            const dim3 grid(stream_grid(n_rg, gy, lds_limited(tune, lds)), (unsigned)gy);
             gemv_kernel<QT, NT, R, D, true><<<grid, 256, (size_t)lds, st>>>(
                 dst, w, x, (int)m, (int)k, (int)n, (int)rb, l, (int)n_rg);
-        else
+        } else {
+            const dim3 grid(stream_grid(n_rg, gy, tune), (unsigned)gy);
             gemv_kernel<QT, NT, R, D, false><<<grid, 256, 0, st>>>(
                 dst, w, x, (int)m, (int)k, (int)n, (int)rb, l, (int)n_rg);
+        }
     });
 }
 
@@ -925,9 +1007,14 @@ static void launch_moe_qt(float* g, float* u, const uint8_t* wg, const uint8_t* 
         const int l = lpr_for(QT, in_f);
         const int64_t n_pairs = t * n_used;
         const int64_t n_rg = (n_ff + rg_rows(l, R) - 1) / rg_rows(l, R);
-        // at most one set of work groups per distinct expert and plane is active
+        // at most one set of work groups per distinct expert and plane is
+        // active; with many pairs the sets are not all distinct, so each set
+        // gets at least MOE_MIN_WG work groups
         const int64_t active = 2 * (n_pairs < n_expert ? n_pairs : n_expert);
-        const dim3 grid(stream_grid(n_rg, active, tune), (unsigned)n_pairs, 2);
+        unsigned gx = stream_grid(n_rg, active, tune);
+        const unsigned need = (unsigned)((n_rg + 3) / 4);
+        if (gx < MOE_MIN_WG) gx = need < MOE_MIN_WG ? need : MOE_MIN_WG;
+        const dim3 grid(gx, (unsigned)n_pairs, 2);
         const int64_t lds = (int64_t)MOE_NT * xpad_len((int)in_f) * 4;
         const int xl = lds <= XLDS_MAX_BYTES;
         moe_gateup_kernel<QT, R, D><<<grid, 256, (size_t)(xl ? lds : 0), st>>>(

@@ -67,14 +67,19 @@ int env_int(const char* name, int dflt, int lo, int hi) {
 
 struct TuneState {
     int wg_per_cu = 4;
-    int rows = 1;
-    int depth = 8;
+    int rows = 2;
+    int depth = 4;
     bool bad = false;
 };
 TuneState g_tune;
 std::once_flag g_tune_once;
 std::mutex g_cu_mu;
-int g_cu[64] = {0};
+struct DevProps {
+    int cu = 0;
+    int lds_wg = 0;
+    int lds_cu = 0;
+};
+DevProps g_dev[64];
 
 void parse_tune() {
     const int w = env_int("QMM_GEMV_WG_PER_CU", g_tune.wg_per_cu, 1, 64);
@@ -95,20 +100,26 @@ bool gemv_tuning(qmm::GemvTuning* t) {
     if (g_tune.bad) return false;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    int cu = 0;
+    DevProps p;
     {
         std::lock_guard<std::mutex> lk(g_cu_mu);
-        if (dev >= 0 && dev < 64) cu = g_cu[dev];
+        if (dev >= 0 && dev < 64) p = g_dev[dev];
     }
-    if (cu <= 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-            v = 256;
-        cu = v;
+    if (p.cu <= 0) {
+        // a failed query leaves the conservative value (64 KB of LDS, 256 CUs)
+        auto attr = [dev](hipDeviceAttribute_t a, int dflt) {
+            int v = 0;
+            return hipDeviceGetAttribute(&v, a, dev) == hipSuccess && v > 0 ? v : dflt;
+        };
+        p.cu = attr(hipDeviceAttributeMultiprocessorCount, 256);
+        p.lds_wg = attr(hipDeviceAttributeMaxSharedMemoryPerBlock, 64 * 1024);
+        p.lds_cu = attr(hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, p.lds_wg);
         std::lock_guard<std::mutex> lk(g_cu_mu);
-        if (dev >= 0 && dev < 64) g_cu[dev] = cu;
+        if (dev >= 0 && dev < 64) g_dev[dev] = p;
     }
-    t->num_cu = cu;
+    t->num_cu = p.cu;
+    t->lds_per_wg = p.lds_wg;
+    t->lds_per_cu = p.lds_cu;
     t->wg_per_cu = g_tune.wg_per_cu;
     t->rows = g_tune.rows;
     t->depth = g_tune.depth;
@@ -133,6 +144,61 @@ int check_weights(const void* w, int64_t m, int64_t k, int qt, int64_t* rb) {
     int64_t total;
     if (!mul_ok(m, *rb, &total)) return QMM_ERR_SHAPE;
     return QMM_OK;
+}
+
+// Shared validation of the gemm entry points; resolves AUTO.  On success
+// *rb is the row stride and *path the concrete path.
+int check_gemm(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qtype,
+               int* path, int64_t* rb) {
+    if (!dst || !x) return QMM_ERR_NULL;
+    int st = check_weights(w, m, k, qtype, rb);
+    if (st) return st;
+    if (n < 1) return QMM_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(dst, 16)) return QMM_ERR_ALIGN;
+    if (n > INT_MAX) return QMM_ERR_RANGE;
+    int64_t t1, t2;
+    if (!mul_ok(n, k, &t1) || !mul_ok(n, m, &t2)) return QMM_ERR_SHAPE;
+    if (*path == QMM_PATH_AUTO) {
+        const int lim = qmm_gemv_max_n();
+        if (lim < 0) return QMM_ERR_RANGE;
+        *path = n <= lim ? QMM_PATH_GEMV : QMM_PATH_MFMA;
+    }
+    if (*path == QMM_PATH_GEMV) {
+        // one work group addresses at most this window of w, and 8 token rows of x
+        if (qmm::gemv_max_window_bytes(qtype, k, *rb) >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+        if (8 * k * 4 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+        return QMM_OK;
+    }
+    if (*path == QMM_PATH_MFMA) {
+        if ((int64_t)qmm::MFMA_BM * *rb + 16 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+        if ((int64_t)qmm::MFMA_BN * k * 4 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+        const int64_t tiles = ((m + qmm::MFMA_BM - 1) / qmm::MFMA_BM) * ((n + qmm::MFMA_BN - 1) / qmm::MFMA_BN);
+        // work items (tiles x k splits, at most 16) are counted in int
+        if (tiles > INT_MAX / 16) return QMM_ERR_RANGE;
+        return QMM_OK;
+    }
+    return QMM_ERR_PATH;
+}
+
+int gemm_impl(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qtype,
+              int path, void* ws, int64_t ws_bytes, hipStream_t stream) {
+    int64_t rb;
+    int st = check_gemm(dst, w, x, m, k, n, qtype, &path, &rb);
+    if (st) return st;
+    qmm::GemvTuning tune;
+    if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
+    if (path == QMM_PATH_GEMV) {
+        qmm::launch_gemv(dst, w, x, m, k, n, qtype, rb, tune, stream);
+        return launch_status();
+    }
+    qmm::MfmaPlan pl = qmm::plan_gemm_mfma(m, k, n, tune.num_cu);
+    if (ws) {
+        if (!aligned(ws, 256)) return QMM_ERR_ALIGN;
+        if (ws_bytes < pl.ws_bytes) return QMM_ERR_WORKSPACE;
+    }
+    if (pl.n_split > 1 && !ws) pl = qmm::plan_gemm_mfma(m, k, n, 0);  // no workspace: no split
+    qmm::launch_gemm_mfma(dst, w, x, m, k, n, qtype, rb, pl, ws, stream);
+    return launch_status();
 }
 
 }  // namespace
@@ -168,44 +234,35 @@ const char* qmm_status_str(int s) {
         case QMM_ERR_LAUNCH: return "kernel launch failed";
         case QMM_ERR_PATH: return "unknown kernel path";
         case QMM_ERR_RANGE: return "size outside the kernels' index range (or bad QMM_GEMV_MAX_N)";
+        case QMM_ERR_WORKSPACE: return "workspace smaller than qmm_gemm_workspace_bytes()";
     }
     return "unknown status";
 }
 
-int qmm_gemm_path(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
-                  int qtype, int path, hipStream_t stream) {
-    if (!dst || !x) return QMM_ERR_NULL;
-    int64_t rb;
-    int st = check_weights(w, m, k, qtype, &rb);
-    if (st) return st;
-    if (n < 1) return QMM_ERR_SHAPE;
-    if (!aligned(x, 16) || !aligned(dst, 16)) return QMM_ERR_ALIGN;
-    if (n > INT_MAX) return QMM_ERR_RANGE;
-    int64_t t1, t2;
-    if (!mul_ok(n, k, &t1) || !mul_ok(n, m, &t2)) return QMM_ERR_SHAPE;
+int64_t qmm_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int qtype, int path) {
+    if (!valid_qt(qtype)) return -QMM_ERR_QTYPE;
+    if (m < 1 || k < 1 || n < 1) return -QMM_ERR_SHAPE;
+    if (m > INT_MAX || k > INT_MAX || n > INT_MAX) return -QMM_ERR_RANGE;
     if (path == QMM_PATH_AUTO) {
         const int lim = qmm_gemv_max_n();
-        if (lim < 0) return QMM_ERR_RANGE;
+        if (lim < 0) return -QMM_ERR_RANGE;
         path = n <= lim ? QMM_PATH_GEMV : QMM_PATH_MFMA;
     }
-    if (path == QMM_PATH_GEMV) {
-        // one work group addresses at most this window of w, and 8 token rows of x
-        if (qmm::gemv_max_window_bytes(qtype, k, rb) >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
-        if (8 * k * 4 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
-        qmm::GemvTuning tune;
-        if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
-        qmm::launch_gemv(dst, w, x, m, k, n, qtype, rb, tune, stream);
-        return launch_status();
-    }
-    if (path == QMM_PATH_MFMA) {
-        if ((int64_t)qmm::MFMA_BM * rb + 16 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
-        if ((int64_t)qmm::MFMA_BN * k * 4 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
-        const int64_t tiles = ((m + qmm::MFMA_BM - 1) / qmm::MFMA_BM) * ((n + qmm::MFMA_BN - 1) / qmm::MFMA_BN);
-        if (tiles > INT_MAX) return QMM_ERR_RANGE;
-        qmm::launch_gemm_mfma(dst, w, x, m, k, n, qtype, rb, stream);
-        return launch_status();
-    }
-    return QMM_ERR_PATH;
+    if (path == QMM_PATH_GEMV) return 0;
+    if (path != QMM_PATH_MFMA) return -QMM_ERR_PATH;
+    qmm::GemvTuning tune;
+    if (!gemv_tuning(&tune)) return -QMM_ERR_RANGE;
+    return qmm::plan_gemm_mfma(m, k, n, tune.num_cu).ws_bytes;
+}
+
+int qmm_gemm_ws(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qtype,
+                int path, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    return gemm_impl(dst, w, x, m, k, n, qtype, path, workspace, workspace_bytes, stream);
+}
+
+int qmm_gemm_path(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
+                  int qtype, int path, hipStream_t stream) {
+    return gemm_impl(dst, w, x, m, k, n, qtype, path, nullptr, 0, stream);
 }
 
 int qmm_gemm(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qtype,

@@ -58,7 +58,8 @@ typedef enum {
     QMM_ERR_ALIGN = 5,     /* w not 16-byte aligned, or x/dst not 16-byte aligned */
     QMM_ERR_LAUNCH = 6,    /* the runtime reported a launch error              */
     QMM_ERR_PATH = 7,      /* unknown path selector                            */
-    QMM_ERR_RANGE = 8      /* a size exceeds what the kernels index (see below) */
+    QMM_ERR_RANGE = 8,     /* a size exceeds what the kernels index (see below) */
+    QMM_ERR_WORKSPACE = 9  /* workspace smaller than qmm_gemm_workspace_bytes()  */
 } qmm_status;
 
 /* Kernel path selector for qmm_gemm_path. */
@@ -81,8 +82,11 @@ typedef enum {
  * within 1e-5 * sum|w*x| of the exact value), otherwise the MFMA kernel,
  * which rounds W and x to f16 (RNE) and accumulates in f32 (within
  * 2e-3 * sum|w*x|).
- * Limits: m*row_bytes and n*k*4 each below 2^31 per 128-row / 128-token tile
- * window; m, n, k below 2^31.  Larger values return QMM_ERR_RANGE.
+ * Limits: the bytes of one 128-row weight tile (or one GEMV row group) and
+ * of 128 (GEMV: 8) token rows of x each below 2^31; m, n, k below 2^31.
+ * Larger values return QMM_ERR_RANGE.
+ * qmm_gemm never splits k on the MFMA path (it has no workspace); products
+ * with few output tiles run faster through qmm_gemm_ws.
  */
 int qmm_gemm(float* dst, const void* w, const float* x,
              int64_t m, int64_t k, int64_t n, int qtype, hipStream_t stream);
@@ -92,6 +96,30 @@ int qmm_gemm(float* dst, const void* w, const float* x,
 int qmm_gemm_path(float* dst, const void* w, const float* x,
                   int64_t m, int64_t k, int64_t n, int qtype, int path,
                   hipStream_t stream);
+
+/*
+ * qmm_gemm_ws: qmm_gemm_path with a caller-owned workspace for the MFMA
+ * path.  When the product has fewer 128x128 output tiles than the device has
+ * compute units, k is split into ranges handled by separate work groups that
+ * write partial results to the workspace; a second kernel on the same stream
+ * adds the partials in a fixed order (two identical calls still give
+ * bit-identical results) and writes dst.
+ *   workspace        DEVICE memory, 256-byte aligned, of at least
+ *                    qmm_gemm_workspace_bytes(m, k, n, qtype, path) bytes, or
+ *                    NULL (then k is never split).  No initial contents are
+ *                    needed.  Calls that share a workspace must not overlap
+ *                    (order them on one stream).
+ *   workspace_bytes  its size; smaller than needed -> QMM_ERR_WORKSPACE.
+ * The GEMV path ignores the workspace.  Other arguments and errors as
+ * qmm_gemm_path.
+ */
+int qmm_gemm_ws(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
+                int qtype, int path, void* workspace, int64_t workspace_bytes,
+                hipStream_t stream);
+
+/* Workspace bytes qmm_gemm_ws uses for this product on the current device
+ * (0 when k is not split, or on the GEMV path); < 0 is -qmm_status. */
+int64_t qmm_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int qtype, int path);
 
 /*
  * qmm_moe_gateup: the MoE gate and up projections over the routed experts

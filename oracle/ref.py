@@ -83,6 +83,32 @@ def moe_ref(name: str, w_gate, w_up, ids, scales, x, n_expert: int, in_f: int, n
     return outs[0][0], outs[1][0], outs[0][1], outs[1][1]
 
 
+def moe_ref_pairs_rows(name: str, w_plane, ids, scales, x, plane: int, n_expert: int, in_f: int,
+                       n_ff: int, pairs, rows):
+    """(ref, S) of out_P[pairs[t], rows[t]] for one plane P, sampled: only the
+    sampled weight rows of the chosen experts are decoded."""
+    ids = np.asarray(ids, dtype=np.int64)
+    t, n_used = ids.shape
+    n_pairs = t * n_used
+    pairs = np.asarray(pairs, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    buf = np.asarray(w_plane).reshape(-1).view(np.uint8)
+    rb = buf.size // (n_expert * n_ff)
+    X = np.asarray(x, dtype=np.float32).reshape(t, in_f).astype(np.float64)
+    sc = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    val = np.empty(len(pairs))
+    tol = np.empty(len(pairs))
+    for i, (p, r) in enumerate(zip(pairs, rows)):
+        e = int(ids.reshape(-1)[p])
+        row = (e * n_ff + int(r)) * rb
+        W = decode(name, buf[row:row + rb], 1, in_f)[0]
+        xv = X[p // n_used]
+        f = sc[plane * n_pairs + p]
+        val[i] = f * float(W @ xv)
+        tol[i] = abs(f) * float(np.abs(W) @ np.abs(xv))
+    return val, tol
+
+
 def tolerance_check(got, ref, S, tau: float):
     """(ok, worst) where worst = max |got - ref| / (tau * S) over the outputs
     (a ratio <= 1 passes).  Any non-finite value in ``got`` fails outright:

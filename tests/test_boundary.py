@@ -125,3 +125,30 @@ def test_default_gemv_max_n():
     if "QMM_GEMV_MAX_N" in os.environ:
         pytest.skip("QMM_GEMV_MAX_N set in the environment")
     assert lib.qmm_gemv_max_n() == 32
+
+
+def test_workspace_bytes_plan_and_errors():
+    """Split-k workspace sizes: few-tile products get one, many-tile products
+    and the GEMV path none; bad arguments give -status."""
+    lib = _lib()
+    f = lib.qmm_gemm_workspace_bytes
+    assert f(1024, 4608, 512, 3, 2) > 0          # 32 output tiles
+    assert f(14336, 4096, 2048, 3, 2) == 0       # 1792 output tiles
+    assert f(4096, 4096, 8, 3, 1) == 0           # GEMV path
+    assert f(4096, 4096, 8, 3, 0) == 0           # AUTO -> GEMV at n = 8
+    assert f(10, 256, 40, 9, 2) == -4
+    assert f(0, 256, 40, 3, 2) == -2
+    assert f(10, 256, 40, 3, 7) == -7
+    ws = f(1024, 4608, 512, 3, 2)
+    assert ws % 256 == 0
+
+
+def test_gemm_ws_validates_before_launch():
+    lib = _lib()
+    import ctypes
+    buf = ctypes.create_string_buffer(64)
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    # null dst / x
+    assert lib.qmm_gemm_ws(None, p, p, 10, 256, 40, 3, 2, None, 0, None) == 1
+    # unknown path
+    assert lib.qmm_gemm_ws(p, p, p, 10, 256, 40, 3, 9, None, 0, None) in (5, 7)

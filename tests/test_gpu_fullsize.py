@@ -1,0 +1,101 @@
+"""GPU parity at the benchmarked sizes, in the launch configurations bench.py
+times: the outputs are compared with the oracle on samples it computes one
+by one (always including the four corners), on the same seeded inputs.
+
+  - Q4_0 GEMM m=1024 k=1024 n=64 (auto dispatch, the matrix-core path), whole output
+  - LFM2.5-350M-shaped prefill n=512: 4 shapes x f32/q4_0/q8_0/q4_k/q6_k
+  - decode sweep n in {1,4,8,16,32}: q4_k/q6_k at 4608x1024 and 14336x4096
+  - NVFP4 MoE gate/up: 64 experts, 8 used, in_f 4096, n_ff 2048, t in {1,16}
+  - 8B-class prefill n=2048: q4_k/q6_k at 14336x4096 and 4096x14336
+"""
+
+import numpy as np
+import pytest
+
+from gpu_helpers import TAU_F16, TAU_F32, check_full, check_sampled, gpu_gemm, note, to_dev, weights
+from oracle import ref
+from synth import gen
+
+pytestmark = pytest.mark.gpu
+
+LFM2 = [("ffn_gate", 4608, 1024), ("ffn_down", 1024, 4608), ("conv_in", 3072, 1024),
+        ("attn_out", 1024, 1024)]
+PREFILL_QTS = ["f32", "q4_0", "q8_0", "q4_k", "q6_k"]
+
+
+def bench_acts(n, k):
+    """The prefill activations bench.py uses (one seed per k)."""
+    return gen.unit_f32(n * k, gen.SEED_X + k).reshape(n, k)
+
+
+def test_q4_0_gemm_1024_n64_whole_output():
+    m = k = 1024
+    n = 64
+    note("q4_0 1024x1024 n=64 auto")
+    w = weights("q4_0", m, k, 0)
+    x = gen.unit_f32(n * k, gen.SEED_X).reshape(n, k)
+    got = gpu_gemm("q4_0", w, x, m, "auto")
+    check_full("q4_0", w, x, m, k, n, got, TAU_F16, "q4_0 1024^2 n=64")
+
+
+@pytest.mark.parametrize("qt", PREFILL_QTS)
+def test_lfm2_prefill_n512(qt):
+    qi = PREFILL_QTS.index(qt)
+    n = 512
+    for si, (label, m, k) in enumerate(LFM2):
+        note(f"prefill {qt} {label} {m}x{k} n={n}")
+        w = weights(qt, m, k, 16 * qi + si)       # the bench's buffers
+        x = bench_acts(n, k)
+        got = gpu_gemm(qt, w, x, m, "mfma")
+        check_sampled(qt, w, x, m, k, got, TAU_F16, n_samples=3000, seed=si,
+                      what=f"prefill {qt} {label}")
+
+
+@pytest.mark.parametrize("qt", ["q4_k", "q6_k"])
+@pytest.mark.parametrize("m,k", [(4608, 1024), (14336, 4096)])
+def test_decode_sweep(qt, m, k):
+    w = weights(qt, m, k, 99)
+    for n in (1, 4, 8, 16, 32):
+        note(f"decode {qt} {m}x{k} n={n}")
+        x = gen.unit_f32(n * k, gen.SEED_X).reshape(n, k)
+        got = gpu_gemm(qt, w, x, m, "gemv")
+        check_sampled(qt, w, x, m, k, got, TAU_F32, n_samples=2000, seed=n,
+                      what=f"decode {qt} {m}x{k} n={n}")
+
+
+@pytest.mark.parametrize("t", [1, 16])
+def test_moe_gateup_full_size(t):
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    n_expert, in_f, n_ff, n_used = 64, 4096, 2048, 8
+    note(f"moe full size t={t}")
+    planes = [np.concatenate([gen.nvfp4_rows(n_ff, in_f, gen.SEED_MOE_W + 2 * e + p)
+                              for e in range(n_expert)]) for p in range(2)]
+    ids = gen.expert_ids(t, n_used, n_expert, gen.SEED_EXPERTS)
+    n_pairs = t * n_used
+    sc = gen.pair_scales(2 * n_pairs)
+    x = gen.xorshift_f32(t * in_f, gen.SEED_MOE_X).reshape(t, in_f)
+    g, u = qmm.moe_gateup(to_dev(planes[0]), to_dev(planes[1]), to_dev(ids), to_dev(sc), to_dev(x),
+                          n_expert, n_ff, "nvfp4")
+    torch.cuda.synchronize()
+    outs = [g.cpu().numpy(), u.cpu().numpy()]
+    rng = np.random.default_rng(t)
+    pairs = np.concatenate([rng.integers(0, n_pairs, 600), [0, n_pairs - 1, 0, n_pairs - 1]])
+    rows = np.concatenate([rng.integers(0, n_ff, 600), [0, 0, n_ff - 1, n_ff - 1]])
+    for plane in (0, 1):
+        assert np.all(np.isfinite(outs[plane]))
+        r, S = ref.moe_ref_pairs_rows("nvfp4", planes[plane], ids, sc, x, plane, n_expert, in_f, n_ff,
+                                      pairs, rows)
+        ok, worst = ref.tolerance_check(outs[plane][pairs, rows], r, S, TAU_F32)
+        assert ok, f"moe t={t} plane {plane}: worst {worst:.3g}"
+
+
+@pytest.mark.parametrize("qt", ["q4_k", "q6_k"])
+@pytest.mark.parametrize("m,k", [(14336, 4096), (4096, 14336)])
+def test_8b_prefill_n2048(qt, m, k):
+    n = 2048
+    note(f"8b prefill {qt} {m}x{k} n={n}")
+    w = weights(qt, m, k, 7)
+    x = gen.unit_f32(n * k, gen.SEED_X + k).reshape(n, k)
+    got = gpu_gemm(qt, w, x, m, "mfma")
+    check_sampled(qt, w, x, m, k, got, TAU_F16, n_samples=2000, seed=1, what=f"8b {qt} {m}x{k}")

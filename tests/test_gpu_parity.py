@@ -222,3 +222,50 @@ def test_loadonly_twin_runs_and_is_deterministic():
         b = qmm.stream_loadonly(w, m, k, qt)
         torch.cuda.synchronize()
         assert torch.equal(a, b)
+
+
+def test_split_k_workspace_contract():
+    """The k-split MFMA path (few output tiles): parity with and without a
+    workspace, bit-identical repeats, size and alignment checks."""
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    qt, m, k, n = "q4_k", 1024, 4608, 200
+    note(f"split-k {qt} {m}x{k} n={n}")
+    nbytes = qmm.workspace_bytes(m, k, n, qt, "mfma")
+    assert nbytes > 0
+    w = weights(qt, m, k, 21)
+    x = acts(n, k, 21)
+    wd, xd = to_dev(w), to_dev(x)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device="cuda")   # contents must not matter
+    a = qmm.gemm(wd, xd, m, qt, path="mfma", workspace=ws).clone()
+    b = qmm.gemm(wd, xd, m, qt, path="mfma", workspace=ws).clone()
+    c = qmm.gemm(wd, xd, m, qt, path="mfma", workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), "split-k result not reproducible"
+    for got in (a, c):
+        check_full(qt, w, x, m, k, n, got.cpu().numpy(), TAU_F16, "split-k")
+    with pytest.raises(qmm.QmmError) as e:
+        qmm.gemm(wd, xd, m, qt, path="mfma", workspace=ws[:nbytes - 256])
+    assert e.value.status == 9
+    with pytest.raises(qmm.QmmError) as e:
+        qmm.gemm(wd, xd, m, qt, path="mfma", workspace=ws[16:])
+    assert e.value.status == 5
+
+
+def test_split_k_shared_workspace_growing_tile_count():
+    """Calls with different shapes share one workspace, each leaving its
+    partials behind for the next."""
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    qt = "q8_0"
+    shapes = [(256, 2048, 130), (640, 1024, 300), (384, 1536, 200)]   # 6, 15, 6 tiles
+    need = max(qmm.workspace_bytes(m, k, n, qt, "mfma") for m, k, n in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for si, (m, k, n) in enumerate(shapes):
+        note(f"shared workspace {qt} {m}x{k} n={n}")
+        assert qmm.workspace_bytes(m, k, n, qt, "mfma") > 0
+        w = weights(qt, m, k, 40 + si)
+        x = acts(n, k, 40 + si)
+        got = qmm.gemm(to_dev(w), to_dev(x), m, qt, path="mfma", workspace=ws)
+        torch.cuda.synchronize()
+        check_full(qt, w, x, m, k, n, got.cpu().numpy(), TAU_F16, f"shared ws {m}x{k}x{n}")

@@ -109,6 +109,30 @@ def test_moe_ref_brute_force_and_expert_renaming():
     assert np.array_equal(g2, g) and np.array_equal(u2, u)
 
 
+def test_moe_sampled_rows_equal_brute_force():
+    """The sampled MoE reference against the literal scalar decoder + fsum."""
+    n_expert, in_f, n_ff, t, n_used = 5, 128, 6, 4, 3
+    wg = np.concatenate([gen.nvfp4_rows(n_ff, in_f, 0x8181 + 2 * e) for e in range(n_expert)])
+    ids = gen.expert_ids(t, n_used, n_expert, 11)
+    sc = gen.pair_scales(2 * t * n_used)
+    x = gen.xorshift_f32(t * in_f, 91)
+    per = n_ff * formats.row_bytes("nvfp4", in_f)
+    n_pairs = t * n_used
+    pairs = np.array([0, 5, 11, 7, 3])
+    rows = np.array([0, 5, 2, 3, 1])
+    for plane in (0, 1):
+        val, tol = ref.moe_ref_pairs_rows("nvfp4", wg, ids, sc, x, plane, n_expert, in_f, n_ff,
+                                          pairs, rows)
+        for i, (p, r) in enumerate(zip(pairs, rows)):
+            e = ids.reshape(-1)[p]
+            blk = bytes(wg[e * per:(e + 1) * per])
+            xt = x[(p // n_used) * in_f:(p // n_used + 1) * in_f].tolist()
+            bf = scalar.gemm("nvfp4", blk, [xt], n_ff, in_f, 1)[0][r]
+            f = np.float64(sc[plane * n_pairs + p])
+            assert abs(val[i] - f * bf) <= 1e-12 * max(1.0, abs(f * bf))
+            assert tol[i] >= abs(val[i])
+
+
 def test_tolerance_check_semantics():
     r = np.array([[1.0, -2.0]])
     S = np.array([[1.0, 2.0]])
