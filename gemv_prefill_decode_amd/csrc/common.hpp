@@ -125,15 +125,22 @@ __device__ __forceinline__ int uniform_i32(int v) { return __builtin_amdgcn_read
 // OCP FP8 E4M3FN byte -> f32 (exact): sign, 4-bit exponent bias 7, 3-bit
 // mantissa, exponent 0 subnormal, S.1111.111 NaN, no infinities.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    // branch-free: normal and subnormal magnitudes both formed, then selected
     const uint32_t e = (b >> 3) & 15u, mt = b & 7u;
-    float mag;
-    if (e == 0) {
-        mag = (float)mt * 0x1p-9f;
-    } else {
-        mag = __builtin_bit_cast(float, ((e + 120u) << 23) | (mt << 20));
-    }
-    if ((b & 0x7Fu) == 0x7Fu) mag = __builtin_nanf("");
-    return (b & 0x80u) ? -mag : mag;
+    const float norm = __builtin_bit_cast(float, ((e + 120u) << 23) | (mt << 20));
+    const float sub = (float)mt * 0x1p-9f;
+    float mag = e == 0u ? sub : norm;
+    mag = (b & 0x7Fu) == 0x7Fu ? __builtin_nanf("") : mag;
+    return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, mag) | ((b & 0x80u) << 24));
+}
+
+// v as a per-lane (VGPR) value: selects that depend on it compile to
+// v_cndmask rather than to uniform branches, which would split the basic
+// block the scheduler interleaves.
+__device__ __forceinline__ int as_vgpr(int v) {
+    int r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
 }
 
 // Two OCP FP4 E2M1 codes in byte `sel` of v -> f32 (low nibble first), exact.

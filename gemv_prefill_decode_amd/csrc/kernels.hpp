@@ -20,9 +20,15 @@ struct GemvTuning {
 void launch_gemv(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
                  int qt, int64_t rb, const GemvTuning& tune, hipStream_t st);
 
-// Launch plan of the MFMA kernel: k split into n_split ranges of sps steps
-// (64 k each; sps even), and the workspace bytes that needs (0 if n_split = 1).
+// Launch plan of the prefill (MFMA) kernels.  x16 = 0: gemm_mfma.hip's
+// kernel (128 x 128 tiles, f32 activations converted in the k loop).
+// x16 = 1: gemm_mfma_x16.hip's kernel ((64*wm) x 128 tiles, activations
+// rounded to f16 by a pre-pass into the workspace).  Either may split k into
+// n_split ranges of sps steps (64 k each; sps even) whose partial results go
+// to the workspace (after the f16 activations), summed by a second kernel.
 struct MfmaPlan {
+    int x16;
+    int wm;
     int n_split;
     int sps;
     int64_t ws_bytes;
@@ -32,13 +38,35 @@ struct MfmaPlan {
 // n*m rounded up to a multiple of 64 (256 bytes).
 __host__ __device__ constexpr int64_t splitk_stride(int64_t n, int64_t m) { return (n * m + 63) / 64 * 64; }
 
-// The plan for an m x k x n product on a device with num_cu compute units.
-MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int num_cu);
+// Halves per row of the f16 activations: k rounded up to whole 64-k steps.
+__host__ __device__ constexpr int64_t x16_row_halves(int64_t k) { return (k + 63) / 64 * 64; }
 
-// Launch with plan pl; ws (256-byte aligned, pl.ws_bytes) holds the k
-// splits' partial results when pl.n_split > 1 (then two kernels are launched).
+// Workspace bytes of the f16 activations (n rows), rounded up to 256.
+__host__ __device__ constexpr int64_t x16_bytes(int64_t n, int64_t k) {
+    return (n * x16_row_halves(k) * 2 + 255) / 256 * 256;
+}
+
+// A plan forced by the caller (kernel family and k split), for tuning.
+struct MfmaForce {
+    int x16;
+    int wm;
+    int n_split;
+};
+
+// The plan for an m x k x n product on a device with num_cu compute units,
+// with (have_ws) or without a workspace; force (or null) restricts the
+// choice.  Without a workspace: gemm_mfma.hip's kernel, unsplit.
+MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int num_cu, bool have_ws, const MfmaForce* force);
+
+// Launch with plan pl; ws (256-byte aligned, pl.ws_bytes) when pl.x16.
 void launch_gemm_mfma(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
                       int qt, int64_t rb, const MfmaPlan& pl, void* ws, hipStream_t st);
+void launch_gemm_mfma_x16(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
+                          int qt, int64_t rb, const MfmaPlan& pl, void* ws, hipStream_t st);
+
+// dst[i] = sum over z < n_split of part[z*zstride + i], in order of z, i < count.
+void launch_splitk_sum(float* dst, const float* part, int64_t count, int64_t zstride, int n_split,
+                       hipStream_t st);
 
 void launch_moe(float* gate_out, float* up_out, const void* w_gate, const void* w_up,
                 const int* ids, const float* scale, const float* x, int64_t t, int64_t n_used,
@@ -53,8 +81,10 @@ void launch_loadonly(uint32_t* sink, const void* w, int64_t m, int64_t k, int qt
 int64_t gemv_max_window_bytes(int qt, int64_t k, int64_t rb);
 int gemv_unit_elems(int qt);
 
-// Tile sizes of the MFMA kernel (rows of W, tokens) for the host's checks.
+// Largest tile sizes of the MFMA kernels (rows of W, tokens), for the host's
+// 32-bit offset checks.
 constexpr int MFMA_BM = 128;
 constexpr int MFMA_BN = 128;
+constexpr int MFMA_BM_MAX = 256;
 
 }  // namespace qmm

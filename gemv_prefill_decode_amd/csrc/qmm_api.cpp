@@ -7,6 +7,7 @@
 #include <cerrno>
 #include <climits>
 #include <cstdlib>
+#include <cstdio>
 #include <cstring>
 #include <mutex>
 
@@ -94,6 +95,30 @@ void parse_tune() {
     g_tune.depth = d;
 }
 
+// QMM_MFMA_PLAN="x16,wm,n_split" forces the prefill plan of calls with a
+// workspace (tuning); unset: the cost model chooses.  Malformed -> bad.
+struct MfmaForceState {
+    bool set = false;
+    bool bad = false;
+    qmm::MfmaForce f{0, 2, 1};
+};
+MfmaForceState g_force;
+std::once_flag g_force_once;
+
+void parse_force() {
+    const char* v = std::getenv("QMM_MFMA_PLAN");
+    if (!v) return;
+    int a = -1, b = -1, c = -1;
+    char tail = 0;
+    if (std::sscanf(v, "%d,%d,%d%c", &a, &b, &c, &tail) != 3 || (a != 0 && a != 1) ||
+        (b != 2 && b != 4) || (a == 0 && b != 2) || c < 1 || c > 16) {
+        g_force.bad = true;
+        return;
+    }
+    g_force.set = true;
+    g_force.f = qmm::MfmaForce{a, b, c};
+}
+
 // Tuning for the current device; false if a tuning variable is malformed.
 bool gemv_tuning(qmm::GemvTuning* t) {
     std::call_once(g_tune_once, parse_tune);
@@ -170,7 +195,7 @@ int check_gemm(float* dst, const void* w, const float* x, int64_t m, int64_t k, 
         return QMM_OK;
     }
     if (*path == QMM_PATH_MFMA) {
-        if ((int64_t)qmm::MFMA_BM * *rb + 16 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+        if ((int64_t)qmm::MFMA_BM_MAX * *rb + 16 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
         if ((int64_t)qmm::MFMA_BN * k * 4 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
         const int64_t tiles = ((m + qmm::MFMA_BM - 1) / qmm::MFMA_BM) * ((n + qmm::MFMA_BN - 1) / qmm::MFMA_BN);
         // work items (tiles x k splits, at most 16) are counted in int
@@ -191,12 +216,14 @@ int gemm_impl(float* dst, const void* w, const float* x, int64_t m, int64_t k, i
         qmm::launch_gemv(dst, w, x, m, k, n, qtype, rb, tune, stream);
         return launch_status();
     }
-    qmm::MfmaPlan pl = qmm::plan_gemm_mfma(m, k, n, tune.num_cu);
+    std::call_once(g_force_once, parse_force);
+    if (g_force.bad) return QMM_ERR_RANGE;
+    const qmm::MfmaPlan pl =
+        qmm::plan_gemm_mfma(m, k, n, tune.num_cu, ws != nullptr, g_force.set ? &g_force.f : nullptr);
     if (ws) {
         if (!aligned(ws, 256)) return QMM_ERR_ALIGN;
         if (ws_bytes < pl.ws_bytes) return QMM_ERR_WORKSPACE;
     }
-    if (pl.n_split > 1 && !ws) pl = qmm::plan_gemm_mfma(m, k, n, 0);  // no workspace: no split
     qmm::launch_gemm_mfma(dst, w, x, m, k, n, qtype, rb, pl, ws, stream);
     return launch_status();
 }
@@ -252,7 +279,9 @@ int64_t qmm_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int qtype, int
     if (path != QMM_PATH_MFMA) return -QMM_ERR_PATH;
     qmm::GemvTuning tune;
     if (!gemv_tuning(&tune)) return -QMM_ERR_RANGE;
-    return qmm::plan_gemm_mfma(m, k, n, tune.num_cu).ws_bytes;
+    std::call_once(g_force_once, parse_force);
+    if (g_force.bad) return -QMM_ERR_RANGE;
+    return qmm::plan_gemm_mfma(m, k, n, tune.num_cu, true, g_force.set ? &g_force.f : nullptr).ws_bytes;
 }
 
 int qmm_gemm_ws(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qtype,

@@ -71,10 +71,12 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
 
 
-def gpu_gemm(qt: str, w: np.ndarray, x: np.ndarray, m: int, path: str) -> np.ndarray:
+def gpu_gemm(qt: str, w: np.ndarray, x: np.ndarray, m: int, path: str, workspace="auto") -> np.ndarray:
+    """qmm.gemm on the device; workspace "auto" takes the f16-activation
+    prefill kernel (and k splits), None the no-workspace kernel."""
     import torch
     import gemv_prefill_decode_amd as qmm
-    out = qmm.gemm(to_dev(w), to_dev(x), m, qt, path=path)
+    out = qmm.gemm(to_dev(w), to_dev(x), m, qt, path=path, workspace=workspace)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 

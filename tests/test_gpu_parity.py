@@ -61,6 +61,34 @@ def test_mfma_parity(qt):
 
 
 @pytest.mark.parametrize("qt", QTS)
+def test_mfma_parity_no_workspace(qt):
+    """The prefill kernel that converts f32 activations in its k loop (calls
+    without a workspace)."""
+    for si, (m, k, n) in enumerate(MFMA_SHAPES[qt]):
+        note(f"mfma no-workspace {qt} m={m} k={k} n={n}")
+        w = weights(qt, m, k, 10 + si)
+        x = acts(n, k, 10 + si)
+        got = gpu_gemm(qt, w, x, m, "mfma", workspace=None)
+        check_full(qt, w, x, m, k, n, got, TAU_F16, f"mfma no-ws {qt} {m}x{k} n={n}")
+
+
+@pytest.mark.parametrize("qt", QTS)
+def test_mfma_paths_agree_bit_for_bit_unsplit(qt):
+    """Both prefill kernels round x and W to f16 the same way; where neither
+    splits k their sums run in the same order, so the outputs are equal."""
+    import gemv_prefill_decode_amd as qmm
+    m, k, n = 512, 1024, 300
+    note(f"mfma kernels agree {qt}")
+    w = weights(qt, m, k, 50)
+    x = acts(n, k, 50)
+    a = gpu_gemm(qt, w, x, m, "mfma", workspace=None)
+    check_full(qt, w, x, m, k, n, a, TAU_F16, f"agree {qt}")
+    if qmm.workspace_bytes(m, k, n, qt, "mfma") > 0:
+        b = gpu_gemm(qt, w, x, m, "mfma")
+        check_full(qt, w, x, m, k, n, b, TAU_F16, f"agree ws {qt}")
+
+
+@pytest.mark.parametrize("qt", QTS)
 def test_auto_dispatch_threshold(qt):
     m, k = 130, 512 if qt != "f32" else 512
     for n in (32, 33):
