@@ -37,6 +37,15 @@ namespace qmm {
 //                of the two runs (the factor is common to each run).
 //   prel0(s), prel1(s)
 //                rel0/rel1 in the padded LDS activation layout.
+//   RUNS > 0     offset formats: in each of the unit's RUNS runs of 16
+//                weights, w = A_r*q - B_r with q a small non-negative
+//                integer.  qsub(s, q) gives the q of sub-unit s as exact
+//                floats, run0(s)/run1(s) the runs its halves belong to,
+//                lastsub(r) the last sub-unit of run r, runrel(r) its first
+//                k relative to e, runA/runB its factors.  With activations
+//                staged in LDS the sums use sum(w*x) = A_r*sum(q*x) -
+//                B_r*sum(x), the run sums of x being computed once per work
+//                group: one FMA per weight and token instead of two.
 
 template <int QT> struct GUnit;
 
@@ -48,6 +57,7 @@ struct LaneBase {
 template <> struct GUnit<QT_F32> {  // 16 weights, 64 bytes
     static constexpr int UE = 16, S = 2, MIN_LPR = 1;
     static constexpr bool SCALED = false;
+    static constexpr int RUNS = 0;
     struct Lane : LaneBase {};
     __device__ static Lane lane(int gl) { return Lane{{(uint32_t)gl * 64u, gl * 16}}; }
     __host__ __device__ static uint32_t ustep(int lpr) { return (uint32_t)lpr * 64u; }
@@ -73,6 +83,11 @@ template <> struct GUnit<QT_F32> {  // 16 weights, 64 bytes
 template <> struct GUnit<QT_Q4_0> {  // one 18-byte block of 32 weights
     static constexpr int UE = 32, S = 4, MIN_LPR = 1;
     static constexpr bool SCALED = false;
+    static constexpr int RUNS = 2;  // w = d*q - 8d; runs: low nibbles (k 0..15), high (16..31)
+    static constexpr int run0(int) { return 0; }
+    static constexpr int run1(int) { return 1; }
+    static constexpr int lastsub(int) { return 3; }
+    static constexpr int runrel(int r) { return 16 * r; }
     struct Lane : LaneBase {};
     __device__ static Lane lane(int gl) { return Lane{{(uint32_t)gl * 18u, gl * 32}}; }
     __host__ __device__ static uint32_t ustep(int lpr) { return (uint32_t)lpr * 18u; }
@@ -90,6 +105,17 @@ template <> struct GUnit<QT_Q4_0> {  // one 18-byte block of 32 weights
         d = h2f(r[0] >> (8u * sh));
         d8 = -8.0f * d;
     }
+    __device__ __forceinline__ float runA(int) const { return d; }
+    __device__ __forceinline__ float runB(int) const { return -d8; }
+    __device__ __forceinline__ void qsub(int s, float (&q)[8]) const {
+        const uint32_t v = shr64(r[s], r[s + 1], sh + 2u);
+        const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            q[b] = ubyte_f32(lo, b);
+            q[4 + b] = ubyte_f32(hi, b);
+        }
+    }
     __device__ __forceinline__ void sub(int s, float (&w)[8], float&, float&) const {
         const uint32_t q = shr64(r[s], r[s + 1], sh + 2u);  // qs[4s..4s+3]
         const uint32_t lo = q & 0x0F0F0F0Fu, hi = (q >> 4) & 0x0F0F0F0Fu;
@@ -104,6 +130,7 @@ template <> struct GUnit<QT_Q4_0> {  // one 18-byte block of 32 weights
 template <> struct GUnit<QT_Q8_0> {  // one 34-byte block of 32 weights
     static constexpr int UE = 32, S = 4, MIN_LPR = 1;
     static constexpr bool SCALED = true;  // d is common to the whole block
+    static constexpr int RUNS = 0;
     struct Lane : LaneBase {};
     __device__ static Lane lane(int gl) { return Lane{{(uint32_t)gl * 34u, gl * 32}}; }
     __host__ __device__ static uint32_t ustep(int lpr) { return (uint32_t)lpr * 34u; }
@@ -138,6 +165,11 @@ template <> struct GUnit<QT_Q8_0> {  // one 34-byte block of 32 weights
 template <> struct GUnit<QT_Q4_K> {
     static constexpr int UE = 32, S = 4, MIN_LPR = 8;
     static constexpr bool SCALED = false;
+    static constexpr int RUNS = 2;  // w = D*q - M; runs: sub-block 2c (k e..e+15), 2c+1 (e+32..)
+    static constexpr int run0(int) { return 0; }
+    static constexpr int run1(int) { return 1; }
+    static constexpr int lastsub(int) { return 3; }
+    static constexpr int runrel(int r) { return 32 * r; }
     struct Lane : LaneBase {
         uint32_t qoff;   // byte offset of the lane's 16 nibble bytes in the superblock
         int lo6;         // c < 2: the (scale, min) pairs are 6-bit fields of sc[j], sc[j+4]
@@ -186,6 +218,17 @@ template <> struct GUnit<QT_Q4_K> {
         }
         D0 = Dv[0]; M0 = Mv[0]; D1 = Dv[1]; M1 = Mv[1];
     }
+    __device__ __forceinline__ float runA(int r) const { return r == 0 ? D0 : D1; }
+    __device__ __forceinline__ float runB(int r) const { return r == 0 ? M0 : M1; }
+    __device__ __forceinline__ void qsub(int s, float (&q)[8]) const {
+        const uint32_t v = s == 0 ? qs.x : (s == 1 ? qs.y : (s == 2 ? qs.z : qs.w));
+        const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            q[b] = ubyte_f32(lo, b);
+            q[4 + b] = ubyte_f32(hi, b);
+        }
+    }
     __device__ __forceinline__ void sub(int s, float (&w)[8], float&, float&) const {
         const uint32_t q = s == 0 ? qs.x : (s == 1 ? qs.y : (s == 2 ? qs.z : qs.w));
         const uint32_t lo = q & 0x0F0F0F0Fu, hi = (q >> 4) & 0x0F0F0F0Fu;
@@ -204,6 +247,11 @@ template <> struct GUnit<QT_Q4_K> {
 template <> struct GUnit<QT_Q6_K> {
     static constexpr int UE = 64, S = 8, MIN_LPR = 4;
     static constexpr bool SCALED = true;  // d * scale is common to each 16-run
+    static constexpr int RUNS = 4;  // w = D_g*q - 32*D_g; run g = quarter g (sub-units 2g, 2g+1)
+    static constexpr int run0(int s) { return s >> 1; }
+    static constexpr int run1(int s) { return s >> 1; }
+    static constexpr int lastsub(int r) { return 2 * r + 1; }
+    static constexpr int runrel(int r) { return 32 * r; }
     struct Lane : LaneBase {
         uint32_t oa, ob, oh, os;  // byte offsets (in the superblock) of the four spans
         uint32_t so;              // bit offset of the half's first used scale byte
@@ -245,6 +293,25 @@ template <> struct GUnit<QT_Q6_K> {
         D[2] = d * (float)(int8_t)(sc1 >> l.so);
         D[3] = d * (float)(int8_t)(sc1 >> (l.so + 16u));
     }
+    __device__ __forceinline__ float runA(int r) const { return D[r]; }
+    __device__ __forceinline__ float runB(int r) const { return 32.0f * D[r]; }
+    __device__ __forceinline__ void qsub(int s, float (&q)[8]) const {
+        const int g = s >> 1, i8 = s & 1;
+        const uint32_t L0 = (g & 1) ? rb[2 * i8] : ra[2 * i8];
+        const uint32_t L1 = (g & 1) ? rb[2 * i8 + 1] : ra[2 * i8 + 1];
+        const uint32_t L2 = (g & 1) ? rb[2 * i8 + 2] : ra[2 * i8 + 2];
+        const uint32_t l_a = shr64(L0, L1, sh), l_b = shr64(L1, L2, sh);
+        const uint32_t h_a = shr64(rh[2 * i8], rh[2 * i8 + 1], sh);
+        const uint32_t h_b = shr64(rh[2 * i8 + 1], rh[2 * i8 + 2], sh);
+        const int nsh = g >= 2 ? 4 : 0;
+        const uint32_t qa = ((l_a >> nsh) & 0x0F0F0F0Fu) | (((h_a >> (2 * g)) & 0x03030303u) << 4);
+        const uint32_t qb = ((l_b >> nsh) & 0x0F0F0F0Fu) | (((h_b >> (2 * g)) & 0x03030303u) << 4);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            q[b] = ubyte_f32(qa, b);
+            q[4 + b] = ubyte_f32(qb, b);
+        }
+    }
     __device__ __forceinline__ void sub(int s, float (&w)[8], float& f0, float& f1) const {
         const int g = s >> 1, i8 = s & 1;
         const uint32_t L0 = (g & 1) ? rb[2 * i8] : ra[2 * i8];
@@ -271,6 +338,7 @@ template <> struct GUnit<QT_Q6_K> {
 template <> struct GUnit<QT_NVFP4> {
     static constexpr int UE = 32, S = 4, MIN_LPR = 2;
     static constexpr bool SCALED = true;  // one E4M3 factor per 16-weight run
+    static constexpr int RUNS = 0;
     struct Lane : LaneBase {
         uint32_t hsh;  // 16 * h: the half's two scale bytes
         uint32_t qoff;
@@ -320,11 +388,16 @@ template <> struct GUnit<QT_NVFP4> {
 __device__ __forceinline__ int xpad(int e) { return e + ((e >> 6) << 2); }
 __host__ __device__ constexpr int xpad_len(int k) { return k + ((k + 63) / 64) * 4; }
 
-template <int NT>
+template <int NT, bool SUMS_ = false>
 struct XLds {
+    static constexpr bool SUMS = SUMS_;
     const float* s;  // [NT][xpad_len(k)]
     int ld;
+    const float* sums;  // SUMS: [NT][k/16] sums of runs of 16 activations
+    int nrun;
     struct Base { const float* p[NT]; };
+    // sum of activations k .. k+15 of token j (k a multiple of 16)
+    __device__ __forceinline__ float runsum(int k, int j) const { return sums[j * nrun + (k >> 4)]; }
     __device__ __forceinline__ Base base(int e) const {
         Base b;
         const int pe = xpad(e);
@@ -340,6 +413,7 @@ struct XLds {
 
 template <int NT>
 struct XGlobal {
+    static constexpr bool SUMS = false;
     rsrc_t xr;
     uint32_t xoff[NT];
     struct Base { uint32_t o[NT]; };
@@ -357,8 +431,10 @@ struct XGlobal {
 
 // Stage rows xoff[j] (j < NT) of x (row length k) into LDS in the padded
 // layout.  All threads of the work group take part, each with at least 8
-// independent 16-byte loads in flight per batch; ends with a barrier.
-template <int NT>
+// independent 16-byte loads in flight per batch; ends with a barrier.  With
+// SUMS, the sums of each run of 16 activations (k/16 per row, k a multiple
+// of 16) follow the rows: ((x0+x1)+(x2+x3)) + ... in a fixed order.
+template <int NT, bool SUMS = false>
 __device__ __forceinline__ void stage_x(float* sx, rsrc_t xr, const uint32_t (&xoff)[NT], int k) {
     constexpr int U = NT >= 8 ? 1 : 8 / NT;  // float4 columns per thread per batch
     const int ld = xpad_len(k);
@@ -382,6 +458,25 @@ __device__ __forceinline__ void stage_x(float* sx, rsrc_t xr, const uint32_t (&x
         }
     }
     __syncthreads();
+    if constexpr (SUMS) {
+        const int nrun = k >> 4;
+        float* sums = sx + NT * ld;
+        for (int t = threadIdx.x; t < NT * nrun; t += 256) {
+            const int j = t / nrun, r = t - j * nrun;
+            const float* p = sx + j * ld + xpad(16 * r);  // 16 contiguous floats
+            const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+            const f32x4 c = *(const f32x4*)(p + 8), d = *(const f32x4*)(p + 12);
+            const float sa = (a.x + a.y) + (a.z + a.w), sb = (b.x + b.y) + (b.z + b.w);
+            const float sc = (c.x + c.y) + (c.z + c.w), sd = (d.x + d.y) + (d.z + d.w);
+            sums[t] = (sa + sb) + (sc + sd);
+        }
+        __syncthreads();
+    }
+}
+
+// LDS floats of NT staged rows (and their run sums).
+__host__ __device__ constexpr int xlds_floats(int nt, int k, bool sums) {
+    return nt * xpad_len(k) + (sums ? nt * (k >> 4) : 0);
 }
 
 // ------------------------------------------------------------------ core
@@ -439,6 +534,56 @@ __device__ __forceinline__ void sub_fma(const GUnit<QT> (&un)[R], const XS& xs,
     }
 }
 
+// Sub-unit S_ of an offset format (RUNS > 0) with run sums of x: the q*x
+// products of each run accumulate in P (slot r & 1; a run's 16 FMAs form one
+// chain); after the run's last sub-unit, part += A_r*P - B_r*sum(x of run).
+template <int QT, int NT, int R, typename XS, int S_>
+__device__ __forceinline__ void sub_runs(const GUnit<QT> (&un)[R], const XS& xs,
+                                         const typename XS::Base& xb, int e, float (&P)[R][NT][2],
+                                         float (&part)[R][NT]) {
+    using UT = GUnit<QT>;
+    constexpr int r0 = UT::run0(S_), r1 = UT::run1(S_);
+    float q[R][8];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) un[rr].qsub(S_, q[rr]);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const f32x4 xa = xs.template get<UT::rel0(S_), UT::prel0(S_)>(xb, j);
+        const f32x4 xb4 = xs.template get<UT::rel1(S_), UT::prel1(S_)>(xb, j);
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+            float& pa = P[rr][j][r0 & 1];
+            pa = __builtin_fmaf(q[rr][0], xa.x, pa);
+            pa = __builtin_fmaf(q[rr][1], xa.y, pa);
+            pa = __builtin_fmaf(q[rr][2], xa.z, pa);
+            pa = __builtin_fmaf(q[rr][3], xa.w, pa);
+            float& pb = P[rr][j][r1 & 1];
+            pb = __builtin_fmaf(q[rr][4], xb4.x, pb);
+            pb = __builtin_fmaf(q[rr][5], xb4.y, pb);
+            pb = __builtin_fmaf(q[rr][6], xb4.z, pb);
+            pb = __builtin_fmaf(q[rr][7], xb4.w, pb);
+        }
+        if constexpr (S_ == UT::lastsub(r0)) {
+            const float sx = xs.runsum(e + UT::runrel(r0), j);
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) {
+                const float t = __builtin_fmaf(un[rr].runA(r0), P[rr][j][r0 & 1], part[rr][j]);
+                part[rr][j] = __builtin_fmaf(-un[rr].runB(r0), sx, t);
+                P[rr][j][r0 & 1] = 0.0f;
+            }
+        }
+        if constexpr (r1 != r0 && S_ == UT::lastsub(r1)) {
+            const float sx = xs.runsum(e + UT::runrel(r1), j);
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) {
+                const float t = __builtin_fmaf(un[rr].runA(r1), P[rr][j][r1 & 1], part[rr][j]);
+                part[rr][j] = __builtin_fmaf(-un[rr].runB(r1), sx, t);
+                P[rr][j][r1 & 1] = 0.0f;
+            }
+        }
+    }
+}
+
 template <int QT, int NT, int R, typename XS, int S_ = 0>
 __device__ __forceinline__ void sub_all(const GUnit<QT> (&un)[R], const XS& xs,
                                         const typename XS::Base& xb, int k, int e,
@@ -446,6 +591,16 @@ __device__ __forceinline__ void sub_all(const GUnit<QT> (&un)[R], const XS& xs,
     if constexpr (S_ < GUnit<QT>::S) {
         sub_fma<QT, NT, R, XS, S_>(un, xs, xb, k, e, part);
         sub_all<QT, NT, R, XS, S_ + 1>(un, xs, xb, k, e, part);
+    }
+}
+
+template <int QT, int NT, int R, typename XS, int S_ = 0>
+__device__ __forceinline__ void sub_all_runs(const GUnit<QT> (&un)[R], const XS& xs,
+                                             const typename XS::Base& xb, int e,
+                                             float (&P)[R][NT][2], float (&part)[R][NT]) {
+    if constexpr (S_ < GUnit<QT>::S) {
+        sub_runs<QT, NT, R, XS, S_>(un, xs, xb, e, P, part);
+        sub_all_runs<QT, NT, R, XS, S_ + 1>(un, xs, xb, e, P, part);
     }
 }
 
@@ -460,7 +615,16 @@ __device__ __forceinline__ void compute_item(GUnit<QT> (&un)[R], const typename 
 #pragma unroll
         for (int j = 0; j < NT; ++j) part[rr][j] = 0.0f;
     const typename XS::Base xb = xs.base(e);
-    sub_all<QT, NT, R, XS>(un, xs, xb, k, e, part);
+    if constexpr (GUnit<QT>::RUNS > 0 && XS::SUMS) {
+        float P[R][NT][2];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) P[rr][j][0] = P[rr][j][1] = 0.0f;
+        sub_all_runs<QT, NT, R, XS>(un, xs, xb, e, P, part);
+    } else {
+        sub_all<QT, NT, R, XS>(un, xs, xb, k, e, part);
+    }
 #pragma unroll
     for (int rr = 0; rr < R; ++rr)
 #pragma unroll
@@ -602,7 +766,7 @@ extern __shared__ __attribute__((aligned(16))) float qmm_dyn_lds[];
 
 // grid: x = work groups (their 4 waves stride over the row groups), y = token
 // groups of NT.  XL: activations staged in LDS (dynamic shared memory of
-// NT * xpad_len(k) floats).
+// xlds_floats(NT, k, RUNS > 0) floats).
 template <int QT, int NT, int R, int D, bool XL>
 __global__ __launch_bounds__(256) void gemv_kernel(float* __restrict__ dst,
                                                    const uint8_t* __restrict__ w,
@@ -621,9 +785,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(float* __restrict__ dst,
         if (row < m && j < ntok) out[(int64_t)j * m + row] = v;
     };
     if constexpr (XL) {
-        const XLds<NT> xs{qmm_dyn_lds, xpad_len(k)};
+        constexpr bool SM = GUnit<QT>::RUNS > 0;
+        const XLds<NT, SM> xs{qmm_dyn_lds, xpad_len(k), qmm_dyn_lds + NT * xpad_len(k), k >> 4};
         gemv_stream<QT, NT, R, D>(g, blockIdx.x * 4 + wave, gridDim.x * 4, n_rg, xs, store,
-                                  [&]() { stage_x<NT>(qmm_dyn_lds, xr, xoff, k); });
+                                  [&]() { stage_x<NT, SM>(qmm_dyn_lds, xr, xoff, k); });
     } else {
         XGlobal<NT> xs;
         xs.xr = xr;
@@ -667,9 +832,10 @@ __device__ __forceinline__ void moe_tokens(float* __restrict__ out, const float*
     };
     if constexpr (XL) {
         __syncthreads();  // the previous chunk's waves are done with the staged x
-        const XLds<NT> xs{qmm_dyn_lds, xpad_len(in_f)};
+        constexpr bool SM = GUnit<QT>::RUNS > 0;
+        const XLds<NT, SM> xs{qmm_dyn_lds, xpad_len(in_f), qmm_dyn_lds + NT * xpad_len(in_f), in_f >> 4};
         gemv_stream<QT, NT, R, D>(g, blockIdx.x * 4 + wave, gridDim.x * 4, n_rg, xs, store,
-                                  [&]() { stage_x<NT>(qmm_dyn_lds, xr, xoff, in_f); });
+                                  [&]() { stage_x<NT, SM>(qmm_dyn_lds, xr, xoff, in_f); });
     } else {
         XGlobal<NT> xs;
         xs.xr = xr;
@@ -959,7 +1125,7 @@ static void launch_gemv_nt(float* dst, const uint8_t* w, const float* x, int64_t
         const int l = lpr_for(QT, k);
         const int64_t n_rg = (m + rg_rows(l, R) - 1) / rg_rows(l, R);
         const int64_t gy = (n + NT - 1) / NT;
-        const int64_t lds = (int64_t)NT * xpad_len((int)k) * 4;
+        const int64_t lds = (int64_t)xlds_floats(NT, (int)k, GUnit<QT>::RUNS > 0) * 4;
         if (lds <= tune.lds_per_wg) {
             const dim3 grid(stream_grid(n_rg, gy, lds_limited(tune, lds)), (unsigned)gy);
             gemv_kernel<QT, NT, R, D, true><<<grid, 256, (size_t)lds, st>>>(
@@ -1015,7 +1181,7 @@ static void launch_moe_qt(float* g, float* u, const uint8_t* wg, const uint8_t* 
         const unsigned need = (unsigned)((n_rg + 3) / 4);
         if (gx < MOE_MIN_WG) gx = need < MOE_MIN_WG ? need : MOE_MIN_WG;
         const dim3 grid(gx, (unsigned)n_pairs, 2);
-        const int64_t lds = (int64_t)MOE_NT * xpad_len((int)in_f) * 4;
+        const int64_t lds = (int64_t)xlds_floats(MOE_NT, (int)in_f, GUnit<QT>::RUNS > 0) * 4;
         const int xl = lds <= XLDS_MAX_BYTES;
         moe_gateup_kernel<QT, R, D><<<grid, 256, (size_t)(xl ? lds : 0), st>>>(
             g, u, wg, wu, ids, sc, x, (int)t, (int)n_used, (int)n_expert, (int)in_f, (int)n_ff,
