@@ -247,6 +247,7 @@ constexpr double LAUNCH_US = 3.0;      // a launch with its first loads and its 
 constexpr double SPLIT_US = 4.0;       // the split sum's launch
 constexpr double X16_US = 3.0;         // the f16 pre-pass launch
 constexpr double BYTES_PER_US = 4.0e6; // partials and pre-pass traffic
+constexpr double X16_MARGIN = 1.1;     // see below
 
 MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int num_cu, bool have_ws, const MfmaForce* force) {
     MfmaPlan best;
@@ -279,9 +280,13 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int num_cu, bool have_w
             const double step_t = step > fc.step_alone_us ? step : fc.step_alone_us;
             double rounds = (double)items / (double)(num_cu * share);
             if (share == 1 || rounds < 1.0) rounds = (double)((items + num_cu * share - 1) / (num_cu * share));
-            const double cost = LAUNCH_US + rounds * sps * step_t +
-                                (se > 1 ? SPLIT_US + (2.0 * se + 1.0) * out_bytes / BYTES_PER_US : 0.0) +
-                                (x16 ? x16_us : 0.0);
+            // the f16 kernels must win by X16_MARGIN to be chosen: one kernel
+            // family per product size keeps small products on the kernel
+            // without a pre-pass (whose time the model knows least well)
+            const double cost = (LAUNCH_US + rounds * sps * step_t +
+                                 (se > 1 ? SPLIT_US + (2.0 * se + 1.0) * out_bytes / BYTES_PER_US : 0.0) +
+                                 (x16 ? x16_us : 0.0)) *
+                                (x16 ? X16_MARGIN : 1.0);
             if (cost < best_cost) {
                 best_cost = cost;
                 best.x16 = x16;
