@@ -15,9 +15,13 @@
  *  - Pointers marked DEVICE are device (HBM) pointers owned by the caller;
  *    the library never frees or retains them.
  *  - Work is enqueued asynchronously on `stream` (0 = the null stream).  No
- *    call allocates device memory, synchronizes, or keeps state beyond a
- *    lazily cached device property and the parsed QMM_GEMV_MAX_N knob, so the
- *    calls can be recorded into a hipGraph.
+ *    call allocates device memory, synchronizes, or keeps state beyond lazily
+ *    cached device properties (compute units, LDS sizes) and the parsed
+ *    tuning variables (QMM_GEMV_MAX_N below; QMM_GEMV_WG_PER_CU 1..64,
+ *    QMM_GEMV_ROWS 1..2, QMM_GEMV_DEPTH 2/4/8 for the streaming kernels'
+ *    launch shape; QMM_MFMA_PLAN at qmm_gemm_ws; a malformed value makes
+ *    the calls that use it return QMM_ERR_RANGE), so the calls can be
+ *    recorded into a hipGraph.
  *  - Arguments are validated on the host before anything is launched; a
  *    rejected call returns a non-zero qmm_status and launches nothing.  A
  *    launch failure reported by the runtime returns QMM_ERR_LAUNCH.
@@ -82,7 +86,7 @@ typedef enum {
  * within 1e-5 * sum|w*x| of the exact value), otherwise the MFMA kernel,
  * which rounds W and x to f16 (RNE) and accumulates in f32 (within
  * 2e-3 * sum|w*x|).
- * Limits: the bytes of one 128-row weight tile (or one GEMV row group) and
+ * Limits: the bytes of one 256-row weight tile (or one GEMV row group) and
  * of 128 (GEMV: 8) token rows of x each below 2^31; m, n, k below 2^31.
  * Larger values return QMM_ERR_RANGE.
  * qmm_gemm never splits k on the MFMA path (it has no workspace); products
@@ -99,16 +103,25 @@ int qmm_gemm_path(float* dst, const void* w, const float* x,
 
 /*
  * qmm_gemm_ws: qmm_gemm_path with a caller-owned workspace for the MFMA
- * path.  When the product has fewer 128x128 output tiles than the device has
- * compute units, k is split into ranges handled by separate work groups that
- * write partial results to the workspace; a second kernel on the same stream
- * adds the partials in a fixed order (two identical calls still give
- * bit-identical results) and writes dst.
+ * path, where it lets the library
+ *  - round the activations to f16 once per call (a pre-pass writing them
+ *    into the workspace in the weight tiles' k order), for products large
+ *    enough that the f16-activation kernel (256- or 128-row tiles) is
+ *    estimated at least 10% faster; and
+ *  - split k when the product has too few output tiles to fill the device:
+ *    separate work groups write partial results to the workspace and a
+ *    second kernel on the same stream adds them in a fixed order, so two
+ *    identical calls still give bit-identical results.
+ * Both kernels round W and x to f16 identically (RNE), so the tolerance is
+ * the one of qmm_gemm.  The plan is a pure function of (m, k, n) and the
+ * device's compute-unit count; the environment variable
+ * QMM_MFMA_PLAN="x16,wm,n_split" forces it (tuning only; malformed ->
+ * QMM_ERR_RANGE).
  *   workspace        DEVICE memory, 256-byte aligned, of at least
  *                    qmm_gemm_workspace_bytes(m, k, n, qtype, path) bytes, or
- *                    NULL (then k is never split).  No initial contents are
- *                    needed.  Calls that share a workspace must not overlap
- *                    (order them on one stream).
+ *                    NULL (then the f32-activation kernel without a k split).
+ *                    No initial contents are needed.  Calls that share a
+ *                    workspace must not overlap (order them on one stream).
  *   workspace_bytes  its size; smaller than needed -> QMM_ERR_WORKSPACE.
  * The GEMV path ignores the workspace.  Other arguments and errors as
  * qmm_gemm_path.
@@ -117,8 +130,8 @@ int qmm_gemm_ws(float* dst, const void* w, const float* x, int64_t m, int64_t k,
                 int qtype, int path, void* workspace, int64_t workspace_bytes,
                 hipStream_t stream);
 
-/* Workspace bytes qmm_gemm_ws uses for this product on the current device
- * (0 when k is not split, or on the GEMV path); < 0 is -qmm_status. */
+/* Workspace bytes qmm_gemm_ws uses for this product on the current device:
+ * 0 on the GEMV path, at least 256 on the MFMA path; < 0 is -qmm_status. */
 int64_t qmm_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int qtype, int path);
 
 /*
