@@ -44,7 +44,6 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 SHAPES = [("ffn_gate", 4608, 1024), ("ffn_down", 1024, 4608), ("conv_in", 3072, 1024),
           ("attn_out", 1024, 1024)]
 QTS = ["f32", "q4_0", "q8_0", "q4_k", "q6_k"]
-QT_ENUM = {"f32": 0, "q4_0": 1, "q8_0": 2, "q4_k": 3, "q6_k": 4, "nvfp4": 5}
 DECODE_SHAPES = [(14336, 4096), (4608, 1024)]
 DECODE_NS = [1, 4, 8, 16, 32]
 
@@ -180,22 +179,25 @@ def run_prefill(args, n):
     for (qt, label, m, k, w) in bufs:
         g = capture([call((qt, label, m, k, w))] * 8)
         t = time_graph(g, 8, 5)
+        plan = qmm.gemm_plan(m, k, n, qt, "mfma")
         per_qt[qt].setdefault("shapes", {})[label] = {
-            "us": round(t * 1e6, 2), "TFLOP/s": round(2.0 * m * k * n / t / 1e12, 1)}
+            "us": round(t * 1e6, 2), "TFLOP/s": round(2.0 * m * k * n / t / 1e12, 1),
+            "kernel": qmm.plan_kernel_name(plan, qt), "k_split": plan["n_split"]}
         del g
     dom = max(QTS, key=lambda q: per_qt[q]["us_per_step"])
     launches = sum(1 for b in bufs if b[0] == dom)
     avg_launch = per_qt[dom]["us_per_step"] * 1e-6 / launches
     fpl = flops[dom] / launches
     ach = fpl / avg_launch / 1e12
+    kernels = sorted({v["kernel"] for v in per_qt[dom]["shapes"].values()})
     roofline = {
-        "kernel": f"qmm::gemm_mfma_kernel<{QT_ENUM[dom]}> ({dom} weights)",
+        "kernel": " + ".join(f"qmm::{kn}" for kn in kernels) + f" ({dom} weights; per qmm_gemm_ws call)",
         "bound": "mfma",
         "achieved": round(ach, 2),
         "peak": PEAK_F16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(ach / PEAK_F16_TFLOPS, 4),
-        "traffic": traffic_from_profiles(f"gemm_mfma_kernel<{QT_ENUM[dom]}>"),
+        "traffic": traffic_from_profiles(kernels[0]) if len(kernels) == 1 else None,
         "avg_launch_us": round(avg_launch * 1e6, 3),
         "launches_per_step": launches,
         "algorithmic_flops_per_launch": fpl,

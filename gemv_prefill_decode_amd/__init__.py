@@ -20,7 +20,8 @@ import os
 import threading
 
 __all__ = [
-    "QTYPES", "PATHS", "QmmError", "lib_path", "load", "gemm", "workspace_bytes", "moe_gateup",
+    "QTYPES", "PATHS", "QmmError", "lib_path", "load", "gemm", "workspace_bytes", "gemm_plan",
+    "plan_kernel_name", "moe_gateup",
     "stream_loadonly",
     "row_bytes", "block_elems", "gemv_max_n", "status_str", "abi_version",
 ]
@@ -64,6 +65,8 @@ def load() -> ctypes.CDLL:
         lib.qmm_gemm_ws.restype = i32
         lib.qmm_gemm_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
         lib.qmm_gemm_workspace_bytes.restype = i64
+        lib.qmm_gemm_plan.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(ctypes.c_int32)]
+        lib.qmm_gemm_plan.restype = i32
         lib.qmm_moe_gateup.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
         lib.qmm_moe_gateup.restype = i32
         lib.qmm_stream_loadonly.argtypes = [vp, vp, i64, i64, i32, vp]
@@ -140,6 +143,28 @@ def workspace_bytes(m: int, k: int, n: int, qtype, path: str = "auto") -> int:
     if v < 0:
         raise QmmError(-v, "qmm_gemm_workspace_bytes")
     return v
+
+
+def gemm_plan(m: int, k: int, n: int, qtype, path: str = "auto", workspace: bool = True) -> dict:
+    """The kernels qmm_gemm_ws (workspace=True) or qmm_gemm would run."""
+    out = (ctypes.c_int32 * 6)()
+    st = load().qmm_gemm_plan(m, k, n, _qt(qtype), PATHS[path], int(workspace), out)
+    if st != 0:
+        raise QmmError(st, "qmm_gemm_plan")
+    if out[0] == PATHS["gemv"]:
+        return {"path": "gemv"}
+    return {"path": "mfma", "x16": out[1], "tile_rows": out[2], "k_groups": out[3], "n_split": out[4],
+            "steps_per_split": out[5]}
+
+
+def plan_kernel_name(plan: dict, qtype) -> str:
+    """Kernel symbol (as the profiler names it) of a gemm_plan() result."""
+    qt = _qt(qtype)
+    if plan["path"] == "gemv":
+        return "gemv_kernel"
+    if plan["x16"]:
+        return f"gemm_mfma_x16_kernel<{qt}, {plan['tile_rows'] // 64}>"
+    return f"gemm_mfma_kernel<{qt}, {plan['k_groups']}>"
 
 
 # Workspaces handed to qmm_gemm_ws by gemm(workspace="auto"): one buffer per

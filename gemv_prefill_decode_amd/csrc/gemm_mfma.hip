@@ -60,16 +60,26 @@ struct XLoad {
 // then adds the n_split partials in the order z = 0, 1, ... into dst; it is a
 // second launch on the same stream, so the partials are visible to it without
 // any fence, and the sum does not depend on the order the work items ran in.
-template <int QT>
-__global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(float* __restrict__ dst,
-                                                           const uint8_t* __restrict__ w,
-                                                           const float* __restrict__ x, int m,
-                                                           int k, int n, int rb, int n_mb,
-                                                           int n_nb, int n_split, int sps,
-                                                           float* __restrict__ partial) {
-    __shared__ __attribute__((aligned(16))) _Float16 sA[2][BM * LDK];
-    __shared__ __attribute__((aligned(16))) _Float16 sB[2][BN * LDK];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// KG k groups (KG = 2: 512 threads): group g of 4 waves takes the steps
+// s0 + g, s0 + g + KG, ... of the item with tiles of its own, so a CU holding
+// one work group has 2 waves per SIMD whose loads, decode and matrix-core
+// work hide each other's latency; at the end group 1 hands its accumulators
+// to group 0 through LDS, which adds them (group 0's + group 1's, a fixed
+// order) and stores the tile.
+template <int QT, int KG>
+__global__ __launch_bounds__(256 * KG, 1) void gemm_mfma_kernel(float* __restrict__ dst,
+                                                                const uint8_t* __restrict__ w,
+                                                                const float* __restrict__ x, int m,
+                                                                int k, int n, int rb, int n_mb,
+                                                                int n_nb, int n_split, int sps,
+                                                                float* __restrict__ partial) {
+    constexpr int TILE_H = BM * LDK;  // halves per A or B tile (BM == BN)
+    __shared__ __attribute__((aligned(16))) _Float16 lds[KG][2][2][TILE_H];  // [group][buffer][A, B]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int g = KG == 1 ? 0 : tid >> 8, lt = tid & 255, wave = lt >> 6;
+    // the weight (A) and activation (B) tiles of buffer buf of this thread's group
+    auto tileA = [&](int buf) -> _Float16* { return lds[g][buf][0]; };
+    auto tileB = [&](int buf) -> _Float16* { return lds[g][buf][1]; };
 
     // Work groups are dealt round-robin to the 8 XCDs (id % 8); give each XCD
     // a contiguous run of work items, numbered with the weight-row tile mb
@@ -86,7 +96,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(float* __restrict__ d
     const rsrc_t wr = row_window(w, m0, BM, m, rb, base);
     const int ntok = (int)imin64(BN, n - n0);
     const rsrc_t xr = make_rsrc(x + n0 * k, (uint32_t)ntok * (uint32_t)k * 4u);
-    const int arow = tid >> 1, part = tid & 1;
+    const int arow = lt >> 1, part = lt & 1;
     const uint32_t roff = (uint32_t)((m0 + arow) * rb - base);
     const int nk_all = (k + BK - 1) / BK;
     const int s0 = z * sps;
@@ -102,20 +112,22 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(float* __restrict__ d
     uint32_t tmp[16];
     auto stage = [&](const ALoad<QT>& al, const XLoad& xl, int buf) {
         al.decode(tmp);
+        _Float16* a = tileA(buf);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            *(u32x4*)&sA[buf][lds_a + 8 * u] = u32x4{tmp[4 * u], tmp[4 * u + 1], tmp[4 * u + 2], tmp[4 * u + 3]};
-        xl.store(sB[buf], tid);
+            *(u32x4*)&a[lds_a + 8 * u] = u32x4{tmp[4 * u], tmp[4 * u + 1], tmp[4 * u + 2], tmp[4 * u + 3]};
+        xl.store(tileB(buf), lt);
     };
 
     // Every load is unconditional (steps at or past nk read zeros through
     // out-of-range offsets, and their staged tiles are never used), so the
     // loop body is straight-line and the compiler's load counters let the
     // loads of step kt+2 stay in flight while step kt computes.
-    al0.load(wr, roff, s0, part, kend, nk);
-    xl0.template load<H>(xr, k, kend, s0, tid);
-    al1.load(wr, roff, s0 + 1, part, kend, nk);
-    xl1.template load<H>(xr, k, kend, s0 + 1, tid);
+    const int g0 = s0 + g;  // this group's first step; it takes every KG-th
+    al0.load(wr, roff, g0, part, kend, nk);
+    xl0.template load<H>(xr, k, kend, g0, lt);
+    al1.load(wr, roff, g0 + KG, part, kend, nk);
+    xl1.template load<H>(xr, k, kend, g0 + KG, lt);
     stage(al0, xl0, 0);
     __syncthreads();
 
@@ -128,8 +140,8 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(float* __restrict__ d
     const int wm = wave >> 1, wn = wave & 1;
     const int frag = (lane & 15) * LDK + (lane >> 4) * 8;
     auto mfma_step = [&](int buf) {
-        const _Float16* A = &sA[buf][wm * 64 * LDK + frag];
-        const _Float16* B = &sB[buf][wn * 64 * LDK + frag];
+        const _Float16* A = tileA(buf) + wm * 64 * LDK + frag;
+        const _Float16* B = tileB(buf) + wn * 64 * LDK + frag;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             f16x8 a[4], b[4];
@@ -148,22 +160,48 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(float* __restrict__ d
     // An odd step count runs one extra step whose weight and activation tiles
     // are all zeros (out-of-range loads): it adds exactly 0 to every sum and
     // keeps a single loop exit, so the accumulators stay in place.
-    const int nk2 = s0 + ((nk - s0 + 1) & ~1);
-    for (int kt = s0; kt < nk2; kt += 2) {
-        // step kt: buffer 0; set 1 holds step kt+1, set 0 takes kt+2
-        al0.load(wr, roff, kt + 2, part, kend, nk);
-        xl0.template load<H>(xr, k, kend, kt + 2, tid);
+    // Every group runs the same number of iterations (that of group 0, which
+    // has the most steps); steps past nk read zeros.
+    const int cnt = (nk - s0 + KG - 1) / KG;
+    const int cnt2 = (cnt + 1) & ~1;
+    for (int i = 0; i < cnt2; i += 2) {
+        const int kt = g0 + KG * i;
+        // step kt: buffer 0; set 1 holds step kt+KG, set 0 takes kt+2KG
+        al0.load(wr, roff, kt + 2 * KG, part, kend, nk);
+        xl0.template load<H>(xr, k, kend, kt + 2 * KG, lt);
         mfma_step(0);
         stage(al1, xl1, 1);
         interleave_hint();
         __syncthreads();
-        // step kt+1: buffer 1; set 0 holds step kt+2, set 1 takes kt+3
-        al1.load(wr, roff, kt + 3, part, kend, nk);
-        xl1.template load<H>(xr, k, kend, kt + 3, tid);
+        // step kt+KG: buffer 1; set 0 holds step kt+2KG, set 1 takes kt+3KG
+        al1.load(wr, roff, kt + 3 * KG, part, kend, nk);
+        xl1.template load<H>(xr, k, kend, kt + 3 * KG, lt);
         mfma_step(1);
         stage(al0, xl0, 0);
         interleave_hint();
         __syncthreads();
+    }
+
+    if constexpr (KG == 2) {
+        // group 1's accumulators to group 0 through group 1's tile space
+        // (2 x 2 x BM*LDK halves >= 64 KB), value v of thread lt at v*256+lt
+        float* red = reinterpret_cast<float*>(&lds[1][0][0][0]);
+        if (g == 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) red[((i * 4 + j) * 4 + r) * 256 + lt] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (g == 1) return;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][j][r] += red[((i * 4 + j) * 4 + r) * 256 + lt];
     }
 
 
@@ -223,8 +261,17 @@ static void launch_qt(float* dst, const uint8_t* w, const float* x, int64_t m, i
                       int64_t rb, const MfmaPlan& pl, void* ws, hipStream_t st) {
     const int n_mb = (int)((m + BM - 1) / BM), n_nb = (int)((n + BN - 1) / BN);
     float* part = (float*)ws;
-    gemm_mfma_kernel<QT><<<dim3((unsigned)(n_mb * n_nb * pl.n_split)), 256, 0, st>>>(
-        dst, w, x, (int)m, (int)k, (int)n, (int)rb, n_mb, n_nb, pl.n_split, pl.sps, part);
+    const dim3 grid((unsigned)(n_mb * n_nb * pl.n_split));
+    if constexpr (QT != QT_F32) {
+        if (pl.kg == 2) {
+            gemm_mfma_kernel<QT, 2><<<grid, 512, 0, st>>>(dst, w, x, (int)m, (int)k, (int)n, (int)rb, n_mb,
+                                                          n_nb, pl.n_split, pl.sps, part);
+            if (pl.n_split > 1) launch_splitk_sum(dst, part, n * m, splitk_stride(n, m), pl.n_split, st);
+            return;
+        }
+    }
+    gemm_mfma_kernel<QT, 1><<<grid, 256, 0, st>>>(dst, w, x, (int)m, (int)k, (int)n, (int)rb, n_mb, n_nb,
+                                                  pl.n_split, pl.sps, part);
     if (pl.n_split > 1) launch_splitk_sum(dst, part, n * m, splitk_stride(n, m), pl.n_split, st);
 }
 
@@ -238,10 +285,11 @@ struct FamCost {
     double step_shared_us;
     int per_cu;
 };
-constexpr FamCost FAM_COST[3] = {
+constexpr FamCost FAM_COST[4] = {
     {1.5, 1.04, 2},   // gemm_mfma_kernel, 128 x 128, f32 activations
     {1.6, 1.61, 1},   // gemm_mfma_x16_kernel, 256 x 128
     {1.2, 0.82, 2},   // gemm_mfma_x16_kernel, 128 x 128
+    {1.3, 1.3, 1},    // gemm_mfma_kernel with 2 k groups (time per step of the item)
 };
 constexpr double LAUNCH_US = 3.0;      // a launch with its first loads and its stores
 constexpr double SPLIT_US = 4.0;       // the split sum's launch
@@ -249,11 +297,13 @@ constexpr double X16_US = 3.0;         // the f16 pre-pass launch
 constexpr double BYTES_PER_US = 4.0e6; // partials and pre-pass traffic
 constexpr double X16_MARGIN = 1.1;     // see below
 
-MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int num_cu, bool have_ws, const MfmaForce* force) {
+MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, bool have_ws,
+                        const MfmaForce* force) {
     MfmaPlan best;
     const int nk = (int)((k + BK - 1) / BK);
     best.x16 = 0;
     best.wm = 2;
+    best.kg = 1;
     best.n_split = 1;
     best.sps = nk + (nk & 1);
     best.ws_bytes = 0;
@@ -261,9 +311,10 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int num_cu, bool have_w
     const double out_bytes = 4.0 * (double)n * (double)m;
     const double x16_us = X16_US + 6.0 * (double)n * (double)k / BYTES_PER_US;
     double best_cost = 1e30;
-    for (int fam = 0; fam < 3; ++fam) {
-        const int x16 = fam > 0, wm = fam == 1 ? 4 : 2;
-        if (force && (force->x16 != x16 || force->wm != wm)) continue;
+    for (int fam = 0; fam < 4; ++fam) {
+        const int x16 = fam == 1 || fam == 2, wm = fam == 1 ? 4 : 2, kg = fam == 3 ? 2 : 1;
+        if (kg == 2 && qt == QT_F32) continue;  // its two register rings of f32 weights exceed 256 VGPRs
+        if (force && (force->x16 != x16 || force->wm != wm || force->kg != kg)) continue;
         const FamCost& fc = FAM_COST[fam];
         const int64_t T = ((m + 64 * wm - 1) / (64 * wm)) * ((n + 127) / 128);
         for (int S = 1; S <= 16 && (S == 1 || S <= nk / 2); ++S) {
@@ -291,6 +342,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int num_cu, bool have_w
                 best_cost = cost;
                 best.x16 = x16;
                 best.wm = wm;
+                best.kg = kg;
                 best.n_split = se;
                 best.sps = sps;
             }

@@ -29,6 +29,7 @@ void launch_gemv(float* dst, const void* w, const float* x, int64_t m, int64_t k
 struct MfmaPlan {
     int x16;
     int wm;
+    int kg;  // k groups of gemm_mfma_kernel (1 or 2; x16 = 0 only)
     int n_split;
     int sps;
     int64_t ws_bytes;
@@ -51,12 +52,14 @@ struct MfmaForce {
     int x16;
     int wm;
     int n_split;
+    int kg;
 };
 
 // The plan for an m x k x n product on a device with num_cu compute units,
 // with (have_ws) or without a workspace; force (or null) restricts the
 // choice.  Without a workspace: gemm_mfma.hip's kernel, unsplit.
-MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int num_cu, bool have_ws, const MfmaForce* force);
+MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, bool have_ws,
+                        const MfmaForce* force);
 
 // Launch with plan pl; ws (256-byte aligned, pl.ws_bytes) when pl.x16.
 void launch_gemm_mfma(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,

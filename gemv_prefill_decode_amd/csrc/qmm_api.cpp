@@ -95,12 +95,12 @@ void parse_tune() {
     g_tune.depth = d;
 }
 
-// QMM_MFMA_PLAN="x16,wm,n_split" forces the prefill plan of calls with a
-// workspace (tuning); unset: the cost model chooses.  Malformed -> bad.
+// QMM_MFMA_PLAN="x16,wm,n_split[,kg]" forces the prefill plan of calls with
+// a workspace (tuning); unset: the cost model chooses.  Malformed -> bad.
 struct MfmaForceState {
     bool set = false;
     bool bad = false;
-    qmm::MfmaForce f{0, 2, 1};
+    qmm::MfmaForce f{0, 2, 1, 1};
 };
 MfmaForceState g_force;
 std::once_flag g_force_once;
@@ -108,15 +108,16 @@ std::once_flag g_force_once;
 void parse_force() {
     const char* v = std::getenv("QMM_MFMA_PLAN");
     if (!v) return;
-    int a = -1, b = -1, c = -1;
+    int a = -1, b = -1, c = -1, d = 1;
     char tail = 0;
-    if (std::sscanf(v, "%d,%d,%d%c", &a, &b, &c, &tail) != 3 || (a != 0 && a != 1) ||
-        (b != 2 && b != 4) || (a == 0 && b != 2) || c < 1 || c > 16) {
+    const int got = std::sscanf(v, "%d,%d,%d,%d%c", &a, &b, &c, &d, &tail);
+    if ((got != 3 && got != 4) || (a != 0 && a != 1) || (b != 2 && b != 4) || (a == 0 && b != 2) ||
+        c < 1 || c > 16 || (d != 1 && d != 2) || (a == 1 && d != 1)) {
         g_force.bad = true;
         return;
     }
     g_force.set = true;
-    g_force.f = qmm::MfmaForce{a, b, c};
+    g_force.f = qmm::MfmaForce{a, b, c, d};
 }
 
 // Tuning for the current device; false if a tuning variable is malformed.
@@ -219,7 +220,7 @@ int gemm_impl(float* dst, const void* w, const float* x, int64_t m, int64_t k, i
     std::call_once(g_force_once, parse_force);
     if (g_force.bad) return QMM_ERR_RANGE;
     const qmm::MfmaPlan pl =
-        qmm::plan_gemm_mfma(m, k, n, tune.num_cu, ws != nullptr, g_force.set ? &g_force.f : nullptr);
+        qmm::plan_gemm_mfma(m, k, n, qtype, tune.num_cu, ws != nullptr, g_force.set ? &g_force.f : nullptr);
     if (ws) {
         if (!aligned(ws, 256)) return QMM_ERR_ALIGN;
         if (ws_bytes < pl.ws_bytes) return QMM_ERR_WORKSPACE;
@@ -281,7 +282,38 @@ int64_t qmm_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int qtype, int
     if (!gemv_tuning(&tune)) return -QMM_ERR_RANGE;
     std::call_once(g_force_once, parse_force);
     if (g_force.bad) return -QMM_ERR_RANGE;
-    return qmm::plan_gemm_mfma(m, k, n, tune.num_cu, true, g_force.set ? &g_force.f : nullptr).ws_bytes;
+    return qmm::plan_gemm_mfma(m, k, n, qtype, tune.num_cu, true, g_force.set ? &g_force.f : nullptr).ws_bytes;
+}
+
+int qmm_gemm_plan(int64_t m, int64_t k, int64_t n, int qtype, int path, int with_workspace, int32_t* out) {
+    if (!out) return QMM_ERR_NULL;
+    if (!valid_qt(qtype)) return QMM_ERR_QTYPE;
+    if (m < 1 || k < 1 || n < 1) return QMM_ERR_SHAPE;
+    if (m > INT_MAX || k > INT_MAX || n > INT_MAX) return QMM_ERR_RANGE;
+    if (path == QMM_PATH_AUTO) {
+        const int lim = qmm_gemv_max_n();
+        if (lim < 0) return QMM_ERR_RANGE;
+        path = n <= lim ? QMM_PATH_GEMV : QMM_PATH_MFMA;
+    }
+    if (path == QMM_PATH_GEMV) {
+        out[0] = QMM_PATH_GEMV;
+        out[1] = out[2] = out[3] = out[4] = out[5] = 0;
+        return QMM_OK;
+    }
+    if (path != QMM_PATH_MFMA) return QMM_ERR_PATH;
+    qmm::GemvTuning tune;
+    if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
+    std::call_once(g_force_once, parse_force);
+    if (g_force.bad) return QMM_ERR_RANGE;
+    const qmm::MfmaPlan pl = qmm::plan_gemm_mfma(m, k, n, qtype, tune.num_cu, with_workspace != 0,
+                                                g_force.set ? &g_force.f : nullptr);
+    out[0] = QMM_PATH_MFMA;
+    out[1] = pl.x16;
+    out[2] = 64 * pl.wm;
+    out[3] = pl.kg;
+    out[4] = pl.n_split;
+    out[5] = pl.sps;
+    return QMM_OK;
 }
 
 int qmm_gemm_ws(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qtype,

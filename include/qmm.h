@@ -135,6 +135,18 @@ int qmm_gemm_ws(float* dst, const void* w, const float* x, int64_t m, int64_t k,
 int64_t qmm_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int qtype, int path);
 
 /*
+ * qmm_gemm_plan: the kernels a call with these sizes runs on the current
+ * device, with (with_workspace != 0: qmm_gemm_ws) or without a workspace.
+ *   out  HOST int32[6], written: path (QMM_PATH_GEMV or QMM_PATH_MFMA); then
+ *        for the MFMA path: 1 if the activations are rounded to f16 by a
+ *        pre-pass (else 0), weight rows per tile, k groups per work group,
+ *        k splits, and 64-k steps per split (zeros on the GEMV path).
+ * Errors as qmm_gemm_workspace_bytes; QMM_ERR_NULL for a null out.
+ */
+int qmm_gemm_plan(int64_t m, int64_t k, int64_t n, int qtype, int path, int with_workspace,
+                  int32_t* out);
+
+/*
  * qmm_moe_gateup: the MoE gate and up projections over the routed experts
  * (memra-engine moe_rows_ceiling_bench.rs: gate/up planes, in_f -> n_ff,
  * n_used experts per token, per-pair f32 scales indexed plane*n_pairs+pair as

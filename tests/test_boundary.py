@@ -153,3 +153,21 @@ def test_gemm_ws_validates_before_launch():
     assert lib.qmm_gemm_ws(None, p, p, 10, 256, 40, 3, 2, None, 0, None) == 1
     # unknown path
     assert lib.qmm_gemm_ws(p, p, p, 10, 256, 40, 3, 9, None, 0, None) in (5, 7)
+
+
+def test_gemm_plan_reports_kernels():
+    """qmm_gemm_plan: GEMV below the crossover, MFMA above; without a
+    workspace never a pre-pass or a k split; bad arguments give a status."""
+    import gemv_prefill_decode_amd as qmm
+    _lib()
+    assert qmm.gemm_plan(4096, 4096, 8, "q4_k") == {"path": "gemv"}
+    p = qmm.gemm_plan(4096, 4096, 512, "q4_k", workspace=False)
+    assert p["path"] == "mfma" and p["x16"] == 0 and p["n_split"] == 1 and p["k_groups"] == 1
+    p = qmm.gemm_plan(1024, 4608, 512, "q4_k", "mfma")
+    assert p["n_split"] > 1 and p["steps_per_split"] % 2 == 0
+    assert p["n_split"] * p["steps_per_split"] >= 4608 // 64
+    import ctypes
+    lib = _lib()
+    out = (ctypes.c_int32 * 6)()
+    assert lib.qmm_gemm_plan(10, 256, 40, 9, 2, 1, out) == 4
+    assert lib.qmm_gemm_plan(10, 256, 40, 3, 2, 1, None) == 1
