@@ -96,28 +96,30 @@ void parse_tune() {
 }
 
 // QMM_MFMA_PLAN="x16,wm,n_split[,kg]" forces the prefill plan of calls with
-// a workspace (tuning); unset: the cost model chooses.  Malformed -> bad.
+// a workspace (tuning and tests): x16 0 (f32-activation kernel, 128-row
+// tiles, kg k groups) or 1 (f16 activations, (64*wm)-row tiles); unset: the
+// cost model chooses.  Malformed -> bad.
 struct MfmaForceState {
     bool set = false;
     bool bad = false;
     qmm::MfmaForce f{0, 2, 1, 1};
 };
-MfmaForceState g_force;
-std::once_flag g_force_once;
-
-void parse_force() {
+// Parsed on every call (tests and sweeps change it within one process).
+MfmaForceState parse_force() {
+    MfmaForceState g_force;
     const char* v = std::getenv("QMM_MFMA_PLAN");
-    if (!v) return;
+    if (!v) return g_force;
     int a = -1, b = -1, c = -1, d = 1;
     char tail = 0;
     const int got = std::sscanf(v, "%d,%d,%d,%d%c", &a, &b, &c, &d, &tail);
     if ((got != 3 && got != 4) || (a != 0 && a != 1) || (b != 2 && b != 4) || (a == 0 && b != 2) ||
         c < 1 || c > 16 || (d != 1 && d != 2) || (a == 1 && d != 1)) {
         g_force.bad = true;
-        return;
+        return g_force;
     }
     g_force.set = true;
     g_force.f = qmm::MfmaForce{a, b, c, d};
+    return g_force;
 }
 
 // Tuning for the current device; false if a tuning variable is malformed.
@@ -217,7 +219,7 @@ int gemm_impl(float* dst, const void* w, const float* x, int64_t m, int64_t k, i
         qmm::launch_gemv(dst, w, x, m, k, n, qtype, rb, tune, stream);
         return launch_status();
     }
-    std::call_once(g_force_once, parse_force);
+    const MfmaForceState g_force = parse_force();
     if (g_force.bad) return QMM_ERR_RANGE;
     const qmm::MfmaPlan pl =
         qmm::plan_gemm_mfma(m, k, n, qtype, tune.num_cu, ws != nullptr, g_force.set ? &g_force.f : nullptr);
@@ -280,7 +282,7 @@ int64_t qmm_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int qtype, int
     if (path != QMM_PATH_MFMA) return -QMM_ERR_PATH;
     qmm::GemvTuning tune;
     if (!gemv_tuning(&tune)) return -QMM_ERR_RANGE;
-    std::call_once(g_force_once, parse_force);
+    const MfmaForceState g_force = parse_force();
     if (g_force.bad) return -QMM_ERR_RANGE;
     return qmm::plan_gemm_mfma(m, k, n, qtype, tune.num_cu, true, g_force.set ? &g_force.f : nullptr).ws_bytes;
 }
@@ -303,7 +305,7 @@ int qmm_gemm_plan(int64_t m, int64_t k, int64_t n, int qtype, int path, int with
     if (path != QMM_PATH_MFMA) return QMM_ERR_PATH;
     qmm::GemvTuning tune;
     if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
-    std::call_once(g_force_once, parse_force);
+    const MfmaForceState g_force = parse_force();
     if (g_force.bad) return QMM_ERR_RANGE;
     const qmm::MfmaPlan pl = qmm::plan_gemm_mfma(m, k, n, qtype, tune.num_cu, with_workspace != 0,
                                                 g_force.set ? &g_force.f : nullptr);

@@ -19,9 +19,9 @@
  *    cached device properties (compute units, LDS sizes) and the parsed
  *    tuning variables (QMM_GEMV_MAX_N below; QMM_GEMV_WG_PER_CU 1..64,
  *    QMM_GEMV_ROWS 1..2, QMM_GEMV_DEPTH 2/4/8 for the streaming kernels'
- *    launch shape; QMM_MFMA_PLAN at qmm_gemm_ws; a malformed value makes
- *    the calls that use it return QMM_ERR_RANGE), so the calls can be
- *    recorded into a hipGraph.
+ *    launch shape; a malformed value makes the calls that use it return
+ *    QMM_ERR_RANGE; QMM_MFMA_PLAN is read again at every call that plans a
+ *    prefill), so the calls can be recorded into a hipGraph.
  *  - Arguments are validated on the host before anything is launched; a
  *    rejected call returns a non-zero qmm_status and launches nothing.  A
  *    launch failure reported by the runtime returns QMM_ERR_LAUNCH.
@@ -115,7 +115,8 @@ int qmm_gemm_path(float* dst, const void* w, const float* x,
  * Both kernels round W and x to f16 identically (RNE), so the tolerance is
  * the one of qmm_gemm.  The plan is a pure function of (m, k, n) and the
  * device's compute-unit count; the environment variable
- * QMM_MFMA_PLAN="x16,wm,n_split" forces it (tuning only; malformed ->
+ * QMM_MFMA_PLAN="x16,wm,n_split[,kg]" forces it (tuning and tests only:
+ * x16 0 with wm 2 and kg 1 or 2, or x16 1 with wm 2 or 4; malformed ->
  * QMM_ERR_RANGE).
  *   workspace        DEVICE memory, 256-byte aligned, of at least
  *                    qmm_gemm_workspace_bytes(m, k, n, qtype, path) bytes, or

@@ -297,3 +297,28 @@ def test_split_k_shared_workspace_growing_tile_count():
         got = qmm.gemm(to_dev(w), to_dev(x), m, qt, path="mfma", workspace=ws)
         torch.cuda.synchronize()
         check_full(qt, w, x, m, k, n, got.cpu().numpy(), TAU_F16, f"shared ws {m}x{k}x{n}")
+
+
+# Every prefill kernel family, forced through QMM_MFMA_PLAN on a ragged shape
+# (m, n not multiples of any tile; k with a partial split): x16, tile rows
+# (wm*64), k splits, k groups.
+FORCED_PLANS = ["0,2,1,1", "0,2,3,1", "0,2,1,2", "0,2,3,2", "1,2,1", "1,2,3", "1,4,1", "1,4,3"]
+
+
+@pytest.mark.parametrize("plan", FORCED_PLANS)
+@pytest.mark.parametrize("qt", ["q4_k", "q6_k", "q8_0", "nvfp4", "q4_0", "f32"])
+def test_forced_prefill_plans(plan, qt, monkeypatch):
+    import gemv_prefill_decode_amd as qmm
+    x16, wm = int(plan.split(",")[0]), int(plan.split(",")[1])
+    kg = int(plan.split(",")[3]) if plan.count(",") == 3 else 1
+    m, k, n = 300, 1536 if qt != "q6_k" else 1792, 270
+    if qt == "f32" and kg == 2:
+        pytest.skip("not a plan the library runs for f32 weights")
+    monkeypatch.setenv("QMM_MFMA_PLAN", plan)
+    p = qmm.gemm_plan(m, k, n, qt, "mfma")
+    assert (p["x16"], p["tile_rows"], p["k_groups"]) == (x16, 64 * wm, kg), p
+    note(f"forced plan {plan} {qt} {p}")
+    w = weights(qt, m, k, 60)
+    x = acts(n, k, 60)
+    got = gpu_gemm(qt, w, x, m, "mfma")
+    check_full(qt, w, x, m, k, n, got, TAU_F16, f"plan {plan} {qt}")
