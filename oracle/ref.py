@@ -17,6 +17,14 @@ plane*n_pairs + pair, as the pointer table is):
     out_P[p, r] = scale[P*n_pairs + p] * sum_c W_P[e_p][r, c] * x[tau_p, c]
 
 for pair p = tau*n_used + s with expert e_p = ids[tau, s].
+
+The MoE down projection (the same page's down arm: one plane of d_model rows
+over n_ff inputs per expert, each pair's own activation row, the down plane's
+scale, the result accumulated into a zeroed y over the token's pairs):
+
+    y[tau, r] = sum_s scale[p] * sum_c Wd[e_p][r, c] * act[p, c]
+
+with the slots s taken in order; S_y sums |scale[p] * Wd[e_p][r, c] * act[p, c]|.
 """
 
 from __future__ import annotations
@@ -106,6 +114,54 @@ def moe_ref_pairs_rows(name: str, w_plane, ids, scales, x, plane: int, n_expert:
         f = sc[plane * n_pairs + p]
         val[i] = f * float(W @ xv)
         tol[i] = abs(f) * float(np.abs(W) @ np.abs(xv))
+    return val, tol
+
+
+def moe_down_ref(name: str, w_down, ids, scales, act, n_expert: int, n_ff: int, d_model: int):
+    """(y, S_y, pair, S_pair): y and S_y float64 [t, d_model]; the per-pair
+    terms scale[p] * Wd[e_p] @ act[p] and their S as float64 [n_pairs, d_model]."""
+    ids = np.asarray(ids, dtype=np.int64)
+    t, n_used = ids.shape
+    n_pairs = t * n_used
+    A = np.asarray(act, dtype=np.float32).reshape(n_pairs, n_ff).astype(np.float64)
+    sc = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    buf = np.asarray(w_down).reshape(-1).view(np.uint8)
+    per = buf.size // n_expert
+    pair = np.empty((n_pairs, d_model))
+    pair_S = np.empty((n_pairs, d_model))
+    cache = {}
+    for p in range(n_pairs):
+        e = int(ids.reshape(-1)[p])
+        if e not in cache:
+            cache[e] = decode(name, buf[e * per:(e + 1) * per], d_model, n_ff)
+        W = cache[e]
+        pair[p] = sc[p] * (W @ A[p])
+        pair_S[p] = abs(sc[p]) * (np.abs(W) @ np.abs(A[p]))
+    y = pair.reshape(t, n_used, d_model).sum(axis=1)
+    S = pair_S.reshape(t, n_used, d_model).sum(axis=1)
+    return y, S, pair, pair_S
+
+
+def moe_down_ref_rows(name: str, w_down, ids, scales, act, n_expert: int, n_ff: int,
+                      d_model: int, toks, rows):
+    """(ref, S) of y[toks[i], rows[i]], sampled: only the sampled weight rows
+    of the token's experts are decoded."""
+    ids = np.asarray(ids, dtype=np.int64)
+    t, n_used = ids.shape
+    buf = np.asarray(w_down).reshape(-1).view(np.uint8)
+    rb = buf.size // (n_expert * d_model)
+    A = np.asarray(act, dtype=np.float32).reshape(t * n_used, n_ff).astype(np.float64)
+    sc = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    val = np.zeros(len(toks))
+    tol = np.zeros(len(toks))
+    for i, (tau, r) in enumerate(zip(np.asarray(toks, dtype=np.int64), np.asarray(rows, dtype=np.int64))):
+        for s in range(n_used):
+            p = int(tau) * n_used + s
+            e = int(ids[tau, s])
+            row = (e * d_model + int(r)) * rb
+            W = decode(name, buf[row:row + rb], 1, n_ff)[0]
+            val[i] += sc[p] * float(W @ A[p])
+            tol[i] += abs(sc[p]) * float(np.abs(W) @ np.abs(A[p]))
     return val, tol
 
 

@@ -6,6 +6,9 @@
 - invariants: row permutation of x, linearity, S >= |ref|
 - MoE: brute force per pair; renaming experts together with their weights
   leaves the outputs unchanged
+- MoE down: brute force per token (pair activations, slot sum by fsum); one
+  slot per token reduces it to a gate/up plane; expert renaming and slot
+  order leave it unchanged
 - planted mistakes (in the oracle, on the CPU) are caught by these pins
 """
 
@@ -131,6 +134,77 @@ def test_moe_sampled_rows_equal_brute_force():
             f = np.float64(sc[plane * n_pairs + p])
             assert abs(val[i] - f * bf) <= 1e-12 * max(1.0, abs(f * bf))
             assert tol[i] >= abs(val[i])
+
+
+def _down_case(n_expert=5, n_ff=128, d_model=6, t=3, n_used=2, seed=7):
+    wd = np.concatenate([gen.nvfp4_rows(d_model, n_ff, 0x4242 + e) for e in range(n_expert)])
+    ids = gen.expert_ids(t, n_used, n_expert, seed)
+    sc = gen.pair_scales(t * n_used)
+    act = gen.xorshift_f32(t * n_used * n_ff, 1234)
+    return wd, ids, sc, act
+
+
+def test_moe_down_ref_brute_force():
+    """y[tau, r] against the literal scalar decoder: each pair's own
+    activation row and scale, the token's slots summed exactly (fsum)."""
+    import math
+    n_expert, n_ff, d_model, t, n_used = 5, 128, 6, 3, 2
+    wd, ids, sc, act = _down_case(n_expert, n_ff, d_model, t, n_used)
+    y, S, pair, pair_S = ref.moe_down_ref("nvfp4", wd, ids, sc, act, n_expert, n_ff, d_model)
+    per = d_model * formats.row_bytes("nvfp4", n_ff)
+    for tau in range(t):
+        terms = [[] for _ in range(d_model)]
+        for s in range(n_used):
+            p = tau * n_used + s
+            e = ids[tau, s]
+            blk = bytes(wd[e * per:(e + 1) * per])
+            a = act[p * n_ff:(p + 1) * n_ff].tolist()
+            bf = scalar.gemm("nvfp4", blk, [a], d_model, n_ff, 1)[0]
+            for r in range(d_model):
+                terms[r].append(float(np.float64(sc[p])) * bf[r])
+                assert abs(pair[p, r] - terms[r][-1]) <= 1e-12 * max(1.0, abs(terms[r][-1]))
+        for r in range(d_model):
+            want = math.fsum(terms[r])
+            assert abs(y[tau, r] - want) <= 1e-12 * max(1.0, sum(abs(v) for v in terms[r]))
+            assert S[tau, r] >= abs(y[tau, r])
+
+
+def test_moe_down_ref_special_cases():
+    """One slot per token reduces the down projection to the gate/up plane
+    with the pair's activation as the token row; renaming experts with their
+    weights and permuting the slots of a token leave y unchanged."""
+    n_expert, n_ff, d_model, t = 4, 64, 5, 3
+    wd, ids1, sc1, act1 = _down_case(n_expert, n_ff, d_model, t, 1, seed=3)
+    y, _, _, _ = ref.moe_down_ref("nvfp4", wd, ids1, sc1, act1, n_expert, n_ff, d_model)
+    g, _, _, _ = ref.moe_ref("nvfp4", wd, wd, ids1, np.concatenate([sc1, sc1]), act1, n_expert,
+                             n_ff, d_model)
+    assert np.allclose(y, g, rtol=1e-13, atol=1e-13)
+    n_used = 3
+    wd, ids, sc, act = _down_case(n_expert, n_ff, d_model, t, n_used, seed=9)
+    y, S, _, _ = ref.moe_down_ref("nvfp4", wd, ids, sc, act, n_expert, n_ff, d_model)
+    per = d_model * formats.row_bytes("nvfp4", n_ff)
+    perm = np.array([2, 0, 3, 1])
+    inv = np.argsort(perm)
+    wd2 = np.concatenate([wd[inv[e] * per:(inv[e] + 1) * per] for e in range(n_expert)])
+    y2, _, _, _ = ref.moe_down_ref("nvfp4", wd2, perm[ids], sc, act, n_expert, n_ff, d_model)
+    assert np.array_equal(y2, y)
+    # reverse the slots of every token (ids, scales and activation rows move together)
+    order = np.concatenate([tau * n_used + np.arange(n_used)[::-1] for tau in range(t)])
+    y3, S3, _, _ = ref.moe_down_ref("nvfp4", wd, ids[:, ::-1].copy(), sc[order],
+                                    act.reshape(t * n_used, n_ff)[order].reshape(-1), n_expert,
+                                    n_ff, d_model)
+    assert np.allclose(y3, y, rtol=1e-13, atol=1e-13) and np.allclose(S3, S, rtol=1e-13)
+
+
+def test_moe_down_sampled_rows_equal_full():
+    n_expert, n_ff, d_model, t, n_used = 5, 128, 7, 4, 3
+    wd, ids, sc, act = _down_case(n_expert, n_ff, d_model, t, n_used, seed=21)
+    y, S, _, _ = ref.moe_down_ref("nvfp4", wd, ids, sc, act, n_expert, n_ff, d_model)
+    toks = np.array([0, 3, 2, 1, 3])
+    rows = np.array([0, 6, 3, 5, 0])
+    val, tol = ref.moe_down_ref_rows("nvfp4", wd, ids, sc, act, n_expert, n_ff, d_model, toks, rows)
+    assert np.allclose(val, y[toks, rows], rtol=1e-12, atol=1e-12)
+    assert np.allclose(tol, S[toks, rows], rtol=1e-12, atol=1e-12)
 
 
 def test_tolerance_check_semantics():
