@@ -21,7 +21,7 @@ import threading
 
 __all__ = [
     "QTYPES", "PATHS", "QmmError", "lib_path", "load", "gemm", "workspace_bytes", "gemm_plan",
-    "plan_kernel_name", "moe_gateup",
+    "plan_kernel_name", "moe_gateup", "moe_down",
     "stream_loadonly",
     "row_bytes", "block_elems", "gemv_max_n", "status_str", "abi_version",
 ]
@@ -69,6 +69,8 @@ def load() -> ctypes.CDLL:
         lib.qmm_gemm_plan.restype = i32
         lib.qmm_moe_gateup.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
         lib.qmm_moe_gateup.restype = i32
+        lib.qmm_moe_down.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+        lib.qmm_moe_down.restype = i32
         lib.qmm_stream_loadonly.argtypes = [vp, vp, i64, i64, i32, vp]
         lib.qmm_stream_loadonly.restype = i32
         lib.qmm_row_bytes.argtypes = [i32, i64]
@@ -252,6 +254,36 @@ def moe_gateup(w_gate, w_up, expert_ids, pair_scale, x, n_expert: int, n_ff: int
     if st != 0:
         raise QmmError(st, "qmm_moe_gateup")
     return gate_out, up_out
+
+
+def moe_down(w_down, expert_ids, pair_scale, act, n_expert: int, d_model: int, qtype="nvfp4",
+             y=None, pair_out=None, stream=None):
+    """MoE down projection; returns (y, pair_out): y float32 [t, d_model] (the
+    token's slots summed in order), pair_out float32 [t*n_used, d_model] (each
+    pair's scaled projection).  expert_ids: int32 [t, n_used]; pair_scale:
+    float32 [t*n_used] (the down plane's); act: float32 [t*n_used, n_ff]."""
+    import torch
+    lib = load()
+    qt = _qt(qtype)
+    t, n_used = expert_ids.shape
+    n_pairs = t * n_used
+    n_p2, n_ff = act.shape
+    if n_p2 != n_pairs:
+        raise ValueError("act must hold one row per pair (t*n_used rows)")
+    if pair_scale.numel() != n_pairs:
+        raise ValueError("pair_scale must hold t*n_used floats")
+    if y is None:
+        y = torch.empty((t, d_model), dtype=torch.float32, device=act.device)
+    if pair_out is None:
+        pair_out = torch.empty((n_pairs, d_model), dtype=torch.float32, device=act.device)
+    st = lib.qmm_moe_down(_dev(y, "y", torch.float32), _dev(pair_out, "pair_out", torch.float32),
+                          _dev(w_down, "w_down"), _dev(expert_ids, "expert_ids", torch.int32),
+                          _dev(pair_scale, "pair_scale", torch.float32),
+                          _dev(act, "act", torch.float32), t, n_used, n_expert, n_ff, d_model, qt,
+                          _stream(stream))
+    if st != 0:
+        raise QmmError(st, "qmm_moe_down")
+    return y, pair_out
 
 
 def stream_loadonly(w, m: int, k: int, qtype, sink=None, stream=None):

@@ -800,13 +800,16 @@ __global__ __launch_bounds__(256) void gemv_kernel(float* __restrict__ dst,
 
 // ------------------------------------------------------------------ MoE gate/up
 // grid: x = work groups per (pair, plane) (their waves stride over the row
-// groups of one expert's n_ff rows), y = pair p, z = plane.
+// groups of one expert's n_ff rows), y = pair p, z = plane (2: gate and up;
+// 1: the down projection's single plane).
 // The work groups of the FIRST pair routed to expert e gather every pair
-// routed to e and apply e's rows to all their tokens, so each selected
-// expert's rows are read once per call when it has at most MOE_NT tokens (in
-// chunks of MOE_NT tokens otherwise), with the chunk's activations staged in
-// LDS; the work groups of later pairs of the same expert exit after the
-// check.  The decision depends on expert_ids only.
+// routed to e and apply e's rows to all their activation rows, so each
+// selected expert's rows are read once per call when it has at most MOE_NT
+// pairs (in chunks of MOE_NT otherwise), with the chunk's activations staged
+// in LDS; the work groups of later pairs of the same expert exit after the
+// check.  The decision depends on expert_ids only.  The activation row of
+// pair q is its token's row q / n_used (gate/up) or its own row q
+// (act_pair: the down projection, whose input is the pair's SwiGLU output).
 constexpr int MOE_CHUNK = 256;  // pairs examined (and gathered) per pass
 constexpr int MOE_NT = 3;       // token rows staged in LDS at a time
 constexpr unsigned MOE_MIN_WG = 32;  // work groups per (pair, plane) at least
@@ -850,7 +853,7 @@ __global__ __launch_bounds__(256) void moe_gateup_kernel(
     float* __restrict__ gate_out, float* __restrict__ up_out, const uint8_t* __restrict__ w_gate,
     const uint8_t* __restrict__ w_up, const int* __restrict__ ids, const float* __restrict__ pscale,
     const float* __restrict__ x, int t, int n_used, int n_expert, int in_f, int n_ff, int rb,
-    int lpr_log2, int n_rg, int xl) {
+    int lpr_log2, int n_rg, int xl, int act_pair) {
     __shared__ int plist[MOE_CHUNK];
     __shared__ int tlist[MOE_CHUNK];
     __shared__ int wcnt[4];
@@ -887,7 +890,7 @@ __global__ __launch_bounds__(256) void moe_gateup_kernel(
 
     const StreamGeom g{(plane == 0 ? w_gate : w_up) + (int64_t)e * n_ff * rb, n_ff, rb, in_f,
                        lpr_log2};
-    const rsrc_t xr = make_rsrc(x, (uint32_t)t * (uint32_t)in_f * 4u);
+    const rsrc_t xr = make_rsrc(x, (uint32_t)(act_pair ? n_pairs : t) * (uint32_t)in_f * 4u);
     for (int q0 = p; q0 < n_pairs; q0 += MOE_CHUNK) {
         // gather the pairs of this chunk routed to e, in pair order
         const int q = q0 + tid;
@@ -902,7 +905,7 @@ __global__ __launch_bounds__(256) void moe_gateup_kernel(
         for (int wv = 0; wv < wave; ++wv) off += wcnt[wv];
         if (hit) {
             plist[off + before] = q;
-            tlist[off + before] = q / n_used;
+            tlist[off + before] = act_pair ? q : q / n_used;  // activation row
         }
         const int cnt = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
         __syncthreads();
@@ -1166,8 +1169,8 @@ void launch_gemv(float* dst, const void* w, const float* x, int64_t m, int64_t k
 template <int QT>
 static void launch_moe_qt(float* g, float* u, const uint8_t* wg, const uint8_t* wu, const int* ids,
                           const float* sc, const float* x, int64_t t, int64_t n_used,
-                          int64_t n_expert, int64_t in_f, int64_t n_ff, int64_t rb,
-                          const GemvTuning& tune, hipStream_t st) {
+                          int64_t n_expert, int64_t in_f, int64_t n_ff, int64_t rb, int planes,
+                          int act_pair, const GemvTuning& tune, hipStream_t st) {
     with_rd<1>(tune, [&](auto Rc, auto Dc) {
         constexpr int R = decltype(Rc)::value, D = decltype(Dc)::value;
         const int l = lpr_for(QT, in_f);
@@ -1176,16 +1179,16 @@ static void launch_moe_qt(float* g, float* u, const uint8_t* wg, const uint8_t* 
         // at most one set of work groups per distinct expert and plane is
         // active; with many pairs the sets are not all distinct, so each set
         // gets at least MOE_MIN_WG work groups
-        const int64_t active = 2 * (n_pairs < n_expert ? n_pairs : n_expert);
+        const int64_t active = planes * (n_pairs < n_expert ? n_pairs : n_expert);
         unsigned gx = stream_grid(n_rg, active, tune);
         const unsigned need = (unsigned)((n_rg + 3) / 4);
         if (gx < MOE_MIN_WG) gx = need < MOE_MIN_WG ? need : MOE_MIN_WG;
-        const dim3 grid(gx, (unsigned)n_pairs, 2);
+        const dim3 grid(gx, (unsigned)n_pairs, (unsigned)planes);
         const int64_t lds = (int64_t)xlds_floats(MOE_NT, (int)in_f, GUnit<QT>::RUNS > 0) * 4;
         const int xl = lds <= XLDS_MAX_BYTES;
         moe_gateup_kernel<QT, R, D><<<grid, 256, (size_t)(xl ? lds : 0), st>>>(
             g, u, wg, wu, ids, sc, x, (int)t, (int)n_used, (int)n_expert, (int)in_f, (int)n_ff,
-            (int)rb, l, (int)n_rg, xl);
+            (int)rb, l, (int)n_rg, xl, act_pair);
     });
 }
 
@@ -1194,7 +1197,47 @@ void launch_moe(float* g, float* u, const void* wg, const void* wu, const int* i
                 int64_t n_ff, int qt, int64_t rb, const GemvTuning& tune, hipStream_t st) {
     const uint8_t* a = (const uint8_t*)wg;
     const uint8_t* b = (const uint8_t*)wu;
-    QMM_QT_SWITCH(qt, (launch_moe_qt<Q>(g, u, a, b, ids, sc, x, t, n_used, n_expert, in_f, n_ff, rb, tune, st)))
+    QMM_QT_SWITCH(qt, (launch_moe_qt<Q>(g, u, a, b, ids, sc, x, t, n_used, n_expert, in_f, n_ff, rb,
+                                        2, 0, tune, st)))
+}
+
+// ------------------------------------------------------------------ MoE down
+// y[tau*d + r] = sum over s < n_used, in order, of pair_out[(tau*n_used + s)*d + r].
+// One thread per four consecutive outputs when d is a multiple of 4.
+template <int V>
+__global__ __launch_bounds__(256) void moe_slot_sum_kernel(float* __restrict__ y,
+                                                           const float* __restrict__ pair_out,
+                                                           int64_t t, int n_used, int64_t d) {
+    const int64_t nv = t * d / V;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nv; i += (int64_t)gridDim.x * 256) {
+        const int64_t tau = i * V / d, r = i * V - tau * d;
+        const float* src = pair_out + tau * n_used * d + r;
+        if constexpr (V == 4) {
+            f32x4 acc = *(const f32x4*)src;
+            for (int s = 1; s < n_used; ++s) acc += *(const f32x4*)(src + (int64_t)s * d);
+            *(f32x4*)(y + i * 4) = acc;
+        } else {
+            float acc = src[0];
+            for (int s = 1; s < n_used; ++s) acc += src[(int64_t)s * d];
+            y[i] = acc;
+        }
+    }
+}
+
+void launch_moe_down(float* y, float* pair_out, const void* wd, const int* ids, const float* sc,
+                     const float* act, int64_t t, int64_t n_used, int64_t n_expert, int64_t n_ff,
+                     int64_t d_model, int qt, int64_t rb, const GemvTuning& tune, hipStream_t st) {
+    const uint8_t* a = (const uint8_t*)wd;
+    QMM_QT_SWITCH(qt, (launch_moe_qt<Q>(pair_out, pair_out, a, a, ids, sc, act, t, n_used, n_expert,
+                                        n_ff, d_model, rb, 1, 1, tune, st)))
+    const bool v4 = (d_model & 3) == 0 && ((uintptr_t)y & 15) == 0 && ((uintptr_t)pair_out & 15) == 0;
+    const int64_t nv = t * d_model / (v4 ? 4 : 1);
+    int64_t blocks = (nv + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (v4)
+        moe_slot_sum_kernel<4><<<dim3((unsigned)blocks), 256, 0, st>>>(y, pair_out, t, (int)n_used, d_model);
+    else
+        moe_slot_sum_kernel<1><<<dim3((unsigned)blocks), 256, 0, st>>>(y, pair_out, t, (int)n_used, d_model);
 }
 
 template <int QT>

@@ -76,6 +76,14 @@ void launch_moe(float* gate_out, float* up_out, const void* w_gate, const void* 
                 int64_t n_expert, int64_t in_f, int64_t n_ff, int qt, int64_t rb,
                 const GemvTuning& tune, hipStream_t st);
 
+// MoE down projection: per-pair scaled rows into pair_out [n_pairs][d_model]
+// (the gate/up kernel with one plane and each pair's own activation row),
+// then y[tau] = the token's n_used pair rows summed in slot order.
+void launch_moe_down(float* y, float* pair_out, const void* w_down, const int* ids,
+                     const float* scale, const float* act, int64_t t, int64_t n_used,
+                     int64_t n_expert, int64_t n_ff, int64_t d_model, int qt, int64_t rb,
+                     const GemvTuning& tune, hipStream_t st);
+
 void launch_loadonly(uint32_t* sink, const void* w, int64_t m, int64_t k, int qt, int64_t rb,
                      const GemvTuning& tune, hipStream_t st);
 

@@ -361,6 +361,31 @@ int qmm_moe_gateup(float* gate_out, float* up_out, const void* w_gate, const voi
     return launch_status();
 }
 
+int qmm_moe_down(float* y, float* pair_out, const void* w_down, const int32_t* expert_ids,
+                 const float* pair_scale, const float* act, int64_t t, int64_t n_used,
+                 int64_t n_expert, int64_t n_ff, int64_t d_model, int qtype, hipStream_t stream) {
+    if (!y || !pair_out || !w_down || !expert_ids || !pair_scale || !act) return QMM_ERR_NULL;
+    if (t < 1 || n_used < 1 || n_expert < 1 || n_used > n_expert) return QMM_ERR_SHAPE;
+    int64_t rb;
+    int64_t rows;
+    if (!mul_ok(n_expert, d_model, &rows)) return QMM_ERR_SHAPE;
+    int st = check_weights(w_down, rows, n_ff, qtype, &rb);
+    if (st) return st;
+    if (!aligned(act, 16) || !aligned(y, 4) || !aligned(pair_out, 4) || !aligned(pair_scale, 4) ||
+        !aligned(expert_ids, 4))
+        return QMM_ERR_ALIGN;
+    int64_t n_pairs, outs;
+    if (!mul_ok(t, n_used, &n_pairs) || !mul_ok(n_pairs, d_model, &outs)) return QMM_ERR_SHAPE;
+    if (n_pairs > 65535 || d_model > INT_MAX || n_pairs * n_ff * 4 >= ((int64_t)1 << 31))
+        return QMM_ERR_RANGE;
+    if (qmm::gemv_max_window_bytes(qtype, n_ff, rb) >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+    qmm::GemvTuning tune;
+    if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
+    qmm::launch_moe_down(y, pair_out, w_down, expert_ids, pair_scale, act, t, n_used, n_expert, n_ff,
+                         d_model, qtype, rb, tune, stream);
+    return launch_status();
+}
+
 int qmm_stream_loadonly(uint32_t* sink, const void* w, int64_t m, int64_t k, int qtype,
                         hipStream_t stream) {
     if (!sink) return QMM_ERR_NULL;

@@ -173,6 +173,37 @@ int qmm_moe_gateup(float* gate_out, float* up_out,
                    int64_t in_f, int64_t n_ff, int qtype, hipStream_t stream);
 
 /*
+ * qmm_moe_down: the MoE down projection (memra-engine moe_rows_ceiling_bench.rs,
+ * the down arm: one plane of d_model rows over n_ff inputs per expert, each
+ * pair's own activation row (the SwiGLU output of its gate/up pair), the down
+ * plane's per-pair scale, and the token's pairs accumulated into a zeroed y).
+ * With n_pairs = t*n_used, pair p = tau*n_used + s and e = expert_ids[p]:
+ *     pair_out[p*d_model + r] = pair_scale[p] * sum_c Wd[e][r][c] * act[p*n_ff + c]
+ *     y[tau*d_model + r]      = sum over s = 0 .. n_used-1, in that order, of
+ *                               pair_out[(tau*n_used + s)*d_model + r]
+ *   y           DEVICE float[t*d_model], written (not accumulated into).
+ *   pair_out    DEVICE float[n_pairs*d_model], written: the per-pair terms.
+ *               Must not overlap y.
+ *   w_down      DEVICE, n_expert*d_model rows of row_bytes(qtype, n_ff) bytes
+ *               (expert-major), 16-byte aligned.
+ *   expert_ids  DEVICE int32[n_pairs]; an id outside [0, n_expert) makes that
+ *               pair's pair_out row, and so its token's y row, NaN (no
+ *               out-of-range read).
+ *   pair_scale  DEVICE float[n_pairs]: the down plane's scales (the third
+ *               n_pairs block of the page's 3*n_pairs scale array).
+ *   act         DEVICE float[n_pairs*n_ff], 16-byte aligned.
+ *   qtype       QMM_NVFP4 (the other formats are accepted too).
+ * Two launches on stream: the gate/up kernel with one plane and per-pair
+ * activation rows (each selected expert's rows read once per call), then a
+ * slot sum in fixed order, so identical calls give bit-identical results.
+ * f32 arithmetic; y within 1e-5*sum_s |pair_scale|*sum_c |w*act|.
+ * Errors as qmm_moe_gateup.
+ */
+int qmm_moe_down(float* y, float* pair_out, const void* w_down, const int32_t* expert_ids,
+                 const float* pair_scale, const float* act, int64_t t, int64_t n_used,
+                 int64_t n_expert, int64_t n_ff, int64_t d_model, int qtype, hipStream_t stream);
+
+/*
  * qmm_stream_loadonly: the load-only twin of the GEMV (memra-engine
  * moe_rows_ceiling_bench.rs, the "loadonly" ceiling-probe arm: the same
  * addresses with the arithmetic deleted).  Reads every byte of the m packed

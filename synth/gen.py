@@ -33,6 +33,8 @@ __all__ = [
     "SEED_MOE_W",
     "SEED_MOE_X",
     "SEED_EXPERTS",
+    "SEED_MOE_DOWN_W",
+    "SEED_MOE_ACT",
 ]
 
 # Numerical Recipes LCG constants used by every byte/float stream on the pages
@@ -52,6 +54,11 @@ SEED_X = 0x9E3779B9
 SEED_MOE_W = 0x8181
 SEED_MOE_X = 91
 SEED_EXPERTS = 0xE4E4
+# MoE down projection (memra `moe_rows_ceiling_bench.rs`, the down arm): the
+# page's rows seed, plus the expert index for distinct experts, and the seed of
+# its synthetic per-pair activations (a stand-in for the SwiGLU output).
+SEED_MOE_DOWN_W = 0x4242
+SEED_MOE_ACT = 1234
 BUFFER_STRIDE = 0x9E37
 
 _BLOCK = 1 << 16

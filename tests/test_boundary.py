@@ -29,7 +29,7 @@ def _declared():
 
 def test_header_declares_entry_points():
     names = _declared()
-    for want in ("qmm_gemm", "qmm_gemm_path", "qmm_moe_gateup", "qmm_row_bytes",
+    for want in ("qmm_gemm", "qmm_gemm_path", "qmm_moe_gateup", "qmm_moe_down", "qmm_row_bytes",
                  "qmm_block_elems", "qmm_status_str", "qmm_stream_loadonly"):
         assert want in names
 
@@ -97,6 +97,13 @@ def test_validation_rejects_before_launch():
     assert m(A, A, A, A, A, A, A, 1, 9, 8, 4096, 2048, 5, s0) == 2    # n_used > n_expert
     assert m(A, A, A, A, A, A, A, 1, 8, 64, 4000, 2048, 5, s0) == 3   # in_f % 64
     assert m(A, A, A, A, A, A, A, 1, 8, 64, 4096, 2048, 8, s0) == 4   # qtype
+    d = lib.qmm_moe_down
+    assert d(A, z, A, A, A, A, 1, 8, 64, 2048, 4096, 5, s0) == 1     # null pair_out
+    assert d(A, A, A, A, A, A, 1, 9, 8, 2048, 4096, 5, s0) == 2      # n_used > n_expert
+    assert d(A, A, A, A, A, A, 0, 8, 64, 2048, 4096, 5, s0) == 2     # t = 0
+    assert d(A, A, A, A, A, A, 1, 8, 64, 2000, 4096, 5, s0) == 3     # n_ff % 64
+    assert d(A, A, A, A, A, A, 1, 8, 64, 2048, 4096, 8, s0) == 4     # qtype
+    assert d(A, A, A, A, A, A, 70000, 1, 64, 64, 4096, 5, s0) == 8   # more pairs than the grid
     lo = lib.qmm_stream_loadonly
     assert lo(z, A, 64, 256, 3, s0) == 1
     assert lo(A, A, 64, 255, 3, s0) == 3

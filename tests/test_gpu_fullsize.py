@@ -6,6 +6,7 @@ by one (always including the four corners), on the same seeded inputs.
   - LFM2.5-350M-shaped prefill n=512: 4 shapes x f32/q4_0/q8_0/q4_k/q6_k
   - decode sweep n in {1,4,8,16,32}: q4_k/q6_k at 4608x1024 and 14336x4096
   - NVFP4 MoE gate/up: 64 experts, 8 used, in_f 4096, n_ff 2048, t in {1,16}
+  - NVFP4 MoE down: 64 experts of 4096 rows over 2048 inputs, t in {1,16}
   - 8B-class prefill n=2048: q4_k/q6_k at 14336x4096 and 4096x14336
 """
 
@@ -88,6 +89,31 @@ def test_moe_gateup_full_size(t):
                                       pairs, rows)
         ok, worst = ref.tolerance_check(outs[plane][pairs, rows], r, S, TAU_F32)
         assert ok, f"moe t={t} plane {plane}: worst {worst:.3g}"
+
+
+@pytest.mark.parametrize("t", [1, 16])
+def test_moe_down_full_size(t):
+    """The down projection at its full shape: 64 experts of 4096 rows over
+    2048 inputs, 8 per token, the same expert draw as the gate/up."""
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    n_expert, n_ff, d_model, n_used = 64, 2048, 4096, 8
+    note(f"moe down full size t={t}")
+    wd = np.concatenate([gen.nvfp4_rows(d_model, n_ff, gen.SEED_MOE_DOWN_W + e) for e in range(n_expert)])
+    ids = gen.expert_ids(t, n_used, n_expert, gen.SEED_EXPERTS)
+    n_pairs = t * n_used
+    sc = gen.pair_scales(3 * n_pairs)[2 * n_pairs:]          # the down plane's block
+    act = gen.xorshift_f32(n_pairs * n_ff, gen.SEED_MOE_ACT).reshape(n_pairs, n_ff)
+    y, _ = qmm.moe_down(to_dev(wd), to_dev(ids), to_dev(sc), to_dev(act), n_expert, d_model, "nvfp4")
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(100 + t)
+    toks = np.concatenate([rng.integers(0, t, 500), [0, 0, t - 1, t - 1]])
+    rows = np.concatenate([rng.integers(0, d_model, 500), [0, d_model - 1, 0, d_model - 1]])
+    r, S = ref.moe_down_ref_rows("nvfp4", wd, ids, sc, act, n_expert, n_ff, d_model, toks, rows)
+    ok, worst = ref.tolerance_check(y[toks, rows], r, S, TAU_F32)
+    assert ok, f"moe down t={t}: worst {worst:.3g}"
 
 
 @pytest.mark.parametrize("qt", ["q4_k", "q6_k"])

@@ -239,6 +239,74 @@ def test_moe_invalid_expert_id_gives_nan():
     assert ref.tolerance_check(g[[0, 2]], rg[[0, 2]], Sg[[0, 2]], TAU_F32)[0]
 
 
+def _down_inputs(n_expert, n_ff, d_model, t, n_used, seed=0):
+    wd = np.concatenate([gen.nvfp4_rows(d_model, n_ff, gen.SEED_MOE_DOWN_W + e) for e in range(n_expert)])
+    ids = gen.expert_ids(t, n_used, n_expert, gen.SEED_EXPERTS + seed)
+    sc = gen.pair_scales(t * n_used)
+    act = gen.xorshift_f32(t * n_used * n_ff, gen.SEED_MOE_ACT + seed).reshape(t * n_used, n_ff)
+    return wd, ids, sc, act
+
+
+def _gpu_down(wd, ids, sc, act, n_expert, d_model, qt="nvfp4"):
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    y, pair = qmm.moe_down(to_dev(wd), to_dev(ids.astype(np.int32)), to_dev(sc), to_dev(act),
+                           n_expert, d_model, qt)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), pair.cpu().numpy()
+
+
+# d_model 80 takes the 4-wide slot sum, 78 the scalar one
+@pytest.mark.parametrize("t,n_used,d_model", [(1, 8, 80), (3, 2, 78), (5, 4, 80), (16, 3, 78)])
+def test_moe_down_parity_small(t, n_used, d_model):
+    n_expert, n_ff = 9, 256
+    note(f"moe down small t={t} n_used={n_used} d_model={d_model}")
+    wd, ids, sc, act = _down_inputs(n_expert, n_ff, d_model, t, n_used, seed=t)
+    y, pair = _gpu_down(wd, ids, sc, act, n_expert, d_model)
+    ry, Sy, rp, Sp = ref.moe_down_ref("nvfp4", wd, ids, sc, act, n_expert, n_ff, d_model)
+    ok, worst = ref.tolerance_check(pair, rp, Sp, TAU_F32)
+    assert ok, f"pair terms: {worst}"
+    ok, worst = ref.tolerance_check(y, ry, Sy, TAU_F32)
+    assert ok, f"y: {worst}"
+    # the slot sum is the plain f32 sum of the returned pair terms in slot order
+    want = pair.reshape(t, n_used, d_model)[:, 0].copy()
+    for s in range(1, n_used):
+        want += pair.reshape(t, n_used, d_model)[:, s]
+    assert np.array_equal(y, want)
+
+
+@pytest.mark.parametrize("qt", ["q4_k", "q8_0"])
+def test_moe_down_other_formats_and_repeats(qt):
+    """Other weight formats; one expert shared by many tokens (several gather
+    chunks); two identical calls are bit-identical."""
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    n_expert, n_ff, d_model, t, n_used = 3, 512, 96, 40, 2
+    note(f"moe down {qt} repeats")
+    wd = weights(qt, n_expert * d_model, n_ff, 31)
+    _, _, sc, act = _down_inputs(n_expert, n_ff, d_model, t, n_used, seed=2)
+    ids = np.stack([np.full(t, 1), np.arange(t) % 2 * 2], axis=1).astype(np.int32)
+    y, pair = _gpu_down(wd, ids, sc, act, n_expert, d_model, qt)
+    ry, Sy, _, _ = ref.moe_down_ref(qt, wd, ids, sc, act, n_expert, n_ff, d_model)
+    ok, worst = ref.tolerance_check(y, ry, Sy, TAU_F32)
+    assert ok, worst
+    y2, pair2 = _gpu_down(wd, ids, sc, act, n_expert, d_model, qt)
+    assert np.array_equal(y, y2) and np.array_equal(pair, pair2)
+
+
+def test_moe_down_invalid_expert_id_gives_nan():
+    n_expert, n_ff, d_model, t, n_used = 4, 128, 40, 3, 2
+    note("moe down invalid id")
+    wd, _, sc, act = _down_inputs(n_expert, n_ff, d_model, t, n_used)
+    ids = np.array([[1, 3], [2, 9], [0, 1]], dtype=np.int32)
+    y, pair = _gpu_down(wd, ids, sc, act, n_expert, d_model)
+    assert np.all(np.isnan(y[1])) and np.all(np.isnan(pair[3]))
+    assert np.all(np.isfinite(y[[0, 2]])) and np.all(np.isfinite(pair[[0, 1, 2, 4, 5]]))
+    ok_ids = np.array([[1, 3], [2, 0], [0, 1]])
+    ry, Sy, _, _ = ref.moe_down_ref("nvfp4", wd, ok_ids, sc, act, n_expert, n_ff, d_model)
+    assert ref.tolerance_check(y[[0, 2]], ry[[0, 2]], Sy[[0, 2]], TAU_F32)[0]
+
+
 def test_loadonly_twin_runs_and_is_deterministic():
     import torch
     import gemv_prefill_decode_amd as qmm
