@@ -16,7 +16,9 @@ The same JSON line also carries the other half of the metric:
            comes from HBM; GB/s of algorithmic bytes (packed W + x + dst) and
            TFLOP/s, each against its roof; the load-only twin at n = 1.
   moe      the NVFP4 gate/up rows at t = 1 and t = 16 (64 experts, 8 used,
-           in_f 4096, n_ff 2048), rotated over 4 weight copies x 8 id draws.
+           in_f 4096, n_ff 2048), rotated over 4 weight copies x 8 id draws,
+           and the down projection after it (4096 rows over 2048 inputs per
+           expert, per-pair activations, slots summed per token).
   roofline the dominant prefill kernel instance: algorithmic flops per launch
            over its average launch time from the events of the timed region.
   cpu_baseline  the CPU oracle over the whole prefill step on the host cores.
@@ -316,6 +318,64 @@ def run_moe(args):
     return res
 
 
+# ---------------------------------------------------------------- MoE down
+
+def run_moe_down(args):
+    """The down projection after the gate/up: 64 experts of d_model = 4096
+    rows over n_ff = 2048 inputs, 8 per token, t in {1, 16}; per-pair
+    activation rows; rotated over weight copies x 8 id draws.  Algorithmic
+    bytes: the unique experts' rows + the activations + y (the per-pair terms
+    the first kernel writes and the slot sum reads back are reported apart)."""
+    import numpy as np
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    from synth import gen
+    n_expert, n_ff, d_model, n_used = 64, 2048, 4096, 8
+    rb = qmm.row_bytes("nvfp4", n_ff)
+    per_e = d_model * rb
+    host = np.empty(n_expert * per_e, dtype=np.uint8)
+    for e in range(n_expert):
+        host[e * per_e:(e + 1) * per_e] = gen.nvfp4_rows(d_model, n_ff, gen.SEED_MOE_DOWN_W + e)
+    base = to_dev(host)
+    del host
+    copies = 2 if args.quick else 4
+    sets = []
+    for c in range(copies):
+        w = base.clone()
+        for e in range(n_expert):
+            w[e * per_e + 7] ^= (c * 16 + 3) & 0xFF
+        sets.append(w)
+    del base
+    res = {}
+    L = 32
+    for t in (1, 16):
+        n_pairs = t * n_used
+        draws_h = [gen.expert_ids(t, n_used, n_expert, gen.SEED_EXPERTS + d) for d in range(8)]
+        draws = [to_dev(d) for d in draws_h]
+        uniq = [len(np.unique(d)) for d in draws_h]
+        sc = to_dev(gen.pair_scales(3 * n_pairs)[2 * n_pairs:])
+        act = to_dev(gen.xorshift_f32(n_pairs * n_ff, gen.SEED_MOE_ACT).reshape(n_pairs, n_ff))
+        y = torch.empty((t, d_model), dtype=torch.float32, device="cuda")
+        po = torch.empty((n_pairs, d_model), dtype=torch.float32, device="cuda")
+        g = capture([(lambda w=sets[i % copies], d=draws[i % 8]:
+                      qmm.moe_down(w, d, sc, act, n_expert, d_model, y=y, pair_out=po))
+                     for i in range(L)])
+        tt = time_graph(g, L, 5)
+        del g
+        byts = statistics.mean(uniq[i % 8] * per_e + 4 * n_pairs * n_ff + 4 * t * d_model
+                               for i in range(L))
+        res[f"t{t}"] = {"us": round(tt * 1e6, 2),
+                        "GB/s": round(byts / tt / 1e9, 1),
+                        "frac_hbm_peak": round(byts / tt / 1e9 / PEAK_HBM_GBS, 4),
+                        "unique_experts_mean": round(statistics.mean(uniq), 2),
+                        "algorithmic_bytes_mean": round(byts),
+                        "pair_terms_bytes": 2 * 4 * n_pairs * d_model}
+        log(f"moe down t={t}: {res[f't{t}']['us']} us {res[f't{t}']['GB/s']} GB/s")
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---------------------------------------------------------------- HBM traffic
 
 COPY_PROBE_BYTES = 1 << 30
@@ -462,6 +522,9 @@ def main():
         extras["decode"] = run_decode(args)
         log("MoE gate/up NVFP4")
         extras["moe_gateup"] = run_moe(args)
+        torch.cuda.empty_cache()
+        log("MoE down NVFP4")
+        extras["moe_down"] = run_moe_down(args)
     cpu = None
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")

@@ -670,6 +670,20 @@ struct NoPre {
 // pre() is called by every wave once the ring's first loads are issued (the
 // work group's activation staging, with its barrier, goes there so that it
 // overlaps the first weight loads).
+// Position (row-group step q, unit uu) of a stream item, advanced by one
+// item without the integer division it / upl (a division is about thirty
+// scalar and vector instructions; the loops below advance two positions per
+// item).
+struct ItemPos {
+    int q, uu;
+    __device__ __forceinline__ void next(int upl) {
+        if (++uu == upl) {
+            uu = 0;
+            ++q;
+        }
+    }
+};
+
 template <int QT, int NT, int R, int D, typename XS, typename Store, typename Pre = NoPre>
 __device__ __forceinline__ void gemv_stream(const StreamGeom& g, int first_rg, int rg_stride,
                                             int n_rg, const XS& xs, Store store, Pre pre = {}) {
@@ -745,19 +759,20 @@ __device__ __forceinline__ void gemv_stream(const StreamGeom& g, int first_rg, i
                           ln.e + uu * e_step, true);
     }
     pre();
+    ItemPos cur{0, 0}, nxt{D / upl, D - (D / upl) * upl};
     for (int base = 0; base < n_items; base += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int it = base + d;
             const bool live = it < n_items;  // wave-uniform
-            const int q = it / upl, uu = it - q * upl;
+            const int q = cur.q, uu = cur.uu;
             if (live && gl + lpr * uu < U)
                 compute_item<QT, NT, R>(ring[d], ln, ln.e + uu * e_step, g.k, xs, acc);
-            const int nx = it + D;
-            const int q2 = nx / upl, uu2 = nx - q2 * upl;
-            issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q2 * rg_stride, uu2,
-                              ln.e + uu2 * e_step, nx < n_items);
+            issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + nxt.q * rg_stride, nxt.uu,
+                              ln.e + nxt.uu * e_step, it + D < n_items);
             if (live && uu == upl - 1) finish(q);
+            cur.next(upl);
+            nxt.next(upl);
         }
     }
 }
@@ -1017,20 +1032,21 @@ __global__ __launch_bounds__(256) void loadonly_kernel(uint32_t* __restrict__ si
         issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q * rg_stride, uu,
                           ln.e + uu * e_step, true);
     }
+    ItemPos cur{0, 0}, nxt{D / upl, D - (D / upl) * upl};
     for (int base = 0; base < n_items; base += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int it = base + d;
             const bool live = it < n_items;
-            const int q = it / upl, uu = it - q * upl;
+            const int q = cur.q, uu = cur.uu;
             if (live && gl + lpr * uu < U)
 #pragma unroll
                 for (int rr = 0; rr < R; ++rr) acc[rr] ^= raw_xor(ring[d][rr]);
-            const int nx = it + D;
-            const int q2 = nx / upl, uu2 = nx - q2 * upl;
-            issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q2 * rg_stride, uu2,
-                              ln.e + uu2 * e_step, nx < n_items);
+            issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + nxt.q * rg_stride, nxt.uu,
+                              ln.e + nxt.uu * e_step, it + D < n_items);
             if (live && uu == upl - 1) finish(q);
+            cur.next(upl);
+            nxt.next(upl);
         }
     }
 }
@@ -1180,7 +1196,9 @@ static void launch_moe_qt(float* g, float* u, const uint8_t* wg, const uint8_t* 
         // active; with many pairs the sets are not all distinct, so each set
         // gets at least MOE_MIN_WG work groups
         const int64_t active = planes * (n_pairs < n_expert ? n_pairs : n_expert);
-        unsigned gx = stream_grid(n_rg, active, tune);
+        GemvTuning mt = tune;
+        mt.wg_per_cu = tune.moe_wg_per_cu;
+        unsigned gx = stream_grid(n_rg, active, mt);
         const unsigned need = (unsigned)((n_rg + 3) / 4);
         if (gx < MOE_MIN_WG) gx = need < MOE_MIN_WG ? need : MOE_MIN_WG;
         const dim3 grid(gx, (unsigned)n_pairs, (unsigned)planes);

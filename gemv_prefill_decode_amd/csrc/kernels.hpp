@@ -11,6 +11,7 @@ namespace qmm {
 struct GemvTuning {
     int num_cu;     // compute units of the device
     int wg_per_cu;  // work groups per CU the grid is sized for
+    int moe_wg_per_cu;  // the same for the MoE kernels
     int rows;       // rows per lane group (1 or 2)
     int depth;      // items of weight loads kept in flight per wave (2, 4 or 8)
     int lds_per_wg; // bytes of LDS one work group may allocate

@@ -66,10 +66,15 @@ int env_int(const char* name, int dflt, int lo, int hi) {
     return (int)val;
 }
 
+// Defaults measured on MI355X (graph-replayed, weights rotated through HBM):
+// two rows per lane group and two items in flight per wave give the GEMV the
+// occupancy to hide its loads; the MoE kernels, whose work groups of one
+// expert share its rows, do best with half the work groups per CU.
 struct TuneState {
     int wg_per_cu = 4;
+    int moe_wg_per_cu = 2;
     int rows = 2;
-    int depth = 4;
+    int depth = 2;
     bool bad = false;
 };
 TuneState g_tune;
@@ -84,13 +89,15 @@ DevProps g_dev[64];
 
 void parse_tune() {
     const int w = env_int("QMM_GEMV_WG_PER_CU", g_tune.wg_per_cu, 1, 64);
+    const int mw = env_int("QMM_MOE_WG_PER_CU", g_tune.moe_wg_per_cu, 1, 64);
     const int r = env_int("QMM_GEMV_ROWS", g_tune.rows, 1, 2);
     const int d = env_int("QMM_GEMV_DEPTH", g_tune.depth, 2, 8);
-    if (w < 0 || r < 0 || d < 0 || (d & (d - 1)) != 0) {
+    if (w < 0 || mw < 0 || r < 0 || d < 0 || (d & (d - 1)) != 0) {
         g_tune.bad = true;
         return;
     }
     g_tune.wg_per_cu = w;
+    g_tune.moe_wg_per_cu = mw;
     g_tune.rows = r;
     g_tune.depth = d;
 }
@@ -149,6 +156,7 @@ bool gemv_tuning(qmm::GemvTuning* t) {
     t->lds_per_wg = p.lds_wg;
     t->lds_per_cu = p.lds_cu;
     t->wg_per_cu = g_tune.wg_per_cu;
+    t->moe_wg_per_cu = g_tune.moe_wg_per_cu;
     t->rows = g_tune.rows;
     t->depth = g_tune.depth;
     return true;

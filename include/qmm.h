@@ -17,8 +17,9 @@
  *  - Work is enqueued asynchronously on `stream` (0 = the null stream).  No
  *    call allocates device memory, synchronizes, or keeps state beyond lazily
  *    cached device properties (compute units, LDS sizes) and the parsed
- *    tuning variables (QMM_GEMV_MAX_N below; QMM_GEMV_WG_PER_CU 1..64,
- *    QMM_GEMV_ROWS 1..2, QMM_GEMV_DEPTH 2/4/8 for the streaming kernels'
+ *    tuning variables (QMM_GEMV_MAX_N below; QMM_GEMV_WG_PER_CU and
+ *    QMM_MOE_WG_PER_CU 1..64, QMM_GEMV_ROWS 1..2, QMM_GEMV_DEPTH 2/4/8 for
+ *    the streaming kernels'
  *    launch shape; a malformed value makes the calls that use it return
  *    QMM_ERR_RANGE; QMM_MFMA_PLAN is read again at every call that plans a
  *    prefill), so the calls can be recorded into a hipGraph.

@@ -127,6 +127,24 @@ def test_gemv_max_n_env_is_strict(value, expect):
         assert int(out.stdout.strip()) == 8
 
 
+@pytest.mark.parametrize("var", ["QMM_GEMV_WG_PER_CU", "QMM_MOE_WG_PER_CU", "QMM_GEMV_ROWS",
+                                 "QMM_GEMV_DEPTH"])
+@pytest.mark.parametrize("value", ["0", "abc", "65", "3x"])
+def test_streaming_tuning_env_is_strict(var, value):
+    """A malformed or out-of-range launch-shape knob makes the streaming
+    entry points fail with QMM_ERR_RANGE before any launch."""
+    _lib()
+    code = ("import sys, ctypes; sys.path.insert(0, %r); from gemv_prefill_decode_amd import load; "
+            "A = ctypes.c_void_p(1 << 20); lib = load(); "
+            "print(lib.qmm_moe_gateup(A, A, A, A, A, A, A, 1, 8, 64, 4096, 2048, 5, ctypes.c_void_p(0)), "
+            "lib.qmm_moe_down(A, A, A, A, A, A, 1, 8, 64, 2048, 4096, 5, ctypes.c_void_p(0)), "
+            "lib.qmm_stream_loadonly(A, A, 64, 256, 3, ctypes.c_void_p(0)))" % ROOT)
+    env = dict(os.environ, **{var: value})
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split() == ["8", "8", "8"]
+
+
 def test_default_gemv_max_n():
     lib = _lib()
     if "QMM_GEMV_MAX_N" in os.environ:
