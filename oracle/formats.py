@@ -25,6 +25,15 @@ them by family (llama.cpp/ggml block quantization).  The readings used here:
   NVFP4     s[4] E4M3FN@0, qs[32]@4 per 64 elems.  Half h covers elems
             32h..32h+31: elem 32h+j (j<16) = E2M1(qs[16h+j]&15)*E4M3(s[2h]);
             elem 32h+16+j = E2M1(qs[16h+j]>>4)*E4M3(s[2h+1]).
+  NVFP4_V2  the same values with quants and scales in separate streams (memra
+            `moe_rows_ceiling_bench.rs`: 18 bytes per 32-element group, 16 of
+            quants and 2 of scales, the scales contiguous; the pages print no
+            byte order, so this is a reading): a row of k elems is the k/2
+            quant bytes, then the k/16 scale bytes.  Group g (elems 32g..32g+31):
+            elem 32g+j (j<16) = E2M1(q[16g+j]&15)*E4M3(s[2g]);
+            elem 32g+16+j = E2M1(q[16g+j]>>4)*E4M3(s[2g+1]).  Rows are whole
+            NVFP4 groups (k a multiple of 64), so a row is the V1 row with each
+            36-byte group split into its 32 quant bytes and its scale word.
 """
 
 from __future__ import annotations
@@ -39,6 +48,7 @@ QTYPES = {
     "q4_k": (3, 256, 144),
     "q6_k": (4, 256, 210),
     "nvfp4": (5, 64, 36),
+    "nvfp4_v2": (6, 64, 36),   # not a contiguous block: see the module docstring
 }
 
 
@@ -211,6 +221,26 @@ def _decode_nvfp4(data, m, k):
     return out.reshape(m, k)
 
 
+def _decode_nvfp4_v2(data, m, k):
+    rows = np.asarray(data).reshape(-1).view(np.uint8).reshape(m, row_bytes("nvfp4_v2", k))
+    q = rows[:, :k // 2].astype(np.int64).reshape(m, k // 32, 16)     # group g, byte j
+    s = e4m3_bits_to_f64(rows[:, k // 2:].reshape(m, k // 32, 2))     # group g, run i
+    out = np.empty((m, k // 32, 2, 16), dtype=np.float64)
+    out[:, :, 0, :] = e2m1_bits_to_f64(q & 0xF) * s[:, :, 0, None]
+    out[:, :, 1, :] = e2m1_bits_to_f64(q >> 4) * s[:, :, 1, None]
+    return out.reshape(m, k)
+
+
+def repack_nvfp4_v2(data, m: int, k: int) -> np.ndarray:
+    """NVFP4 rows (V1) -> the same values in the V2 layout (uint8 [m*row_bytes]):
+    per 36-byte group G of a row, bytes 4..35 go to quant bytes 32G..32G+31 and
+    the scale word (bytes 0..3) to the row's scale bytes 4G..4G+3."""
+    blk = _blocks(data, m, k, "nvfp4")                    # [m, k/64, 36]
+    quants = blk[..., 4:36].reshape(m, -1)
+    scales = blk[..., 0:4].reshape(m, -1)
+    return np.concatenate([quants, scales], axis=1).reshape(-1).copy()
+
+
 _DECODERS = {
     "f32": _decode_f32,
     "q4_0": _decode_q4_0,
@@ -218,6 +248,7 @@ _DECODERS = {
     "q4_k": _decode_q4_k,
     "q6_k": _decode_q6_k,
     "nvfp4": _decode_nvfp4,
+    "nvfp4_v2": _decode_nvfp4_v2,
 }
 
 

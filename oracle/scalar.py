@@ -12,7 +12,7 @@ from __future__ import annotations
 import math
 
 _SIZES = {"f32": (1, 4), "q4_0": (32, 18), "q8_0": (32, 34), "q4_k": (256, 144),
-          "q6_k": (256, 210), "nvfp4": (64, 36)}
+          "q6_k": (256, 210), "nvfp4": (64, 36), "nvfp4_v2": (64, 36)}
 
 
 def half(lo: int, hi: int) -> float:
@@ -86,6 +86,13 @@ def element(name: str, row: bytes, e: int) -> float:
         q = low | (high << 4)
         d = half(blk[208], blk[209])
         return d * int8(blk[192 + i // 16]) * (q - 32)
+    if name == "nvfp4_v2":
+        # row = k/2 quant bytes, then k/16 scale bytes (two per 32-element group)
+        k = len(row) // 18 * 32
+        g, r = divmod(e, 32)
+        byte = row[16 * g + (r % 16)]
+        code = (byte & 15) if r < 16 else (byte >> 4)
+        return fp4_e2m1(code) * fp8_e4m3(row[k // 2 + 2 * g + (1 if r >= 16 else 0)])
     if name == "nvfp4":
         h, r = divmod(i, 32)
         byte = blk[4 + 16 * h + (r % 16)]

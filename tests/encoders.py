@@ -96,6 +96,21 @@ def nvfp4(scale_bytes, codes) -> bytes:
     return bytes(scale_bytes + qs)
 
 
+def nvfp4_v2(scale_bytes, codes) -> bytes:
+    """One V2 row of k = len(codes) elements: the quant bytes (group g's
+    element 32g+j in the low nibble of byte 16g+j, element 32g+16+j in its
+    high nibble), then the scale bytes (2g covers 32g..32g+15, 2g+1 the next 16)."""
+    codes = [int(v) for v in codes]
+    scale_bytes = [int(v) for v in scale_bytes]
+    k = len(codes)
+    assert k % 64 == 0 and len(scale_bytes) == k // 16
+    qs = [0] * (k // 2)
+    for e in range(k):
+        g, r = divmod(e, 32)
+        qs[16 * g + r % 16] |= (codes[e] & 0xF) << (4 if r >= 16 else 0)
+    return bytes(qs + scale_bytes)
+
+
 E2M1_MAG = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 
 

@@ -160,7 +160,53 @@ def test_nvfp4_scale_coverage_one_hot():
         assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("qt", ["f32", "q4_0", "q8_0", "q4_k", "q6_k", "nvfp4"])
+@pytest.mark.parametrize("seed", range(3))
+def test_nvfp4_v2_roundtrip(seed):
+    """V2 rows built by the test encoder from chosen (scale, code) values
+    decode to exactly those values."""
+    rng = np.random.default_rng(400 + seed)
+    k = 192
+    sbytes = rng.integers(0, 256, k // 16)
+    sbytes[(sbytes & 0x7F) == 0x7F] = 0x38
+    codes = rng.integers(0, 16, k)
+    row = np.frombuffer(enc.nvfp4_v2(sbytes, codes), np.uint8)
+    assert row.size == formats.row_bytes("nvfp4_v2", k) == k // 32 * 18
+    got = formats.decode("nvfp4_v2", row, 1, k)[0]
+    sv = formats.e4m3_bits_to_f64(sbytes)
+    assert np.array_equal(got, [enc.e2m1_value(codes[e]) * sv[e // 16] for e in range(k)])
+
+
+def test_nvfp4_v2_scale_coverage_one_hot():
+    """Scale byte g of a V2 row scales exactly elements 16g..16g+15."""
+    k = 128
+    for g in range(k // 16):
+        sb = [0] * (k // 16)
+        sb[g] = 0x40  # 2.0
+        got = formats.decode("nvfp4_v2", np.frombuffer(enc.nvfp4_v2(sb, [2] * k), np.uint8), 1, k)[0]
+        want = np.zeros(k)
+        want[16 * g:16 * g + 16] = 2.0
+        assert np.array_equal(got, want)
+
+
+def test_nvfp4_v2_repack_keeps_values_and_matches_encoders():
+    """The oracle's V1 -> V2 repack: decoded values are unchanged, and a V1
+    row built by the V1 encoder repacks to the V2 encoder's bytes for the
+    same (scale, code) values."""
+    from synth import gen
+    m, k = 5, 256
+    v1 = gen.nvfp4_rows(m, k, 0x8181)
+    v2 = formats.repack_nvfp4_v2(v1, m, k)
+    assert v2.size == v1.size
+    assert np.array_equal(formats.decode("nvfp4_v2", v2, m, k), formats.decode("nvfp4", v1, m, k))
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 16, k)
+    sbytes = (rng.integers(0, 8, k // 16) | 0x38)
+    v1_row = b"".join(enc.nvfp4(sbytes[4 * G:4 * G + 4], codes[64 * G:64 * G + 64]) for G in range(k // 64))
+    got = formats.repack_nvfp4_v2(np.frombuffer(v1_row, np.uint8), 1, k)
+    assert bytes(got) == enc.nvfp4_v2(sbytes, codes)
+
+
+@pytest.mark.parametrize("qt", ["f32", "q4_0", "q8_0", "q4_k", "q6_k", "nvfp4", "nvfp4_v2"])
 def test_scalar_equals_vectorized_random(qt):
     from synth import gen
     qk = formats.block_elems(qt)
@@ -169,6 +215,8 @@ def test_scalar_equals_vectorized_random(qt):
         data = gen.unit_f32(m * k, 7).view(np.uint8)
     elif qt == "nvfp4":
         data = gen.nvfp4_rows(m, k, 11)
+    elif qt == "nvfp4_v2":
+        data = formats.repack_nvfp4_v2(gen.nvfp4_rows(m, k, 11), m, k)
     else:
         data = gen.quant_bytes(m * formats.row_bytes(qt, k), 13)
     vec = formats.decode(qt, data, m, k)
