@@ -22,11 +22,11 @@ import threading
 __all__ = [
     "QTYPES", "PATHS", "QmmError", "lib_path", "load", "gemm", "workspace_bytes", "gemm_plan",
     "plan_kernel_name", "moe_gateup", "moe_down",
-    "stream_loadonly",
+    "stream_loadonly", "repack_nvfp4_v2",
     "row_bytes", "block_elems", "gemv_max_n", "status_str", "abi_version",
 ]
 
-QTYPES = {"f32": 0, "q4_0": 1, "q8_0": 2, "q4_k": 3, "q6_k": 4, "nvfp4": 5}
+QTYPES = {"f32": 0, "q4_0": 1, "q8_0": 2, "q4_k": 3, "q6_k": 4, "nvfp4": 5, "nvfp4_v2": 6}
 PATHS = {"auto": 0, "gemv": 1, "mfma": 2}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +71,8 @@ def load() -> ctypes.CDLL:
         lib.qmm_moe_gateup.restype = i32
         lib.qmm_moe_down.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
         lib.qmm_moe_down.restype = i32
+        lib.qmm_nvfp4_repack_v2.argtypes = [vp, vp, i64, i64, vp]
+        lib.qmm_nvfp4_repack_v2.restype = i32
         lib.qmm_stream_loadonly.argtypes = [vp, vp, i64, i64, i32, vp]
         lib.qmm_stream_loadonly.restype = i32
         lib.qmm_row_bytes.argtypes = [i32, i64]
@@ -284,6 +286,22 @@ def moe_down(w_down, expert_ids, pair_scale, act, n_expert: int, d_model: int, q
     if st != 0:
         raise QmmError(st, "qmm_moe_down")
     return y, pair_out
+
+
+def repack_nvfp4_v2(w, rows: int, k: int, out=None, stream=None):
+    """NVFP4 rows (uint8, rows*k/64*36 bytes) -> the same values in the
+    NVFP4_V2 layout (a new uint8 tensor, or ``out``)."""
+    import torch
+    lib = load()
+    nbytes = rows * (k // 64) * 36
+    if w.numel() * w.element_size() < nbytes:
+        raise ValueError("w holds fewer than rows*k/64*36 bytes")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    st = lib.qmm_nvfp4_repack_v2(_dev(out, "out"), _dev(w, "w"), rows, k, _stream(stream))
+    if st != 0:
+        raise QmmError(st, "qmm_nvfp4_repack_v2")
+    return out
 
 
 def stream_loadonly(w, m: int, k: int, qtype, sink=None, stream=None):

@@ -12,7 +12,7 @@
 
 namespace qmm {
 
-enum : int { QT_F32 = 0, QT_Q4_0 = 1, QT_Q8_0 = 2, QT_Q4_K = 3, QT_Q6_K = 4, QT_NVFP4 = 5 };
+enum : int { QT_F32 = 0, QT_Q4_0 = 1, QT_Q8_0 = 2, QT_Q4_K = 3, QT_Q6_K = 4, QT_NVFP4 = 5, QT_NVFP4_V2 = 6 };
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

@@ -381,6 +381,55 @@ template <> struct GUnit<QT_NVFP4> {
     }
 };
 
+// NVFP4 V2: the same values as NVFP4 with a row's quant bytes first and its
+// scale bytes after them (k/2 + 2g holds the two scales of 32-element group
+// g).  A unit is one group: 16 quant bytes at 16g and the scale dword holding
+// its two scale bytes.  The weights, their order and the arithmetic are those
+// of GUnit<QT_NVFP4>, so both layouts give bit-identical results.
+template <> struct GUnit<QT_NVFP4_V2> {
+    static constexpr int UE = 32, S = 4, MIN_LPR = 1;
+    static constexpr bool SCALED = true;
+    static constexpr int RUNS = 0;
+    struct Lane : LaneBase {};
+    __device__ static Lane lane(int gl) {
+        Lane l;
+        l.boff = 16u * (uint32_t)gl;
+        l.e = 32 * gl;
+        return l;
+    }
+    __host__ __device__ static uint32_t ustep(int lpr) { return 16u * (uint32_t)lpr; }
+    static constexpr int rel0(int s) { return 4 * s; }
+    static constexpr int rel1(int s) { return 16 + 4 * s; }
+    static constexpr int prel0(int s) { return rel0(s); }
+    static constexpr int prel1(int s) { return rel1(s); }
+    uint32_t sd, hsh;
+    u32x4 qs;
+    float s_lo, s_hi;
+    // off: the group's quant bytes (row start + 16g); its scale bytes are at
+    // row start + k/2 + 2g = off + k/2 - 14g (rows start 4-byte aligned).
+    __device__ __forceinline__ void load(rsrc_t wr, uint32_t off, int e, int k, const Lane&) {
+        const uint32_t soff = off + (uint32_t)(k >> 1) - 14u * (uint32_t)(e >> 5);
+        hsh = 8u * (soff & 3u);
+        sd = ld32(wr, soff & ~3u);
+        qs = ld128(wr, off);
+    }
+    __device__ __forceinline__ void prep(const Lane&) {
+        s_lo = e4m3_to_f32((sd >> hsh) & 0xFFu);
+        s_hi = e4m3_to_f32((sd >> (hsh + 8u)) & 0xFFu);
+    }
+    __device__ __forceinline__ void sub(int s, float (&w)[8], float& f0, float& f1) const {
+        const uint32_t q = s == 0 ? qs.x : (s == 1 ? qs.y : (s == 2 ? qs.z : qs.w));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const f32x2 v = e2m1x2_to_f32(q, b);
+            w[b] = v.x;
+            w[4 + b] = v.y;
+        }
+        f0 = s_lo;
+        f1 = s_hi;
+    }
+};
+
 // ------------------------------------------------------------------ activations
 // NT activation rows, either staged in LDS (4 floats of padding after every
 // 64 so that the lanes of a wave, which read 16 bytes at unit-strided k
@@ -971,6 +1020,10 @@ template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_NVFP4>& u
     return u.sd ^ u.qs.x ^ u.qs.y ^ u.qs.z ^ u.qs.w;
 }
 
+template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_NVFP4_V2>& u) {
+    return u.sd ^ u.qs.x ^ u.qs.y ^ u.qs.z ^ u.qs.w;
+}
+
 template <int QT, int R, int D>
 __global__ __launch_bounds__(256) void loadonly_kernel(uint32_t* __restrict__ sink,
                                                        const uint8_t* __restrict__ w, int m, int k,
@@ -1061,6 +1114,7 @@ int gemv_unit_elems(int qt) {
         case QT_Q4_K: return GUnit<QT_Q4_K>::UE;
         case QT_Q6_K: return GUnit<QT_Q6_K>::UE;
         case QT_NVFP4: return GUnit<QT_NVFP4>::UE;
+        case QT_NVFP4_V2: return GUnit<QT_NVFP4_V2>::UE;
     }
     return 0;
 }
@@ -1070,6 +1124,7 @@ static int min_lpr(int qt) {
         case QT_Q4_K: return GUnit<QT_Q4_K>::MIN_LPR;
         case QT_Q6_K: return GUnit<QT_Q6_K>::MIN_LPR;
         case QT_NVFP4: return GUnit<QT_NVFP4>::MIN_LPR;
+        case QT_NVFP4_V2: return GUnit<QT_NVFP4_V2>::MIN_LPR;
     }
     return 1;
 }
@@ -1174,6 +1229,7 @@ static void launch_gemv_qt(float* dst, const uint8_t* w, const float* x, int64_t
         case QT_Q4_K: { constexpr int Q = QT_Q4_K; CALL; break; }   \
         case QT_Q6_K: { constexpr int Q = QT_Q6_K; CALL; break; }   \
         case QT_NVFP4: { constexpr int Q = QT_NVFP4; CALL; break; } \
+        case QT_NVFP4_V2: { constexpr int Q = QT_NVFP4_V2; CALL; break; } \
     }
 
 void launch_gemv(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
@@ -1274,6 +1330,36 @@ void launch_loadonly(uint32_t* sink, const void* w, int64_t m, int64_t k, int qt
                      const GemvTuning& tune, hipStream_t st) {
     const uint8_t* wb = (const uint8_t*)w;
     QMM_QT_SWITCH(qt, (launch_lo_qt<Q>(sink, wb, m, k, rb, tune, st)))
+}
+
+// ------------------------------------------------------------------ V2 repack
+// NVFP4 rows -> NVFP4 V2 rows.  Item (row, G): the 36 bytes of group G are
+// its scale word and 32 quant bytes; the quant bytes go to 32G and the scale
+// word to k/2 + 4G of the same row (9 dword loads, 9 dword stores).
+__global__ __launch_bounds__(256) void nvfp4_repack_v2_kernel(uint32_t* __restrict__ dst,
+                                                              const uint32_t* __restrict__ src,
+                                                              int64_t rows, int64_t k) {
+    const int64_t groups = k / 64, rw = groups * 9;  // dwords per row
+    const int64_t items = rows * groups;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < items; i += (int64_t)gridDim.x * 256) {
+        const int64_t r = i / groups, G = i - r * groups;
+        const uint32_t* s = src + r * rw + 9 * G;
+        uint32_t* d = dst + r * rw;
+        uint32_t v[9];
+#pragma unroll
+        for (int j = 0; j < 9; ++j) v[j] = s[j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d[8 * G + j] = v[1 + j];
+        d[8 * groups + G] = v[0];
+    }
+}
+
+void launch_nvfp4_repack_v2(void* dst, const void* src, int64_t rows, int64_t k, hipStream_t st) {
+    const int64_t items = rows * (k / 64);
+    int64_t blocks = (items + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    nvfp4_repack_v2_kernel<<<dim3((unsigned)blocks), 256, 0, st>>>((uint32_t*)dst, (const uint32_t*)src,
+                                                                   rows, k);
 }
 
 }  // namespace qmm

@@ -85,6 +85,9 @@ void launch_moe_down(float* y, float* pair_out, const void* w_down, const int* i
                      int64_t n_expert, int64_t n_ff, int64_t d_model, int qt, int64_t rb,
                      const GemvTuning& tune, hipStream_t st);
 
+// NVFP4 rows (rows x k/64 groups of 36 bytes) -> the NVFP4 V2 layout.
+void launch_nvfp4_repack_v2(void* dst, const void* src, int64_t rows, int64_t k, hipStream_t st);
+
 void launch_loadonly(uint32_t* sink, const void* w, int64_t m, int64_t k, int qt, int64_t rb,
                      const GemvTuning& tune, hipStream_t st);
 

@@ -22,9 +22,10 @@ struct Fmt {
 
 // Packed sizes: cera wgpu_gemm_bench.rs VARIANTS (f32 e*4, q4_0 e/32*18,
 // q8_0 e/32*34, q4_k e/256*144, q6_k e/256*210); memra synth_rows (NVFP4 36
-// bytes per 64 weights).
-constexpr Fmt kFmt[] = {{1, 4}, {32, 18}, {32, 34}, {256, 144}, {256, 210}, {64, 36}};
-constexpr int kNumQt = 6;
+// bytes per 64 weights) and its V2 rows (18 bytes per 32 weights, whole
+// 64-weight groups per row).
+constexpr Fmt kFmt[] = {{1, 4}, {32, 18}, {32, 34}, {256, 144}, {256, 210}, {64, 36}, {64, 36}};
+constexpr int kNumQt = 7;
 
 bool valid_qt(int qt) { return qt >= 0 && qt < kNumQt; }
 
@@ -206,6 +207,7 @@ int check_gemm(float* dst, const void* w, const float* x, int64_t m, int64_t k, 
         return QMM_OK;
     }
     if (*path == QMM_PATH_MFMA) {
+        if (qtype == QMM_NVFP4_V2) return QMM_ERR_QTYPE;  // streaming paths only
         if ((int64_t)qmm::MFMA_BM_MAX * *rb + 16 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
         if ((int64_t)qmm::MFMA_BN * k * 4 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
         const int64_t tiles = ((m + qmm::MFMA_BM - 1) / qmm::MFMA_BM) * ((n + qmm::MFMA_BN - 1) / qmm::MFMA_BN);
@@ -273,6 +275,7 @@ const char* qmm_status_str(int s) {
         case QMM_ERR_PATH: return "unknown kernel path";
         case QMM_ERR_RANGE: return "size outside the kernels' index range (or bad QMM_GEMV_MAX_N)";
         case QMM_ERR_WORKSPACE: return "workspace smaller than qmm_gemm_workspace_bytes()";
+        case QMM_ERR_ALIAS: return "an output overlaps an input";
     }
     return "unknown status";
 }
@@ -288,6 +291,7 @@ int64_t qmm_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int qtype, int
     }
     if (path == QMM_PATH_GEMV) return 0;
     if (path != QMM_PATH_MFMA) return -QMM_ERR_PATH;
+    if (qtype == QMM_NVFP4_V2) return -QMM_ERR_QTYPE;  // streaming paths only
     qmm::GemvTuning tune;
     if (!gemv_tuning(&tune)) return -QMM_ERR_RANGE;
     const MfmaForceState g_force = parse_force();
@@ -311,6 +315,7 @@ int qmm_gemm_plan(int64_t m, int64_t k, int64_t n, int qtype, int path, int with
         return QMM_OK;
     }
     if (path != QMM_PATH_MFMA) return QMM_ERR_PATH;
+    if (qtype == QMM_NVFP4_V2) return QMM_ERR_QTYPE;  // streaming paths only
     qmm::GemvTuning tune;
     if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
     const MfmaForceState g_force = parse_force();
@@ -391,6 +396,19 @@ int qmm_moe_down(float* y, float* pair_out, const void* w_down, const int32_t* e
     if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
     qmm::launch_moe_down(y, pair_out, w_down, expert_ids, pair_scale, act, t, n_used, n_expert, n_ff,
                          d_model, qtype, rb, tune, stream);
+    return launch_status();
+}
+
+int qmm_nvfp4_repack_v2(void* dst, const void* src, int64_t rows, int64_t k, hipStream_t stream) {
+    if (!dst || !src) return QMM_ERR_NULL;
+    if (rows < 1 || k < 1) return QMM_ERR_SHAPE;
+    if (k % 64 != 0) return QMM_ERR_K_ALIGN;
+    if (!aligned(dst, 4) || !aligned(src, 4)) return QMM_ERR_ALIGN;
+    int64_t bytes;
+    if (!mul_ok(rows, k / 64 * 36, &bytes)) return QMM_ERR_SHAPE;
+    const uintptr_t a = (uintptr_t)dst, b = (uintptr_t)src;
+    if (a < b + (uintptr_t)bytes && b < a + (uintptr_t)bytes) return QMM_ERR_ALIAS;
+    qmm::launch_nvfp4_repack_v2(dst, src, rows, k, stream);
     return launch_status();
 }
 

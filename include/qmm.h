@@ -44,14 +44,23 @@ extern "C" {
 
 /* Weight formats.  Block sizes (elements / bytes): F32 1/4, Q4_0 32/18,
  * Q8_0 32/34, Q4_K 256/144, Q6_K 256/210, NVFP4 64/36 (the packed-size
- * formulas of cera wgpu_gemm_bench.rs VARIANTS and memra synth_rows). */
+ * formulas of cera wgpu_gemm_bench.rs VARIANTS and memra synth_rows).
+ * NVFP4_V2 holds the values of NVFP4 rows in two streams per row (memra
+ * moe_rows_ceiling_bench.rs, the V2 rows: 18 bytes per 32 weights, 16 of
+ * quants and 2 of scales, the scales contiguous): the k/2 quant bytes (byte
+ * 16g+j: weight 32g+j in its low nibble, 32g+16+j in its high nibble), then
+ * the k/16 E4M3 scale bytes (byte 2g+i scales weights 32g+16i .. +15); k is
+ * a multiple of 64 and a row is k/64*36 bytes, as for NVFP4.  qmm_nvfp4_repack_v2
+ * converts.  NVFP4_V2 is accepted by the streaming paths (GEMV, MoE, load-only
+ * twin); the matrix-core path returns QMM_ERR_QTYPE for it. */
 typedef enum {
     QMM_F32 = 0,
     QMM_Q4_0 = 1,
     QMM_Q8_0 = 2,
     QMM_Q4_K = 3,
     QMM_Q6_K = 4,
-    QMM_NVFP4 = 5
+    QMM_NVFP4 = 5,
+    QMM_NVFP4_V2 = 6
 } qmm_qtype;
 
 typedef enum {
@@ -64,7 +73,8 @@ typedef enum {
     QMM_ERR_LAUNCH = 6,    /* the runtime reported a launch error              */
     QMM_ERR_PATH = 7,      /* unknown path selector                            */
     QMM_ERR_RANGE = 8,     /* a size exceeds what the kernels index (see below) */
-    QMM_ERR_WORKSPACE = 9  /* workspace smaller than qmm_gemm_workspace_bytes()  */
+    QMM_ERR_WORKSPACE = 9, /* workspace smaller than qmm_gemm_workspace_bytes()  */
+    QMM_ERR_ALIAS = 10     /* an output overlaps an input that must stay intact  */
 } qmm_status;
 
 /* Kernel path selector for qmm_gemm_path. */
@@ -81,7 +91,7 @@ typedef enum {
  *         For QMM_F32, float[m*k].
  *   x     DEVICE float[n*k] activations, row-major, 16-byte aligned.
  *   m,k,n >= 1; k % block_elems(qtype) == 0 and k % 4 == 0.
- *   qtype one of QMM_F32..QMM_NVFP4.
+ *   qtype one of QMM_F32..QMM_NVFP4_V2 (NVFP4_V2 on the GEMV path only).
  * Dispatch (the GEMV-vs-GEMM crossover of aprender-serve cublas_prefill,
  * cublas_gemm_threshold): n <= qmm_gemv_max_n() runs the f32 GEMV (results
  * within 1e-5 * sum|w*x| of the exact value), otherwise the MFMA kernel,
@@ -203,6 +213,19 @@ int qmm_moe_gateup(float* gate_out, float* up_out,
 int qmm_moe_down(float* y, float* pair_out, const void* w_down, const int32_t* expert_ids,
                  const float* pair_scale, const float* act, int64_t t, int64_t n_used,
                  int64_t n_expert, int64_t n_ff, int64_t d_model, int qtype, hipStream_t stream);
+
+/*
+ * qmm_nvfp4_repack_v2: NVFP4 rows -> the same values as NVFP4_V2 rows (memra
+ * moe_rows_ceiling_bench.rs repacks the expert rows once before its V2 arms).
+ * Per row and 36-byte group G: the 32 quant bytes (group bytes 4..35) go to
+ * row bytes 32G..32G+31, the scale word (group bytes 0..3) to row bytes
+ * k/2 + 4G .. +3.  A pure byte permutation: decoding gives identical values.
+ *   dst, src  DEVICE, rows * (k/64*36) bytes each, 4-byte aligned, not
+ *             overlapping (QMM_ERR_ALIAS).
+ *   rows      rows of k weights (for expert tensors: n_expert * rows per expert).
+ *   k         a multiple of 64 (QMM_ERR_K_ALIGN).
+ */
+int qmm_nvfp4_repack_v2(void* dst, const void* src, int64_t rows, int64_t k, hipStream_t stream);
 
 /*
  * qmm_stream_loadonly: the load-only twin of the GEMV (memra-engine

@@ -86,7 +86,7 @@ def test_validation_rejects_before_launch():
     assert g(A, A, A, 64, 128, 4, 3, 0, s0) == 3          # Q4_K needs k % 256
     assert g(A, A, A, 64, 48, 4, 1, 0, s0) == 3           # Q4_0 needs k % 32
     assert g(A, A, A, 64, 6, 4, 0, 0, s0) == 3            # f32 needs k % 4
-    assert g(A, A, A, 64, 256, 4, 6, 0, s0) == 4          # unknown qtype
+    assert g(A, A, A, 64, 256, 4, 7, 0, s0) == 4          # unknown qtype
     assert g(A, B, A, 64, 256, 4, 3, 0, s0) == 5          # misaligned w
     assert g(A, A, B, 64, 256, 4, 3, 0, s0) == 5          # misaligned x
     assert g(B, A, A, 64, 256, 4, 3, 0, s0) == 5          # misaligned dst
@@ -104,6 +104,16 @@ def test_validation_rejects_before_launch():
     assert d(A, A, A, A, A, A, 1, 8, 64, 2000, 4096, 5, s0) == 3     # n_ff % 64
     assert d(A, A, A, A, A, A, 1, 8, 64, 2048, 4096, 8, s0) == 4     # qtype
     assert d(A, A, A, A, A, A, 70000, 1, 64, 64, 4096, 5, s0) == 8   # more pairs than the grid
+    r = lib.qmm_nvfp4_repack_v2
+    assert r(z, A, 4, 128, s0) == 1                                  # null dst
+    assert r(A, A, 0, 128, s0) == 2                                  # rows < 1
+    assert r(A, ctypes.c_void_p((1 << 21)), 4, 96, s0) == 3          # k % 64
+    assert r(ctypes.c_void_p((1 << 20) + 2), ctypes.c_void_p(1 << 21), 4, 128, s0) == 5
+    assert r(A, ctypes.c_void_p((1 << 20) + 64), 4, 128, s0) == 10   # overlapping
+    # NVFP4 V2 is a streaming-path format: the matrix-core path rejects it
+    assert g(A, A, A, 64, 256, 64, 6, 2, s0) == 4
+    assert lib.qmm_gemm_workspace_bytes(64, 256, 64, 6, 2) == -4
+    assert lib.qmm_gemm_workspace_bytes(64, 256, 8, 6, 0) == 0        # auto -> GEMV
     lo = lib.qmm_stream_loadonly
     assert lo(z, A, 64, 256, 3, s0) == 1
     assert lo(A, A, 64, 255, 3, s0) == 3

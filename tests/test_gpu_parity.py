@@ -390,3 +390,72 @@ def test_forced_prefill_plans(plan, qt, monkeypatch):
     x = acts(n, k, 60)
     got = gpu_gemm(qt, w, x, m, "mfma")
     check_full(qt, w, x, m, k, n, got, TAU_F16, f"plan {plan} {qt}")
+
+
+# ------------------------------------------------------------------ NVFP4 V2
+
+def test_nvfp4_v2_repack_bit_exact():
+    """The device repack equals the oracle's byte permutation, on a ragged
+    row count and on an expert tensor (experts x rows flattened)."""
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    for rows, k in ((37, 192), (8 * 96, 1024)):
+        note(f"nvfp4 v2 repack rows={rows} k={k}")
+        v1 = gen.nvfp4_rows(rows, k, gen.SEED_MOE_W + rows)
+        got = qmm.repack_nvfp4_v2(to_dev(v1), rows, k)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), formats.repack_nvfp4_v2(v1, rows, k))
+
+
+@pytest.mark.parametrize("n", [1, 3, 8, 32])
+def test_gemv_nvfp4_v2_parity_and_identity(n):
+    """GEMV on V2 rows: oracle parity, and bit-identical to the same values
+    in V1 rows (the unit arithmetic is the same)."""
+    m, k = 300, 1536
+    note(f"gemv nvfp4_v2 n={n}")
+    v1 = gen.nvfp4_rows(m, k, gen.SEED_MOE_W + 77)
+    v2 = formats.repack_nvfp4_v2(v1, m, k)
+    x = acts(n, k, 5)
+    got = gpu_gemm("nvfp4_v2", v2, x, m, "gemv")
+    check_full("nvfp4_v2", v2, x, m, k, n, got, TAU_F32, f"gemv nvfp4_v2 n={n}")
+    assert np.array_equal(got, gpu_gemm("nvfp4", v1, x, m, "gemv"))
+
+
+def test_nvfp4_v2_rejected_on_matrix_cores():
+    import gemv_prefill_decode_amd as qmm
+    m, k, n = 64, 256, 64
+    v2 = formats.repack_nvfp4_v2(gen.nvfp4_rows(m, k, 3), m, k)
+    with pytest.raises(qmm.QmmError) as ei:
+        gpu_gemm("nvfp4_v2", v2, acts(n, k), m, "mfma", workspace=None)
+    assert ei.value.status == 4
+
+
+@pytest.mark.parametrize("t,n_used", [(1, 8), (16, 3)])
+def test_moe_nvfp4_v2_bit_identical_to_v1(t, n_used):
+    """Gate/up and down on V2 expert rows (repacked on the device) equal the
+    V1 results bit for bit, as the pages assert before timing their V2 arms;
+    and the V1 results pass the oracle."""
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    n_expert, in_f, n_ff = 9, 512, 96
+    note(f"moe nvfp4_v2 t={t}")
+    wg, wu, ids, sc, x = _moe_inputs(n_expert, in_f, n_ff, t, n_used, seed=t)
+    rows = n_expert * n_ff
+    dg, du, di, ds, dx = to_dev(wg), to_dev(wu), to_dev(ids.astype(np.int32)), to_dev(sc), to_dev(x)
+    g1, u1 = qmm.moe_gateup(dg, du, di, ds, dx, n_expert, n_ff, "nvfp4")
+    g2, u2 = qmm.moe_gateup(qmm.repack_nvfp4_v2(dg, rows, in_f), qmm.repack_nvfp4_v2(du, rows, in_f),
+                            di, ds, dx, n_expert, n_ff, "nvfp4_v2")
+    torch.cuda.synchronize()
+    assert torch.equal(g1, g2) and torch.equal(u1, u2)
+    rg, ru, Sg, Su = ref.moe_ref("nvfp4", wg, wu, ids, sc, x, n_expert, in_f, n_ff)
+    assert ref.tolerance_check(g1.cpu().numpy(), rg, Sg, TAU_F32)[0]
+    assert ref.tolerance_check(u1.cpu().numpy(), ru, Su, TAU_F32)[0]
+    # down projection: d_model rows over n_ff inputs
+    d_model = 80
+    wd, _, scd, act = _down_inputs(n_expert, 128, d_model, t, n_used, seed=t)
+    dwd = to_dev(wd)
+    y1, p1 = qmm.moe_down(dwd, di, to_dev(scd), to_dev(act), n_expert, d_model, "nvfp4")
+    y2, p2 = qmm.moe_down(qmm.repack_nvfp4_v2(dwd, n_expert * d_model, 128), di, to_dev(scd),
+                          to_dev(act), n_expert, d_model, "nvfp4_v2")
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(p1, p2)
