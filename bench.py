@@ -18,7 +18,9 @@ The same JSON line also carries the other half of the metric:
   moe      the NVFP4 gate/up rows at t = 1 and t = 16 (64 experts, 8 used,
            in_f 4096, n_ff 2048), rotated over 4 weight copies x 8 id draws,
            and the down projection after it (4096 rows over 2048 inputs per
-           expert, per-pair activations, slots summed per token).
+           expert, per-pair activations, slots summed per token); each also
+           on the same values in NVFP4 V2 rows (outputs checked bit-identical
+           to V1 before timing).
   roofline the dominant prefill kernel instance: algorithmic flops per launch
            over its average launch time from the events of the timed region.
   cpu_baseline  the CPU oracle over the whole prefill step on the host cores.
@@ -291,6 +293,8 @@ def run_moe(args):
             u[e * per_e + 5] ^= (c * 16 + 2) & 0xFF
         sets.append((g, u))
     del planes
+    rows = n_expert * n_ff
+    sets_v2 = [(qmm.repack_nvfp4_v2(g, rows, in_f), qmm.repack_nvfp4_v2(u, rows, in_f)) for g, u in sets]
     res = {}
     L = 32
     for t in (1, 16):
@@ -309,12 +313,28 @@ def run_moe(args):
         del g
         byts = statistics.mean(2 * uniq[i % 8] * per_e + 4 * t * in_f + 2 * 4 * n_pairs * n_ff
                                for i in range(L))
+        # the same values in NVFP4 V2 rows: bit-identical outputs, then timed
+        ref_g, ref_u = qmm.moe_gateup(sets[0][0], sets[0][1], draws[0], sc, x, n_expert, n_ff)
+        ref_g, ref_u = ref_g.clone(), ref_u.clone()
+        v2_g, v2_u = qmm.moe_gateup(sets_v2[0][0], sets_v2[0][1], draws[0], sc, x, n_expert, n_ff,
+                                    "nvfp4_v2")
+        if not (torch.equal(ref_g, v2_g) and torch.equal(ref_u, v2_u)):
+            raise SystemExit("MoE gate/up: NVFP4 V2 differs from V1")
+        g = capture([(lambda c=sets_v2[i % copies], d=draws[i % 8]:
+                      qmm.moe_gateup(c[0], c[1], d, sc, x, n_expert, n_ff, "nvfp4_v2", gate_out=go,
+                                     up_out=uo))
+                     for i in range(L)])
+        tv2 = time_graph(g, L, 5)
+        del g
         res[f"t{t}"] = {"us": round(tt * 1e6, 2),
                         "GB/s": round(byts / tt / 1e9, 1),
                         "frac_hbm_peak": round(byts / tt / 1e9 / PEAK_HBM_GBS, 4),
                         "unique_experts_mean": round(statistics.mean(uniq), 2),
-                        "algorithmic_bytes_mean": round(byts)}
-        log(f"moe t={t}: {res[f't{t}']['us']} us {res[f't{t}']['GB/s']} GB/s")
+                        "algorithmic_bytes_mean": round(byts),
+                        "v2": {"us": round(tv2 * 1e6, 2), "GB/s": round(byts / tv2 / 1e9, 1),
+                               "bit_identical_to_v1": True}}
+        log(f"moe t={t}: {res[f't{t}']['us']} us {res[f't{t}']['GB/s']} GB/s; "
+            f"V2 {res[f't{t}']['v2']['us']} us")
     return res
 
 
@@ -346,6 +366,7 @@ def run_moe_down(args):
             w[e * per_e + 7] ^= (c * 16 + 3) & 0xFF
         sets.append(w)
     del base
+    sets_v2 = [qmm.repack_nvfp4_v2(w, n_expert * d_model, n_ff) for w in sets]
     res = {}
     L = 32
     for t in (1, 16):
@@ -364,14 +385,27 @@ def run_moe_down(args):
         del g
         byts = statistics.mean(uniq[i % 8] * per_e + 4 * n_pairs * n_ff + 4 * t * d_model
                                for i in range(L))
+        y1, _ = qmm.moe_down(sets[0], draws[0], sc, act, n_expert, d_model)
+        y1 = y1.clone()
+        y2, _ = qmm.moe_down(sets_v2[0], draws[0], sc, act, n_expert, d_model, "nvfp4_v2")
+        if not torch.equal(y1, y2):
+            raise SystemExit("MoE down: NVFP4 V2 differs from V1")
+        g = capture([(lambda w=sets_v2[i % copies], d=draws[i % 8]:
+                      qmm.moe_down(w, d, sc, act, n_expert, d_model, "nvfp4_v2", y=y, pair_out=po))
+                     for i in range(L)])
+        tv2 = time_graph(g, L, 5)
+        del g
         res[f"t{t}"] = {"us": round(tt * 1e6, 2),
                         "GB/s": round(byts / tt / 1e9, 1),
                         "frac_hbm_peak": round(byts / tt / 1e9 / PEAK_HBM_GBS, 4),
                         "unique_experts_mean": round(statistics.mean(uniq), 2),
                         "algorithmic_bytes_mean": round(byts),
-                        "pair_terms_bytes": 2 * 4 * n_pairs * d_model}
-        log(f"moe down t={t}: {res[f't{t}']['us']} us {res[f't{t}']['GB/s']} GB/s")
-    del sets
+                        "pair_terms_bytes": 2 * 4 * n_pairs * d_model,
+                        "v2": {"us": round(tv2 * 1e6, 2), "GB/s": round(byts / tv2 / 1e9, 1),
+                               "bit_identical_to_v1": True}}
+        log(f"moe down t={t}: {res[f't{t}']['us']} us {res[f't{t}']['GB/s']} GB/s; "
+            f"V2 {res[f't{t}']['v2']['us']} us")
+    del sets, sets_v2
     torch.cuda.empty_cache()
     return res
 
