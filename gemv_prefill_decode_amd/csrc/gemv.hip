@@ -483,16 +483,16 @@ struct XGlobal {
 // independent 16-byte loads in flight per batch; ends with a barrier.  With
 // SUMS, the sums of each run of 16 activations (k/16 per row, k a multiple
 // of 16) follow the rows: ((x0+x1)+(x2+x3)) + ... in a fixed order.
-template <int NT, bool SUMS = false>
+template <int NT, bool SUMS = false, int TPB = 256>
 __device__ __forceinline__ void stage_x(float* sx, rsrc_t xr, const uint32_t (&xoff)[NT], int k) {
     constexpr int U = NT >= 8 ? 1 : 8 / NT;  // float4 columns per thread per batch
     const int ld = xpad_len(k);
     const int per = k >> 2;  // float4 per row
-    for (int c0 = threadIdx.x; c0 < per; c0 += 256 * U) {
+    for (int c0 = threadIdx.x; c0 < per; c0 += TPB * U) {
         f32x4 v[NT][U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int c = c0 + 256 * u;
+            const int c = c0 + TPB * u;
 #pragma unroll
             for (int j = 0; j < NT; ++j)
                 v[j][u] = __builtin_bit_cast(
@@ -500,7 +500,7 @@ __device__ __forceinline__ void stage_x(float* sx, rsrc_t xr, const uint32_t (&x
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int c = c0 + 256 * u;
+            const int c = c0 + TPB * u;
             if (c < per)
 #pragma unroll
                 for (int j = 0; j < NT; ++j) *(f32x4*)(sx + j * ld + xpad(4 * c)) = v[j][u];
@@ -510,7 +510,7 @@ __device__ __forceinline__ void stage_x(float* sx, rsrc_t xr, const uint32_t (&x
     if constexpr (SUMS) {
         const int nrun = k >> 4;
         float* sums = sx + NT * ld;
-        for (int t = threadIdx.x; t < NT * nrun; t += 256) {
+        for (int t = threadIdx.x; t < NT * nrun; t += TPB) {
             const int j = t / nrun, r = t - j * nrun;
             const float* p = sx + j * ld + xpad(16 * r);  // 16 contiguous floats
             const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
@@ -831,11 +831,11 @@ extern __shared__ __attribute__((aligned(16))) float qmm_dyn_lds[];
 // grid: x = work groups (their 4 waves stride over the row groups), y = token
 // groups of NT.  XL: activations staged in LDS (dynamic shared memory of
 // xlds_floats(NT, k, RUNS > 0) floats).
-template <int QT, int NT, int R, int D, bool XL>
-__global__ __launch_bounds__(256) void gemv_kernel(float* __restrict__ dst,
-                                                   const uint8_t* __restrict__ w,
-                                                   const float* __restrict__ x, int m, int k,
-                                                   int n, int rb, int lpr_log2, int n_rg) {
+template <int QT, int NT, int R, int D, bool XL, int WPG = 4>
+__global__ __launch_bounds__(64 * WPG) void gemv_kernel(float* __restrict__ dst,
+                                                        const uint8_t* __restrict__ w,
+                                                        const float* __restrict__ x, int m, int k,
+                                                        int n, int rb, int lpr_log2, int n_rg) {
     const int wave = wave_id();
     const int tok0 = blockIdx.y * NT;
     const int ntok = min(NT, n - tok0);
@@ -851,14 +851,14 @@ __global__ __launch_bounds__(256) void gemv_kernel(float* __restrict__ dst,
     if constexpr (XL) {
         constexpr bool SM = GUnit<QT>::RUNS > 0;
         const XLds<NT, SM> xs{qmm_dyn_lds, xpad_len(k), qmm_dyn_lds + NT * xpad_len(k), k >> 4};
-        gemv_stream<QT, NT, R, D>(g, blockIdx.x * 4 + wave, gridDim.x * 4, n_rg, xs, store,
-                                  [&]() { stage_x<NT, SM>(qmm_dyn_lds, xr, xoff, k); });
+        gemv_stream<QT, NT, R, D>(g, blockIdx.x * WPG + wave, gridDim.x * WPG, n_rg, xs, store,
+                                  [&]() { stage_x<NT, SM, 64 * WPG>(qmm_dyn_lds, xr, xoff, k); });
     } else {
         XGlobal<NT> xs;
         xs.xr = xr;
 #pragma unroll
         for (int j = 0; j < NT; ++j) xs.xoff[j] = xoff[j];
-        gemv_stream<QT, NT, R, D>(g, blockIdx.x * 4 + wave, gridDim.x * 4, n_rg, xs, store);
+        gemv_stream<QT, NT, R, D>(g, blockIdx.x * WPG + wave, gridDim.x * WPG, n_rg, xs, store);
     }
 }
 
@@ -1151,10 +1151,12 @@ int64_t gemv_max_window_bytes(int qt, int64_t k, int64_t rb) {
 // Work groups for a stream of n_rg row groups shared by `sets` independent
 // streams: about num_cu * wg_per_cu work groups in total, never more than one
 // wave per row group.
-static unsigned stream_grid(int64_t n_rg, int64_t sets, const GemvTuning& tune) {
-    int64_t target = ((int64_t)tune.num_cu * tune.wg_per_cu + sets - 1) / (sets > 0 ? sets : 1);
+static unsigned stream_grid(int64_t n_rg, int64_t sets, const GemvTuning& tune, int wpg = 4) {
+    // rounded down: a few work groups past what is resident at once would run
+    // as a second round (the whole time of a round again)
+    int64_t target = (int64_t)tune.num_cu * tune.wg_per_cu / (sets > 0 ? sets : 1);
     if (target < 1) target = 1;
-    const int64_t need = (n_rg + 3) / 4;
+    const int64_t need = (n_rg + wpg - 1) / wpg;
     return (unsigned)(need < target ? need : target);
 }
 
@@ -1201,9 +1203,17 @@ static void launch_gemv_nt(float* dst, const uint8_t* w, const float* x, int64_t
         const int64_t gy = (n + NT - 1) / NT;
         const int64_t lds = (int64_t)xlds_floats(NT, (int)k, GUnit<QT>::RUNS > 0) * 4;
         if (lds <= tune.lds_per_wg) {
-            const dim3 grid(stream_grid(n_rg, gy, lds_limited(tune, lds)), (unsigned)gy);
-            gemv_kernel<QT, NT, R, D, true><<<grid, 256, (size_t)lds, st>>>(
-                dst, w, x, (int)m, (int)k, (int)n, (int)rb, l, (int)n_rg);
+            const GemvTuning lt = lds_limited(tune, lds);
+            if (lt.wg_per_cu == 1) {
+                // one work group per CU: 8 waves share the staged rows
+                const dim3 grid(stream_grid(n_rg, gy, lt, 8), (unsigned)gy);
+                gemv_kernel<QT, NT, R, D, true, 8><<<grid, 512, (size_t)lds, st>>>(
+                    dst, w, x, (int)m, (int)k, (int)n, (int)rb, l, (int)n_rg);
+            } else {
+                const dim3 grid(stream_grid(n_rg, gy, lt), (unsigned)gy);
+                gemv_kernel<QT, NT, R, D, true><<<grid, 256, (size_t)lds, st>>>(
+                    dst, w, x, (int)m, (int)k, (int)n, (int)rb, l, (int)n_rg);
+            }
         } else {
             const dim3 grid(stream_grid(n_rg, gy, tune), (unsigned)gy);
             gemv_kernel<QT, NT, R, D, false><<<grid, 256, 0, st>>>(
@@ -1215,9 +1225,12 @@ static void launch_gemv_nt(float* dst, const uint8_t* w, const float* x, int64_t
 template <int QT>
 static void launch_gemv_qt(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k,
                            int64_t n, int64_t rb, const GemvTuning& tune, hipStream_t st) {
+    const bool fits8 = (int64_t)xlds_floats(8, (int)k, GUnit<QT>::RUNS > 0) * 4 <= tune.lds_per_wg;
+    const bool fits4 = (int64_t)xlds_floats(4, (int)k, GUnit<QT>::RUNS > 0) * 4 <= tune.lds_per_wg;
     if (n == 1) launch_gemv_nt<QT, 1>(dst, w, x, m, k, n, rb, tune, st);
     else if (n == 2) launch_gemv_nt<QT, 2>(dst, w, x, m, k, n, rb, tune, st);
-    else if (n <= 4) launch_gemv_nt<QT, 4>(dst, w, x, m, k, n, rb, tune, st);
+    else if (n <= 4 || (!fits8 && fits4))  // groups of 4 staged rows beat 8 rows read from L2
+        launch_gemv_nt<QT, 4>(dst, w, x, m, k, n, rb, tune, st);
     else launch_gemv_nt<QT, 8>(dst, w, x, m, k, n, rb, tune, st);
 }
 

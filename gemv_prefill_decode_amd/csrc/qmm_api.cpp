@@ -38,12 +38,26 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
     return true;
 }
 
-int g_gemv_max_n = 32;
+// QMM_PATH_AUTO: the GEMV for n <= 8, and for n <= 16 when the weight
+// matrix has at most 8 Mi elements; the matrix-core path otherwise.  Measured
+// on MI355X (both paths graph-replayed over n = 4 .. 64 with weights rotated
+// through HBM): at 14336x4096 the matrix-core path is faster from n = 12
+// (at n = 32, 50 us against 105 us), at 4608x1024 and 3072x1024 only from
+// n = 16 .. 32, because its time has a floor of about 12 us (pre-pass, split
+// sum, launch gaps) while the GEMV's grows with the weight bytes times
+// ceil(n / 8).  QMM_GEMV_MAX_N replaces the rule by a plain threshold.
+constexpr int AUTO_GEMV_N = 8;
+constexpr int AUTO_GEMV_N_SMALL = 16;
+constexpr int64_t AUTO_SMALL_ELEMS = (int64_t)8 << 20;
+
+int g_gemv_max_n = AUTO_GEMV_N_SMALL;
+bool g_gemv_max_n_set = false;
 std::once_flag g_env_once;
 
 void parse_env() {
     const char* v = std::getenv("QMM_GEMV_MAX_N");
     if (!v) return;
+    g_gemv_max_n_set = true;
     char* end = nullptr;
     errno = 0;
     const long val = std::strtol(v, &end, 10);
@@ -183,6 +197,14 @@ int check_weights(const void* w, int64_t m, int64_t k, int qt, int64_t* rb) {
     return QMM_OK;
 }
 
+int auto_path(int64_t m, int64_t k, int64_t n) {
+    const int lim = qmm_gemv_max_n();
+    if (lim < 0) return -1;
+    if (g_gemv_max_n_set) return n <= lim ? QMM_PATH_GEMV : QMM_PATH_MFMA;
+    const bool gemv = n <= AUTO_GEMV_N || (n <= AUTO_GEMV_N_SMALL && m * k <= AUTO_SMALL_ELEMS);
+    return gemv ? QMM_PATH_GEMV : QMM_PATH_MFMA;
+}
+
 // Shared validation of the gemm entry points; resolves AUTO.  On success
 // *rb is the row stride and *path the concrete path.
 int check_gemm(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qtype,
@@ -196,9 +218,8 @@ int check_gemm(float* dst, const void* w, const float* x, int64_t m, int64_t k, 
     int64_t t1, t2;
     if (!mul_ok(n, k, &t1) || !mul_ok(n, m, &t2)) return QMM_ERR_SHAPE;
     if (*path == QMM_PATH_AUTO) {
-        const int lim = qmm_gemv_max_n();
-        if (lim < 0) return QMM_ERR_RANGE;
-        *path = n <= lim ? QMM_PATH_GEMV : QMM_PATH_MFMA;
+        *path = auto_path(m, k, n);
+        if (*path < 0) return QMM_ERR_RANGE;
     }
     if (*path == QMM_PATH_GEMV) {
         // one work group addresses at most this window of w, and 8 token rows of x
@@ -285,9 +306,8 @@ int64_t qmm_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int qtype, int
     if (m < 1 || k < 1 || n < 1) return -QMM_ERR_SHAPE;
     if (m > INT_MAX || k > INT_MAX || n > INT_MAX) return -QMM_ERR_RANGE;
     if (path == QMM_PATH_AUTO) {
-        const int lim = qmm_gemv_max_n();
-        if (lim < 0) return -QMM_ERR_RANGE;
-        path = n <= lim ? QMM_PATH_GEMV : QMM_PATH_MFMA;
+        path = auto_path(m, k, n);
+        if (path < 0) return -QMM_ERR_RANGE;
     }
     if (path == QMM_PATH_GEMV) return 0;
     if (path != QMM_PATH_MFMA) return -QMM_ERR_PATH;
@@ -305,9 +325,8 @@ int qmm_gemm_plan(int64_t m, int64_t k, int64_t n, int qtype, int path, int with
     if (m < 1 || k < 1 || n < 1) return QMM_ERR_SHAPE;
     if (m > INT_MAX || k > INT_MAX || n > INT_MAX) return QMM_ERR_RANGE;
     if (path == QMM_PATH_AUTO) {
-        const int lim = qmm_gemv_max_n();
-        if (lim < 0) return QMM_ERR_RANGE;
-        path = n <= lim ? QMM_PATH_GEMV : QMM_PATH_MFMA;
+        path = auto_path(m, k, n);
+        if (path < 0) return QMM_ERR_RANGE;
     }
     if (path == QMM_PATH_GEMV) {
         out[0] = QMM_PATH_GEMV;

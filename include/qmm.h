@@ -79,7 +79,7 @@ typedef enum {
 
 /* Kernel path selector for qmm_gemm_path. */
 typedef enum {
-    QMM_PATH_AUTO = 0,     /* n <= qmm_gemv_max_n() -> GEMV, else MFMA        */
+    QMM_PATH_AUTO = 0,     /* the measured crossover (qmm_gemm) -> GEMV or MFMA */
     QMM_PATH_GEMV = 1,     /* f32 FMA, any n (decode path)                     */
     QMM_PATH_MFMA = 2      /* f16 MFMA tiles, f32 accumulation, any n (prefill) */
 } qmm_path;
@@ -93,10 +93,11 @@ typedef enum {
  *   m,k,n >= 1; k % block_elems(qtype) == 0 and k % 4 == 0.
  *   qtype one of QMM_F32..QMM_NVFP4_V2 (NVFP4_V2 on the GEMV path only).
  * Dispatch (the GEMV-vs-GEMM crossover of aprender-serve cublas_prefill,
- * cublas_gemm_threshold): n <= qmm_gemv_max_n() runs the f32 GEMV (results
- * within 1e-5 * sum|w*x| of the exact value), otherwise the MFMA kernel,
- * which rounds W and x to f16 (RNE) and accumulates in f32 (within
- * 2e-3 * sum|w*x|).
+ * cublas_gemm_threshold, re-measured on MI355X): the f32 GEMV (results within
+ * 1e-5 * sum|w*x| of the exact value) for n <= 8, and for n <= 16 when
+ * m*k <= 8 Mi weights; otherwise the MFMA kernel, which rounds W and x to
+ * f16 (RNE) and accumulates in f32 (within 2e-3 * sum|w*x|).  With
+ * QMM_GEMV_MAX_N set: the GEMV for n <= that value, else MFMA.
  * Limits: the bytes of one 256-row weight tile (or one GEMV row group) and
  * of 128 (GEMV: 8) token rows of x each below 2^31; m, n, k below 2^31.
  * Larger values return QMM_ERR_RANGE.
@@ -246,10 +247,12 @@ int64_t qmm_row_bytes(int qtype, int64_t k);
 /* Elements per block of qtype, or -QMM_ERR_QTYPE. */
 int qmm_block_elems(int qtype);
 
-/* The n at or below which QMM_PATH_AUTO uses the GEMV (default 32; the
- * environment variable QMM_GEMV_MAX_N overrides it; a set but unparseable or
- * non-positive value makes this return -QMM_ERR_RANGE and every AUTO call
- * fail with QMM_ERR_RANGE, never a silent default). */
+/* The largest n that QMM_PATH_AUTO sends to the GEMV (16 by default: n <= 8
+ * always, 9..16 for weight matrices of at most 8 Mi elements); the
+ * environment variable QMM_GEMV_MAX_N replaces the rule by the threshold it
+ * gives; a set but unparseable or non-positive value makes this return
+ * -QMM_ERR_RANGE and every AUTO call fail with QMM_ERR_RANGE, never a silent
+ * default. */
 int qmm_gemv_max_n(void);
 
 /* Static string for a status code. */

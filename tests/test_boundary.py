@@ -159,7 +159,7 @@ def test_default_gemv_max_n():
     lib = _lib()
     if "QMM_GEMV_MAX_N" in os.environ:
         pytest.skip("QMM_GEMV_MAX_N set in the environment")
-    assert lib.qmm_gemv_max_n() == 32
+    assert lib.qmm_gemv_max_n() == 16
 
 
 def test_workspace_bytes_plan_and_errors():

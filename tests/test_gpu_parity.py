@@ -90,14 +90,16 @@ def test_mfma_paths_agree_bit_for_bit_unsplit(qt):
 
 @pytest.mark.parametrize("qt", QTS)
 def test_auto_dispatch_threshold(qt):
-    m, k = 130, 512 if qt != "f32" else 512
-    for n in (32, 33):
-        note(f"auto {qt} n={n}")
+    """AUTO: the GEMV up to n = 16 for a small weight matrix, up to n = 8
+    for one of more than 8 Mi weights; the matrix-core path above."""
+    for m, k, lim in ((130, 512, 16), (2112, 4096, 8)):
         w = weights(qt, m, k, 3)
-        x = acts(n, k, 3)
-        got = gpu_gemm(qt, w, x, m, "auto")
-        gv = gpu_gemm(qt, w, x, m, "gemv" if n <= 32 else "mfma")
-        assert np.array_equal(got, gv)
+        for n in (lim, lim + 1):
+            note(f"auto {qt} {m}x{k} n={n}")
+            x = acts(n, k, 3)
+            got = gpu_gemm(qt, w, x, m, "auto")
+            gv = gpu_gemm(qt, w, x, m, "gemv" if n <= lim else "mfma")
+            assert np.array_equal(got, gv)
 
 
 @pytest.mark.parametrize("qt", QTS)
