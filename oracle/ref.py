@@ -25,6 +25,10 @@ scale, the result accumulated into a zeroed y over the token's pairs):
     y[tau, r] = sum_s scale[p] * sum_c Wd[e_p][r, c] * act[p, c]
 
 with the slots s taken in order; S_y sums |scale[p] * Wd[e_p][r, c] * act[p, c]|.
+
+Q8_1 activations (the served arithmetic of the same page): x is replaced by
+its per-32 quantization d*q (quantize_q8_1 below) and the gate/up is the
+projection of those dequantized activations.
 """
 
 from __future__ import annotations
@@ -63,12 +67,15 @@ def gemm_ref_rows(name: str, w, x, m: int, k: int, rows, cols, row_bytes: int):
     return np.einsum("tk,tk->t", W, X), np.einsum("tk,tk->t", np.abs(W), np.abs(X))
 
 
-def moe_ref(name: str, w_gate, w_up, ids, scales, x, n_expert: int, in_f: int, n_ff: int):
-    """(gate, up, S_gate, S_up) as float64 [n_pairs, n_ff]."""
+def moe_ref(name: str, w_gate, w_up, ids, scales, x, n_expert: int, in_f: int, n_ff: int,
+            exact_x: bool = False):
+    """(gate, up, S_gate, S_up) as float64 [n_pairs, n_ff].  x is float32
+    (exact_x: float64 values used as they are)."""
     ids = np.asarray(ids, dtype=np.int64)
     t, n_used = ids.shape
     n_pairs = t * n_used
-    X = np.asarray(x, dtype=np.float32).reshape(t, in_f).astype(np.float64)
+    X = (np.asarray(x, dtype=np.float64) if exact_x else
+         np.asarray(x, dtype=np.float32).astype(np.float64)).reshape(t, in_f)
     sc = np.asarray(scales, dtype=np.float32).astype(np.float64)
     outs = []
     for plane, wp in enumerate((w_gate, w_up)):
@@ -163,6 +170,40 @@ def moe_down_ref_rows(name: str, w_down, ids, scales, act, n_expert: int, n_ff: 
             val[i] += sc[p] * float(W @ A[p])
             tol[i] += abs(sc[p]) * float(np.abs(W) @ np.abs(A[p]))
     return val, tol
+
+
+def quantize_q8_1(x, k: int):
+    """Q8_1 activations (memra `moe_rows_ceiling_bench.rs` quantizes x with
+    quantize_q8_1 before the served kernel; the pages name the ggml format
+    without printing it, so this is a reading): per block of 32 consecutive
+    activations of a row, d = max|x| / 127 and q = round-half-away-from-zero
+    of x * (1/d) (q = 0 when d = 0), every step in float32 as the device does
+    it, since these decide the integer codes.  Returns (q int8 [rows, k],
+    d float32 [rows, k/32])."""
+    X = np.asarray(x, dtype=np.float32).reshape(-1, k // 32, 32)
+    amax = np.max(np.abs(X), axis=2)
+    d = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(d != 0, d, np.float32(1.0)).astype(np.float32)
+    inv = np.where(d != 0, np.float32(1.0) / safe, np.float32(0.0)).astype(np.float32)
+    v = (X * inv[..., None]).astype(np.float32).astype(np.float64)
+    q = np.trunc(v + np.copysign(0.5, v))
+    assert np.all(np.abs(q) <= 127)
+    return q.astype(np.int8).reshape(-1, k), d
+
+
+def dequantize_q8_1(q, d, k: int):
+    """x_hat = d[block] * q (exact in float64)."""
+    Q = np.asarray(q, dtype=np.int64).reshape(-1, k // 32, 32).astype(np.float64)
+    D = np.asarray(d, dtype=np.float32).reshape(-1, k // 32, 1).astype(np.float64)
+    return (Q * D).reshape(-1, k)
+
+
+def moe_q8_ref(name: str, w_gate, w_up, ids, scales, xq, xd, n_expert: int, in_f: int, n_ff: int):
+    """The gate/up projections of Q8_1 activations: moe_ref applied to the
+    dequantized activations d*q (what the integer group dot products, scaled
+    by the group and block scales, compute).  (gate, up, S_gate, S_up)."""
+    xh = dequantize_q8_1(xq, xd, in_f)
+    return moe_ref(name, w_gate, w_up, ids, scales, xh, n_expert, in_f, n_ff, exact_x=True)
 
 
 def tolerance_check(got, ref, S, tau: float):

@@ -207,6 +207,72 @@ def test_moe_down_sampled_rows_equal_full():
     assert np.allclose(tol, S[toks, rows], rtol=1e-12, atol=1e-12)
 
 
+def test_quantize_q8_1_pins():
+    """Q8_1 quantization: exactly representable blocks come back exactly;
+    halves round away from zero (not to even); a zero block gives d = q = 0;
+    the block maximum maps to +-127; |x - d*q| <= d/2 otherwise."""
+    k = 96
+    # block 0: x = d0 * c with d0 = 2^-6 and max |c| = 127 -> (c, d0) exactly
+    c = np.arange(-127, 129, 8)[:32].astype(np.float64)
+    c[5] = 127
+    blk0 = (c * 2.0 ** -6).astype(np.float32)
+    # block 1: amax 127 -> d = 1, id = 1: values +-2.5 and +-0.5 sit on halves
+    blk1 = np.zeros(32, np.float32)
+    blk1[:6] = [127.0, 2.5, -2.5, 0.5, -0.5, 3.5]
+    blk2 = np.zeros(32, np.float32)
+    x = np.concatenate([blk0, blk1, blk2])
+    q, d = ref.quantize_q8_1(x, k)
+    assert d[0, 0] == np.float32(2.0 ** -6) and np.array_equal(q[0, :32], c.astype(np.int8))
+    assert d[0, 1] == 1.0 and list(q[0, 32:38]) == [127, 3, -3, 1, -1, 4]
+    assert d[0, 2] == 0.0 and not q[0, 64:].any()
+    rng = np.random.default_rng(3)
+    xr = (rng.standard_normal(4 * 256) * rng.choice([1e-3, 1.0, 50.0], 4 * 256)).astype(np.float32)
+    q, d = ref.quantize_q8_1(xr, 256)
+    X = xr.reshape(4, 8, 32).astype(np.float64)
+    Q = q.reshape(4, 8, 32).astype(np.int64)
+    D = d.reshape(4, 8, 1).astype(np.float64)
+    am = np.argmax(np.abs(X), axis=2)
+    assert np.all(np.abs(np.take_along_axis(Q, am[..., None], 2)) == 127)
+    assert np.all(np.abs(X - D * Q) <= D / 2 * (1 + 1e-6))
+    assert np.array_equal(ref.dequantize_q8_1(q, d, 256), (D * Q).reshape(4, 256))
+
+
+def test_moe_q8_ref_brute_force():
+    """Gate/up of Q8_1 activations against the literal decoder with the group
+    dot products summed as exact integers (2 * E2M1 codes times int8 codes)."""
+    from fractions import Fraction
+    n_expert, in_f, n_ff, t, n_used = 4, 128, 5, 2, 2
+    wg = np.concatenate([gen.nvfp4_rows(n_ff, in_f, 0x8181 + 2 * e) for e in range(n_expert)])
+    wu = np.concatenate([gen.nvfp4_rows(n_ff, in_f, 0x8181 + 2 * e + 1) for e in range(n_expert)])
+    ids = gen.expert_ids(t, n_used, n_expert, 5)
+    sc = gen.pair_scales(2 * t * n_used)
+    x = gen.xorshift_f32(t * in_f, 91)
+    xq, xd = ref.quantize_q8_1(x, in_f)
+    g, u, Sg, Su = ref.moe_q8_ref("nvfp4", wg, wu, ids, sc, xq, xd, n_expert, in_f, n_ff)
+    per = n_ff * formats.row_bytes("nvfp4", in_f)
+    rb = formats.row_bytes("nvfp4", in_f)
+    n_pairs = t * n_used
+    for tau in range(t):
+        for s in range(n_used):
+            p = tau * n_used + s
+            e = int(ids[tau, s])
+            for plane, wp, out in ((0, wg, g), (1, wu, u)):
+                for r in range(n_ff):
+                    row = bytes(wp[e * per + r * rb:e * per + (r + 1) * rb])
+                    tot = Fraction(0)
+                    for b in range(in_f // 32):
+                        for h in range(2):          # the two 16-element scale groups
+                            isum = 0
+                            for i in range(16):
+                                c = 32 * b + 16 * h + i
+                                w2 = scalar.element("nvfp4", row, c) / scalar.fp8_e4m3(row[(c // 64) * 36 + (c % 64) // 16])
+                                isum += int(round(2 * w2)) * int(xq[tau, c])
+                            gs = row[(32 * b + 16 * h) // 64 * 36 + ((32 * b + 16 * h) % 64) // 16]
+                            tot += Fraction(isum) * Fraction(scalar.fp8_e4m3(gs)) / 2 * Fraction(float(xd[tau, b]))
+                    want = float(tot * Fraction(float(sc[plane * n_pairs + p])))
+                    assert abs(out[p, r] - want) <= 1e-13 * max(1.0, abs(want))
+
+
 def test_tolerance_check_semantics():
     r = np.array([[1.0, -2.0]])
     S = np.array([[1.0, 2.0]])
