@@ -22,7 +22,7 @@ import threading
 __all__ = [
     "QTYPES", "PATHS", "QmmError", "lib_path", "load", "gemm", "workspace_bytes", "gemm_plan",
     "plan_kernel_name", "moe_gateup", "moe_down",
-    "stream_loadonly", "repack_nvfp4_v2",
+    "stream_loadonly", "repack_nvfp4_v2", "quantize_q8_1", "moe_gateup_q8",
     "row_bytes", "block_elems", "gemv_max_n", "status_str", "abi_version",
 ]
 
@@ -71,6 +71,10 @@ def load() -> ctypes.CDLL:
         lib.qmm_moe_gateup.restype = i32
         lib.qmm_moe_down.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
         lib.qmm_moe_down.restype = i32
+        lib.qmm_quantize_q8_1.argtypes = [vp, vp, vp, i64, i64, vp]
+        lib.qmm_quantize_q8_1.restype = i32
+        lib.qmm_moe_gateup_q8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+        lib.qmm_moe_gateup_q8.restype = i32
         lib.qmm_nvfp4_repack_v2.argtypes = [vp, vp, i64, i64, vp]
         lib.qmm_nvfp4_repack_v2.restype = i32
         lib.qmm_stream_loadonly.argtypes = [vp, vp, i64, i64, i32, vp]
@@ -286,6 +290,52 @@ def moe_down(w_down, expert_ids, pair_scale, act, n_expert: int, d_model: int, q
     if st != 0:
         raise QmmError(st, "qmm_moe_down")
     return y, pair_out
+
+
+def quantize_q8_1(x, q=None, d=None, stream=None):
+    """Q8_1 activations of x (float32 [rows, k], k % 32 == 0): returns
+    (q int8 [rows, k], d float32 [rows, k/32])."""
+    import torch
+    lib = load()
+    rows, k = x.shape
+    if q is None:
+        q = torch.empty((rows, k), dtype=torch.int8, device=x.device)
+    if d is None:
+        d = torch.empty((rows, k // 32), dtype=torch.float32, device=x.device)
+    st = lib.qmm_quantize_q8_1(_dev(q, "q", torch.int8), _dev(d, "d", torch.float32),
+                               _dev(x, "x", torch.float32), rows, k, _stream(stream))
+    if st != 0:
+        raise QmmError(st, "qmm_quantize_q8_1")
+    return q, d
+
+
+def moe_gateup_q8(w_gate, w_up, expert_ids, pair_scale, xq, xd, n_expert: int, n_ff: int,
+                  qtype="nvfp4", gate_out=None, up_out=None, stream=None):
+    """moe_gateup on Q8_1 activations (xq int8 [t, in_f], xd float32
+    [t, in_f/32] from quantize_q8_1); returns (gate, up)."""
+    import torch
+    lib = load()
+    qt = _qt(qtype)
+    t, n_used = expert_ids.shape
+    t2, in_f = xq.shape
+    if t2 != t or xd.numel() != t * (in_f // 32):
+        raise ValueError("xq / xd do not match expert_ids")
+    n_pairs = t * n_used
+    if pair_scale.numel() != 2 * n_pairs:
+        raise ValueError("pair_scale must hold 2*t*n_used floats")
+    if gate_out is None:
+        gate_out = torch.empty((n_pairs, n_ff), dtype=torch.float32, device=xq.device)
+    if up_out is None:
+        up_out = torch.empty((n_pairs, n_ff), dtype=torch.float32, device=xq.device)
+    st = lib.qmm_moe_gateup_q8(_dev(gate_out, "gate_out", torch.float32),
+                               _dev(up_out, "up_out", torch.float32), _dev(w_gate, "w_gate"),
+                               _dev(w_up, "w_up"), _dev(expert_ids, "expert_ids", torch.int32),
+                               _dev(pair_scale, "pair_scale", torch.float32),
+                               _dev(xq, "xq", torch.int8), _dev(xd, "xd", torch.float32), t, n_used,
+                               n_expert, in_f, n_ff, qt, _stream(stream))
+    if st != 0:
+        raise QmmError(st, "qmm_moe_gateup_q8")
+    return gate_out, up_out
 
 
 def repack_nvfp4_v2(w, rows: int, k: int, out=None, stream=None):

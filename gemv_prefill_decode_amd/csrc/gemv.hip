@@ -680,6 +680,112 @@ __device__ __forceinline__ void compute_item(GUnit<QT> (&un)[R], const typename 
         for (int j = 0; j < NT; ++j) acc[rr][j] += part[rr][j];
 }
 
+// ------------------------------------------------------------------ Q8_1 activations
+// NT rows of Q8_1 activations staged in LDS: the int8 codes as f16 (exact),
+// 8 halves of padding after every 32 (one quantization block, one NVFP4 unit)
+// so the 16-byte reads of a wave's lanes at unit-strided offsets spread over
+// the banks, then each row's k/32 block scales.
+__host__ __device__ constexpr int q8pad_len(int k) { return k / 32 * 40; }
+__host__ __device__ constexpr int q8lds_bytes(int nt, int k) { return nt * (q8pad_len(k) * 2 + k / 32 * 4); }
+
+template <int NT>
+struct XLdsQ8 {
+    static constexpr bool SUMS = false;
+    const _Float16* s;  // [NT][q8pad_len(k)]
+    int ld;
+    const float* d;     // [NT][k/32]
+    int nblk;
+};
+
+// Stage NT Q8_1 rows: codes at byte offsets qoff[j] of qr, scales at byte
+// offsets doff[j] of dr.
+template <int NT>
+__device__ __forceinline__ void stage_q8(_Float16* sx, rsrc_t qr, rsrc_t dr, const uint32_t (&qoff)[NT],
+                                         const uint32_t (&doff)[NT], int k) {
+    const int ld = q8pad_len(k), nblk = k / 32;
+    float* sd = (float*)(sx + NT * ld);
+    const int per = k >> 4;  // 16-code chunks per row
+    // rows one after another (compile-time j: a wave-varying index into the
+    // offset arrays would put them in scratch memory)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        for (int cc = threadIdx.x; cc < per; cc += 256) {
+            const u32x4 v = ld128(qr, qoff[j] + 16u * (uint32_t)cc);
+            const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+            f16x8 h0, h1;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                h0[b] = (_Float16)(float)(int8_t)(vw[b >> 2] >> (8 * (b & 3)));
+                h1[b] = (_Float16)(float)(int8_t)(vw[2 + (b >> 2)] >> (8 * (b & 3)));
+            }
+            _Float16* dst = sx + j * ld + (cc >> 1) * 40 + (cc & 1) * 16;
+            *(u32x4*)dst = __builtin_bit_cast(u32x4, h0);
+            *(u32x4*)(dst + 8) = __builtin_bit_cast(u32x4, h1);
+        }
+        for (int b = threadIdx.x; b < nblk; b += 256)
+            sd[j * nblk + b] = __builtin_bit_cast(float, ld32(dr, doff[j] + 4u * (uint32_t)b));
+    }
+    __syncthreads();
+}
+
+// One NVFP4 unit (32 weights: two groups of 16 with their E4M3 scales)
+// against Q8_1 rows.  Each group's dot product is exact: E2M1 values and
+// int8 codes are exact in f16, their products and the sums of 16 of them
+// exact in f32 (v_dot2_f32_f16), as an integer dot product would be.  Then
+// acc += d_block * (s_lo * dot_lo + s_hi * dot_hi).
+template <int QT, int NT, int R>
+__device__ __forceinline__ void compute_item(GUnit<QT> (&un)[R], const typename GUnit<QT>::Lane& ln,
+                                             int e, int, const XLdsQ8<NT>& xs, float (&acc)[R][NT]) {
+    static_assert(QT == QT_NVFP4 || QT == QT_NVFP4_V2, "Q8_1 activations with NVFP4 weights only");
+    f16x2 wl[R][8], wh[R][8];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+        un[rr].prep(ln);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t q = s == 0 ? un[rr].qs.x : (s == 1 ? un[rr].qs.y : (s == 2 ? un[rr].qs.z : un[rr].qs.w));
+            // low nibbles of bytes 0,1 (2,3) into byte 0 (2): weights 4s..4s+3
+            const uint32_t lo = q & 0x0F0F0F0Fu, hi = (q >> 4) & 0x0F0F0F0Fu;
+            const uint32_t tl = lo | (lo >> 4), th = hi | (hi >> 4);
+            wl[rr][2 * s] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(tl, 1.0f, 0);
+            wl[rr][2 * s + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(tl, 1.0f, 2);
+            wh[rr][2 * s] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(th, 1.0f, 0);
+            wh[rr][2 * s + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(th, 1.0f, 2);
+        }
+    }
+    const int pe = (e >> 5) * 40;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const _Float16* xp = xs.s + j * xs.ld + pe;
+        f16x2 xl[8], xh[8];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const u32x4 a = *(const u32x4*)(xp + 8 * i);
+            const u32x4 b = *(const u32x4*)(xp + 16 + 8 * i);
+            // components copied to scalars first: hipcc compiles a bit_cast of
+            // a vector-element expression (a.y) as one of the vector's first
+            // element
+            const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                xl[4 * i + c] = __builtin_bit_cast(f16x2, av[c]);
+                xh[4 * i + c] = __builtin_bit_cast(f16x2, bv[c]);
+            }
+        }
+        const float db = xs.d[j * xs.nblk + (e >> 5)];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+            float sl = 0.0f, sh = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                sl = __builtin_amdgcn_fdot2(wl[rr][i], xl[i], sl, false);
+                sh = __builtin_amdgcn_fdot2(wh[rr][i], xh[i], sh, false);
+            }
+            acc[rr][j] = __builtin_fmaf(db, __builtin_fmaf(un[rr].s_lo, sl, un[rr].s_hi * sh), acc[rr][j]);
+        }
+    }
+}
+
 // Issue the loads of item (row group rg, unit iteration uu) into un[].
 // Callers issue every ring refill, also for items past the end (live =
 // false), so that the number of loads issued after any item is the same on
@@ -912,12 +1018,42 @@ __device__ __forceinline__ void moe_tokens(float* __restrict__ out, const float*
     }
 }
 
-template <int QT, int R, int D>
+// moe_tokens for Q8_1 activations: codes and block scales of the chunk's
+// token rows staged in LDS (always: a row is 2.6 bytes per weight there).
+template <int QT, int NT, int R, int D>
+__device__ __forceinline__ void moe_tokens_q8(float* __restrict__ out, const float* __restrict__ scale,
+                                              const StreamGeom& g, int n_rg, rsrc_t qr, rsrc_t dr,
+                                              const int* plist, const int* tlist, int c0, int cnt,
+                                              int in_f, int n_ff) {
+    const int wave = wave_id();
+    uint32_t qoff[NT], doff[NT];
+    int pj[NT];
+    float fj[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int c = (c0 + j < cnt) ? c0 + j : c0;  // absent slots repeat a real token
+        qoff[j] = (uint32_t)tlist[c] * (uint32_t)in_f;
+        doff[j] = (uint32_t)tlist[c] * (uint32_t)(in_f / 32) * 4u;
+        pj[j] = (c0 + j < cnt) ? plist[c] : -1;
+        fj[j] = scale[plist[c]];
+    }
+    auto store = [&](int64_t row, int j, float v) {
+        if (row < n_ff && pj[j] >= 0) out[(int64_t)pj[j] * n_ff + row] = fj[j] * v;
+    };
+    __syncthreads();  // the previous chunk's waves are done with the staged rows
+    _Float16* sx = (_Float16*)qmm_dyn_lds;
+    const XLdsQ8<NT> xs{sx, q8pad_len(in_f), (const float*)(sx + NT * q8pad_len(in_f)), in_f / 32};
+    gemv_stream<QT, NT, R, D>(g, blockIdx.x * 4 + wave, gridDim.x * 4, n_rg, xs, store,
+                              [&]() { stage_q8<NT>(sx, qr, dr, qoff, doff, in_f); });
+}
+
+template <int QT, int R, int D, bool Q8 = false>
 __global__ __launch_bounds__(256) void moe_gateup_kernel(
     float* __restrict__ gate_out, float* __restrict__ up_out, const uint8_t* __restrict__ w_gate,
     const uint8_t* __restrict__ w_up, const int* __restrict__ ids, const float* __restrict__ pscale,
     const float* __restrict__ x, int t, int n_used, int n_expert, int in_f, int n_ff, int rb,
-    int lpr_log2, int n_rg, int xl, int act_pair) {
+    int lpr_log2, int n_rg, int xl, int act_pair, const int8_t* __restrict__ xq = nullptr,
+    const float* __restrict__ xd = nullptr) {
     __shared__ int plist[MOE_CHUNK];
     __shared__ int tlist[MOE_CHUNK];
     __shared__ int wcnt[4];
@@ -975,7 +1111,16 @@ __global__ __launch_bounds__(256) void moe_gateup_kernel(
         __syncthreads();
         for (int c0 = 0; c0 < cnt; c0 += MOE_NT) {
             const int left = cnt - c0;
-            if (xl) {
+            if constexpr (Q8) {
+                const rsrc_t qr = make_rsrc(xq, (uint32_t)t * (uint32_t)in_f);
+                const rsrc_t dr = make_rsrc(xd, (uint32_t)t * (uint32_t)(in_f / 32) * 4u);
+                if (left == 1)
+                    moe_tokens_q8<QT, 1, R, D>(out, scale, g, n_rg, qr, dr, plist, tlist, c0, cnt, in_f, n_ff);
+                else if (left == 2)
+                    moe_tokens_q8<QT, 2, R, D>(out, scale, g, n_rg, qr, dr, plist, tlist, c0, cnt, in_f, n_ff);
+                else
+                    moe_tokens_q8<QT, 3, R, D>(out, scale, g, n_rg, qr, dr, plist, tlist, c0, cnt, in_f, n_ff);
+            } else if (xl) {
                 if (left == 1)
                     moe_tokens<QT, 1, R, D, true>(out, scale, g, n_rg, xr, plist, tlist, c0, cnt, in_f, n_ff);
                 else if (left == 2)
@@ -1286,6 +1431,79 @@ void launch_moe(float* g, float* u, const void* wg, const void* wu, const int* i
     const uint8_t* b = (const uint8_t*)wu;
     QMM_QT_SWITCH(qt, (launch_moe_qt<Q>(g, u, a, b, ids, sc, x, t, n_used, n_expert, in_f, n_ff, rb,
                                         2, 0, tune, st)))
+}
+
+// ------------------------------------------------------------------ Q8_1 gate/up
+template <int QT>
+static void launch_moe_q8_qt(float* g, float* u, const uint8_t* wg, const uint8_t* wu, const int* ids,
+                             const float* sc, const int8_t* xq, const float* xd, int64_t t,
+                             int64_t n_used, int64_t n_expert, int64_t in_f, int64_t n_ff, int64_t rb,
+                             const GemvTuning& tune, hipStream_t st) {
+    with_rd<1>(tune, [&](auto Rc, auto Dc) {
+        constexpr int R = decltype(Rc)::value, D = decltype(Dc)::value;
+        const int l = lpr_for(QT, in_f);
+        const int64_t n_pairs = t * n_used;
+        const int64_t n_rg = (n_ff + rg_rows(l, R) - 1) / rg_rows(l, R);
+        const int64_t active = 2 * (n_pairs < n_expert ? n_pairs : n_expert);
+        GemvTuning mt = tune;
+        mt.wg_per_cu = tune.moe_wg_per_cu;
+        unsigned gx = stream_grid(n_rg, active, mt);
+        const unsigned need = (unsigned)((n_rg + 3) / 4);
+        if (gx < MOE_MIN_WG) gx = need < MOE_MIN_WG ? need : MOE_MIN_WG;
+        const dim3 grid(gx, (unsigned)n_pairs, 2);
+        moe_gateup_kernel<QT, R, D, true><<<grid, 256, (size_t)q8lds_bytes(MOE_NT, (int)in_f), st>>>(
+            g, u, wg, wu, ids, sc, nullptr, (int)t, (int)n_used, (int)n_expert, (int)in_f, (int)n_ff,
+            (int)rb, l, (int)n_rg, 1, 0, xq, xd);
+    });
+}
+
+int64_t moe_q8_lds_bytes(int64_t in_f) { return q8lds_bytes(MOE_NT, (int)in_f); }
+
+void launch_moe_q8(float* g, float* u, const void* wg, const void* wu, const int* ids, const float* sc,
+                   const int8_t* xq, const float* xd, int64_t t, int64_t n_used, int64_t n_expert,
+                   int64_t in_f, int64_t n_ff, int qt, int64_t rb, const GemvTuning& tune, hipStream_t st) {
+    const uint8_t* a = (const uint8_t*)wg;
+    const uint8_t* b = (const uint8_t*)wu;
+    if (qt == QT_NVFP4)
+        launch_moe_q8_qt<QT_NVFP4>(g, u, a, b, ids, sc, xq, xd, t, n_used, n_expert, in_f, n_ff, rb, tune, st);
+    else if (qt == QT_NVFP4_V2)
+        launch_moe_q8_qt<QT_NVFP4_V2>(g, u, a, b, ids, sc, xq, xd, t, n_used, n_expert, in_f, n_ff, rb, tune, st);
+}
+
+// Q8_1 quantization, one thread per block of 32 activations: d = max|x| /
+// 127 and q = round-half-away(x * (1/d)) (0 when d = 0), in f32.
+__global__ __launch_bounds__(256) void quantize_q8_1_kernel(int8_t* __restrict__ q, float* __restrict__ d,
+                                                            const float* __restrict__ x, int64_t nblk) {
+    for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * 256) {
+        const f32x4* xp = (const f32x4*)(x + 32 * b);
+        f32x4 v[8];
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[i] = xp[i];
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+        }
+        const float dd = amax / 127.0f;
+        const float id = dd != 0.0f ? 1.0f / dd : 0.0f;
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t c0 = (uint32_t)(uint8_t)(int8_t)(int)roundf(v[i].x * id);
+            const uint32_t c1 = (uint32_t)(uint8_t)(int8_t)(int)roundf(v[i].y * id);
+            const uint32_t c2 = (uint32_t)(uint8_t)(int8_t)(int)roundf(v[i].z * id);
+            const uint32_t c3 = (uint32_t)(uint8_t)(int8_t)(int)roundf(v[i].w * id);
+            w[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+        }
+        *(u32x4*)(q + 32 * b) = u32x4{w[0], w[1], w[2], w[3]};
+        *(u32x4*)(q + 32 * b + 16) = u32x4{w[4], w[5], w[6], w[7]};
+        d[b] = dd;
+    }
+}
+
+void launch_quantize_q8_1(int8_t* q, float* d, const float* x, int64_t nblk, hipStream_t st) {
+    int64_t blocks = (nblk + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    quantize_q8_1_kernel<<<dim3((unsigned)blocks), 256, 0, st>>>(q, d, x, nblk);
 }
 
 // ------------------------------------------------------------------ MoE down

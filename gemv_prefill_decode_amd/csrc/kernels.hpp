@@ -88,6 +88,17 @@ void launch_moe_down(float* y, float* pair_out, const void* w_down, const int* i
 // NVFP4 rows (rows x k/64 groups of 36 bytes) -> the NVFP4 V2 layout.
 void launch_nvfp4_repack_v2(void* dst, const void* src, int64_t rows, int64_t k, hipStream_t st);
 
+// MoE gate/up with Q8_1 activations (codes xq [t][in_f], block scales xd
+// [t][in_f/32]); NVFP4 or NVFP4 V2 weights.  LDS bytes it stages per work group:
+void launch_moe_q8(float* gate_out, float* up_out, const void* w_gate, const void* w_up,
+                   const int* ids, const float* scale, const int8_t* xq, const float* xd, int64_t t,
+                   int64_t n_used, int64_t n_expert, int64_t in_f, int64_t n_ff, int qt, int64_t rb,
+                   const GemvTuning& tune, hipStream_t st);
+int64_t moe_q8_lds_bytes(int64_t in_f);
+
+// Q8_1 quantization of nblk blocks of 32 activations.
+void launch_quantize_q8_1(int8_t* q, float* d, const float* x, int64_t nblk, hipStream_t st);
+
 void launch_loadonly(uint32_t* sink, const void* w, int64_t m, int64_t k, int qt, int64_t rb,
                      const GemvTuning& tune, hipStream_t st);
 

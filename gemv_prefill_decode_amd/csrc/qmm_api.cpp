@@ -418,6 +418,47 @@ int qmm_moe_down(float* y, float* pair_out, const void* w_down, const int32_t* e
     return launch_status();
 }
 
+int qmm_quantize_q8_1(int8_t* q, float* d, const float* x, int64_t rows, int64_t k, hipStream_t stream) {
+    if (!q || !d || !x) return QMM_ERR_NULL;
+    if (rows < 1 || k < 1) return QMM_ERR_SHAPE;
+    if (k % 32 != 0) return QMM_ERR_K_ALIGN;
+    if (!aligned(q, 16) || !aligned(x, 16) || !aligned(d, 4)) return QMM_ERR_ALIGN;
+    int64_t elems;
+    if (!mul_ok(rows, k, &elems)) return QMM_ERR_SHAPE;
+    qmm::launch_quantize_q8_1(q, d, x, elems / 32, stream);
+    return launch_status();
+}
+
+int qmm_moe_gateup_q8(float* gate_out, float* up_out, const void* w_gate, const void* w_up,
+                      const int32_t* expert_ids, const float* pair_scale, const int8_t* xq,
+                      const float* xd, int64_t t, int64_t n_used, int64_t n_expert, int64_t in_f,
+                      int64_t n_ff, int qtype, hipStream_t stream) {
+    if (!gate_out || !up_out || !w_gate || !w_up || !expert_ids || !pair_scale || !xq || !xd)
+        return QMM_ERR_NULL;
+    if (t < 1 || n_used < 1 || n_expert < 1 || n_used > n_expert) return QMM_ERR_SHAPE;
+    if (qtype != QMM_NVFP4 && qtype != QMM_NVFP4_V2) return QMM_ERR_QTYPE;
+    int64_t rb;
+    int64_t rows;
+    if (!mul_ok(n_expert, n_ff, &rows)) return QMM_ERR_SHAPE;
+    int st = check_weights(w_gate, rows, in_f, qtype, &rb);
+    if (st) return st;
+    st = check_weights(w_up, rows, in_f, qtype, &rb);
+    if (st) return st;
+    if (!aligned(xq, 16) || !aligned(xd, 4) || !aligned(gate_out, 4) || !aligned(up_out, 4) ||
+        !aligned(pair_scale, 4) || !aligned(expert_ids, 4))
+        return QMM_ERR_ALIGN;
+    int64_t n_pairs;
+    if (!mul_ok(t, n_used, &n_pairs)) return QMM_ERR_SHAPE;
+    if (n_pairs > 65535 || n_ff > INT_MAX || t * in_f >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+    if (qmm::gemv_max_window_bytes(qtype, in_f, rb) >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+    if (qmm::moe_q8_lds_bytes(in_f) > 64 * 1024) return QMM_ERR_RANGE;
+    qmm::GemvTuning tune;
+    if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
+    qmm::launch_moe_q8(gate_out, up_out, w_gate, w_up, expert_ids, pair_scale, xq, xd, t, n_used,
+                       n_expert, in_f, n_ff, qtype, rb, tune, stream);
+    return launch_status();
+}
+
 int qmm_nvfp4_repack_v2(void* dst, const void* src, int64_t rows, int64_t k, hipStream_t stream) {
     if (!dst || !src) return QMM_ERR_NULL;
     if (rows < 1 || k < 1) return QMM_ERR_SHAPE;

@@ -216,6 +216,38 @@ int qmm_moe_down(float* y, float* pair_out, const void* w_down, const int32_t* e
                  int64_t n_expert, int64_t n_ff, int64_t d_model, int qtype, hipStream_t stream);
 
 /*
+ * qmm_quantize_q8_1: Q8_1 activations (memra-engine moe_rows_ceiling_bench.rs
+ * quantizes the activations with quantize_q8_1 before its served gate/up
+ * kernel; the format is ggml's, not printed on the pages).  Per block of 32
+ * consecutive activations of a row, in f32: d = max|x| / 127, then
+ * q = round-half-away-from-zero(x * (1/d)), or q = 0 when d = 0.
+ *   q     DEVICE int8[rows*k], written, 16-byte aligned.
+ *   d     DEVICE float[rows*k/32], written (one scale per block).
+ *   x     DEVICE float[rows*k], 16-byte aligned.
+ *   k     a multiple of 32 (QMM_ERR_K_ALIGN).
+ */
+int qmm_quantize_q8_1(int8_t* q, float* d, const float* x, int64_t rows, int64_t k, hipStream_t stream);
+
+/*
+ * qmm_moe_gateup_q8: qmm_moe_gateup on Q8_1 activations (the served
+ * arithmetic of memra-engine moe_rows_ceiling_bench.rs: quantized activations
+ * and integer dot products).  With x_hat[tau*in_f + c] = xd[tau*in_f/32 + c/32]
+ * * xq[tau*in_f + c], the outputs are those of qmm_moe_gateup on x_hat.  Each
+ * 16-weight group's dot product (E2M1 weights times int8 codes) is exact;
+ * its E4M3 scale, the block scale and the sum over groups are applied in f32,
+ * so results are within 1e-5*|scale|*sum|w*x_hat|.
+ *   xq, xd      DEVICE, as written by qmm_quantize_q8_1 for t rows of in_f;
+ *               xq 16-byte aligned.
+ *   qtype       QMM_NVFP4 or QMM_NVFP4_V2 (else QMM_ERR_QTYPE).
+ *   in_f        a multiple of 64, at most 8320 (LDS: QMM_ERR_RANGE above).
+ * Other arguments and errors as qmm_moe_gateup.
+ */
+int qmm_moe_gateup_q8(float* gate_out, float* up_out, const void* w_gate, const void* w_up,
+                      const int32_t* expert_ids, const float* pair_scale, const int8_t* xq,
+                      const float* xd, int64_t t, int64_t n_used, int64_t n_expert, int64_t in_f,
+                      int64_t n_ff, int qtype, hipStream_t stream);
+
+/*
  * qmm_nvfp4_repack_v2: NVFP4 rows -> the same values as NVFP4_V2 rows (memra
  * moe_rows_ceiling_bench.rs repacks the expert rows once before its V2 arms).
  * Per row and 36-byte group G: the 32 quant bytes (group bytes 4..35) go to

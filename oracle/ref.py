@@ -99,9 +99,10 @@ def moe_ref(name: str, w_gate, w_up, ids, scales, x, n_expert: int, in_f: int, n
 
 
 def moe_ref_pairs_rows(name: str, w_plane, ids, scales, x, plane: int, n_expert: int, in_f: int,
-                       n_ff: int, pairs, rows):
+                       n_ff: int, pairs, rows, exact_x: bool = False):
     """(ref, S) of out_P[pairs[t], rows[t]] for one plane P, sampled: only the
-    sampled weight rows of the chosen experts are decoded."""
+    sampled weight rows of the chosen experts are decoded.  x is float32
+    (exact_x: float64 values used as they are)."""
     ids = np.asarray(ids, dtype=np.int64)
     t, n_used = ids.shape
     n_pairs = t * n_used
@@ -109,7 +110,8 @@ def moe_ref_pairs_rows(name: str, w_plane, ids, scales, x, plane: int, n_expert:
     rows = np.asarray(rows, dtype=np.int64)
     buf = np.asarray(w_plane).reshape(-1).view(np.uint8)
     rb = buf.size // (n_expert * n_ff)
-    X = np.asarray(x, dtype=np.float32).reshape(t, in_f).astype(np.float64)
+    X = (np.asarray(x, dtype=np.float64) if exact_x else
+         np.asarray(x, dtype=np.float32).astype(np.float64)).reshape(t, in_f)
     sc = np.asarray(scales, dtype=np.float32).astype(np.float64)
     val = np.empty(len(pairs))
     tol = np.empty(len(pairs))

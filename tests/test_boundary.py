@@ -104,6 +104,17 @@ def test_validation_rejects_before_launch():
     assert d(A, A, A, A, A, A, 1, 8, 64, 2000, 4096, 5, s0) == 3     # n_ff % 64
     assert d(A, A, A, A, A, A, 1, 8, 64, 2048, 4096, 8, s0) == 4     # qtype
     assert d(A, A, A, A, A, A, 70000, 1, 64, 64, 4096, 5, s0) == 8   # more pairs than the grid
+    qz = lib.qmm_quantize_q8_1
+    assert qz(A, z, A, 4, 256, s0) == 1                               # null d
+    assert qz(A, A, A, 0, 256, s0) == 2                               # rows < 1
+    assert qz(A, A, A, 4, 48, s0) == 3                                # k % 32
+    assert qz(B, A, A, 4, 256, s0) == 5                               # misaligned q
+    mq = lib.qmm_moe_gateup_q8
+    assert mq(A, A, A, A, A, A, z, A, 1, 8, 64, 4096, 2048, 5, s0) == 1   # null xq
+    assert mq(A, A, A, A, A, A, A, A, 1, 8, 64, 4096, 2048, 3, s0) == 4   # Q4_K weights
+    assert mq(A, A, A, A, A, A, A, A, 1, 9, 8, 4096, 2048, 5, s0) == 2    # n_used > n_expert
+    assert mq(A, A, A, A, A, A, A, A, 1, 8, 64, 4000, 2048, 5, s0) == 3   # in_f % 64
+    assert mq(A, A, A, A, A, A, A, A, 1, 8, 64, 8448, 2048, 5, s0) == 8   # rows exceed LDS
     r = lib.qmm_nvfp4_repack_v2
     assert r(z, A, 4, 128, s0) == 1                                  # null dst
     assert r(A, A, 0, 128, s0) == 2                                  # rows < 1

@@ -7,6 +7,7 @@ by one (always including the four corners), on the same seeded inputs.
   - decode sweep n in {1,4,8,16,32}: q4_k/q6_k at 4608x1024 and 14336x4096
   - NVFP4 MoE gate/up: 64 experts, 8 used, in_f 4096, n_ff 2048, t in {1,16}
   - NVFP4 MoE down: 64 experts of 4096 rows over 2048 inputs, t in {1,16}
+  - NVFP4 MoE gate/up on Q8_1 activations at the gate/up shape, t in {1,16}
   - 8B-class prefill n=2048: q4_k/q6_k at 14336x4096 and 4096x14336
 """
 
@@ -89,6 +90,39 @@ def test_moe_gateup_full_size(t):
                                       pairs, rows)
         ok, worst = ref.tolerance_check(outs[plane][pairs, rows], r, S, TAU_F32)
         assert ok, f"moe t={t} plane {plane}: worst {worst:.3g}"
+
+
+@pytest.mark.parametrize("t", [1, 16])
+def test_moe_gateup_q8_full_size(t):
+    """Gate/up on Q8_1 activations at the full shape, sampled against the
+    oracle on the dequantized activations."""
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    n_expert, in_f, n_ff, n_used = 64, 4096, 2048, 8
+    note(f"moe q8 full size t={t}")
+    planes = [np.concatenate([gen.nvfp4_rows(n_ff, in_f, gen.SEED_MOE_W + 2 * e + p)
+                              for e in range(n_expert)]) for p in range(2)]
+    ids = gen.expert_ids(t, n_used, n_expert, gen.SEED_EXPERTS)
+    n_pairs = t * n_used
+    sc = gen.pair_scales(2 * n_pairs)
+    x = gen.xorshift_f32(t * in_f, gen.SEED_MOE_X).reshape(t, in_f)
+    xq, xd = qmm.quantize_q8_1(to_dev(x))
+    g, u = qmm.moe_gateup_q8(to_dev(planes[0]), to_dev(planes[1]), to_dev(ids), to_dev(sc), xq, xd,
+                             n_expert, n_ff, "nvfp4")
+    torch.cuda.synchronize()
+    outs = [g.cpu().numpy(), u.cpu().numpy()]
+    rq, rd = ref.quantize_q8_1(x, in_f)
+    assert np.array_equal(xq.cpu().numpy(), rq)
+    xh = ref.dequantize_q8_1(rq, rd, in_f)
+    rng = np.random.default_rng(200 + t)
+    pairs = np.concatenate([rng.integers(0, n_pairs, 400), [0, n_pairs - 1]])
+    rows = np.concatenate([rng.integers(0, n_ff, 400), [0, n_ff - 1]])
+    for plane in (0, 1):
+        assert np.all(np.isfinite(outs[plane]))
+        r, S = ref.moe_ref_pairs_rows("nvfp4", planes[plane], ids, sc, xh, plane, n_expert, in_f, n_ff,
+                                      pairs, rows, exact_x=True)
+        ok, worst = ref.tolerance_check(outs[plane][pairs, rows], r, S, TAU_F32)
+        assert ok, f"moe q8 t={t} plane {plane}: worst {worst:.3g}"
 
 
 @pytest.mark.parametrize("t", [1, 16])

@@ -461,3 +461,72 @@ def test_moe_nvfp4_v2_bit_identical_to_v1(t, n_used):
                           to_dev(act), n_expert, d_model, "nvfp4_v2")
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(p1, p2)
+
+
+# ------------------------------------------------------------------ Q8_1 activations
+
+def test_quantize_q8_1_bit_exact():
+    """Device quantization equals the oracle's float32 steps bit for bit:
+    random magnitudes, zero blocks, halves that round away from zero."""
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    rng = np.random.default_rng(11)
+    rows, k = 7, 1024
+    x = (rng.standard_normal(rows * k) * rng.choice([1e-4, 1.0, 300.0], rows * k)).astype(np.float32)
+    x[:32] = 0.0                                   # a zero block
+    x[32:64] = 0.0
+    x[32:38] = [127.0, 2.5, -2.5, 0.5, -0.5, 3.5]  # d = 1: halves
+    x = x.reshape(rows, k)
+    note("quantize q8_1")
+    q, d = qmm.quantize_q8_1(to_dev(x))
+    torch.cuda.synchronize()
+    rq, rd = ref.quantize_q8_1(x, k)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(d.cpu().numpy().view(np.uint32), rd.reshape(rows, k // 32).view(np.uint32))
+
+
+@pytest.mark.parametrize("t,n_used", [(1, 8), (3, 2), (16, 3)])
+def test_moe_q8_parity_and_v2_identity(t, n_used):
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    n_expert, in_f, n_ff = 9, 512, 96
+    note(f"moe q8 t={t} n_used={n_used}")
+    wg, wu, ids, sc, x = _moe_inputs(n_expert, in_f, n_ff, t, n_used, seed=t + 40)
+    dg, du, di, ds = to_dev(wg), to_dev(wu), to_dev(ids.astype(np.int32)), to_dev(sc)
+    xq, xd = qmm.quantize_q8_1(to_dev(x))
+    g, u = qmm.moe_gateup_q8(dg, du, di, ds, xq, xd, n_expert, n_ff, "nvfp4")
+    rows = n_expert * n_ff
+    g2, u2 = qmm.moe_gateup_q8(qmm.repack_nvfp4_v2(dg, rows, in_f), qmm.repack_nvfp4_v2(du, rows, in_f),
+                               di, ds, xq, xd, n_expert, n_ff, "nvfp4_v2")
+    torch.cuda.synchronize()
+    assert torch.equal(g, g2) and torch.equal(u, u2)
+    rq, rd = ref.quantize_q8_1(x, in_f)
+    assert np.array_equal(xq.cpu().numpy(), rq)
+    rg, ru, Sg, Su = ref.moe_q8_ref("nvfp4", wg, wu, ids, sc, rq, rd, n_expert, in_f, n_ff)
+    for got, r, S in ((g, rg, Sg), (u, ru, Su)):
+        ok, worst = ref.tolerance_check(got.cpu().numpy(), r, S, TAU_F32)
+        assert ok, worst
+
+
+def test_moe_q8_exact_activations_match_f32_path():
+    """Activations that Q8_1 represents exactly (x = d0 * code, d0 a power of
+    two, one code +-127 per block): the Q8_1 path and the f32 path compute
+    the same exact products; both pass the same oracle."""
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    n_expert, in_f, n_ff, t, n_used = 5, 256, 40, 2, 2
+    note("moe q8 exact activations")
+    wg, wu, ids, sc, _ = _moe_inputs(n_expert, in_f, n_ff, t, n_used, seed=3)
+    rng = np.random.default_rng(5)
+    codes = rng.integers(-126, 127, (t, in_f))
+    codes[:, ::32] = 127
+    x = (codes * 2.0 ** -7).astype(np.float32)
+    xq, xd = qmm.quantize_q8_1(to_dev(x))
+    dg, du, di, ds = to_dev(wg), to_dev(wu), to_dev(ids.astype(np.int32)), to_dev(sc)
+    g, u = qmm.moe_gateup_q8(dg, du, di, ds, xq, xd, n_expert, n_ff)
+    torch.cuda.synchronize()
+    assert np.array_equal(xq.cpu().numpy(), codes.astype(np.int8))
+    assert np.all(xd.cpu().numpy() == np.float32(2.0 ** -7))
+    rg, ru, Sg, Su = ref.moe_ref("nvfp4", wg, wu, ids, sc, x, n_expert, in_f, n_ff)
+    assert ref.tolerance_check(g.cpu().numpy(), rg, Sg, TAU_F32)[0]
+    assert ref.tolerance_check(u.cpu().numpy(), ru, Su, TAU_F32)[0]
