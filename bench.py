@@ -20,7 +20,8 @@ The same JSON line also carries the other half of the metric:
            and the down projection after it (4096 rows over 2048 inputs per
            expert, per-pair activations, slots summed per token); each also
            on the same values in NVFP4 V2 rows (outputs checked bit-identical
-           to V1 before timing).
+           to V1 before timing); the gate/up also on Q8_1 activations
+           (quantization included in the timed launches).
   roofline the dominant prefill kernel instance: algorithmic flops per launch
            over its average launch time from the events of the timed region.
   cpu_baseline  the CPU oracle over the whole prefill step on the host cores.
@@ -326,15 +327,26 @@ def run_moe(args):
                      for i in range(L)])
         tv2 = time_graph(g, L, 5)
         del g
+        # Q8_1 activations: the quantization once per call, then the gate/up
+        xq, xd = qmm.quantize_q8_1(x)
+        g = capture([(lambda c=sets[i % copies], d=draws[i % 8]:
+                      (qmm.quantize_q8_1(x, q=xq, d=xd),
+                       qmm.moe_gateup_q8(c[0], c[1], d, sc, xq, xd, n_expert, n_ff, gate_out=go,
+                                         up_out=uo)))
+                     for i in range(L)])
+        tq8 = time_graph(g, L, 5)
+        del g
         res[f"t{t}"] = {"us": round(tt * 1e6, 2),
                         "GB/s": round(byts / tt / 1e9, 1),
                         "frac_hbm_peak": round(byts / tt / 1e9 / PEAK_HBM_GBS, 4),
                         "unique_experts_mean": round(statistics.mean(uniq), 2),
                         "algorithmic_bytes_mean": round(byts),
                         "v2": {"us": round(tv2 * 1e6, 2), "GB/s": round(byts / tv2 / 1e9, 1),
-                               "bit_identical_to_v1": True}}
+                               "bit_identical_to_v1": True},
+                        "q8_1": {"us": round(tq8 * 1e6, 2), "GB/s": round(byts / tq8 / 1e9, 1),
+                                 "includes": "quantize_q8_1 + gate/up"}}
         log(f"moe t={t}: {res[f't{t}']['us']} us {res[f't{t}']['GB/s']} GB/s; "
-            f"V2 {res[f't{t}']['v2']['us']} us")
+            f"V2 {res[f't{t}']['v2']['us']} us; Q8_1 {res[f't{t}']['q8_1']['us']} us")
     return res
 
 
@@ -414,6 +426,38 @@ def run_moe_down(args):
 
 COPY_PROBE_BYTES = 1 << 30
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def run_crossover():
+    """GEMV against the matrix-core path over n (the measurement behind the
+    AUTO dispatch): both paths graph-replayed over weight copies rotated
+    through >= 1 GiB; prints one JSON object {shape: {n: [gemv_us, mfma_us]}}."""
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    from synth import gen
+    res = {}
+    for qt, m, k in (("q4_k", 4608, 1024), ("q6_k", 4608, 1024), ("q4_k", 14336, 4096),
+                     ("q4_0", 1024, 4608), ("f32", 3072, 1024)):
+        wbytes = m * qmm.row_bytes(qt, k)
+        copies = max(4, -(-(1 << 30) // wbytes))
+        ws = rotated_copies(to_dev(gen_weights(qt, m, k, 5)), copies)
+        L = max(copies, 32)
+        ent = {}
+        for n in (4, 8, 12, 16, 24, 32, 48, 64):
+            x = to_dev(gen.unit_f32(n * k, gen.SEED_X).reshape(n, k))
+            out = torch.empty((n, m), dtype=torch.float32, device="cuda")
+            t = []
+            for path in ("gemv", "mfma"):
+                g = capture([(lambda w=ws[i % copies], p=path: qmm.gemm(w, x, m, qt, out=out, path=p))
+                             for i in range(L)])
+                t.append(round(time_graph(g, L, 5) * 1e6, 2))
+                del g
+            ent[n] = t
+        res[f"{qt} {m}x{k}"] = ent
+        log(f"crossover {qt} {m}x{k}: {ent}")
+        del ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"crossover_us_gemv_mfma": res}))
 
 
 def copy_probe():
@@ -521,6 +565,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode and MoE measurements")
     ap.add_argument("--quick", action="store_true", help="fewer rotation copies")
+    ap.add_argument("--crossover", action="store_true",
+                    help="only measure GEMV vs matrix-core time over n (prints its own JSON)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run the 1 GiB copy that calibrates the HBM byte counters")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -542,6 +588,9 @@ def main():
         sys.exit(2)
     import gemv_prefill_decode_amd as qmm
     qmm.load()
+    if args.crossover:
+        run_crossover()
+        return
     if args.copy_probe:
         log("copy probe: 3 x 1 GiB device copies")
         copy_probe()
