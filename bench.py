@@ -440,7 +440,8 @@ def run_crossover():
                      ("q4_0", 1024, 4608), ("f32", 3072, 1024)):
         wbytes = m * qmm.row_bytes(qt, k)
         copies = max(4, -(-(1 << 30) // wbytes))
-        ws = rotated_copies(to_dev(gen_weights(qt, m, k, 5)), copies)
+        base = to_dev(gen_weights(qt, m, k, 5))
+        ws = rotated_copies(base if base.dtype == torch.uint8 else base.view(torch.uint8), copies)
         L = max(copies, 32)
         ent = {}
         for n in (4, 8, 12, 16, 24, 32, 48, 64):
