@@ -62,6 +62,8 @@ def load() -> ctypes.CDLL:
         lib.qmm_gemm_path.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, vp]
         lib.qmm_gemm_path.restype = i32
         lib.qmm_gemm_ws.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, vp, i64, vp]
+        lib.qmm_gemm_ex.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, i32, i32, vp, i64, vp]
+        lib.qmm_gemm_ex.restype = i32
         lib.qmm_gemm_ws.restype = i32
         lib.qmm_gemm_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
         lib.qmm_gemm_workspace_bytes.restype = i64
@@ -197,7 +199,9 @@ def gemm(w, x, m: int, qtype, out=None, path: str = "auto", stream=None, workspa
     """dst[n, m] with dst[j, i] = sum_c deq(w)[i, c] * x[j, c].
 
     w: packed weights (uint8, m*row_bytes(qtype, k) bytes; float32 [m, k] for
-    "f32"); x: float32 [n, k]; out: optional float32 [n, m].
+    "f32"); x: float32 [n, k]; out: optional float32 [n, m].  x and out may
+    be row-strided views (unit stride along a row, rows any stride apart:
+    qmm_gemm_ex); otherwise they must be contiguous.
     workspace: "auto" (a buffer kept per device and stream), None (no k split
     on the matrix-core path), or a device tensor of at least
     workspace_bytes() bytes."""
@@ -225,11 +229,27 @@ def gemm(w, x, m: int, qtype, out=None, path: str = "auto", stream=None, workspa
                 workspace = _auto_workspace(x.device, sh.value or 0, nbytes)
             ws_ptr = _dev(workspace, "workspace")
             ws_len = workspace.numel() * workspace.element_size()
-    st = lib.qmm_gemm_ws(_dev(out, "out", torch.float32), _dev(w, "w"), _dev(x, "x", torch.float32),
-                         m, k, n, qt, PATHS[path], ws_ptr, ws_len, sh)
+    st = lib.qmm_gemm_ex(*_rows(out, "out"), _dev(w, "w"), *_rows(x, "x"), m, k, n, qt, PATHS[path],
+                         ws_ptr, ws_len, sh)
     if st != 0:
-        raise QmmError(st, "qmm_gemm_ws")
+        raise QmmError(st, "qmm_gemm_ex")
     return out
+
+
+def _rows(t, what):
+    """(pointer, row stride in elements) of a float32 [rows, cols] device
+    tensor with unit stride along its rows."""
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a device (cuda/hip) tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{what} must be torch.float32, got {t.dtype}")
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{what} must be 2-D with unit stride along its rows")
+    ld = t.stride(0) if t.shape[0] > 1 else t.shape[1]
+    if ld < t.shape[1]:
+        raise ValueError(f"{what} rows overlap (row stride {ld} < {t.shape[1]})")
+    return ctypes.c_void_p(t.data_ptr()), ld
 
 
 def moe_gateup(w_gate, w_up, expert_ids, pair_scale, x, n_expert: int, n_ff: int,

@@ -72,7 +72,8 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_mfma_kernel(float* __restric
                                                                 const float* __restrict__ x, int m,
                                                                 int k, int n, int rb, int n_mb,
                                                                 int n_nb, int n_split, int sps,
-                                                                float* __restrict__ partial) {
+                                                                float* __restrict__ partial, int ldx,
+                                                                int ldd) {
     constexpr int TILE_H = BM * LDK;  // halves per A or B tile (BM == BN)
     __shared__ __attribute__((aligned(16))) _Float16 lds[KG][2][2][TILE_H];  // [group][buffer][A, B]
     const int tid = threadIdx.x, lane = tid & 63;
@@ -95,7 +96,8 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_mfma_kernel(float* __restric
     int64_t base;
     const rsrc_t wr = row_window(w, m0, BM, m, rb, base);
     const int ntok = (int)imin64(BN, n - n0);
-    const rsrc_t xr = make_rsrc(x + n0 * k, (uint32_t)ntok * (uint32_t)k * 4u);
+    // token rows ldx floats apart; the window ends with the last row's k floats
+    const rsrc_t xr = make_rsrc(x + n0 * ldx, ((uint32_t)(ntok - 1) * (uint32_t)ldx + (uint32_t)k) * 4u);
     const int arow = lt >> 1, part = lt & 1;
     const uint32_t roff = (uint32_t)((m0 + arow) * rb - base);
     const int nk_all = (k + BK - 1) / BK;
@@ -125,9 +127,9 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_mfma_kernel(float* __restric
     // loads of step kt+2 stay in flight while step kt computes.
     const int g0 = s0 + g;  // this group's first step; it takes every KG-th
     al0.load(wr, roff, g0, part, kend, nk);
-    xl0.template load<H>(xr, k, kend, g0, lt);
+    xl0.template load<H>(xr, ldx, kend, g0, lt);
     al1.load(wr, roff, g0 + KG, part, kend, nk);
-    xl1.template load<H>(xr, k, kend, g0 + KG, lt);
+    xl1.template load<H>(xr, ldx, kend, g0 + KG, lt);
     stage(al0, xl0, 0);
     __syncthreads();
 
@@ -168,14 +170,14 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_mfma_kernel(float* __restric
         const int kt = g0 + KG * i;
         // step kt: buffer 0; set 1 holds step kt+KG, set 0 takes kt+2KG
         al0.load(wr, roff, kt + 2 * KG, part, kend, nk);
-        xl0.template load<H>(xr, k, kend, kt + 2 * KG, lt);
+        xl0.template load<H>(xr, ldx, kend, kt + 2 * KG, lt);
         mfma_step(0);
         stage(al1, xl1, 1);
         interleave_hint();
         __syncthreads();
         // step kt+KG: buffer 1; set 0 holds step kt+2KG, set 1 takes kt+3KG
         al1.load(wr, roff, kt + 3 * KG, part, kend, nk);
-        xl1.template load<H>(xr, k, kend, kt + 3 * KG, lt);
+        xl1.template load<H>(xr, ldx, kend, kt + 3 * KG, lt);
         mfma_step(1);
         stage(al0, xl0, 0);
         interleave_hint();
@@ -208,6 +210,7 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_mfma_kernel(float* __restric
     // D[row][col] of a 16x16 tile sits in lane (row/4)*16 + col, element row%4:
     // rows are weight rows (contiguous in dst), cols are tokens.
     float* out = n_split > 1 ? partial + (int64_t)z * splitk_stride(n, m) : dst;
+    const int64_t ldo = n_split > 1 ? m : ldd;  // partials are dense
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -215,9 +218,9 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_mfma_kernel(float* __restric
             const int64_t mrow = m0 + wm * 64 + i * 16 + (lane >> 4) * 4;
             const int64_t tok = n0 + wn * 64 + j * 16 + (lane & 15);
             if (tok < n) {
-                float* p = out + tok * m + mrow;
+                float* p = out + tok * ldo + mrow;
                 const f32x4 v = acc[i][j];
-                if ((m & 3) == 0 && mrow + 4 <= m) {
+                if ((ldo & 3) == 0 && mrow + 4 <= m) {
                     *(f32x4*)p = v;
                 } else {
 #pragma unroll
@@ -233,7 +236,17 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_mfma_kernel(float* __restric
 // order, for i < count; part[z] starts at z * splitk_stride (16-byte aligned).
 __global__ __launch_bounds__(256) void splitk_sum_kernel(float* __restrict__ dst,
                                                          const float* __restrict__ part,
-                                                         int64_t count, int64_t zstride, int n_split) {
+                                                         int64_t count, int64_t zstride, int n_split,
+                                                         int64_t m, int64_t ldd) {
+    if (ldd != m) {  // dst rows ldd apart: element i is row i / m, column i % m
+        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
+            float v = part[i];
+            for (int z = 1; z < n_split; ++z) v += part[z * zstride + i];
+            const int64_t row = i / m;
+            dst[row * ldd + (i - row * m)] = v;
+        }
+        return;
+    }
     const int64_t n4 = count >> 2;
     const int64_t stride = (int64_t)gridDim.x * 256;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
@@ -249,30 +262,31 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(float* __restrict__ dst
 }
 
 void launch_splitk_sum(float* dst, const float* part, int64_t count, int64_t zstride, int n_split,
-                       hipStream_t st) {
-    int64_t blocks = (count / 4 + 255) / 256;
+                       int64_t m, int64_t ldd, hipStream_t st) {
+    int64_t blocks = ((ldd == m ? count / 4 : count) + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     if (blocks < 1) blocks = 1;
-    splitk_sum_kernel<<<dim3((unsigned)blocks), 256, 0, st>>>(dst, part, count, zstride, n_split);
+    splitk_sum_kernel<<<dim3((unsigned)blocks), 256, 0, st>>>(dst, part, count, zstride, n_split, m, ldd);
 }
 
 template <int QT>
 static void launch_qt(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k, int64_t n,
-                      int64_t rb, const MfmaPlan& pl, void* ws, hipStream_t st) {
+                      int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd, hipStream_t st) {
     const int n_mb = (int)((m + BM - 1) / BM), n_nb = (int)((n + BN - 1) / BN);
     float* part = (float*)ws;
     const dim3 grid((unsigned)(n_mb * n_nb * pl.n_split));
     if constexpr (QT != QT_F32) {
         if (pl.kg == 2) {
             gemm_mfma_kernel<QT, 2><<<grid, 512, 0, st>>>(dst, w, x, (int)m, (int)k, (int)n, (int)rb, n_mb,
-                                                          n_nb, pl.n_split, pl.sps, part);
-            if (pl.n_split > 1) launch_splitk_sum(dst, part, n * m, splitk_stride(n, m), pl.n_split, st);
+                                                          n_nb, pl.n_split, pl.sps, part, (int)ldx, (int)ldd);
+            if (pl.n_split > 1)
+                launch_splitk_sum(dst, part, n * m, splitk_stride(n, m), pl.n_split, m, ldd, st);
             return;
         }
     }
     gemm_mfma_kernel<QT, 1><<<grid, 256, 0, st>>>(dst, w, x, (int)m, (int)k, (int)n, (int)rb, n_mb, n_nb,
-                                                  pl.n_split, pl.sps, part);
-    if (pl.n_split > 1) launch_splitk_sum(dst, part, n * m, splitk_stride(n, m), pl.n_split, st);
+                                                  pl.n_split, pl.sps, part, (int)ldx, (int)ldd);
+    if (pl.n_split > 1) launch_splitk_sum(dst, part, n * m, splitk_stride(n, m), pl.n_split, m, ldd, st);
 }
 
 // Cost model of the prefill plans, fitted to MI355X measurements of the
@@ -355,19 +369,20 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
 }
 
 void launch_gemm_mfma(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
-                      int qt, int64_t rb, const MfmaPlan& pl, void* ws, hipStream_t st) {
+                      int qt, int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd,
+                      hipStream_t st) {
     if (pl.x16) {
-        launch_gemm_mfma_x16(dst, w, x, m, k, n, qt, rb, pl, ws, st);
+        launch_gemm_mfma_x16(dst, w, x, m, k, n, qt, rb, pl, ws, ldx, ldd, st);
         return;
     }
     const uint8_t* wb = (const uint8_t*)w;
     switch (qt) {
-        case QT_F32: launch_qt<QT_F32>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
-        case QT_Q4_0: launch_qt<QT_Q4_0>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
-        case QT_Q8_0: launch_qt<QT_Q8_0>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
-        case QT_Q4_K: launch_qt<QT_Q4_K>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
-        case QT_Q6_K: launch_qt<QT_Q6_K>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
-        case QT_NVFP4: launch_qt<QT_NVFP4>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
+        case QT_F32: launch_qt<QT_F32>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
+        case QT_Q4_0: launch_qt<QT_Q4_0>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
+        case QT_Q8_0: launch_qt<QT_Q8_0>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
+        case QT_Q4_K: launch_qt<QT_Q4_K>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
+        case QT_Q6_K: launch_qt<QT_Q6_K>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
+        case QT_NVFP4: launch_qt<QT_NVFP4>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
     }
 }
 

@@ -27,7 +27,7 @@ namespace qmm {
 template <int H>
 __global__ __launch_bounds__(256) void x16_perm_kernel(uint16_t* __restrict__ x16,
                                                        const float* __restrict__ x, int n, int k,
-                                                       int kp) {
+                                                       int kp, int ldx) {
     const int units = kp >> 3;  // 8-slot units per row
     const int64_t total = (int64_t)n * units;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void x16_perm_kernel(uint16_t* __restrict__ x1
         const int j = (int)(i / units), su = (int)(i - (int64_t)j * units);
         const int g = su / (H / 4), sp = su % (H / 4);  // U = su: 8 units per 64-slot step
         const int e = g * 2 * H + 4 * sp;
-        const float* xr = x + (int64_t)j * k;
+        const float* xr = x + (int64_t)j * ldx;
         const f32x4 a = e < k ? *(const f32x4*)(xr + e) : f32x4{0.f, 0.f, 0.f, 0.f};
         const f32x4 b = e + H < k ? *(const f32x4*)(xr + e + H) : f32x4{0.f, 0.f, 0.f, 0.f};
         *(u32x4*)(x16 + (int64_t)j * kp + 8 * (int64_t)su) =
@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256) void x16_perm_kernel(uint16_t* __restrict__ x1
 template <int QT, int WM>
 __global__ __launch_bounds__(128 * WM, 1) void gemm_mfma_x16_kernel(
     float* __restrict__ dst, const uint8_t* __restrict__ w, const uint16_t* __restrict__ x16, int m,
-    int k, int n, int rb, int kp, int n_mb, int n_nb, int n_split, int sps, float* __restrict__ partial) {
+    int k, int n, int rb, int kp, int n_mb, int n_nb, int n_split, int sps, float* __restrict__ partial,
+    int ldd) {
     constexpr int BMX = 64 * WM, BNX = 128, NT = 128 * WM;
     constexpr int NBC = 1024 / NT;  // 16-byte activation chunks per thread per step
     __shared__ __attribute__((aligned(16))) _Float16 sA[2][BMX * LDK];
@@ -155,6 +156,7 @@ __global__ __launch_bounds__(128 * WM, 1) void gemm_mfma_x16_kernel(
     }
 
     float* out = n_split > 1 ? partial + (int64_t)z * splitk_stride(n, m) : dst;
+    const int64_t ldo = n_split > 1 ? m : ldd;  // partials are dense
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -162,9 +164,9 @@ __global__ __launch_bounds__(128 * WM, 1) void gemm_mfma_x16_kernel(
             const int64_t mrow = m0 + wm * 64 + i * 16 + (lane >> 4) * 4;
             const int64_t tok = n0 + wn * 64 + j * 16 + (lane & 15);
             if (tok < n) {
-                float* p = out + tok * m + mrow;
+                float* p = out + tok * ldo + mrow;
                 const f32x4 v = acc[i][j];
-                if ((m & 3) == 0 && mrow + 4 <= m) {
+                if ((ldo & 3) == 0 && mrow + 4 <= m) {
                     *(f32x4*)p = v;
                 } else {
 #pragma unroll
@@ -178,7 +180,8 @@ __global__ __launch_bounds__(128 * WM, 1) void gemm_mfma_x16_kernel(
 
 template <int QT>
 static void launch_x16_qt(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k,
-                          int64_t n, int64_t rb, const MfmaPlan& pl, void* ws, hipStream_t st) {
+                          int64_t n, int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd,
+                          hipStream_t st) {
     constexpr int H = Perm<QT>::H;
     const int64_t kp = x16_row_halves(k);
     uint16_t* x16 = (uint16_t*)ws;
@@ -187,30 +190,33 @@ static void launch_x16_qt(float* dst, const uint8_t* w, const float* x, int64_t 
         const int64_t total = n * (kp / 8);
         int64_t blocks = (total + 255) / 256;
         if (blocks > 8192) blocks = 8192;
-        x16_perm_kernel<H><<<dim3((unsigned)blocks), 256, 0, st>>>(x16, x, (int)n, (int)k, (int)kp);
+        x16_perm_kernel<H><<<dim3((unsigned)blocks), 256, 0, st>>>(x16, x, (int)n, (int)k, (int)kp, (int)ldx);
     }
     const int bm = 64 * pl.wm;
     const int n_mb = (int)((m + bm - 1) / bm), n_nb = (int)((n + 127) / 128);
     const dim3 grid((unsigned)(n_mb * n_nb * pl.n_split));
     if (pl.wm == 4)
         gemm_mfma_x16_kernel<QT, 4><<<grid, 512, 0, st>>>(dst, w, x16, (int)m, (int)k, (int)n, (int)rb,
-                                                          (int)kp, n_mb, n_nb, pl.n_split, pl.sps, part);
+                                                          (int)kp, n_mb, n_nb, pl.n_split, pl.sps, part,
+                                                          (int)ldd);
     else
         gemm_mfma_x16_kernel<QT, 2><<<grid, 256, 0, st>>>(dst, w, x16, (int)m, (int)k, (int)n, (int)rb,
-                                                          (int)kp, n_mb, n_nb, pl.n_split, pl.sps, part);
-    if (pl.n_split > 1) launch_splitk_sum(dst, part, n * m, splitk_stride(n, m), pl.n_split, st);
+                                                          (int)kp, n_mb, n_nb, pl.n_split, pl.sps, part,
+                                                          (int)ldd);
+    if (pl.n_split > 1) launch_splitk_sum(dst, part, n * m, splitk_stride(n, m), pl.n_split, m, ldd, st);
 }
 
 void launch_gemm_mfma_x16(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
-                          int qt, int64_t rb, const MfmaPlan& pl, void* ws, hipStream_t st) {
+                          int qt, int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd,
+                          hipStream_t st) {
     const uint8_t* wb = (const uint8_t*)w;
     switch (qt) {
-        case QT_F32: launch_x16_qt<QT_F32>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
-        case QT_Q4_0: launch_x16_qt<QT_Q4_0>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
-        case QT_Q8_0: launch_x16_qt<QT_Q8_0>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
-        case QT_Q4_K: launch_x16_qt<QT_Q4_K>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
-        case QT_Q6_K: launch_x16_qt<QT_Q6_K>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
-        case QT_NVFP4: launch_x16_qt<QT_NVFP4>(dst, wb, x, m, k, n, rb, pl, ws, st); break;
+        case QT_F32: launch_x16_qt<QT_F32>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
+        case QT_Q4_0: launch_x16_qt<QT_Q4_0>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
+        case QT_Q8_0: launch_x16_qt<QT_Q8_0>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
+        case QT_Q4_K: launch_x16_qt<QT_Q4_K>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
+        case QT_Q6_K: launch_x16_qt<QT_Q6_K>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
+        case QT_NVFP4: launch_x16_qt<QT_NVFP4>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
     }
 }
 

@@ -941,18 +941,21 @@ template <int QT, int NT, int R, int D, bool XL, int WPG = 4>
 __global__ __launch_bounds__(64 * WPG) void gemv_kernel(float* __restrict__ dst,
                                                         const uint8_t* __restrict__ w,
                                                         const float* __restrict__ x, int m, int k,
-                                                        int n, int rb, int lpr_log2, int n_rg) {
+                                                        int n, int rb, int lpr_log2, int n_rg, int ldx,
+                                                        int ldd) {
     const int wave = wave_id();
     const int tok0 = blockIdx.y * NT;
     const int ntok = min(NT, n - tok0);
-    const rsrc_t xr = make_rsrc(x + (int64_t)tok0 * k, (uint32_t)ntok * (uint32_t)k * 4u);
+    // token rows ldx floats apart; the window ends with the last row's k floats
+    const rsrc_t xr = make_rsrc(x + (int64_t)tok0 * ldx,
+                                ((uint32_t)(ntok - 1) * (uint32_t)ldx + (uint32_t)k) * 4u);
     uint32_t xoff[NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) xoff[j] = (uint32_t)j * (uint32_t)k * 4u;
+    for (int j = 0; j < NT; ++j) xoff[j] = (uint32_t)(j < ntok ? j : 0) * (uint32_t)ldx * 4u;
     const StreamGeom g{w, m, rb, k, lpr_log2};
-    float* out = dst + (int64_t)tok0 * m;
+    float* out = dst + (int64_t)tok0 * ldd;
     auto store = [&](int64_t row, int j, float v) {
-        if (row < m && j < ntok) out[(int64_t)j * m + row] = v;
+        if (row < m && j < ntok) out[(int64_t)j * ldd + row] = v;
     };
     if constexpr (XL) {
         constexpr bool SM = GUnit<QT>::RUNS > 0;
@@ -1340,7 +1343,8 @@ static void with_rd(const GemvTuning& t, F&& f) {
 
 template <int QT, int NT>
 static void launch_gemv_nt(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k,
-                           int64_t n, int64_t rb, const GemvTuning& tune, hipStream_t st) {
+                           int64_t n, int64_t rb, int64_t ldx, int64_t ldd, const GemvTuning& tune,
+                           hipStream_t st) {
     with_rd<NT>(tune, [&](auto Rc, auto Dc) {
         constexpr int R = decltype(Rc)::value, D = decltype(Dc)::value;
         const int l = lpr_for(QT, k);
@@ -1353,30 +1357,31 @@ static void launch_gemv_nt(float* dst, const uint8_t* w, const float* x, int64_t
                 // one work group per CU: 8 waves share the staged rows
                 const dim3 grid(stream_grid(n_rg, gy, lt, 8), (unsigned)gy);
                 gemv_kernel<QT, NT, R, D, true, 8><<<grid, 512, (size_t)lds, st>>>(
-                    dst, w, x, (int)m, (int)k, (int)n, (int)rb, l, (int)n_rg);
+                    dst, w, x, (int)m, (int)k, (int)n, (int)rb, l, (int)n_rg, (int)ldx, (int)ldd);
             } else {
                 const dim3 grid(stream_grid(n_rg, gy, lt), (unsigned)gy);
                 gemv_kernel<QT, NT, R, D, true><<<grid, 256, (size_t)lds, st>>>(
-                    dst, w, x, (int)m, (int)k, (int)n, (int)rb, l, (int)n_rg);
+                    dst, w, x, (int)m, (int)k, (int)n, (int)rb, l, (int)n_rg, (int)ldx, (int)ldd);
             }
         } else {
             const dim3 grid(stream_grid(n_rg, gy, tune), (unsigned)gy);
             gemv_kernel<QT, NT, R, D, false><<<grid, 256, 0, st>>>(
-                dst, w, x, (int)m, (int)k, (int)n, (int)rb, l, (int)n_rg);
+                dst, w, x, (int)m, (int)k, (int)n, (int)rb, l, (int)n_rg, (int)ldx, (int)ldd);
         }
     });
 }
 
 template <int QT>
 static void launch_gemv_qt(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k,
-                           int64_t n, int64_t rb, const GemvTuning& tune, hipStream_t st) {
+                           int64_t n, int64_t rb, int64_t ldx, int64_t ldd, const GemvTuning& tune,
+                           hipStream_t st) {
     const bool fits8 = (int64_t)xlds_floats(8, (int)k, GUnit<QT>::RUNS > 0) * 4 <= tune.lds_per_wg;
     const bool fits4 = (int64_t)xlds_floats(4, (int)k, GUnit<QT>::RUNS > 0) * 4 <= tune.lds_per_wg;
-    if (n == 1) launch_gemv_nt<QT, 1>(dst, w, x, m, k, n, rb, tune, st);
-    else if (n == 2) launch_gemv_nt<QT, 2>(dst, w, x, m, k, n, rb, tune, st);
+    if (n == 1) launch_gemv_nt<QT, 1>(dst, w, x, m, k, n, rb, ldx, ldd, tune, st);
+    else if (n == 2) launch_gemv_nt<QT, 2>(dst, w, x, m, k, n, rb, ldx, ldd, tune, st);
     else if (n <= 4 || (!fits8 && fits4))  // groups of 4 staged rows beat 8 rows read from L2
-        launch_gemv_nt<QT, 4>(dst, w, x, m, k, n, rb, tune, st);
-    else launch_gemv_nt<QT, 8>(dst, w, x, m, k, n, rb, tune, st);
+        launch_gemv_nt<QT, 4>(dst, w, x, m, k, n, rb, ldx, ldd, tune, st);
+    else launch_gemv_nt<QT, 8>(dst, w, x, m, k, n, rb, ldx, ldd, tune, st);
 }
 
 #define QMM_QT_SWITCH(qt, CALL)                                     \
@@ -1391,9 +1396,9 @@ static void launch_gemv_qt(float* dst, const uint8_t* w, const float* x, int64_t
     }
 
 void launch_gemv(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
-                 int qt, int64_t rb, const GemvTuning& tune, hipStream_t st) {
+                 int qt, int64_t rb, int64_t ldx, int64_t ldd, const GemvTuning& tune, hipStream_t st) {
     const uint8_t* wb = (const uint8_t*)w;
-    QMM_QT_SWITCH(qt, (launch_gemv_qt<Q>(dst, wb, x, m, k, n, rb, tune, st)))
+    QMM_QT_SWITCH(qt, (launch_gemv_qt<Q>(dst, wb, x, m, k, n, rb, ldx, ldd, tune, st)))
 }
 
 template <int QT>

@@ -18,8 +18,10 @@ struct GemvTuning {
     int lds_per_cu; // bytes of LDS per CU (limits resident work groups)
 };
 
+// x rows are ldx floats apart (ldx >= k, a multiple of 4), dst rows ldd
+// floats apart (ldd >= m); ldx = k and ldd = m for contiguous tensors.
 void launch_gemv(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
-                 int qt, int64_t rb, const GemvTuning& tune, hipStream_t st);
+                 int qt, int64_t rb, int64_t ldx, int64_t ldd, const GemvTuning& tune, hipStream_t st);
 
 // Launch plan of the prefill (MFMA) kernels.  x16 = 0: gemm_mfma.hip's
 // kernel (128 x 128 tiles, f32 activations converted in the k loop).
@@ -64,13 +66,16 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
 
 // Launch with plan pl; ws (256-byte aligned, pl.ws_bytes) when pl.x16.
 void launch_gemm_mfma(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
-                      int qt, int64_t rb, const MfmaPlan& pl, void* ws, hipStream_t st);
+                      int qt, int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd,
+                      hipStream_t st);
 void launch_gemm_mfma_x16(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
-                          int qt, int64_t rb, const MfmaPlan& pl, void* ws, hipStream_t st);
+                          int qt, int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd,
+                          hipStream_t st);
 
-// dst[i] = sum over z < n_split of part[z*zstride + i], in order of z, i < count.
+// dst[(i / m)*ldd + i % m] = sum over z < n_split of part[z*zstride + i], in
+// order of z, i < count.
 void launch_splitk_sum(float* dst, const float* part, int64_t count, int64_t zstride, int n_split,
-                       hipStream_t st);
+                       int64_t m, int64_t ldd, hipStream_t st);
 
 void launch_moe(float* gate_out, float* up_out, const void* w_gate, const void* w_up,
                 const int* ids, const float* scale, const float* x, int64_t t, int64_t n_used,

@@ -208,15 +208,15 @@ int auto_path(int64_t m, int64_t k, int64_t n) {
 // Shared validation of the gemm entry points; resolves AUTO.  On success
 // *rb is the row stride and *path the concrete path.
 int check_gemm(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qtype,
-               int* path, int64_t* rb) {
+               int64_t ldx, int64_t ldd, int* path, int64_t* rb) {
     if (!dst || !x) return QMM_ERR_NULL;
     int st = check_weights(w, m, k, qtype, rb);
     if (st) return st;
-    if (n < 1) return QMM_ERR_SHAPE;
-    if (!aligned(x, 16) || !aligned(dst, 16)) return QMM_ERR_ALIGN;
-    if (n > INT_MAX) return QMM_ERR_RANGE;
+    if (n < 1 || ldx < k || ldd < m) return QMM_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(dst, 16) || ldx % 4 != 0) return QMM_ERR_ALIGN;
+    if (n > INT_MAX || ldx > INT_MAX || ldd > INT_MAX) return QMM_ERR_RANGE;
     int64_t t1, t2;
-    if (!mul_ok(n, k, &t1) || !mul_ok(n, m, &t2)) return QMM_ERR_SHAPE;
+    if (!mul_ok(n, ldx, &t1) || !mul_ok(n, ldd, &t2)) return QMM_ERR_SHAPE;
     if (*path == QMM_PATH_AUTO) {
         *path = auto_path(m, k, n);
         if (*path < 0) return QMM_ERR_RANGE;
@@ -224,13 +224,13 @@ int check_gemm(float* dst, const void* w, const float* x, int64_t m, int64_t k, 
     if (*path == QMM_PATH_GEMV) {
         // one work group addresses at most this window of w, and 8 token rows of x
         if (qmm::gemv_max_window_bytes(qtype, k, *rb) >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
-        if (8 * k * 4 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+        if ((7 * ldx + k) * 4 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
         return QMM_OK;
     }
     if (*path == QMM_PATH_MFMA) {
         if (qtype == QMM_NVFP4_V2) return QMM_ERR_QTYPE;  // streaming paths only
         if ((int64_t)qmm::MFMA_BM_MAX * *rb + 16 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
-        if ((int64_t)qmm::MFMA_BN * k * 4 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+        if (((int64_t)(qmm::MFMA_BN - 1) * ldx + k) * 4 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
         const int64_t tiles = ((m + qmm::MFMA_BM - 1) / qmm::MFMA_BM) * ((n + qmm::MFMA_BN - 1) / qmm::MFMA_BN);
         // work items (tiles x k splits, at most 16) are counted in int
         if (tiles > INT_MAX / 16) return QMM_ERR_RANGE;
@@ -239,15 +239,15 @@ int check_gemm(float* dst, const void* w, const float* x, int64_t m, int64_t k, 
     return QMM_ERR_PATH;
 }
 
-int gemm_impl(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qtype,
-              int path, void* ws, int64_t ws_bytes, hipStream_t stream) {
+int gemm_impl(float* dst, int64_t ldd, const void* w, const float* x, int64_t ldx, int64_t m, int64_t k,
+              int64_t n, int qtype, int path, void* ws, int64_t ws_bytes, hipStream_t stream) {
     int64_t rb;
-    int st = check_gemm(dst, w, x, m, k, n, qtype, &path, &rb);
+    int st = check_gemm(dst, w, x, m, k, n, qtype, ldx, ldd, &path, &rb);
     if (st) return st;
     qmm::GemvTuning tune;
     if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
     if (path == QMM_PATH_GEMV) {
-        qmm::launch_gemv(dst, w, x, m, k, n, qtype, rb, tune, stream);
+        qmm::launch_gemv(dst, w, x, m, k, n, qtype, rb, ldx, ldd, tune, stream);
         return launch_status();
     }
     const MfmaForceState g_force = parse_force();
@@ -258,7 +258,7 @@ int gemm_impl(float* dst, const void* w, const float* x, int64_t m, int64_t k, i
         if (!aligned(ws, 256)) return QMM_ERR_ALIGN;
         if (ws_bytes < pl.ws_bytes) return QMM_ERR_WORKSPACE;
     }
-    qmm::launch_gemm_mfma(dst, w, x, m, k, n, qtype, rb, pl, ws, stream);
+    qmm::launch_gemm_mfma(dst, w, x, m, k, n, qtype, rb, pl, ws, ldx, ldd, stream);
     return launch_status();
 }
 
@@ -352,12 +352,17 @@ int qmm_gemm_plan(int64_t m, int64_t k, int64_t n, int qtype, int path, int with
 
 int qmm_gemm_ws(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qtype,
                 int path, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
-    return gemm_impl(dst, w, x, m, k, n, qtype, path, workspace, workspace_bytes, stream);
+    return gemm_impl(dst, m, w, x, k, m, k, n, qtype, path, workspace, workspace_bytes, stream);
+}
+
+int qmm_gemm_ex(float* dst, int64_t ldd, const void* w, const float* x, int64_t ldx, int64_t m, int64_t k,
+                int64_t n, int qtype, int path, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    return gemm_impl(dst, ldd, w, x, ldx, m, k, n, qtype, path, workspace, workspace_bytes, stream);
 }
 
 int qmm_gemm_path(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
                   int qtype, int path, hipStream_t stream) {
-    return gemm_impl(dst, w, x, m, k, n, qtype, path, nullptr, 0, stream);
+    return gemm_impl(dst, m, w, x, k, m, k, n, qtype, path, nullptr, 0, stream);
 }
 
 int qmm_gemm(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qtype,

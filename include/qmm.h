@@ -143,6 +143,22 @@ int qmm_gemm_ws(float* dst, const void* w, const float* x, int64_t m, int64_t k,
                 int qtype, int path, void* workspace, int64_t workspace_bytes,
                 hipStream_t stream);
 
+/*
+ * qmm_gemm_ex: qmm_gemm_ws on row-strided activations and output (the F9
+ * stride fields of cera wgpu_gemm_bench.rs's MulMatParams, where the rows of
+ * src1 and dst need not be packed):
+ *     dst[j*ldd + i] = sum_c deq(W)[i][c] * x[j*ldx + c]
+ *   ldx   floats between consecutive rows of x: >= k (QMM_ERR_SHAPE) and a
+ *         multiple of 4 (QMM_ERR_ALIGN), so every row is 16-byte aligned.
+ *   ldd   floats between consecutive rows of dst: >= m (QMM_ERR_SHAPE).
+ *         Elements of dst between m and ldd are not written.
+ * qmm_gemm_ws(...) is qmm_gemm_ex with ldx = k and ldd = m.  Limits as
+ * qmm_gemm with k replaced by ldx in the activation windows (8 rows for the
+ * GEMV, 128 for the matrix-core tiles, below 2^31 bytes).
+ */
+int qmm_gemm_ex(float* dst, int64_t ldd, const void* w, const float* x, int64_t ldx, int64_t m, int64_t k,
+                int64_t n, int qtype, int path, void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes qmm_gemm_ws uses for this product on the current device:
  * 0 on the GEMV path, at least 256 on the MFMA path; < 0 is -qmm_status. */
 int64_t qmm_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int qtype, int path);

@@ -104,6 +104,13 @@ def test_validation_rejects_before_launch():
     assert d(A, A, A, A, A, A, 1, 8, 64, 2000, 4096, 5, s0) == 3     # n_ff % 64
     assert d(A, A, A, A, A, A, 1, 8, 64, 2048, 4096, 8, s0) == 4     # qtype
     assert d(A, A, A, A, A, A, 70000, 1, 64, 64, 4096, 5, s0) == 8   # more pairs than the grid
+    ex = lib.qmm_gemm_ex
+    assert ex(A, 64, A, A, 255, 64, 256, 4, 3, 0, z, 0, s0) == 2      # ldx < k
+    assert ex(A, 63, A, A, 256, 64, 256, 4, 3, 0, z, 0, s0) == 2      # ldd < m
+    assert ex(A, 64, A, A, 258, 64, 256, 4, 3, 0, z, 0, s0) == 5      # ldx % 4
+    assert ex(z, 64, A, A, 256, 64, 256, 4, 3, 0, z, 0, s0) == 1      # null dst
+    assert ex(A, 64, A, A, 1 << 28, 64, 256, 4, 3, 1, z, 0, s0) == 8  # GEMV x window >= 2^31
+    assert ex(A, 64, A, A, 1 << 23, 64, 256, 200, 3, 2, z, 0, s0) == 8  # tile x window >= 2^31
     qz = lib.qmm_quantize_q8_1
     assert qz(A, z, A, 4, 256, s0) == 1                               # null d
     assert qz(A, A, A, 0, 256, s0) == 2                               # rows < 1

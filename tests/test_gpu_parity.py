@@ -530,3 +530,36 @@ def test_moe_q8_exact_activations_match_f32_path():
     rg, ru, Sg, Su = ref.moe_ref("nvfp4", wg, wu, ids, sc, x, n_expert, in_f, n_ff)
     assert ref.tolerance_check(g.cpu().numpy(), rg, Sg, TAU_F32)[0]
     assert ref.tolerance_check(u.cpu().numpy(), ru, Su, TAU_F32)[0]
+
+
+# ------------------------------------------------------------------ strided x and dst
+
+@pytest.mark.parametrize("plan", [None, "0,2,1,1", "0,2,3,2", "1,2,1", "1,4,3"])
+@pytest.mark.parametrize("qt", ["q4_k", "f32"])
+def test_strided_rows_bit_identical(qt, plan, monkeypatch):
+    """Row-strided x and dst (qmm_gemm_ex) give bit-identical results to the
+    contiguous call on every path and prefill kernel family, and leave the
+    padding between dst rows untouched."""
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    if plan is not None:
+        if qt == "f32" and plan.count(",") == 3 and plan.endswith(",2"):
+            pytest.skip("not a plan the library runs for f32 weights")
+        monkeypatch.setenv("QMM_MFMA_PLAN", plan)
+    m, k = 300, 1024
+    w = to_dev(weights(qt, m, k, 41))
+    for n, path in ((5, "gemv"), (13, "gemv"), (200, "mfma")):
+        if plan is not None and path == "gemv":
+            continue
+        note(f"strided {qt} plan={plan} n={n} {path}")
+        x = acts(n, k, 41)
+        ref_out = qmm.gemm(w, to_dev(x), m, qt, path=path)
+        for padx, padd in ((12, 7), (4, 4)):
+            xb = torch.zeros((n, k + padx), dtype=torch.float32, device="cuda")
+            xb[:, :k] = to_dev(x)
+            ob = torch.full((n, m + padd), -7.0, dtype=torch.float32, device="cuda")
+            got = qmm.gemm(w, xb[:, :k], m, qt, out=ob[:, :m], path=path)
+            torch.cuda.synchronize()
+            assert got.data_ptr() == ob.data_ptr()
+            assert torch.equal(ob[:, :m], ref_out), f"padx={padx} padd={padd}"
+            assert torch.all(ob[:, m:] == -7.0)
