@@ -31,6 +31,12 @@ bool valid_qt(int qt) { return qt >= 0 && qt < kNumQt; }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// [a, a + an) and [b, b + bn) share a byte (sizes in bytes, >= 0).
+bool overlap(const void* a, int64_t an, const void* b, int64_t bn) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return an > 0 && bn > 0 && x < y + (uintptr_t)bn && y < x + (uintptr_t)an;
+}
+
 // a*b without int64 overflow (both >= 0)
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
     if (a != 0 && b > INT64_MAX / a) return false;
@@ -217,6 +223,11 @@ int check_gemm(float* dst, const void* w, const float* x, int64_t m, int64_t k, 
     if (n > INT_MAX || ldx > INT_MAX || ldd > INT_MAX) return QMM_ERR_RANGE;
     int64_t t1, t2;
     if (!mul_ok(n, ldx, &t1) || !mul_ok(n, ldd, &t2)) return QMM_ERR_SHAPE;
+    const int64_t dst_b = ((n - 1) * ldd + m) * 4, x_b = ((n - 1) * ldx + k) * 4;
+    // last of the checks: an output overlapping an input
+    auto alias = [&]() {
+        return overlap(dst, dst_b, x, x_b) || overlap(dst, dst_b, w, m * *rb) ? QMM_ERR_ALIAS : QMM_OK;
+    };
     if (*path == QMM_PATH_AUTO) {
         *path = auto_path(m, k, n);
         if (*path < 0) return QMM_ERR_RANGE;
@@ -225,7 +236,7 @@ int check_gemm(float* dst, const void* w, const float* x, int64_t m, int64_t k, 
         // one work group addresses at most this window of w, and 8 token rows of x
         if (qmm::gemv_max_window_bytes(qtype, k, *rb) >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
         if ((7 * ldx + k) * 4 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
-        return QMM_OK;
+        return alias();
     }
     if (*path == QMM_PATH_MFMA) {
         if (qtype == QMM_NVFP4_V2) return QMM_ERR_QTYPE;  // streaming paths only
@@ -234,7 +245,7 @@ int check_gemm(float* dst, const void* w, const float* x, int64_t m, int64_t k, 
         const int64_t tiles = ((m + qmm::MFMA_BM - 1) / qmm::MFMA_BM) * ((n + qmm::MFMA_BN - 1) / qmm::MFMA_BN);
         // work items (tiles x k splits, at most 16) are counted in int
         if (tiles > INT_MAX / 16) return QMM_ERR_RANGE;
-        return QMM_OK;
+        return alias();
     }
     return QMM_ERR_PATH;
 }
@@ -393,6 +404,16 @@ int qmm_moe_gateup(float* gate_out, float* up_out, const void* w_gate, const voi
     if (qmm::gemv_max_window_bytes(qtype, in_f, rb) >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
     qmm::GemvTuning tune;
     if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
+    {
+        const int64_t ob = n_pairs * n_ff * 4, wb = rows * rb;
+        if (overlap(gate_out, ob, up_out, ob) || overlap(gate_out, ob, x, t * in_f * 4) ||
+            overlap(up_out, ob, x, t * in_f * 4) || overlap(gate_out, ob, w_gate, wb) ||
+            overlap(gate_out, ob, w_up, wb) || overlap(up_out, ob, w_gate, wb) ||
+            overlap(up_out, ob, w_up, wb) || overlap(gate_out, ob, expert_ids, n_pairs * 4) ||
+            overlap(up_out, ob, expert_ids, n_pairs * 4) || overlap(gate_out, ob, pair_scale, n_pairs * 8) ||
+            overlap(up_out, ob, pair_scale, n_pairs * 8))
+            return QMM_ERR_ALIAS;
+    }
     qmm::launch_moe(gate_out, up_out, w_gate, w_up, expert_ids, pair_scale, x, t, n_used, n_expert,
                     in_f, n_ff, qtype, rb, tune, stream);
     return launch_status();
@@ -418,6 +439,14 @@ int qmm_moe_down(float* y, float* pair_out, const void* w_down, const int32_t* e
     if (qmm::gemv_max_window_bytes(qtype, n_ff, rb) >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
     qmm::GemvTuning tune;
     if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
+    {
+        const int64_t yb = t * d_model * 4, pb = outs * 4, wb = rows * rb, ab = n_pairs * n_ff * 4;
+        if (overlap(y, yb, pair_out, pb) || overlap(y, yb, act, ab) || overlap(pair_out, pb, act, ab) ||
+            overlap(y, yb, w_down, wb) || overlap(pair_out, pb, w_down, wb) ||
+            overlap(y, yb, expert_ids, n_pairs * 4) || overlap(pair_out, pb, expert_ids, n_pairs * 4) ||
+            overlap(y, yb, pair_scale, n_pairs * 4) || overlap(pair_out, pb, pair_scale, n_pairs * 4))
+            return QMM_ERR_ALIAS;
+    }
     qmm::launch_moe_down(y, pair_out, w_down, expert_ids, pair_scale, act, t, n_used, n_expert, n_ff,
                          d_model, qtype, rb, tune, stream);
     return launch_status();
@@ -430,6 +459,8 @@ int qmm_quantize_q8_1(int8_t* q, float* d, const float* x, int64_t rows, int64_t
     if (!aligned(q, 16) || !aligned(x, 16) || !aligned(d, 4)) return QMM_ERR_ALIGN;
     int64_t elems;
     if (!mul_ok(rows, k, &elems)) return QMM_ERR_SHAPE;
+    if (overlap(q, elems, d, elems / 8) || overlap(q, elems, x, elems * 4) || overlap(d, elems / 8, x, elems * 4))
+        return QMM_ERR_ALIAS;
     qmm::launch_quantize_q8_1(q, d, x, elems / 32, stream);
     return launch_status();
 }
@@ -459,6 +490,17 @@ int qmm_moe_gateup_q8(float* gate_out, float* up_out, const void* w_gate, const 
     if (qmm::moe_q8_lds_bytes(in_f) > 64 * 1024) return QMM_ERR_RANGE;
     qmm::GemvTuning tune;
     if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
+    {
+        const int64_t ob = n_pairs * n_ff * 4, wb = rows * rb;
+        if (overlap(gate_out, ob, up_out, ob) || overlap(gate_out, ob, xq, t * in_f) ||
+            overlap(up_out, ob, xq, t * in_f) || overlap(gate_out, ob, xd, t * in_f / 8) ||
+            overlap(up_out, ob, xd, t * in_f / 8) || overlap(gate_out, ob, w_gate, wb) ||
+            overlap(gate_out, ob, w_up, wb) || overlap(up_out, ob, w_gate, wb) ||
+            overlap(up_out, ob, w_up, wb) || overlap(gate_out, ob, expert_ids, n_pairs * 4) ||
+            overlap(up_out, ob, expert_ids, n_pairs * 4) || overlap(gate_out, ob, pair_scale, n_pairs * 8) ||
+            overlap(up_out, ob, pair_scale, n_pairs * 8))
+            return QMM_ERR_ALIAS;
+    }
     qmm::launch_moe_q8(gate_out, up_out, w_gate, w_up, expert_ids, pair_scale, xq, xd, t, n_used,
                        n_expert, in_f, n_ff, qtype, rb, tune, stream);
     return launch_status();

@@ -30,7 +30,9 @@
  *    the shapes define (loads past the end are bounds-checked by the buffer
  *    descriptors and return zero) and use no float atomics, so two identical
  *    calls produce bit-identical results.
- *  - dst must not alias w or x.
+ *  - Outputs must not overlap inputs (or each other): every entry point
+ *    checks the byte ranges its sizes define and returns QMM_ERR_ALIAS,
+ *    after all other checks and before any launch.
  */
 #ifndef QMM_H
 #define QMM_H

@@ -111,7 +111,16 @@ def test_validation_rejects_before_launch():
     assert ex(z, 64, A, A, 256, 64, 256, 4, 3, 0, z, 0, s0) == 1      # null dst
     assert ex(A, 64, A, A, 1 << 28, 64, 256, 4, 3, 1, z, 0, s0) == 8  # GEMV x window >= 2^31
     assert ex(A, 64, A, A, 1 << 23, 64, 256, 200, 3, 2, z, 0, s0) == 8  # tile x window >= 2^31
+    # an output overlapping an input is rejected (checked last, before any launch)
+    C = ctypes.c_void_p((1 << 20) + 64)
+    D = ctypes.c_void_p(1 << 24)
+    E = ctypes.c_void_p(1 << 26)
+    assert ex(A, 64, D, C, 256, 64, 256, 4, 3, 1, z, 0, s0) == 10     # dst over x
+    assert ex(A, 64, C, E, 256, 64, 256, 4, 3, 1, z, 0, s0) == 10     # dst over w
+    assert d(A, C, D, E, ctypes.c_void_p(1 << 27), ctypes.c_void_p(1 << 28), 1, 8, 64, 2048, 4096, 5,
+             s0) == 10                                                  # y over pair_out
     qz = lib.qmm_quantize_q8_1
+    assert qz(A, C, D, 4, 256, s0) == 10                              # q over d
     assert qz(A, z, A, 4, 256, s0) == 1                               # null d
     assert qz(A, A, A, 0, 256, s0) == 2                               # rows < 1
     assert qz(A, A, A, 4, 48, s0) == 3                                # k % 32
