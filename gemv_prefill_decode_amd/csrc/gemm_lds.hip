@@ -1,0 +1,495 @@
+// Prefill path, LDS-ring form: the packed weight bytes and the f16
+// activations of each 64-k step are streamed straight from memory into a
+// ring of NS LDS stages by buffer-to-LDS loads (buffer_load_dwordx4 ... lds),
+// issued NS-1 steps ahead of their use.  No register holds data in flight,
+// so the ring can be deep, and the k loop is a single rolled step.
+//
+// One work group of 4 waves computes a BM x 128 tile of dst (BM = 4*WR
+// weight rows, 128 tokens).  Wave w owns weight rows [w*WR, w*WR + WR) and
+// all 128 tokens.  Per step it decodes its rows' packed bytes from the LDS
+// stage straight into the A operands of v_mfma_f32_16x16x32_f16 (no decoded
+// weight tile is written back to LDS), reads the B operands (f16 activations)
+// from the stage, and runs (WR/16) x 8 x 2 matrix-core ops with f32
+// accumulators.
+//
+// Operand layout of v_mfma_f32_16x16x32_f16: lane l holds A row l % 16 and B
+// column l % 16, each at the 8 k slots 8*(l / 16) .. +7 of the op's 32; the
+// result D[r][c] sits in lane (r / 4) * 16 + c, element r % 4.  A 64-k step
+// is two such ops (ks = 0, 1) per 16 x 16 block, so lane (r16, g) of a wave
+// needs, per weight row, the 16 weights in slots 32*ks + 8*g + i (i < 8).
+// Each format assigns k values to slots so that these 16 weights come from a
+// few adjacent packed bytes of the row (slot_k below); the activations are
+// laid out in the same slot order by the f16 pre-pass, so the contraction
+// over the step's 64 k values is unchanged.
+//
+// Step k sets: a step is k in [64 kt, 64 kt + 64), except Q6_K, whose step kt
+// covers the two 32-runs of super-block kt/4 whose codes share one set of ql
+// bytes (the ggml Q6_K layout: low and high nibbles of ql[l] belong to
+// elements l and l + 64 of a 128-half).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qmm {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+namespace lds_ring {
+
+constexpr int BN = 128;          // tokens per tile
+constexpr int B_STAGE = BN * 128;  // bytes of one stage's activations (128 tokens x 64 f16)
+constexpr int LDS_BYTES = 160 * 1024;
+
+// 16-byte chunks one weight row occupies in a stage (a pad chunk where it
+// spreads rows over the LDS banks), and how a step's bytes are fetched.
+template <int QT> struct Fmt;
+template <> struct Fmt<QT_F32> { static constexpr int CPR = 16; };   // chunks XOR-swizzled per row
+template <> struct Fmt<QT_Q4_0> { static constexpr int CPR = 3; };   // 36 B from a dword-aligned start
+template <> struct Fmt<QT_Q8_0> { static constexpr int CPR = 5; };   // 68 B from a dword-aligned start
+template <> struct Fmt<QT_Q4_K> { static constexpr int CPR = 3; };   // header 16 B + 32 B of qs
+template <> struct Fmt<QT_Q6_K> { static constexpr int CPR = 9; };   // ql 32, qh 32, scales+d 18, pad
+template <> struct Fmt<QT_NVFP4> { static constexpr int CPR = 3; };  // 36 B group
+
+template <int QT, int WR> struct Geo {
+    static constexpr int BM = 4 * WR;
+    static constexpr int CPR = Fmt<QT>::CPR;
+    static constexpr int A_ROWS_CHUNKS = BM * CPR;
+    // the A loads of a stage cover whole rounds of 4 waves x 64 chunks; the
+    // chunks past the rows' land in a tail of the stage nobody reads
+    static constexpr int A_CHUNKS = (A_ROWS_CHUNKS + 255) / 256 * 256;
+    static constexpr int A_STAGE = A_CHUNKS * 16;
+    static constexpr int STAGE = A_STAGE + B_STAGE;
+    static constexpr int NS_FIT = LDS_BYTES / STAGE;
+    static constexpr int NS = NS_FIT > 4 ? 4 : NS_FIT;
+    static constexpr int DA = A_CHUNKS / 256;  // A loads per wave per step (64 chunks each)
+    static constexpr int DB = 4;               // B loads per wave per step
+    static_assert(NS >= 3, "the ring needs at least 3 stages");
+    static_assert((NS - 2) * (DA + DB) <= 63, "vmcnt range");
+};
+
+// k of slot s = 32*ks + 8*g + i of step kt (see the file comment).
+template <int QT>
+__host__ __device__ __forceinline__ int slot_k(int kt, int ks, int g, int i) {
+    if constexpr (QT == QT_Q4_0 || QT == QT_NVFP4) {
+        // byte 4g+b of a 32-run (16 packed bytes) holds elements 4g+b (low
+        // nibble) and 16+4g+b (high nibble)
+        return 64 * kt + 32 * ks + (i < 4 ? 4 * g + i : 16 + 4 * g + i - 4);
+    } else if constexpr (QT == QT_Q6_K) {
+        return 256 * (kt >> 2) + 128 * ((kt >> 1) & 1) + 64 * ks + 32 * (kt & 1) + 8 * g + i;
+    } else {
+        return 64 * kt + 32 * ks + 8 * g + i;  // identity
+    }
+}
+
+// Byte offset (from the weight window's base) of chunk c of a row whose first
+// byte is at rowoff, for step kt (pad chunks are masked by the caller).
+template <int QT>
+__device__ __forceinline__ uint32_t a_chunk_off(uint32_t rowoff, int c, int kt) {
+    if constexpr (QT == QT_F32) {
+        return rowoff + 256u * (uint32_t)kt + 16u * (uint32_t)c;
+    } else if constexpr (QT == QT_Q4_0) {
+        return ((rowoff + 36u * (uint32_t)kt) & ~3u) + 16u * (uint32_t)c;
+    } else if constexpr (QT == QT_Q8_0) {
+        return ((rowoff + 68u * (uint32_t)kt) & ~3u) + 16u * (uint32_t)c;
+    } else if constexpr (QT == QT_Q4_K) {
+        const uint32_t o = rowoff + 144u * ((uint32_t)kt >> 2);
+        return c == 0 ? o : o + 16u + 32u * ((uint32_t)kt & 3u) + 16u * (uint32_t)(c - 1);
+    } else if constexpr (QT == QT_Q6_K) {
+        // c = 3*piece + chunk: pieces ql (64hh + 32kh), qh (128 + 32hh) and
+        // scales + d (192), each from the dword at or below its first byte
+        const uint32_t o = rowoff + 210u * ((uint32_t)kt >> 2);
+        const uint32_t hh = ((uint32_t)kt >> 1) & 1u, kh = (uint32_t)kt & 1u;
+        const int p = c >= 6 ? 2 : (c >= 3 ? 1 : 0);
+        const uint32_t pb = p == 0 ? 64u * hh + 32u * kh : (p == 1 ? 128u + 32u * hh : 192u);
+        return ((o + pb) & ~3u) + 16u * (uint32_t)(c - 3 * p);
+    } else {  // NVFP4: 36-byte groups, rows a multiple of 4 bytes
+        return rowoff + 36u * (uint32_t)kt + 16u * (uint32_t)c;
+    }
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) { return *(const uint32_t*)p; }
+
+// f16x8 A operand from four packed f16 pairs
+__device__ __forceinline__ f16x8 frag4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const u32x4 v = {a, b, c, d};
+    return __builtin_bit_cast(f16x8, v);
+}
+
+// (1024 + byte) as binary16 for bytes b0 and b0+1 of v, as one f16x2
+__device__ __forceinline__ f16x2 mpair(uint32_t v, int b0) {
+    const uint32_t bits = ((v >> (8 * b0)) & 0xFFu) | (((v >> (8 * b0 + 8)) & 0xFFu) << 16) | 0x64006400u;
+    return __builtin_bit_cast(f16x2, bits);
+}
+
+// ------------------------------------------------------------ row decoders
+// Decode one weight row's 16 weights of lane group g for the step into the
+// two A operands (ks = 0, 1).  row: the row's bytes in the LDS stage;
+// rowoff: its byte offset in the weight window (alignment of unaligned
+// formats); kt: the step.
+
+template <int QT> struct Dec;
+
+template <> struct Dec<QT_F32> {
+    __device__ __forceinline__ static void run(const uint8_t* row, uint32_t, int, int g, int rsw,
+                                               f16x8& a0, f16x8& a1) {
+        // chunk c of the row sits at chunk c ^ rsw (rsw = row & 15)
+        auto ld = [&](int c) { return *(const f32x4*)(row + 16 * (c ^ rsw)); };
+        const f32x4 p0 = ld(2 * g), p1 = ld(2 * g + 1), q0 = ld(8 + 2 * g), q1 = ld(9 + 2 * g);
+        a0 = frag4(pack_f2h(p0.x, p0.y), pack_f2h(p0.z, p0.w), pack_f2h(p1.x, p1.y), pack_f2h(p1.z, p1.w));
+        a1 = frag4(pack_f2h(q0.x, q0.y), pack_f2h(q0.z, q0.w), pack_f2h(q1.x, q1.y), pack_f2h(q1.z, q1.w));
+    }
+};
+
+template <> struct Dec<QT_Q4_0> {
+    // block ks (18 bytes) at byte sh + 18 ks of the stage row, sh = rowoff & 3
+    __device__ __forceinline__ static f16x8 blk(const uint8_t* row, int sh, int ks, int g) {
+        const int db = sh + 18 * ks;                    // d
+        const uint32_t dw = lds_u32(row + (db & ~3));
+        const _Float16 d = bits_h(dw >> (8 * (db & 3)));
+        const int qb = db + 2 + 4 * g;                  // qs[4g .. 4g+3]
+        const uint32_t q = __builtin_amdgcn_alignbyte(lds_u32(row + (qb & ~3) + 4), lds_u32(row + (qb & ~3)),
+                                                      (uint32_t)(qb & 3));
+        const uint32_t lo = q & 0x0F0F0F0Fu, hi = (q >> 4) & 0x0F0F0F0Fu;
+        const f16x2 dd = {d, d}, off = {(_Float16)1032.0f, (_Float16)1032.0f};
+        // (1024 + q) - 1032 = q - 8 exactly; one f16 rounding in the product
+        return frag4(__builtin_bit_cast(uint32_t, (mpair(lo, 0) - off) * dd),
+                     __builtin_bit_cast(uint32_t, (mpair(lo, 2) - off) * dd),
+                     __builtin_bit_cast(uint32_t, (mpair(hi, 0) - off) * dd),
+                     __builtin_bit_cast(uint32_t, (mpair(hi, 2) - off) * dd));
+    }
+    __device__ __forceinline__ static void run(const uint8_t* row, uint32_t rowoff, int, int g, int,
+                                               f16x8& a0, f16x8& a1) {
+        const int sh = (int)(rowoff & 3u);
+        a0 = blk(row, sh, 0, g);
+        a1 = blk(row, sh, 1, g);
+    }
+};
+
+template <> struct Dec<QT_Q8_0> {
+    __device__ __forceinline__ static f16x8 blk(const uint8_t* row, int sh, int ks, int g) {
+        const int db = sh + 34 * ks;
+        const uint32_t dw = lds_u32(row + (db & ~3));
+        const _Float16 d = bits_h(dw >> (8 * (db & 3)));
+        const int qb = db + 2 + 8 * g;                  // qs[8g .. 8g+7]
+        const uint8_t* p = row + (qb & ~3);
+        const uint32_t s = (uint32_t)(qb & 3);
+        const uint32_t w0 = lds_u32(p), w1 = lds_u32(p + 4), w2 = lds_u32(p + 8);
+        // int8 q -> byte q + 128 -> 1024 + q + 128 in f16, minus 1152 = q exactly
+        const uint32_t qa = __builtin_amdgcn_alignbyte(w1, w0, s) ^ 0x80808080u;
+        const uint32_t qc = __builtin_amdgcn_alignbyte(w2, w1, s) ^ 0x80808080u;
+        const f16x2 dd = {d, d}, off = {(_Float16)1152.0f, (_Float16)1152.0f};
+        return frag4(__builtin_bit_cast(uint32_t, (mpair(qa, 0) - off) * dd),
+                     __builtin_bit_cast(uint32_t, (mpair(qa, 2) - off) * dd),
+                     __builtin_bit_cast(uint32_t, (mpair(qc, 0) - off) * dd),
+                     __builtin_bit_cast(uint32_t, (mpair(qc, 2) - off) * dd));
+    }
+    __device__ __forceinline__ static void run(const uint8_t* row, uint32_t rowoff, int, int g, int,
+                                               f16x8& a0, f16x8& a1) {
+        const int sh = (int)(rowoff & 3u);
+        a0 = blk(row, sh, 0, g);
+        a1 = blk(row, sh, 1, g);
+    }
+};
+
+// 8 weights D*q - M for the nibbles or bytes of q0 (elements 0..3) and q1 (4..7)
+__device__ __forceinline__ f16x8 affine8(uint32_t q0, uint32_t q1, float D, float Mneg) {
+    float v[8];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        v[b] = __builtin_fmaf(D, ubyte_f32(q0, b), Mneg);
+        v[4 + b] = __builtin_fmaf(D, ubyte_f32(q1, b), Mneg);
+    }
+    return frag4(pack_f2h(v[0], v[1]), pack_f2h(v[2], v[3]), pack_f2h(v[4], v[5]), pack_f2h(v[6], v[7]));
+}
+
+template <> struct Dec<QT_Q4_K> {
+    __device__ __forceinline__ static void run(const uint8_t* row, uint32_t, int kt, int g, int,
+                                               f16x8& a0, f16x8& a1) {
+        const u32x4 hdr = *(const u32x4*)row;
+        const u32x2 q = *(const u32x2*)(row + 16 + 8 * g);
+        const float d = h2f(hdr.x), dmin = h2f(hdr.x >> 16);
+        // sub-blocks j0 = 2c (low nibbles) and j1 = 2c + 1 (high nibbles) of
+        // chunk c = kt & 3.  With jj = j & 3, the packing uses the bytes
+        // A = sc[jj], B = sc[jj + 4], C = sc[jj + 8]: for j < 4 the scale is
+        // A & 63 and the min B & 63; for j >= 4 the scale is
+        // (C & 15) | (A >> 6) << 4 and the min (C >> 4) | (B >> 6) << 4.
+        const int c = kt & 3;
+        const uint32_t sh0 = 16u * (uint32_t)(c & 1);  // byte jj0 = 2(c & 1), jj1 = jj0 + 1
+        const uint32_t A = hdr.y >> sh0, B = hdr.z >> sh0, C = hdr.w >> sh0;
+        // all ones for c < 2, else zero; a per-lane value so the blends stay
+        // bit operations in the loop's single basic block
+        const uint32_t lo = (uint32_t)as_vgpr(-(int)(c < 2));
+        auto blend = [lo](uint32_t a, uint32_t b) { return (a & lo) | (b & ~lo); };
+        const uint32_t s0 = blend(A & 63u, (C & 15u) | (((A >> 6) & 3u) << 4));
+        const uint32_t m0 = blend(B & 63u, ((C >> 4) & 15u) | (((B >> 6) & 3u) << 4));
+        const uint32_t s1 = blend((A >> 8) & 63u, ((C >> 8) & 15u) | (((A >> 14) & 3u) << 4));
+        const uint32_t m1 = blend((B >> 8) & 63u, ((C >> 12) & 15u) | (((B >> 14) & 3u) << 4));
+        const float D0 = d * (float)s0, M0 = dmin * (float)m0;
+        const float D1 = d * (float)s1, M1 = dmin * (float)m1;
+        a0 = affine8(q.x & 0x0F0F0F0Fu, q.y & 0x0F0F0F0Fu, D0, -M0);
+        a1 = affine8((q.x >> 4) & 0x0F0F0F0Fu, (q.y >> 4) & 0x0F0F0F0Fu, D1, -M1);
+    }
+};
+
+template <> struct Dec<QT_Q6_K> {
+    // stage row: chunks 0-2 ql piece, 3-5 qh piece, 6-7 scales + d piece;
+    // every piece starts at the dword at or below its first byte, sh = the
+    // super-block's offset & 3 (0 or 2)
+    __device__ __forceinline__ static void run(const uint8_t* row, uint32_t rowoff, int kt, int g, int,
+                                               f16x8& a0, f16x8& a1) {
+        const uint32_t sh = (rowoff + 210u * ((uint32_t)kt >> 2)) & 3u;
+        const int hh = (kt >> 1) & 1, kh = kt & 1;
+        const uint8_t* L = row + 8 * g;
+        const uint8_t* H = row + 48 + 8 * g;
+        const uint8_t* S = row + 96;
+        const uint32_t l0 = __builtin_amdgcn_alignbyte(lds_u32(L + 4), lds_u32(L), sh);
+        const uint32_t l1 = __builtin_amdgcn_alignbyte(lds_u32(L + 8), lds_u32(L + 4), sh);
+        const uint32_t h0 = __builtin_amdgcn_alignbyte(lds_u32(H + 4), lds_u32(H), sh);
+        const uint32_t h1 = __builtin_amdgcn_alignbyte(lds_u32(H + 8), lds_u32(H + 4), sh);
+        const int i0 = (int)sh + 8 * hh + 2 * kh + (g >> 1), i1 = i0 + 4;  // scale bytes
+        const int8_t sc0 = (int8_t)(lds_u32(S + (i0 & ~3)) >> (8 * (i0 & 3)));
+        const int8_t sc1 = (int8_t)(lds_u32(S + (i1 & ~3)) >> (8 * (i1 & 3)));
+        const float d = h2f(lds_u32(S + 16) >> (8 * sh));  // bytes sh+16, sh+17
+        const float Dl = d * (float)sc0, Dh = d * (float)sc1;
+        const int hs = 2 * kh;
+        const uint32_t ql0 = (l0 & 0x0F0F0F0Fu) | (((h0 >> hs) & 0x03030303u) << 4);
+        const uint32_t ql1 = (l1 & 0x0F0F0F0Fu) | (((h1 >> hs) & 0x03030303u) << 4);
+        const uint32_t qh0 = ((l0 >> 4) & 0x0F0F0F0Fu) | (((h0 >> (hs + 4)) & 0x03030303u) << 4);
+        const uint32_t qh1 = ((l1 >> 4) & 0x0F0F0F0Fu) | (((h1 >> (hs + 4)) & 0x03030303u) << 4);
+        a0 = affine8(ql0, ql1, Dl, -32.0f * Dl);
+        a1 = affine8(qh0, qh1, Dh, -32.0f * Dh);
+    }
+};
+
+template <> struct Dec<QT_NVFP4> {
+    __device__ __forceinline__ static f16x8 half(uint32_t q, float sl, float sh_) {
+        float lo[4], hi[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const f32x2 v = e2m1x2_to_f32(q, b);
+            lo[b] = v.x * sl;   // exact: at most 5 significant bits, within f16 range
+            hi[b] = v.y * sh_;
+        }
+        return frag4(pack_f2h(lo[0], lo[1]), pack_f2h(lo[2], lo[3]), pack_f2h(hi[0], hi[1]), pack_f2h(hi[2], hi[3]));
+    }
+    __device__ __forceinline__ static void run(const uint8_t* row, uint32_t, int, int g, int,
+                                               f16x8& a0, f16x8& a1) {
+        const uint32_t s = lds_u32(row);
+        const uint32_t q0 = lds_u32(row + 4 + 4 * g), q1 = lds_u32(row + 20 + 4 * g);
+        a0 = half(q0, e4m3_to_f32(s & 0xFFu), e4m3_to_f32((s >> 8) & 0xFFu));
+        a1 = half(q1, e4m3_to_f32((s >> 16) & 0xFFu), e4m3_to_f32(s >> 24));
+    }
+};
+
+// s_waitcnt with vmcnt(vm), lgkmcnt(lg), expcnt left free (gfx9 encoding)
+template <int VM, int LG>
+__device__ __forceinline__ void waitcnt() {
+    static_assert(VM >= 0 && VM < 64 && LG >= 0 && LG < 16, "waitcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LG << 8));
+}
+
+}  // namespace lds_ring
+
+// ------------------------------------------------------------ f16 pre-pass
+// x16[j][64 kt + s] = f16(x[j][slot_k(kt, s)]) (round to nearest even), zero
+// past k.  One thread per 8-slot unit (16 bytes out).
+template <int QT>
+__global__ __launch_bounds__(256) void x16_slot_kernel(uint16_t* __restrict__ x16, const float* __restrict__ x,
+                                                       int n, int k, int kp, int ldx) {
+    const int units = kp >> 3;
+    const int64_t total = (int64_t)n * units;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int j = (int)(i / units), u = (int)(i - (int64_t)j * units);
+        const int kt = u >> 3, ks = (u >> 2) & 1, g = u & 3;
+        const int ka = lds_ring::slot_k<QT>(kt, ks, g, 0), kb = lds_ring::slot_k<QT>(kt, ks, g, 4);
+        const float* xr = x + (int64_t)j * ldx;
+        const f32x4 a = ka < k ? *(const f32x4*)(xr + ka) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 b = kb < k ? *(const f32x4*)(xr + kb) : f32x4{0.f, 0.f, 0.f, 0.f};
+        *(u32x4*)(x16 + (int64_t)j * kp + 8 * (int64_t)u) =
+            u32x4{pack_f2h(a.x, a.y), pack_f2h(a.z, a.w), pack_f2h(b.x, b.y), pack_f2h(b.z, b.w)};
+    }
+}
+
+// ------------------------------------------------------------ the GEMM kernel
+// Work items (k split z, tile) are dealt to the 8 XCDs in contiguous runs,
+// weight-row tile fastest (as in the other prefill kernels).  Item z covers
+// steps [z*sps, min(nk, (z+1)*sps)); with n_split > 1 it writes its partial
+// tile to partial + z*splitk_stride(n, m), summed by splitk_sum_kernel.
+template <int QT, int WR>
+__global__ __launch_bounds__(256, 1) void gemm_lds_kernel(float* __restrict__ dst, const uint8_t* __restrict__ w,
+                                                          const uint16_t* __restrict__ x16, int m, int k, int n,
+                                                          int rb, int kp, int n_mb, int n_nb, int n_split, int sps,
+                                                          float* __restrict__ partial, int ldd) {
+    using G = lds_ring::Geo<QT, WR>;
+    constexpr int BM = G::BM, BN = lds_ring::BN, CPR = G::CPR, NS = G::NS, DA = G::DA, DB = G::DB;
+    constexpr int RI = WR / 16;  // 16-row blocks per wave
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * G::STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int r16 = lane & 15, g = lane >> 4;
+
+    const int T = n_mb * n_nb, NI = T * n_split, L = blockIdx.x;
+    const int xcd = L & 7, idx = L >> 3, per = NI >> 3, rem = NI & 7;
+    const int item = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    const int z = item / T, tile = item - z * T;
+    const int nb = tile / n_mb, mb = tile - nb * n_mb;
+    const int64_t m0 = (int64_t)mb * BM, n0 = (int64_t)nb * BN;
+
+    int64_t base;
+    const rsrc_t wr = row_window(w, m0, BM, m, rb, base);
+    const int ntok = (int)imin64(BN, n - n0);
+    const rsrc_t xr = make_rsrc(x16 + n0 * kp, (uint32_t)ntok * (uint32_t)kp * 2u);
+    const uint32_t rowoff0 = (uint32_t)(m0 * rb - base);  // byte offset of the tile's first row
+
+    const int nk_all = k >> 6;
+    const int s0 = z * sps;
+    const int nk = min(nk_all, s0 + sps);
+
+    // This lane's chunks of the buffer-to-LDS loads: A load u covers chunks
+    // (wave*DA + u)*64 + lane, B load u chunks (wave*DB + u)*64 + lane.
+    uint32_t a_rowoff[DA], a_dead[DA];
+    int a_c[DA];
+#pragma unroll
+    for (int u = 0; u < DA; ++u) {
+        const int q = (wave * DA + u) * 64 + lane;
+        const int r = q / CPR, c = q - r * CPR;
+        a_rowoff[u] = rowoff0 + (uint32_t)r * (uint32_t)rb;
+        // F32 rows: physical chunk q % 16 holds logical chunk c ^ (r & 15)
+        a_c[u] = QT == QT_F32 ? (c ^ (r & 15)) : c;
+        // chunks of the stage's tail and Q6_K's pad chunk load zeros: their
+        // offsets get bit 31 (past every window)
+        a_dead[u] = (q >= G::A_ROWS_CHUNKS || (QT == QT_Q6_K && c == 8)) ? OOB_OFF : 0u;
+    }
+    uint32_t b_off[DB];
+#pragma unroll
+    for (int u = 0; u < DB; ++u) {
+        const int q = (wave * DB + u) * 64 + lane;
+        const int t = q >> 3, p = q & 7;
+        b_off[u] = (uint32_t)t * (uint32_t)kp * 2u + 16u * (uint32_t)(p ^ (t & 7));
+    }
+    auto issue = [&](int kt, int stg) {
+        uint8_t* sa = lds + stg * G::STAGE;
+        uint8_t* sb = sa + G::A_STAGE;
+        // steps past the item's end load zeros (bit 31: past every window)
+        const uint32_t dead = kt < nk ? 0u : OOB_OFF;
+#pragma unroll
+        for (int u = 0; u < DA; ++u) {
+            const uint32_t off = lds_ring::a_chunk_off<QT>(a_rowoff[u], a_c[u], kt) | a_dead[u] | dead;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void_t*)(sa + (wave * DA + u) * 1024), 16, off, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < DB; ++u) {
+            const uint32_t off = (b_off[u] + 128u * (uint32_t)kt) | dead;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(sb + (wave * DB + u) * 1024), 16, off, 0, 0, 0);
+        }
+    };
+
+    f32x4 acc[RI][8];
+#pragma unroll
+    for (int i = 0; i < RI; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // this lane's weight rows in a stage, and their offsets in the window
+    const int rbase = wave * WR + r16;
+    const int bsw = 16 * (g ^ (r16 & 7));  // B chunk of slots [8g, 8g+8) of run ks = 0 (ks = 1: ^4 -> +64)
+
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p) issue(s0 + p, p);
+
+    int cur = 0;
+    for (int kt = s0; kt < nk; ++kt) {
+        // this wave's loads of step kt have landed (later steps' stay in
+        // flight), its LDS reads of step kt-1 are done; then every wave's
+        lds_ring::waitcnt<(NS - 2) * (DA + DB), 0>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // refill the stage step kt-1 used, NS-1 steps ahead
+        issue(kt + NS - 1, cur == 0 ? NS - 1 : cur - 1);
+
+        const uint8_t* sa = lds + cur * G::STAGE;
+        const uint8_t* sb = sa + G::A_STAGE;
+        f16x8 b0[8], b1[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint8_t* bt = sb + (16 * j + r16) * 128;
+            b0[j] = *(const f16x8*)(bt + bsw);
+            b1[j] = *(const f16x8*)(bt + (bsw ^ 64));
+        }
+#pragma unroll
+        for (int i = 0; i < RI; ++i) {
+            const int r = rbase + 16 * i;
+            f16x8 a0, a1;
+            lds_ring::Dec<QT>::run(sa + r * CPR * 16, rowoff0 + (uint32_t)r * (uint32_t)rb, kt, g, r & 15, a0, a1);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1[j], acc[i][j], 0, 0, 0);
+            }
+        }
+        cur = cur == NS - 1 ? 0 : cur + 1;
+    }
+    // drain the loads past the last step before the work group ends
+    lds_ring::waitcnt<0, 0>();
+
+    float* out = n_split > 1 ? partial + (int64_t)z * splitk_stride(n, m) : dst;
+    const int64_t ldo = n_split > 1 ? m : ldd;  // partials are dense
+#pragma unroll
+    for (int i = 0; i < RI; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t mrow = m0 + wave * WR + i * 16 + g * 4;
+            const int64_t tok = n0 + j * 16 + r16;
+            if (tok < n) {
+                float* p = out + tok * ldo + mrow;
+                const f32x4 v = acc[i][j];
+                if ((ldo & 3) == 0 && mrow + 4 <= m) {
+                    *(f32x4*)p = v;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (mrow + r < m) p[r] = v[r];
+                }
+            }
+        }
+    }
+}
+
+template <int QT>
+static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k, int64_t n,
+                          int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd, hipStream_t st) {
+    const int64_t kp = x16_row_halves(k);
+    uint16_t* x16 = (uint16_t*)ws;
+    float* part = (float*)((uint8_t*)ws + x16_bytes(n, k));
+    {
+        const int64_t total = n * (kp / 8);
+        int64_t blocks = (total + 255) / 256;
+        if (blocks > 8192) blocks = 8192;
+        x16_slot_kernel<QT><<<dim3((unsigned)blocks), 256, 0, st>>>(x16, x, (int)n, (int)k, (int)kp, (int)ldx);
+    }
+    const int bm = 64 * pl.wm;
+    const int n_mb = (int)((m + bm - 1) / bm), n_nb = (int)((n + 127) / 128);
+    const dim3 grid((unsigned)(n_mb * n_nb * pl.n_split));
+    if (QT != QT_F32 && pl.wm == 4)  // f32 rows fit the ring with 128-row tiles only
+        gemm_lds_kernel<QT == QT_F32 ? QT_Q4_K : QT, 64><<<grid, 256, 0, st>>>(dst, w, x16, (int)m, (int)k, (int)n, (int)rb, (int)kp, n_mb,
+                                                      n_nb, pl.n_split, pl.sps, part, (int)ldd);
+    else
+        gemm_lds_kernel<QT, 32><<<grid, 256, 0, st>>>(dst, w, x16, (int)m, (int)k, (int)n, (int)rb, (int)kp, n_mb,
+                                                      n_nb, pl.n_split, pl.sps, part, (int)ldd);
+    if (pl.n_split > 1) launch_splitk_sum(dst, part, n * m, splitk_stride(n, m), pl.n_split, m, ldd, st);
+}
+
+void launch_gemm_lds(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qt,
+                     int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd, hipStream_t st) {
+    const uint8_t* wb = (const uint8_t*)w;
+    switch (qt) {
+        case QT_F32: launch_lds_qt<QT_F32>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
+        case QT_Q4_0: launch_lds_qt<QT_Q4_0>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
+        case QT_Q8_0: launch_lds_qt<QT_Q8_0>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
+        case QT_Q4_K: launch_lds_qt<QT_Q4_K>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
+        case QT_Q6_K: launch_lds_qt<QT_Q6_K>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
+        case QT_NVFP4: launch_lds_qt<QT_NVFP4>(dst, wb, x, m, k, n, rb, pl, ws, ldx, ldd, st); break;
+    }
+}
+
+}  // namespace qmm

@@ -26,9 +26,12 @@ void launch_gemv(float* dst, const void* w, const float* x, int64_t m, int64_t k
 // Launch plan of the prefill (MFMA) kernels.  x16 = 0: gemm_mfma.hip's
 // kernel (128 x 128 tiles, f32 activations converted in the k loop).
 // x16 = 1: gemm_mfma_x16.hip's kernel ((64*wm) x 128 tiles, activations
-// rounded to f16 by a pre-pass into the workspace).  Either may split k into
-// n_split ranges of sps steps (64 k each; sps even) whose partial results go
-// to the workspace (after the f16 activations), summed by a second kernel.
+// rounded to f16 by a pre-pass into the workspace).  x16 = 2: gemm_lds.hip's
+// kernel ((64*wm) x 128 tiles; f16 activations from its own pre-pass, weight
+// bytes and activations streamed through an LDS ring; k % 64 == 0 only).
+// Any of them may split k into n_split ranges of sps steps (64 k each; sps
+// even) whose partial results go to the workspace (after the f16
+// activations), summed by a second kernel.
 struct MfmaPlan {
     int x16;
     int wm;
@@ -71,6 +74,8 @@ void launch_gemm_mfma(float* dst, const void* w, const float* x, int64_t m, int6
 void launch_gemm_mfma_x16(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
                           int qt, int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd,
                           hipStream_t st);
+void launch_gemm_lds(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qt,
+                     int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd, hipStream_t st);
 
 // dst[(i / m)*ldd + i % m] = sum over z < n_split of part[z*zstride + i], in
 // order of z, i < count.

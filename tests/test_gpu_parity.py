@@ -74,8 +74,11 @@ def test_mfma_parity_no_workspace(qt):
 
 @pytest.mark.parametrize("qt", QTS)
 def test_mfma_paths_agree_bit_for_bit_unsplit(qt):
-    """Both prefill kernels round x and W to f16 the same way; where neither
-    splits k their sums run in the same order, so the outputs are equal."""
+    """The f32- and f16-activation prefill kernels round x and W to f16 the
+    same way and order their k slots alike; unsplit, their sums run in the
+    same order, so the outputs are equal.  (The LDS-ring kernel orders the
+    slots inside each matrix-core op differently: within tolerance only.)"""
+    import os
     import gemv_prefill_decode_amd as qmm
     m, k, n = 512, 1024, 300
     note(f"mfma kernels agree {qt}")
@@ -83,9 +86,14 @@ def test_mfma_paths_agree_bit_for_bit_unsplit(qt):
     x = acts(n, k, 50)
     a = gpu_gemm(qt, w, x, m, "mfma", workspace=None)
     check_full(qt, w, x, m, k, n, a, TAU_F16, f"agree {qt}")
-    if qmm.workspace_bytes(m, k, n, qt, "mfma") > 0:
+    os.environ["QMM_MFMA_PLAN"] = "1,2,1"
+    try:
         b = gpu_gemm(qt, w, x, m, "mfma")
-        check_full(qt, w, x, m, k, n, b, TAU_F16, f"agree ws {qt}")
+    finally:
+        del os.environ["QMM_MFMA_PLAN"]
+    assert np.array_equal(a, b)
+    c = gpu_gemm(qt, w, x, m, "mfma")
+    check_full(qt, w, x, m, k, n, c, TAU_F16, f"agree planned {qt}")
 
 
 @pytest.mark.parametrize("qt", QTS)
@@ -120,18 +128,44 @@ def test_exact_structured_inputs(qt, path):
 
 @pytest.mark.parametrize("qt", QTS)
 def test_identity_activations_mfma(qt):
-    """x = I_k (n = k): dst[j, i] = f16(f32(W[i, j])) exactly (the weight is
-    decoded to f32 and rounded once more to f16 for the matrix cores; both
-    roundings are to nearest even).  Pins the tile mapping of every weight row
-    and k index into dst."""
+    """x = I_k (n = k): dst[j, i] = f16(W[i, j]) exactly (each weight reaches
+    the matrix cores rounded once, to nearest even, from its exact decoded
+    value).  Pins the tile mapping of every weight row and k index into dst."""
     m, k = 130, 256
     note(f"identity mfma {qt}")
     w = weights(qt, m, k, 21)
     x = np.eye(k, dtype=np.float32)
     got = gpu_gemm(qt, w, x, m, "mfma")
     W = formats.decode(qt, w, m, k)
-    want = W.T.astype(np.float32).astype(np.float16).astype(np.float64)
+    want = W.T.astype(np.float16).astype(np.float64)   # numpy rounds f64 -> f16 once, RNE
     assert np.array_equal(got.astype(np.float64), want)
+
+
+# The LDS-ring kernel assigns k to operand slots per format and lays the f16
+# activations out in the same order; identity activations and exact inputs
+# pin that mapping bit for bit for both tile heights.
+@pytest.mark.parametrize("plan", ["2,2,1", "2,4,1", "2,4,2"])
+@pytest.mark.parametrize("qt", QTS)
+def test_lds_ring_identity_and_exact(qt, plan, monkeypatch):
+    import gemv_prefill_decode_amd as qmm
+    if qt == "f32" and plan.startswith("2,4"):
+        pytest.skip("not a plan the library runs for f32 weights")
+    monkeypatch.setenv("QMM_MFMA_PLAN", plan)
+    m, k = 300, 512
+    assert qmm.gemm_plan(m, k, k, qt, "mfma")["x16"] == 2
+    note(f"lds ring identity {qt} {plan}")
+    w = weights(qt, m, k, 23)
+    x = np.eye(k, dtype=np.float32)
+    got = gpu_gemm(qt, w, x, m, "mfma")
+    W = formats.decode(qt, w, m, k)
+    want = W.T.astype(np.float16).astype(np.float64)   # numpy rounds f64 -> f16 once, RNE
+    assert np.array_equal(got.astype(np.float64), want)
+    note(f"lds ring exact {qt} {plan}")
+    we = exact_weights(qt, m, k, 8)
+    xe = gen.structured_exact(150 * k, 12).reshape(150, k)
+    got = gpu_gemm(qt, we, xe, m, "mfma")
+    r, _ = ref.gemm_ref(qt, we, xe, m, k, 150)
+    assert np.array_equal(got.astype(np.float64), r)
 
 
 @pytest.mark.parametrize("qt", QTS)
@@ -372,7 +406,8 @@ def test_split_k_shared_workspace_growing_tile_count():
 # Every prefill kernel family, forced through QMM_MFMA_PLAN on a ragged shape
 # (m, n not multiples of any tile; k with a partial split): x16, tile rows
 # (wm*64), k splits, k groups.
-FORCED_PLANS = ["0,2,1,1", "0,2,3,1", "0,2,1,2", "0,2,3,2", "1,2,1", "1,2,3", "1,4,1", "1,4,3"]
+FORCED_PLANS = ["0,2,1,1", "0,2,3,1", "0,2,1,2", "0,2,3,2", "1,2,1", "1,2,3", "1,4,1", "1,4,3",
+                "2,2,1", "2,2,3", "2,4,1", "2,4,3"]
 
 
 @pytest.mark.parametrize("plan", FORCED_PLANS)
@@ -382,7 +417,7 @@ def test_forced_prefill_plans(plan, qt, monkeypatch):
     x16, wm = int(plan.split(",")[0]), int(plan.split(",")[1])
     kg = int(plan.split(",")[3]) if plan.count(",") == 3 else 1
     m, k, n = 300, 1536 if qt != "q6_k" else 1792, 270
-    if qt == "f32" and kg == 2:
+    if qt == "f32" and (kg == 2 or (x16, wm) == (2, 4)):
         pytest.skip("not a plan the library runs for f32 weights")
     monkeypatch.setenv("QMM_MFMA_PLAN", plan)
     p = qmm.gemm_plan(m, k, n, qt, "mfma")
@@ -534,7 +569,7 @@ def test_moe_q8_exact_activations_match_f32_path():
 
 # ------------------------------------------------------------------ strided x and dst
 
-@pytest.mark.parametrize("plan", [None, "0,2,1,1", "0,2,3,2", "1,2,1", "1,4,3"])
+@pytest.mark.parametrize("plan", [None, "0,2,1,1", "0,2,3,2", "1,2,1", "1,4,3", "2,2,1", "2,4,3"])
 @pytest.mark.parametrize("qt", ["q4_k", "f32"])
 def test_strided_rows_bit_identical(qt, plan, monkeypatch):
     """Row-strided x and dst (qmm_gemm_ex) give bit-identical results to the
@@ -543,7 +578,7 @@ def test_strided_rows_bit_identical(qt, plan, monkeypatch):
     import torch
     import gemv_prefill_decode_amd as qmm
     if plan is not None:
-        if qt == "f32" and plan.count(",") == 3 and plan.endswith(",2"):
+        if qt == "f32" and ((plan.count(",") == 3 and plan.endswith(",2")) or plan.startswith("2,4")):
             pytest.skip("not a plan the library runs for f32 weights")
         monkeypatch.setenv("QMM_MFMA_PLAN", plan)
     m, k = 300, 1024
