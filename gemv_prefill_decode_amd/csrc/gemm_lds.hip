@@ -4,12 +4,13 @@
 // issued NS-1 steps ahead of their use.  No register holds data in flight,
 // so the ring can be deep, and the k loop is a single rolled step.
 //
-// One work group of 4 waves computes a BM x 128 tile of dst (BM = 4*WR
-// weight rows, 128 tokens).  Wave w owns weight rows [w*WR, w*WR + WR) and
-// all 128 tokens.  Per step it decodes its rows' packed bytes from the LDS
+// One work group of 4 waves computes a BM x BNT tile of dst (BM = 4*WR
+// weight rows, BNT = 128 or 256 tokens).  Wave w owns weight rows
+// [w*WR, w*WR + WR) and all the tile's tokens; 256-token tiles halve the
+// decode work per matrix-core op.  Per step it decodes its rows' packed bytes from the LDS
 // stage straight into the A operands of v_mfma_f32_16x16x32_f16 (no decoded
 // weight tile is written back to LDS), reads the B operands (f16 activations)
-// from the stage, and runs (WR/16) x 8 x 2 matrix-core ops with f32
+// from the stage, and runs (WR/16) x (BNT/16) x 2 matrix-core ops with f32
 // accumulators.
 //
 // Operand layout of v_mfma_f32_16x16x32_f16: lane l holds A row l % 16 and B
@@ -35,8 +36,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 namespace lds_ring {
 
-constexpr int BN = 128;          // tokens per tile
-constexpr int B_STAGE = BN * 128;  // bytes of one stage's activations (128 tokens x 64 f16)
 constexpr int LDS_BYTES = 160 * 1024;
 
 // 16-byte chunks one weight row occupies in a stage (a pad chunk where it
@@ -49,8 +48,12 @@ template <> struct Fmt<QT_Q4_K> { static constexpr int CPR = 3; };   // header 1
 template <> struct Fmt<QT_Q6_K> { static constexpr int CPR = 9; };   // ql 32, qh 32, scales+d 18, pad
 template <> struct Fmt<QT_NVFP4> { static constexpr int CPR = 3; };  // 36 B group
 
-template <int QT, int WR> struct Geo {
+// KG k groups of 4 waves: group g computes the steps s0 + g, s0 + g + KG,
+// ... of the item, so a CU holding one work group runs KG waves per SIMD.
+// The ring holds NS stages, KG per round of steps.
+template <int QT, int WR, int BNT, int KG> struct Geo {
     static constexpr int BM = 4 * WR;
+    static constexpr int B_STAGE = BNT * 128;  // one stage's activations (BNT tokens x 64 f16)
     static constexpr int CPR = Fmt<QT>::CPR;
     static constexpr int A_ROWS_CHUNKS = BM * CPR;
     // the A loads of a stage cover whole rounds of 4 waves x 64 chunks; the
@@ -58,12 +61,15 @@ template <int QT, int WR> struct Geo {
     static constexpr int A_CHUNKS = (A_ROWS_CHUNKS + 255) / 256 * 256;
     static constexpr int A_STAGE = A_CHUNKS * 16;
     static constexpr int STAGE = A_STAGE + B_STAGE;
-    static constexpr int NS_FIT = LDS_BYTES / STAGE;
-    static constexpr int NS = NS_FIT > 4 ? 4 : NS_FIT;
+    static constexpr int NR_FIT = LDS_BYTES / (KG * STAGE);     // rounds of KG stages that fit
+    static constexpr int NR_MAX = KG == 1 ? (BNT == 128 ? 4 : 3) : 3;
+    static constexpr int NR = NR_FIT > NR_MAX ? NR_MAX : NR_FIT;
+    static constexpr int NS = NR * KG;
     static constexpr int DA = A_CHUNKS / 256;  // A loads per wave per step (64 chunks each)
-    static constexpr int DB = 4;               // B loads per wave per step
-    static_assert(NS >= 3, "the ring needs at least 3 stages");
-    static_assert((NS - 2) * (DA + DB) <= 63, "vmcnt range");
+    static constexpr int DB = BNT / 32;        // B loads per wave per step
+    // runnable: a ring of at least 2 rounds, its waits within vmcnt's range,
+    // and (KG = 2) room for group 1's accumulators in the ring's LDS
+    static constexpr bool OK = NR >= 2 && (NR - 2) * (DA + DB) <= 63 && (KG == 1 || NS * STAGE >= BM * BNT * 4);
 };
 
 // k of slot s = 32*ks + 8*g + i of step kt (see the file comment).
@@ -314,17 +320,19 @@ __global__ __launch_bounds__(256) void x16_slot_kernel(uint16_t* __restrict__ x1
 // weight-row tile fastest (as in the other prefill kernels).  Item z covers
 // steps [z*sps, min(nk, (z+1)*sps)); with n_split > 1 it writes its partial
 // tile to partial + z*splitk_stride(n, m), summed by splitk_sum_kernel.
-template <int QT, int WR>
-__global__ __launch_bounds__(256, 1) void gemm_lds_kernel(float* __restrict__ dst, const uint8_t* __restrict__ w,
-                                                          const uint16_t* __restrict__ x16, int m, int k, int n,
-                                                          int rb, int kp, int n_mb, int n_nb, int n_split, int sps,
-                                                          float* __restrict__ partial, int ldd) {
-    using G = lds_ring::Geo<QT, WR>;
-    constexpr int BM = G::BM, BN = lds_ring::BN, CPR = G::CPR, NS = G::NS, DA = G::DA, DB = G::DB;
-    constexpr int RI = WR / 16;  // 16-row blocks per wave
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * G::STAGE];
+template <int QT, int WR, int BNT, int KG>
+__global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict__ dst, const uint8_t* __restrict__ w,
+                                                               const uint16_t* __restrict__ x16, int m, int k, int n,
+                                                               int rb, int kp, int n_mb, int n_nb, int n_split,
+                                                               int sps, float* __restrict__ partial, int ldd) {
+    using G = lds_ring::Geo<QT, WR, BNT, KG>;
+    static_assert(G::OK, "no LDS ring of this shape fits");
+    constexpr int BM = G::BM, BN = BNT, CPR = G::CPR, NR = G::NR, DA = G::DA, DB = G::DB;
+    constexpr int RI = WR / 16, NJ = BN / 16;  // 16-row and 16-token blocks per wave
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[G::NS * G::STAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int tid = threadIdx.x, lane = tid & 63, wave_all = wave_id();
+    const int grp = KG == 1 ? 0 : wave_all >> 2, wave = wave_all & 3;  // k group, wave in the group
     const int r16 = lane & 15, g = lane >> 4;
 
     const int T = n_mb * n_nb, NI = T * n_split, L = blockIdx.x;
@@ -344,8 +352,9 @@ __global__ __launch_bounds__(256, 1) void gemm_lds_kernel(float* __restrict__ ds
     const int s0 = z * sps;
     const int nk = min(nk_all, s0 + sps);
 
-    // This lane's chunks of the buffer-to-LDS loads: A load u covers chunks
-    // (wave*DA + u)*64 + lane, B load u chunks (wave*DB + u)*64 + lane.
+    // This lane's chunks of the buffer-to-LDS loads of its group's stages:
+    // A load u covers chunks (wave*DA + u)*64 + lane, B load u chunks
+    // (wave*DB + u)*64 + lane.
     uint32_t a_rowoff[DA], a_dead[DA];
     int a_c[DA];
 #pragma unroll
@@ -359,15 +368,15 @@ __global__ __launch_bounds__(256, 1) void gemm_lds_kernel(float* __restrict__ ds
         // offsets get bit 31 (past every window)
         a_dead[u] = (q >= G::A_ROWS_CHUNKS || (QT == QT_Q6_K && c == 8)) ? OOB_OFF : 0u;
     }
-    uint32_t b_off[DB];
-#pragma unroll
-    for (int u = 0; u < DB; ++u) {
-        const int q = (wave * DB + u) * 64 + lane;
-        const int t = q >> 3, p = q & 7;
-        b_off[u] = (uint32_t)t * (uint32_t)kp * 2u + 16u * (uint32_t)(p ^ (t & 7));
-    }
-    auto issue = [&](int kt, int stg) {
-        uint8_t* sa = lds + stg * G::STAGE;
+    // B load u: token t = 8*(wave*DB + u) + lane/8, physical chunk lane % 8
+    // holding logical chunk (lane % 8) ^ (t % 8); the per-load part of the
+    // offset is wave-uniform (a scalar offset)
+    const uint32_t b_off0 = (uint32_t)(8 * wave * DB + (lane >> 3)) * (uint32_t)kp * 2u +
+                            16u * (uint32_t)((lane & 7) ^ ((lane >> 3) & 7));
+    // round r: group grp's step s0 + KG*r + grp into stage KG*slot + grp
+    auto issue = [&](int r, int slot) {
+        const int kt = s0 + KG * r + grp;
+        uint8_t* sa = lds + (KG * slot + grp) * G::STAGE;
         uint8_t* sb = sa + G::A_STAGE;
         // steps past the item's end load zeros (bit 31: past every window)
         const uint32_t dead = kt < nk ? 0u : OOB_OFF;
@@ -378,66 +387,122 @@ __global__ __launch_bounds__(256, 1) void gemm_lds_kernel(float* __restrict__ ds
         }
 #pragma unroll
         for (int u = 0; u < DB; ++u) {
-            const uint32_t off = (b_off[u] + 128u * (uint32_t)kt) | dead;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(sb + (wave * DB + u) * 1024), 16, off, 0, 0, 0);
+            const uint32_t soff = kt < nk ? 16u * (uint32_t)u * (uint32_t)kp + 128u * (uint32_t)kt : OOB_OFF;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(sb + (wave * DB + u) * 1024), 16, b_off0, soff,
+                                                     0, 0);
         }
     };
 
-    f32x4 acc[RI][8];
+    f32x4 acc[RI][NJ];
 #pragma unroll
     for (int i = 0; i < RI; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // this lane's weight rows in a stage, and their offsets in the window
     const int rbase = wave * WR + r16;
     const int bsw = 16 * (g ^ (r16 & 7));  // B chunk of slots [8g, 8g+8) of run ks = 0 (ks = 1: ^4 -> +64)
 
 #pragma unroll
-    for (int p = 0; p < NS - 1; ++p) issue(s0 + p, p);
+    for (int p = 0; p < NR - 1; ++p) issue(p, p);
 
+    const int nrounds = (nk - s0 + KG - 1) / KG;
     int cur = 0;
-    for (int kt = s0; kt < nk; ++kt) {
-        // this wave's loads of step kt have landed (later steps' stay in
-        // flight), its LDS reads of step kt-1 are done; then every wave's
-        lds_ring::waitcnt<(NS - 2) * (DA + DB), 0>();
+    for (int r = 0; r < nrounds; ++r) {
+        // this wave's loads of round r have landed (later rounds' stay in
+        // flight), its LDS reads of round r-1 are done; then every wave's
+        lds_ring::waitcnt<(NR - 2) * (DA + DB), 0>();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        // refill the stage step kt-1 used, NS-1 steps ahead
-        issue(kt + NS - 1, cur == 0 ? NS - 1 : cur - 1);
+        // refill the stages round r-1 used, NR-1 rounds ahead
+        issue(r + NR - 1, cur == 0 ? NR - 1 : cur - 1);
 
-        const uint8_t* sa = lds + cur * G::STAGE;
+        const int kt = s0 + KG * r + grp;
+        const uint8_t* sa = lds + (KG * cur + grp) * G::STAGE;
         const uint8_t* sb = sa + G::A_STAGE;
-        f16x8 b0[8], b1[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint8_t* bt = sb + (16 * j + r16) * 128;
-            b0[j] = *(const f16x8*)(bt + bsw);
-            b1[j] = *(const f16x8*)(bt + (bsw ^ 64));
-        }
-#pragma unroll
-        for (int i = 0; i < RI; ++i) {
-            const int r = rbase + 16 * i;
-            f16x8 a0, a1;
-            lds_ring::Dec<QT>::run(sa + r * CPR * 16, rowoff0 + (uint32_t)r * (uint32_t)rb, kt, g, r & 15, a0, a1);
+        cur = cur == NR - 1 ? 0 : cur + 1;
+        if (KG > 1 && kt >= nk) continue;  // this group's step of the last round is past the item's end
+        if constexpr (NJ == 8) {
+            // all B operands of the step in registers, rows decoded one by one
+            f16x8 b0[8], b1[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0[j], acc[i][j], 0, 0, 0);
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1[j], acc[i][j], 0, 0, 0);
+                const uint8_t* bt = sb + (16 * j + r16) * 128;
+                b0[j] = *(const f16x8*)(bt + bsw);
+                b1[j] = *(const f16x8*)(bt + (bsw ^ 64));
+            }
+#pragma unroll
+            for (int i = 0; i < RI; ++i) {
+                const int rr = rbase + 16 * i;
+                f16x8 a0, a1;
+                lds_ring::Dec<QT>::run(sa + rr * CPR * 16, rowoff0 + (uint32_t)rr * (uint32_t)rb, kt, g, rr & 15,
+                                       a0, a1);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1[j], acc[i][j], 0, 0, 0);
+                }
+            }
+        } else {
+            // all rows' A operands in registers, B operands read per token block
+            f16x8 a0[RI], a1[RI];
+#pragma unroll
+            for (int i = 0; i < RI; ++i) {
+                const int rr = rbase + 16 * i;
+                lds_ring::Dec<QT>::run(sa + rr * CPR * 16, rowoff0 + (uint32_t)rr * (uint32_t)rb, kt, g, rr & 15,
+                                       a0[i], a1[i]);
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const uint8_t* bt = sb + (16 * j + r16) * 128;
+                const f16x8 b0 = *(const f16x8*)(bt + bsw);
+                const f16x8 b1 = *(const f16x8*)(bt + (bsw ^ 64));
+#pragma unroll
+                for (int i = 0; i < RI; ++i) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[i], b0, acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1[i], b1, acc[i][j], 0, 0, 0);
+                }
             }
         }
-        cur = cur == NS - 1 ? 0 : cur + 1;
     }
-    // drain the loads past the last step before the work group ends
+    // drain the loads past the last step before the ring is reused or the
+    // work group ends
     lds_ring::waitcnt<0, 0>();
+
+    if constexpr (KG == 2) {
+        // group 1 hands its accumulators to group 0 through the ring's LDS
+        // (value v of lane tid at v*256 + tid); group 0 adds them to its own
+        // (group 0's + group 1's: a fixed order)
+        float* red = reinterpret_cast<float*>(lds);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // every wave is done with the ring
+        asm volatile("" ::: "memory");
+        const int lt = tid & 255;
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 0; i < RI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) red[((i * NJ + j) * 4 + e) * 256 + lt] = acc[i][j][e];
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int i = 0; i < RI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][j][e] += red[((i * NJ + j) * 4 + e) * 256 + lt];
+    }
 
     float* out = n_split > 1 ? partial + (int64_t)z * splitk_stride(n, m) : dst;
     const int64_t ldo = n_split > 1 ? m : ldd;  // partials are dense
 #pragma unroll
     for (int i = 0; i < RI; ++i) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const int64_t mrow = m0 + wave * WR + i * 16 + g * 4;
             const int64_t tok = n0 + j * 16 + r16;
             if (tok < n) {
@@ -447,8 +512,8 @@ __global__ __launch_bounds__(256, 1) void gemm_lds_kernel(float* __restrict__ ds
                     *(f32x4*)p = v;
                 } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (mrow + r < m) p[r] = v[r];
+                    for (int e = 0; e < 4; ++e)
+                        if (mrow + e < m) p[e] = v[e];
                 }
             }
         }
@@ -467,16 +532,49 @@ static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t 
         if (blocks > 8192) blocks = 8192;
         x16_slot_kernel<QT><<<dim3((unsigned)blocks), 256, 0, st>>>(x16, x, (int)n, (int)k, (int)kp, (int)ldx);
     }
-    const int bm = 64 * pl.wm;
-    const int n_mb = (int)((m + bm - 1) / bm), n_nb = (int)((n + 127) / 128);
+    const int bm = 64 * pl.wm, bn = pl.x16 == 3 ? 256 : 128;
+    const int n_mb = (int)((m + bm - 1) / bm), n_nb = (int)((n + bn - 1) / bn);
     const dim3 grid((unsigned)(n_mb * n_nb * pl.n_split));
-    if (QT != QT_F32 && pl.wm == 4)  // f32 rows fit the ring with 128-row tiles only
-        gemm_lds_kernel<QT == QT_F32 ? QT_Q4_K : QT, 64><<<grid, 256, 0, st>>>(dst, w, x16, (int)m, (int)k, (int)n, (int)rb, (int)kp, n_mb,
-                                                      n_nb, pl.n_split, pl.sps, part, (int)ldd);
-    else
-        gemm_lds_kernel<QT, 32><<<grid, 256, 0, st>>>(dst, w, x16, (int)m, (int)k, (int)n, (int)rb, (int)kp, n_mb,
-                                                      n_nb, pl.n_split, pl.sps, part, (int)ldd);
+    // only shapes lds_ring_fits() accepts are planned
+    const int bnt = pl.x16 == 3 ? 256 : 128, wr = pl.x16 == 3 ? 32 : 16 * pl.wm;
+#define QMM_LDS_LAUNCH(WR_, BN_, KG_)                                                                         \
+    if constexpr (lds_ring::Geo<QT, WR_, BN_, KG_>::OK) {                                                     \
+        if (wr == WR_ && bnt == BN_ && pl.kg == KG_)                                                          \
+            gemm_lds_kernel<QT, WR_, BN_, KG_><<<grid, 256 * KG_, 0, st>>>(                                   \
+                dst, w, x16, (int)m, (int)k, (int)n, (int)rb, (int)kp, n_mb, n_nb, pl.n_split, pl.sps, part, \
+                (int)ldd);                                                                                    \
+    }
+    QMM_LDS_LAUNCH(32, 128, 1)
+    QMM_LDS_LAUNCH(64, 128, 1)
+    QMM_LDS_LAUNCH(32, 256, 1)
+    QMM_LDS_LAUNCH(32, 128, 2)
+    QMM_LDS_LAUNCH(32, 256, 2)
+#undef QMM_LDS_LAUNCH
     if (pl.n_split > 1) launch_splitk_sum(dst, part, n * m, splitk_stride(n, m), pl.n_split, m, ldd, st);
+}
+
+template <int QT>
+static bool fits_qt(int wr, int bnt, int kg) {
+    using namespace lds_ring;
+    if (wr == 32 && bnt == 128 && kg == 1) return Geo<QT, 32, 128, 1>::OK;
+    if (wr == 64 && bnt == 128 && kg == 1) return Geo<QT, 64, 128, 1>::OK;
+    if (wr == 32 && bnt == 256 && kg == 1) return Geo<QT, 32, 256, 1>::OK;
+    if (wr == 32 && bnt == 128 && kg == 2) return Geo<QT, 32, 128, 2>::OK;
+    if (wr == 32 && bnt == 256 && kg == 2) return Geo<QT, 32, 256, 2>::OK;
+    return false;
+}
+
+bool lds_ring_fits(int qt, int tile_rows, int tile_tokens, int kg) {
+    const int wr = tile_rows / 4;
+    switch (qt) {
+        case QT_F32: return fits_qt<QT_F32>(wr, tile_tokens, kg);
+        case QT_Q4_0: return fits_qt<QT_Q4_0>(wr, tile_tokens, kg);
+        case QT_Q8_0: return fits_qt<QT_Q8_0>(wr, tile_tokens, kg);
+        case QT_Q4_K: return fits_qt<QT_Q4_K>(wr, tile_tokens, kg);
+        case QT_Q6_K: return fits_qt<QT_Q6_K>(wr, tile_tokens, kg);
+        case QT_NVFP4: return fits_qt<QT_NVFP4>(wr, tile_tokens, kg);
+    }
+    return false;
 }
 
 void launch_gemm_lds(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qt,

@@ -299,22 +299,24 @@ struct FamCost {
     double step_shared_us;
     int per_cu;
 };
-constexpr int N_FAM = 6;
+constexpr int N_FAM = 9;
 constexpr FamCost FAM_COST[N_FAM] = {
     {1.5, 1.04, 2},   // gemm_mfma_kernel, 128 x 128, f32 activations
     {1.6, 1.61, 1},   // gemm_mfma_x16_kernel, 256 x 128
     {1.2, 0.82, 2},   // gemm_mfma_x16_kernel, 128 x 128
     {1.3, 1.3, 1},    // gemm_mfma_kernel with 2 k groups (time per step of the item)
-    {1.0, 1.0, 1},    // gemm_lds_kernel, 128 x 128 (one work group per CU: its LDS ring)
-    {2.0, 2.0, 1},    // gemm_lds_kernel, 256 x 128 (slower than two 128-row tiles everywhere measured)
+    // gemm_lds_kernel (one work group per CU: its LDS ring); 128 x 256 tiles
+    // are priced per step of twice the work
+    {1.0, 0.9, 1},    // 128 x 128
+    {2.0, 2.0, 1},    // 256 x 128 (slower than two 128-row tiles everywhere measured)
+    {1.3, 1.3, 1},    // 128 x 256
+    {0.9, 0.8, 1},    // 128 x 128, 2 k groups
+    {1.1, 1.1, 1},    // 128 x 256, 2 k groups
 };
-// The LDS-ring kernel's step time by format (the decode share of its step):
-// Q6_K's two-field 6-bit codes take a third longer than the others.
-constexpr double LDS_Q6K_FACTOR = 1.35;
-// The LDS-ring kernel is planned for products that fit one round of work
-// groups (it was measured slower than the 128 x 128 f16-activation kernel on
-// the 8B-class products, which take several rounds), and always for f32
-// weights, where it avoids the f32 weight tile's register ring.
+// The LDS-ring kernel's step time by format: Q6_K's two-field 6-bit codes
+// take about a third longer to decode; with 256-token tiles the decode is a
+// smaller share of the step.
+constexpr double LDS_Q6K_FACTOR_128 = 1.3, LDS_Q6K_FACTOR_128_KG2 = 1.15, LDS_Q6K_FACTOR_256 = 1.07;
 constexpr double LAUNCH_US = 3.0;      // a launch with its first loads and its stores
 constexpr double SPLIT_US = 4.0;       // the split sum's launch
 constexpr double X16_US = 3.0;         // the f16 pre-pass launch
@@ -336,16 +338,19 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
     const double x16_us = X16_US + 6.0 * (double)n * (double)k / BYTES_PER_US;
     double best_cost = 1e30;
     for (int fam = 0; fam < N_FAM; ++fam) {
-        const int x16 = fam >= 4 ? 2 : (fam == 1 || fam == 2), wm = fam == 1 || fam == 5 ? 4 : 2,
-                  kg = fam == 3 ? 2 : 1;
+        const int x16 = fam == 6 || fam == 8 ? 3 : (fam >= 4 ? 2 : (fam == 1 || fam == 2)),
+                  wm = fam == 1 || fam == 5 ? 4 : 2, kg = fam == 3 || fam >= 7 ? 2 : 1;
         if (kg == 2 && qt == QT_F32) continue;  // its two register rings of f32 weights exceed 256 VGPRs
         // the LDS ring: whole 64-k steps only, and f32 rows fit it with 128-row tiles only
-        if (x16 == 2 && (k % 64 != 0 || (qt == QT_F32 && wm == 4))) continue;
+        if (x16 >= 2 && (k % 64 != 0 || !lds_ring_fits(qt, 64 * wm, x16 == 3 ? 256 : 128, kg))) continue;
         if (force && (force->x16 != x16 || force->wm != wm || force->kg != kg)) continue;
         const FamCost& fc0 = FAM_COST[fam];
-        const double fmul = x16 == 2 && qt == QT_Q6_K ? LDS_Q6K_FACTOR : 1.0;
+        const double fmul = x16 < 2 || qt != QT_Q6_K
+                                ? 1.0
+                                : (x16 == 3 ? LDS_Q6K_FACTOR_256 : (kg == 2 ? LDS_Q6K_FACTOR_128_KG2 : LDS_Q6K_FACTOR_128));
         const FamCost fc{fc0.step_alone_us * fmul, fc0.step_shared_us * fmul, fc0.per_cu};
-        const int64_t T = ((m + 64 * wm - 1) / (64 * wm)) * ((n + 127) / 128);
+        const int bn = x16 == 3 ? 256 : 128;
+        const int64_t T = ((m + 64 * wm - 1) / (64 * wm)) * ((n + bn - 1) / bn);
         for (int S = 1; S <= 16 && (S == 1 || S <= nk / 2); ++S) {
             const int sps = ((nk + S - 1) / S + 1) & ~1;
             const int se = (nk + sps - 1) / sps;
@@ -353,7 +358,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
             if (force && force->n_split != se) continue;
             const int64_t items = T * se;
             if (items > (int64_t)1 << 30) continue;
-            if (x16 == 2 && !force && qt != QT_F32 && items > num_cu) continue;
+            if (fam == 5 && !force) continue;
             // work groups sharing a CU, time per step, and rounds of them
             const int64_t fill = (items + num_cu - 1) / num_cu;
             const int64_t share = fill < fc.per_cu ? fill : fc.per_cu;
@@ -387,7 +392,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
 void launch_gemm_mfma(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
                       int qt, int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd,
                       hipStream_t st) {
-    if (pl.x16 == 2) {
+    if (pl.x16 >= 2) {
         launch_gemm_lds(dst, w, x, m, k, n, qt, rb, pl, ws, ldx, ldd, st);
         return;
     }
