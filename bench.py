@@ -5,10 +5,11 @@ A step is one pass of the LFM2.5-350M-shaped 512-token prefill: the four
 projection shapes (ffn_gate 4608x1024, ffn_down 1024x4608, conv_in 3072x1024,
 attn_out 1024x1024; the SHAPES of cera wgpu_gemm_bench.rs) in each of the
 five weight formats (f32, q4_0, q8_0, q4_k, q6_k) = 20 GEMMs with n = 512,
-all on the f16 matrix-core path.  Each format's four launches are captured
-once in a HIP graph; a timed step replays the five graphs back to back on
-one stream, with HIP events between them.  `value` is TFLOP/s (2*m*k*n per
-GEMM) over the K timed steps, inputs resident in HBM.
+all on the f16 matrix-core path.  Each format's four calls (with their f16
+pre-pass and k-split sum, where the plan has them) are captured once in a HIP
+graph; a timed step replays the five graphs back to back on one stream, with
+HIP events between them.  `value` is TFLOP/s (2*m*k*n per GEMM) over the K
+timed steps, inputs resident in HBM.
 
 The same JSON line also carries the other half of the metric:
   decode   the GEMV sweep n in {1,4,8,16,32}, q4_k and q6_k at 14336x4096 and
@@ -22,8 +23,10 @@ The same JSON line also carries the other half of the metric:
            on the same values in NVFP4 V2 rows (outputs checked bit-identical
            to V1 before timing); the gate/up also on Q8_1 activations
            (quantization included in the timed launches).
-  roofline the dominant prefill kernel instance: algorithmic flops per launch
-           over its average launch time from the events of the timed region.
+  roofline the dominant format's prefill calls (the largest time per step):
+           algorithmic flops per call over the average call time from the
+           events of the timed region, with the GEMM kernel instance and grid
+           each call runs, and their HBM bytes from the counter profiles.
   cpu_baseline  the CPU oracle over the whole prefill step on the host cores.
 Decode and MoE launches are graph-replayed too (32+ launches per graph).
 
@@ -81,6 +84,16 @@ def traffic_from_profiles(kernel: str):
         return None
     ent = tab.get("kernels", {}).get(kernel)
     return None if not ent else ent.get("bytes_per_launch")
+
+
+def plan_grid_size(plan, m, n):
+    """Work-items of the GEMM kernel a qmm_gemm_plan() result launches (the
+    Grid_Size the profiler records for that dispatch)."""
+    x16, rows, kg, split = plan["x16"], plan["tile_rows"], plan["k_groups"], plan["n_split"]
+    cols = 256 if x16 == 3 else 128
+    threads = 2 * rows if x16 == 1 else 256 * kg
+    groups = -(-m // rows) * -(-n // cols) * split
+    return groups * threads
 
 
 def gen_weights(qt, m, k, buf_id):
@@ -181,34 +194,41 @@ def run_prefill(args, n):
                       "TFLOP/s": round(flops[qt] / mean / 1e12, 1),
                       "frac_mfma_peak": round(flops[qt] / mean / 1e12 / PEAK_F16_TFLOPS, 4)}
     # per-shape times (outside the timed region): each launch graph-replayed alone
+    kern = {}
     for (qt, label, m, k, w) in bufs:
         g = capture([call((qt, label, m, k, w))] * 8)
         t = time_graph(g, 8, 5)
         plan = qmm.gemm_plan(m, k, n, qt, "mfma")
+        kern[(qt, label)] = (qmm.plan_kernel_name(plan, qt), plan_grid_size(plan, m, n))
         per_qt[qt].setdefault("shapes", {})[label] = {
             "us": round(t * 1e6, 2), "TFLOP/s": round(2.0 * m * k * n / t / 1e12, 1),
-            "kernel": qmm.plan_kernel_name(plan, qt), "k_split": plan["n_split"]}
+            "kernel": kern[(qt, label)][0], "grid": kern[(qt, label)][1], "k_split": plan["n_split"]}
         del g
+    # the dominant format (the largest time per step); its four calls, each a
+    # GEMM kernel (plus the f16 pre-pass and the k-split sum where planned)
     dom = max(QTS, key=lambda q: per_qt[q]["us_per_step"])
-    launches = sum(1 for b in bufs if b[0] == dom)
+    calls = [b for b in bufs if b[0] == dom]
+    launches = len(calls)
     avg_launch = per_qt[dom]["us_per_step"] * 1e-6 / launches
     fpl = flops[dom] / launches
     ach = fpl / avg_launch / 1e12
-    kernels = sorted({v["kernel"] for v in per_qt[dom]["shapes"].values()})
+    names = [kern[(dom, label)] for (_, label, _, _, _) in calls]
+    traffic = [traffic_from_profiles(f"{kn}@{grid}") for (kn, grid) in names]
     roofline = {
-        "kernel": " + ".join(f"qmm::{kn}" for kn in kernels) + f" ({dom} weights; per qmm_gemm_ws call)",
+        "kernel": " + ".join(f"qmm::{kn} (grid {grid})" for (kn, grid) in names) +
+                  f" ({dom} weights, the four LFM2 shapes; per qmm_gemm_ws call)",
         "bound": "mfma",
         "achieved": round(ach, 2),
         "peak": PEAK_F16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(ach / PEAK_F16_TFLOPS, 4),
-        "traffic": traffic_from_profiles(kernels[0]) if len(kernels) == 1 else None,
+        # HBM bytes of the GEMM kernels, averaged over the four calls
+        "traffic": round(sum(traffic) / launches) if all(t is not None for t in traffic) else None,
         "avg_launch_us": round(avg_launch * 1e6, 3),
         "launches_per_step": launches,
         "algorithmic_flops_per_launch": fpl,
         "algorithmic_bytes_per_launch": sum(
-            (m * qmm.row_bytes(q, k) + 4 * n * k + 4 * n * m) for (q, _, m, k, _) in bufs
-            if q == dom) / launches,
+            (m * qmm.row_bytes(q, k) + 4 * n * k + 4 * n * m) for (q, _, m, k, _) in calls) / launches,
     }
     return step_flops, wall, per_qt, roofline
 
@@ -485,12 +505,16 @@ def pmc_summary(fetch_csv, write_csv, out_path):
     import collections
 
     def read(path, counter):
+        # per kernel name, and per kernel name @ grid size (one launch shape)
         per = collections.defaultdict(list)
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"].split("(")[0].replace("void ", "").strip()
-            per[name].append(float(r["Counter_Value"]) * 1024.0)
+            v = float(r["Counter_Value"]) * 1024.0
+            per[name].append(v)
+            if r.get("Grid_Size"):
+                per[f"{name}@{r['Grid_Size']}"].append(v)
         return per
 
     fetch, write = read(fetch_csv, "FETCH_SIZE"), read(write_csv, "WRITE_SIZE")

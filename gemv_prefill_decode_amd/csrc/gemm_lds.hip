@@ -324,7 +324,8 @@ template <int QT, int WR, int BNT, int KG>
 __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict__ dst, const uint8_t* __restrict__ w,
                                                                const uint16_t* __restrict__ x16, int m, int k, int n,
                                                                int rb, int kp, int n_mb, int n_nb, int n_split,
-                                                               int sps, float* __restrict__ partial, int ldd) {
+                                                               int sps, float* __restrict__ partial, int ldd,
+                                                               int nb_fast) {
     using G = lds_ring::Geo<QT, WR, BNT, KG>;
     static_assert(G::OK, "no LDS ring of this shape fits");
     constexpr int BM = G::BM, BN = BNT, CPR = G::CPR, NR = G::NR, DA = G::DA, DB = G::DB;
@@ -339,7 +340,12 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
     const int xcd = L & 7, idx = L >> 3, per = NI >> 3, rem = NI & 7;
     const int item = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
     const int z = item / T, tile = item - z * T;
-    const int nb = tile / n_mb, mb = tile - nb * n_mb;
+    // nb_fast: an XCD's run of items holds all token tiles of a few weight
+    // tiles (each weight tile read into one L2), else all weight tiles of a
+    // token tile; the host picks the order with the smaller total of bytes
+    // that several XCDs read
+    const int nb = nb_fast ? tile % n_nb : tile / n_mb;
+    const int mb = nb_fast ? tile / n_nb : tile - nb * n_mb;
     const int64_t m0 = (int64_t)mb * BM, n0 = (int64_t)nb * BN;
 
     int64_t base;
@@ -535,6 +541,12 @@ static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t 
     const int bm = 64 * pl.wm, bn = pl.x16 == 3 ? 256 : 128;
     const int n_mb = (int)((m + bm - 1) / bm), n_nb = (int)((n + bn - 1) / bn);
     const dim3 grid((unsigned)(n_mb * n_nb * pl.n_split));
+    // Item order: with the weight tile fastest, every token tile's XCDs read
+    // all the weights (about n_nb reads of w in all); with the token tile
+    // fastest, every XCD reads about all the activations (min(8, n_mb)
+    // reads of them).  Take the order that reads fewer bytes.
+    const double w_bytes = (double)m * (double)rb, x_bytes = (double)n * (double)kp * 2.0;
+    const int nb_fast = (double)(n_nb - 1) * w_bytes > (double)((n_mb < 8 ? n_mb : 8) - 1) * x_bytes;
     // only shapes lds_ring_fits() accepts are planned
     const int bnt = pl.x16 == 3 ? 256 : 128, wr = pl.x16 == 3 ? 32 : 16 * pl.wm;
 #define QMM_LDS_LAUNCH(WR_, BN_, KG_)                                                                         \
@@ -542,7 +554,7 @@ static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t 
         if (wr == WR_ && bnt == BN_ && pl.kg == KG_)                                                          \
             gemm_lds_kernel<QT, WR_, BN_, KG_><<<grid, 256 * KG_, 0, st>>>(                                   \
                 dst, w, x16, (int)m, (int)k, (int)n, (int)rb, (int)kp, n_mb, n_nb, pl.n_split, pl.sps, part, \
-                (int)ldd);                                                                                    \
+                (int)ldd, nb_fast);                                                                           \
     }
     QMM_LDS_LAUNCH(32, 128, 1)
     QMM_LDS_LAUNCH(64, 128, 1)
