@@ -51,9 +51,11 @@ template <> struct Fmt<QT_NVFP4> { static constexpr int CPR = 3; };  // 36 B gro
 // KG k groups of 4 waves: group g computes the steps s0 + g, s0 + g + KG,
 // ... of the item, so a CU holding one work group runs KG waves per SIMD.
 // The ring holds NS stages, KG per round of steps.
-template <int QT, int WR, int BNT, int KG> struct Geo {
+template <int QT, int WR, int BNT, int KG, bool XF = false> struct Geo {
     static constexpr int BM = 4 * WR;
-    static constexpr int B_STAGE = BNT * 128;  // one stage's activations (BNT tokens x 64 f16)
+    // one stage's activations: BNT tokens x 64 f16, or x 64 f32 (XF: read
+    // straight from the f32 activations, rounded to f16 as they are read)
+    static constexpr int B_STAGE = BNT * (XF ? 256 : 128);
     static constexpr int CPR = Fmt<QT>::CPR;
     static constexpr int A_ROWS_CHUNKS = BM * CPR;
     // the A loads of a stage cover whole rounds of 4 waves x 64 chunks; the
@@ -66,7 +68,7 @@ template <int QT, int WR, int BNT, int KG> struct Geo {
     static constexpr int NR = NR_FIT > NR_MAX ? NR_MAX : NR_FIT;
     static constexpr int NS = NR * KG;
     static constexpr int DA = A_CHUNKS / 256;  // A loads per wave per step (64 chunks each)
-    static constexpr int DB = BNT / 32;        // B loads per wave per step
+    static constexpr int DB = B_STAGE / 4096;  // B loads per wave per step
     // runnable: a ring of at least 2 rounds, its waits within vmcnt's range,
     // and (KG = 2) room for group 1's accumulators in the ring's LDS
     static constexpr bool OK = NR >= 2 && (NR - 2) * (DA + DB) <= 63 && (KG == 1 || NS * STAGE >= BM * BNT * 4);
@@ -124,6 +126,25 @@ __device__ __forceinline__ f16x8 frag4(uint32_t a, uint32_t b, uint32_t c, uint3
 __device__ __forceinline__ f16x2 mpair(uint32_t v, int b0) {
     const uint32_t bits = ((v >> (8 * b0)) & 0xFFu) | (((v >> (8 * b0 + 8)) & 0xFFu) << 16) | 0x64006400u;
     return __builtin_bit_cast(f16x2, bits);
+}
+
+// In-step slot of the first of the 4 consecutive k in f32 chunk c (slots
+// 4c .. 4c+3) and its k offset from the step's base k (step_k0 below): every
+// format's 64 slots are runs of 4 (or 8) consecutive k.
+template <int QT>
+__device__ __forceinline__ int chunk_rel_k(int c) {
+    const int ks = c >> 3, g = (c >> 1) & 3, i = 4 * (c & 1);
+    if constexpr (QT == QT_Q6_K)
+        return 64 * ks + 8 * g + i;
+    else
+        return slot_k<QT>(0, ks, g, i);
+}
+template <int QT>
+__device__ __forceinline__ int step_k0(int kt) {
+    if constexpr (QT == QT_Q6_K)
+        return 256 * (kt >> 2) + 128 * ((kt >> 1) & 1) + 32 * (kt & 1);
+    else
+        return 64 * kt;
 }
 
 // ------------------------------------------------------------ row decoders
@@ -320,13 +341,17 @@ __global__ __launch_bounds__(256) void x16_slot_kernel(uint16_t* __restrict__ x1
 // weight-row tile fastest (as in the other prefill kernels).  Item z covers
 // steps [z*sps, min(nk, (z+1)*sps)); with n_split > 1 it writes its partial
 // tile to partial + z*splitk_stride(n, m), summed by splitk_sum_kernel.
-template <int QT, int WR, int BNT, int KG>
+// XF: the activations are the caller's f32 rows x (ldx floats apart), loaded
+// into the ring as f32 and rounded to f16 (nearest even) as the operands are
+// read, instead of the f16 pre-pass's rows x16 (kp halves apart).
+template <int QT, int WR, int BNT, int KG, bool XF>
 __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict__ dst, const uint8_t* __restrict__ w,
-                                                               const uint16_t* __restrict__ x16, int m, int k, int n,
-                                                               int rb, int kp, int n_mb, int n_nb, int n_split,
+                                                               const uint16_t* __restrict__ x16,
+                                                               const float* __restrict__ x, int ldx, int m, int k,
+                                                               int n, int rb, int kp, int n_mb, int n_nb, int n_split,
                                                                int sps, float* __restrict__ partial, int ldd,
                                                                int nb_fast) {
-    using G = lds_ring::Geo<QT, WR, BNT, KG>;
+    using G = lds_ring::Geo<QT, WR, BNT, KG, XF>;
     static_assert(G::OK, "no LDS ring of this shape fits");
     constexpr int BM = G::BM, BN = BNT, CPR = G::CPR, NR = G::NR, DA = G::DA, DB = G::DB;
     constexpr int RI = WR / 16, NJ = BN / 16;  // 16-row and 16-token blocks per wave
@@ -351,7 +376,10 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
     int64_t base;
     const rsrc_t wr = row_window(w, m0, BM, m, rb, base);
     const int ntok = (int)imin64(BN, n - n0);
-    const rsrc_t xr = make_rsrc(x16 + n0 * kp, (uint32_t)ntok * (uint32_t)kp * 2u);
+    // token rows: x16 rows of kp halves, or x rows ldx floats apart (the
+    // window ends with the last row's k floats)
+    const rsrc_t xr = XF ? make_rsrc(x + n0 * ldx, ((uint32_t)(ntok - 1) * (uint32_t)ldx + (uint32_t)k) * 4u)
+                         : make_rsrc(x16 + n0 * kp, (uint32_t)ntok * (uint32_t)kp * 2u);
     const uint32_t rowoff0 = (uint32_t)(m0 * rb - base);  // byte offset of the tile's first row
 
     const int nk_all = k >> 6;
@@ -374,11 +402,16 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
         // offsets get bit 31 (past every window)
         a_dead[u] = (q >= G::A_ROWS_CHUNKS || (QT == QT_Q6_K && c == 8)) ? OOB_OFF : 0u;
     }
-    // B load u: token t = 8*(wave*DB + u) + lane/8, physical chunk lane % 8
-    // holding logical chunk (lane % 8) ^ (t % 8); the per-load part of the
-    // offset is wave-uniform (a scalar offset)
+    // f16 rows: B load u covers token t = 8*(wave*DB + u) + lane/8, physical
+    // chunk lane % 8 holding logical chunk (lane % 8) ^ (t % 8); the per-load
+    // part of the offset is wave-uniform (a scalar offset).
+    // f32 rows (XF): token t = 4*(wave*DB + u) + lane/16, physical chunk
+    // lane % 16 holding logical chunk c = (lane % 16) ^ (t % 16), the 4 f32
+    // of slots 4c .. 4c+3.
     const uint32_t b_off0 = (uint32_t)(8 * wave * DB + (lane >> 3)) * (uint32_t)kp * 2u +
                             16u * (uint32_t)((lane & 7) ^ ((lane >> 3) & 7));
+    // (XF offsets are computed per load in issue(): with a per-lane array of
+    // them, hipcc's host pass failed to instantiate the XF kernels)
     // round r: group grp's step s0 + KG*r + grp into stage KG*slot + grp
     auto issue = [&](int r, int slot) {
         const int kt = s0 + KG * r + grp;
@@ -393,9 +426,18 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
         }
 #pragma unroll
         for (int u = 0; u < DB; ++u) {
-            const uint32_t soff = kt < nk ? 16u * (uint32_t)u * (uint32_t)kp + 128u * (uint32_t)kt : OOB_OFF;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(sb + (wave * DB + u) * 1024), 16, b_off0, soff,
-                                                     0, 0);
+            if constexpr (XF) {
+                const uint32_t soff = kt < nk ? 4u * (uint32_t)lds_ring::step_k0<QT>(kt) : OOB_OFF;
+                const int t = 4 * (wave * DB + u) + (lane >> 4);
+                const int c = (lane & 15) ^ (t & 15);
+                const uint32_t voff = ((uint32_t)t * (uint32_t)ldx + (uint32_t)lds_ring::chunk_rel_k<QT>(c)) * 4u;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(sb + (wave * DB + u) * 1024), 16, voff,
+                                                         soff, 0, 0);
+            } else {
+                const uint32_t soff = kt < nk ? 16u * (uint32_t)u * (uint32_t)kp + 128u * (uint32_t)kt : OOB_OFF;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(sb + (wave * DB + u) * 1024), 16, b_off0,
+                                                         soff, 0, 0);
+            }
         }
     };
 
@@ -408,6 +450,18 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
     // this lane's weight rows in a stage, and their offsets in the window
     const int rbase = wave * WR + r16;
     const int bsw = 16 * (g ^ (r16 & 7));  // B chunk of slots [8g, 8g+8) of run ks = 0 (ks = 1: ^4 -> +64)
+    // the B operand of token row bt for run ks: 8 f16, or (XF) the f32
+    // chunks 8ks + 2g and 8ks + 2g + 1 (at chunk ^ r16) rounded to f16
+    auto bfrag = [&](const uint8_t* bt, int ks) -> f16x8 {
+        if constexpr (XF) {
+            const f32x4 p = *(const f32x4*)(bt + 16 * ((8 * ks + 2 * g) ^ r16));
+            const f32x4 q = *(const f32x4*)(bt + 16 * ((8 * ks + 2 * g + 1) ^ r16));
+            return lds_ring::frag4(pack_f2h(p.x, p.y), pack_f2h(p.z, p.w), pack_f2h(q.x, q.y), pack_f2h(q.z, q.w));
+        } else {
+            return *(const f16x8*)(bt + (ks ? bsw ^ 64 : bsw));
+        }
+    };
+    constexpr int BROW = XF ? 256 : 128;  // bytes of one token row of a stage
 
 #pragma unroll
     for (int p = 0; p < NR - 1; ++p) issue(p, p);
@@ -434,9 +488,9 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
             f16x8 b0[8], b1[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const uint8_t* bt = sb + (16 * j + r16) * 128;
-                b0[j] = *(const f16x8*)(bt + bsw);
-                b1[j] = *(const f16x8*)(bt + (bsw ^ 64));
+                const uint8_t* bt = sb + (16 * j + r16) * BROW;
+                b0[j] = bfrag(bt, 0);
+                b1[j] = bfrag(bt, 1);
             }
 #pragma unroll
             for (int i = 0; i < RI; ++i) {
@@ -461,9 +515,9 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
             }
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const uint8_t* bt = sb + (16 * j + r16) * 128;
-                const f16x8 b0 = *(const f16x8*)(bt + bsw);
-                const f16x8 b1 = *(const f16x8*)(bt + (bsw ^ 64));
+                const uint8_t* bt = sb + (16 * j + r16) * BROW;
+                const f16x8 b0 = bfrag(bt, 0);
+                const f16x8 b1 = bfrag(bt, 1);
 #pragma unroll
                 for (int i = 0; i < RI; ++i) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[i], b0, acc[i][j], 0, 0, 0);
@@ -530,9 +584,10 @@ template <int QT>
 static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k, int64_t n,
                           int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd, hipStream_t st) {
     const int64_t kp = x16_row_halves(k);
+    const bool xf = pl.x16 == 4;  // f32 activations straight into the ring: no pre-pass
     uint16_t* x16 = (uint16_t*)ws;
-    float* part = (float*)((uint8_t*)ws + x16_bytes(n, k));
-    {
+    float* part = xf ? (float*)ws : (float*)((uint8_t*)ws + x16_bytes(n, k));
+    if (!xf) {
         const int64_t total = n * (kp / 8);
         int64_t blocks = (total + 255) / 256;
         if (blocks > 8192) blocks = 8192;
@@ -545,46 +600,50 @@ static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t 
     // all the weights (about n_nb reads of w in all); with the token tile
     // fastest, every XCD reads about all the activations (min(8, n_mb)
     // reads of them).  Take the order that reads fewer bytes.
-    const double w_bytes = (double)m * (double)rb, x_bytes = (double)n * (double)kp * 2.0;
+    const double w_bytes = (double)m * (double)rb, x_bytes = (double)n * (double)kp * (xf ? 4.0 : 2.0);
     const int nb_fast = (double)(n_nb - 1) * w_bytes > (double)((n_mb < 8 ? n_mb : 8) - 1) * x_bytes;
     // only shapes lds_ring_fits() accepts are planned
     const int bnt = pl.x16 == 3 ? 256 : 128, wr = pl.x16 == 3 ? 32 : 16 * pl.wm;
-#define QMM_LDS_LAUNCH(WR_, BN_, KG_)                                                                         \
-    if constexpr (lds_ring::Geo<QT, WR_, BN_, KG_>::OK) {                                                     \
-        if (wr == WR_ && bnt == BN_ && pl.kg == KG_)                                                          \
-            gemm_lds_kernel<QT, WR_, BN_, KG_><<<grid, 256 * KG_, 0, st>>>(                                   \
-                dst, w, x16, (int)m, (int)k, (int)n, (int)rb, (int)kp, n_mb, n_nb, pl.n_split, pl.sps, part, \
-                (int)ldd, nb_fast);                                                                           \
+#define QMM_LDS_LAUNCH(WR_, BN_, KG_, XF_)                                                                      \
+    if constexpr (lds_ring::Geo<QT, WR_, BN_, KG_, XF_>::OK) {                                                  \
+        if (wr == WR_ && bnt == BN_ && pl.kg == KG_ && xf == XF_)                                               \
+            gemm_lds_kernel<QT, WR_, BN_, KG_, XF_><<<grid, 256 * KG_, 0, st>>>(                                \
+                dst, w, x16, x, (int)ldx, (int)m, (int)k, (int)n, (int)rb, (int)kp, n_mb, n_nb, pl.n_split,     \
+                pl.sps, part, (int)ldd, nb_fast);                                                               \
     }
-    QMM_LDS_LAUNCH(32, 128, 1)
-    QMM_LDS_LAUNCH(64, 128, 1)
-    QMM_LDS_LAUNCH(32, 256, 1)
-    QMM_LDS_LAUNCH(32, 128, 2)
-    QMM_LDS_LAUNCH(32, 256, 2)
+    QMM_LDS_LAUNCH(32, 128, 1, false)
+    QMM_LDS_LAUNCH(64, 128, 1, false)
+    QMM_LDS_LAUNCH(32, 256, 1, false)
+    QMM_LDS_LAUNCH(32, 128, 2, false)
+    QMM_LDS_LAUNCH(32, 256, 2, false)
+    QMM_LDS_LAUNCH(32, 128, 1, true)
+    QMM_LDS_LAUNCH(32, 128, 2, true)
 #undef QMM_LDS_LAUNCH
     if (pl.n_split > 1) launch_splitk_sum(dst, part, n * m, splitk_stride(n, m), pl.n_split, m, ldd, st);
 }
 
 template <int QT>
-static bool fits_qt(int wr, int bnt, int kg) {
+static bool fits_qt(int wr, int bnt, int kg, bool xf) {
     using namespace lds_ring;
-    if (wr == 32 && bnt == 128 && kg == 1) return Geo<QT, 32, 128, 1>::OK;
-    if (wr == 64 && bnt == 128 && kg == 1) return Geo<QT, 64, 128, 1>::OK;
-    if (wr == 32 && bnt == 256 && kg == 1) return Geo<QT, 32, 256, 1>::OK;
-    if (wr == 32 && bnt == 128 && kg == 2) return Geo<QT, 32, 128, 2>::OK;
-    if (wr == 32 && bnt == 256 && kg == 2) return Geo<QT, 32, 256, 2>::OK;
+    if (!xf && wr == 32 && bnt == 128 && kg == 1) return Geo<QT, 32, 128, 1>::OK;
+    if (!xf && wr == 64 && bnt == 128 && kg == 1) return Geo<QT, 64, 128, 1>::OK;
+    if (!xf && wr == 32 && bnt == 256 && kg == 1) return Geo<QT, 32, 256, 1>::OK;
+    if (!xf && wr == 32 && bnt == 128 && kg == 2) return Geo<QT, 32, 128, 2>::OK;
+    if (!xf && wr == 32 && bnt == 256 && kg == 2) return Geo<QT, 32, 256, 2>::OK;
+    if (xf && wr == 32 && bnt == 128 && kg == 1) return Geo<QT, 32, 128, 1, true>::OK;
+    if (xf && wr == 32 && bnt == 128 && kg == 2) return Geo<QT, 32, 128, 2, true>::OK;
     return false;
 }
 
-bool lds_ring_fits(int qt, int tile_rows, int tile_tokens, int kg) {
+bool lds_ring_fits(int qt, int tile_rows, int tile_tokens, int kg, bool xf) {
     const int wr = tile_rows / 4;
     switch (qt) {
-        case QT_F32: return fits_qt<QT_F32>(wr, tile_tokens, kg);
-        case QT_Q4_0: return fits_qt<QT_Q4_0>(wr, tile_tokens, kg);
-        case QT_Q8_0: return fits_qt<QT_Q8_0>(wr, tile_tokens, kg);
-        case QT_Q4_K: return fits_qt<QT_Q4_K>(wr, tile_tokens, kg);
-        case QT_Q6_K: return fits_qt<QT_Q6_K>(wr, tile_tokens, kg);
-        case QT_NVFP4: return fits_qt<QT_NVFP4>(wr, tile_tokens, kg);
+        case QT_F32: return fits_qt<QT_F32>(wr, tile_tokens, kg, xf);
+        case QT_Q4_0: return fits_qt<QT_Q4_0>(wr, tile_tokens, kg, xf);
+        case QT_Q8_0: return fits_qt<QT_Q8_0>(wr, tile_tokens, kg, xf);
+        case QT_Q4_K: return fits_qt<QT_Q4_K>(wr, tile_tokens, kg, xf);
+        case QT_Q6_K: return fits_qt<QT_Q6_K>(wr, tile_tokens, kg, xf);
+        case QT_NVFP4: return fits_qt<QT_NVFP4>(wr, tile_tokens, kg, xf);
     }
     return false;
 }

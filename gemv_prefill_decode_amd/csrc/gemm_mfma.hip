@@ -299,7 +299,7 @@ struct FamCost {
     double step_shared_us;
     int per_cu;
 };
-constexpr int N_FAM = 9;
+constexpr int N_FAM = 11;
 constexpr FamCost FAM_COST[N_FAM] = {
     {1.5, 1.04, 2},   // gemm_mfma_kernel, 128 x 128, f32 activations
     {1.6, 1.61, 1},   // gemm_mfma_x16_kernel, 256 x 128
@@ -312,6 +312,11 @@ constexpr FamCost FAM_COST[N_FAM] = {
     {1.3, 1.3, 1},    // 128 x 256
     {0.9, 0.8, 1},    // 128 x 128, 2 k groups
     {1.1, 1.1, 1},    // 128 x 256, 2 k groups
+    // the same with 128 x 128 tiles on the f32 activations (no pre-pass;
+    // more VALU and LDS reads per step for the rounding, which one k group
+    // per CU does not hide)
+    {1.4, 1.3, 1},    // 1 k group
+    {0.95, 0.85, 1},  // 2 k groups
 };
 // The LDS-ring kernel's step time by format: Q6_K's two-field 6-bit codes
 // take about a third longer to decode; with 256-token tiles the decode is a
@@ -338,11 +343,11 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
     const double x16_us = X16_US + 6.0 * (double)n * (double)k / BYTES_PER_US;
     double best_cost = 1e30;
     for (int fam = 0; fam < N_FAM; ++fam) {
-        const int x16 = fam == 6 || fam == 8 ? 3 : (fam >= 4 ? 2 : (fam == 1 || fam == 2)),
-                  wm = fam == 1 || fam == 5 ? 4 : 2, kg = fam == 3 || fam >= 7 ? 2 : 1;
+        const int x16 = fam >= 9 ? 4 : (fam == 6 || fam == 8 ? 3 : (fam >= 4 ? 2 : (fam == 1 || fam == 2))),
+                  wm = fam == 1 || fam == 5 ? 4 : 2, kg = fam == 3 || fam == 7 || fam == 8 || fam == 10 ? 2 : 1;
         if (kg == 2 && qt == QT_F32) continue;  // its two register rings of f32 weights exceed 256 VGPRs
         // the LDS ring: whole 64-k steps only, and f32 rows fit it with 128-row tiles only
-        if (x16 >= 2 && (k % 64 != 0 || !lds_ring_fits(qt, 64 * wm, x16 == 3 ? 256 : 128, kg))) continue;
+        if (x16 >= 2 && (k % 64 != 0 || !lds_ring_fits(qt, 64 * wm, x16 == 3 ? 256 : 128, kg, x16 == 4))) continue;
         if (force && (force->x16 != x16 || force->wm != wm || force->kg != kg)) continue;
         const FamCost& fc0 = FAM_COST[fam];
         const double fmul = x16 < 2 || qt != QT_Q6_K
@@ -371,7 +376,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
             // without a pre-pass (whose time the model knows least well)
             const double cost = (LAUNCH_US + rounds * sps * step_t +
                                  (se > 1 ? SPLIT_US + (2.0 * se + 1.0) * out_bytes / BYTES_PER_US : 0.0) +
-                                 (x16 ? x16_us : 0.0)) *
+                                 (x16 >= 1 && x16 <= 3 ? x16_us : 0.0)) *
                                 (x16 == 1 ? X16_MARGIN : 1.0);
             if (cost < best_cost) {
                 best_cost = cost;
@@ -383,7 +388,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
             }
         }
     }
-    best.ws_bytes = (best.x16 ? x16_bytes(n, k) : 0) +
+    best.ws_bytes = (best.x16 >= 1 && best.x16 <= 3 ? x16_bytes(n, k) : 0) +
                     (best.n_split > 1 ? (int64_t)best.n_split * splitk_stride(n, m) * 4 : 0);
     if (best.ws_bytes == 0) best.ws_bytes = 256;  // a plan that uses no workspace still takes one
     return best;

@@ -29,8 +29,10 @@ void launch_gemv(float* dst, const void* w, const float* x, int64_t m, int64_t k
 // rounded to f16 by a pre-pass into the workspace).  x16 = 2: gemm_lds.hip's
 // kernel ((64*wm) x 128 tiles; f16 activations from its own pre-pass, weight
 // bytes and activations streamed through an LDS ring; k % 64 == 0 only);
-// x16 = 3: the same kernel with 128 x 256 tiles (wm = 2).  kg = 2 on
-// x16 >= 2: two groups of 4 waves take alternate k steps of each tile.
+// x16 = 3: the same kernel with 128 x 256 tiles (wm = 2).  x16 = 4: the
+// same kernel with 128 x 128 tiles reading the f32 activations into its
+// ring and rounding them as it reads (no pre-pass, no f16 workspace).  kg =
+// 2 on x16 >= 2: two groups of 4 waves take alternate k steps of each tile.
 // Any of them may split k into n_split ranges of sps steps (64 k each; sps
 // even) whose partial results go to the workspace (after the f16
 // activations), summed by a second kernel.
@@ -81,7 +83,7 @@ void launch_gemm_lds(float* dst, const void* w, const float* x, int64_t m, int64
 // Whether the LDS ring of gemm_lds.hip holds tiles of tile_rows x
 // tile_tokens for format qt with kg k groups (its stages, or the k-group
 // reduction, must fit the 160 KB of LDS).
-bool lds_ring_fits(int qt, int tile_rows, int tile_tokens, int kg);
+bool lds_ring_fits(int qt, int tile_rows, int tile_tokens, int kg, bool xf);
 
 // dst[(i / m)*ldd + i % m] = sum over z < n_split of part[z*zstride + i], in
 // order of z, i < count.

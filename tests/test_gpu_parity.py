@@ -144,13 +144,14 @@ def test_identity_activations_mfma(qt):
 # The LDS-ring kernel assigns k to operand slots per format and lays the f16
 # activations out in the same order; identity activations and exact inputs
 # pin that mapping bit for bit for both tile heights.
-@pytest.mark.parametrize("plan", ["2,2,1", "2,4,1", "2,4,2", "3,2,1", "3,2,2", "2,2,1,2", "2,2,2,2", "3,2,1,2"])
+@pytest.mark.parametrize("plan", ["2,2,1", "2,4,1", "2,4,2", "3,2,1", "3,2,2", "2,2,1,2", "2,2,2,2", "3,2,1,2",
+                                  "4,2,1", "4,2,2", "4,2,1,2"])
 @pytest.mark.parametrize("qt", QTS)
 def test_lds_ring_identity_and_exact(qt, plan, monkeypatch):
     import gemv_prefill_decode_amd as qmm
     if qt == "f32" and (plan.startswith("2,4") or plan.count(",") == 3):
         pytest.skip("not a plan the library runs for f32 weights")
-    if plan == "3,2,1,2" and qt in ("q6_k", "q8_0"):
+    if plan in ("3,2,1,2", "4,2,1,2") and qt in ("q6_k", "q8_0"):
         pytest.skip("its LDS ring does not fit 160 KB")
     monkeypatch.setenv("QMM_MFMA_PLAN", plan)
     m, k = 300, 512
@@ -409,7 +410,8 @@ def test_split_k_shared_workspace_growing_tile_count():
 # (m, n not multiples of any tile; k with a partial split): x16, tile rows
 # (wm*64), k splits, k groups.
 FORCED_PLANS = ["0,2,1,1", "0,2,3,1", "0,2,1,2", "0,2,3,2", "1,2,1", "1,2,3", "1,4,1", "1,4,3",
-                "2,2,1", "2,2,3", "2,4,1", "2,4,3", "3,2,1", "3,2,3", "2,2,1,2", "2,2,3,2", "3,2,1,2", "3,2,3,2"]
+                "2,2,1", "2,2,3", "2,4,1", "2,4,3", "3,2,1", "3,2,3", "2,2,1,2", "2,2,3,2", "3,2,1,2", "3,2,3,2",
+                "4,2,1", "4,2,3", "4,2,1,2", "4,2,3,2"]
 
 
 @pytest.mark.parametrize("plan", FORCED_PLANS)
@@ -421,7 +423,7 @@ def test_forced_prefill_plans(plan, qt, monkeypatch):
     m, k, n = 300, 1536 if qt != "q6_k" else 1792, 270
     if qt == "f32" and (kg == 2 or (x16, wm) == (2, 4)):
         pytest.skip("not a plan the library runs for f32 weights")
-    if x16 == 3 and kg == 2 and qt in ("q6_k", "q8_0"):
+    if (x16 == 3 or x16 == 4) and kg == 2 and qt in ("q6_k", "q8_0", "f32"):
         pytest.skip("its LDS ring does not fit 160 KB")
     monkeypatch.setenv("QMM_MFMA_PLAN", plan)
     p = qmm.gemm_plan(m, k, n, qt, "mfma")
@@ -573,7 +575,8 @@ def test_moe_q8_exact_activations_match_f32_path():
 
 # ------------------------------------------------------------------ strided x and dst
 
-@pytest.mark.parametrize("plan", [None, "0,2,1,1", "0,2,3,2", "1,2,1", "1,4,3", "2,2,1", "2,4,3", "3,2,2"])
+@pytest.mark.parametrize("plan", [None, "0,2,1,1", "0,2,3,2", "1,2,1", "1,4,3", "2,2,1", "2,4,3", "3,2,2",
+                                  "4,2,1", "4,2,2,2"])
 @pytest.mark.parametrize("qt", ["q4_k", "f32"])
 def test_strided_rows_bit_identical(qt, plan, monkeypatch):
     """Row-strided x and dst (qmm_gemm_ex) give bit-identical results to the
