@@ -481,6 +481,51 @@ def run_crossover():
     print(json.dumps({"crossover_us_gemv_mfma": res}))
 
 
+PLAN_SHAPES = [("ffn_gate", 4608, 1024, 512), ("ffn_down", 1024, 4608, 512), ("conv_in", 3072, 1024, 512),
+               ("attn_out", 1024, 1024, 512), ("8b_up", 14336, 4096, 2048), ("8b_down", 4096, 14336, 2048)]
+# forced prefill plans compared with the planned one (QMM_MFMA_PLAN codes)
+PLAN_FAMILIES = ["0,2,1,2", "1,2,1", "2,2,1", "2,2,1,2", "3,2,1", "3,2,1,2", "4,2,1,2"]
+
+
+def run_prefill_plans():
+    """The planned prefill kernel against forced kernel families, unsplit, per
+    LFM2 and 8B-class shape and format (graph of 8 calls, median of 5)."""
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    from synth import gen
+    rows = []
+    for label, m, k, n in PLAN_SHAPES:
+        qts = ["q4_k", "q6_k"] if label.startswith("8b") else QTS
+        x = to_dev(gen.unit_f32(n * k, gen.SEED_X + k).reshape(n, k))
+        for qi, qt in enumerate(qts):
+            w = to_dev(gen_weights(qt, m, k, 16 * qi))
+            out = torch.empty((n, m), dtype=torch.float32, device="cuda")
+            for force in [None] + PLAN_FAMILIES:
+                if force is None:
+                    os.environ.pop("QMM_MFMA_PLAN", None)
+                else:
+                    os.environ["QMM_MFMA_PLAN"] = force
+                plan = qmm.gemm_plan(m, k, n, qt, "mfma")
+                if force is not None and (plan["x16"], plan["k_groups"]) != (
+                        int(force.split(",")[0]), int(force.split(",")[3]) if force.count(",") == 3 else 1):
+                    continue  # a family this format does not run
+                ws = torch.empty(max(qmm.workspace_bytes(m, k, n, qt, "mfma"), 256), dtype=torch.uint8,
+                                 device="cuda")
+                g = capture([lambda: qmm.gemm(w, x, m, qt, out=out, path="mfma", workspace=ws)] * 8)
+                for _ in range(3):  # the row's first graph also warms the clocks and the fresh weights
+                    g.replay()
+                t = time_graph(g, 8, 5)
+                rows.append({"shape": f"{label} {m}x{k} n={n}", "qtype": qt, "plan": force or "auto",
+                             "kernel": qmm.plan_kernel_name(plan, qt), "k_split": plan["n_split"],
+                             "us": round(t * 1e6, 2), "TFLOP/s": round(2.0 * m * k * n / t / 1e12, 1)})
+                log(f"{label} {qt} {force or 'auto':8s} {t * 1e6:8.2f} us {rows[-1]['kernel']} split {plan['n_split']}")
+                del g, ws
+            os.environ.pop("QMM_MFMA_PLAN", None)
+            del w, out
+            torch.cuda.empty_cache()
+    print(json.dumps({"prefill_plans": rows}), flush=True)
+
+
 def copy_probe():
     """Three device-to-device copies of 1 GiB (the runtime's copy kernel): the
     calibration for the FETCH_SIZE / WRITE_SIZE counters.  The largest copies
@@ -592,6 +637,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="fewer rotation copies")
     ap.add_argument("--crossover", action="store_true",
                     help="only measure GEMV vs matrix-core time over n (prints its own JSON)")
+    ap.add_argument("--prefill-plans", action="store_true",
+                    help="only time the planned prefill kernel against forced kernel families (own JSON)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run the 1 GiB copy that calibrates the HBM byte counters")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -615,6 +662,9 @@ def main():
     qmm.load()
     if args.crossover:
         run_crossover()
+        return
+    if args.prefill_plans:
+        run_prefill_plans()
         return
     if args.copy_probe:
         log("copy probe: 3 x 1 GiB device copies")
