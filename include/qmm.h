@@ -119,19 +119,35 @@ int qmm_gemm_path(float* dst, const void* w, const float* x,
  * qmm_gemm_ws: qmm_gemm_path with a caller-owned workspace for the MFMA
  * path, where it lets the library
  *  - round the activations to f16 once per call (a pre-pass writing them
- *    into the workspace in the weight tiles' k order), for products large
- *    enough that the f16-activation kernel (256- or 128-row tiles) is
- *    estimated at least 10% faster; and
+ *    into the workspace in the weight tiles' k order) for the kernels that
+ *    read f16 activations; and
  *  - split k when the product has too few output tiles to fill the device:
  *    separate work groups write partial results to the workspace and a
  *    second kernel on the same stream adds them in a fixed order, so two
  *    identical calls still give bit-identical results.
- * Both kernels round W and x to f16 identically (RNE), so the tolerance is
- * the one of qmm_gemm.  The plan is a pure function of (m, k, n) and the
- * device's compute-unit count; the environment variable
+ * A cost model fitted to MI355X measurements picks the kernel family, tile
+ * shape, k groups and k split.  The families (the "x16" code of
+ * qmm_gemm_plan and QMM_MFMA_PLAN):
+ *   0  f32 activations rounded in the k loop, 128 x 128 tiles (1 or 2 k
+ *      groups); the only family of calls without a workspace;
+ *   1  f16 activations from the pre-pass, register-ring tiles of 128 or 256
+ *      weight rows x 128 tokens;
+ *   2  the LDS ring (weight bytes and f16 activations streamed into a ring
+ *      of LDS stages by buffer-to-LDS loads; weights decoded straight into
+ *      the matrix-core operands), 128 or 256 weight rows x 128 tokens, 1 or
+ *      2 k groups; k a multiple of 64;
+ *   3  the LDS ring with 128 x 256 tiles (half the decode work per
+ *      matrix-core op; for products of many tiles);
+ *   4  the LDS ring on the f32 activations themselves (no pre-pass and no
+ *      f16 workspace), 128 x 128 tiles.
+ * Every family rounds each decoded weight and each activation to f16 once
+ * (RNE) and accumulates in f32, so the tolerance is the one of qmm_gemm.
+ * The plan is a pure function of (m, k, n, qtype) and the device's
+ * compute-unit count; the environment variable
  * QMM_MFMA_PLAN="x16,wm,n_split[,kg]" forces it (tuning and tests only:
- * x16 0 with wm 2 and kg 1 or 2, or x16 1 with wm 2 or 4; malformed ->
- * QMM_ERR_RANGE).
+ * x16 0 with wm 2; 1 with wm 2 or 4 and kg 1; 2 with wm 2 or 4; 3 or 4 with
+ * wm 2; kg 1 or 2; malformed -> QMM_ERR_RANGE; a family the format or k
+ * cannot run falls back to family 0 unsplit).
  *   workspace        DEVICE memory, 256-byte aligned, of at least
  *                    qmm_gemm_workspace_bytes(m, k, n, qtype, path) bytes, or
  *                    NULL (then the f32-activation kernel without a k split).
@@ -169,9 +185,10 @@ int64_t qmm_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int qtype, int
  * qmm_gemm_plan: the kernels a call with these sizes runs on the current
  * device, with (with_workspace != 0: qmm_gemm_ws) or without a workspace.
  *   out  HOST int32[6], written: path (QMM_PATH_GEMV or QMM_PATH_MFMA); then
- *        for the MFMA path: 1 if the activations are rounded to f16 by a
- *        pre-pass (else 0), weight rows per tile, k groups per work group,
- *        k splits, and 64-k steps per split (zeros on the GEMV path).
+ *        for the MFMA path: the kernel family (0-4, as listed at
+ *        qmm_gemm_ws; families 1-3 round the activations to f16 in a
+ *        pre-pass), weight rows per tile, k groups per work group, k
+ *        splits, and 64-k steps per split (zeros on the GEMV path).
  * Errors as qmm_gemm_workspace_bytes; QMM_ERR_NULL for a null out.
  */
 int qmm_gemm_plan(int64_t m, int64_t k, int64_t n, int qtype, int path, int with_workspace,
