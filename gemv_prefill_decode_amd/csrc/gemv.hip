@@ -1280,11 +1280,23 @@ static int min_lpr(int qt) {
 // log2 of the lane-group size: the largest power of two <= min(units, 64),
 // and at least the format's MIN_LPR (a row then leaves lanes of its group
 // idle rather than breaking the per-lane constant unit position).
-static int lpr_for(int qt, int64_t k) {
+// Lane groups down to 1 << LPR_CAP_MULTI lanes for the streams that apply
+// each weight to several activation rows (GEMV n > 2, the MoE): a lane then
+// takes more units of its row between two lane-group reductions, and a wave
+// more rows at once.  Measured on 14336x4096 (q4_k / q6_k): n = 8 from
+// 43.5 / 48.1 to 31.4 / 35.2 us, n = 32 from 125 / 128 to 98 / 96 us, the MoE
+// gate/up at t = 16 from 210 to 188 us and the down projection from 119 to
+// 97 us; at n = 1 whole-wave groups stay (q6_k 16.4 against 17.7 us).  The
+// GEMV shrinks its groups only while the rows still give one row group per
+// SIMD (on 1024x4608 q4_0, n = 4, 16-lane groups left 128 waves for 1024
+// SIMDs: 17.3 against 9.3 us).
+constexpr int LPR_CAP_SINGLE = 6, LPR_CAP_MULTI = 4;
+
+static int lpr_for(int qt, int64_t k, int cap_log2) {
     const int ue = gemv_unit_elems(qt);
     const int64_t units = (k + ue - 1) / ue;
     int l = 0;
-    while (l < 6 && (int64_t(2) << l) <= units) ++l;
+    while (l < cap_log2 && (int64_t(2) << l) <= units) ++l;
     while ((1 << l) < min_lpr(qt)) ++l;
     return l;
 }
@@ -1293,7 +1305,8 @@ static int lpr_for(int qt, int64_t k) {
 static int64_t rg_rows(int lpr_log2, int R) { return (int64_t)(64 >> lpr_log2) * R; }
 
 int64_t gemv_max_window_bytes(int qt, int64_t k, int64_t rb) {
-    return rg_rows(lpr_for(qt, k), 2) * rb + 16;
+    // the smaller lane groups give the taller row groups
+    return rg_rows(lpr_for(qt, k, LPR_CAP_MULTI), 2) * rb + 16;
 }
 
 // Work groups for a stream of n_rg row groups shared by `sets` independent
@@ -1347,7 +1360,11 @@ static void launch_gemv_nt(float* dst, const uint8_t* w, const float* x, int64_t
                            hipStream_t st) {
     with_rd<NT>(tune, [&](auto Rc, auto Dc) {
         constexpr int R = decltype(Rc)::value, D = decltype(Dc)::value;
-        const int l = lpr_for(QT, k);
+        int l = lpr_for(QT, k, LPR_CAP_SINGLE);
+        if (n > 2) {
+            const int lmin = lpr_for(QT, k, LPR_CAP_MULTI);
+            while (l > lmin && (m + rg_rows(l - 1, R) - 1) / rg_rows(l - 1, R) >= 4 * (int64_t)tune.num_cu) --l;
+        }
         const int64_t n_rg = (m + rg_rows(l, R) - 1) / rg_rows(l, R);
         const int64_t gy = (n + NT - 1) / NT;
         const int64_t lds = (int64_t)xlds_floats(NT, (int)k, GUnit<QT>::RUNS > 0) * 4;
@@ -1408,7 +1425,7 @@ static void launch_moe_qt(float* g, float* u, const uint8_t* wg, const uint8_t* 
                           int act_pair, const GemvTuning& tune, hipStream_t st) {
     with_rd<1>(tune, [&](auto Rc, auto Dc) {
         constexpr int R = decltype(Rc)::value, D = decltype(Dc)::value;
-        const int l = lpr_for(QT, in_f);
+        const int l = lpr_for(QT, in_f, LPR_CAP_MULTI);
         const int64_t n_pairs = t * n_used;
         const int64_t n_rg = (n_ff + rg_rows(l, R) - 1) / rg_rows(l, R);
         // at most one set of work groups per distinct expert and plane is
@@ -1446,7 +1463,7 @@ static void launch_moe_q8_qt(float* g, float* u, const uint8_t* wg, const uint8_
                              const GemvTuning& tune, hipStream_t st) {
     with_rd<1>(tune, [&](auto Rc, auto Dc) {
         constexpr int R = decltype(Rc)::value, D = decltype(Dc)::value;
-        const int l = lpr_for(QT, in_f);
+        const int l = lpr_for(QT, in_f, LPR_CAP_MULTI);
         const int64_t n_pairs = t * n_used;
         const int64_t n_rg = (n_ff + rg_rows(l, R) - 1) / rg_rows(l, R);
         const int64_t active = 2 * (n_pairs < n_expert ? n_pairs : n_expert);
@@ -1555,7 +1572,7 @@ static void launch_lo_qt(uint32_t* sink, const uint8_t* w, int64_t m, int64_t k,
                          const GemvTuning& tune, hipStream_t st) {
     with_rd<1>(tune, [&](auto Rc, auto Dc) {
         constexpr int R = decltype(Rc)::value, D = decltype(Dc)::value;
-        const int l = lpr_for(QT, k);
+        const int l = lpr_for(QT, k, LPR_CAP_SINGLE);
         const int64_t n_rg = (m + rg_rows(l, R) - 1) / rg_rows(l, R);
         loadonly_kernel<QT, R, D><<<dim3(stream_grid(n_rg, 1, tune)), 256, 0, st>>>(
             sink, w, (int)m, (int)k, (int)rb, l, (int)n_rg);
