@@ -90,6 +90,13 @@ __device__ __forceinline__ uint32_t pack_f2h(float a, float b) {
     return pack_h2((_Float16)a, (_Float16)b);
 }
 
+// The low / high half of a dword read as f16 and widened to f32 (exact).
+// A small integer q in a half's mantissa field, exponent field zero, is the
+// subnormal q * 2^-24; a multiply-add with f32 operands on such a half
+// compiles to one v_fma_mix_f32 (widening, product and sum rounded once).
+__device__ __forceinline__ float f16lo(uint32_t p) { return (float)__builtin_bit_cast(f16x2, p).x; }
+__device__ __forceinline__ float f16hi(uint32_t p) { return (float)__builtin_bit_cast(f16x2, p).y; }
+
 __device__ __forceinline__ uint32_t byte_of(uint32_t v, int b) { return (v >> (8 * b)) & 0xFFu; }
 
 // Byte b of v as f32 (v_cvt_f32_ubyte{0..3}: select and convert in one

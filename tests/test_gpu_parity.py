@@ -187,6 +187,22 @@ def test_identity_windows_gemv(qt):
         assert np.array_equal(got, want), c0
 
 
+@pytest.mark.parametrize("qt", ["q4_0", "q4_k", "q6_k"])
+def test_gemv_single_row_equals_row_of_two(qt):
+    """One activation row takes the packed-half products (q as an f16
+    subnormal scaled by a power of two, one v_fma_mix_f32 each), two rows the
+    widened-float ones; the scaling is exact for activations of normal size,
+    so each output equals, bit for bit, the same row computed beside another."""
+    for si, (m, k) in enumerate([(67, 1280), (300, 1024), (1030, 4096)]):
+        note(f"gemv n=1 vs n=2 {qt} m={m} k={k}")
+        w = weights(qt, m, k, 40 + si)
+        x2 = acts(2, k, 40 + si)
+        got1 = gpu_gemm(qt, w, x2[:1].copy(), m, "gemv")
+        got1b = gpu_gemm(qt, w, x2[1:].copy(), m, "gemv")
+        got2 = gpu_gemm(qt, w, x2, m, "gemv")
+        assert np.array_equal(got1[0], got2[0]) and np.array_equal(got1b[0], got2[1]), (m, k)
+
+
 @pytest.mark.parametrize("path", ["gemv", "mfma"])
 def test_deterministic_and_guard_bands(path):
     import torch
