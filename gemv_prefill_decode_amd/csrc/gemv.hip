@@ -1449,8 +1449,8 @@ static void launch_gemv_nt(float* dst, const uint8_t* w, const float* x, int64_t
         const int64_t lds = (int64_t)xlds_floats(NT, (int)k, GUnit<QT>::RUNS > 0) * 4;
         if (lds <= tune.lds_per_wg) {
             const GemvTuning lt = lds_limited(tune, lds);
-            if (lt.wg_per_cu == 1) {
-                // one work group per CU: 8 waves share the staged rows
+            if (lt.wg_per_cu <= 2) {
+                // one or two work groups per CU: 8 waves share the staged rows
                 const dim3 grid(stream_grid(n_rg, gy, lt, 8), (unsigned)gy);
                 gemv_kernel<QT, NT, R, D, true, 8><<<grid, 512, (size_t)lds, st>>>(
                     dst, w, x, (int)m, (int)k, (int)n, (int)rb, l, (int)n_rg, (int)ldx, (int)ldd);
