@@ -203,6 +203,21 @@ def test_gemv_single_row_equals_row_of_two(qt):
         assert np.array_equal(got1[0], got2[0]) and np.array_equal(got1b[0], got2[1]), (m, k)
 
 
+@pytest.mark.parametrize("qt", QTS)
+@pytest.mark.parametrize("n", [1, 2])
+def test_gemv_long_rows(qt, n):
+    """Rows of k = 14336: the staged activations leave room for one or two
+    work groups per CU, which then run 8 waves each; fewer row groups than
+    resident waves, and a ragged last work group at m = 301."""
+    k = 14336
+    for si, m in enumerate((301, 1030)):
+        note(f"gemv long rows {qt} m={m} k={k} n={n}")
+        w = weights(qt, m, k, 50 + si)
+        x = acts(n, k, 50 + si)
+        got = gpu_gemm(qt, w, x, m, "gemv")
+        check_full(qt, w, x, m, k, n, got, TAU_F32, f"gemv {qt} {m}x{k} n={n}")
+
+
 @pytest.mark.parametrize("path", ["gemv", "mfma"])
 def test_deterministic_and_guard_bands(path):
     import torch
