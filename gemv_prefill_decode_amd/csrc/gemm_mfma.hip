@@ -304,13 +304,13 @@ constexpr FamCost FAM_COST[N_FAM] = {
     {1.5, 1.04, 2},   // gemm_mfma_kernel, 128 x 128, f32 activations
     {1.6, 1.61, 1},   // gemm_mfma_x16_kernel, 256 x 128
     {1.2, 0.82, 2},   // gemm_mfma_x16_kernel, 128 x 128
-    {1.3, 1.3, 1},    // gemm_mfma_kernel with 2 k groups (time per step of the item)
+    {1.6, 1.6, 1},    // gemm_mfma_kernel with 2 k groups (time per step of the item)
     // gemm_lds_kernel (one work group per CU: its LDS ring); 128 x 256 tiles
     // are priced per step of twice the work
     {1.0, 0.9, 1},    // 128 x 128
     {2.0, 2.0, 1},    // 256 x 128 (slower than two 128-row tiles everywhere measured)
     {1.3, 1.3, 1},    // 128 x 256
-    {0.9, 0.8, 1},    // 128 x 128, 2 k groups
+    {0.8, 0.8, 1},    // 128 x 128, 2 k groups
     {1.1, 1.1, 1},    // 128 x 256, 2 k groups
     // the same with 128 x 128 tiles on the f32 activations (no pre-pass;
     // more VALU and LDS reads per step for the rounding, which one k group
@@ -325,7 +325,8 @@ constexpr double LDS_Q6K_FACTOR_128 = 1.3, LDS_Q6K_FACTOR_128_KG2 = 1.15, LDS_Q6
 constexpr double LAUNCH_US = 3.0;      // a launch with its first loads and its stores
 constexpr double SPLIT_US = 4.0;       // the split sum's launch
 constexpr double X16_US = 3.0;         // the f16 pre-pass launch
-constexpr double BYTES_PER_US = 4.0e6; // partials and pre-pass traffic
+constexpr double BYTES_PER_US = 4.0e6; // split partials' traffic
+constexpr double X16_BYTES_PER_US = 6.0e6;  // the pre-pass's traffic (a plain stream)
 constexpr double X16_MARGIN = 1.1;     // see below
 
 MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, bool have_ws,
@@ -340,7 +341,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
     best.ws_bytes = 0;
     if (!have_ws || num_cu < 1) return best;
     const double out_bytes = 4.0 * (double)n * (double)m;
-    const double x16_us = X16_US + 6.0 * (double)n * (double)k / BYTES_PER_US;
+    const double x16_us = X16_US + 6.0 * (double)n * (double)k / X16_BYTES_PER_US;
     double best_cost = 1e30;
     for (int fam = 0; fam < N_FAM; ++fam) {
         const int x16 = fam >= 9 ? 4 : (fam == 6 || fam == 8 ? 3 : (fam >= 4 ? 2 : (fam == 1 || fam == 2))),
