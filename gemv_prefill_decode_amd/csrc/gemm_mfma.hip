@@ -327,6 +327,13 @@ constexpr double SPLIT_US = 4.0;       // the split sum's launch
 constexpr double X16_US = 3.0;         // the f16 pre-pass launch
 constexpr double BYTES_PER_US = 4.0e6; // split partials' traffic
 constexpr double X16_BYTES_PER_US = 6.0e6;  // the pre-pass's traffic (a plain stream)
+// Kernels on f32 activations read twice the activation bytes of the f16
+// ones, once per weight-row tile, from L2: 2nk bytes more per tile row,
+// priced at this rate for the quantized formats (measured: 4096x4096
+// n = 256, 32 tile rows, 4-way split, ran 3-4 us slower on f32 activations
+// than on the pre-pass's f16).  With f32 weights, whose own rows dominate
+// the step, the family's step time already holds it.
+constexpr double XF_L2_BYTES_PER_US = 15.0e6;
 constexpr double X16_MARGIN = 1.1;     // see below
 
 MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, bool have_ws,
@@ -375,9 +382,12 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
             // the f16 kernels must win by X16_MARGIN to be chosen: one kernel
             // family per product size keeps small products on the kernel
             // without a pre-pass (whose time the model knows least well)
+            const double xf_us = x16 == 4 && qt != QT_F32 ? 2.0 * (double)n * (double)k * (double)((m + 64 * wm - 1) / (64 * wm)) /
+                                                 XF_L2_BYTES_PER_US
+                                          : 0.0;
             const double cost = (LAUNCH_US + rounds * sps * step_t +
                                  (se > 1 ? SPLIT_US + (2.0 * se + 1.0) * out_bytes / BYTES_PER_US : 0.0) +
-                                 (x16 >= 1 && x16 <= 3 ? x16_us : 0.0)) *
+                                 (x16 >= 1 && x16 <= 3 ? x16_us : 0.0) + xf_us) *
                                 (x16 == 1 ? X16_MARGIN : 1.0);
             if (cost < best_cost) {
                 best_cost = cost;
