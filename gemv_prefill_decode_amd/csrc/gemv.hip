@@ -17,6 +17,8 @@
 // most 64 terms) before joining the lane's running sum, and the LPR lane sums
 // are combined by a butterfly: every f32 chain has at most
 // 64 + k/(UE*LPR) + log2(LPR) terms.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -1618,15 +1620,20 @@ __global__ __launch_bounds__(256) void moe_slot_sum_kernel(float* __restrict__ y
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nv; i += (int64_t)gridDim.x * 256) {
         const int64_t tau = i * V / d, r = i * V - tau * d;
         const float* src = pair_out + tau * n_used * d + r;
-        if constexpr (V == 4) {
-            f32x4 acc = *(const f32x4*)src;
-            for (int s = 1; s < n_used; ++s) acc += *(const f32x4*)(src + (int64_t)s * d);
-            *(f32x4*)(y + i * 4) = acc;
-        } else {
-            float acc = src[0];
-            for (int s = 1; s < n_used; ++s) acc += src[(int64_t)s * d];
-            y[i] = acc;
+        // slots in order 0, 1, ...; the loads of up to 8 slots are issued
+        // before their sums, so their latencies overlap
+        using T = typename std::conditional<V == 4, f32x4, float>::type;
+        T acc = *(const T*)src;
+        for (int s0 = 1; s0 < n_used; s0 += 8) {
+            T v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < n_used) v[u] = *(const T*)(src + (int64_t)(s0 + u) * d);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < n_used) acc += v[u];
         }
+        *(T*)(y + i * V) = acc;
     }
 }
 
