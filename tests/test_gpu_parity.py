@@ -326,10 +326,12 @@ def _gpu_down(wd, ids, sc, act, n_expert, d_model, qt="nvfp4"):
     return y.cpu().numpy(), pair.cpu().numpy()
 
 
-# d_model 80 takes the 4-wide slot sum, 78 the scalar one
-@pytest.mark.parametrize("t,n_used,d_model", [(1, 8, 80), (3, 2, 78), (5, 4, 80), (16, 3, 78)])
+# d_model 80 takes the 4-wide slot sum, 78 the scalar one; n_used 10 and 12
+# take the slot sum's second batch of 8 loads
+@pytest.mark.parametrize("t,n_used,d_model", [(1, 8, 80), (3, 2, 78), (5, 4, 80), (16, 3, 78), (2, 10, 80),
+                                              (3, 12, 78)])
 def test_moe_down_parity_small(t, n_used, d_model):
-    n_expert, n_ff = 9, 256
+    n_expert, n_ff = max(9, n_used), 256
     note(f"moe down small t={t} n_used={n_used} d_model={d_model}")
     wd, ids, sc, act = _down_inputs(n_expert, n_ff, d_model, t, n_used, seed=t)
     y, pair = _gpu_down(wd, ids, sc, act, n_expert, d_model)
