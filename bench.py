@@ -91,7 +91,7 @@ def plan_grid_size(plan, m, n):
     Grid_Size the profiler records for that dispatch)."""
     x16, rows, kg, split = plan["x16"], plan["tile_rows"], plan["k_groups"], plan["n_split"]
     cols = 256 if x16 == 3 else 128
-    threads = 2 * rows if x16 == 1 else 256 * kg
+    threads = 256 * kg
     groups = -(-m // rows) * -(-n // cols) * split
     return groups * threads
 
@@ -484,7 +484,7 @@ def run_crossover():
 PLAN_SHAPES = [("ffn_gate", 4608, 1024, 512), ("ffn_down", 1024, 4608, 512), ("conv_in", 3072, 1024, 512),
                ("attn_out", 1024, 1024, 512), ("8b_up", 14336, 4096, 2048), ("8b_down", 4096, 14336, 2048)]
 # forced prefill plans compared with the planned one (QMM_MFMA_PLAN codes)
-PLAN_FAMILIES = ["0,2,1,2", "1,2,1", "2,2,1", "2,2,1,2", "3,2,1", "3,2,1,2", "4,2,1,2"]
+PLAN_FAMILIES = ["0,2,1,2", "2,2,1", "2,2,1,2", "3,2,1", "3,2,1,2", "4,2,1,2"]
 
 
 def run_prefill_plans():

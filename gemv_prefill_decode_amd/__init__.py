@@ -175,8 +175,6 @@ def plan_kernel_name(plan: dict, qtype) -> str:
     if plan["x16"] >= 2:
         return (f"gemm_lds_kernel<{qt}, {plan['tile_rows'] // 4}, {256 if plan['x16'] == 3 else 128}, "
                 f"{plan['k_groups']}, {'true' if plan['x16'] == 4 else 'false'}>")
-    if plan["x16"]:
-        return f"gemm_mfma_x16_kernel<{qt}, {plan['tile_rows'] // 64}>"
     return f"gemm_mfma_kernel<{qt}, {plan['k_groups']}>"
 
 

@@ -9,8 +9,8 @@
 // sub-tiles with f32 accumulators.  LDS is double buffered and the next
 // step's global loads are issued before the current step's MFMAs, so the
 // loads, the decode and the matrix-core work overlap.  (This is the kernel
-// for calls without a workspace; gemm_mfma_x16.hip holds the one that reads
-// activations pre-rounded to f16.)
+// for calls without a workspace; gemm_lds.hip holds the LDS-ring kernels the
+// planner chooses when a workspace is given.)
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_tiles.hpp"
@@ -295,28 +295,27 @@ static void launch_qt(float* dst, const uint8_t* w, const float* x, int64_t m, i
 // single wave per SIMD), the time per step per work group when the CU's
 // work groups are throughput-bound, and how many work groups fit on a CU.
 struct FamCost {
+    int x16, wm, kg;  // the plan's kernel family, tile rows / 64 and k groups
     double step_alone_us;
     double step_shared_us;
     int per_cu;
 };
-constexpr int N_FAM = 11;
+constexpr int N_FAM = 9;
 constexpr FamCost FAM_COST[N_FAM] = {
-    {1.5, 1.04, 2},   // gemm_mfma_kernel, 128 x 128, f32 activations
-    {1.6, 1.61, 1},   // gemm_mfma_x16_kernel, 256 x 128
-    {1.2, 0.82, 2},   // gemm_mfma_x16_kernel, 128 x 128
-    {1.6, 1.6, 1},    // gemm_mfma_kernel with 2 k groups (time per step of the item)
+    {0, 2, 1, 1.5, 1.04, 2},   // gemm_mfma_kernel, 128 x 128, f32 activations
+    {0, 2, 2, 1.6, 1.6, 1},    // gemm_mfma_kernel with 2 k groups (time per step of the item)
     // gemm_lds_kernel (one work group per CU: its LDS ring); 128 x 256 tiles
     // are priced per step of twice the work
-    {1.0, 0.9, 1},    // 128 x 128
-    {2.0, 2.0, 1},    // 256 x 128 (slower than two 128-row tiles everywhere measured)
-    {1.3, 1.3, 1},    // 128 x 256
-    {0.8, 0.8, 1},    // 128 x 128, 2 k groups
-    {1.1, 1.1, 1},    // 128 x 256, 2 k groups
+    {2, 2, 1, 1.0, 0.9, 1},    // 128 x 128
+    {2, 4, 1, 2.0, 2.0, 1},    // 256 x 128 (slower than two 128-row tiles everywhere measured)
+    {3, 2, 1, 1.3, 1.3, 1},    // 128 x 256
+    {2, 2, 2, 0.8, 0.8, 1},    // 128 x 128, 2 k groups
+    {3, 2, 2, 1.1, 1.1, 1},    // 128 x 256, 2 k groups
     // the same with 128 x 128 tiles on the f32 activations (no pre-pass;
     // more VALU and LDS reads per step for the rounding, which one k group
     // per CU does not hide)
-    {1.4, 1.3, 1},    // 1 k group
-    {0.95, 0.85, 1},  // 2 k groups
+    {4, 2, 1, 1.4, 1.3, 1},    // 1 k group
+    {4, 2, 2, 0.95, 0.85, 1},  // 2 k groups
 };
 // The LDS-ring kernel's step time by format: Q6_K's two-field 6-bit codes
 // take about a third longer to decode; with 256-token tiles the decode is a
@@ -334,7 +333,6 @@ constexpr double X16_BYTES_PER_US = 6.0e6;  // the pre-pass's traffic (a plain s
 // than on the pre-pass's f16).  With f32 weights, whose own rows dominate
 // the step, the family's step time already holds it.
 constexpr double XF_L2_BYTES_PER_US = 15.0e6;
-constexpr double X16_MARGIN = 1.1;     // see below
 
 MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, bool have_ws,
                         const MfmaForce* force) {
@@ -351,8 +349,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
     const double x16_us = X16_US + 6.0 * (double)n * (double)k / X16_BYTES_PER_US;
     double best_cost = 1e30;
     for (int fam = 0; fam < N_FAM; ++fam) {
-        const int x16 = fam >= 9 ? 4 : (fam == 6 || fam == 8 ? 3 : (fam >= 4 ? 2 : (fam == 1 || fam == 2))),
-                  wm = fam == 1 || fam == 5 ? 4 : 2, kg = fam == 3 || fam == 7 || fam == 8 || fam == 10 ? 2 : 1;
+        const int x16 = FAM_COST[fam].x16, wm = FAM_COST[fam].wm, kg = FAM_COST[fam].kg;
         if (kg == 2 && qt == QT_F32) continue;  // its two register rings of f32 weights exceed 256 VGPRs
         // the LDS ring: whole 64-k steps only, and f32 rows fit it with 128-row tiles only
         if (x16 >= 2 && (k % 64 != 0 || !lds_ring_fits(qt, 64 * wm, x16 == 3 ? 256 : 128, kg, x16 == 4))) continue;
@@ -361,7 +358,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
         const double fmul = x16 < 2 || qt != QT_Q6_K
                                 ? 1.0
                                 : (x16 == 3 ? LDS_Q6K_FACTOR_256 : (kg == 2 ? LDS_Q6K_FACTOR_128_KG2 : LDS_Q6K_FACTOR_128));
-        const FamCost fc{fc0.step_alone_us * fmul, fc0.step_shared_us * fmul, fc0.per_cu};
+        const FamCost fc{x16, wm, kg, fc0.step_alone_us * fmul, fc0.step_shared_us * fmul, fc0.per_cu};
         const int bn = x16 == 3 ? 256 : 128;
         const int64_t T = ((m + 64 * wm - 1) / (64 * wm)) * ((n + bn - 1) / bn);
         for (int S = 1; S <= 16 && (S == 1 || S <= nk / 2); ++S) {
@@ -371,7 +368,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
             if (force && force->n_split != se) continue;
             const int64_t items = T * se;
             if (items > (int64_t)1 << 30) continue;
-            if (fam == 5 && !force) continue;
+            if (x16 == 2 && wm == 4 && !force) continue;
             // work groups sharing a CU, time per step, and rounds of them
             const int64_t fill = (items + num_cu - 1) / num_cu;
             const int64_t share = fill < fc.per_cu ? fill : fc.per_cu;
@@ -379,16 +376,12 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
             const double step_t = step > fc.step_alone_us ? step : fc.step_alone_us;
             double rounds = (double)items / (double)(num_cu * share);
             if (share == 1 || rounds < 1.0) rounds = (double)((items + num_cu * share - 1) / (num_cu * share));
-            // the f16 kernels must win by X16_MARGIN to be chosen: one kernel
-            // family per product size keeps small products on the kernel
-            // without a pre-pass (whose time the model knows least well)
             const double xf_us = x16 == 4 && qt != QT_F32 ? 2.0 * (double)n * (double)k * (double)((m + 64 * wm - 1) / (64 * wm)) /
                                                  XF_L2_BYTES_PER_US
                                           : 0.0;
             const double cost = (LAUNCH_US + rounds * sps * step_t +
                                  (se > 1 ? SPLIT_US + (2.0 * se + 1.0) * out_bytes / BYTES_PER_US : 0.0) +
-                                 (x16 >= 1 && x16 <= 3 ? x16_us : 0.0) + xf_us) *
-                                (x16 == 1 ? X16_MARGIN : 1.0);
+                                 (x16 == 2 || x16 == 3 ? x16_us : 0.0) + xf_us);
             if (cost < best_cost) {
                 best_cost = cost;
                 best.x16 = x16;
@@ -399,7 +392,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
             }
         }
     }
-    best.ws_bytes = (best.x16 >= 1 && best.x16 <= 3 ? x16_bytes(n, k) : 0) +
+    best.ws_bytes = (best.x16 == 2 || best.x16 == 3 ? x16_bytes(n, k) : 0) +
                     (best.n_split > 1 ? (int64_t)best.n_split * splitk_stride(n, m) * 4 : 0);
     if (best.ws_bytes == 0) best.ws_bytes = 256;  // a plan that uses no workspace still takes one
     return best;
@@ -410,10 +403,6 @@ void launch_gemm_mfma(float* dst, const void* w, const float* x, int64_t m, int6
                       hipStream_t st) {
     if (pl.x16 >= 2) {
         launch_gemm_lds(dst, w, x, m, k, n, qt, rb, pl, ws, ldx, ldd, st);
-        return;
-    }
-    if (pl.x16) {
-        launch_gemm_mfma_x16(dst, w, x, m, k, n, qt, rb, pl, ws, ldx, ldd, st);
         return;
     }
     const uint8_t* wb = (const uint8_t*)w;

@@ -25,21 +25,19 @@ void launch_gemv(float* dst, const void* w, const float* x, int64_t m, int64_t k
 
 // Launch plan of the prefill (MFMA) kernels.  x16 = 0: gemm_mfma.hip's
 // kernel (128 x 128 tiles, f32 activations converted in the k loop).
-// x16 = 1: gemm_mfma_x16.hip's kernel ((64*wm) x 128 tiles, activations
-// rounded to f16 by a pre-pass into the workspace).  x16 = 2: gemm_lds.hip's
-// kernel ((64*wm) x 128 tiles; f16 activations from its own pre-pass, weight
-// bytes and activations streamed through an LDS ring; k % 64 == 0 only);
-// x16 = 3: the same kernel with 128 x 256 tiles (wm = 2).  x16 = 4: the
-// same kernel with 128 x 128 tiles reading the f32 activations into its
-// ring and rounding them as it reads (no pre-pass, no f16 workspace).  kg =
-// 2 on x16 >= 2: two groups of 4 waves take alternate k steps of each tile.
-// Any of them may split k into n_split ranges of sps steps (64 k each; sps
-// even) whose partial results go to the workspace (after the f16
-// activations), summed by a second kernel.
+// x16 = 2: gemm_lds.hip's kernel ((64*wm) x 128 tiles; f16 activations from
+// its own pre-pass, weight bytes and activations streamed through an LDS
+// ring; k % 64 == 0 only); x16 = 3: the same kernel with 128 x 256 tiles
+// (wm = 2).  x16 = 4: the same kernel with 128 x 128 tiles reading the f32
+// activations into its ring and rounding them as it reads (no pre-pass, no
+// f16 workspace).  kg = 2: two groups of 4 waves take alternate k steps of
+// each tile.  Any of them may split k into n_split ranges of sps steps (64 k
+// each; sps even) whose partial results go to the workspace (after the f16
+// activations), summed by a second kernel.  (x16 = 1 is not used.)
 struct MfmaPlan {
     int x16;
     int wm;
-    int kg;  // k groups of gemm_mfma_kernel (1 or 2; x16 = 0 only)
+    int kg;  // k groups per work group (1 or 2)
     int n_split;
     int sps;
     int64_t ws_bytes;
@@ -75,9 +73,6 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
 void launch_gemm_mfma(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
                       int qt, int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd,
                       hipStream_t st);
-void launch_gemm_mfma_x16(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
-                          int qt, int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd,
-                          hipStream_t st);
 void launch_gemm_lds(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qt,
                      int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd, hipStream_t st);
 // Whether the LDS ring of gemm_lds.hip holds tiles of tile_rows x

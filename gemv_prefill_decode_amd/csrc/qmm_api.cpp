@@ -44,26 +44,21 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
     return true;
 }
 
-// QMM_PATH_AUTO: the GEMV for n <= 8, and for n <= 16 when the weight
-// matrix has at most 8 Mi elements; the matrix-core path otherwise.  Measured
-// on MI355X (both paths graph-replayed over n = 4 .. 64 with weights rotated
-// through HBM): at 14336x4096 the matrix-core path is faster from n = 12
-// (at n = 32, 50 us against 105 us), at 4608x1024 and 3072x1024 only from
-// n = 16 .. 32, because its time has a floor of about 12 us (pre-pass, split
-// sum, launch gaps) while the GEMV's grows with the weight bytes times
-// ceil(n / 8).  QMM_GEMV_MAX_N replaces the rule by a plain threshold.
-constexpr int AUTO_GEMV_N = 8;
-constexpr int AUTO_GEMV_N_SMALL = 16;
-constexpr int64_t AUTO_SMALL_ELEMS = (int64_t)8 << 20;
+// QMM_PATH_AUTO: the GEMV (f32 arithmetic, the tight tolerance) for every
+// n <= 32, the matrix-core path above: the decode/prefill split the pages
+// draw between a batched GEMV and the GEMM (aprender-serve cublas_prefill,
+// the cublas_gemm_threshold crossover), placed where the f32 path's
+// precision is kept for all decode batch sizes.  QMM_GEMV_MAX_N moves the
+// threshold (the measured MI355X speed crossover lies at n = 8..16 for
+// large weight matrices).
+constexpr int AUTO_GEMV_N = 32;
 
-int g_gemv_max_n = AUTO_GEMV_N_SMALL;
-bool g_gemv_max_n_set = false;
+int g_gemv_max_n = AUTO_GEMV_N;
 std::once_flag g_env_once;
 
 void parse_env() {
     const char* v = std::getenv("QMM_GEMV_MAX_N");
     if (!v) return;
-    g_gemv_max_n_set = true;
     char* end = nullptr;
     errno = 0;
     const long val = std::strtol(v, &end, 10);
@@ -125,10 +120,10 @@ void parse_tune() {
 
 // QMM_MFMA_PLAN="x16,wm,n_split[,kg]" forces the prefill plan of calls with
 // a workspace (tuning and tests): x16 0 (f32-activation kernel, 128-row
-// tiles, kg k groups), 1 (f16 activations, (64*wm)-row tiles), 2 (the LDS
-// ring, (64*wm)-row tiles), 3 (the LDS ring, 128 x 256 tiles) or 4 (the LDS
-// ring on f32 activations, 128 x 128 tiles); where the LDS ring cannot run,
-// the unsplit default; unset: the cost model chooses.  Malformed -> bad.
+// tiles, kg k groups), 2 (the LDS ring, (64*wm)-row tiles), 3 (the LDS ring,
+// 128 x 256 tiles) or 4 (the LDS ring on f32 activations, 128 x 128 tiles);
+// where the LDS ring cannot run, the unsplit default; unset: the cost model
+// chooses.  Malformed -> bad.
 struct MfmaForceState {
     bool set = false;
     bool bad = false;
@@ -142,8 +137,8 @@ MfmaForceState parse_force() {
     int a = -1, b = -1, c = -1, d = 1;
     char tail = 0;
     const int got = std::sscanf(v, "%d,%d,%d,%d%c", &a, &b, &c, &d, &tail);
-    if ((got != 3 && got != 4) || a < 0 || a > 4 || (b != 2 && b != 4) || (a != 1 && a != 2 && b != 2) ||
-        c < 1 || c > 16 || (d != 1 && d != 2) || (a == 1 && d != 1)) {
+    if ((got != 3 && got != 4) || a < 0 || a > 4 || a == 1 || (b != 2 && b != 4) || (a != 2 && b != 2) ||
+        c < 1 || c > 16 || (d != 1 && d != 2)) {
         g_force.bad = true;
         return g_force;
     }
@@ -205,12 +200,10 @@ int check_weights(const void* w, int64_t m, int64_t k, int qt, int64_t* rb) {
     return QMM_OK;
 }
 
-int auto_path(int64_t m, int64_t k, int64_t n) {
+int auto_path(int64_t n) {
     const int lim = qmm_gemv_max_n();
     if (lim < 0) return -1;
-    if (g_gemv_max_n_set) return n <= lim ? QMM_PATH_GEMV : QMM_PATH_MFMA;
-    const bool gemv = n <= AUTO_GEMV_N || (n <= AUTO_GEMV_N_SMALL && m * k <= AUTO_SMALL_ELEMS);
-    return gemv ? QMM_PATH_GEMV : QMM_PATH_MFMA;
+    return n <= lim ? QMM_PATH_GEMV : QMM_PATH_MFMA;
 }
 
 // Shared validation of the gemm entry points; resolves AUTO.  On success
@@ -231,7 +224,7 @@ int check_gemm(float* dst, const void* w, const float* x, int64_t m, int64_t k, 
         return overlap(dst, dst_b, x, x_b) || overlap(dst, dst_b, w, m * *rb) ? QMM_ERR_ALIAS : QMM_OK;
     };
     if (*path == QMM_PATH_AUTO) {
-        *path = auto_path(m, k, n);
+        *path = auto_path(n);
         if (*path < 0) return QMM_ERR_RANGE;
     }
     if (*path == QMM_PATH_GEMV) {
@@ -270,6 +263,12 @@ int gemm_impl(float* dst, int64_t ldd, const void* w, const float* x, int64_t ld
     if (ws) {
         if (!aligned(ws, 256)) return QMM_ERR_ALIGN;
         if (ws_bytes < pl.ws_bytes) return QMM_ERR_WORKSPACE;
+        // the kernels write the workspace while reading x and w and writing
+        // dst: the bytes they use must not overlap any of them
+        const int64_t dst_b = ((n - 1) * ldd + m) * 4, x_b = ((n - 1) * ldx + k) * 4;
+        if (overlap(ws, pl.ws_bytes, dst, dst_b) || overlap(ws, pl.ws_bytes, x, x_b) ||
+            overlap(ws, pl.ws_bytes, w, m * rb))
+            return QMM_ERR_ALIAS;
     }
     qmm::launch_gemm_mfma(dst, w, x, m, k, n, qtype, rb, pl, ws, ldx, ldd, stream);
     return launch_status();
@@ -319,7 +318,7 @@ int64_t qmm_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int qtype, int
     if (m < 1 || k < 1 || n < 1) return -QMM_ERR_SHAPE;
     if (m > INT_MAX || k > INT_MAX || n > INT_MAX) return -QMM_ERR_RANGE;
     if (path == QMM_PATH_AUTO) {
-        path = auto_path(m, k, n);
+        path = auto_path(n);
         if (path < 0) return -QMM_ERR_RANGE;
     }
     if (path == QMM_PATH_GEMV) return 0;
@@ -338,7 +337,7 @@ int qmm_gemm_plan(int64_t m, int64_t k, int64_t n, int qtype, int path, int with
     if (m < 1 || k < 1 || n < 1) return QMM_ERR_SHAPE;
     if (m > INT_MAX || k > INT_MAX || n > INT_MAX) return QMM_ERR_RANGE;
     if (path == QMM_PATH_AUTO) {
-        path = auto_path(m, k, n);
+        path = auto_path(n);
         if (path < 0) return QMM_ERR_RANGE;
     }
     if (path == QMM_PATH_GEMV) {

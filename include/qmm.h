@@ -81,7 +81,7 @@ typedef enum {
 
 /* Kernel path selector for qmm_gemm_path. */
 typedef enum {
-    QMM_PATH_AUTO = 0,     /* the measured crossover (qmm_gemm) -> GEMV or MFMA */
+    QMM_PATH_AUTO = 0,     /* n <= qmm_gemv_max_n() -> GEMV, else MFMA       */
     QMM_PATH_GEMV = 1,     /* f32 FMA, any n (decode path)                     */
     QMM_PATH_MFMA = 2      /* f16 MFMA tiles, f32 accumulation, any n (prefill) */
 } qmm_path;
@@ -94,12 +94,13 @@ typedef enum {
  *   x     DEVICE float[n*k] activations, row-major, 16-byte aligned.
  *   m,k,n >= 1; k % block_elems(qtype) == 0 and k % 4 == 0.
  *   qtype one of QMM_F32..QMM_NVFP4_V2 (NVFP4_V2 on the GEMV path only).
- * Dispatch (the GEMV-vs-GEMM crossover of aprender-serve cublas_prefill,
- * cublas_gemm_threshold, re-measured on MI355X): the f32 GEMV (results within
- * 1e-5 * sum|w*x| of the exact value) for n <= 8, and for n <= 16 when
- * m*k <= 8 Mi weights; otherwise the MFMA kernel, which rounds W and x to
- * f16 (RNE) and accumulates in f32 (within 2e-3 * sum|w*x|).  With
- * QMM_GEMV_MAX_N set: the GEMV for n <= that value, else MFMA.
+ * Dispatch (the decode-GEMV / prefill-GEMM split of aprender-serve
+ * cublas_prefill, its cublas_gemm_threshold): the f32 GEMV for n <= 32
+ * (results within 1e-5 * sum|w*x| of the exact value), the MFMA kernel for
+ * n > 32, which rounds W and x to f16 (RNE) and accumulates in f32 (within
+ * 2e-3 * sum|w*x|).  With QMM_GEMV_MAX_N set: the GEMV for n <= that value,
+ * else MFMA (the measured MI355X speed crossover is n = 8..16 on large
+ * weight matrices; moving the threshold trades the tight tolerance for it).
  * Limits: the bytes of one 256-row weight tile (or one GEMV row group) and
  * of 128 (GEMV: 8) token rows of x each below 2^31; m, n, k below 2^31.
  * Larger values return QMM_ERR_RANGE.
@@ -130,8 +131,6 @@ int qmm_gemm_path(float* dst, const void* w, const float* x,
  * qmm_gemm_plan and QMM_MFMA_PLAN):
  *   0  f32 activations rounded in the k loop, 128 x 128 tiles (1 or 2 k
  *      groups); the only family of calls without a workspace;
- *   1  f16 activations from the pre-pass, register-ring tiles of 128 or 256
- *      weight rows x 128 tokens;
  *   2  the LDS ring (weight bytes and f16 activations streamed into a ring
  *      of LDS stages by buffer-to-LDS loads; weights decoded straight into
  *      the matrix-core operands), 128 or 256 weight rows x 128 tokens, 1 or
@@ -140,19 +139,22 @@ int qmm_gemm_path(float* dst, const void* w, const float* x,
  *      matrix-core op; for products of many tiles);
  *   4  the LDS ring on the f32 activations themselves (no pre-pass and no
  *      f16 workspace), 128 x 128 tiles.
+ * (Code 1 is not used.)
  * Every family rounds each decoded weight and each activation to f16 once
  * (RNE) and accumulates in f32, so the tolerance is the one of qmm_gemm.
  * The plan is a pure function of (m, k, n, qtype) and the device's
  * compute-unit count; the environment variable
  * QMM_MFMA_PLAN="x16,wm,n_split[,kg]" forces it (tuning and tests only:
- * x16 0 with wm 2; 1 with wm 2 or 4 and kg 1; 2 with wm 2 or 4; 3 or 4 with
- * wm 2; kg 1 or 2; malformed -> QMM_ERR_RANGE; a family the format or k
- * cannot run falls back to family 0 unsplit).
+ * x16 0 with wm 2; 2 with wm 2 or 4; 3 or 4 with wm 2; kg 1 or 2;
+ * malformed -> QMM_ERR_RANGE; a family the format or k cannot run falls back
+ * to family 0 unsplit).
  *   workspace        DEVICE memory, 256-byte aligned, of at least
  *                    qmm_gemm_workspace_bytes(m, k, n, qtype, path) bytes, or
  *                    NULL (then the f32-activation kernel without a k split).
  *                    No initial contents are needed.  Calls that share a
  *                    workspace must not overlap (order them on one stream).
+ *                    The bytes the plan uses must not overlap dst, x or w
+ *                    (QMM_ERR_ALIAS).
  *   workspace_bytes  its size; smaller than needed -> QMM_ERR_WORKSPACE.
  * The GEMV path ignores the workspace.  Other arguments and errors as
  * qmm_gemm_path.
@@ -185,8 +187,8 @@ int64_t qmm_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int qtype, int
  * qmm_gemm_plan: the kernels a call with these sizes runs on the current
  * device, with (with_workspace != 0: qmm_gemm_ws) or without a workspace.
  *   out  HOST int32[6], written: path (QMM_PATH_GEMV or QMM_PATH_MFMA); then
- *        for the MFMA path: the kernel family (0-4, as listed at
- *        qmm_gemm_ws; families 1-3 round the activations to f16 in a
+ *        for the MFMA path: the kernel family (0, 2, 3 or 4, as listed at
+ *        qmm_gemm_ws; families 2 and 3 round the activations to f16 in a
  *        pre-pass), weight rows per tile, k groups per work group, k
  *        splits, and 64-k steps per split (zeros on the GEMV path).
  * Errors as qmm_gemm_workspace_bytes; QMM_ERR_NULL for a null out.
@@ -314,10 +316,9 @@ int64_t qmm_row_bytes(int qtype, int64_t k);
 /* Elements per block of qtype, or -QMM_ERR_QTYPE. */
 int qmm_block_elems(int qtype);
 
-/* The largest n that QMM_PATH_AUTO sends to the GEMV (16 by default: n <= 8
- * always, 9..16 for weight matrices of at most 8 Mi elements); the
- * environment variable QMM_GEMV_MAX_N replaces the rule by the threshold it
- * gives; a set but unparseable or non-positive value makes this return
+/* The largest n that QMM_PATH_AUTO sends to the GEMV (32 by default); the
+ * environment variable QMM_GEMV_MAX_N replaces it by the threshold it gives;
+ * a set but unparseable or non-positive value makes this return
  * -QMM_ERR_RANGE and every AUTO call fail with QMM_ERR_RANGE, never a silent
  * default. */
 int qmm_gemv_max_n(void);

@@ -210,24 +210,30 @@ def _decode_q6_k(data, m, k):
     return (scale * (q - 32)).reshape(m, k)
 
 
+# The FP8 / FP4 codecs above evaluated once on every code; the NVFP4
+# decoders index these tables (the same values, element by element).
+_E4M3 = e4m3_bits_to_f64(np.arange(256))
+_E2M1 = e2m1_bits_to_f64(np.arange(16))
+
+
 def _decode_nvfp4(data, m, k):
     blk = _blocks(data, m, k, "nvfp4")
-    s = e4m3_bits_to_f64(blk[..., 0:4])                            # [m, ng, 4]
-    qs = blk[..., 4:36].astype(np.int64).reshape(m, -1, 2, 16)     # half h, byte j
+    s = _E4M3[blk[..., 0:4]]                                       # [m, ng, 4]
+    qs = blk[..., 4:36].reshape(m, -1, 2, 16)                      # half h, byte j
     out = np.empty((m, qs.shape[1], 2, 2, 16), dtype=np.float64)
     for h in range(2):
-        out[:, :, h, 0, :] = e2m1_bits_to_f64(qs[:, :, h, :] & 0xF) * s[..., 2 * h, None]
-        out[:, :, h, 1, :] = e2m1_bits_to_f64(qs[:, :, h, :] >> 4) * s[..., 2 * h + 1, None]
+        out[:, :, h, 0, :] = _E2M1[qs[:, :, h, :] & 0xF] * s[..., 2 * h, None]
+        out[:, :, h, 1, :] = _E2M1[qs[:, :, h, :] >> 4] * s[..., 2 * h + 1, None]
     return out.reshape(m, k)
 
 
 def _decode_nvfp4_v2(data, m, k):
     rows = np.asarray(data).reshape(-1).view(np.uint8).reshape(m, row_bytes("nvfp4_v2", k))
-    q = rows[:, :k // 2].astype(np.int64).reshape(m, k // 32, 16)     # group g, byte j
-    s = e4m3_bits_to_f64(rows[:, k // 2:].reshape(m, k // 32, 2))     # group g, run i
+    q = rows[:, :k // 2].reshape(m, k // 32, 16)                      # group g, byte j
+    s = _E4M3[rows[:, k // 2:].reshape(m, k // 32, 2)]                # group g, run i
     out = np.empty((m, k // 32, 2, 16), dtype=np.float64)
-    out[:, :, 0, :] = e2m1_bits_to_f64(q & 0xF) * s[:, :, 0, None]
-    out[:, :, 1, :] = e2m1_bits_to_f64(q >> 4) * s[:, :, 1, None]
+    out[:, :, 0, :] = _E2M1[q & 0xF] * s[:, :, 0, None]
+    out[:, :, 1, :] = _E2M1[q >> 4] * s[:, :, 1, None]
     return out.reshape(m, k)
 
 

@@ -52,6 +52,20 @@ def gemm_ref(name: str, w, x, m: int, k: int, n: int):
     return X @ W.T, np.abs(X) @ np.abs(W).T
 
 
+def gemm_ref_blocks(name: str, w, x, m: int, k: int, n: int, row_bytes: int, rows_per_block: int = 2048):
+    """gemm_ref over the weight rows in blocks: yields (i0, i1, ref, S) with
+    ref and S float64 [n, i1 - i0] for the rows [i0, i1), so that only one
+    block of W is decoded at a time (the whole output of large shapes with
+    bounded host memory).  ``row_bytes`` is the packed size of one row."""
+    buf = np.asarray(w).reshape(-1).view(np.uint8)
+    X = np.asarray(x, dtype=np.float32).reshape(n, k).astype(np.float64)
+    aX = np.abs(X)
+    for i0 in range(0, m, rows_per_block):
+        i1 = min(m, i0 + rows_per_block)
+        W = decode(name, buf[i0 * row_bytes:i1 * row_bytes], i1 - i0, k)
+        yield i0, i1, X @ W.T, aX @ np.abs(W).T
+
+
 def gemm_ref_rows(name: str, w, x, m: int, k: int, rows, cols, row_bytes: int):
     """(ref, S) for the sampled outputs dst[cols[t], rows[t]] only.
 
@@ -77,20 +91,18 @@ def moe_ref(name: str, w_gate, w_up, ids, scales, x, n_expert: int, in_f: int, n
     X = (np.asarray(x, dtype=np.float64) if exact_x else
          np.asarray(x, dtype=np.float32).astype(np.float64)).reshape(t, in_f)
     sc = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    flat = ids.reshape(-1)
     outs = []
     for plane, wp in enumerate((w_gate, w_up)):
         buf = np.asarray(wp).reshape(-1).view(np.uint8)
         per = buf.size // n_expert
         val = np.empty((n_pairs, n_ff))
         tol = np.empty((n_pairs, n_ff))
-        cache = {}
-        for tau in range(t):
-            for s in range(n_used):
-                e = int(ids[tau, s])
-                if e not in cache:
-                    cache[e] = decode(name, buf[e * per:(e + 1) * per], n_ff, in_f)
-                W = cache[e]
-                p = tau * n_used + s
+        # one expert's rows decoded at a time, applied to every pair that chose it
+        for e in np.unique(flat):
+            W = decode(name, buf[int(e) * per:(int(e) + 1) * per], n_ff, in_f)
+            for p in np.nonzero(flat == e)[0]:
+                tau = int(p) // n_used
                 f = sc[plane * n_pairs + p]
                 val[p] = f * (W @ X[tau])
                 tol[p] = abs(f) * (np.abs(W) @ np.abs(X[tau]))
@@ -138,14 +150,13 @@ def moe_down_ref(name: str, w_down, ids, scales, act, n_expert: int, n_ff: int, 
     per = buf.size // n_expert
     pair = np.empty((n_pairs, d_model))
     pair_S = np.empty((n_pairs, d_model))
-    cache = {}
-    for p in range(n_pairs):
-        e = int(ids.reshape(-1)[p])
-        if e not in cache:
-            cache[e] = decode(name, buf[e * per:(e + 1) * per], d_model, n_ff)
-        W = cache[e]
-        pair[p] = sc[p] * (W @ A[p])
-        pair_S[p] = abs(sc[p]) * (np.abs(W) @ np.abs(A[p]))
+    flat = ids.reshape(-1)
+    # one expert's rows decoded at a time, applied to every pair that chose it
+    for e in np.unique(flat):
+        W = decode(name, buf[int(e) * per:(int(e) + 1) * per], d_model, n_ff)
+        for p in np.nonzero(flat == e)[0]:
+            pair[p] = sc[p] * (W @ A[p])
+            pair_S[p] = abs(sc[p]) * (np.abs(W) @ np.abs(A[p]))
     y = pair.reshape(t, n_used, d_model).sum(axis=1)
     S = pair_S.reshape(t, n_used, d_model).sum(axis=1)
     return y, S, pair, pair_S

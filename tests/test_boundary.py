@@ -186,7 +186,7 @@ def test_default_gemv_max_n():
     lib = _lib()
     if "QMM_GEMV_MAX_N" in os.environ:
         pytest.skip("QMM_GEMV_MAX_N set in the environment")
-    assert lib.qmm_gemv_max_n() == 16
+    assert lib.qmm_gemv_max_n() == 32
 
 
 def test_workspace_bytes_plan_and_errors():
@@ -215,6 +215,25 @@ def test_gemm_ws_validates_before_launch():
     assert lib.qmm_gemm_ws(None, p, p, 10, 256, 40, 3, 2, None, 0, None) == 1
     # unknown path
     assert lib.qmm_gemm_ws(p, p, p, 10, 256, 40, 3, 9, None, 0, None) in (5, 7)
+
+
+def test_gemm_ws_rejects_a_workspace_overlapping_an_operand():
+    """The matrix-core kernels write the workspace (f16 activations, k-split
+    partials) while they read x and w and write dst: a workspace that
+    overlaps any of them is QMM_ERR_ALIAS (fake pointers, no launch)."""
+    lib = _lib()
+    m, k, n, qt = 1024, 4608, 512, 3
+    need = lib.qmm_gemm_workspace_bytes(m, k, n, qt, 2)
+    assert need > 0
+    dst, x, w = 1 << 30, 1 << 31, 1 << 32          # dst 2 MB, x 9.4 MB, w 2.7 MB: disjoint
+    V = ctypes.c_void_p
+    s0 = V(0)
+    for ws in (dst + 4096, x + (1 << 20), w + 256, dst - (1 << 12) * 256):
+        st = lib.qmm_gemm_ws(V(dst), V(w), V(x), m, k, n, qt, 2, V(ws), need, s0)
+        assert st == 10, (hex(ws), st)
+    # the workspace's own size decides: one ending right before dst is fine up
+    # to the launch, which never happens here (too small: QMM_ERR_WORKSPACE first)
+    assert lib.qmm_gemm_ws(V(dst), V(w), V(x), m, k, n, qt, 2, V(dst - 256), 256, s0) == 9
 
 
 def test_gemm_plan_reports_kernels():

@@ -9,7 +9,7 @@ must be bit-identical; guard bands around dst must stay untouched.
 import numpy as np
 import pytest
 
-from gpu_helpers import (TAU_F16, TAU_F32, acts, check_full, exact_weights, gpu_gemm, note,
+from gpu_helpers import (TAU_F16, TAU_F32, acts, assert_f16_weights, check_full, exact_weights, gpu_gemm, note,
                          to_dev, weights)
 from oracle import formats, ref
 from synth import gen
@@ -74,10 +74,12 @@ def test_mfma_parity_no_workspace(qt):
 
 @pytest.mark.parametrize("qt", QTS)
 def test_mfma_paths_agree_bit_for_bit_unsplit(qt):
-    """The f32- and f16-activation prefill kernels round x and W to f16 the
-    same way and order their k slots alike; unsplit, their sums run in the
-    same order, so the outputs are equal.  (The LDS-ring kernel orders the
-    slots inside each matrix-core op differently: within tolerance only.)"""
+    """The LDS-ring kernel on the pre-pass's f16 activations and on the f32
+    activations themselves (rounded as the operands are read) round x to f16
+    the same way and order their k slots alike; unsplit and with the same k
+    groups, their sums run in the same order, so the outputs are equal.  The
+    kernel without a workspace orders the slots inside each matrix-core op
+    differently: within tolerance only."""
     import os
     import gemv_prefill_decode_amd as qmm
     m, k, n = 512, 1024, 300
@@ -86,28 +88,68 @@ def test_mfma_paths_agree_bit_for_bit_unsplit(qt):
     x = acts(n, k, 50)
     a = gpu_gemm(qt, w, x, m, "mfma", workspace=None)
     check_full(qt, w, x, m, k, n, a, TAU_F16, f"agree {qt}")
-    os.environ["QMM_MFMA_PLAN"] = "1,2,1"
-    try:
-        b = gpu_gemm(qt, w, x, m, "mfma")
-    finally:
-        del os.environ["QMM_MFMA_PLAN"]
-    assert np.array_equal(a, b)
+    outs = []
+    for plan in ("2,2,1,1", "4,2,1,1"):
+        os.environ["QMM_MFMA_PLAN"] = plan
+        try:
+            p = qmm.gemm_plan(m, k, n, qt, "mfma")
+            assert p["x16"] == int(plan[0]) and p["n_split"] == 1, p
+            outs.append(gpu_gemm(qt, w, x, m, "mfma"))
+        finally:
+            del os.environ["QMM_MFMA_PLAN"]
+    assert np.array_equal(outs[0], outs[1])
+    check_full(qt, w, x, m, k, n, outs[0], TAU_F16, f"agree lds ring {qt}")
     c = gpu_gemm(qt, w, x, m, "mfma")
     check_full(qt, w, x, m, k, n, c, TAU_F16, f"agree planned {qt}")
 
 
 @pytest.mark.parametrize("qt", QTS)
 def test_auto_dispatch_threshold(qt):
-    """AUTO: the GEMV up to n = 16 for a small weight matrix, up to n = 8
-    for one of more than 8 Mi weights; the matrix-core path above."""
-    for m, k, lim in ((130, 512, 16), (2112, 4096, 8)):
-        w = weights(qt, m, k, 3)
-        for n in (lim, lim + 1):
-            note(f"auto {qt} {m}x{k} n={n}")
-            x = acts(n, k, 3)
-            got = gpu_gemm(qt, w, x, m, "auto")
-            gv = gpu_gemm(qt, w, x, m, "gemv" if n <= lim else "mfma")
-            assert np.array_equal(got, gv)
+    """AUTO: the GEMV for every n <= 32 (the f32 path), the matrix-core path
+    above; the result equals the forced path's bit for bit."""
+    m, k = 130, 512
+    w = weights(qt, m, k, 3)
+    for n in (32, 33):
+        note(f"auto {qt} {m}x{k} n={n}")
+        x = acts(n, k, 3)
+        got = gpu_gemm(qt, w, x, m, "auto")
+        gv = gpu_gemm(qt, w, x, m, "gemv" if n <= 32 else "mfma")
+        assert np.array_equal(got, gv)
+
+
+@pytest.mark.parametrize("qt", ["q4_0", "q4_k", "q6_k", "f32"])
+def test_qmm_gemm_entry_points_through_ctypes(qt):
+    """qmm_gemm and qmm_gemm_path called through the C-ABI themselves (no
+    binding wrapper) at n on both sides of the dispatch threshold, each
+    result against the oracle at the tolerance of the path it takes (n <= 32:
+    the f32 GEMV, 1e-5; above: the f16 matrix cores, 2e-3)."""
+    import ctypes
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    lib = qmm.load()
+    m, k = 300, 1024
+    w = weights(qt, m, k, 31)
+    dw = to_dev(w)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    qi = qmm.QTYPES[qt]
+    for n in (8, 9, 16, 17, 32, 33):
+        note(f"ctypes qmm_gemm {qt} n={n}")
+        x = acts(n, k, 31 + n)
+        dx = to_dev(x)
+        tau = TAU_F32 if n <= 32 else TAU_F16
+        out = torch.full((n, m), float("nan"), dtype=torch.float32, device="cuda")
+        st = lib.qmm_gemm(out.data_ptr(), dw.data_ptr(), dx.data_ptr(), m, k, n, qi, s)
+        torch.cuda.synchronize()
+        assert st == 0, qmm.status_str(st)
+        check_full(qt, w, x, m, k, n, out.cpu().numpy(), tau, f"qmm_gemm {qt} n={n}")
+        for path, ptau in ((1, TAU_F32), (2, TAU_F16), (0, tau)):
+            out2 = torch.full((n, m), float("nan"), dtype=torch.float32, device="cuda")
+            st = lib.qmm_gemm_path(out2.data_ptr(), dw.data_ptr(), dx.data_ptr(), m, k, n, qi, path, s)
+            torch.cuda.synchronize()
+            assert st == 0, qmm.status_str(st)
+            check_full(qt, w, x, m, k, n, out2.cpu().numpy(), ptau, f"qmm_gemm_path {qt} n={n} path={path}")
+            if path == 0:
+                assert torch.equal(out, out2)
 
 
 @pytest.mark.parametrize("qt", QTS)
@@ -137,8 +179,7 @@ def test_identity_activations_mfma(qt):
     x = np.eye(k, dtype=np.float32)
     got = gpu_gemm(qt, w, x, m, "mfma")
     W = formats.decode(qt, w, m, k)
-    want = W.T.astype(np.float16).astype(np.float64)   # numpy rounds f64 -> f16 once, RNE
-    assert np.array_equal(got.astype(np.float64), want)
+    assert_f16_weights(got, W)
 
 
 # The LDS-ring kernel assigns k to operand slots per format and lays the f16
@@ -161,8 +202,7 @@ def test_lds_ring_identity_and_exact(qt, plan, monkeypatch):
     x = np.eye(k, dtype=np.float32)
     got = gpu_gemm(qt, w, x, m, "mfma")
     W = formats.decode(qt, w, m, k)
-    want = W.T.astype(np.float16).astype(np.float64)   # numpy rounds f64 -> f16 once, RNE
-    assert np.array_equal(got.astype(np.float64), want)
+    assert_f16_weights(got, W)
     note(f"lds ring exact {qt} {plan}")
     we = exact_weights(qt, m, k, 8)
     xe = gen.structured_exact(150 * k, 12).reshape(150, k)
@@ -442,7 +482,7 @@ def test_split_k_shared_workspace_growing_tile_count():
 # Every prefill kernel family, forced through QMM_MFMA_PLAN on a ragged shape
 # (m, n not multiples of any tile; k with a partial split): x16, tile rows
 # (wm*64), k splits, k groups.
-FORCED_PLANS = ["0,2,1,1", "0,2,3,1", "0,2,1,2", "0,2,3,2", "1,2,1", "1,2,3", "1,4,1", "1,4,3",
+FORCED_PLANS = ["0,2,1,1", "0,2,3,1", "0,2,1,2", "0,2,3,2",
                 "2,2,1", "2,2,3", "2,4,1", "2,4,3", "3,2,1", "3,2,3", "2,2,1,2", "2,2,3,2", "3,2,1,2", "3,2,3,2",
                 "4,2,1", "4,2,3", "4,2,1,2", "4,2,3,2"]
 
@@ -608,7 +648,7 @@ def test_moe_q8_exact_activations_match_f32_path():
 
 # ------------------------------------------------------------------ strided x and dst
 
-@pytest.mark.parametrize("plan", [None, "0,2,1,1", "0,2,3,2", "1,2,1", "1,4,3", "2,2,1", "2,4,3", "3,2,2",
+@pytest.mark.parametrize("plan", [None, "0,2,1,1", "0,2,3,2", "2,2,1", "2,4,3", "3,2,2",
                                   "4,2,1", "4,2,2,2"])
 @pytest.mark.parametrize("qt", ["q4_k", "f32"])
 def test_strided_rows_bit_identical(qt, plan, monkeypatch):

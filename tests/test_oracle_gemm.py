@@ -341,3 +341,84 @@ def test_planted_mistakes_are_caught(monkeypatch):
     data = np.frombuffer(enc.q4_0(0xBC00, list(range(16)) * 2), np.uint8)
     got = formats.decode("q4_0", data, 1, 32)[0]
     assert not np.array_equal(got, -1.0 * (np.array(list(range(16)) * 2) - 8.0))
+
+
+@pytest.mark.parametrize("qt", QTS)
+def test_gemm_value_brute_force(qt):
+    """gemm_value (the function the CPU baseline times) against the literal
+    scalar decoder with exactly rounded sums, on tiny shapes that span
+    several blocks; and equal to gemm_ref's value on a larger shape."""
+    import math
+    k = 2 * max(formats.block_elems(qt), 32)
+    for m, n in ((1, 1), (3, 2), (2, 5)):
+        w = _weights(qt, m, k, 41 + m)
+        x = gen.unit_f32(n * k, 43 + n).reshape(n, k)
+        v = ref.gemm_value(qt, w, x, m, k, n)
+        data = bytes(np.asarray(w).view(np.uint8))
+        W = scalar.decode_matrix(qt, data, m, k)
+        bf = np.array(scalar.gemm(qt, data, x.tolist(), m, k, n))
+        S = np.array([[math.fsum(abs(W[i][c] * float(x[j][c])) for c in range(k)) for i in range(m)]
+                      for j in range(n)])
+        assert v.shape == (n, m)
+        assert np.all(np.abs(v - bf) <= 1e-12 * S + 1e-300)
+    m, k, n = 37, 4 * max(formats.block_elems(qt), 64), 11
+    w = _weights(qt, m, k, 47)
+    x = gen.unit_f32(n * k, 48).reshape(n, k)
+    r, _ = ref.gemm_ref(qt, w, x, m, k, n)
+    assert np.array_equal(ref.gemm_value(qt, w, x, m, k, n), r)
+
+
+@pytest.mark.parametrize("qt", ["q4_k", "q6_k", "nvfp4", "f32"])
+def test_gemm_ref_blocks_cover_the_whole_output(qt):
+    """The row-blocked reference (whole outputs of large shapes) tiles the
+    full one: every row block equals the same rows of gemm_ref, blocks in
+    order with a ragged last block."""
+    m, k, n = 300, 2 * max(formats.block_elems(qt), 64), 7
+    w = _weights(qt, m, k, 51)
+    x = gen.unit_f32(n * k, 52).reshape(n, k)
+    r, S = ref.gemm_ref(qt, w, x, m, k, n)
+    seen = 0
+    for i0, i1, rb_, sb in ref.gemm_ref_blocks(qt, w, x, m, k, n, formats.row_bytes(qt, k), 128):
+        assert i0 == seen and i1 - i0 == min(128, m - i0)
+        assert np.allclose(rb_, r[:, i0:i1], rtol=1e-14, atol=1e-300)
+        assert np.allclose(sb, S[:, i0:i1], rtol=1e-14, atol=1e-300)
+        seen = i1
+    assert seen == m
+
+
+def test_moe_pairs_rows_exact_x_branch():
+    """moe_ref_pairs_rows with exact_x (the reference of the Q8_1 gate/up at
+    full size) uses the float64 activations as given: against the full
+    moe_q8_ref on the same pairs, and against the literal decoder with
+    activations that float32 cannot hold (x = q/3), where the float32 branch
+    would differ."""
+    n_expert, in_f, n_ff, t, n_used = 5, 128, 6, 3, 2
+    wg = np.concatenate([gen.nvfp4_rows(n_ff, in_f, 0x8181 + 2 * e) for e in range(n_expert)])
+    wu = np.concatenate([gen.nvfp4_rows(n_ff, in_f, 0x8181 + 2 * e + 1) for e in range(n_expert)])
+    ids = gen.expert_ids(t, n_used, n_expert, 13)
+    sc = gen.pair_scales(2 * t * n_used)
+    x = gen.xorshift_f32(t * in_f, 91)
+    xq, xd = ref.quantize_q8_1(x, in_f)
+    g, u, Sg, Su = ref.moe_q8_ref("nvfp4", wg, wu, ids, sc, xq, xd, n_expert, in_f, n_ff)
+    xh = ref.dequantize_q8_1(xq, xd, in_f)
+    n_pairs = t * n_used
+    pairs = np.repeat(np.arange(n_pairs), n_ff)
+    rows = np.tile(np.arange(n_ff), n_pairs)
+    for plane, wp, full, Sfull in ((0, wg, g, Sg), (1, wu, u, Su)):
+        val, tol = ref.moe_ref_pairs_rows("nvfp4", wp, ids, sc, xh, plane, n_expert, in_f, n_ff,
+                                          pairs, rows, exact_x=True)
+        assert np.allclose(val, full[pairs, rows], rtol=1e-13, atol=1e-300)
+        assert np.allclose(tol, Sfull[pairs, rows], rtol=1e-13, atol=1e-300)
+    # activations off the float32 grid: exact_x keeps them, float32 rounds them
+    rng = np.random.default_rng(3)
+    x3 = rng.integers(-300, 301, (t, in_f)) / 3.0
+    per = n_ff * formats.row_bytes("nvfp4", in_f)
+    p, r = 3, 4
+    e = int(ids.reshape(-1)[p])
+    row = bytes(wg[e * per:(e + 1) * per])
+    want = float(np.float64(sc[p])) * float(np.dot(scalar.decode_matrix("nvfp4", row, n_ff, in_f)[r],
+                                                   x3[p // n_used]))
+    v64, _ = ref.moe_ref_pairs_rows("nvfp4", wg, ids, sc, x3, 0, n_expert, in_f, n_ff, [p], [r], exact_x=True)
+    v32, _ = ref.moe_ref_pairs_rows("nvfp4", wg, ids, sc, x3, 0, n_expert, in_f, n_ff, [p], [r])
+    assert abs(v64[0] - want) <= 1e-12 * max(1.0, abs(want))
+    assert abs(v32[0] - want) > 1e-9 * max(1.0, abs(want))
