@@ -487,14 +487,17 @@ PLAN_SHAPES = [("ffn_gate", 4608, 1024, 512), ("ffn_down", 1024, 4608, 512), ("c
 PLAN_FAMILIES = ["0,2,1,2", "2,2,1", "2,2,1,2", "3,2,1", "3,2,1,2", "4,2,1,2"]
 
 
-def run_prefill_plans():
+def run_prefill_plans(families=None, shapes=None):
     """The planned prefill kernel against forced kernel families, unsplit, per
-    LFM2 and 8B-class shape and format (graph of 8 calls, median of 5)."""
+    LFM2 and 8B-class shape and format (graph of 8 calls, median of 5).
+    families / shapes: restrict to these QMM_MFMA_PLAN codes / shape labels."""
     import torch
     import gemv_prefill_decode_amd as qmm
     from synth import gen
     rows = []
     for label, m, k, n in PLAN_SHAPES:
+        if shapes and label not in shapes:
+            continue
         qts = ["q4_k", "q6_k"] if label.startswith("8b") else QTS
         x = to_dev(gen.unit_f32(n * k, gen.SEED_X + k).reshape(n, k))
         for qi, qt in enumerate(qts):
@@ -502,14 +505,15 @@ def run_prefill_plans():
             out = torch.empty((n, m), dtype=torch.float32, device="cuda")
             # the planned kernel last: the row's first graphs also warm the
             # clocks and bring the fresh weights in
-            for force in PLAN_FAMILIES + [None]:
+            for force in (families or PLAN_FAMILIES) + [None]:
                 if force is None:
                     os.environ.pop("QMM_MFMA_PLAN", None)
                 else:
                     os.environ["QMM_MFMA_PLAN"] = force
                 plan = qmm.gemm_plan(m, k, n, qt, "mfma")
-                if force is not None and (plan["x16"], plan["k_groups"]) != (
-                        int(force.split(",")[0]), int(force.split(",")[3]) if force.count(",") == 3 else 1):
+                if force is not None and (plan["x16"], plan["k_groups"], plan["n_split"]) != (
+                        int(force.split(",")[0]), int(force.split(",")[3]) if force.count(",") == 3 else 1,
+                        int(force.split(",")[2])):
                     continue  # a family this format does not run
                 ws = torch.empty(max(qmm.workspace_bytes(m, k, n, qt, "mfma"), 256), dtype=torch.uint8,
                                  device="cuda")
@@ -526,6 +530,83 @@ def run_prefill_plans():
             del w, out
             torch.cuda.empty_cache()
     print(json.dumps({"prefill_plans": rows}), flush=True)
+
+
+COUNTER_SETS = [
+    # (rocprofv3 --pmc set, one run each: at most 8 SQ counters per run)
+    "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES "
+    "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_ANY",
+    "SQ_WAVE_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_MISC "
+    "SQ_INSTS_SALU SQ_VALU_MFMA_COEXEC_CYCLES SQ_WAIT_ANY",
+]
+COUNTER_SHAPES = [("q4_0_1024_n64", "q4_0", 1024, 1024, 64)] + \
+    [(f"lfm2_{label}_{qt}", qt, m, k, 512) for qt in QTS for (label, m, k) in SHAPES] + \
+    [(f"8b_{m}x{k}_{qt}", qt, m, k, 2048) for qt in ("q4_k", "q6_k") for (m, k) in ((14336, 4096), (4096, 14336))]
+
+
+def run_counter_workload():
+    """The prefill calls of every headline configuration, three times each
+    (synchronized), for rocprofv3 --pmc runs: the Q4_0 1024x1024 n=64 GEMM,
+    the 20 LFM2 n=512 GEMMs and the four 8B-class n=2048 GEMMs, each with
+    the workspace bench.py uses."""
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    from synth import gen
+    for tag, qt, m, k, n in COUNTER_SHAPES:
+        w = to_dev(gen_weights(qt, m, k, 3))
+        x = to_dev(gen.unit_f32(n * k, gen.SEED_X + k).reshape(n, k))
+        out = torch.empty((n, m), dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            qmm.gemm(w, x, m, qt, out=out, path="mfma")
+        torch.cuda.synchronize()
+        plan = qmm.gemm_plan(m, k, n, qt, "mfma")
+        print(json.dumps({"tag": tag, "qt": qt, "m": m, "k": k, "n": n,
+                          "kernel": qmm.plan_kernel_name(plan, qt),
+                          "grid": plan_grid_size(plan, m, n)}), flush=True)
+        del w, x, out
+        torch.cuda.empty_cache()
+
+
+def mfma_counter_summary(tags_path, csv_paths, out_path):
+    """profiles/mfma_counters_prefill.md from --counter-workload's printed
+    tags and the counter_collection.csv of each --pmc run: per GEMM kernel
+    dispatch (kernel name and grid size), MFMA flops from
+    SQ_INSTS_VALU_MFMA_MOPS_F16 (x 512) against 2mkn, matrix cores busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / (SQ_BUSY_CYCLES x 32 SIMDs per shader
+    engine), VALU and LDS instructions per MFMA, waits."""
+    import csv
+    import collections
+    tags = [json.loads(ln) for ln in open(tags_path) if ln.startswith("{")]
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("qmm::", "").strip()
+            vals[(name, int(r["Grid_Size"]))][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    rows = []
+    for t in tags:
+        key = (t["kernel"], t["grid"])
+        c = {k: statistics.mean(v) for k, v in vals.get(key, {}).items()}
+        if not c:
+            continue
+        flops = 2.0 * t["m"] * t["k"] * t["n"]
+        mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_F16", float("nan")) * 512
+        mfma = c.get("SQ_INSTS_MFMA", float("nan"))
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (c.get("SQ_BUSY_CYCLES", float("nan")) * 32)
+        rows.append((t["tag"], t["kernel"], t["grid"], mops / flops, busy,
+                     c.get("SQ_INSTS_VALU", float("nan")) / mfma, c.get("SQ_INSTS_LDS", float("nan")) / mfma,
+                     c.get("SQ_LDS_BANK_CONFLICT", float("nan")),
+                     c.get("SQ_WAIT_INST_ANY", float("nan")) / c.get("SQ_WAVE_CYCLES", float("nan")),
+                     c.get("SQ_ACTIVE_INST_VALU", float("nan")) / c.get("SQ_WAVE_CYCLES", float("nan")),
+                     c.get("SQ_VALU_MFMA_COEXEC_CYCLES", float("nan")) /
+                     c.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan"))))
+    with open(out_path, "w") as f:
+        f.write("| config | kernel | grid | MFMA flops / 2mkn | matrix cores busy | VALU / MFMA | "
+                "LDS / MFMA | LDS bank conflicts | wait-inst / wave cycles | VALU-active / wave cycles | "
+                "VALU co-issued / MFMA busy |\n|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|\n")
+        for r in rows:
+            f.write(f"| {r[0]} | `{r[1]}` | {r[2]} | {r[3]:.3f} | {100 * r[4]:.1f}% | {r[5]:.2f} | {r[6]:.2f} | "
+                    f"{r[7]:.0f} | {r[8]:.3f} | {r[9]:.3f} | {r[10]:.3f} |\n")
+    print(open(out_path).read())
 
 
 def copy_probe():
@@ -641,13 +722,24 @@ def main():
                     help="only measure GEMV vs matrix-core time over n (prints its own JSON)")
     ap.add_argument("--prefill-plans", action="store_true",
                     help="only time the planned prefill kernel against forced kernel families (own JSON)")
+    ap.add_argument("--plans", default=None,
+                    help="with --prefill-plans: forced QMM_MFMA_PLAN codes separated by ';'")
+    ap.add_argument("--plan-shapes", default=None,
+                    help="with --prefill-plans: shape labels separated by ',' (ffn_gate, 8b_up, ...)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run the 1 GiB copy that calibrates the HBM byte counters")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--counter-workload", action="store_true",
+                    help="only run every headline prefill GEMM three times (for rocprofv3 --pmc runs)")
+    ap.add_argument("--mfma-summary", nargs="+", metavar="FILE",
+                    help="TAGS OUT_MD CSV...: the MFMA counter table from --counter-workload runs")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], os.path.join(ROOT, "profiles", "traffic.json"))
+        return
+    if args.mfma_summary:
+        mfma_counter_summary(args.mfma_summary[0], args.mfma_summary[2:], args.mfma_summary[1])
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; there is no multi-GPU path (asked for --gpus {args.gpus})",
@@ -666,7 +758,11 @@ def main():
         run_crossover()
         return
     if args.prefill_plans:
-        run_prefill_plans()
+        run_prefill_plans(args.plans.split(";") if args.plans else None,
+                          args.plan_shapes.split(",") if args.plan_shapes else None)
+        return
+    if args.counter_workload:
+        run_counter_workload()
         return
     if args.copy_probe:
         log("copy probe: 3 x 1 GiB device copies")
