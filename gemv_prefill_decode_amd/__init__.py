@@ -65,6 +65,10 @@ def load() -> ctypes.CDLL:
         lib.qmm_gemm_ex.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, i32, i32, vp, i64, vp]
         lib.qmm_gemm_ex.restype = i32
         lib.qmm_gemm_ws.restype = i32
+        lib.qmm_gemm_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, vp]
+        lib.qmm_gemm_noalloc.restype = i32
+        lib.qmm_gemm_noalloc_max_bytes.argtypes = []
+        lib.qmm_gemm_noalloc_max_bytes.restype = i64
         lib.qmm_gemm_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
         lib.qmm_gemm_workspace_bytes.restype = i64
         lib.qmm_gemm_plan.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(ctypes.c_int32)]

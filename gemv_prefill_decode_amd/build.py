@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libqmm.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["gemv.hip", "moe.hip", "gemm_mfma.hip", "gemm_lds.hip", "qmm_api.cpp"]
+SOURCES = ["gemv.hip", "moe.hip", "gemm_mfma.hip", "gemm_lds.hip", "noalloc.hip", "qmm_api.cpp"]
 ARCH = os.environ.get("QMM_OFFLOAD_ARCH", "gfx950")
 
 

@@ -309,6 +309,7 @@ const char* qmm_status_str(int s) {
         case QMM_ERR_RANGE: return "size outside the kernels' index range (or bad QMM_GEMV_MAX_N)";
         case QMM_ERR_WORKSPACE: return "workspace smaller than qmm_gemm_workspace_bytes()";
         case QMM_ERR_ALIAS: return "an output overlaps an input";
+        case QMM_ERR_SCRATCH: return "product needs more workspace than the library's static scratch holds";
     }
     return "unknown status";
 }

@@ -76,7 +76,9 @@ typedef enum {
     QMM_ERR_PATH = 7,      /* unknown path selector                            */
     QMM_ERR_RANGE = 8,     /* a size exceeds what the kernels index (see below) */
     QMM_ERR_WORKSPACE = 9, /* workspace smaller than qmm_gemm_workspace_bytes()  */
-    QMM_ERR_ALIAS = 10     /* an output overlaps an input that must stay intact  */
+    QMM_ERR_ALIAS = 10,    /* an output overlaps an input that must stay intact  */
+    QMM_ERR_SCRATCH = 11   /* qmm_gemm_noalloc: the plan needs more than the
+                              library's static scratch holds                    */
 } qmm_status;
 
 /* Kernel path selector for qmm_gemm_path. */
@@ -178,6 +180,32 @@ int qmm_gemm_ws(float* dst, const void* w, const float* x, int64_t m, int64_t k,
  */
 int qmm_gemm_ex(float* dst, int64_t ldd, const void* w, const float* x, int64_t ldx, int64_t m, int64_t k,
                 int64_t n, int qtype, int path, void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * qmm_gemm_noalloc: qmm_gemm_ws without caller memory, for callers that
+ * cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is the library's own
+ * static device array of qmm_gemm_noalloc_max_bytes() bytes (64 MiB), one
+ * per GPU, held until the process ends; nothing is allocated by the call.
+ *   Arguments and errors as qmm_gemm_path, plus QMM_ERR_SCRATCH when
+ *   qmm_gemm_workspace_bytes(m, k, n, qtype, path) exceeds the array (no
+ *   launch; such products can still run through qmm_gemm, unsplit, or
+ *   qmm_gemm_ws with caller memory).  The plan, kernels and results are
+ *   those of qmm_gemm_ws with a workspace of that size, bit for bit.
+ *   The first call on a device looks up that device's address of the array
+ *   (hipGetSymbolAddress, not a stream operation); QMM_ERR_LAUNCH if the
+ *   runtime cannot give it.
+ *   Every call on one GPU shares that GPU's array: calls that may overlap
+ *   in time on one GPU (different streams without ordering, several host
+ *   threads) race and must not be issued; calls ordered on one stream are
+ *   safe.  The array needs no initial contents; it keeps whatever the last
+ *   call left.
+ */
+int qmm_gemm_noalloc(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
+                     int qtype, int path, hipStream_t stream);
+
+/* Bytes of qmm_gemm_noalloc's static scratch array (per GPU). */
+int64_t qmm_gemm_noalloc_max_bytes(void);
 
 /* Workspace bytes qmm_gemm_ws uses for this product on the current device:
  * 0 on the GEMV path, at least 256 on the MFMA path; < 0 is -qmm_status. */
