@@ -14,7 +14,8 @@ from its definition, in float64, and contracts with a plain f64 matmul.
 Modules
   formats  vectorized numpy block decoders (exact in f64) + element codecs
   scalar   a literal per-element pure-Python decoder for tiny inputs
-  ref      the f64 reference GEMM / MoE gate-up and the tolerance scale S
+  ref      the f64 reference GEMM, MoE gate/up, SwiGLU/clamp activation and
+           down projection (f32 or Q8_1 activations), and the tolerance scale S
 
 Every decoder is pinned in ``tests/test_oracle_*.py`` against hand-built
 blocks, library routines (numpy float16, torch float8/float4 dtypes),

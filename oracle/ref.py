@@ -27,8 +27,16 @@ scale, the result accumulated into a zeroed y over the token's pairs):
 with the slots s taken in order; S_y sums |scale[p] * Wd[e_p][r, c] * act[p, c]|.
 
 Q8_1 activations (the served arithmetic of the same page): x is replaced by
-its per-32 quantization d*q (quantize_q8_1 below) and the gate/up is the
-projection of those dequantized activations.
+its per-32 quantization d*q (quantize_q8_1 below) and the gate/up (or the
+down projection, on each pair's activation row) is the projection of those
+dequantized activations.
+
+The activation between gate/up and down (a reading of the same page's
+"preclamp" gate/up with argument 7.0 and its "swiglu output"):
+
+    act[p, r] = silu(min(gate[p, r], L)) * clamp(up[p, r], -L, L)
+
+with silu(z) = z / (1 + exp(-z)).
 """
 
 from __future__ import annotations
@@ -138,13 +146,17 @@ def moe_ref_pairs_rows(name: str, w_plane, ids, scales, x, plane: int, n_expert:
     return val, tol
 
 
-def moe_down_ref(name: str, w_down, ids, scales, act, n_expert: int, n_ff: int, d_model: int):
+def moe_down_ref(name: str, w_down, ids, scales, act, n_expert: int, n_ff: int, d_model: int,
+                 exact_act: bool = False):
     """(y, S_y, pair, S_pair): y and S_y float64 [t, d_model]; the per-pair
-    terms scale[p] * Wd[e_p] @ act[p] and their S as float64 [n_pairs, d_model]."""
+    terms scale[p] * Wd[e_p] @ act[p] and their S as float64 [n_pairs, d_model].
+    act is float32 (exact_act: float64 values used as they are, e.g. Q8_1
+    activations d*q dequantized exactly)."""
     ids = np.asarray(ids, dtype=np.int64)
     t, n_used = ids.shape
     n_pairs = t * n_used
-    A = np.asarray(act, dtype=np.float32).reshape(n_pairs, n_ff).astype(np.float64)
+    A = (np.asarray(act, dtype=np.float64) if exact_act else
+         np.asarray(act, dtype=np.float32).astype(np.float64)).reshape(n_pairs, n_ff)
     sc = np.asarray(scales, dtype=np.float32).astype(np.float64)
     buf = np.asarray(w_down).reshape(-1).view(np.uint8)
     per = buf.size // n_expert
@@ -185,6 +197,53 @@ def moe_down_ref_rows(name: str, w_down, ids, scales, act, n_expert: int, n_ff: 
     return val, tol
 
 
+# |d/dz silu(z)| <= 1.0999 for every real z (its extremes are at z = +-2.3994:
+# sigma(z)(1 + z(1 - sigma(z))) = 1.0998 and -0.0998).
+SILU_LIPSCHITZ = 1.1
+
+
+def swiglu_clamp(g, u, limit: float):
+    """The activation between the MoE gate/up and down projections, float64.
+
+    The memra page serves its gate/up as `moe_gate_up_preclamp8_q8_rows(...,
+    7.0, ...)` and feeds its down arm "a synthetic swiglu output"; the clamp
+    it applies before the activation is not spelled out.  Reading: the gate
+    is clamped above at `limit`, the up projection to [-limit, limit], then
+    SwiGLU: silu(g') * u' with silu(z) = z / (1 + exp(-z)).  limit = inf is
+    plain SwiGLU.  NaN inputs stay NaN (np.minimum / np.maximum propagate
+    them)."""
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    gc = np.minimum(g, limit)
+    uc = np.maximum(np.minimum(u, limit), -limit)
+    with np.errstate(over="ignore"):
+        return gc / (1.0 + np.exp(-gc)) * uc
+
+
+def moe_act_ref(name: str, w_gate, w_up, ids, scales, x, n_expert: int, in_f: int, n_ff: int,
+                limit: float, tau: float, exact_x: bool = False):
+    """(act, S) float64 [n_pairs, n_ff]: swiglu_clamp of the gate and up
+    projections of moe_ref, with the tolerance scale carried through it.
+
+    A device result computes the projections within tau*S_g and tau*S_u of
+    the exact ones, then the epilogue in f32.  The clamps are 1-Lipschitz and
+    silu is SILU_LIPSCHITZ-Lipschitz, so with gc, uc the clamped exact
+    projections and s = silu(gc):
+        |act' - act| <= tau*(SILU_LIPSCHITZ*|uc|*S_g + |s|*S_u)
+                        + SILU_LIPSCHITZ*tau^2*S_g*S_u + (f32 epilogue rounding),
+    the last at most 8 f32 ulps of |act| (exp, add, divide, multiply).  S is
+    that bound divided by tau, so |act' - act| <= tau*S is the pass test."""
+    g, u, Sg, Su = moe_ref(name, w_gate, w_up, ids, scales, x, n_expert, in_f, n_ff, exact_x=exact_x)
+    gc = np.minimum(g, limit)
+    uc = np.maximum(np.minimum(u, limit), -limit)
+    with np.errstate(over="ignore"):
+        s = gc / (1.0 + np.exp(-gc))
+    act = s * uc
+    S = (SILU_LIPSCHITZ * np.abs(uc) * Sg + np.abs(s) * Su + SILU_LIPSCHITZ * tau * Sg * Su
+         + 2.0 ** -20 * np.abs(act) / tau)
+    return act, S
+
+
 def quantize_q8_1(x, k: int):
     """Q8_1 activations (memra `moe_rows_ceiling_bench.rs` quantizes x with
     quantize_q8_1 before the served kernel; the pages name the ggml format
@@ -217,6 +276,15 @@ def moe_q8_ref(name: str, w_gate, w_up, ids, scales, xq, xd, n_expert: int, in_f
     by the group and block scales, compute).  (gate, up, S_gate, S_up)."""
     xh = dequantize_q8_1(xq, xd, in_f)
     return moe_ref(name, w_gate, w_up, ids, scales, xh, n_expert, in_f, n_ff, exact_x=True)
+
+
+def moe_down_q8_ref(name: str, w_down, ids, scales, aq, ad, n_expert: int, n_ff: int, d_model: int):
+    """The down projection of Q8_1 pair activations (the memra page's down
+    arm quantizes each pair's activation row with quantize_q8_1 before
+    moe_down8_fma_q8_rows): moe_down_ref on the dequantized rows d*q.
+    (y, S_y, pair, S_pair)."""
+    ah = dequantize_q8_1(aq, ad, n_ff)
+    return moe_down_ref(name, w_down, ids, scales, ah, n_expert, n_ff, d_model, exact_act=True)
 
 
 def tolerance_check(got, ref, S, tau: float):

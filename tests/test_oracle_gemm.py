@@ -422,3 +422,148 @@ def test_moe_pairs_rows_exact_x_branch():
     v32, _ = ref.moe_ref_pairs_rows("nvfp4", wg, ids, sc, x3, 0, n_expert, in_f, n_ff, [p], [r])
     assert abs(v64[0] - want) <= 1e-12 * max(1.0, abs(want))
     assert abs(v32[0] - want) > 1e-9 * max(1.0, abs(want))
+
+
+# ------------------------------------------------------------ SwiGLU/clamp epilogue
+
+def test_swiglu_clamp_closed_forms_and_clamp_edges():
+    """Values fixed by the definition: silu(0) = 0; the logistic function
+    at 1 is 0.7310585786300049 (and 1 - that at -1); the gate clamp is
+    flat above L and the up clamp flat outside [-L, L]; NaN stays NaN; a
+    very negative gate gives -0, not NaN; limit = inf is plain SwiGLU."""
+    L = 7.0
+    f = ref.swiglu_clamp
+    assert f(0.0, 3.0, L) == 0.0
+    assert abs(f(1.0, 1.0, L) - 0.7310585786300049) <= 1e-16
+    assert abs(f(-1.0, 1.0, L) - (-1.0) * (1.0 - 0.7310585786300049)) <= 1e-16
+    top = f(L, 1.0, L)
+    for g in (L, L + 1e-9, 8.0, 50.0, 1e30):
+        assert f(g, 1.0, L) == top                       # gate clamped above at L
+    assert f(L - 1e-3, 1.0, L) < top
+    for u, want in ((L, L), (L + 0.5, L), (1e30, L), (-L, -L), (-L - 0.5, -L), (-1e30, -L), (3.0, 3.0)):
+        assert f(2.0, u, L) == f(2.0, 1.0, L) * want     # up clamped to [-L, L]
+    assert f(-1e9, 5.0, L) == 0.0 and not np.isnan(f(-1e9, 5.0, L))
+    assert np.isnan(f(np.nan, 1.0, L)) and np.isnan(f(1.0, np.nan, L))
+    assert f(10.0, 10.0, np.inf) == f(10.0, 1.0, np.inf) * 10.0
+    assert f(10.0, 10.0, np.inf) > f(10.0, 10.0, L)
+
+
+def test_swiglu_silu_matches_library_logistic():
+    """silu(z) = z * expit(z) with scipy's logistic function (a library
+    routine independent of the oracle's expression), for |z| up to 40."""
+    from scipy.special import expit
+    rng = np.random.default_rng(4)
+    z = np.concatenate([rng.uniform(-40, 40, 5000), np.linspace(-8, 8, 1601)])
+    got = ref.swiglu_clamp(z, np.ones_like(z), np.inf)
+    want = z * expit(z)
+    assert np.all(np.abs(got - want) <= 4e-16 * np.maximum(1.0, np.abs(want)))
+
+
+def test_silu_lipschitz_bound_is_tight():
+    """The derivative sigma(z)(1 + z(1 - sigma(z))) stays within
+    +-SILU_LIPSCHITZ, and its extremes come within 0.1% of it."""
+    from scipy.special import expit
+    z = np.linspace(-60, 60, 1200001)
+    s = expit(z)
+    d = s * (1 + z * (1 - s))
+    assert np.max(np.abs(d)) < ref.SILU_LIPSCHITZ
+    assert np.max(np.abs(d)) > 0.999 * 1.0998
+
+
+def _act_case(t=3, n_used=2, n_expert=5, in_f=128, n_ff=7, seed=5):
+    wg = np.concatenate([gen.nvfp4_rows(n_ff, in_f, 0x8181 + 2 * e) for e in range(n_expert)])
+    wu = np.concatenate([gen.nvfp4_rows(n_ff, in_f, 0x8181 + 2 * e + 1) for e in range(n_expert)])
+    ids = gen.expert_ids(t, n_used, n_expert, seed)
+    sc = gen.pair_scales(2 * t * n_used) * 20.0        # large enough that the clamps act
+    x = gen.xorshift_f32(t * in_f, 91)
+    return wg, wu, ids, sc.astype(np.float32), x
+
+
+def test_moe_act_ref_brute_force():
+    """act against the literal scalar decoder, exactly rounded sums and
+    math.exp, pair by pair; the scales make some projections exceed L."""
+    import math
+    n_expert, in_f, n_ff, t, n_used = 5, 128, 7, 3, 2
+    wg, wu, ids, sc, x = _act_case(t, n_used, n_expert, in_f, n_ff)
+    L = 7.0
+    act, S = ref.moe_act_ref("nvfp4", wg, wu, ids, sc, x, n_expert, in_f, n_ff, L, 1e-5)
+    per = n_ff * formats.row_bytes("nvfp4", in_f)
+    n_pairs = t * n_used
+    clamped = 0
+    for p in range(n_pairs):
+        tau_, e = p // n_used, int(ids.reshape(-1)[p])
+        xt = [float(v) for v in x[tau_ * in_f:(tau_ + 1) * in_f]]
+        Wg = scalar.decode_matrix("nvfp4", bytes(wg[e * per:(e + 1) * per]), n_ff, in_f)
+        Wu = scalar.decode_matrix("nvfp4", bytes(wu[e * per:(e + 1) * per]), n_ff, in_f)
+        for r in range(n_ff):
+            g = float(sc[p]) * math.fsum(a * b for a, b in zip(Wg[r], xt))
+            u = float(sc[n_pairs + p]) * math.fsum(a * b for a, b in zip(Wu[r], xt))
+            clamped += (g > L) + (abs(u) > L)
+            gc, uc = min(g, L), max(-L, min(u, L))
+            want = gc / (1.0 + math.exp(-gc)) * uc
+            assert abs(act[p, r] - want) <= 1e-12 * max(1.0, abs(want))
+            assert S[p, r] >= 0.0
+    assert clamped > 0
+
+
+def test_moe_act_tolerance_covers_worst_perturbations():
+    """The propagated tolerance: projections moved by up to tau*S_g and
+    tau*S_u (every sign combination, and random interior points) and the
+    epilogue then evaluated in float32 stay within tau*S_act of the exact
+    activation.  A planted mistake (the S_u term dropped) is caught."""
+    n_expert, in_f, n_ff, t, n_used = 5, 128, 7, 3, 2
+    wg, wu, ids, sc, x = _act_case(t, n_used, n_expert, in_f, n_ff)
+    tau, L = 1e-5, 7.0
+    g, u, Sg, Su = ref.moe_ref("nvfp4", wg, wu, ids, sc, x, n_expert, in_f, n_ff)
+    act, S = ref.moe_act_ref("nvfp4", wg, wu, ids, sc, x, n_expert, in_f, n_ff, L, tau)
+
+    def epi32(gv, uv):
+        g32, u32 = gv.astype(np.float32), uv.astype(np.float32)
+        L32 = np.float32(L)
+        gc = np.minimum(g32, L32)
+        uc = np.maximum(np.minimum(u32, L32), -L32)
+        with np.errstate(over="ignore"):
+            return (gc / (np.float32(1) + np.exp(-gc)) * uc).astype(np.float64)
+
+    rng = np.random.default_rng(8)
+    worst = 0.0
+    for a in (-1.0, 1.0):
+        for b in (-1.0, 1.0):
+            for _ in range(3):
+                ga = g + a * tau * Sg * rng.uniform(0.5, 1.0, g.shape)
+                ub = u + b * tau * Su * rng.uniform(0.5, 1.0, u.shape)
+                err = np.abs(epi32(ga, ub) - act)
+                assert np.all(err <= tau * S), float(np.max(err / (tau * S)))
+                worst = max(worst, float(np.max(err / (tau * S))))
+    assert worst > 0.05                              # the bound is not vacuous
+    # the bound without the up term does not cover moving u alone
+    s = np.minimum(g, L) / (1 + np.exp(-np.minimum(g, L)))
+    S_bad = S - np.abs(s) * Su
+    err = np.abs(epi32(g, u + tau * Su) - act)
+    assert np.any(err > tau * S_bad)
+
+
+def test_moe_down_q8_ref_brute_force():
+    """Down projection of Q8_1 pair activations against the literal decoder
+    with exact rational sums: y[tau, r] = sum_s scale[p] * sum_c Wd[r, c] *
+    d_p[c/32] * q_p[c]."""
+    from fractions import Fraction
+    n_expert, n_ff, d_model, t, n_used = 4, 128, 5, 2, 2
+    wd = np.concatenate([gen.nvfp4_rows(d_model, n_ff, 0x4242 + e) for e in range(n_expert)])
+    ids = gen.expert_ids(t, n_used, n_expert, 9)
+    sc = gen.pair_scales(t * n_used)
+    act = gen.xorshift_f32(t * n_used * n_ff, 1234)
+    aq, ad = ref.quantize_q8_1(act, n_ff)
+    y, S, pair, pS = ref.moe_down_q8_ref("nvfp4", wd, ids, sc, aq, ad, n_expert, n_ff, d_model)
+    per = d_model * formats.row_bytes("nvfp4", n_ff)
+    for tau_ in range(t):
+        for r in range(d_model):
+            tot = Fraction(0)
+            for s_ in range(n_used):
+                p = tau_ * n_used + s_
+                e = int(ids[tau_, s_])
+                W = scalar.decode_matrix("nvfp4", bytes(wd[e * per:(e + 1) * per]), d_model, n_ff)[r]
+                dot = sum(Fraction(W[c]) * Fraction(float(ad[p, c // 32])) * int(aq[p, c]) for c in range(n_ff))
+                tot += Fraction(float(sc[p])) * dot
+            assert abs(y[tau_, r] - float(tot)) <= 1e-13 * max(1.0, abs(float(tot)))
+            assert S[tau_, r] >= abs(y[tau_, r]) * (1 - 1e-12)
