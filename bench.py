@@ -47,7 +47,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_F16_TFLOPS = 2516.6   # MI355X dense f16 MFMA
-PEAK_F32_TFLOPS = 157.3    # MI355X f32 vector FMA
+# MI355X f32 vector FMA: 157.3 TFLOP/s needs packed FMA (v_pk_fma_f32), which
+# this build disables; the roof of the code built is the unpacked rate
+PEAK_F32_TFLOPS = 78.6
+PEAK_F32_PACKED_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 SHAPES = [("ffn_gate", 4608, 1024), ("ffn_down", 1024, 4608), ("conv_in", 3072, 1024),
           ("attn_out", 1024, 1024)]
@@ -272,7 +275,7 @@ def run_decode(args):
                                 "GB/s": round(alg / t / 1e9, 1),
                                 "frac_hbm_peak": round(alg / t / 1e9 / PEAK_HBM_GBS, 4),
                                 "TFLOP/s": round(2.0 * m * k * n / t / 1e12, 2),
-                                "frac_f32_peak": round(2.0 * m * k * n / t / 1e12 / PEAK_F32_TFLOPS, 4)}
+                                "frac_f32_unpacked_peak": round(2.0 * m * k * n / t / 1e12 / PEAK_F32_TFLOPS, 4)}
             sink = torch.empty(m, dtype=torch.int32, device="cuda")
             g = capture([(lambda w=ws[i % copies]: qmm.stream_loadonly(w, m, k, qt, sink=sink))
                          for i in range(L)])
@@ -356,6 +359,25 @@ def run_moe(args):
                      for i in range(L)])
         tq8 = time_graph(g, L, 5)
         del g
+        # the gate/up fused with the SwiGLU/clamp activation (limit 7.0):
+        # the same weight bytes, the act rows written instead of gate and up
+        act = torch.empty((n_pairs, n_ff), dtype=torch.float32, device="cuda")
+        g = capture([(lambda c=sets[i % copies], d=draws[i % 8]:
+                      qmm.moe_gateup_act(c[0], c[1], d, sc, x, n_expert, n_ff, "nvfp4", 7.0, act=act))
+                     for i in range(L)])
+        tact = time_graph(g, L, 5)
+        del g
+        byts_act = statistics.mean(2 * uniq[i % 8] * per_e + 4 * t * in_f + 4 * n_pairs * n_ff for i in range(L))
+        # the measurement twins of the gate/up kernel (the memra page's
+        # ceiling-probe arms): load-only and math-only on the same grid
+        twins = {}
+        for arm in ("loadonly", "mathonly"):
+            g = capture([(lambda c=sets[i % copies], d=draws[i % 8], a=arm:
+                          qmm.moe_gateup_probe(a, c[0], c[1], d, sc, x, n_expert, n_ff, gate_out=go, up_out=uo))
+                         for i in range(L)])
+            tw = time_graph(g, L, 5)
+            del g
+            twins[arm] = {"us": round(tw * 1e6, 2), "GB/s": round(byts / tw / 1e9, 1)}
         res[f"t{t}"] = {"us": round(tt * 1e6, 2),
                         "GB/s": round(byts / tt / 1e9, 1),
                         "frac_hbm_peak": round(byts / tt / 1e9 / PEAK_HBM_GBS, 4),
@@ -364,9 +386,15 @@ def run_moe(args):
                         "v2": {"us": round(tv2 * 1e6, 2), "GB/s": round(byts / tv2 / 1e9, 1),
                                "bit_identical_to_v1": True},
                         "q8_1": {"us": round(tq8 * 1e6, 2), "GB/s": round(byts / tq8 / 1e9, 1),
-                                 "includes": "quantize_q8_1 + gate/up"}}
+                                 "includes": "quantize_q8_1 + gate/up"},
+                        "swiglu_clamp_fused": {"us": round(tact * 1e6, 2), "GB/s": round(byts_act / tact / 1e9, 1),
+                                               "frac_hbm_peak": round(byts_act / tact / 1e9 / PEAK_HBM_GBS, 4),
+                                               "limit": 7.0},
+                        "loadonly_twin": twins["loadonly"], "mathonly_twin": twins["mathonly"]}
         log(f"moe t={t}: {res[f't{t}']['us']} us {res[f't{t}']['GB/s']} GB/s; "
-            f"V2 {res[f't{t}']['v2']['us']} us; Q8_1 {res[f't{t}']['q8_1']['us']} us")
+            f"V2 {res[f't{t}']['v2']['us']} us; Q8_1 {res[f't{t}']['q8_1']['us']} us; "
+            f"+SwiGLU {res[f't{t}']['swiglu_clamp_fused']['us']} us; load-only {twins['loadonly']['us']} us, "
+            f"math-only {twins['mathonly']['us']} us")
     return res
 
 
@@ -427,6 +455,15 @@ def run_moe_down(args):
                      for i in range(L)])
         tv2 = time_graph(g, L, 5)
         del g
+        # the down arm of the page on Q8_1 pair activations (quantization of
+        # the activation rows included in the timed launches)
+        aq, ad = qmm.quantize_q8_1(act)
+        g = capture([(lambda w=sets_v2[i % copies], d=draws[i % 8]:
+                      (qmm.quantize_q8_1(act, q=aq, d=ad),
+                       qmm.moe_down_q8(w, d, sc, aq, ad, n_expert, d_model, "nvfp4_v2", y=y, pair_out=po)))
+                     for i in range(L)])
+        tq8 = time_graph(g, L, 5)
+        del g
         res[f"t{t}"] = {"us": round(tt * 1e6, 2),
                         "GB/s": round(byts / tt / 1e9, 1),
                         "frac_hbm_peak": round(byts / tt / 1e9 / PEAK_HBM_GBS, 4),
@@ -434,11 +471,114 @@ def run_moe_down(args):
                         "algorithmic_bytes_mean": round(byts),
                         "pair_terms_bytes": 2 * 4 * n_pairs * d_model,
                         "v2": {"us": round(tv2 * 1e6, 2), "GB/s": round(byts / tv2 / 1e9, 1),
-                               "bit_identical_to_v1": True}}
+                               "bit_identical_to_v1": True},
+                        "q8_1_v2": {"us": round(tq8 * 1e6, 2), "GB/s": round(byts / tq8 / 1e9, 1),
+                                    "includes": "quantize_q8_1 of the pair rows + down on V2 rows"}}
         log(f"moe down t={t}: {res[f't{t}']['us']} us {res[f't{t}']['GB/s']} GB/s; "
-            f"V2 {res[f't{t}']['v2']['us']} us")
+            f"V2 {res[f't{t}']['v2']['us']} us; Q8_1 on V2 {res[f't{t}']['q8_1_v2']['us']} us")
     del sets, sets_v2
     torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------- MoE block
+
+def run_moe_block(args):
+    """The MoE block on the device: gate/up fused with the SwiGLU/clamp
+    activation (limit 7.0), then the down projection with its slot sum, for
+    t in {1, 16}; 64 experts, 8 used, d_model 4096, n_ff 2048; 2 copies of
+    all three planes (1.8 GB) x 8 id draws rotated.  Algorithmic bytes: the
+    unique experts' gate, up and down rows, x, the activation rows (written
+    and read back) and y."""
+    import numpy as np
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    from synth import gen
+    n_expert, d_model, n_ff, n_used = 64, 4096, 2048, 8
+    rb_gu, rb_d = qmm.row_bytes("nvfp4", d_model), qmm.row_bytes("nvfp4", n_ff)
+    per_gu, per_d = n_ff * rb_gu, d_model * rb_d
+    copies = 2
+    sets = []
+    for c in range(copies):
+        planes = []
+        for plane, (per, rows, cols, seed) in enumerate(((per_gu, n_ff, d_model, gen.SEED_MOE_W),
+                                                         (per_gu, n_ff, d_model, gen.SEED_MOE_W),
+                                                         (per_d, d_model, n_ff, gen.SEED_MOE_DOWN_W))):
+            host = np.empty(n_expert * per, dtype=np.uint8)
+            for e in range(n_expert):
+                sd = seed + (2 * e + plane if plane < 2 else e)
+                host[e * per:(e + 1) * per] = gen.nvfp4_rows(rows, cols, sd)
+                host[e * per + 5] ^= (c * 16 + plane + 1) & 0xFF
+            planes.append(to_dev(host))
+            del host
+        sets.append(planes)
+    res = {}
+    L = 32
+    for t in (1, 16):
+        n_pairs = t * n_used
+        draws_h = [gen.expert_ids(t, n_used, n_expert, gen.SEED_EXPERTS + d) for d in range(8)]
+        draws = [to_dev(d) for d in draws_h]
+        uniq = [len(np.unique(d)) for d in draws_h]
+        sc = to_dev(gen.pair_scales(3 * n_pairs))
+        sc_gu, sc_d = sc[:2 * n_pairs], sc[2 * n_pairs:]
+        x = to_dev(gen.xorshift_f32(t * d_model, gen.SEED_MOE_X).reshape(t, d_model))
+        act = torch.empty((n_pairs, n_ff), dtype=torch.float32, device="cuda")
+        y = torch.empty((t, d_model), dtype=torch.float32, device="cuda")
+        po = torch.empty((n_pairs, d_model), dtype=torch.float32, device="cuda")
+
+        def block(c, d):
+            qmm.moe_gateup_act(c[0], c[1], d, sc_gu, x, n_expert, n_ff, "nvfp4", 7.0, act=act)
+            qmm.moe_down(c[2], d, sc_d, act, n_expert, d_model, y=y, pair_out=po)
+        g = capture([(lambda c=sets[i % copies], d=draws[i % 8]: block(c, d)) for i in range(L)])
+        tt = time_graph(g, L, 5)
+        del g
+        byts = statistics.mean(uniq[i % 8] * (2 * per_gu + per_d) + 4 * t * d_model + 2 * 4 * n_pairs * n_ff +
+                               4 * t * d_model for i in range(L))
+        res[f"t{t}"] = {"us": round(tt * 1e6, 2), "GB/s": round(byts / tt / 1e9, 1),
+                        "frac_hbm_peak": round(byts / tt / 1e9 / PEAK_HBM_GBS, 4),
+                        "algorithmic_bytes_mean": round(byts),
+                        "launches": "gate/up+SwiGLU/clamp, down, slot sum"}
+        log(f"moe block t={t}: {res[f't{t}']['us']} us {res[f't{t}']['GB/s']} GB/s")
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------- other prefill configs
+
+PREFILL_CONFIGS = [("q4_0_1024x1024_n64", "q4_0", 1024, 1024, 64),
+                   ("8b_q4_k_14336x4096_n2048", "q4_k", 14336, 4096, 2048),
+                   ("8b_q4_k_4096x14336_n2048", "q4_k", 4096, 14336, 2048),
+                   ("8b_q6_k_14336x4096_n2048", "q6_k", 14336, 4096, 2048),
+                   ("8b_q6_k_4096x14336_n2048", "q6_k", 4096, 14336, 2048)]
+
+
+def run_prefill_configs(args):
+    """The Q4_0 1024x1024 n=64 GEMM (qmm_gemm's AUTO dispatch, the matrix
+    cores) and the 8B-class n=2048 GEMMs (qmm_gemm_ws), each graph-replayed
+    8 times, median of 5; TFLOP/s against the f16 MFMA peak."""
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    from synth import gen
+    res = {}
+    for tag, qt, m, k, n in PREFILL_CONFIGS:
+        w = to_dev(gen_weights(qt, m, k, 7))
+        x = to_dev(gen.unit_f32(n * k, gen.SEED_X + k).reshape(n, k))
+        out = torch.empty((n, m), dtype=torch.float32, device="cuda")
+        path = "auto" if n <= 64 else "mfma"
+        g = capture([lambda: qmm.gemm(w, x, m, qt, out=out, path=path)] * 8)
+        for _ in range(2):
+            g.replay()
+        t = time_graph(g, 8, 5)
+        del g
+        plan = qmm.gemm_plan(m, k, n, qt, path)
+        fl = 2.0 * m * k * n
+        res[tag] = {"us": round(t * 1e6, 2), "TFLOP/s": round(fl / t / 1e12, 1),
+                    "frac_mfma_peak": round(fl / t / 1e12 / PEAK_F16_TFLOPS, 4),
+                    "kernel": qmm.plan_kernel_name(plan, qt), "k_split": plan.get("n_split", 1)}
+        log(f"{tag}: {res[tag]['us']} us {res[tag]['TFLOP/s']} TFLOP/s ({res[tag]['kernel']})")
+        del w, x, out
+        torch.cuda.empty_cache()
     return res
 
 
@@ -676,36 +816,94 @@ def pmc_summary(fetch_csv, write_csv, out_path):
 
 # ---------------------------------------------------------------- CPU oracle
 
+def host_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def run_cpu_baseline(args, n):
-    from oracle import ref
+    """The oracle (numpy decode to f64, then f64 BLAS matmul) on the host
+    cores, median of 3 after 1 warm-up, decode and contraction timed apart.
+    The headline entry is the whole LFM2 step; the other configurations are
+    bounded samples scaled to their whole job (said per entry)."""
+    import numpy as np
+    from oracle import formats, ref
     from synth import gen
     try:
         from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
-        cores = os.cpu_count() or 1
+        threads = os.cpu_count() or 1
+
+    def timed(decode_jobs, contract):
+        """(decode s, contraction s): decode_jobs() -> decoded matrices,
+        contract(mats) -> None; median of 3 after a warm-up."""
+        def once():
+            t0 = time.perf_counter()
+            mats = decode_jobs()
+            t1 = time.perf_counter()
+            contract(mats)
+            return t1 - t0, time.perf_counter() - t1
+        once()
+        runs = [once() for _ in range(3)]
+        return statistics.median(r[0] for r in runs), statistics.median(r[1] for r in runs)
+
+    out = {}
+    # the LFM2 step: 20 GEMMs at n = 512
     work = []
     for qi, qt in enumerate(QTS):
         for si, (label, m, k) in enumerate(SHAPES):
-            w = gen_weights(qt, m, k, 16 * qi + si)
-            x = gen.unit_f32(n * k, gen.SEED_X + k).reshape(n, k)
-            work.append((qt, m, k, w, x))
+            work.append((qt, m, k, gen_weights(qt, m, k, 16 * qi + si), gen.unit_f32(n * k, gen.SEED_X + k).reshape(n, k)))
     flops = sum(2.0 * m * k * n for (_, m, k, _, _) in work)
-
-    def once():
-        t0 = time.perf_counter()
-        for (qt, m, k, w, x) in work:
-            ref.gemm_value(qt, w, x, m, k, n)
-        return time.perf_counter() - t0
-    once()
-    t = statistics.median([once() for _ in range(3)])
+    xs = [x.astype(np.float64) for (_, _, _, _, x) in work]
+    td, tc = timed(lambda: [formats.decode(qt, w, m, k) for (qt, m, k, w, _) in work],
+                   lambda mats: [x @ W.T for x, W in zip(xs, mats)])
+    out["lfm2_prefill_n512"] = {"TFLOP/s": round(flops / (td + tc) / 1e12, 5), "decode_s": round(td, 4),
+                                "contraction_s": round(tc, 4), "sample": "the whole 20-GEMM step"}
+    # Q4_0 1024x1024 n=64
+    w = gen_weights("q4_0", 1024, 1024, 0)
+    x = gen.unit_f32(64 * 1024, gen.SEED_X).reshape(64, 1024).astype(np.float64)
+    td1, tc1 = timed(lambda: formats.decode("q4_0", w, 1024, 1024), lambda W: x @ W.T)
+    out["q4_0_1024x1024_n64"] = {"TFLOP/s": round(2.0 * 1024 ** 2 * 64 / (td1 + tc1) / 1e12, 5),
+                                 "decode_s": round(td1, 4), "contraction_s": round(tc1, 4), "sample": "whole"}
+    # decode GEMV n = 1, q4_k 14336x4096
+    w = gen_weights("q4_k", 14336, 4096, 99)
+    x1 = gen.unit_f32(4096, gen.SEED_X).astype(np.float64)
+    td2, tc2 = timed(lambda: formats.decode("q4_k", w, 14336, 4096), lambda W: W @ x1)
+    out["decode_q4_k_14336x4096_n1"] = {"GB/s": round(w.size / (td2 + tc2) / 1e9, 4), "decode_s": round(td2, 4),
+                                        "contraction_s": round(tc2, 4), "sample": "whole"}
+    # MoE gate/up t = 1: 8 experts x 2 planes of 2048 x 4096 NVFP4 rows
+    rows = [gen.nvfp4_rows(2048, 4096, gen.SEED_MOE_W + i) for i in range(16)]
+    xm = gen.xorshift_f32(4096, gen.SEED_MOE_X).astype(np.float64)
+    td3, tc3 = timed(lambda: [formats.decode("nvfp4", r, 2048, 4096) for r in rows],
+                     lambda mats: [W @ xm for W in mats])
+    out["moe_gateup_t1"] = {"GB/s": round(sum(r.size for r in rows) / (td3 + tc3) / 1e9, 4),
+                            "decode_s": round(td3, 4), "contraction_s": round(tc3, 4), "sample": "whole"}
+    # 8B-class q4_k 14336x4096 n = 2048: one 2048-row block of W, scaled by 7
+    m_s = 2048
+    w = gen_weights("q4_k", m_s, 4096, 7)
+    x8 = gen.unit_f32(2048 * 4096, gen.SEED_X + 4096).reshape(2048, 4096).astype(np.float64)
+    td4, tc4 = timed(lambda: formats.decode("q4_k", w, m_s, 4096), lambda W: x8 @ W.T)
+    out["8b_q4_k_14336x4096_n2048"] = {"TFLOP/s": round(2.0 * m_s * 4096 * 2048 / (td4 + tc4) / 1e12, 5),
+                                       "decode_s": round(td4 * 7, 4), "contraction_s": round(tc4 * 7, 4),
+                                       "sample": "rows 0..2047 of 14336 (1/7), times scaled by 7"}
+    main = out["lfm2_prefill_n512"]
     return {
-        "value": round(flops / t / 1e12, 5),
+        "value": main["TFLOP/s"],
         "unit": "TFLOP/s",
-        "cores": cores,
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"the whole 20-GEMM prefill step (4 shapes x 5 formats, n={n}): numpy decode to "
-                  f"f64 + f64 matmul (BLAS); median of 3 after 1 warm-up, {t:.2f} s per step",
+        "sample": f"the whole 20-GEMM prefill step (4 shapes x 5 formats, n={n}): numpy decode to f64 "
+                  f"({main['decode_s']:.3f} s) + f64 matmul ({main['contraction_s']:.3f} s, BLAS); "
+                  f"median of 3 after 1 warm-up",
+        "host_cpus": os.cpu_count(),
+        "host_model": host_model(),
+        "configs": out,
     }
 
 
@@ -781,6 +979,11 @@ def main():
         torch.cuda.empty_cache()
         log("MoE down NVFP4")
         extras["moe_down"] = run_moe_down(args)
+        torch.cuda.empty_cache()
+        log("MoE block: gate/up + SwiGLU/clamp + down")
+        extras["moe_block"] = run_moe_block(args)
+        log("prefill configs: Q4_0 1024^2 n=64, 8B-class n=2048")
+        extras["prefill_configs"] = run_prefill_configs(args)
     cpu = None
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")

@@ -21,7 +21,8 @@ import threading
 
 __all__ = [
     "QTYPES", "PATHS", "QmmError", "lib_path", "load", "gemm", "workspace_bytes", "gemm_plan",
-    "plan_kernel_name", "moe_gateup", "moe_down",
+    "plan_kernel_name", "moe_gateup", "moe_down", "moe_gateup_act", "moe_gateup_act_q8", "moe_gateup_probe",
+    "moe_down_q8",
     "stream_loadonly", "repack_nvfp4_v2", "quantize_q8_1", "moe_gateup_q8",
     "row_bytes", "block_elems", "gemv_max_n", "status_str", "abi_version",
 ]
@@ -77,6 +78,15 @@ def load() -> ctypes.CDLL:
         lib.qmm_moe_gateup.restype = i32
         lib.qmm_moe_down.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
         lib.qmm_moe_down.restype = i32
+        f32 = ctypes.c_float
+        lib.qmm_moe_gateup_act.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32, vp]
+        lib.qmm_moe_gateup_act.restype = i32
+        lib.qmm_moe_gateup_act_q8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32, vp]
+        lib.qmm_moe_gateup_act_q8.restype = i32
+        lib.qmm_moe_gateup_probe.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+        lib.qmm_moe_gateup_probe.restype = i32
+        lib.qmm_moe_down_q8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+        lib.qmm_moe_down_q8.restype = i32
         lib.qmm_quantize_q8_1.argtypes = [vp, vp, vp, i64, i64, vp]
         lib.qmm_quantize_q8_1.restype = i32
         lib.qmm_moe_gateup_q8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
@@ -361,6 +371,114 @@ def moe_gateup_q8(w_gate, w_up, expert_ids, pair_scale, xq, xd, n_expert: int, n
     if st != 0:
         raise QmmError(st, "qmm_moe_gateup_q8")
     return gate_out, up_out
+
+
+def moe_gateup_act(w_gate, w_up, expert_ids, pair_scale, x, n_expert: int, n_ff: int, qtype="nvfp4",
+                   limit: float = 7.0, act=None, stream=None):
+    """Gate and up projections fused with the SwiGLU/clamp activation:
+    returns act float32 [t*n_used, n_ff] = silu(min(gate, limit)) *
+    clamp(up, -limit, limit) (the down projection's input).  Arguments as
+    moe_gateup; limit > 0 or inf."""
+    import torch
+    lib = load()
+    qt = _qt(qtype)
+    t, n_used = expert_ids.shape
+    t2, in_f = x.shape
+    if t2 != t:
+        raise ValueError("x and expert_ids disagree on t")
+    n_pairs = t * n_used
+    if pair_scale.numel() != 2 * n_pairs:
+        raise ValueError("pair_scale must hold 2*t*n_used floats")
+    if act is None:
+        act = torch.empty((n_pairs, n_ff), dtype=torch.float32, device=x.device)
+    st = lib.qmm_moe_gateup_act(_dev(act, "act", torch.float32), _dev(w_gate, "w_gate"), _dev(w_up, "w_up"),
+                                _dev(expert_ids, "expert_ids", torch.int32),
+                                _dev(pair_scale, "pair_scale", torch.float32), _dev(x, "x", torch.float32),
+                                t, n_used, n_expert, in_f, n_ff, qt, float(limit), _stream(stream))
+    if st != 0:
+        raise QmmError(st, "qmm_moe_gateup_act")
+    return act
+
+
+def moe_gateup_act_q8(w_gate, w_up, expert_ids, pair_scale, xq, xd, n_expert: int, n_ff: int,
+                      qtype="nvfp4", limit: float = 7.0, act=None, stream=None):
+    """moe_gateup_act on Q8_1 activations (xq, xd from quantize_q8_1)."""
+    import torch
+    lib = load()
+    qt = _qt(qtype)
+    t, n_used = expert_ids.shape
+    t2, in_f = xq.shape
+    if t2 != t or xd.numel() != t * (in_f // 32):
+        raise ValueError("xq / xd do not match expert_ids")
+    n_pairs = t * n_used
+    if pair_scale.numel() != 2 * n_pairs:
+        raise ValueError("pair_scale must hold 2*t*n_used floats")
+    if act is None:
+        act = torch.empty((n_pairs, n_ff), dtype=torch.float32, device=xq.device)
+    st = lib.qmm_moe_gateup_act_q8(_dev(act, "act", torch.float32), _dev(w_gate, "w_gate"), _dev(w_up, "w_up"),
+                                   _dev(expert_ids, "expert_ids", torch.int32),
+                                   _dev(pair_scale, "pair_scale", torch.float32), _dev(xq, "xq", torch.int8),
+                                   _dev(xd, "xd", torch.float32), t, n_used, n_expert, in_f, n_ff, qt,
+                                   float(limit), _stream(stream))
+    if st != 0:
+        raise QmmError(st, "qmm_moe_gateup_act_q8")
+    return act
+
+
+def moe_gateup_probe(arm: str, w_gate, w_up, expert_ids, pair_scale, x, n_expert: int, n_ff: int,
+                     qtype="nvfp4", gate_out=None, up_out=None, stream=None):
+    """A measurement twin of moe_gateup: arm "loadonly" (the same loads, no
+    arithmetic) or "mathonly" (the arithmetic on one cached unit per row
+    group).  The outputs are not projections."""
+    import torch
+    lib = load()
+    arms = {"loadonly": 1, "mathonly": 2}
+    if arm not in arms:
+        raise ValueError(f"unknown arm {arm!r}")
+    qt = _qt(qtype)
+    t, n_used = expert_ids.shape
+    in_f = x.shape[1]
+    n_pairs = t * n_used
+    if gate_out is None:
+        gate_out = torch.empty((n_pairs, n_ff), dtype=torch.float32, device=x.device)
+    if up_out is None:
+        up_out = torch.empty((n_pairs, n_ff), dtype=torch.float32, device=x.device)
+    st = lib.qmm_moe_gateup_probe(arms[arm], _dev(gate_out, "gate_out", torch.float32),
+                                  _dev(up_out, "up_out", torch.float32), _dev(w_gate, "w_gate"),
+                                  _dev(w_up, "w_up"), _dev(expert_ids, "expert_ids", torch.int32),
+                                  _dev(pair_scale, "pair_scale", torch.float32), _dev(x, "x", torch.float32),
+                                  t, n_used, n_expert, in_f, n_ff, qt, _stream(stream))
+    if st != 0:
+        raise QmmError(st, "qmm_moe_gateup_probe")
+    return gate_out, up_out
+
+
+def moe_down_q8(w_down, expert_ids, pair_scale, aq, ad, n_expert: int, d_model: int, qtype="nvfp4",
+                y=None, pair_out=None, stream=None):
+    """moe_down on Q8_1 pair activations (aq int8 [t*n_used, n_ff], ad
+    float32 [t*n_used, n_ff/32] from quantize_q8_1); returns (y, pair_out)."""
+    import torch
+    lib = load()
+    qt = _qt(qtype)
+    t, n_used = expert_ids.shape
+    n_pairs = t * n_used
+    n_p2, n_ff = aq.shape
+    if n_p2 != n_pairs or ad.numel() != n_pairs * (n_ff // 32):
+        raise ValueError("aq / ad must hold one row per pair (t*n_used rows)")
+    if pair_scale.numel() != n_pairs:
+        raise ValueError("pair_scale must hold t*n_used floats")
+    if y is None:
+        y = torch.empty((t, d_model), dtype=torch.float32, device=aq.device)
+    if pair_out is None:
+        pair_out = torch.empty((n_pairs, d_model), dtype=torch.float32, device=aq.device)
+    st = lib.qmm_moe_down_q8(_dev(y, "y", torch.float32), _dev(pair_out, "pair_out", torch.float32),
+                             _dev(w_down, "w_down"), _dev(expert_ids, "expert_ids", torch.int32),
+                             _dev(pair_scale, "pair_scale", torch.float32), _dev(aq, "aq", torch.int8),
+                             _dev(ad, "ad", torch.float32), t, n_used, n_expert, n_ff, d_model, qt,
+                             _stream(stream))
+    if st != 0:
+        raise QmmError(st, "qmm_moe_down_q8")
+    return y, pair_out
 
 
 def repack_nvfp4_v2(w, rows: int, k: int, out=None, stream=None):

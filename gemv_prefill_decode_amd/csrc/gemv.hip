@@ -42,40 +42,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_kernel(float* __restrict__ dst,
 }
 
 // ------------------------------------------------------------------ load-only twin
-// The GEMV's streaming loop with the decode and FMAs replaced by an XOR of
-// the raw words: the same descriptors, unit loads and item order.
-template <typename UT>
-__device__ __forceinline__ uint32_t raw_xor(const UT& un);
-
-template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_F32>& u) {
-    uint32_t v = 0;
-    for (int i = 0; i < 16; ++i) v ^= u.r[i];
-    return v;
-}
-template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_Q4_0>& u) {
-    return u.r[0] ^ u.r[1] ^ u.r[2] ^ u.r[3] ^ u.r[4];
-}
-template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_Q8_0>& u) {
-    uint32_t v = 0;
-    for (int i = 0; i < 9; ++i) v ^= u.r[i];
-    return v;
-}
-template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_Q4_K>& u) {
-    return u.hdr.x ^ u.hdr.y ^ u.hdr.z ^ u.hdr.w ^ u.qs.x ^ u.qs.y ^ u.qs.z ^ u.qs.w;
-}
-template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_Q6_K>& u) {
-    uint32_t v = u.rd ^ u.rs[0] ^ u.rs[1] ^ u.rs[2];
-    for (int i = 0; i < 5; ++i) v ^= u.ra[i] ^ u.rb[i] ^ u.rh[i];
-    return v;
-}
-template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_NVFP4>& u) {
-    return u.sd ^ u.qs.x ^ u.qs.y ^ u.qs.z ^ u.qs.w;
-}
-
-template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_NVFP4_V2>& u) {
-    return u.sd ^ u.qs.x ^ u.qs.y ^ u.qs.z ^ u.qs.w;
-}
-
+// (raw_xor, the checksum of a unit's raw words, is in stream.hpp)
 template <int QT, int R, int D>
 __global__ __launch_bounds__(256) void loadonly_kernel(uint32_t* __restrict__ sink,
                                                        const uint8_t* __restrict__ w, int m, int k,

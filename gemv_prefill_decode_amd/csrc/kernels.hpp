@@ -98,6 +98,29 @@ void launch_moe_down(float* y, float* pair_out, const void* w_down, const int* i
                      int64_t n_expert, int64_t n_ff, int64_t d_model, int qt, int64_t rb,
                      const GemvTuning& tune, hipStream_t st);
 
+// The gate and up projections fused with the SwiGLU/clamp activation:
+// act[p][r] = silu(min(g, limit)) * clamp(u, -limit, limit) with g, u the
+// scaled projections of launch_moe (f32 activations, or Q8_1 activations
+// for NVFP4 / NVFP4 V2 weights).
+void launch_moe_act(float* act, const void* wg, const void* wu, const int* ids, const float* sc, const float* x,
+                    int64_t t, int64_t n_used, int64_t n_expert, int64_t in_f, int64_t n_ff, int qt, int64_t rb,
+                    float limit, const GemvTuning& tune, hipStream_t st);
+void launch_moe_act_q8(float* act, const void* wg, const void* wu, const int* ids, const float* sc,
+                       const int8_t* xq, const float* xd, int64_t t, int64_t n_used, int64_t n_expert, int64_t in_f,
+                       int64_t n_ff, int qt, int64_t rb, float limit, const GemvTuning& tune, hipStream_t st);
+
+// The down projection on Q8_1 pair activations (aq [n_pairs][n_ff] codes, ad
+// their block scales; NVFP4 or NVFP4 V2 weights), then the slot sum.
+void launch_moe_down_q8(float* y, float* pair_out, const void* wd, const int* ids, const float* sc,
+                        const int8_t* aq, const float* ad, int64_t t, int64_t n_used, int64_t n_expert, int64_t n_ff,
+                        int64_t d_model, int qt, int64_t rb, const GemvTuning& tune, hipStream_t st);
+
+// The measurement twins of launch_moe (arm 1: load-only, 2: math-only) on
+// NVFP4 / NVFP4 V2 weights: the same grid, de-duplication and addresses.
+void launch_moe_probe(int arm, float* g, float* u, const void* wg, const void* wu, const int* ids, const float* sc,
+                      const float* x, int64_t t, int64_t n_used, int64_t n_expert, int64_t in_f, int64_t n_ff,
+                      int qt, int64_t rb, const GemvTuning& tune, hipStream_t st);
+
 // NVFP4 rows (rows x k/64 groups of 36 bytes) -> the NVFP4 V2 layout.
 void launch_nvfp4_repack_v2(void* dst, const void* src, int64_t rows, int64_t k, hipStream_t st);
 

@@ -8,7 +8,9 @@ namespace qmm {
 // ------------------------------------------------------------------ MoE gate/up
 // grid: x = work groups per (pair, plane) (their waves stride over the row
 // groups of one expert's n_ff rows), y = pair p, z = plane (2: gate and up;
-// 1: the down projection's single plane).
+// 1: the down projection's single plane, or the fused SwiGLU mode, whose
+// work groups stream the gate rows and then the up rows of the same row
+// groups).
 // The work groups of the FIRST pair routed to expert e gather every pair
 // routed to e and apply e's rows to all their activation rows, so each
 // selected expert's rows are read once per call when it has at most MOE_NT
@@ -21,117 +23,180 @@ constexpr int MOE_CHUNK = 256;  // pairs examined (and gathered) per pass
 constexpr int MOE_NT = 3;       // token rows staged in LDS at a time
 constexpr unsigned MOE_MIN_WG = 32;  // work groups per (pair, plane) at least
 
-template <int QT, int NT, int R, int D, bool XL>
-__device__ __forceinline__ void moe_tokens(float* __restrict__ out, const float* __restrict__ scale,
-                                           const StreamGeom& g, int n_rg, rsrc_t xr,
-                                           const int* plist, const int* tlist, int c0, int cnt,
-                                           int in_f, int n_ff) {
-    const int wave = wave_id();
-    uint32_t xoff[NT];
+// Kernel modes: the projections per plane; the gate and up projections of
+// each row fused with the SwiGLU/clamp activation; the two measurement
+// twins of the per-plane mode (load-only and math-only arms).
+enum : int { MOE_PLANES = 0, MOE_ACT = 1, MOE_LOADONLY = 2, MOE_MATHONLY = 3 };
+
+struct MoeArgs {
+    float* out0;            // gate_out (or the single plane's output, or act)
+    float* out1;            // up_out
+    const uint8_t* w0;      // gate (or the single) plane's rows
+    const uint8_t* w1;      // up plane's rows
+    const int* ids;
+    const float* pscale;    // plane P's scales at P * n_pairs
+    const float* x;         // f32 activation rows
+    const int8_t* xq;       // Q8_1 codes and block scales (Q8 kernels)
+    const float* xd;
+    int t, n_used, n_expert, in_f, n_ff, rb, lpr_log2, n_rg;
+    int xl;                 // f32 activations staged in LDS
+    int act_pair;           // activation row of pair q is row q (else q / n_used)
+    float limit;            // the SwiGLU clamp (MOE_ACT)
+    int gbuf_off;           // floats of dynamic LDS before the gate buffer (MOE_ACT)
+};
+
+// The activation between gate/up and down: the gate clamped above at L, the
+// up projection clamped to [-L, L], then silu(g) * u with silu(z) = z / (1 +
+// exp(-z)) (a reading of the memra page's "preclamp" gate/up with argument
+// 7.0, whose down arm consumes a SwiGLU output).  The comparisons keep a NaN
+// projection NaN.
+__device__ __forceinline__ float swiglu_clamp(float g, float u, float L) {
+    const float gc = g > L ? L : g;
+    const float uc = u > L ? L : (u < -L ? -L : u);
+    return gc / (1.0f + expf(-gc)) * uc;
+}
+
+// The chunk [c0, c0 + NT) of the gathered pairs (absent slots repeat a real
+// token): per-slot activation rows, pair numbers (-1: absent) and scales of
+// plane `plane` (and, with both, of the up plane: MOE_ACT).
+template <int NT>
+struct Chunk {
+    uint32_t row[NT];  // activation row of the slot
     int pj[NT];
-    float fj[NT];
+    float f0[NT], f1[NT];
+    __device__ __forceinline__ Chunk(const MoeArgs& a, const int* plist, const int* tlist, int c0, int cnt,
+                                     int plane, bool both) {
+        const int n_pairs = a.t * a.n_used;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-        const int c = (c0 + j < cnt) ? c0 + j : c0;  // absent slots repeat a real token
-        xoff[j] = (uint32_t)tlist[c] * (uint32_t)in_f * 4u;
-        pj[j] = (c0 + j < cnt) ? plist[c] : -1;
-        fj[j] = scale[plist[c]];
+        for (int j = 0; j < NT; ++j) {
+            const int c = (c0 + j < cnt) ? c0 + j : c0;
+            row[j] = (uint32_t)tlist[c];
+            pj[j] = (c0 + j < cnt) ? plist[c] : -1;
+            f0[j] = a.pscale[plane * n_pairs + plist[c]];
+            f1[j] = both ? a.pscale[n_pairs + plist[c]] : 0.0f;
+        }
     }
+};
+
+// Slot of (row, token j) in the work group's gate buffer (MOE_ACT): the
+// same lane stores a row's gate value and reads it back in the up pass, so
+// the index only has to be unique within the work group: row group rg is
+// the q-th of wave `wave` (rg = blockIdx.x * 4 + wave + q * 4 * gridDim.x).
+__device__ __forceinline__ int gate_slot(int64_t row, int j, int RG, int nt) {
+    const int rg = (int)(row / RG);
+    const int q = (rg - (int)blockIdx.x * 4 - wave_id()) / (4 * (int)gridDim.x);
+    return ((q * 4 + wave_id()) * RG + (int)(row - (int64_t)rg * RG)) * nt + j;
+}
+
+// One chunk of pairs on f32 activations (XL: staged in LDS) or Q8_1
+// activations (staged in LDS).  MOE_PLANES and the twins: the rows of plane
+// blockIdx.z; MOE_ACT: the gate rows, then the up rows, then the activation.
+template <int QT, int NT, int R, int D, bool XL, bool Q8, int MODE>
+__device__ __forceinline__ void moe_chunk(const MoeArgs& a, int e, const int* plist, const int* tlist, int c0,
+                                          int cnt) {
+    const int wave = wave_id();
+    const int plane = MODE == MOE_ACT ? 0 : (int)blockIdx.z;
+    const Chunk<NT> ck(a, plist, tlist, c0, cnt, plane, MODE == MOE_ACT);
+    const int64_t n_ff = a.n_ff;
+    const int RG = (64 >> a.lpr_log2) * R;
+    const StreamGeom g0{(plane == 0 ? a.w0 : a.w1) + (int64_t)e * n_ff * a.rb, n_ff, a.rb, a.in_f, a.lpr_log2};
+    float* out = plane == 0 ? a.out0 : a.out1;
+    constexpr int ARM = MODE == MOE_LOADONLY ? STREAM_LOADONLY : (MODE == MOE_MATHONLY ? STREAM_MATHONLY : STREAM_SERVED);
     auto store = [&](int64_t row, int j, float v) {
-        if (row < n_ff && pj[j] >= 0) out[(int64_t)pj[j] * n_ff + row] = fj[j] * v;
+        if (row < n_ff && ck.pj[j] >= 0) out[(int64_t)ck.pj[j] * n_ff + row] = ck.f0[j] * v;
     };
-    if constexpr (XL) {
-        __syncthreads();  // the previous chunk's waves are done with the staged x
-        constexpr bool SM = GUnit<QT>::RUNS > 0;
-        const XLds<NT, SM> xs{qmm_dyn_lds, xpad_len(in_f), qmm_dyn_lds + NT * xpad_len(in_f), in_f >> 4};
-        gemv_stream<QT, NT, R, D>(g, blockIdx.x * 4 + wave, gridDim.x * 4, n_rg, xs, store,
-                                  [&]() { stage_x<NT, SM>(qmm_dyn_lds, xr, xoff, in_f); });
+    float* gbuf = qmm_dyn_lds + a.gbuf_off;
+    auto store_gate = [&](int64_t row, int j, float v) {
+        if (row < n_ff && ck.pj[j] >= 0) gbuf[gate_slot(row, j, RG, NT)] = ck.f0[j] * v;
+    };
+    auto store_act = [&](int64_t row, int j, float v) {
+        if (row < n_ff && ck.pj[j] >= 0)
+            a.out0[(int64_t)ck.pj[j] * n_ff + row] =
+                swiglu_clamp(gbuf[gate_slot(row, j, RG, NT)], ck.f1[j] * v, a.limit);
+    };
+    auto run = [&](const auto& xs, auto pre) {
+        if constexpr (MODE == MOE_ACT) {
+            const StreamGeom g1{a.w1 + (int64_t)e * n_ff * a.rb, n_ff, a.rb, a.in_f, a.lpr_log2};
+            gemv_stream<QT, NT, R, D>(g0, blockIdx.x * 4 + wave, gridDim.x * 4, a.n_rg, xs, store_gate, pre);
+            gemv_stream<QT, NT, R, D>(g1, blockIdx.x * 4 + wave, gridDim.x * 4, a.n_rg, xs, store_act);
+        } else {
+            gemv_stream<QT, NT, R, D, std::decay_t<decltype(xs)>, decltype(store), decltype(pre), ARM>(
+                g0, blockIdx.x * 4 + wave, gridDim.x * 4, a.n_rg, xs, store, pre);
+        }
+    };
+    const int n_rows = a.act_pair ? a.t * a.n_used : a.t;  // activation rows
+    if constexpr (Q8) {
+        const rsrc_t qr = make_rsrc(a.xq, (uint32_t)n_rows * (uint32_t)a.in_f);
+        const rsrc_t dr = make_rsrc(a.xd, (uint32_t)n_rows * (uint32_t)(a.in_f / 32) * 4u);
+        uint32_t qoff[NT], doff[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            qoff[j] = ck.row[j] * (uint32_t)a.in_f;
+            doff[j] = ck.row[j] * (uint32_t)(a.in_f / 32) * 4u;
+        }
+        __syncthreads();  // the previous chunk's waves are done with the staged rows
+        _Float16* sx = (_Float16*)qmm_dyn_lds;
+        const XLdsQ8<NT> xs{sx, q8pad_len(a.in_f), (const float*)(sx + NT * q8pad_len(a.in_f)), a.in_f / 32};
+        run(xs, [&]() { stage_q8<NT>(sx, qr, dr, qoff, doff, a.in_f); });
     } else {
-        XGlobal<NT> xs;
-        xs.xr = xr;
+        const rsrc_t xr = make_rsrc(a.x, (uint32_t)n_rows * (uint32_t)a.in_f * 4u);
+        uint32_t xoff[NT];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) xs.xoff[j] = xoff[j];
-        gemv_stream<QT, NT, R, D>(g, blockIdx.x * 4 + wave, gridDim.x * 4, n_rg, xs, store);
+        for (int j = 0; j < NT; ++j) xoff[j] = ck.row[j] * (uint32_t)a.in_f * 4u;
+        if constexpr (XL) {
+            __syncthreads();  // the previous chunk's waves are done with the staged x
+            constexpr bool SM = GUnit<QT>::RUNS > 0;
+            const XLds<NT, SM> xs{qmm_dyn_lds, xpad_len(a.in_f), qmm_dyn_lds + NT * xpad_len(a.in_f), a.in_f >> 4};
+            run(xs, [&]() { stage_x<NT, SM>(qmm_dyn_lds, xr, xoff, a.in_f); });
+        } else {
+            XGlobal<NT> xs;
+            xs.xr = xr;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) xs.xoff[j] = xoff[j];
+            run(xs, NoPre{});
+        }
     }
 }
 
-// moe_tokens for Q8_1 activations: codes and block scales of the chunk's
-// token rows staged in LDS (always: a row is 2.6 bytes per weight there).
-template <int QT, int NT, int R, int D>
-__device__ __forceinline__ void moe_tokens_q8(float* __restrict__ out, const float* __restrict__ scale,
-                                              const StreamGeom& g, int n_rg, rsrc_t qr, rsrc_t dr,
-                                              const int* plist, const int* tlist, int c0, int cnt,
-                                              int in_f, int n_ff) {
-    const int wave = wave_id();
-    uint32_t qoff[NT], doff[NT];
-    int pj[NT];
-    float fj[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-        const int c = (c0 + j < cnt) ? c0 + j : c0;  // absent slots repeat a real token
-        qoff[j] = (uint32_t)tlist[c] * (uint32_t)in_f;
-        doff[j] = (uint32_t)tlist[c] * (uint32_t)(in_f / 32) * 4u;
-        pj[j] = (c0 + j < cnt) ? plist[c] : -1;
-        fj[j] = scale[plist[c]];
-    }
-    auto store = [&](int64_t row, int j, float v) {
-        if (row < n_ff && pj[j] >= 0) out[(int64_t)pj[j] * n_ff + row] = fj[j] * v;
-    };
-    __syncthreads();  // the previous chunk's waves are done with the staged rows
-    _Float16* sx = (_Float16*)qmm_dyn_lds;
-    const XLdsQ8<NT> xs{sx, q8pad_len(in_f), (const float*)(sx + NT * q8pad_len(in_f)), in_f / 32};
-    gemv_stream<QT, NT, R, D>(g, blockIdx.x * 4 + wave, gridDim.x * 4, n_rg, xs, store,
-                              [&]() { stage_q8<NT>(sx, qr, dr, qoff, doff, in_f); });
-}
-
-template <int QT, int R, int D, bool Q8 = false>
-__global__ __launch_bounds__(256) void moe_gateup_kernel(
-    float* __restrict__ gate_out, float* __restrict__ up_out, const uint8_t* __restrict__ w_gate,
-    const uint8_t* __restrict__ w_up, const int* __restrict__ ids, const float* __restrict__ pscale,
-    const float* __restrict__ x, int t, int n_used, int n_expert, int in_f, int n_ff, int rb,
-    int lpr_log2, int n_rg, int xl, int act_pair, const int8_t* __restrict__ xq = nullptr,
-    const float* __restrict__ xd = nullptr) {
+template <int QT, int R, int D, bool Q8, int MODE>
+__global__ __launch_bounds__(256) void moe_kernel(MoeArgs a) {
     __shared__ int plist[MOE_CHUNK];
     __shared__ int tlist[MOE_CHUNK];
     __shared__ int wcnt[4];
     __shared__ int s_seen;
-    const int n_pairs = t * n_used;
-    const int p = blockIdx.y, plane = blockIdx.z;
+    const int n_pairs = a.t * a.n_used;
+    const int p = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-    const int e = uniform_i32(ids[p]);
-    float* out = plane == 0 ? gate_out : up_out;
-    const float* scale = pscale + (int64_t)plane * n_pairs;
+    const int e = uniform_i32(a.ids[p]);
 
     // Is p the first pair routed to e?
     if (tid == 0) s_seen = 0;
     __syncthreads();
     for (int q0 = 0; q0 < p; q0 += MOE_CHUNK) {
         const int q = q0 + tid;
-        if (q < p && ids[q] == e) s_seen = 1;
+        if (q < p && a.ids[q] == e) s_seen = 1;
     }
     __syncthreads();
     if (s_seen) return;
 
-    const int RG = (64 >> lpr_log2) * R;
-    if (e < 0 || e >= n_expert) {  // invalid id: poison every pair that carries it
+    const int RG = (64 >> a.lpr_log2) * R;
+    if (e < 0 || e >= a.n_expert) {  // invalid id: poison every pair that carries it
+        float* out = MODE == MOE_ACT || blockIdx.z == 0 ? a.out0 : a.out1;
         for (int q = p; q < n_pairs; ++q) {
-            if (ids[q] != e) continue;
-            for (int rg = blockIdx.x; rg < n_rg; rg += gridDim.x)
+            if (a.ids[q] != e) continue;
+            for (int rg = blockIdx.x; rg < a.n_rg; rg += gridDim.x)
                 for (int r = tid; r < RG; r += 256) {
                     const int64_t row = (int64_t)rg * RG + r;
-                    if (row < n_ff) out[(int64_t)q * n_ff + row] = __builtin_nanf("");
+                    if (row < a.n_ff) out[(int64_t)q * a.n_ff + row] = __builtin_nanf("");
                 }
         }
         return;
     }
 
-    const StreamGeom g{(plane == 0 ? w_gate : w_up) + (int64_t)e * n_ff * rb, n_ff, rb, in_f,
-                       lpr_log2};
-    const rsrc_t xr = make_rsrc(x, (uint32_t)(act_pair ? n_pairs : t) * (uint32_t)in_f * 4u);
     for (int q0 = p; q0 < n_pairs; q0 += MOE_CHUNK) {
         // gather the pairs of this chunk routed to e, in pair order
         const int q = q0 + tid;
-        const bool hit = q < n_pairs && ids[q] == e;
+        const bool hit = q < n_pairs && a.ids[q] == e;
         const uint64_t bal = __ballot(hit);
         const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
@@ -142,30 +207,21 @@ __global__ __launch_bounds__(256) void moe_gateup_kernel(
         for (int wv = 0; wv < wave; ++wv) off += wcnt[wv];
         if (hit) {
             plist[off + before] = q;
-            tlist[off + before] = act_pair ? q : q / n_used;  // activation row
+            tlist[off + before] = a.act_pair ? q : q / a.n_used;  // activation row
         }
         const int cnt = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
         __syncthreads();
         for (int c0 = 0; c0 < cnt; c0 += MOE_NT) {
             const int left = cnt - c0;
-            if constexpr (Q8) {
-                const rsrc_t qr = make_rsrc(xq, (uint32_t)t * (uint32_t)in_f);
-                const rsrc_t dr = make_rsrc(xd, (uint32_t)t * (uint32_t)(in_f / 32) * 4u);
+            if (Q8 || a.xl) {
                 if (left == 1)
-                    moe_tokens_q8<QT, 1, R, D>(out, scale, g, n_rg, qr, dr, plist, tlist, c0, cnt, in_f, n_ff);
+                    moe_chunk<QT, 1, R, D, true, Q8, MODE>(a, e, plist, tlist, c0, cnt);
                 else if (left == 2)
-                    moe_tokens_q8<QT, 2, R, D>(out, scale, g, n_rg, qr, dr, plist, tlist, c0, cnt, in_f, n_ff);
+                    moe_chunk<QT, 2, R, D, true, Q8, MODE>(a, e, plist, tlist, c0, cnt);
                 else
-                    moe_tokens_q8<QT, 3, R, D>(out, scale, g, n_rg, qr, dr, plist, tlist, c0, cnt, in_f, n_ff);
-            } else if (xl) {
-                if (left == 1)
-                    moe_tokens<QT, 1, R, D, true>(out, scale, g, n_rg, xr, plist, tlist, c0, cnt, in_f, n_ff);
-                else if (left == 2)
-                    moe_tokens<QT, 2, R, D, true>(out, scale, g, n_rg, xr, plist, tlist, c0, cnt, in_f, n_ff);
-                else
-                    moe_tokens<QT, 3, R, D, true>(out, scale, g, n_rg, xr, plist, tlist, c0, cnt, in_f, n_ff);
-            } else {
-                moe_tokens<QT, MOE_NT, R, 2, false>(out, scale, g, n_rg, xr, plist, tlist, c0, cnt, in_f, n_ff);
+                    moe_chunk<QT, 3, R, D, true, Q8, MODE>(a, e, plist, tlist, c0, cnt);
+            } else if constexpr (!Q8) {  // Q8_1 activations are always staged
+                moe_chunk<QT, MOE_NT, R, 2, false, Q8, MODE>(a, e, plist, tlist, c0, cnt);
             }
         }
     }
@@ -173,78 +229,122 @@ __global__ __launch_bounds__(256) void moe_gateup_kernel(
 
 // ------------------------------------------------------------------ launchers
 
-template <int QT>
-static void launch_moe_qt(float* g, float* u, const uint8_t* wg, const uint8_t* wu, const int* ids,
-                          const float* sc, const float* x, int64_t t, int64_t n_used,
-                          int64_t n_expert, int64_t in_f, int64_t n_ff, int64_t rb, int planes,
-                          int act_pair, const GemvTuning& tune, hipStream_t st) {
-    with_rd<1>(tune, [&](auto Rc, auto Dc) {
-        constexpr int R = decltype(Rc)::value, D = decltype(Dc)::value;
-        const int l = lpr_for(QT, in_f, LPR_CAP_MULTI);
-        const int64_t n_pairs = t * n_used;
-        const int64_t n_rg = (n_ff + rg_rows(l, R) - 1) / rg_rows(l, R);
+// Largest dynamic LDS one MoE work group takes: the staged activations (at
+// most XLDS_MAX_BYTES) plus, in MOE_ACT, the gate buffer.
+constexpr int64_t MOE_LDS_MAX = 96 * 1024;
+
+// The MoE kernels run two rows per lane group and two items in flight per
+// wave (the streaming defaults measured best on MI355X); QMM_GEMV_ROWS and
+// QMM_GEMV_DEPTH tune the GEMV only.
+template <int QT, bool Q8, int MODE>
+static void launch_moe_mode(MoeArgs a, int planes, const GemvTuning& tune, hipStream_t st) {
+    {
+        constexpr int R = 2, D = 2;
+        const int l = lpr_for(QT, a.in_f, LPR_CAP_MULTI);
+        const int64_t n_pairs = (int64_t)a.t * a.n_used;
+        const int64_t RG = rg_rows(l, R);
+        const int64_t n_rg = (a.n_ff + RG - 1) / RG;
         // at most one set of work groups per distinct expert and plane is
         // active; with many pairs the sets are not all distinct, so each set
         // gets at least MOE_MIN_WG work groups
-        const int64_t active = planes * (n_pairs < n_expert ? n_pairs : n_expert);
+        const int64_t active = planes * (n_pairs < a.n_expert ? n_pairs : a.n_expert);
         GemvTuning mt = tune;
         mt.wg_per_cu = tune.moe_wg_per_cu;
         unsigned gx = stream_grid(n_rg, active, mt);
         const unsigned need = (unsigned)((n_rg + 3) / 4);
         if (gx < MOE_MIN_WG) gx = need < MOE_MIN_WG ? need : MOE_MIN_WG;
-        const dim3 grid(gx, (unsigned)n_pairs, (unsigned)planes);
-        const int64_t lds = (int64_t)xlds_floats(MOE_NT, (int)in_f, GUnit<QT>::RUNS > 0) * 4;
-        const int xl = lds <= XLDS_MAX_BYTES;
-        moe_gateup_kernel<QT, R, D><<<grid, 256, (size_t)(xl ? lds : 0), st>>>(
-            g, u, wg, wu, ids, sc, x, (int)t, (int)n_used, (int)n_expert, (int)in_f, (int)n_ff,
-            (int)rb, l, (int)n_rg, xl, act_pair);
-    });
+        int64_t xbytes = Q8 ? (int64_t)q8lds_bytes(MOE_NT, a.in_f)
+                            : (int64_t)xlds_floats(MOE_NT, a.in_f, GUnit<QT>::RUNS > 0) * 4;
+        a.xl = Q8 || xbytes <= XLDS_MAX_BYTES;
+        if (!a.xl) xbytes = 0;
+        int64_t lds = xbytes;
+        a.gbuf_off = 0;
+        if constexpr (MODE == MOE_ACT) {
+            // the gate buffer after the staged activations: a value per row
+            // group the work group streams, per row and token slot; more work
+            // groups (fewer row groups each) until it fits
+            a.gbuf_off = (int)((xbytes + 15) / 16 * 4);
+            auto gbytes = [&](unsigned w) { return (n_rg + 4 * (int64_t)w - 1) / (4 * (int64_t)w) * 4 * RG * MOE_NT * 4; };
+            while (gx < need && 4 * (int64_t)a.gbuf_off + gbytes(gx) > MOE_LDS_MAX) gx = gx * 2 < need ? gx * 2 : need;
+            lds = 4 * (int64_t)a.gbuf_off + gbytes(gx);
+        }
+        a.lpr_log2 = l;
+        a.n_rg = (int)n_rg;
+        const dim3 grid(gx, (unsigned)n_pairs, (unsigned)(MODE == MOE_ACT ? 1 : planes));
+        moe_kernel<QT, R, D, Q8, MODE><<<grid, 256, (size_t)lds, st>>>(a);
+    }
+}
+
+static MoeArgs moe_args(float* o0, float* o1, const void* w0, const void* w1, const int* ids, const float* sc,
+                        const float* x, const int8_t* xq, const float* xd, int64_t t, int64_t n_used,
+                        int64_t n_expert, int64_t in_f, int64_t n_ff, int64_t rb, int act_pair, float limit) {
+    MoeArgs a{};
+    a.out0 = o0;
+    a.out1 = o1;
+    a.w0 = (const uint8_t*)w0;
+    a.w1 = (const uint8_t*)w1;
+    a.ids = ids;
+    a.pscale = sc;
+    a.x = x;
+    a.xq = xq;
+    a.xd = xd;
+    a.t = (int)t;
+    a.n_used = (int)n_used;
+    a.n_expert = (int)n_expert;
+    a.in_f = (int)in_f;
+    a.n_ff = (int)n_ff;
+    a.rb = (int)rb;
+    a.act_pair = act_pair;
+    a.limit = limit;
+    return a;
 }
 
 void launch_moe(float* g, float* u, const void* wg, const void* wu, const int* ids, const float* sc,
                 const float* x, int64_t t, int64_t n_used, int64_t n_expert, int64_t in_f,
                 int64_t n_ff, int qt, int64_t rb, const GemvTuning& tune, hipStream_t st) {
-    const uint8_t* a = (const uint8_t*)wg;
-    const uint8_t* b = (const uint8_t*)wu;
-    QMM_QT_SWITCH(qt, (launch_moe_qt<Q>(g, u, a, b, ids, sc, x, t, n_used, n_expert, in_f, n_ff, rb,
-                                        2, 0, tune, st)))
+    const MoeArgs a = moe_args(g, u, wg, wu, ids, sc, x, nullptr, nullptr, t, n_used, n_expert, in_f, n_ff, rb, 0, 0.f);
+    QMM_QT_SWITCH(qt, (launch_moe_mode<Q, false, MOE_PLANES>(a, 2, tune, st)))
 }
 
-// ------------------------------------------------------------------ Q8_1 gate/up
-template <int QT>
-static void launch_moe_q8_qt(float* g, float* u, const uint8_t* wg, const uint8_t* wu, const int* ids,
-                             const float* sc, const int8_t* xq, const float* xd, int64_t t,
-                             int64_t n_used, int64_t n_expert, int64_t in_f, int64_t n_ff, int64_t rb,
-                             const GemvTuning& tune, hipStream_t st) {
-    with_rd<1>(tune, [&](auto Rc, auto Dc) {
-        constexpr int R = decltype(Rc)::value, D = decltype(Dc)::value;
-        const int l = lpr_for(QT, in_f, LPR_CAP_MULTI);
-        const int64_t n_pairs = t * n_used;
-        const int64_t n_rg = (n_ff + rg_rows(l, R) - 1) / rg_rows(l, R);
-        const int64_t active = 2 * (n_pairs < n_expert ? n_pairs : n_expert);
-        GemvTuning mt = tune;
-        mt.wg_per_cu = tune.moe_wg_per_cu;
-        unsigned gx = stream_grid(n_rg, active, mt);
-        const unsigned need = (unsigned)((n_rg + 3) / 4);
-        if (gx < MOE_MIN_WG) gx = need < MOE_MIN_WG ? need : MOE_MIN_WG;
-        const dim3 grid(gx, (unsigned)n_pairs, 2);
-        moe_gateup_kernel<QT, R, D, true><<<grid, 256, (size_t)q8lds_bytes(MOE_NT, (int)in_f), st>>>(
-            g, u, wg, wu, ids, sc, nullptr, (int)t, (int)n_used, (int)n_expert, (int)in_f, (int)n_ff,
-            (int)rb, l, (int)n_rg, 1, 0, xq, xd);
-    });
+void launch_moe_act(float* act, const void* wg, const void* wu, const int* ids, const float* sc, const float* x,
+                    int64_t t, int64_t n_used, int64_t n_expert, int64_t in_f, int64_t n_ff, int qt, int64_t rb,
+                    float limit, const GemvTuning& tune, hipStream_t st) {
+    const MoeArgs a = moe_args(act, nullptr, wg, wu, ids, sc, x, nullptr, nullptr, t, n_used, n_expert, in_f, n_ff,
+                               rb, 0, limit);
+    QMM_QT_SWITCH(qt, (launch_moe_mode<Q, false, MOE_ACT>(a, 1, tune, st)))
 }
 
+void launch_moe_probe(int arm, float* g, float* u, const void* wg, const void* wu, const int* ids, const float* sc,
+                      const float* x, int64_t t, int64_t n_used, int64_t n_expert, int64_t in_f, int64_t n_ff,
+                      int qt, int64_t rb, const GemvTuning& tune, hipStream_t st) {
+    const MoeArgs a = moe_args(g, u, wg, wu, ids, sc, x, nullptr, nullptr, t, n_used, n_expert, in_f, n_ff, rb, 0, 0.f);
+    if (qt == QT_NVFP4) {
+        if (arm == 1) launch_moe_mode<QT_NVFP4, false, MOE_LOADONLY>(a, 2, tune, st);
+        else launch_moe_mode<QT_NVFP4, false, MOE_MATHONLY>(a, 2, tune, st);
+    } else if (qt == QT_NVFP4_V2) {
+        if (arm == 1) launch_moe_mode<QT_NVFP4_V2, false, MOE_LOADONLY>(a, 2, tune, st);
+        else launch_moe_mode<QT_NVFP4_V2, false, MOE_MATHONLY>(a, 2, tune, st);
+    }
+}
+
+// ------------------------------------------------------------------ Q8_1 activations
 int64_t moe_q8_lds_bytes(int64_t in_f) { return q8lds_bytes(MOE_NT, (int)in_f); }
 
 void launch_moe_q8(float* g, float* u, const void* wg, const void* wu, const int* ids, const float* sc,
                    const int8_t* xq, const float* xd, int64_t t, int64_t n_used, int64_t n_expert,
                    int64_t in_f, int64_t n_ff, int qt, int64_t rb, const GemvTuning& tune, hipStream_t st) {
-    const uint8_t* a = (const uint8_t*)wg;
-    const uint8_t* b = (const uint8_t*)wu;
-    if (qt == QT_NVFP4)
-        launch_moe_q8_qt<QT_NVFP4>(g, u, a, b, ids, sc, xq, xd, t, n_used, n_expert, in_f, n_ff, rb, tune, st);
-    else if (qt == QT_NVFP4_V2)
-        launch_moe_q8_qt<QT_NVFP4_V2>(g, u, a, b, ids, sc, xq, xd, t, n_used, n_expert, in_f, n_ff, rb, tune, st);
+    const MoeArgs a = moe_args(g, u, wg, wu, ids, sc, nullptr, xq, xd, t, n_used, n_expert, in_f, n_ff, rb, 0, 0.f);
+    if (qt == QT_NVFP4) launch_moe_mode<QT_NVFP4, true, MOE_PLANES>(a, 2, tune, st);
+    else if (qt == QT_NVFP4_V2) launch_moe_mode<QT_NVFP4_V2, true, MOE_PLANES>(a, 2, tune, st);
+}
+
+void launch_moe_act_q8(float* act, const void* wg, const void* wu, const int* ids, const float* sc,
+                       const int8_t* xq, const float* xd, int64_t t, int64_t n_used, int64_t n_expert, int64_t in_f,
+                       int64_t n_ff, int qt, int64_t rb, float limit, const GemvTuning& tune, hipStream_t st) {
+    const MoeArgs a = moe_args(act, nullptr, wg, wu, ids, sc, nullptr, xq, xd, t, n_used, n_expert, in_f, n_ff, rb, 0,
+                               limit);
+    if (qt == QT_NVFP4) launch_moe_mode<QT_NVFP4, true, MOE_ACT>(a, 1, tune, st);
+    else if (qt == QT_NVFP4_V2) launch_moe_mode<QT_NVFP4_V2, true, MOE_ACT>(a, 1, tune, st);
 }
 
 // Q8_1 quantization, one thread per block of 32 activations: d = max|x| /
@@ -311,12 +411,7 @@ __global__ __launch_bounds__(256) void moe_slot_sum_kernel(float* __restrict__ y
     }
 }
 
-void launch_moe_down(float* y, float* pair_out, const void* wd, const int* ids, const float* sc,
-                     const float* act, int64_t t, int64_t n_used, int64_t n_expert, int64_t n_ff,
-                     int64_t d_model, int qt, int64_t rb, const GemvTuning& tune, hipStream_t st) {
-    const uint8_t* a = (const uint8_t*)wd;
-    QMM_QT_SWITCH(qt, (launch_moe_qt<Q>(pair_out, pair_out, a, a, ids, sc, act, t, n_used, n_expert,
-                                        n_ff, d_model, rb, 1, 1, tune, st)))
+static void launch_slot_sum(float* y, float* pair_out, int64_t t, int64_t n_used, int64_t d_model, hipStream_t st) {
     const bool v4 = (d_model & 3) == 0 && ((uintptr_t)y & 15) == 0 && ((uintptr_t)pair_out & 15) == 0;
     const int64_t nv = t * d_model / (v4 ? 4 : 1);
     int64_t blocks = (nv + 255) / 256;
@@ -325,6 +420,25 @@ void launch_moe_down(float* y, float* pair_out, const void* wd, const int* ids, 
         moe_slot_sum_kernel<4><<<dim3((unsigned)blocks), 256, 0, st>>>(y, pair_out, t, (int)n_used, d_model);
     else
         moe_slot_sum_kernel<1><<<dim3((unsigned)blocks), 256, 0, st>>>(y, pair_out, t, (int)n_used, d_model);
+}
+
+void launch_moe_down(float* y, float* pair_out, const void* wd, const int* ids, const float* sc,
+                     const float* act, int64_t t, int64_t n_used, int64_t n_expert, int64_t n_ff,
+                     int64_t d_model, int qt, int64_t rb, const GemvTuning& tune, hipStream_t st) {
+    const MoeArgs a = moe_args(pair_out, pair_out, wd, wd, ids, sc, act, nullptr, nullptr, t, n_used, n_expert, n_ff,
+                               d_model, rb, 1, 0.f);
+    QMM_QT_SWITCH(qt, (launch_moe_mode<Q, false, MOE_PLANES>(a, 1, tune, st)))
+    launch_slot_sum(y, pair_out, t, n_used, d_model, st);
+}
+
+void launch_moe_down_q8(float* y, float* pair_out, const void* wd, const int* ids, const float* sc,
+                        const int8_t* aq, const float* ad, int64_t t, int64_t n_used, int64_t n_expert, int64_t n_ff,
+                        int64_t d_model, int qt, int64_t rb, const GemvTuning& tune, hipStream_t st) {
+    const MoeArgs a = moe_args(pair_out, pair_out, wd, wd, ids, sc, nullptr, aq, ad, t, n_used, n_expert, n_ff,
+                               d_model, rb, 1, 0.f);
+    if (qt == QT_NVFP4) launch_moe_mode<QT_NVFP4, true, MOE_PLANES>(a, 1, tune, st);
+    else if (qt == QT_NVFP4_V2) launch_moe_mode<QT_NVFP4_V2, true, MOE_PLANES>(a, 1, tune, st);
+    launch_slot_sum(y, pair_out, t, n_used, d_model, st);
 }
 
 // ------------------------------------------------------------------ V2 repack

@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 
 #include "kernels.hpp"
@@ -178,6 +179,17 @@ bool gemv_tuning(qmm::GemvTuning* t) {
     t->rows = g_tune.rows;
     t->depth = g_tune.depth;
     return true;
+}
+
+// A byte range of an input, for the overlap checks.
+struct Span {
+    const void* p;
+    int64_t n;
+};
+bool overlaps_any(const void* o, int64_t ob, std::initializer_list<Span> ins) {
+    for (const Span& s : ins)
+        if (overlap(o, ob, s.p, s.n)) return true;
+    return false;
 }
 
 int launch_status() {
@@ -418,6 +430,125 @@ int qmm_moe_gateup(float* gate_out, float* up_out, const void* w_gate, const voi
     }
     qmm::launch_moe(gate_out, up_out, w_gate, w_up, expert_ids, pair_scale, x, t, n_used, n_expert,
                     in_f, n_ff, qtype, rb, tune, stream);
+    return launch_status();
+}
+
+// Shared checks of the gate/up family: pairs, both planes' weights, the
+// activation window (x_bytes per token row) and the streaming windows.  On
+// success *rb, *rows (n_expert * n_ff) and *n_pairs are set.
+static int check_moe_gateup(const void* w_gate, const void* w_up, int64_t t, int64_t n_used, int64_t n_expert,
+                            int64_t in_f, int64_t n_ff, int qtype, int64_t x_row_bytes, int64_t* rb, int64_t* rows,
+                            int64_t* n_pairs) {
+    if (t < 1 || n_used < 1 || n_expert < 1 || n_used > n_expert) return QMM_ERR_SHAPE;
+    if (!mul_ok(n_expert, n_ff, rows)) return QMM_ERR_SHAPE;
+    int st = check_weights(w_gate, *rows, in_f, qtype, rb);
+    if (st) return st;
+    st = check_weights(w_up, *rows, in_f, qtype, rb);
+    if (st) return st;
+    if (!mul_ok(t, n_used, n_pairs)) return QMM_ERR_SHAPE;
+    if (*n_pairs > 65535 || n_ff > INT_MAX || t * x_row_bytes >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+    if (qmm::gemv_max_window_bytes(qtype, in_f, *rb) >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+    return QMM_OK;
+}
+
+int qmm_moe_gateup_act(float* act, const void* w_gate, const void* w_up, const int32_t* expert_ids,
+                       const float* pair_scale, const float* x, int64_t t, int64_t n_used, int64_t n_expert,
+                       int64_t in_f, int64_t n_ff, int qtype, float limit, hipStream_t stream) {
+    if (!act || !w_gate || !w_up || !expert_ids || !pair_scale || !x) return QMM_ERR_NULL;
+    int64_t rb, rows, n_pairs;
+    int st = check_moe_gateup(w_gate, w_up, t, n_used, n_expert, in_f, n_ff, qtype, in_f * 4, &rb, &rows, &n_pairs);
+    if (st) return st;
+    if (!aligned(x, 16) || !aligned(act, 4) || !aligned(pair_scale, 4) || !aligned(expert_ids, 4))
+        return QMM_ERR_ALIGN;
+    if (!(limit > 0.0f)) return QMM_ERR_RANGE;  // also NaN
+    qmm::GemvTuning tune;
+    if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
+    const int64_t wb = rows * rb;
+    if (overlaps_any(act, n_pairs * n_ff * 4, {{x, t * in_f * 4}, {w_gate, wb}, {w_up, wb},
+                                                 {expert_ids, n_pairs * 4}, {pair_scale, n_pairs * 8}}))
+        return QMM_ERR_ALIAS;
+    qmm::launch_moe_act(act, w_gate, w_up, expert_ids, pair_scale, x, t, n_used, n_expert, in_f, n_ff, qtype, rb,
+                        limit, tune, stream);
+    return launch_status();
+}
+
+int qmm_moe_gateup_act_q8(float* act, const void* w_gate, const void* w_up, const int32_t* expert_ids,
+                          const float* pair_scale, const int8_t* xq, const float* xd, int64_t t, int64_t n_used,
+                          int64_t n_expert, int64_t in_f, int64_t n_ff, int qtype, float limit, hipStream_t stream) {
+    if (!act || !w_gate || !w_up || !expert_ids || !pair_scale || !xq || !xd) return QMM_ERR_NULL;
+    if (qtype != QMM_NVFP4 && qtype != QMM_NVFP4_V2) return QMM_ERR_QTYPE;
+    int64_t rb, rows, n_pairs;
+    int st = check_moe_gateup(w_gate, w_up, t, n_used, n_expert, in_f, n_ff, qtype, in_f, &rb, &rows, &n_pairs);
+    if (st) return st;
+    if (!aligned(xq, 16) || !aligned(xd, 4) || !aligned(act, 4) || !aligned(pair_scale, 4) ||
+        !aligned(expert_ids, 4))
+        return QMM_ERR_ALIGN;
+    if (qmm::moe_q8_lds_bytes(in_f) > 64 * 1024) return QMM_ERR_RANGE;
+    if (!(limit > 0.0f)) return QMM_ERR_RANGE;
+    qmm::GemvTuning tune;
+    if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
+    const int64_t wb = rows * rb;
+    if (overlaps_any(act, n_pairs * n_ff * 4, {{xq, t * in_f}, {xd, t * in_f / 8}, {w_gate, wb}, {w_up, wb},
+                                                 {expert_ids, n_pairs * 4}, {pair_scale, n_pairs * 8}}))
+        return QMM_ERR_ALIAS;
+    qmm::launch_moe_act_q8(act, w_gate, w_up, expert_ids, pair_scale, xq, xd, t, n_used, n_expert, in_f, n_ff, qtype,
+                           rb, limit, tune, stream);
+    return launch_status();
+}
+
+int qmm_moe_gateup_probe(int arm, float* gate_out, float* up_out, const void* w_gate, const void* w_up,
+                         const int32_t* expert_ids, const float* pair_scale, const float* x, int64_t t,
+                         int64_t n_used, int64_t n_expert, int64_t in_f, int64_t n_ff, int qtype, hipStream_t stream) {
+    if (arm != 1 && arm != 2) return QMM_ERR_PATH;
+    if (!gate_out || !up_out || !w_gate || !w_up || !expert_ids || !pair_scale || !x) return QMM_ERR_NULL;
+    if (qtype != QMM_NVFP4 && qtype != QMM_NVFP4_V2) return QMM_ERR_QTYPE;
+    int64_t rb, rows, n_pairs;
+    int st = check_moe_gateup(w_gate, w_up, t, n_used, n_expert, in_f, n_ff, qtype, in_f * 4, &rb, &rows, &n_pairs);
+    if (st) return st;
+    if (!aligned(x, 16) || !aligned(gate_out, 4) || !aligned(up_out, 4) || !aligned(pair_scale, 4) ||
+        !aligned(expert_ids, 4))
+        return QMM_ERR_ALIGN;
+    qmm::GemvTuning tune;
+    if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
+    const int64_t ob = n_pairs * n_ff * 4, wb = rows * rb;
+    for (float* o : {gate_out, up_out})
+        if (overlaps_any(o, ob, {{x, t * in_f * 4}, {w_gate, wb}, {w_up, wb}, {expert_ids, n_pairs * 4},
+                                 {pair_scale, n_pairs * 8}}))
+            return QMM_ERR_ALIAS;
+    if (overlap(gate_out, ob, up_out, ob)) return QMM_ERR_ALIAS;
+    qmm::launch_moe_probe(arm, gate_out, up_out, w_gate, w_up, expert_ids, pair_scale, x, t, n_used, n_expert, in_f,
+                          n_ff, qtype, rb, tune, stream);
+    return launch_status();
+}
+
+int qmm_moe_down_q8(float* y, float* pair_out, const void* w_down, const int32_t* expert_ids,
+                    const float* pair_scale, const int8_t* aq, const float* ad, int64_t t, int64_t n_used,
+                    int64_t n_expert, int64_t n_ff, int64_t d_model, int qtype, hipStream_t stream) {
+    if (!y || !pair_out || !w_down || !expert_ids || !pair_scale || !aq || !ad) return QMM_ERR_NULL;
+    if (qtype != QMM_NVFP4 && qtype != QMM_NVFP4_V2) return QMM_ERR_QTYPE;
+    if (t < 1 || n_used < 1 || n_expert < 1 || n_used > n_expert) return QMM_ERR_SHAPE;
+    int64_t rb, rows;
+    if (!mul_ok(n_expert, d_model, &rows)) return QMM_ERR_SHAPE;
+    int st = check_weights(w_down, rows, n_ff, qtype, &rb);
+    if (st) return st;
+    if (!aligned(aq, 16) || !aligned(ad, 4) || !aligned(y, 4) || !aligned(pair_out, 4) || !aligned(pair_scale, 4) ||
+        !aligned(expert_ids, 4))
+        return QMM_ERR_ALIGN;
+    int64_t n_pairs, outs;
+    if (!mul_ok(t, n_used, &n_pairs) || !mul_ok(n_pairs, d_model, &outs)) return QMM_ERR_SHAPE;
+    if (n_pairs > 65535 || d_model > INT_MAX || n_pairs * n_ff >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+    if (qmm::gemv_max_window_bytes(qtype, n_ff, rb) >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
+    if (qmm::moe_q8_lds_bytes(n_ff) > 64 * 1024) return QMM_ERR_RANGE;
+    qmm::GemvTuning tune;
+    if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
+    const int64_t yb = t * d_model * 4, pb = outs * 4, wb = rows * rb;
+    for (const Span& o : {Span{y, yb}, Span{pair_out, pb}})
+        if (overlaps_any(o.p, o.n, {{aq, n_pairs * n_ff}, {ad, n_pairs * n_ff / 8}, {w_down, wb},
+                                    {expert_ids, n_pairs * 4}, {pair_scale, n_pairs * 4}}))
+            return QMM_ERR_ALIAS;
+    if (overlap(y, yb, pair_out, pb)) return QMM_ERR_ALIAS;
+    qmm::launch_moe_down_q8(y, pair_out, w_down, expert_ids, pair_scale, aq, ad, t, n_used, n_expert, n_ff, d_model,
+                            qtype, rb, tune, stream);
     return launch_status();
 }
 

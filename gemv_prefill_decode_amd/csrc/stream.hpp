@@ -895,6 +895,41 @@ __device__ __forceinline__ void issue_item(GUnit<QT> (&un)[R], const StreamGeom&
     for (int rr = 0; rr < R; ++rr) un[rr].load(wr, off0 + (uint32_t)(rr * g.rb), e, g.k, ln);
 }
 
+// ------------------------------------------------------------------ measurement twins
+// XOR of a unit's raw words: the load-only twins keep their loads live
+// with it in place of the decode and FMAs.
+template <typename UT>
+__device__ __forceinline__ uint32_t raw_xor(const UT& un);
+
+template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_F32>& u) {
+    uint32_t v = 0;
+    for (int i = 0; i < 16; ++i) v ^= u.r[i];
+    return v;
+}
+template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_Q4_0>& u) {
+    return u.r[0] ^ u.r[1] ^ u.r[2] ^ u.r[3] ^ u.r[4];
+}
+template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_Q8_0>& u) {
+    uint32_t v = 0;
+    for (int i = 0; i < 9; ++i) v ^= u.r[i];
+    return v;
+}
+template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_Q4_K>& u) {
+    return u.hdr.x ^ u.hdr.y ^ u.hdr.z ^ u.hdr.w ^ u.qs.x ^ u.qs.y ^ u.qs.z ^ u.qs.w;
+}
+template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_Q6_K>& u) {
+    uint32_t v = u.rd ^ u.rs[0] ^ u.rs[1] ^ u.rs[2];
+    for (int i = 0; i < 5; ++i) v ^= u.ra[i] ^ u.rb[i] ^ u.rh[i];
+    return v;
+}
+template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_NVFP4>& u) {
+    return u.sd ^ u.qs.x ^ u.qs.y ^ u.qs.z ^ u.qs.w;
+}
+
+template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_NVFP4_V2>& u) {
+    return u.sd ^ u.qs.x ^ u.qs.y ^ u.qs.z ^ u.qs.w;
+}
+
 // Row groups first_rg, first_rg + rg_stride, ... < n_rg.  A row group is the
 // RG = (64/LPR)*R rows that the wave's lane groups cover at once.  Items are
 // numbered it = 0, 1, ...: row group first_rg + (it / upl) * rg_stride, unit
@@ -923,7 +958,15 @@ struct ItemPos {
     }
 };
 
-template <int QT, int NT, int R, int D, typename XS, typename Store, typename Pre = NoPre>
+// ARM selects a measurement twin of the stream (the memra page's ceiling
+// probe arms): STREAM_SERVED computes; STREAM_LOADONLY issues the same loads
+// and folds the raw words into acc[rr][0] by XOR instead of decoding;
+// STREAM_MATHONLY loads the first item's unit for every item (so every load
+// hits the cache) and runs the full arithmetic on it.
+enum : int { STREAM_SERVED = 0, STREAM_LOADONLY = 1, STREAM_MATHONLY = 2 };
+
+template <int QT, int NT, int R, int D, typename XS, typename Store, typename Pre = NoPre,
+          int ARM = STREAM_SERVED>
 __device__ __forceinline__ void gemv_stream(const StreamGeom& g, int first_rg, int rg_stride,
                                             int n_rg, const XS& xs, Store store, Pre pre = {}) {
     using UT = GUnit<QT>;
@@ -981,8 +1024,16 @@ __device__ __forceinline__ void gemv_stream(const StreamGeom& g, int first_rg, i
         for (int d = 0; d < D; ++d) {
             if (d < n_items) {
                 const int q = d / upl, uu = d - q * upl;
-                if (gl + lpr * uu < U)
-                    compute_item<QT, NT, R>(ring[d], ln, ln.e + uu * e_step, g.k, xs, acc);
+                if (gl + lpr * uu < U) {
+                    if constexpr (ARM == STREAM_LOADONLY) {
+#pragma unroll
+                        for (int rr = 0; rr < R; ++rr)
+                            acc[rr][0] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, acc[rr][0]) ^
+                                                                       raw_xor(ring[d][rr]));
+                    } else {
+                        compute_item<QT, NT, R>(ring[d], ln, ln.e + uu * e_step, g.k, xs, acc);
+                    }
+                }
                 if (uu == upl - 1) finish(q);
             }
         }
@@ -1005,10 +1056,21 @@ __device__ __forceinline__ void gemv_stream(const StreamGeom& g, int first_rg, i
             const int it = base + d;
             const bool live = it < n_items;  // wave-uniform
             const int q = cur.q, uu = cur.uu;
-            if (live && gl + lpr * uu < U)
-                compute_item<QT, NT, R>(ring[d], ln, ln.e + uu * e_step, g.k, xs, acc);
-            issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + nxt.q * rg_stride, nxt.uu,
-                              ln.e + nxt.uu * e_step, it + D < n_items);
+            if (live && gl + lpr * uu < U) {
+                if constexpr (ARM == STREAM_LOADONLY) {
+#pragma unroll
+                    for (int rr = 0; rr < R; ++rr)
+                        acc[rr][0] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, acc[rr][0]) ^
+                                                                   raw_xor(ring[d][rr]));
+                } else {
+                    compute_item<QT, NT, R>(ring[d], ln, ln.e + uu * e_step, g.k, xs, acc);
+                }
+            }
+            if constexpr (ARM == STREAM_MATHONLY)
+                issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg, 0, ln.e, it + D < n_items);
+            else
+                issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + nxt.q * rg_stride, nxt.uu,
+                                  ln.e + nxt.uu * e_step, it + D < n_items);
             if (live && uu == upl - 1) finish(q);
             cur.next(upl);
             nxt.next(upl);

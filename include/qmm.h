@@ -250,6 +250,57 @@ int qmm_moe_gateup(float* gate_out, float* up_out,
                    int64_t in_f, int64_t n_ff, int qtype, hipStream_t stream);
 
 /*
+ * qmm_moe_gateup_act: qmm_moe_gateup fused with the activation between the
+ * gate/up and down projections (memra-engine moe_rows_ceiling_bench.rs: the
+ * served gate/up is the "preclamp" kernel with argument 7.0, and its down
+ * arm takes a SwiGLU output as input).  The page does not spell out the
+ * clamp; the reading implemented: with g = gate_out[p*n_ff + r] and
+ * u = up_out[p*n_ff + r] of qmm_moe_gateup,
+ *     act[p*n_ff + r] = silu(min(g, limit)) * clamp(u, -limit, limit),
+ *     silu(z) = z / (1 + exp(-z)),
+ * so the gate is clamped above and the up projection on both sides before
+ * SwiGLU.  limit = +inf is plain SwiGLU.
+ *   act         DEVICE float[n_pairs*n_ff], written: the down projection's
+ *               input (qmm_moe_down's act).
+ *   limit       > 0 (7.0 on the page), or +inf; <= 0 or NaN -> QMM_ERR_RANGE.
+ * Each selected expert's gate and up rows are read once per call, by work
+ * groups that stream a row group's gate rows and then its up rows and
+ * apply the activation in f32 (no gate/up output in memory).  Results
+ * within tau*S_act of the exact value, where S_act carries the projections'
+ * 1e-5 bound through the epilogue (clamps 1-Lipschitz, silu 1.1-Lipschitz)
+ * plus 8 f32 ulps of |act|.  An invalid expert id gives NaN rows.  Other
+ * arguments and errors as qmm_moe_gateup.
+ */
+int qmm_moe_gateup_act(float* act, const void* w_gate, const void* w_up, const int32_t* expert_ids,
+                       const float* pair_scale, const float* x, int64_t t, int64_t n_used, int64_t n_expert,
+                       int64_t in_f, int64_t n_ff, int qtype, float limit, hipStream_t stream);
+
+/* qmm_moe_gateup_act on Q8_1 activations (xq, xd from qmm_quantize_q8_1,
+ * the served arithmetic of the same page): the projections of
+ * qmm_moe_gateup_q8, then the activation.  qtype QMM_NVFP4 or QMM_NVFP4_V2;
+ * in_f at most 8320.  Other arguments and errors as qmm_moe_gateup_act. */
+int qmm_moe_gateup_act_q8(float* act, const void* w_gate, const void* w_up, const int32_t* expert_ids,
+                          const float* pair_scale, const int8_t* xq, const float* xd, int64_t t, int64_t n_used,
+                          int64_t n_expert, int64_t in_f, int64_t n_ff, int qtype, float limit, hipStream_t stream);
+
+/*
+ * qmm_moe_gateup_probe: the measurement twins of qmm_moe_gateup (memra
+ * moe_rows_ceiling_bench.rs, its ceiling-probe arms): the same grid, expert
+ * de-duplication, descriptors and addresses as the served kernel, with
+ *   arm 1  (load-only) the arithmetic deleted: each row's raw words folded
+ *          by XOR into its output slot (a checksum, not a projection);
+ *   arm 2  (math-only) every item loading the first unit of its row group
+ *          (so every load hits the cache) and the full arithmetic run on it.
+ * The outputs are not projections; they only keep the work live.  qtype
+ * QMM_NVFP4 or QMM_NVFP4_V2; arm other than 1 or 2 -> QMM_ERR_PATH.  Other
+ * arguments and errors as qmm_moe_gateup.  For measurement only.
+ */
+int qmm_moe_gateup_probe(int arm, float* gate_out, float* up_out, const void* w_gate, const void* w_up,
+                         const int32_t* expert_ids, const float* pair_scale, const float* x, int64_t t,
+                         int64_t n_used, int64_t n_expert, int64_t in_f, int64_t n_ff, int qtype,
+                         hipStream_t stream);
+
+/*
  * qmm_moe_down: the MoE down projection (memra-engine moe_rows_ceiling_bench.rs,
  * the down arm: one plane of d_model rows over n_ff inputs per expert, each
  * pair's own activation row (the SwiGLU output of its gate/up pair), the down
@@ -279,6 +330,25 @@ int qmm_moe_gateup(float* gate_out, float* up_out,
 int qmm_moe_down(float* y, float* pair_out, const void* w_down, const int32_t* expert_ids,
                  const float* pair_scale, const float* act, int64_t t, int64_t n_used,
                  int64_t n_expert, int64_t n_ff, int64_t d_model, int qtype, hipStream_t stream);
+
+/*
+ * qmm_moe_down_q8: qmm_moe_down on Q8_1 pair activations (memra
+ * moe_rows_ceiling_bench.rs, the down arm: each pair's activation row is
+ * quantized with quantize_q8_1 before moe_down8_fma_q8_rows).  With
+ * act_hat[p*n_ff + c] = ad[p*n_ff/32 + c/32] * aq[p*n_ff + c], the outputs
+ * are those of qmm_moe_down on act_hat; each 16-weight group's dot product
+ * (E2M1 weights times int8 codes) is exact, its E4M3 scale, the block scale
+ * and the sum over groups are applied in f32: within 1e-5 * sum_s
+ * |pair_scale| * sum_c |w * act_hat|.
+ *   aq, ad      DEVICE, as written by qmm_quantize_q8_1 for n_pairs rows of
+ *               n_ff; aq 16-byte aligned.
+ *   qtype       QMM_NVFP4 or QMM_NVFP4_V2 (else QMM_ERR_QTYPE).
+ *   n_ff        a multiple of 64, at most 8320 (LDS: QMM_ERR_RANGE above).
+ * Other arguments and errors as qmm_moe_down.
+ */
+int qmm_moe_down_q8(float* y, float* pair_out, const void* w_down, const int32_t* expert_ids,
+                    const float* pair_scale, const int8_t* aq, const float* ad, int64_t t, int64_t n_used,
+                    int64_t n_expert, int64_t n_ff, int64_t d_model, int qtype, hipStream_t stream);
 
 /*
  * qmm_quantize_q8_1: Q8_1 activations (memra-engine moe_rows_ceiling_bench.rs

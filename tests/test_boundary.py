@@ -252,3 +252,41 @@ def test_gemm_plan_reports_kernels():
     out = (ctypes.c_int32 * 6)()
     assert lib.qmm_gemm_plan(10, 256, 40, 9, 2, 1, out) == 4
     assert lib.qmm_gemm_plan(10, 256, 40, 3, 2, 1, None) == 1
+
+
+def test_moe_block_entry_points_validate_before_launch():
+    """The SwiGLU/clamp gate/up, its Q8_1 form, the Q8_1 down projection
+    and the gate/up measurement twins reject bad arguments on the host."""
+    lib = _lib()
+    A = ctypes.c_void_p(1 << 20)
+    z = ctypes.c_void_p(0)
+    s0 = ctypes.c_void_p(0)
+    F = ctypes.c_float
+    act = lib.qmm_moe_gateup_act
+    act.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 5 + [ctypes.c_int, F, ctypes.c_void_p]
+    ok_args = (1, 8, 64, 4096, 2048, 5)
+    assert act(z, A, A, A, A, A, *ok_args, F(7.0), s0) == 1                 # null act
+    assert act(A, A, A, A, A, A, 1, 9, 8, 4096, 2048, 5, F(7.0), s0) == 2   # n_used > n_expert
+    assert act(A, A, A, A, A, A, 1, 8, 64, 4096, 2048, 8, F(7.0), s0) == 4  # qtype
+    assert act(A, A, A, A, A, A, *ok_args, F(0.0), s0) == 8                 # limit <= 0
+    assert act(A, A, A, A, A, A, *ok_args, F(float("nan")), s0) == 8       # limit NaN
+    X = ctypes.c_void_p(1 << 24)
+    assert act(ctypes.c_void_p((1 << 24) + 64), ctypes.c_void_p(1 << 30), ctypes.c_void_p(1 << 31),
+               ctypes.c_void_p(1 << 26), ctypes.c_void_p(1 << 27), X, *ok_args, F(7.0), s0) == 10  # act over x
+    aq8 = lib.qmm_moe_gateup_act_q8
+    aq8.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 5 + [ctypes.c_int, F, ctypes.c_void_p]
+    assert aq8(A, A, A, A, A, A, A, *ok_args[:5], 3, F(7.0), s0) == 4         # Q4_K weights
+    assert aq8(A, A, A, A, A, A, z, *ok_args, F(7.0), s0) == 1                # null xd
+    assert aq8(A, A, A, A, A, A, A, 1, 8, 64, 8448, 2048, 5, F(7.0), s0) == 8  # rows exceed LDS
+    dq = lib.qmm_moe_down_q8
+    dq.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 5 + [ctypes.c_int, ctypes.c_void_p]
+    assert dq(A, A, A, A, A, z, A, 1, 8, 64, 2048, 4096, 5, s0) == 1        # null aq
+    assert dq(A, A, A, A, A, A, A, 1, 8, 64, 2048, 4096, 2, s0) == 4        # Q8_0 weights
+    assert dq(A, A, A, A, A, A, A, 1, 8, 64, 2000, 4096, 5, s0) == 3        # n_ff % 64
+    assert dq(A, A, A, A, A, A, A, 1, 9, 8, 2048, 4096, 5, s0) == 2         # n_used > n_expert
+    pr = lib.qmm_moe_gateup_probe
+    pr.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 5 + [ctypes.c_int, ctypes.c_void_p]
+    assert pr(0, A, A, A, A, A, A, A, *ok_args, s0) == 7                    # unknown arm
+    assert pr(3, A, A, A, A, A, A, A, *ok_args, s0) == 7
+    assert pr(1, A, A, A, A, A, A, A, 1, 8, 64, 4096, 2048, 3, s0) == 4     # Q4_K weights
+    assert pr(2, z, A, A, A, A, A, A, *ok_args, s0) == 1
