@@ -64,8 +64,15 @@ template <int QT, int WR, int BNT, int KG, bool XF = false> struct Geo {
     static constexpr int A_STAGE = A_CHUNKS * 16;
     static constexpr int STAGE = A_STAGE + B_STAGE;
     static constexpr int NR_FIT = LDS_BYTES / (KG * STAGE);     // rounds of KG stages that fit
+    static constexpr int NR_HALF = LDS_BYTES / 2 / (KG * STAGE);  // ... in half the CU's LDS
     static constexpr int NR_MAX = KG == 1 ? (BNT == 128 ? 4 : 3) : 3;
-    static constexpr int NR = NR_FIT > NR_MAX ? NR_MAX : NR_FIT;
+    // Two work groups per CU (two waves per SIMD, one hiding the other's
+    // load and LDS latency) beat one work group with a deeper ring by 20-45%
+    // wherever a ring of two rounds fits in half the LDS: take the deepest
+    // such ring, else the deepest ring of one work group.
+    static constexpr int NR_PICK = NR_HALF >= 2 ? NR_HALF : NR_FIT;
+    static constexpr int NR = NR_PICK > NR_MAX ? NR_MAX : NR_PICK;
+    static constexpr int PER_CU = LDS_BYTES / (NR * KG * STAGE) >= 2 ? 2 : 1;  // work groups an LDS holds
     static constexpr int NS = NR * KG;
     static constexpr int DA = A_CHUNKS / 256;  // A loads per wave per step (64 chunks each)
     static constexpr int DB = B_STAGE / 4096;  // B loads per wave per step
@@ -623,29 +630,36 @@ static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t 
 }
 
 template <int QT>
-static bool fits_qt(int wr, int bnt, int kg, bool xf) {
+static int per_cu_qt(int wr, int bnt, int kg, bool xf) {
     using namespace lds_ring;
-    if (!xf && wr == 32 && bnt == 128 && kg == 1) return Geo<QT, 32, 128, 1>::OK;
-    if (!xf && wr == 64 && bnt == 128 && kg == 1) return Geo<QT, 64, 128, 1>::OK;
-    if (!xf && wr == 32 && bnt == 256 && kg == 1) return Geo<QT, 32, 256, 1>::OK;
-    if (!xf && wr == 32 && bnt == 128 && kg == 2) return Geo<QT, 32, 128, 2>::OK;
-    if (!xf && wr == 32 && bnt == 256 && kg == 2) return Geo<QT, 32, 256, 2>::OK;
-    if (xf && wr == 32 && bnt == 128 && kg == 1) return Geo<QT, 32, 128, 1, true>::OK;
-    if (xf && wr == 32 && bnt == 128 && kg == 2) return Geo<QT, 32, 128, 2, true>::OK;
-    return false;
+#define QMM_LDS_PER_CU(WR_, BN_, KG_, XF_) \
+    if (xf == XF_ && wr == WR_ && bnt == BN_ && kg == KG_) return Geo<QT, WR_, BN_, KG_, XF_>::OK ? Geo<QT, WR_, BN_, KG_, XF_>::PER_CU : 0;
+    QMM_LDS_PER_CU(32, 128, 1, false)
+    QMM_LDS_PER_CU(64, 128, 1, false)
+    QMM_LDS_PER_CU(32, 256, 1, false)
+    QMM_LDS_PER_CU(32, 128, 2, false)
+    QMM_LDS_PER_CU(32, 256, 2, false)
+    QMM_LDS_PER_CU(32, 128, 1, true)
+    QMM_LDS_PER_CU(32, 128, 2, true)
+#undef QMM_LDS_PER_CU
+    return 0;
+}
+
+int lds_ring_per_cu(int qt, int tile_rows, int tile_tokens, int kg, bool xf) {
+    const int wr = tile_rows / 4;
+    switch (qt) {
+        case QT_F32: return per_cu_qt<QT_F32>(wr, tile_tokens, kg, xf);
+        case QT_Q4_0: return per_cu_qt<QT_Q4_0>(wr, tile_tokens, kg, xf);
+        case QT_Q8_0: return per_cu_qt<QT_Q8_0>(wr, tile_tokens, kg, xf);
+        case QT_Q4_K: return per_cu_qt<QT_Q4_K>(wr, tile_tokens, kg, xf);
+        case QT_Q6_K: return per_cu_qt<QT_Q6_K>(wr, tile_tokens, kg, xf);
+        case QT_NVFP4: return per_cu_qt<QT_NVFP4>(wr, tile_tokens, kg, xf);
+    }
+    return 0;
 }
 
 bool lds_ring_fits(int qt, int tile_rows, int tile_tokens, int kg, bool xf) {
-    const int wr = tile_rows / 4;
-    switch (qt) {
-        case QT_F32: return fits_qt<QT_F32>(wr, tile_tokens, kg, xf);
-        case QT_Q4_0: return fits_qt<QT_Q4_0>(wr, tile_tokens, kg, xf);
-        case QT_Q8_0: return fits_qt<QT_Q8_0>(wr, tile_tokens, kg, xf);
-        case QT_Q4_K: return fits_qt<QT_Q4_K>(wr, tile_tokens, kg, xf);
-        case QT_Q6_K: return fits_qt<QT_Q6_K>(wr, tile_tokens, kg, xf);
-        case QT_NVFP4: return fits_qt<QT_NVFP4>(wr, tile_tokens, kg, xf);
-    }
-    return false;
+    return lds_ring_per_cu(qt, tile_rows, tile_tokens, kg, xf) > 0;
 }
 
 void launch_gemm_lds(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n, int qt,

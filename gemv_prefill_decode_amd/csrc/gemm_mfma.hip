@@ -293,7 +293,8 @@ static void launch_qt(float* dst, const uint8_t* w, const float* x, int64_t m, i
 // LFM2 (n = 512) and 8B-class (n = 2048) shapes.  Per kernel family: the
 // time of one k step of a work group alone on its CU (latency-bound: a
 // single wave per SIMD), the time per step per work group when the CU's
-// work groups are throughput-bound, and how many work groups fit on a CU.
+// work groups are throughput-bound, and how many work groups fit on a CU
+// (for the LDS-ring kernels the ring decides: lds_ring_per_cu).
 struct FamCost {
     int x16, wm, kg;  // the plan's kernel family, tile rows / 64 and k groups
     double step_alone_us;
@@ -304,23 +305,23 @@ constexpr int N_FAM = 9;
 constexpr FamCost FAM_COST[N_FAM] = {
     {0, 2, 1, 1.5, 1.04, 2},   // gemm_mfma_kernel, 128 x 128, f32 activations
     {0, 2, 2, 1.6, 1.6, 1},    // gemm_mfma_kernel with 2 k groups (time per step of the item)
-    // gemm_lds_kernel (one work group per CU: its LDS ring); 128 x 256 tiles
-    // are priced per step of twice the work
-    {2, 2, 1, 1.0, 0.9, 1},    // 128 x 128
-    {2, 4, 1, 2.0, 2.0, 1},    // 256 x 128 (slower than two 128-row tiles everywhere measured)
-    {3, 2, 1, 1.3, 1.3, 1},    // 128 x 256
+    // gemm_lds_kernel; 128 x 256 tiles are priced per step of twice the work.
+    // Two work groups per CU where the ring allows (Q4_0, Q4_K, NVFP4 and
+    // Q8_0 128 x 128, Q6_K 128 x 128, the 4-bit formats' 128 x 256)
+    {2, 2, 1, 1.0, 0.64, 1},   // 128 x 128
+    {2, 4, 1, 2.0, 1.4, 1},    // 256 x 128 (slower than two 128-row tiles everywhere measured)
+    {3, 2, 1, 1.36, 1.07, 1},  // 128 x 256
     {2, 2, 2, 0.8, 0.8, 1},    // 128 x 128, 2 k groups
     {3, 2, 2, 1.1, 1.1, 1},    // 128 x 256, 2 k groups
     // the same with 128 x 128 tiles on the f32 activations (no pre-pass;
-    // more VALU and LDS reads per step for the rounding, which one k group
-    // per CU does not hide)
-    {4, 2, 1, 1.4, 1.3, 1},    // 1 k group
+    // more VALU and LDS reads per step for the rounding)
+    {4, 2, 1, 1.4, 0.85, 1},   // 1 k group
     {4, 2, 2, 0.95, 0.85, 1},  // 2 k groups
 };
 // The LDS-ring kernel's step time by format: Q6_K's two-field 6-bit codes
-// take about a third longer to decode; with 256-token tiles the decode is a
-// smaller share of the step.
-constexpr double LDS_Q6K_FACTOR_128 = 1.3, LDS_Q6K_FACTOR_128_KG2 = 1.15, LDS_Q6K_FACTOR_256 = 1.07;
+// take about a quarter longer to decode; with 256-token tiles the decode is
+// a smaller share of the step.
+constexpr double LDS_Q6K_FACTOR_128 = 1.25, LDS_Q6K_FACTOR_128_KG2 = 1.15, LDS_Q6K_FACTOR_256 = 1.07;
 constexpr double LAUNCH_US = 3.0;      // a launch with its first loads and its stores
 constexpr double SPLIT_US = 4.0;       // the split sum's launch
 constexpr double X16_US = 3.0;         // the f16 pre-pass launch
@@ -358,7 +359,8 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
         const double fmul = x16 < 2 || qt != QT_Q6_K
                                 ? 1.0
                                 : (x16 == 3 ? LDS_Q6K_FACTOR_256 : (kg == 2 ? LDS_Q6K_FACTOR_128_KG2 : LDS_Q6K_FACTOR_128));
-        const FamCost fc{x16, wm, kg, fc0.step_alone_us * fmul, fc0.step_shared_us * fmul, fc0.per_cu};
+        const int per_cu = x16 >= 2 ? lds_ring_per_cu(qt, 64 * wm, x16 == 3 ? 256 : 128, kg, x16 == 4) : fc0.per_cu;
+        const FamCost fc{x16, wm, kg, fc0.step_alone_us * fmul, fc0.step_shared_us * fmul, per_cu};
         const int bn = x16 == 3 ? 256 : 128;
         const int64_t T = ((m + 64 * wm - 1) / (64 * wm)) * ((n + bn - 1) / bn);
         for (int S = 1; S <= 16 && (S == 1 || S <= nk / 2); ++S) {

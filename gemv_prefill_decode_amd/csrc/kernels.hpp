@@ -79,6 +79,8 @@ void launch_gemm_lds(float* dst, const void* w, const float* x, int64_t m, int64
 // tile_tokens for format qt with kg k groups (its stages, or the k-group
 // reduction, must fit the 160 KB of LDS).
 bool lds_ring_fits(int qt, int tile_rows, int tile_tokens, int kg, bool xf);
+// Work groups of that kernel the CU's LDS holds at once (1 or 2), 0 if none fits.
+int lds_ring_per_cu(int qt, int tile_rows, int tile_tokens, int kg, bool xf);
 
 // dst[(i / m)*ldd + i % m] = sum over z < n_split of part[z*zstride + i], in
 // order of z, i < count.
