@@ -53,9 +53,9 @@ template <> struct Fmt<QT_NVFP4> { static constexpr int CPR = 3; };  // 36 B gro
 // The ring holds NS stages, KG per round of steps.
 template <int QT, int WR, int BNT, int KG, bool XF = false> struct Geo {
     static constexpr int BM = 4 * WR;
-    // one stage's activations: BNT tokens x 64 f16, or x 64 f32 (XF: read
-    // straight from the f32 activations, rounded to f16 as they are read)
-    static constexpr int B_STAGE = BNT * (XF ? 256 : 128);
+    // one stage's activations: BNT tokens x 64 f16 (XF: written by the work
+    // group itself from the caller's f32 rows, rounded to f16 once)
+    static constexpr int B_STAGE = BNT * 128;
     static constexpr int CPR = Fmt<QT>::CPR;
     static constexpr int A_ROWS_CHUNKS = BM * CPR;
     // the A loads of a stage cover whole rounds of 4 waves x 64 chunks; the
@@ -74,11 +74,15 @@ template <int QT, int WR, int BNT, int KG, bool XF = false> struct Geo {
     static constexpr int NR = NR_PICK > NR_MAX ? NR_MAX : NR_PICK;
     static constexpr int PER_CU = LDS_BYTES / (NR * KG * STAGE) >= 2 ? 2 : 1;  // work groups an LDS holds
     static constexpr int NS = NR * KG;
-    static constexpr int DA = A_CHUNKS / 256;  // A loads per wave per step (64 chunks each)
-    static constexpr int DB = B_STAGE / 4096;  // B loads per wave per step
+    static constexpr int DA = A_CHUNKS / 256;          // A loads per wave per step (64 chunks each)
+    static constexpr int DB = XF ? 0 : B_STAGE / 4096;  // B loads to LDS per wave per step
+    static constexpr int XC = XF ? BNT / 32 : 0;        // XF: 8-slot units a thread converts per step
+    static constexpr int XL = 2 * XC;                   // XF: its 16-byte f32 loads per step
     // runnable: a ring of at least 2 rounds, its waits within vmcnt's range,
-    // and (KG = 2) room for group 1's accumulators in the ring's LDS
-    static constexpr bool OK = NR >= 2 && (NR - 2) * (DA + DB) <= 63 && (KG == 1 || NS * STAGE >= BM * BNT * 4);
+    // (KG = 2) room for group 1's accumulators in the ring's LDS, and (XF)
+    // 128-token tiles with at most 3 rounds (the waits below assume them)
+    static constexpr bool OK = NR >= 2 && (NR - 2) * (DA + DB + XL) <= 63 &&
+                               (KG == 1 || NS * STAGE >= BM * BNT * 4) && (!XF || (BNT == 128 && NR <= 3));
 };
 
 // k of slot s = 32*ks + 8*g + i of step kt (see the file comment).
@@ -348,9 +352,12 @@ __global__ __launch_bounds__(256) void x16_slot_kernel(uint16_t* __restrict__ x1
 // weight-row tile fastest (as in the other prefill kernels).  Item z covers
 // steps [z*sps, min(nk, (z+1)*sps)); with n_split > 1 it writes its partial
 // tile to partial + z*splitk_stride(n, m), summed by splitk_sum_kernel.
-// XF: the activations are the caller's f32 rows x (ldx floats apart), loaded
-// into the ring as f32 and rounded to f16 (nearest even) as the operands are
-// read, instead of the f16 pre-pass's rows x16 (kp halves apart).
+// XF: the activations are the caller's f32 rows x (ldx floats apart) instead
+// of the f16 pre-pass's rows x16 (kp halves apart).  Each thread of a k group
+// loads XC 8-slot units of its group's step into registers one round ahead,
+// and after the round's barrier writes them, rounded to f16 (nearest even),
+// where the buffer-to-LDS loads would have put the pre-pass's rows: every
+// activation is converted once per work group and no pre-pass runs.
 template <int QT, int WR, int BNT, int KG, bool XF>
 __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict__ dst, const uint8_t* __restrict__ w,
                                                                const uint16_t* __restrict__ x16,
@@ -412,13 +419,8 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
     // f16 rows: B load u covers token t = 8*(wave*DB + u) + lane/8, physical
     // chunk lane % 8 holding logical chunk (lane % 8) ^ (t % 8); the per-load
     // part of the offset is wave-uniform (a scalar offset).
-    // f32 rows (XF): token t = 4*(wave*DB + u) + lane/16, physical chunk
-    // lane % 16 holding logical chunk c = (lane % 16) ^ (t % 16), the 4 f32
-    // of slots 4c .. 4c+3.
     const uint32_t b_off0 = (uint32_t)(8 * wave * DB + (lane >> 3)) * (uint32_t)kp * 2u +
                             16u * (uint32_t)((lane & 7) ^ ((lane >> 3) & 7));
-    // (XF offsets are computed per load in issue(): with a per-lane array of
-    // them, hipcc's host pass failed to instantiate the XF kernels)
     // round r: group grp's step s0 + KG*r + grp into stage KG*slot + grp
     auto issue = [&](int r, int slot) {
         const int kt = s0 + KG * r + grp;
@@ -433,17 +435,45 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
         }
 #pragma unroll
         for (int u = 0; u < DB; ++u) {
-            if constexpr (XF) {
-                const uint32_t soff = kt < nk ? 4u * (uint32_t)lds_ring::step_k0<QT>(kt) : OOB_OFF;
-                const int t = 4 * (wave * DB + u) + (lane >> 4);
-                const int c = (lane & 15) ^ (t & 15);
-                const uint32_t voff = ((uint32_t)t * (uint32_t)ldx + (uint32_t)lds_ring::chunk_rel_k<QT>(c)) * 4u;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(sb + (wave * DB + u) * 1024), 16, voff,
-                                                         soff, 0, 0);
-            } else {
-                const uint32_t soff = kt < nk ? 16u * (uint32_t)u * (uint32_t)kp + 128u * (uint32_t)kt : OOB_OFF;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(sb + (wave * DB + u) * 1024), 16, b_off0,
-                                                         soff, 0, 0);
+            const uint32_t soff = kt < nk ? 16u * (uint32_t)u * (uint32_t)kp + 128u * (uint32_t)kt : OOB_OFF;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(sb + (wave * DB + u) * 1024), 16, b_off0,
+                                                     soff, 0, 0);
+        }
+    };
+
+    // XF: thread lt of the group converts unit xc8 (slots 8*xc8 .. +7) of
+    // tokens xt0 + 32q, q < XC: two 16-byte loads each (slots 8*xc8 .. +3 and
+    // +4 .. +7, each 4 consecutive k), written as 16 bytes of f16 at the
+    // unit's swizzled place in the token's 128-byte stage row.  The token and
+    // the out-of-range bit sit in the vector offset (range-checked), the
+    // step's first k in the scalar one.
+    const int xlt = tid & 255, xc8 = xlt & 7, xt0 = xlt >> 3;
+    const uint32_t xva = ((uint32_t)xt0 * (uint32_t)ldx + (uint32_t)lds_ring::chunk_rel_k<QT>(2 * xc8)) * 4u;
+    const uint32_t xvb = ((uint32_t)xt0 * (uint32_t)ldx + (uint32_t)lds_ring::chunk_rel_k<QT>(2 * xc8 + 1)) * 4u;
+    const uint32_t xwo = (uint32_t)xt0 * 128u + 16u * (uint32_t)(xc8 ^ (xt0 & 7));
+    constexpr int XC1 = G::XC > 0 ? G::XC : 1;
+    u32x4 xa[XC1], xb[XC1];
+    auto xload = [&](int r) {
+        if constexpr (XF) {
+            const int kt = s0 + KG * r + grp;
+            const uint32_t dead = kt < nk ? 0u : OOB_OFF;
+            const uint32_t soff = kt < nk ? 4u * (uint32_t)lds_ring::step_k0<QT>(kt) : 0u;
+#pragma unroll
+            for (int q = 0; q < G::XC; ++q) {
+                const uint32_t tq = 128u * (uint32_t)q * (uint32_t)ldx;  // 32q token rows
+                xa[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, (xva + tq) | dead, soff, 0);
+                xb[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, (xvb + tq) | dead, soff, 0);
+            }
+        }
+    };
+    auto xstore = [&](int slot) {
+        if constexpr (XF) {
+            uint8_t* sb = lds + (KG * slot + grp) * G::STAGE + G::A_STAGE;
+#pragma unroll
+            for (int q = 0; q < G::XC; ++q) {
+                const f32x4 a = __builtin_bit_cast(f32x4, xa[q]), b = __builtin_bit_cast(f32x4, xb[q]);
+                *(u32x4*)(sb + xwo + 4096u * (uint32_t)q) =
+                    u32x4{pack_f2h(a.x, a.y), pack_f2h(a.z, a.w), pack_f2h(b.x, b.y), pack_f2h(b.z, b.w)};
             }
         }
     };
@@ -457,19 +487,17 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
     // this lane's weight rows in a stage, and their offsets in the window
     const int rbase = wave * WR + r16;
     const int bsw = 16 * (g ^ (r16 & 7));  // B chunk of slots [8g, 8g+8) of run ks = 0 (ks = 1: ^4 -> +64)
-    // the B operand of token row bt for run ks: 8 f16, or (XF) the f32
-    // chunks 8ks + 2g and 8ks + 2g + 1 (at chunk ^ r16) rounded to f16
-    auto bfrag = [&](const uint8_t* bt, int ks) -> f16x8 {
-        if constexpr (XF) {
-            const f32x4 p = *(const f32x4*)(bt + 16 * ((8 * ks + 2 * g) ^ r16));
-            const f32x4 q = *(const f32x4*)(bt + 16 * ((8 * ks + 2 * g + 1) ^ r16));
-            return lds_ring::frag4(pack_f2h(p.x, p.y), pack_f2h(p.z, p.w), pack_f2h(q.x, q.y), pack_f2h(q.z, q.w));
-        } else {
-            return *(const f16x8*)(bt + (ks ? bsw ^ 64 : bsw));
-        }
-    };
-    constexpr int BROW = XF ? 256 : 128;  // bytes of one token row of a stage
+    // the B operand of token row bt for run ks: 8 f16
+    auto bfrag = [&](const uint8_t* bt, int ks) -> f16x8 { return *(const f16x8*)(bt + (ks ? bsw ^ 64 : bsw)); };
+    constexpr int BROW = 128;  // bytes of one token row of a stage
 
+    if constexpr (XF) {
+        // round 0's activations into stage 0 before any weight load, then
+        // round 1's in flight behind the first rounds' weight loads
+        xload(0);
+        xstore(0);
+        xload(1);
+    }
 #pragma unroll
     for (int p = 0; p < NR - 1; ++p) issue(p, p);
 
@@ -477,11 +505,24 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
     int cur = 0;
     for (int r = 0; r < nrounds; ++r) {
         // this wave's loads of round r have landed (later rounds' stay in
-        // flight), its LDS reads of round r-1 are done; then every wave's
-        lds_ring::waitcnt<(NR - 2) * (DA + DB), 0>();
+        // flight), its LDS reads of round r-1 and writes of round r's
+        // activations are done; then every wave's.  Loads issued after round
+        // r's weights: rounds r+1 .. r+NR-2 of them, and (XF) the activations
+        // of rounds r+2 .. r+NR-1, except at r = 0, where round 1's
+        // activations went out before all weight loads.
+        if (XF && r == 0)
+            lds_ring::waitcnt<(NR - 2) * DA, 0>();
+        else
+            lds_ring::waitcnt<(NR - 2) * (DA + DB + G::XL), 0>();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+        if constexpr (XF) {
+            // round r+1's activations into the stage round r+1-NR used (every
+            // wave is past it), then round r+2's loads
+            xstore(cur == NR - 1 ? 0 : cur + 1);
+            xload(r + 2);
+        }
         // refill the stages round r-1 used, NR-1 rounds ahead
         issue(r + NR - 1, cur == 0 ? NR - 1 : cur - 1);
 

@@ -314,14 +314,17 @@ constexpr FamCost FAM_COST[N_FAM] = {
     {2, 2, 2, 0.8, 0.8, 1},    // 128 x 128, 2 k groups
     {3, 2, 2, 1.1, 1.1, 1},    // 128 x 256, 2 k groups
     // the same with 128 x 128 tiles on the f32 activations (no pre-pass;
-    // more VALU and LDS reads per step for the rounding)
-    {4, 2, 1, 1.4, 0.85, 1},   // 1 k group
-    {4, 2, 2, 0.95, 0.85, 1},  // 2 k groups
+    // each thread rounds its share of the step's activations to f16 once)
+    {4, 2, 1, 1.1, 0.8, 1},    // 1 k group
+    {4, 2, 2, 0.8, 0.8, 1},    // 2 k groups
 };
 // The LDS-ring kernel's step time by format: Q6_K's two-field 6-bit codes
 // take about a quarter longer to decode; with 256-token tiles the decode is
 // a smaller share of the step.
 constexpr double LDS_Q6K_FACTOR_128 = 1.25, LDS_Q6K_FACTOR_128_KG2 = 1.15, LDS_Q6K_FACTOR_256 = 1.07;
+// f32 weights on f32 activations: the activation rounding adds to the
+// largest weight stages (one work group per CU)
+constexpr double LDS_F32_XF_FACTOR = 1.2;
 constexpr double LAUNCH_US = 3.0;      // a launch with its first loads and its stores
 constexpr double SPLIT_US = 4.0;       // the split sum's launch
 constexpr double X16_US = 3.0;         // the f16 pre-pass launch
@@ -356,7 +359,8 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
         if (x16 >= 2 && (k % 64 != 0 || !lds_ring_fits(qt, 64 * wm, x16 == 3 ? 256 : 128, kg, x16 == 4))) continue;
         if (force && (force->x16 != x16 || force->wm != wm || force->kg != kg)) continue;
         const FamCost& fc0 = FAM_COST[fam];
-        const double fmul = x16 < 2 || qt != QT_Q6_K
+        const double fmul = x16 == 4 && qt == QT_F32 ? LDS_F32_XF_FACTOR
+                            : x16 < 2 || qt != QT_Q6_K
                                 ? 1.0
                                 : (x16 == 3 ? LDS_Q6K_FACTOR_256 : (kg == 2 ? LDS_Q6K_FACTOR_128_KG2 : LDS_Q6K_FACTOR_128));
         const int per_cu = x16 >= 2 ? lds_ring_per_cu(qt, 64 * wm, x16 == 3 ? 256 : 128, kg, x16 == 4) : fc0.per_cu;
