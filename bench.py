@@ -622,9 +622,11 @@ def run_crossover():
 
 
 PLAN_SHAPES = [("ffn_gate", 4608, 1024, 512), ("ffn_down", 1024, 4608, 512), ("conv_in", 3072, 1024, 512),
-               ("attn_out", 1024, 1024, 512), ("8b_up", 14336, 4096, 2048), ("8b_down", 4096, 14336, 2048)]
+               ("attn_out", 1024, 1024, 512), ("8b_up", 14336, 4096, 2048), ("8b_down", 4096, 14336, 2048),
+               ("q4_0_1024_n64", 1024, 1024, 64)]
 # forced prefill plans compared with the planned one (QMM_MFMA_PLAN codes)
-PLAN_FAMILIES = ["0,2,1,2", "2,2,1", "2,2,1,2", "3,2,1", "3,2,1,2", "4,2,1,2"]
+PLAN_FAMILIES = ["0,2,1,2", "2,2,1", "2,2,1,2", "3,2,1", "3,2,1,2", "4,2,1,2", "2,1,1", "2,1,1,2", "4,1,1,2",
+                 "4,1,4,2"]
 
 
 def run_prefill_plans(families=None, shapes=None):
@@ -638,7 +640,7 @@ def run_prefill_plans(families=None, shapes=None):
     for label, m, k, n in PLAN_SHAPES:
         if shapes and label not in shapes:
             continue
-        qts = ["q4_k", "q6_k"] if label.startswith("8b") else QTS
+        qts = ["q4_k", "q6_k"] if label.startswith("8b") else (["q4_0"] if label.startswith("q4_0") else QTS)
         x = to_dev(gen.unit_f32(n * k, gen.SEED_X + k).reshape(n, k))
         for qi, qt in enumerate(qts):
             w = to_dev(gen_weights(qt, m, k, 16 * qi))

@@ -42,7 +42,9 @@ class QmmError(RuntimeError):
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "libqmm.so")
+    """The in-tree libqmm.so, or the library QMM_LIBRARY names (the host-only
+    sanitized build that the boundary tests also run against)."""
+    return os.environ.get("QMM_LIBRARY") or os.path.join(_HERE, "libqmm.so")
 
 
 def load() -> ctypes.CDLL:

@@ -99,9 +99,14 @@ __device__ __forceinline__ float f16hi(uint32_t p) { return (float)__builtin_bit
 
 __device__ __forceinline__ uint32_t byte_of(uint32_t v, int b) { return (v >> (8 * b)) & 0xFFu; }
 
-// Byte b of v as f32 (v_cvt_f32_ubyte{0..3}: select and convert in one
-// instruction; the compiler's own pattern is lost once the byte is known to
-// hold a nibble).
+// Byte B of v as f32: v_cvt_f32_ubyte{0..3}, select and convert in one
+// instruction.  There is no builtin for it, and the plain expression
+// (float)((v >> 8B) & 0xFF) on a nibble-masked v compiles to v_bfe_u32 plus
+// v_cvt_f32_ubyte0 (20 more VALU instructions per Q4_K LDS-ring step): the
+// masks' known bits turn the byte select into a 4-bit field extract.  The
+// result only ever feeds VALU instructions (the f32 or f16 multiply-adds of
+// the decoders), never a matrix-core operand, so no MFMA hazard depends on
+// the compiler seeing this instruction.
 template <int B>
 __device__ __forceinline__ float ubyte_f32(uint32_t v) {
     float r;
@@ -139,15 +144,6 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
     float mag = e == 0u ? sub : norm;
     mag = (b & 0x7Fu) == 0x7Fu ? __builtin_nanf("") : mag;
     return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, mag) | ((b & 0x80u) << 24));
-}
-
-// v as a per-lane (VGPR) value: selects that depend on it compile to
-// v_cndmask rather than to uniform branches, which would split the basic
-// block the scheduler interleaves.
-__device__ __forceinline__ int as_vgpr(int v) {
-    int r;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
-    return r;
 }
 
 // Two OCP FP4 E2M1 codes in byte `sel` of v -> f32 (low nibble first), exact.

@@ -65,7 +65,7 @@ template <int QT, int WR, int BNT, int KG, bool XF = false> struct Geo {
     static constexpr int STAGE = A_STAGE + B_STAGE;
     static constexpr int NR_FIT = LDS_BYTES / (KG * STAGE);     // rounds of KG stages that fit
     static constexpr int NR_HALF = LDS_BYTES / 2 / (KG * STAGE);  // ... in half the CU's LDS
-    static constexpr int NR_MAX = KG == 1 ? (BNT == 128 ? 4 : 3) : 3;
+    static constexpr int NR_MAX = KG == 1 && BNT == 128 && !XF ? 4 : 3;
     // Two work groups per CU (two waves per SIMD, one hiding the other's
     // load and LDS latency) beat one work group with a deeper ring by 20-45%
     // wherever a ring of two rounds fits in half the LDS: take the deepest
@@ -133,10 +133,12 @@ __device__ __forceinline__ f16x8 frag4(uint32_t a, uint32_t b, uint32_t c, uint3
     return __builtin_bit_cast(f16x8, v);
 }
 
-// (1024 + byte) as binary16 for bytes b0 and b0+1 of v, as one f16x2
+// (1024 + byte) as binary16 for bytes b0 and b0+1 of v, as one f16x2: one
+// v_perm_b32 puts the two bytes under the exponent byte 0x64 (selectors 0-3
+// pick bytes of v, 4 the constant's)
 __device__ __forceinline__ f16x2 mpair(uint32_t v, int b0) {
-    const uint32_t bits = ((v >> (8 * b0)) & 0xFFu) | (((v >> (8 * b0 + 8)) & 0xFFu) << 16) | 0x64006400u;
-    return __builtin_bit_cast(f16x2, bits);
+    const uint32_t sel = b0 == 0 ? 0x04010400u : 0x04030402u;
+    return __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, v, sel));
 }
 
 // In-step slot of the first of the 4 consecutive k in f32 chunk c (slots
@@ -253,9 +255,8 @@ template <> struct Dec<QT_Q4_K> {
         const int c = kt & 3;
         const uint32_t sh0 = 16u * (uint32_t)(c & 1);  // byte jj0 = 2(c & 1), jj1 = jj0 + 1
         const uint32_t A = hdr.y >> sh0, B = hdr.z >> sh0, C = hdr.w >> sh0;
-        // all ones for c < 2, else zero; a per-lane value so the blends stay
-        // bit operations in the loop's single basic block
-        const uint32_t lo = (uint32_t)as_vgpr(-(int)(c < 2));
+        // all ones for c < 2, else zero
+        const uint32_t lo = (uint32_t)(-(int)(c < 2));
         auto blend = [lo](uint32_t a, uint32_t b) { return (a & lo) | (b & ~lo); };
         const uint32_t s0 = blend(A & 63u, (C & 15u) | (((A >> 6) & 3u) << 4));
         const uint32_t m0 = blend(B & 63u, ((C >> 4) & 15u) | (((B >> 6) & 3u) << 4));
@@ -659,6 +660,10 @@ static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t 
                 dst, w, x16, x, (int)ldx, (int)m, (int)k, (int)n, (int)rb, (int)kp, n_mb, n_nb, pl.n_split,     \
                 pl.sps, part, (int)ldd, nb_fast);                                                               \
     }
+    QMM_LDS_LAUNCH(16, 128, 1, false)
+    QMM_LDS_LAUNCH(16, 128, 2, false)
+    QMM_LDS_LAUNCH(16, 128, 1, true)
+    QMM_LDS_LAUNCH(16, 128, 2, true)
     QMM_LDS_LAUNCH(32, 128, 1, false)
     QMM_LDS_LAUNCH(64, 128, 1, false)
     QMM_LDS_LAUNCH(32, 256, 1, false)
@@ -675,6 +680,10 @@ static int per_cu_qt(int wr, int bnt, int kg, bool xf) {
     using namespace lds_ring;
 #define QMM_LDS_PER_CU(WR_, BN_, KG_, XF_) \
     if (xf == XF_ && wr == WR_ && bnt == BN_ && kg == KG_) return Geo<QT, WR_, BN_, KG_, XF_>::OK ? Geo<QT, WR_, BN_, KG_, XF_>::PER_CU : 0;
+    QMM_LDS_PER_CU(16, 128, 1, false)
+    QMM_LDS_PER_CU(16, 128, 2, false)
+    QMM_LDS_PER_CU(16, 128, 1, true)
+    QMM_LDS_PER_CU(16, 128, 2, true)
     QMM_LDS_PER_CU(32, 128, 1, false)
     QMM_LDS_PER_CU(64, 128, 1, false)
     QMM_LDS_PER_CU(32, 256, 1, false)

@@ -289,54 +289,59 @@ static void launch_qt(float* dst, const uint8_t* w, const float* x, int64_t m, i
     if (pl.n_split > 1) launch_splitk_sum(dst, part, n * m, splitk_stride(n, m), pl.n_split, m, ldd, st);
 }
 
-// Cost model of the prefill plans, fitted to MI355X measurements of the
-// LFM2 (n = 512) and 8B-class (n = 2048) shapes.  Per kernel family: the
-// time of one k step of a work group alone on its CU (latency-bound: a
-// single wave per SIMD), the time per step per work group when the CU's
-// work groups are throughput-bound, and how many work groups fit on a CU
-// (for the LDS-ring kernels the ring decides: lds_ring_per_cu).
+// Cost model of the prefill plans, fitted (least squares on log time, 242
+// forced-plan timings) to MI355X measurements of the LFM2 (n = 512) and
+// 8B-class (n = 2048) shapes: 7% rms error.  Per kernel family: the time of
+// one k step of a work group alone on its CU (latency-bound), the time per
+// step per work group when the CU's work groups are throughput-bound, and how
+// many work groups fit on a CU (for the LDS-ring kernels the ring decides:
+// lds_ring_per_cu).
 struct FamCost {
     int x16, wm, kg;  // the plan's kernel family, tile rows / 64 and k groups
     double step_alone_us;
     double step_shared_us;
     int per_cu;
 };
-constexpr int N_FAM = 9;
+constexpr int N_FAM = 13;
 constexpr FamCost FAM_COST[N_FAM] = {
-    {0, 2, 1, 1.5, 1.04, 2},   // gemm_mfma_kernel, 128 x 128, f32 activations
-    {0, 2, 2, 1.6, 1.6, 1},    // gemm_mfma_kernel with 2 k groups (time per step of the item)
+    {0, 2, 1, 1.50, 1.04, 2},  // gemm_mfma_kernel, 128 x 128, f32 activations
+    {0, 2, 2, 1.06, 1.60, 1},  // gemm_mfma_kernel with 2 k groups (time per step of the item)
     // gemm_lds_kernel; 128 x 256 tiles are priced per step of twice the work.
     // Two work groups per CU where the ring allows (Q4_0, Q4_K, NVFP4 and
     // Q8_0 128 x 128, Q6_K 128 x 128, the 4-bit formats' 128 x 256)
-    {2, 2, 1, 1.0, 0.64, 1},   // 128 x 128
-    {2, 4, 1, 2.0, 1.4, 1},    // 256 x 128 (slower than two 128-row tiles everywhere measured)
+    {2, 2, 1, 1.00, 0.62, 1},  // 128 x 128
+    {2, 4, 1, 2.00, 1.40, 1},  // 256 x 128 (slower than two 128-row tiles everywhere measured)
     {3, 2, 1, 1.36, 1.07, 1},  // 128 x 256
-    {2, 2, 2, 0.8, 0.8, 1},    // 128 x 128, 2 k groups
-    {3, 2, 2, 1.1, 1.1, 1},    // 128 x 256, 2 k groups
+    {2, 2, 2, 0.72, 0.80, 1},  // 128 x 128, 2 k groups
+    {3, 2, 2, 1.14, 1.10, 1},  // 128 x 256, 2 k groups
     // the same with 128 x 128 tiles on the f32 activations (no pre-pass;
     // each thread rounds its share of the step's activations to f16 once)
-    {4, 2, 1, 1.1, 0.8, 1},    // 1 k group
-    {4, 2, 2, 0.8, 0.8, 1},    // 2 k groups
+    {4, 2, 1, 1.10, 0.80, 1},  // 1 k group
+    {4, 2, 2, 0.81, 0.80, 1},  // 2 k groups
+    // 64 x 128 tiles (twice the work groups of 128-row tiles for the small
+    // products), on f16 and on f32 activations
+    {2, 1, 1, 0.53, 0.41, 1},
+    {2, 1, 2, 0.43, 0.40, 1},
+    {4, 1, 1, 0.65, 0.45, 1},
+    {4, 1, 2, 0.51, 0.42, 1},
 };
 // The LDS-ring kernel's step time by format: Q6_K's two-field 6-bit codes
 // take about a quarter longer to decode; with 256-token tiles the decode is
 // a smaller share of the step.
-constexpr double LDS_Q6K_FACTOR_128 = 1.25, LDS_Q6K_FACTOR_128_KG2 = 1.15, LDS_Q6K_FACTOR_256 = 1.07;
+constexpr double LDS_Q6K_FACTOR_128 = 1.27, LDS_Q6K_FACTOR_128_KG2 = 1.31, LDS_Q6K_FACTOR_256 = 1.04;
 // f32 weights on f32 activations: the activation rounding adds to the
-// largest weight stages (one work group per CU)
-constexpr double LDS_F32_XF_FACTOR = 1.2;
-constexpr double LAUNCH_US = 3.0;      // a launch with its first loads and its stores
-constexpr double SPLIT_US = 4.0;       // the split sum's launch
-constexpr double X16_US = 3.0;         // the f16 pre-pass launch
+// largest weight stages
+constexpr double LDS_F32_XF_FACTOR = 1.29;
+constexpr double LAUNCH_US = 4.4;      // a launch with its first loads and its stores
+constexpr double SPLIT_US = 2.1;       // the split sum's launch
+constexpr double X16_US = 2.7;         // the f16 pre-pass launch
 constexpr double BYTES_PER_US = 4.0e6; // split partials' traffic
-constexpr double X16_BYTES_PER_US = 6.0e6;  // the pre-pass's traffic (a plain stream)
+constexpr double X16_BYTES_PER_US = 8.1e6;  // the pre-pass's traffic (a plain stream)
 // Kernels on f32 activations read twice the activation bytes of the f16
 // ones, once per weight-row tile, from L2: 2nk bytes more per tile row,
-// priced at this rate for the quantized formats (measured: 4096x4096
-// n = 256, 32 tile rows, 4-way split, ran 3-4 us slower on f32 activations
-// than on the pre-pass's f16).  With f32 weights, whose own rows dominate
-// the step, the family's step time already holds it.
-constexpr double XF_L2_BYTES_PER_US = 15.0e6;
+// priced at this rate for the quantized formats.  With f32 weights, whose
+// own rows dominate the step, the family's step time already holds it.
+constexpr double XF_L2_BYTES_PER_US = 20.6e6;
 
 MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, bool have_ws,
                         const MfmaForce* force) {

@@ -126,14 +126,12 @@ template <> struct ALoad<QT_Q4_K> {
         // sub-blocks j0 = 2c, j1 = 2c+1: 6-bit scale and min, unpacked for
         // both halves of the packing and selected (no branch, so the decode
         // stays in the basic block of the matrix-core work it interleaves with)
-        const int cv = as_vgpr(c);
-        const int j0 = 2 * cv, j1 = 2 * cv + 1;
+        const int j0 = 2 * c, j1 = 2 * c + 1;
         const uint32_t b0 = scb(hdr, j0 & 7), b1 = scb(hdr, j1 & 7);            // sc[j]   (j < 4: scale)
         const uint32_t b4 = scb(hdr, j0 + 4), b5 = scb(hdr, j1 + 4);            // sc[j+4]
         const uint32_t bm0 = scb(hdr, (j0 - 4) & 7), bm1 = scb(hdr, (j1 - 4) & 7);  // sc[j-4]
-        // all ones for the first half of the packing (c < 2), else zero; opaque
-        // to the optimizer, so the blends below stay bit operations
-        const uint32_t lo = (uint32_t)as_vgpr(-(int)(cv < 2));
+        // all ones for the first half of the packing (c < 2), else zero
+        const uint32_t lo = (uint32_t)(-(int)(c < 2));
         auto blend = [lo](uint32_t a, uint32_t b) { return (a & lo) | (b & ~lo); };
         const uint32_t s0 = blend(b0 & 63u, (b4 & 15u) | ((bm0 >> 6) << 4));
         const uint32_t m0 = blend(b4 & 63u, (b4 >> 4) | ((b0 >> 6) << 4));

@@ -138,7 +138,7 @@ MfmaForceState parse_force() {
     int a = -1, b = -1, c = -1, d = 1;
     char tail = 0;
     const int got = std::sscanf(v, "%d,%d,%d,%d%c", &a, &b, &c, &d, &tail);
-    if ((got != 3 && got != 4) || a < 0 || a > 4 || a == 1 || (b != 2 && b != 4) || (a != 2 && b != 2) ||
+    if ((got != 3 && got != 4) || a < 0 || a > 4 || a == 1 || (b != 1 && b != 2 && b != 4) || (b == 4 && a != 2) || (b == 1 && a != 2 && a != 4) ||
         c < 1 || c > 16 || (d != 1 && d != 2)) {
         g_force.bad = true;
         return g_force;
