@@ -31,7 +31,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_kernel(float* __restrict__ dst,
         constexpr bool SM = GUnit<QT>::RUNS > 0;
         const XLds<NT, SM> xs{qmm_dyn_lds, xpad_len(k), qmm_dyn_lds + NT * xpad_len(k), k >> 4};
         gemv_stream<QT, NT, R, D>(g, blockIdx.x * WPG + wave, gridDim.x * WPG, n_rg, xs, store,
-                                  [&]() { stage_x<NT, SM, 64 * WPG>(qmm_dyn_lds, xr, xoff, k); });
+                                  make_xstage<NT, SM, 64 * WPG>(qmm_dyn_lds, xr, xoff, k));
     } else {
         XGlobal<NT> xs;
         xs.xr = xr;
@@ -129,7 +129,7 @@ int gemv_unit_elems(int qt) { return unit_elems_of(qt); }
 
 int64_t gemv_max_window_bytes(int qt, int64_t k, int64_t rb) {
     // the smaller lane groups give the taller row groups
-    return rg_rows(lpr_for(qt, k, LPR_CAP_MULTI), 2) * rb + 16;
+    return rg_rows(lpr_for(qt, k, LPR_CAP_MIN), 2) * rb + 16;
 }
 
 template <int QT, int NT>

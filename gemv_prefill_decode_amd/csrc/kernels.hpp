@@ -8,12 +8,19 @@
 namespace qmm {
 
 // Launch-shape choices for the streaming (GEMV / MoE / load-only) kernels.
+// log2 of the largest lane group per weight row in the streams that apply
+// each weight to several activation rows (the GEMV at n > 2 and the MoE), and
+// the smallest value the MoE tuning may set (the row windows' range checks
+// assume it)
+constexpr int LPR_CAP_MULTI = 4, LPR_CAP_MIN = 3;
+
 struct GemvTuning {
     int num_cu;     // compute units of the device
     int wg_per_cu;  // work groups per CU the grid is sized for
     int moe_wg_per_cu;  // the same for the MoE kernels
     int rows;       // rows per lane group (1 or 2)
     int depth;      // items of weight loads kept in flight per wave (2, 4 or 8)
+    int moe_lpr_cap;  // log2 of the largest lane group per row in the MoE streams
     int lds_per_wg; // bytes of LDS one work group may allocate
     int lds_per_cu; // bytes of LDS per CU (limits resident work groups)
 };

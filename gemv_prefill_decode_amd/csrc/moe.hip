@@ -137,7 +137,13 @@ __device__ __forceinline__ void moe_chunk(const MoeArgs& a, int e, const int* pl
         __syncthreads();  // the previous chunk's waves are done with the staged rows
         _Float16* sx = (_Float16*)qmm_dyn_lds;
         const XLdsQ8<NT> xs{sx, q8pad_len(a.in_f), (const float*)(sx + NT * q8pad_len(a.in_f)), a.in_f / 32};
-        run(xs, [&]() { stage_q8<NT>(sx, qr, dr, qoff, doff, a.in_f); });
+        Q8Stage<NT> st{sx, qr, dr, {}, {}, a.in_f};
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            st.qoff[j] = qoff[j];
+            st.doff[j] = doff[j];
+        }
+        run(xs, st);
     } else {
         const rsrc_t xr = make_rsrc(a.x, (uint32_t)n_rows * (uint32_t)a.in_f * 4u);
         uint32_t xoff[NT];
@@ -147,7 +153,7 @@ __device__ __forceinline__ void moe_chunk(const MoeArgs& a, int e, const int* pl
             __syncthreads();  // the previous chunk's waves are done with the staged x
             constexpr bool SM = GUnit<QT>::RUNS > 0;
             const XLds<NT, SM> xs{qmm_dyn_lds, xpad_len(a.in_f), qmm_dyn_lds + NT * xpad_len(a.in_f), a.in_f >> 4};
-            run(xs, [&]() { stage_x<NT, SM>(qmm_dyn_lds, xr, xoff, a.in_f); });
+            run(xs, make_xstage<NT, SM>(qmm_dyn_lds, xr, xoff, a.in_f));
         } else {
             XGlobal<NT> xs;
             xs.xr = xr;
@@ -240,7 +246,7 @@ template <int QT, bool Q8, int MODE>
 static void launch_moe_mode(MoeArgs a, int planes, const GemvTuning& tune, hipStream_t st) {
     {
         constexpr int R = 2, D = 2;
-        const int l = lpr_for(QT, a.in_f, LPR_CAP_MULTI);
+        const int l = lpr_for(QT, a.in_f, tune.moe_lpr_cap);
         const int64_t n_pairs = (int64_t)a.t * a.n_used;
         const int64_t RG = rg_rows(l, R);
         const int64_t n_rg = (a.n_ff + RG - 1) / RG;

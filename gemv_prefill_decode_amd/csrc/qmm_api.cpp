@@ -92,6 +92,7 @@ struct TuneState {
     int moe_wg_per_cu = 2;
     int rows = 2;
     int depth = 2;
+    int moe_lpr_cap = qmm::LPR_CAP_MULTI;
     bool bad = false;
 };
 TuneState g_tune;
@@ -109,7 +110,8 @@ void parse_tune() {
     const int mw = env_int("QMM_MOE_WG_PER_CU", g_tune.moe_wg_per_cu, 1, 64);
     const int r = env_int("QMM_GEMV_ROWS", g_tune.rows, 1, 2);
     const int d = env_int("QMM_GEMV_DEPTH", g_tune.depth, 2, 8);
-    if (w < 0 || mw < 0 || r < 0 || d < 0 || (d & (d - 1)) != 0) {
+    const int ml = env_int("QMM_MOE_LPR_LOG2", g_tune.moe_lpr_cap, qmm::LPR_CAP_MIN, 6);
+    if (w < 0 || mw < 0 || r < 0 || d < 0 || ml < 0 || (d & (d - 1)) != 0) {
         g_tune.bad = true;
         return;
     }
@@ -117,6 +119,7 @@ void parse_tune() {
     g_tune.moe_wg_per_cu = mw;
     g_tune.rows = r;
     g_tune.depth = d;
+    g_tune.moe_lpr_cap = ml;
 }
 
 // QMM_MFMA_PLAN="x16,wm,n_split[,kg]" forces the prefill plan of calls with
@@ -178,6 +181,7 @@ bool gemv_tuning(qmm::GemvTuning* t) {
     t->moe_wg_per_cu = g_tune.moe_wg_per_cu;
     t->rows = g_tune.rows;
     t->depth = g_tune.depth;
+    t->moe_lpr_cap = g_tune.moe_lpr_cap;
     return true;
 }
 

@@ -532,25 +532,34 @@ struct XGlobal {
 };
 
 // Stage rows xoff[j] (j < NT) of x (row length k) into LDS in the padded
-// layout.  All threads of the work group take part, each with at least 8
-// independent 16-byte loads in flight per batch; ends with a barrier.  With
-// SUMS, the sums of each run of 16 activations (k/16 per row, k a multiple
-// of 16) follow the rows: ((x0+x1)+(x2+x3)) + ... in a fixed order.
+// layout, in two phases.  issue() loads the first batch into registers (each
+// thread at least 8 independent 16-byte loads); finish() writes it, stages
+// the remaining batches, and ends with a barrier.  A stream issues the first
+// batch before its weight loads: waits count loads in issue order, so the
+// activations then land without waiting for the weights.  With SUMS, the sums
+// of each run of 16 activations (k/16 per row, k a multiple of 16) follow the
+// rows: ((x0+x1)+(x2+x3)) + ... in a fixed order.
 template <int NT, bool SUMS = false, int TPB = 256>
-__device__ __forceinline__ void stage_x(float* sx, rsrc_t xr, const uint32_t (&xoff)[NT], int k) {
-    constexpr int U = NT >= 8 ? 1 : 8 / NT;  // float4 columns per thread per batch
-    const int ld = xpad_len(k);
-    const int per = k >> 2;  // float4 per row
-    for (int c0 = threadIdx.x; c0 < per; c0 += TPB * U) {
-        f32x4 v[NT][U];
+struct XStage {
+    static constexpr int U = NT >= 8 ? 1 : 8 / NT;  // float4 columns per thread per batch
+    float* sx;
+    rsrc_t xr;
+    uint32_t xoff[NT];
+    int k;
+    f32x4 v[NT][U];
+
+    __device__ __forceinline__ void load(int c0) {
+        const int per = k >> 2;  // float4 per row
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c = c0 + TPB * u;
 #pragma unroll
             for (int j = 0; j < NT; ++j)
-                v[j][u] = __builtin_bit_cast(
-                    f32x4, ld128(xr, c < per ? xoff[j] + 16u * (uint32_t)c : OOB_OFF));
+                v[j][u] = __builtin_bit_cast(f32x4, ld128(xr, c < per ? xoff[j] + 16u * (uint32_t)c : OOB_OFF));
         }
+    }
+    __device__ __forceinline__ void store(int c0) {
+        const int ld = xpad_len(k), per = k >> 2;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c = c0 + TPB * u;
@@ -559,21 +568,41 @@ __device__ __forceinline__ void stage_x(float* sx, rsrc_t xr, const uint32_t (&x
                 for (int j = 0; j < NT; ++j) *(f32x4*)(sx + j * ld + xpad(4 * c)) = v[j][u];
         }
     }
-    __syncthreads();
-    if constexpr (SUMS) {
-        const int nrun = k >> 4;
-        float* sums = sx + NT * ld;
-        for (int t = threadIdx.x; t < NT * nrun; t += TPB) {
-            const int j = t / nrun, r = t - j * nrun;
-            const float* p = sx + j * ld + xpad(16 * r);  // 16 contiguous floats
-            const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
-            const f32x4 c = *(const f32x4*)(p + 8), d = *(const f32x4*)(p + 12);
-            const float sa = (a.x + a.y) + (a.z + a.w), sb = (b.x + b.y) + (b.z + b.w);
-            const float sc = (c.x + c.y) + (c.z + c.w), sd = (d.x + d.y) + (d.z + d.w);
-            sums[t] = (sa + sb) + (sc + sd);
+    __device__ __forceinline__ void issue() { load((int)threadIdx.x); }
+    __device__ __forceinline__ void finish() {
+        store((int)threadIdx.x);
+        for (int c0 = (int)threadIdx.x + TPB * U; c0 < (k >> 2); c0 += TPB * U) {
+            load(c0);
+            store(c0);
         }
         __syncthreads();
+        if constexpr (SUMS) {
+            const int ld = xpad_len(k), nrun = k >> 4;
+            float* sums = sx + NT * ld;
+            for (int t = threadIdx.x; t < NT * nrun; t += TPB) {
+                const int j = t / nrun, r = t - j * nrun;
+                const float* p = sx + j * ld + xpad(16 * r);  // 16 contiguous floats
+                const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+                const f32x4 c = *(const f32x4*)(p + 8), d = *(const f32x4*)(p + 12);
+                const float sa = (a.x + a.y) + (a.z + a.w), sb = (b.x + b.y) + (b.z + b.w);
+                const float sc = (c.x + c.y) + (c.z + c.w), sd = (d.x + d.y) + (d.z + d.w);
+                sums[t] = (sa + sb) + (sc + sd);
+            }
+            __syncthreads();
+        }
     }
+};
+
+template <int NT, bool SUMS = false, int TPB = 256>
+__device__ __forceinline__ XStage<NT, SUMS, TPB> make_xstage(float* sx, rsrc_t xr, const uint32_t (&xoff)[NT],
+                                                            int k) {
+    XStage<NT, SUMS, TPB> st;
+    st.sx = sx;
+    st.xr = xr;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) st.xoff[j] = xoff[j];
+    st.k = k;
+    return st;
 }
 
 // LDS floats of NT staged rows (and their run sums).
@@ -812,6 +841,17 @@ __device__ __forceinline__ void stage_q8(_Float16* sx, rsrc_t qr, rsrc_t dr, con
     __syncthreads();
 }
 
+// stage_q8 as a stream's staging step (no early loads).
+template <int NT>
+struct Q8Stage {
+    _Float16* sx;
+    rsrc_t qr, dr;
+    uint32_t qoff[NT], doff[NT];
+    int k;
+    __device__ __forceinline__ void issue() {}
+    __device__ __forceinline__ void finish() { stage_q8<NT>(sx, qr, dr, qoff, doff, k); }
+};
+
 // One NVFP4 unit (32 weights: two groups of 16 with their E4M3 scales)
 // against Q8_1 rows.  Each group's dot product is exact: E2M1 values and
 // int8 codes are exact in f16, their products and the sums of 16 of them
@@ -938,12 +978,13 @@ template <> __device__ __forceinline__ uint32_t raw_xor(const GUnit<QT_NVFP4_V2>
 // with item it + D right after item it is consumed.  store(row, j, value) is
 // called by lane gl == 0 of each lane group for every row (rows >= m too).
 struct NoPre {
-    __device__ void operator()() const {}
+    __device__ void issue() {}
+    __device__ void finish() {}
 };
 
-// pre() is called by every wave once the ring's first loads are issued (the
-// work group's activation staging, with its barrier, goes there so that it
-// overlaps the first weight loads).
+// pre.issue() is called by every wave before the ring's first loads and
+// pre.finish() once they are issued (the work group's activation staging,
+// with its barrier, goes there so that it overlaps the first weight loads).
 // Position (row-group step q, unit uu) of a stream item, advanced by one
 // item without the integer division it / upl (a division is about thirty
 // scalar and vector instructions; the loops below advance two positions per
@@ -1011,6 +1052,7 @@ __device__ __forceinline__ void gemv_stream(const StreamGeom& g, int first_rg, i
     if (n_items <= D) {
         // Short stream: every item's loads are in flight before the first
         // is consumed.
+        pre.issue();
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             if (d < n_items) {
@@ -1019,7 +1061,7 @@ __device__ __forceinline__ void gemv_stream(const StreamGeom& g, int first_rg, i
                                   ln.e + uu * e_step, true);
             }
         }
-        pre();
+        pre.finish();
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             if (d < n_items) {
@@ -1042,13 +1084,14 @@ __device__ __forceinline__ void gemv_stream(const StreamGeom& g, int first_rg, i
     // Long stream: a ring of D items.  Every refill is issued, also for items
     // past the end (they read nothing), so the wait before an item counts
     // only the loads issued after it on every path.
+    pre.issue();
 #pragma unroll
     for (int d = 0; d < D; ++d) {
         const int q = d / upl, uu = d - q * upl;
         issue_item<QT, R>(ring[d], g, RG, lane_row_off, ln, first_rg + q * rg_stride, uu,
                           ln.e + uu * e_step, true);
     }
-    pre();
+    pre.finish();
     ItemPos cur{0, 0}, nxt{D / upl, D - (D / upl) * upl};
     for (int base = 0; base < n_items; base += D) {
 #pragma unroll
@@ -1118,7 +1161,7 @@ static inline int min_lpr(int qt) {
 // GEMV shrinks its groups only while the rows still give one row group per
 // SIMD (on 1024x4608 q4_0, n = 4, 16-lane groups left 128 waves for 1024
 // SIMDs: 17.3 against 9.3 us).
-constexpr int LPR_CAP_SINGLE = 6, LPR_CAP_MULTI = 4;
+constexpr int LPR_CAP_SINGLE = 6;  // LPR_CAP_MULTI, LPR_CAP_MIN: kernels.hpp
 
 static inline int lpr_for(int qt, int64_t k, int cap_log2) {
     const int ue = unit_elems_of(qt);
