@@ -165,7 +165,7 @@ def test_gemv_max_n_env_is_strict(value, expect):
 
 
 @pytest.mark.parametrize("var", ["QMM_GEMV_WG_PER_CU", "QMM_MOE_WG_PER_CU", "QMM_GEMV_ROWS",
-                                 "QMM_GEMV_DEPTH"])
+                                 "QMM_GEMV_DEPTH", "QMM_MOE_LPR_LOG2"])
 @pytest.mark.parametrize("value", ["0", "abc", "65", "3x"])
 def test_streaming_tuning_env_is_strict(var, value):
     """A malformed or out-of-range launch-shape knob makes the streaming

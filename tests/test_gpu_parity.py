@@ -512,6 +512,43 @@ def test_forced_prefill_plans(plan, qt, monkeypatch):
 
 # ------------------------------------------------------------------ NVFP4 V2
 
+def _nvfp4_every_scale_code(m, k, seed):
+    """NVFP4 rows (36-byte groups: 4 E4M3 scale bytes, 32 bytes of E2M1
+    nibbles) whose scale bytes run through every finite E4M3 code (all but
+    0x7F and 0xFF) in turn, random nibbles."""
+    w = gen.nvfp4_rows(m, k, gen.SEED_MOE_W + seed).copy()
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    groups = w.reshape(-1, 36)
+    groups[:, :4] = np.resize(codes, groups.shape[0] * 4).reshape(-1, 4)
+    return w
+
+
+def test_nvfp4_every_scale_code():
+    """The device's E4M3 scale decode (v_cvt_f32_fp8) on all 254 finite codes,
+    subnormals and both signs included: the GEMV against the oracle at the f32
+    tolerance, and the matrix-core paths on identity activations giving
+    f16(W) exactly (every NVFP4 weight is exact in f16)."""
+    import os
+    import gemv_prefill_decode_amd as qmm
+    m, k = 96, 768   # 96 * 12 groups * 4 = 4608 scale slots: every code 18 times
+    w = _nvfp4_every_scale_code(m, k, 71)
+    W = formats.decode("nvfp4", w, m, k)
+    assert np.all(np.isfinite(W))
+    note("nvfp4 every scale code: gemv")
+    x = acts(3, k, 71)
+    check_full("nvfp4", w, x, m, k, 3, gpu_gemm("nvfp4", w, x, m, "gemv"), TAU_F32, "e4m3 codes gemv")
+    eye = np.eye(k, dtype=np.float32)
+    for plan in (None, "0,2,1,1", "2,2,1", "4,1,1,2"):
+        note(f"nvfp4 every scale code: mfma plan {plan}")
+        if plan:
+            os.environ["QMM_MFMA_PLAN"] = plan
+        try:
+            got = gpu_gemm("nvfp4", w, eye, m, "mfma")
+        finally:
+            os.environ.pop("QMM_MFMA_PLAN", None)
+        assert_f16_weights(got, W)
+
+
 def test_nvfp4_v2_repack_bit_exact():
     """The device repack equals the oracle's byte permutation, on a ragged
     row count and on an expert tensor (experts x rows flattened)."""
