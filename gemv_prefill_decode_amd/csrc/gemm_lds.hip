@@ -562,16 +562,35 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
                 lds_ring::Dec<QT>::run(sa + rr * CPR * 16, rowoff0 + (uint32_t)rr * (uint32_t)rb, kt, g, rr & 15,
                                        a0[i], a1[i]);
             }
+            // B operands PF token blocks ahead in a register ring, so each
+            // block's LDS reads are in flight behind the matrix-core ops of
+            // the blocks before it (with two work groups per CU; with one,
+            // PF = 1 reads each block just before its use, as measured
+            // faster there: Q6_K 14336x4096x2048 386 against 401 us)
+            constexpr int PF = G::PER_CU == 2 ? 4 : 1;
+            f16x8 bq0[PF], bq1[PF];
+#pragma unroll
+            for (int j = 0; j < PF; ++j) {
+                const uint8_t* bt = sb + (16 * j + r16) * BROW;
+                bq0[j] = bfrag(bt, 0);
+                bq1[j] = bfrag(bt, 1);
+            }
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const uint8_t* bt = sb + (16 * j + r16) * BROW;
-                const f16x8 b0 = bfrag(bt, 0);
-                const f16x8 b1 = bfrag(bt, 1);
+                const f16x8 b0 = bq0[j % PF], b1 = bq1[j % PF];
+                if (j + PF < NJ) {
+                    const uint8_t* bt = sb + (16 * (j + PF) + r16) * BROW;
+                    bq0[j % PF] = bfrag(bt, 0);
+                    bq1[j % PF] = bfrag(bt, 1);
+                }
 #pragma unroll
                 for (int i = 0; i < RI; ++i) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[i], b0, acc[i][j], 0, 0, 0);
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1[i], b1, acc[i][j], 0, 0, 0);
                 }
+                // a scheduling fence per block: the scheduler would otherwise
+                // sink each prefetch read down to its use
+                if constexpr (PF > 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
