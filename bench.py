@@ -709,6 +709,105 @@ def run_counter_workload():
         torch.cuda.empty_cache()
 
 
+STREAM_COUNTER_SET = ("SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES "
+                      "SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU")
+
+
+def run_stream_counter_workload():
+    """The streaming kernels three times each (synchronized, eager), for a
+    rocprofv3 --pmc run: the n=1 GEMV and its load-only twin on 14336x4096
+    Q4_K and Q6_K, the NVFP4 MoE gate/up at t=1 and t=16 with its load-only
+    and math-only twins."""
+    import numpy as np
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    from synth import gen
+    for qt in ("q4_k", "q6_k"):
+        m, k = 14336, 4096
+        w = to_dev(gen_weights(qt, m, k, 99))
+        x = to_dev(gen.unit_f32(k, gen.SEED_X).reshape(1, k))
+        out = torch.empty((1, m), dtype=torch.float32, device="cuda")
+        sink = torch.empty(m, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            qmm.gemm(w, x, m, qt, out=out, path="gemv")
+            torch.cuda.synchronize()
+            qmm.stream_loadonly(w, m, k, qt, sink)
+            torch.cuda.synchronize()
+        print(json.dumps({"tag": f"gemv_n1_{qt}_{m}x{k}", "weights": m * k}), flush=True)
+        del w, x, out, sink
+    n_expert, in_f, n_ff, n_used = 64, 4096, 2048, 8
+    wg = to_dev(np.concatenate([gen.nvfp4_rows(n_ff, in_f, gen.SEED_MOE_W + 2 * e) for e in range(n_expert)]))
+    wu = to_dev(np.concatenate([gen.nvfp4_rows(n_ff, in_f, gen.SEED_MOE_W + 2 * e + 1) for e in range(n_expert)]))
+    for t in (1, 16):
+        ids_h = gen.expert_ids(t, n_used, n_expert, gen.SEED_EXPERTS)
+        ids = to_dev(ids_h)
+        sc = to_dev(gen.pair_scales(2 * t * n_used))
+        x = to_dev(gen.xorshift_f32(t * in_f, gen.SEED_MOE_X).reshape(t, in_f))
+        for _ in range(3):
+            qmm.moe_gateup(wg, wu, ids, sc, x, n_expert, n_ff)
+            torch.cuda.synchronize()
+            qmm.moe_gateup_probe("loadonly", wg, wu, ids, sc, x, n_expert, n_ff)
+            torch.cuda.synchronize()
+            qmm.moe_gateup_probe("mathonly", wg, wu, ids, sc, x, n_expert, n_ff)
+            torch.cuda.synchronize()
+        print(json.dumps({"tag": f"moe_gateup_t{t}", "weights": 2 * len(np.unique(ids_h)) * n_ff * in_f}),
+              flush=True)
+
+
+def stream_counter_summary(tags_path, csv_path, out_path):
+    """profiles/stream_counters.md from --stream-counter-workload's tags and
+    its --pmc counter_collection.csv: per streaming kernel and grid, wave
+    instructions per weight (VALU, LDS, SALU), VALU issue time per SIMD at 4
+    cycles per wave64 instruction, and the share of wave cycles spent waiting
+    or issuing VALU."""
+    import csv
+    import collections
+    tags = [json.loads(ln) for ln in open(tags_path) if ln.startswith("{")]
+    order = []
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(csv_path)):
+        name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("qmm::", "").strip()
+        if not name.startswith(("gemv_kernel", "loadonly_kernel", "moe_kernel")):
+            continue
+        key = (name, int(r["Grid_Size"]))
+        if key not in vals:
+            order.append(key)
+        vals[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    # kernels in call order: gemv q4_k (served, load-only), gemv q6_k, then per t the MoE served,
+    # load-only and math-only twins
+    groups = {"gemv": [t for t in tags if t["tag"].startswith("gemv")],
+              "moe": [t for t in tags if t["tag"].startswith("moe")]}
+    labels = []
+    for t in groups["gemv"]:
+        labels += [(t, "served"), (t, "load-only twin")]
+    for t in groups["moe"]:
+        labels += [(t, "served"), (t, "load-only twin"), (t, "math-only twin")]
+    with open(out_path, "w") as f:
+        f.write("# Streaming-kernel counters: n=1 GEMV and NVFP4 MoE gate/up with their twins\n\n"
+                "Commands (on one MI355X, from the repository root):\n\n"
+                "```\ncd /tmp && export TMPDIR=/tmp && cd \"$GRAFT_REPO_ROOT\"\n"
+                "rocprofv3 --pmc " + STREAM_COUNTER_SET + " --output-format csv -d gpurun_out/sw -o run -- "
+                "python3 bench.py --stream-counter-workload > gpurun_out/sw_tags.txt\n"
+                "python3 bench.py --stream-summary gpurun_out/sw_tags.txt gpurun_out/sw/run_counter_collection.csv "
+                "profiles/stream_counters.md\n```\n\n"
+                "Wave instructions per weight streamed (x 64 lanes / weights); VALU issue per SIMD = "
+                "SQ_INSTS_VALU x 4 cycles / 1024 SIMDs at 2.4 GHz (the VALU time if nothing else ran); the last "
+                "two columns as shares of SQ_WAVE_CYCLES.\n\n")
+        f.write("| config | arm | kernel | grid | waves | VALU / weight | LDS / weight | SALU / weight | "
+                "VALU issue per SIMD (us) | VALU-active / wave cycles | wait-inst / wave cycles |\n"
+                "|---|---|---|---:|---:|---:|---:|---:|---:|---:|---:|\n")
+        for (t, arm), key in zip(labels, order):
+            c = {k: statistics.mean(v) for k, v in vals[key].items()}
+            wgt = t["weights"]
+            valu = c.get("SQ_INSTS_VALU", float("nan"))
+            f.write(f"| {t['tag']} | {arm} | `{key[0]}` | {key[1]} | {c.get('SQ_WAVES', 0):.0f} | "
+                    f"{64 * valu / wgt:.2f} | {64 * c.get('SQ_INSTS_LDS', 0) / wgt:.3f} | "
+                    f"{64 * c.get('SQ_INSTS_SALU', 0) / wgt:.3f} | {valu * 4 / 1024 / 2.4e3:.2f} | "
+                    f"{c.get('SQ_ACTIVE_INST_VALU', 0) / c.get('SQ_WAVE_CYCLES', 1):.3f} | "
+                    f"{c.get('SQ_WAIT_INST_ANY', 0) / c.get('SQ_WAVE_CYCLES', 1):.3f} |\n")
+    print(open(out_path).read())
+
+
 def mfma_counter_summary(tags_path, csv_paths, out_path):
     """profiles/mfma_counters_prefill.md from --counter-workload's printed
     tags and the counter_collection.csv of each --pmc run: per GEMM kernel
@@ -742,12 +841,26 @@ def mfma_counter_summary(tags_path, csv_paths, out_path):
                      c.get("SQ_VALU_MFMA_COEXEC_CYCLES", float("nan")) /
                      c.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan"))))
     with open(out_path, "w") as f:
+        f.write("# Matrix-core counters of the prefill GEMM kernels (current sources)\n\n"
+                "Commands (on one MI355X, from the repository root; two counter passes, then the table):\n\n"
+                "```\ncd /tmp && export TMPDIR=/tmp && cd \"$GRAFT_REPO_ROOT\"\n"
+                "rocprofv3 --pmc " + COUNTER_SETS[0] + " --output-format csv -d gpurun_out/cw0 -o run -- "
+                "python3 bench.py --counter-workload > gpurun_out/cw_tags.txt\n"
+                "rocprofv3 --pmc " + COUNTER_SETS[1] + " --output-format csv -d gpurun_out/cw1 -o run -- "
+                "python3 bench.py --counter-workload > gpurun_out/cw_tags1.txt\n"
+                "python3 bench.py --mfma-summary gpurun_out/cw_tags.txt profiles/mfma_counters_prefill.md "
+                "gpurun_out/cw0/run_counter_collection.csv gpurun_out/cw1/run_counter_collection.csv\n```\n\n"
+                "Per GEMM call of each headline configuration (the planned kernel at its grid, mean of 3 "
+                "dispatches): MFMA flops from SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 against 2mkn; matrix cores busy = "
+                "SQ_VALU_MFMA_BUSY_CYCLES / (SQ_BUSY_CYCLES x 32); VALU / MFMA counts the matrix-core "
+                "instructions among the VALU ones (SQ_INSTS_VALU includes them), other VALU / MFMA does not.\n\n")
         f.write("| config | kernel | grid | MFMA flops / 2mkn | matrix cores busy | VALU / MFMA | "
-                "LDS / MFMA | LDS bank conflicts | wait-inst / wave cycles | VALU-active / wave cycles | "
-                "VALU co-issued / MFMA busy |\n|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|\n")
+                "other VALU / MFMA | LDS / MFMA | LDS bank conflicts | wait-inst / wave cycles | "
+                "VALU-active / wave cycles | VALU co-issued / MFMA busy |\n"
+                "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|\n")
         for r in rows:
-            f.write(f"| {r[0]} | `{r[1]}` | {r[2]} | {r[3]:.3f} | {100 * r[4]:.1f}% | {r[5]:.2f} | {r[6]:.2f} | "
-                    f"{r[7]:.0f} | {r[8]:.3f} | {r[9]:.3f} | {r[10]:.3f} |\n")
+            f.write(f"| {r[0]} | `{r[1]}` | {r[2]} | {r[3]:.3f} | {100 * r[4]:.1f}% | {r[5]:.2f} | {r[5] - 1:.2f} | "
+                    f"{r[6]:.2f} | {r[7]:.0f} | {r[8]:.3f} | {r[9]:.3f} | {r[10]:.3f} |\n")
     print(open(out_path).read())
 
 
@@ -934,7 +1047,14 @@ def main():
                     help="only run every headline prefill GEMM three times (for rocprofv3 --pmc runs)")
     ap.add_argument("--mfma-summary", nargs="+", metavar="FILE",
                     help="TAGS OUT_MD CSV...: the MFMA counter table from --counter-workload runs")
+    ap.add_argument("--stream-counter-workload", action="store_true",
+                    help="only run the n=1 GEMV and MoE gate/up kernels and twins (for a rocprofv3 --pmc run)")
+    ap.add_argument("--stream-summary", nargs=3, metavar=("TAGS", "CSV", "OUT_MD"),
+                    help="the streaming counter table from a --stream-counter-workload run")
     args = ap.parse_args()
+    if args.stream_summary:
+        stream_counter_summary(args.stream_summary[0], args.stream_summary[1], args.stream_summary[2])
+        return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], os.path.join(ROOT, "profiles", "traffic.json"))
         return
@@ -963,6 +1083,9 @@ def main():
         return
     if args.counter_workload:
         run_counter_workload()
+        return
+    if args.stream_counter_workload:
+        run_stream_counter_workload()
         return
     if args.copy_probe:
         log("copy probe: 3 x 1 GiB device copies")
