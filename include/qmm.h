@@ -18,9 +18,9 @@
  *    call allocates device memory, synchronizes, or keeps state beyond lazily
  *    cached device properties (compute units, LDS sizes) and the parsed
  *    tuning variables (QMM_GEMV_MAX_N below; QMM_GEMV_WG_PER_CU and
- *    QMM_MOE_WG_PER_CU 1..64, QMM_GEMV_ROWS 1..2, QMM_GEMV_DEPTH 2/4/8 for
- *    the streaming kernels'
- *    launch shape; a malformed value makes the calls that use it return
+ *    QMM_MOE_WG_PER_CU 1..64, QMM_GEMV_ROWS 1..2, QMM_GEMV_DEPTH 2/4/8,
+ *    QMM_MOE_LPR_LOG2 3..6 (log2 of the MoE streams' lanes per row) for the
+ *    streaming kernels' launch shape; a malformed value makes the calls that use it return
  *    QMM_ERR_RANGE; QMM_MFMA_PLAN is read again at every call that plans a
  *    prefill), so the calls can be recorded into a hipGraph.
  *  - Arguments are validated on the host before anything is launched; a
