@@ -28,7 +28,7 @@ __all__ = [
 ]
 
 QTYPES = {"f32": 0, "q4_0": 1, "q8_0": 2, "q4_k": 3, "q6_k": 4, "nvfp4": 5, "nvfp4_v2": 6}
-PATHS = {"auto": 0, "gemv": 1, "mfma": 2}
+PATHS = {"auto": 0, "gemv": 1, "mfma": 2, "gemv_fma": 3, "gemv_matrix": 4}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -178,7 +178,7 @@ def gemm_plan(m: int, k: int, n: int, qtype, path: str = "auto", workspace: bool
     if st != 0:
         raise QmmError(st, "qmm_gemm_plan")
     if out[0] == PATHS["gemv"]:
-        return {"path": "gemv"}
+        return {"path": "gemv", "stream": "matrix" if out[1] else "fma", "tokens_per_pass": out[2]}
     return {"path": "mfma", "x16": out[1], "tile_rows": out[2], "k_groups": out[3], "n_split": out[4],
             "steps_per_split": out[5]}
 
@@ -187,7 +187,7 @@ def plan_kernel_name(plan: dict, qtype) -> str:
     """Kernel symbol (as the profiler names it) of a gemm_plan() result."""
     qt = _qt(qtype)
     if plan["path"] == "gemv":
-        return "gemv_kernel"
+        return "gemv_mfma_kernel" if plan["stream"] == "matrix" else "gemv_kernel"
     if plan["x16"] >= 2:
         return (f"gemm_lds_kernel<{qt}, {plan['tile_rows'] // 4}, {256 if plan['x16'] == 3 else 128}, "
                 f"{plan['k_groups']}, {'true' if plan['x16'] == 4 else 'false'}>")

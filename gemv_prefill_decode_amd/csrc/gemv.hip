@@ -1,6 +1,8 @@
-// Decode path: the f32 GEMV for small n and its load-only twin (the
-// streaming core, units and activation staging are in stream.hpp).
-#include "stream.hpp"
+// Decode path: the f32 GEMV for small n (on f32 FMAs, or for several
+// activation rows on the matrix-core stream) and its load-only twin (the
+// streaming cores, units and activation staging are in stream.hpp and
+// mstream.hpp).
+#include "mstream.hpp"
 
 namespace qmm {
 
@@ -39,6 +41,37 @@ __global__ __launch_bounds__(64 * WPG) void gemv_kernel(float* __restrict__ dst,
         for (int j = 0; j < NT; ++j) xs.xoff[j] = xoff[j];
         gemv_stream<QT, NT, R, D>(g, blockIdx.x * WPG + wave, gridDim.x * WPG, n_rg, xs, store);
     }
+}
+
+// The matrix-core stream: grid x = work groups, y = token groups of 4 * TT
+// rows, staged in LDS in the quad layout (qlds_floats(4 * TT, k, lm) floats,
+// row stride mld).
+template <int QT, int TT, int R, int D, int WPG = 4>
+__global__ __launch_bounds__(64 * WPG) void gemv_mfma_kernel(float* __restrict__ dst,
+                                                             const uint8_t* __restrict__ w,
+                                                             const float* __restrict__ x, int m, int k, int n,
+                                                             int rb, int n_rg, int ldx, int ldd, int mld) {
+    constexpr int NTOK = 4 * TT;
+    const int wave = wave_id();
+    const int tok0 = blockIdx.y * NTOK;
+    const int ntok = min(NTOK, n - tok0);
+    const rsrc_t xr = make_rsrc(x + (int64_t)tok0 * ldx,
+                                ((uint32_t)(ntok - 1) * (uint32_t)ldx + (uint32_t)k) * 4u);
+    uint32_t xoff[NTOK];
+#pragma unroll
+    for (int j = 0; j < NTOK; ++j) xoff[j] = (uint32_t)(j < ntok ? j : 0) * (uint32_t)ldx * 4u;
+    const StreamGeom g{w, m, rb, k, 4};
+    float* out = dst + (int64_t)tok0 * ldd;
+    auto store = [&](int64_t row, int j, float v) {
+        if (row < m && j < ntok) out[(int64_t)j * ldd + row] = v;
+    };
+    float* sx = qmm_dyn_lds;
+    XQuad<TT> xq;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) xq.row[t] = sx + (4 * t + (int)(threadIdx.x & 3)) * mld;
+    xq.zero = sx + NTOK * mld;
+    mfma_stream<QT, TT, R, D>(g, blockIdx.x * WPG + wave, gridDim.x * WPG, n_rg, xq, store,
+                              make_qstage<NTOK, 64 * WPG>(sx, xr, xoff, k, mld));
 }
 
 // ------------------------------------------------------------------ load-only twin
@@ -166,10 +199,51 @@ static void launch_gemv_nt(float* dst, const uint8_t* w, const float* x, int64_t
     });
 }
 
+// The matrix-core stream with token groups of 4 * TT rows; false if they do
+// not fit one work group's LDS.
+template <int QT, int TT>
+static bool launch_gemv_mfma(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k, int64_t n,
+                             int64_t rb, int64_t ldx, int64_t ldd, const GemvTuning& tune, hipStream_t st) {
+    constexpr int R = 2, D = 2;
+    const int lm = MTraits<QT>::LM;
+    const int64_t lds = (int64_t)qlds_floats(4 * TT, (int)k, lm) * 4;
+    if (lds > tune.lds_per_wg) return false;
+    const int mld = qld((int)k, lm);
+    const int64_t n_rg = (m + 4 * R - 1) / (4 * R);
+    const int64_t gy = (n + 4 * TT - 1) / (4 * TT);
+    const GemvTuning lt = lds_limited(tune, lds);
+    if (lt.wg_per_cu <= 2) {
+        // one or two work groups per CU: 8 waves share the staged rows
+        const dim3 grid(stream_grid(n_rg, gy, lt, 8), (unsigned)gy);
+        gemv_mfma_kernel<QT, TT, R, D, 8><<<grid, 512, (size_t)lds, st>>>(
+            dst, w, x, (int)m, (int)k, (int)n, (int)rb, (int)n_rg, (int)ldx, (int)ldd, mld);
+    } else {
+        const dim3 grid(stream_grid(n_rg, gy, lt), (unsigned)gy);
+        gemv_mfma_kernel<QT, TT, R, D><<<grid, 256, (size_t)lds, st>>>(
+            dst, w, x, (int)m, (int)k, (int)n, (int)rb, (int)n_rg, (int)ldx, (int)ldd, mld);
+    }
+    return true;
+}
+
+// Token groups of the matrix-core stream: 8 rows where they fit (half the
+// passes over the weights) and n > 4, else 4 where they fit, else 0.
+int gemv_matrix_tokens(int64_t m, int64_t k, int64_t n, int qt, int kind, const GemvTuning& tune) {
+    (void)m;
+    const bool use = kind == GEMV_MATRIX || (kind == GEMV_AUTO && tune.gemv_mfma_min > 0 && n >= tune.gemv_mfma_min);
+    if (!use) return 0;
+    const int lm = mtraits_lm(qt);
+    if (n > 4 && tune.gemv_mfma_tt >= 2 && (int64_t)qlds_floats(8, (int)k, lm) * 4 <= tune.lds_per_wg) return 8;
+    if ((int64_t)qlds_floats(4, (int)k, lm) * 4 <= tune.lds_per_wg) return 4;
+    return 0;
+}
+
 template <int QT>
 static void launch_gemv_qt(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k,
-                           int64_t n, int64_t rb, int64_t ldx, int64_t ldd, const GemvTuning& tune,
+                           int64_t n, int64_t rb, int64_t ldx, int64_t ldd, int kind, const GemvTuning& tune,
                            hipStream_t st) {
+    const int tok = gemv_matrix_tokens(m, k, n, QT, kind, tune);
+    if (tok == 8 && launch_gemv_mfma<QT, 2>(dst, w, x, m, k, n, rb, ldx, ldd, tune, st)) return;
+    if (tok == 4 && launch_gemv_mfma<QT, 1>(dst, w, x, m, k, n, rb, ldx, ldd, tune, st)) return;
     const bool fits8 = (int64_t)xlds_floats(8, (int)k, GUnit<QT>::RUNS > 0) * 4 <= tune.lds_per_wg;
     const bool fits4 = (int64_t)xlds_floats(4, (int)k, GUnit<QT>::RUNS > 0) * 4 <= tune.lds_per_wg;
     if (n == 1) launch_gemv_nt<QT, 1>(dst, w, x, m, k, n, rb, ldx, ldd, tune, st);
@@ -180,9 +254,9 @@ static void launch_gemv_qt(float* dst, const uint8_t* w, const float* x, int64_t
 }
 
 void launch_gemv(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
-                 int qt, int64_t rb, int64_t ldx, int64_t ldd, const GemvTuning& tune, hipStream_t st) {
+                 int qt, int64_t rb, int64_t ldx, int64_t ldd, int kind, const GemvTuning& tune, hipStream_t st) {
     const uint8_t* wb = (const uint8_t*)w;
-    QMM_QT_SWITCH(qt, (launch_gemv_qt<Q>(dst, wb, x, m, k, n, rb, ldx, ldd, tune, st)))
+    QMM_QT_SWITCH(qt, (launch_gemv_qt<Q>(dst, wb, x, m, k, n, rb, ldx, ldd, kind, tune, st)))
 }
 
 template <int QT>

@@ -21,14 +21,26 @@ struct GemvTuning {
     int rows;       // rows per lane group (1 or 2)
     int depth;      // items of weight loads kept in flight per wave (2, 4 or 8)
     int moe_lpr_cap;  // log2 of the largest lane group per row in the MoE streams
+    int moe_mfma_min; // MoE chunks of at least this many pairs use the matrix-core stream (0: never)
+    int gemv_mfma_min; // GEMV calls with at least this many activation rows use it (0: never)
+    int gemv_mfma_tt;  // its token groups: 4 * gemv_mfma_tt rows at most (1 or 2)
     int lds_per_wg; // bytes of LDS one work group may allocate
     int lds_per_cu; // bytes of LDS per CU (limits resident work groups)
 };
 
 // x rows are ldx floats apart (ldx >= k, a multiple of 4), dst rows ldd
 // floats apart (ldd >= m); ldx = k and ldd = m for contiguous tensors.
+// The GEMV's two streams: f32 products on FMAs, or on the matrix cores
+// (v_mfma_f32_4x4x1f32); GEMV_AUTO takes the matrix cores for n >=
+// tune.gemv_mfma_min.  Both stage the activations in LDS where they fit; the
+// matrix-core stream needs 4 rows of them in one work group's LDS and falls
+// back to the FMA stream otherwise.
+enum : int { GEMV_AUTO = 0, GEMV_FMA = 1, GEMV_MATRIX = 2 };
 void launch_gemv(float* dst, const void* w, const float* x, int64_t m, int64_t k, int64_t n,
-                 int qt, int64_t rb, int64_t ldx, int64_t ldd, const GemvTuning& tune, hipStream_t st);
+                 int qt, int64_t rb, int64_t ldx, int64_t ldd, int kind, const GemvTuning& tune, hipStream_t st);
+// Activation rows per token group of the matrix-core stream for this call
+// (4 or 8), or 0 if the FMA stream runs it.
+int gemv_matrix_tokens(int64_t m, int64_t k, int64_t n, int qt, int kind, const GemvTuning& tune);
 
 // Launch plan of the prefill (MFMA) kernels.  x16 = 0: gemm_mfma.hip's
 // kernel (128 x 128 tiles, f32 activations converted in the k loop).

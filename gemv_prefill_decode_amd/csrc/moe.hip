@@ -1,7 +1,7 @@
 // MoE projections on the streaming core (stream.hpp): the gate/up rows with
 // per-expert de-duplication, on f32 or Q8_1 activations; the down
 // projection and its slot sum; the Q8_1 quantization; the NVFP4 V2 repack.
-#include "stream.hpp"
+#include "mstream.hpp"
 
 namespace qmm {
 
@@ -20,7 +20,8 @@ namespace qmm {
 // pair q is its token's row q / n_used (gate/up) or its own row q
 // (act_pair: the down projection, whose input is the pair's SwiGLU output).
 constexpr int MOE_CHUNK = 256;  // pairs examined (and gathered) per pass
-constexpr int MOE_NT = 3;       // token rows staged in LDS at a time
+constexpr int MOE_NT = 3;       // token rows staged in LDS at a time (FMA stream)
+constexpr int MOE_MT = 4;       // token rows of a matrix-core chunk
 constexpr unsigned MOE_MIN_WG = 32;  // work groups per (pair, plane) at least
 
 // Kernel modes: the projections per plane; the gate and up projections of
@@ -43,6 +44,9 @@ struct MoeArgs {
     int act_pair;           // activation row of pair q is row q (else q / n_used)
     float limit;            // the SwiGLU clamp (MOE_ACT)
     int gbuf_off;           // floats of dynamic LDS before the gate buffer (MOE_ACT)
+    int mt_min;             // chunks of at least mt_min pairs run on the matrix-core stream (0: none)
+    int mld;                // row stride of the matrix-core chunk's staged activations
+    int n_rg_m;             // row groups of the matrix-core stream
 };
 
 // The activation between gate/up and down: the gate clamped above at L, the
@@ -164,6 +168,54 @@ __device__ __forceinline__ void moe_chunk(const MoeArgs& a, int e, const int* pl
     }
 }
 
+// A chunk of up to MOE_MT pairs on the matrix-core stream (f32 activations
+// staged in LDS in the quad layout); modes as moe_chunk.
+template <int QT, int R, int D, int MODE>
+__device__ __forceinline__ void moe_mchunk(const MoeArgs& a, int e, const int* plist, const int* tlist, int c0,
+                                           int cnt) {
+    constexpr int NT = MOE_MT;
+    const int wave = wave_id();
+    const int plane = MODE == MOE_ACT ? 0 : (int)blockIdx.z;
+    const Chunk<NT> ck(a, plist, tlist, c0, cnt, plane, MODE == MOE_ACT);
+    const int64_t n_ff = a.n_ff;
+    const int RG = 4 * R;
+    const StreamGeom g0{(plane == 0 ? a.w0 : a.w1) + (int64_t)e * n_ff * a.rb, n_ff, a.rb, a.in_f, 4};
+    float* out = plane == 0 ? a.out0 : a.out1;
+    constexpr int ARM = MODE == MOE_LOADONLY ? STREAM_LOADONLY : (MODE == MOE_MATHONLY ? STREAM_MATHONLY : STREAM_SERVED);
+    auto store = [&](int64_t row, int j, float v) {
+        if (row < n_ff && ck.pj[j] >= 0) out[(int64_t)ck.pj[j] * n_ff + row] = ck.f0[j] * v;
+    };
+    float* gbuf = qmm_dyn_lds + a.gbuf_off;
+    auto store_gate = [&](int64_t row, int j, float v) {
+        if (row < n_ff && ck.pj[j] >= 0) gbuf[gate_slot(row, j, RG, NT)] = ck.f0[j] * v;
+    };
+    auto store_act = [&](int64_t row, int j, float v) {
+        if (row < n_ff && ck.pj[j] >= 0)
+            a.out0[(int64_t)ck.pj[j] * n_ff + row] =
+                swiglu_clamp(gbuf[gate_slot(row, j, RG, NT)], ck.f1[j] * v, a.limit);
+    };
+    const int n_rows = a.act_pair ? a.t * a.n_used : a.t;  // activation rows
+    const rsrc_t xr = make_rsrc(a.x, (uint32_t)n_rows * (uint32_t)a.in_f * 4u);
+    uint32_t xoff[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) xoff[j] = ck.row[j] * (uint32_t)a.in_f * 4u;
+    __syncthreads();  // the previous chunk's waves are done with the staged rows
+    float* sx = qmm_dyn_lds;
+    XQuad<1> xq;
+    xq.row[0] = sx + (threadIdx.x & 3) * a.mld;
+    xq.zero = sx + NT * a.mld;
+    const auto st = make_qstage<NT>(sx, xr, xoff, a.in_f, a.mld);
+    const int first = blockIdx.x * 4 + wave, stride = gridDim.x * 4;
+    if constexpr (MODE == MOE_ACT) {
+        const StreamGeom g1{a.w1 + (int64_t)e * n_ff * a.rb, n_ff, a.rb, a.in_f, 4};
+        mfma_stream<QT, 1, R, D>(g0, first, stride, a.n_rg_m, xq, store_gate, st);
+        mfma_stream<QT, 1, R, D>(g1, first, stride, a.n_rg_m, xq, store_act);
+    } else {
+        mfma_stream<QT, 1, R, D, decltype(store), std::decay_t<decltype(st)>, ARM>(g0, first, stride, a.n_rg_m, xq,
+                                                                                  store, st);
+    }
+}
+
 template <int QT, int R, int D, bool Q8, int MODE>
 __global__ __launch_bounds__(256) void moe_kernel(MoeArgs a) {
     __shared__ int plist[MOE_CHUNK];
@@ -217,8 +269,15 @@ __global__ __launch_bounds__(256) void moe_kernel(MoeArgs a) {
         }
         const int cnt = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
         __syncthreads();
-        for (int c0 = 0; c0 < cnt; c0 += MOE_NT) {
+        for (int c0 = 0; c0 < cnt;) {
             const int left = cnt - c0;
+            if constexpr (!Q8) {
+                if (a.mt_min > 0 && left >= a.mt_min) {
+                    moe_mchunk<QT, R, D, MODE>(a, e, plist, tlist, c0, cnt);
+                    c0 += MOE_MT;
+                    continue;
+                }
+            }
             if (Q8 || a.xl) {
                 if (left == 1)
                     moe_chunk<QT, 1, R, D, true, Q8, MODE>(a, e, plist, tlist, c0, cnt);
@@ -229,6 +288,7 @@ __global__ __launch_bounds__(256) void moe_kernel(MoeArgs a) {
             } else if constexpr (!Q8) {  // Q8_1 activations are always staged
                 moe_chunk<QT, MOE_NT, R, 2, false, Q8, MODE>(a, e, plist, tlist, c0, cnt);
             }
+            c0 += MOE_NT;
         }
     }
 }
@@ -238,6 +298,9 @@ __global__ __launch_bounds__(256) void moe_kernel(MoeArgs a) {
 // Largest dynamic LDS one MoE work group takes: the staged activations (at
 // most XLDS_MAX_BYTES) plus, in MOE_ACT, the gate buffer.
 constexpr int64_t MOE_LDS_MAX = 96 * 1024;
+// Largest staged activations of a matrix-core chunk (four rows of up to
+// about 4.4K activations: two work groups per CU).
+constexpr int64_t MOE_MT_LDS_MAX = 76 * 1024;
 
 // The MoE kernels run two rows per lane group and two items in flight per
 // wave (the streaming defaults measured best on MI355X); QMM_GEMV_ROWS and
@@ -263,6 +326,17 @@ static void launch_moe_mode(MoeArgs a, int planes, const GemvTuning& tune, hipSt
                             : (int64_t)xlds_floats(MOE_NT, a.in_f, GUnit<QT>::RUNS > 0) * 4;
         a.xl = Q8 || xbytes <= XLDS_MAX_BYTES;
         if (!a.xl) xbytes = 0;
+        // chunks of several pairs on the matrix-core stream: with more than
+        // one activation row (one token's pairs go to distinct experts), f32
+        // activations, and MOE_MT staged rows within the LDS limit
+        const int lm = mtraits_lm(QT);
+        const int64_t mbytes = (int64_t)qlds_floats(MOE_MT, a.in_f, lm) * 4;
+        const int64_t RGM = 4 * R;
+        const int64_t n_rg_m = (a.n_ff + RGM - 1) / RGM;
+        a.mt_min = !Q8 && a.t > 1 && mbytes <= MOE_MT_LDS_MAX ? tune.moe_mfma_min : 0;
+        a.mld = qld(a.in_f, lm);
+        a.n_rg_m = (int)n_rg_m;
+        if (a.mt_min > 0 && mbytes > xbytes) xbytes = mbytes;
         int64_t lds = xbytes;
         a.gbuf_off = 0;
         if constexpr (MODE == MOE_ACT) {
@@ -270,7 +344,11 @@ static void launch_moe_mode(MoeArgs a, int planes, const GemvTuning& tune, hipSt
             // group the work group streams, per row and token slot; more work
             // groups (fewer row groups each) until it fits
             a.gbuf_off = (int)((xbytes + 15) / 16 * 4);
-            auto gbytes = [&](unsigned w) { return (n_rg + 4 * (int64_t)w - 1) / (4 * (int64_t)w) * 4 * RG * MOE_NT * 4; };
+            auto gbytes = [&](unsigned w) {
+                const int64_t fma = (n_rg + 4 * (int64_t)w - 1) / (4 * (int64_t)w) * 4 * RG * MOE_NT * 4;
+                const int64_t mat = a.mt_min > 0 ? (n_rg_m + 4 * (int64_t)w - 1) / (4 * (int64_t)w) * 4 * RGM * MOE_MT * 4 : 0;
+                return fma > mat ? fma : mat;
+            };
             while (gx < need && 4 * (int64_t)a.gbuf_off + gbytes(gx) > MOE_LDS_MAX) gx = gx * 2 < need ? gx * 2 : need;
             lds = 4 * (int64_t)a.gbuf_off + gbytes(gx);
         }

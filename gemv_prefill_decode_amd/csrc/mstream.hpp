@@ -1,0 +1,351 @@
+// The matrix-core variant of the streaming core, for streams that apply each
+// weight to several activation rows (the GEMV at n > 2, the MoE experts with
+// several tokens).  The weights stream and decode exactly as in stream.hpp
+// (the same units, loads and decoders); the products with the activations
+// run on v_mfma_f32_4x4x1f32 instead of f32 FMAs, in f32 throughout: every
+// product w*x is formed and summed in f32, as the FMA stream does.
+//
+// v_mfma_f32_4x4x1f32 computes 16 independent 4x4 outer products: lane
+// 4b + i supplies A[i] of block b, lane 4b + j supplies B[j], and lane 4b + j
+// holds D[i][j] of block b in its accumulator register i.  Here A is four
+// activation rows (tokens) and B four weight rows at one k: the lanes of a
+// quad (the four lanes 4b..4b+3) decode the same unit position of four rows,
+// each lane its own row, and supply the same k of four tokens, each lane its
+// own token.  A lane's register i then accumulates its own row against token
+// i, so per-row scale factors are the lane's own.  The 16 quads take 16
+// units of their rows at a time (a row has 16 lanes, like a lane group of 16
+// in the FMA stream), and the quads' sums are added by a butterfly at the
+// end of each row group.
+//
+// Rounding chains.  Each unit's products accumulate in fresh registers (a
+// run of one scale factor, at most 64 terms, or the whole unit) before
+// joining the lane's running sum, so every f32 chain has at most
+// 64 + k/(16*UE) + 4 terms, the bound the FMA stream keeps.
+#pragma once
+#include "stream.hpp"
+
+namespace qmm {
+
+// ------------------------------------------------------------------ activations
+// Token-major rows with 4 floats of padding after every 32 and a row stride
+// of lm (mod 32) floats: the 8 lanes of an LDS phase (two quads: four tokens
+// at two neighbouring units) then read distinct 16-byte bank groups, with
+// lm = 8 for formats whose neighbouring units are 32 weights apart and
+// lm = 4 for those 16 apart.  A block of QZERO zero floats follows the rows:
+// quads whose unit lies past the row's end read it.
+__host__ __device__ constexpr int qpad(int e) { return e + ((e >> 5) << 2); }
+__host__ __device__ constexpr int qld(int k, int lm) {
+    const int b = qpad((k + 31) & ~31);
+    return b + ((lm - b % 32) % 32 + 32) % 32;
+}
+constexpr int QZERO = 128;
+// LDS floats of nt staged rows and the zero block.
+__host__ __device__ constexpr int qlds_floats(int nt, int k, int lm) { return nt * qld(k, lm) + QZERO; }
+
+// Offset of k = e + rel from k = e in the padded layout.  Every unit starts
+// at e with e % 32 + rel % 32 + 4 <= 32 for the offsets it reads, so the
+// padding crossed depends on rel alone (qrel_ok checks it for each format at
+// compile time over the residues e % 32 its units start at).
+__host__ __device__ constexpr int qrel(int rel) { return rel + 4 * (rel >> 5); }
+
+// Per format: LM (the row stride residue above), CH (chains per sub-unit: 2
+// when its two halves carry different scale factors), EM1 (the second residue
+// e % 32 that units start at, besides 0), flush(s) (whether a run of one
+// scale factor, or the unit, ends with sub-unit s).
+template <int QT> struct MTraits;
+template <> struct MTraits<QT_F32> { static constexpr int LM = 4, CH = 1, EM1 = 16; static constexpr bool flush(int s) { return s == 1; } };
+template <> struct MTraits<QT_Q4_0> { static constexpr int LM = 8, CH = 1, EM1 = 0; static constexpr bool flush(int s) { return s == 3; } };
+template <> struct MTraits<QT_Q8_0> { static constexpr int LM = 8, CH = 1, EM1 = 0; static constexpr bool flush(int s) { return s == 3; } };
+template <> struct MTraits<QT_Q4_K> { static constexpr int LM = 4, CH = 1, EM1 = 16; static constexpr bool flush(int s) { return s == 3; } };
+// Q6_K: a scale factor per quarter (sub-units 2g, 2g + 1)
+template <> struct MTraits<QT_Q6_K> { static constexpr int LM = 4, CH = 1, EM1 = 16; static constexpr bool flush(int s) { return (s & 1) == 1; } };
+// NVFP4: the two halves of a sub-unit belong to the unit's two scale groups
+template <> struct MTraits<QT_NVFP4> { static constexpr int LM = 8, CH = 2, EM1 = 0; static constexpr bool flush(int s) { return s == 3; } };
+template <> struct MTraits<QT_NVFP4_V2> { static constexpr int LM = 8, CH = 2, EM1 = 0; static constexpr bool flush(int s) { return s == 3; } };
+
+// The four activations at e + rel .. e + rel + 3 are contiguous at
+// qpad(e) + qrel(rel) for every sub-unit offset and unit start residue.
+template <int QT>
+constexpr bool qrel_ok() {
+    using UT = GUnit<QT>;
+    for (int i = 0; i < 2; ++i) {
+        const int e = i == 0 ? 0 : MTraits<QT>::EM1;
+        for (int s = 0; s < UT::S; ++s)
+            for (int h = 0; h < 2; ++h) {
+                const int rel = h == 0 ? UT::rel0(s) : UT::rel1(s);
+                for (int q = 0; q < 4; ++q)
+                    if (qpad(e + rel + q) - qpad(e) != qrel(rel) + q) return false;
+            }
+    }
+    return true;
+}
+static_assert(qrel_ok<QT_F32>() && qrel_ok<QT_Q4_0>() && qrel_ok<QT_Q8_0>() && qrel_ok<QT_Q4_K>() &&
+                  qrel_ok<QT_Q6_K>() && qrel_ok<QT_NVFP4>() && qrel_ok<QT_NVFP4_V2>(),
+              "a unit's activations cross the quad layout's padding");
+
+inline int mtraits_lm(int qt) {
+    switch (qt) {
+        case QT_F32: return MTraits<QT_F32>::LM;
+        case QT_Q4_0: return MTraits<QT_Q4_0>::LM;
+        case QT_Q8_0: return MTraits<QT_Q8_0>::LM;
+        case QT_Q4_K: return MTraits<QT_Q4_K>::LM;
+        case QT_Q6_K: return MTraits<QT_Q6_K>::LM;
+        case QT_NVFP4: return MTraits<QT_NVFP4>::LM;
+        case QT_NVFP4_V2: return MTraits<QT_NVFP4_V2>::LM;
+    }
+    return 8;
+}
+
+// Activation rows of TT tiles of four tokens in the quad layout: row[t] is
+// this lane's token row in tile t (token lane & 3 of the tile), zero the
+// zero block.
+template <int TT>
+struct XQuad {
+    const float* row[TT];
+    const float* zero;
+};
+
+// Stage rows xoff[j] (j < NTOK) of x into LDS in the quad layout (two-phase,
+// as XStage), then clear the zero block.
+template <int NTOK, int TPB = 256>
+struct QStage {
+    static constexpr int U = NTOK >= 8 ? 1 : 8 / NTOK;  // float4 columns per thread per batch
+    float* sx;
+    rsrc_t xr;
+    uint32_t xoff[NTOK];
+    int k, ld;
+    f32x4 v[NTOK][U];
+
+    __device__ __forceinline__ void load(int c0) {
+        const int per = k >> 2;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + TPB * u;
+#pragma unroll
+            for (int j = 0; j < NTOK; ++j)
+                v[j][u] = __builtin_bit_cast(f32x4, ld128(xr, c < per ? xoff[j] + 16u * (uint32_t)c : OOB_OFF));
+        }
+    }
+    __device__ __forceinline__ void store(int c0) {
+        const int per = k >> 2;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + TPB * u;
+            if (c < per)
+#pragma unroll
+                for (int j = 0; j < NTOK; ++j) *(f32x4*)(sx + j * ld + qpad(4 * c)) = v[j][u];
+        }
+    }
+    __device__ __forceinline__ void issue() { load((int)threadIdx.x); }
+    __device__ __forceinline__ void finish() {
+        store((int)threadIdx.x);
+        for (int c0 = (int)threadIdx.x + TPB * U; c0 < (k >> 2); c0 += TPB * U) {
+            load(c0);
+            store(c0);
+        }
+        for (int i = (int)threadIdx.x; i < QZERO; i += TPB) sx[NTOK * ld + i] = 0.0f;
+        __syncthreads();
+    }
+};
+
+template <int NTOK, int TPB = 256>
+__device__ __forceinline__ QStage<NTOK, TPB> make_qstage(float* sx, rsrc_t xr, const uint32_t (&xoff)[NTOK], int k,
+                                                         int ld) {
+    QStage<NTOK, TPB> st;
+    st.sx = sx;
+    st.xr = xr;
+#pragma unroll
+    for (int j = 0; j < NTOK; ++j) st.xoff[j] = xoff[j];
+    st.k = k;
+    st.ld = ld;
+    return st;
+}
+
+// ------------------------------------------------------------------ core
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
+}
+
+// Sub-unit S_ of every row rr and tile t: 8 products per lane into chain(s)
+// P; at the format's flush points the chains join acc (times the run's scale
+// factor for the SCALED formats).
+template <int QT, int TT, int R, int S_>
+__device__ __forceinline__ void msub(const GUnit<QT> (&un)[R], const float* const (&xp)[TT], int k, int e,
+                                     f32x4 (&P)[R][TT][MTraits<QT>::CH], f32x4 (&acc)[R][TT]) {
+    using UT = GUnit<QT>;
+    using MT = MTraits<QT>;
+    float w[R][8], f0[R], f1[R];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) un[rr].sub(S_, w[rr], f0[rr], f1[rr]);
+    f32x4 xa[TT], xb[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        xa[t] = *(const f32x4*)(xp[t] + qrel(UT::rel0(S_)));
+        xb[t] = *(const f32x4*)(xp[t] + qrel(UT::rel1(S_)));
+        if constexpr (QT == QT_F32) {  // runs past k belong to the next row
+            if (e + UT::rel0(S_) >= k) xa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (e + UT::rel1(S_) >= k) xb[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    // independent chains interleaved (rows, tiles and, with two chains, the
+    // halves), so that no product waits for the one before it
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) {
+                P[rr][t][0] = mfma4(xa[t][q], w[rr][q], P[rr][t][0]);
+                if constexpr (MT::CH == 2) P[rr][t][1] = mfma4(xb[t][q], w[rr][4 + q], P[rr][t][1]);
+            }
+    if constexpr (MT::CH == 1)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+#pragma unroll
+                for (int rr = 0; rr < R; ++rr) P[rr][t][0] = mfma4(xb[t][q], w[rr][4 + q], P[rr][t][0]);
+    if constexpr (MT::flush(S_)) {
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+#pragma unroll
+                for (int c = 0; c < MT::CH; ++c) {
+                    const float f = c == 0 ? f0[rr] : f1[rr];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if constexpr (UT::SCALED) acc[rr][t][i] = __builtin_fmaf(f, P[rr][t][c][i], acc[rr][t][i]);
+                        else acc[rr][t][i] += P[rr][t][c][i];
+                    }
+                    P[rr][t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+    }
+}
+
+template <int QT, int TT, int R, int S_ = 0>
+__device__ __forceinline__ void msub_all(const GUnit<QT> (&un)[R], const float* const (&xp)[TT], int k, int e,
+                                         f32x4 (&P)[R][TT][MTraits<QT>::CH], f32x4 (&acc)[R][TT]) {
+    if constexpr (S_ < GUnit<QT>::S) {
+        msub<QT, TT, R, S_>(un, xp, k, e, P, acc);
+        msub_all<QT, TT, R, S_ + 1>(un, xp, k, e, P, acc);
+    }
+}
+
+// One item: the unit at k = e of the lane's R rows against the lane's token
+// in each tile; valid = false (the quad's unit lies past the row's end; its
+// weights were loaded as zeros) reads the zero block instead.
+template <int QT, int TT, int R>
+__device__ __forceinline__ void mcompute_item(GUnit<QT> (&un)[R], const typename GUnit<QT>::Lane& ln, int e,
+                                              bool valid, int k, const XQuad<TT>& xq, f32x4 (&acc)[R][TT]) {
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) un[rr].prep(ln);
+    const float* xp[TT];
+    const int pe = qpad(e);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) xp[t] = valid ? xq.row[t] + pe : xq.zero;
+    f32x4 P[R][TT][MTraits<QT>::CH];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int c = 0; c < MTraits<QT>::CH; ++c) P[rr][t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    msub_all<QT, TT, R>(un, xp, k, e, P, acc);
+}
+
+// Row groups of 4R rows (lane l takes rows (l & 3) * R + rr of the group, and
+// units (l >> 2) + 16 uu of them); items numbered as in gemv_stream, a ring
+// of D items of loads in flight, pre.issue()/pre.finish() around the first
+// loads.  store(row, j, value) is called by lanes 0..3 for token j = 4t + i
+// of every row (rows >= m too).  The quad whose unit lies past the row's end
+// loads nothing (zeros) and reads the zero block, so it adds exact zeros.
+// ARM: the measurement twins as in gemv_stream (load-only: the raw words
+// XORed into acc[rr][0][0]; math-only: the first item's unit for every item).
+template <int QT, int TT, int R, int D, typename Store, typename Pre = NoPre, int ARM = STREAM_SERVED>
+__device__ __forceinline__ void mfma_stream(const StreamGeom& g, int first_rg, int rg_stride, int n_rg,
+                                            const XQuad<TT>& xq, Store store, Pre pre = {}) {
+    using UT = GUnit<QT>;
+    constexpr int LPR = 16;
+    const int lane = threadIdx.x & 63;
+    const int gl = lane >> 2, slot = lane & 3;
+    const int RG = 4 * R;
+    const int U = (g.k + UT::UE - 1) / UT::UE;
+    const int upl = (U + LPR - 1) / LPR;
+    const int n_items = first_rg < n_rg ? (n_rg - first_rg + rg_stride - 1) / rg_stride * upl : 0;
+    const typename UT::Lane ln = UT::lane(gl);
+    const uint32_t lane_row_off = (uint32_t)(slot * R) * (uint32_t)g.rb;
+    const int e_step = LPR * UT::UE;
+    const StreamGeom g16{g.w, g.m, g.rb, g.k, 4};  // the unit step of 16-lane groups
+
+    f32x4 acc[R][TT];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) acc[rr][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto finish = [&](int q) {
+#pragma unroll
+        for (int off = 4; off < 64; off <<= 1)
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                for (int t = 0; t < TT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[rr][t][i] += __shfl_xor(acc[rr][t][i], off, 64);
+        if (lane < 4) {
+            const int64_t r0 = (int64_t)(first_rg + q * rg_stride) * RG + slot * R;
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                for (int t = 0; t < TT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) store(r0 + rr, 4 * t + i, acc[rr][t][i]);
+        }
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int t = 0; t < TT; ++t) acc[rr][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    // loads of item (q, uu): a quad whose unit is past the row's end loads zeros
+    auto issue = [&](UT (&slot_un)[R], int q, int uu, bool live) {
+        issue_item<QT, R>(slot_un, g16, RG, lane_row_off, ln, first_rg + q * rg_stride, uu,
+                          ln.e + uu * e_step, live, gl + LPR * uu < U);
+    };
+
+    UT ring[D][R];
+    pre.issue();
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        const int q = d / upl, uu = d - q * upl;
+        issue(ring[d], q, uu, d < n_items);
+    }
+    pre.finish();
+    ItemPos cur{0, 0}, nxt{D / upl, D - (D / upl) * upl};
+    for (int base = 0; base < n_items; base += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int it = base + d;
+            const bool live = it < n_items;  // wave-uniform
+            const int q = cur.q, uu = cur.uu;
+            if (live) {
+                if constexpr (ARM == STREAM_LOADONLY) {
+#pragma unroll
+                    for (int rr = 0; rr < R; ++rr)
+                        acc[rr][0][0] = __builtin_bit_cast(
+                            float, __builtin_bit_cast(uint32_t, acc[rr][0][0]) ^ raw_xor(ring[d][rr]));
+                } else {
+                    mcompute_item<QT, TT, R>(ring[d], ln, ln.e + uu * e_step, gl + LPR * uu < U, g.k, xq, acc);
+                }
+            }
+            if constexpr (ARM == STREAM_MATHONLY) issue(ring[d], 0, 0, it + D < n_items);
+            else issue(ring[d], nxt.q, nxt.uu, it + D < n_items);
+            if (live && uu == upl - 1) finish(q);
+            cur.next(upl);
+            nxt.next(upl);
+        }
+    }
+}
+
+}  // namespace qmm

@@ -93,6 +93,9 @@ struct TuneState {
     int rows = 2;
     int depth = 2;
     int moe_lpr_cap = qmm::LPR_CAP_MULTI;
+    int moe_mfma_min = 2;
+    int gemv_mfma_min = 3;
+    int gemv_mfma_tt = 2;
     bool bad = false;
 };
 TuneState g_tune;
@@ -111,7 +114,10 @@ void parse_tune() {
     const int r = env_int("QMM_GEMV_ROWS", g_tune.rows, 1, 2);
     const int d = env_int("QMM_GEMV_DEPTH", g_tune.depth, 2, 8);
     const int ml = env_int("QMM_MOE_LPR_LOG2", g_tune.moe_lpr_cap, qmm::LPR_CAP_MIN, 6);
-    if (w < 0 || mw < 0 || r < 0 || d < 0 || ml < 0 || (d & (d - 1)) != 0) {
+    const int mm = env_int("QMM_MOE_MFMA_MIN", g_tune.moe_mfma_min, 0, 4);
+    const int gm = env_int("QMM_GEMV_MFMA_MIN", g_tune.gemv_mfma_min, 0, 64);
+    const int gt = env_int("QMM_GEMV_MFMA_TT", g_tune.gemv_mfma_tt, 1, 2);
+    if (w < 0 || mw < 0 || r < 0 || d < 0 || ml < 0 || mm < 0 || gm < 0 || gt < 0 || (d & (d - 1)) != 0) {
         g_tune.bad = true;
         return;
     }
@@ -120,6 +126,9 @@ void parse_tune() {
     g_tune.rows = r;
     g_tune.depth = d;
     g_tune.moe_lpr_cap = ml;
+    g_tune.moe_mfma_min = mm;
+    g_tune.gemv_mfma_min = gm;
+    g_tune.gemv_mfma_tt = gt;
 }
 
 // QMM_MFMA_PLAN="x16,wm,n_split[,kg]" forces the prefill plan of calls with
@@ -182,6 +191,9 @@ bool gemv_tuning(qmm::GemvTuning* t) {
     t->rows = g_tune.rows;
     t->depth = g_tune.depth;
     t->moe_lpr_cap = g_tune.moe_lpr_cap;
+    t->moe_mfma_min = g_tune.moe_mfma_min;
+    t->gemv_mfma_min = g_tune.gemv_mfma_min;
+    t->gemv_mfma_tt = g_tune.gemv_mfma_tt;
     return true;
 }
 
@@ -243,7 +255,7 @@ int check_gemm(float* dst, const void* w, const float* x, int64_t m, int64_t k, 
         *path = auto_path(n);
         if (*path < 0) return QMM_ERR_RANGE;
     }
-    if (*path == QMM_PATH_GEMV) {
+    if (*path == QMM_PATH_GEMV || *path == QMM_PATH_GEMV_FMA || *path == QMM_PATH_GEMV_MATRIX) {
         // one work group addresses at most this window of w, and 8 token rows of x
         if (qmm::gemv_max_window_bytes(qtype, k, *rb) >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
         if ((7 * ldx + k) * 4 >= ((int64_t)1 << 31)) return QMM_ERR_RANGE;
@@ -268,8 +280,9 @@ int gemm_impl(float* dst, int64_t ldd, const void* w, const float* x, int64_t ld
     if (st) return st;
     qmm::GemvTuning tune;
     if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
-    if (path == QMM_PATH_GEMV) {
-        qmm::launch_gemv(dst, w, x, m, k, n, qtype, rb, ldx, ldd, tune, stream);
+    if (path == QMM_PATH_GEMV || path == QMM_PATH_GEMV_FMA || path == QMM_PATH_GEMV_MATRIX) {
+        const int kind = path == QMM_PATH_GEMV_FMA ? qmm::GEMV_FMA : (path == QMM_PATH_GEMV_MATRIX ? qmm::GEMV_MATRIX : qmm::GEMV_AUTO);
+        qmm::launch_gemv(dst, w, x, m, k, n, qtype, rb, ldx, ldd, kind, tune, stream);
         return launch_status();
     }
     const MfmaForceState g_force = parse_force();
@@ -338,7 +351,7 @@ int64_t qmm_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int qtype, int
         path = auto_path(n);
         if (path < 0) return -QMM_ERR_RANGE;
     }
-    if (path == QMM_PATH_GEMV) return 0;
+    if (path == QMM_PATH_GEMV || path == QMM_PATH_GEMV_FMA || path == QMM_PATH_GEMV_MATRIX) return 0;
     if (path != QMM_PATH_MFMA) return -QMM_ERR_PATH;
     if (qtype == QMM_NVFP4_V2) return -QMM_ERR_QTYPE;  // streaming paths only
     qmm::GemvTuning tune;
@@ -357,9 +370,15 @@ int qmm_gemm_plan(int64_t m, int64_t k, int64_t n, int qtype, int path, int with
         path = auto_path(n);
         if (path < 0) return QMM_ERR_RANGE;
     }
-    if (path == QMM_PATH_GEMV) {
+    if (path == QMM_PATH_GEMV || path == QMM_PATH_GEMV_FMA || path == QMM_PATH_GEMV_MATRIX) {
+        qmm::GemvTuning tune;
+        if (!gemv_tuning(&tune)) return QMM_ERR_RANGE;
+        const int kind = path == QMM_PATH_GEMV_FMA ? qmm::GEMV_FMA : (path == QMM_PATH_GEMV_MATRIX ? qmm::GEMV_MATRIX : qmm::GEMV_AUTO);
+        const int tok = qmm::gemv_matrix_tokens(m, k, n, qtype, kind, tune);
         out[0] = QMM_PATH_GEMV;
-        out[1] = out[2] = out[3] = out[4] = out[5] = 0;
+        out[1] = tok > 0 ? 1 : 0;
+        out[2] = tok;
+        out[3] = out[4] = out[5] = 0;
         return QMM_OK;
     }
     if (path != QMM_PATH_MFMA) return QMM_ERR_PATH;

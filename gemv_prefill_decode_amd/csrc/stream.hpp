@@ -918,19 +918,21 @@ __device__ __forceinline__ void compute_item(GUnit<QT> (&un)[R], const typename 
 // The descriptor covers the row group's rows from the 16-byte boundary at or
 // below its first byte (wave-uniform, scalar registers); a lane's offset is
 // its per-lane row/unit constant plus the group's sub-16 remainder and uu
-// times the format's step.
+// times the format's step.  lane_ok = false sends this lane's loads past
+// the descriptor's end (zeros) while the descriptor stays wave-uniform.
 template <int QT, int R>
 __device__ __forceinline__ void issue_item(GUnit<QT> (&un)[R], const StreamGeom& g, int RG,
                                            uint32_t lane_row_off, const typename GUnit<QT>::Lane& ln,
-                                           int rg, int uu, int e, bool live) {
+                                           int rg, int uu, int e, bool live, bool lane_ok = true) {
     const int64_t row0 = (int64_t)rg * RG;
     const int64_t byte0 = row0 * g.rb;
     // an item past the end gets an empty descriptor: its loads return zeros
     const int64_t base = live ? byte0 & ~(int64_t)15 : 0;
     const int64_t end = live ? imin64(g.m, row0 + RG) * g.rb : 0;
     const rsrc_t wr = make_rsrc(g.w + base, (uint32_t)((end - base + 15) & ~(int64_t)15));
-    const uint32_t off0 = lane_row_off + (uint32_t)(byte0 & 15) + ln.boff +
-                          (uint32_t)uu * GUnit<QT>::ustep(1 << g.lpr_log2);
+    const uint32_t off = lane_row_off + (uint32_t)(byte0 & 15) + ln.boff +
+                         (uint32_t)uu * GUnit<QT>::ustep(1 << g.lpr_log2);
+    const uint32_t off0 = lane_ok ? off : OOB_OFF;
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) un[rr].load(wr, off0 + (uint32_t)(rr * g.rb), e, g.k, ln);
 }

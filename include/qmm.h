@@ -20,7 +20,13 @@
  *    tuning variables (QMM_GEMV_MAX_N below; QMM_GEMV_WG_PER_CU and
  *    QMM_MOE_WG_PER_CU 1..64, QMM_GEMV_ROWS 1..2, QMM_GEMV_DEPTH 2/4/8,
  *    QMM_MOE_LPR_LOG2 3..6 (log2 of the MoE streams' lanes per row) for the
- *    streaming kernels' launch shape; a malformed value makes the calls that use it return
+ *    streaming kernels' launch shape; QMM_GEMV_MFMA_MIN 0..64 (default 3:
+ *    the smallest n that QMM_PATH_GEMV runs on its matrix-core stream, 0 =
+ *    never), QMM_GEMV_MFMA_TT 1..2 (that stream's activation rows per pass
+ *    over the weights: at most 4 or 8), QMM_MOE_MFMA_MIN 0..4 (default 2:
+ *    with more than one token, the MoE kernels run the experts' chunks of at
+ *    least that many pairs on the matrix-core stream, 0 = never);
+ *    a malformed value makes the calls that use it return
  *    QMM_ERR_RANGE; QMM_MFMA_PLAN is read again at every call that plans a
  *    prefill), so the calls can be recorded into a hipGraph.
  *  - Arguments are validated on the host before anything is launched; a
@@ -84,8 +90,15 @@ typedef enum {
 /* Kernel path selector for qmm_gemm_path. */
 typedef enum {
     QMM_PATH_AUTO = 0,     /* n <= qmm_gemv_max_n() -> GEMV, else MFMA       */
-    QMM_PATH_GEMV = 1,     /* f32 FMA, any n (decode path)                     */
-    QMM_PATH_MFMA = 2      /* f16 MFMA tiles, f32 accumulation, any n (prefill) */
+    QMM_PATH_GEMV = 1,     /* the f32 decode path, any n: GEMV_FMA for n below
+                              QMM_GEMV_MFMA_MIN (3), else GEMV_MATRIX          */
+    QMM_PATH_MFMA = 2,     /* f16 MFMA tiles, f32 accumulation, any n (prefill) */
+    QMM_PATH_GEMV_FMA = 3, /* the f32 decode path on f32 FMAs                  */
+    QMM_PATH_GEMV_MATRIX = 4 /* the f32 decode path with its products on
+                              v_mfma_f32_4x4x1f32 (f32 inputs, f32 sums), 4 or
+                              8 activation rows per pass over the weights; where
+                              4 rows do not fit one work group's LDS (k above
+                              about 9000) it runs as GEMV_FMA                   */
 } qmm_path;
 
 /*
@@ -98,7 +111,9 @@ typedef enum {
  *   qtype one of QMM_F32..QMM_NVFP4_V2 (NVFP4_V2 on the GEMV path only).
  * Dispatch (the decode-GEMV / prefill-GEMM split of aprender-serve
  * cublas_prefill, its cublas_gemm_threshold): the f32 GEMV for n <= 32
- * (results within 1e-5 * sum|w*x| of the exact value), the MFMA kernel for
+ * (results within 1e-5 * sum|w*x| of the exact value; its products on f32
+ * FMAs for n < 3 and on v_mfma_f32_4x4x1f32 above, f32 inputs and sums
+ * either way: QMM_PATH_GEMV below), the MFMA kernel for
  * n > 32, which rounds W and x to f16 (RNE) and accumulates in f32 (within
  * 2e-3 * sum|w*x|).  With QMM_GEMV_MAX_N set: the GEMV for n <= that value,
  * else MFMA (the measured MI355X speed crossover is n = 8..16 on large
@@ -214,11 +229,13 @@ int64_t qmm_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int qtype, int
 /*
  * qmm_gemm_plan: the kernels a call with these sizes runs on the current
  * device, with (with_workspace != 0: qmm_gemm_ws) or without a workspace.
- *   out  HOST int32[6], written: path (QMM_PATH_GEMV or QMM_PATH_MFMA); then
- *        for the MFMA path: the kernel family (0, 2, 3 or 4, as listed at
- *        qmm_gemm_ws; families 2 and 3 round the activations to f16 in a
- *        pre-pass), weight rows per tile, k groups per work group, k
- *        splits, and 64-k steps per split (zeros on the GEMV path).
+ *   out  HOST int32[6], written: path (QMM_PATH_GEMV for the three GEMV
+ *        paths, or QMM_PATH_MFMA); then for the GEMV: 1 if it runs on the
+ *        matrix-core stream (else 0), its activation rows per pass (4 or 8;
+ *        0 on the FMA stream), zeros; for the MFMA path: the kernel family
+ *        (0, 2, 3 or 4, as listed at qmm_gemm_ws; families 2 and 3 round the
+ *        activations to f16 in a pre-pass), weight rows per tile, k groups
+ *        per work group, k splits, and 64-k steps per split.
  * Errors as qmm_gemm_workspace_bytes; QMM_ERR_NULL for a null out.
  */
 int qmm_gemm_plan(int64_t m, int64_t k, int64_t n, int qtype, int path, int with_workspace,

@@ -164,9 +164,10 @@ def test_gemv_max_n_env_is_strict(value, expect):
         assert int(out.stdout.strip()) == 8
 
 
-@pytest.mark.parametrize("var", ["QMM_GEMV_WG_PER_CU", "QMM_MOE_WG_PER_CU", "QMM_GEMV_ROWS",
-                                 "QMM_GEMV_DEPTH", "QMM_MOE_LPR_LOG2"])
-@pytest.mark.parametrize("value", ["0", "abc", "65", "3x"])
+@pytest.mark.parametrize("var,value", [(v, x) for v in ("QMM_GEMV_WG_PER_CU", "QMM_MOE_WG_PER_CU", "QMM_GEMV_ROWS",
+                                                         "QMM_GEMV_DEPTH", "QMM_MOE_LPR_LOG2", "QMM_GEMV_MFMA_TT")
+                                       for x in ("0", "abc", "65", "3x")] +
+                         [(v, x) for v in ("QMM_MOE_MFMA_MIN", "QMM_GEMV_MFMA_MIN") for x in ("-1", "abc", "65", "3x")])
 def test_streaming_tuning_env_is_strict(var, value):
     """A malformed or out-of-range launch-shape knob makes the streaming
     entry points fail with QMM_ERR_RANGE before any launch."""
@@ -237,11 +238,18 @@ def test_gemm_ws_rejects_a_workspace_overlapping_an_operand():
 
 
 def test_gemm_plan_reports_kernels():
-    """qmm_gemm_plan: GEMV below the crossover, MFMA above; without a
+    """qmm_gemm_plan: GEMV below the crossover (its FMA stream at n < 3, the
+    matrix-core stream above, with 8 activation rows per pass where they fit
+    the LDS, which at k = 1024 they do on any device), MFMA above; without a
     workspace never a pre-pass or a k split; bad arguments give a status."""
     import gemv_prefill_decode_amd as qmm
     _lib()
-    assert qmm.gemm_plan(4096, 4096, 8, "q4_k") == {"path": "gemv"}
+    assert qmm.gemm_plan(4096, 1024, 8, "q4_k") == {"path": "gemv", "stream": "matrix", "tokens_per_pass": 8}
+    assert qmm.gemm_plan(4096, 1024, 4, "q4_k") == {"path": "gemv", "stream": "matrix", "tokens_per_pass": 4}
+    assert qmm.gemm_plan(4096, 1024, 2, "q4_k") == {"path": "gemv", "stream": "fma", "tokens_per_pass": 0}
+    assert qmm.gemm_plan(4096, 1024, 8, "q4_k", "gemv_fma")["stream"] == "fma"
+    assert qmm.gemm_plan(4096, 1024, 1, "q4_k", "gemv_matrix")["tokens_per_pass"] == 4
+    assert qmm.gemm_plan(4096, 4096, 8, "q4_k")["path"] == "gemv"
     p = qmm.gemm_plan(4096, 4096, 512, "q4_k", workspace=False)
     assert p["path"] == "mfma" and p["x16"] == 0 and p["n_split"] == 1 and p["k_groups"] == 1
     p = qmm.gemm_plan(1024, 4608, 512, "q4_k", "mfma")

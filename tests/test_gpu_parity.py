@@ -29,15 +29,54 @@ GEMV_SHAPES = {
 }
 
 
+@pytest.mark.parametrize("path", ["gemv_fma", "gemv_matrix"])
 @pytest.mark.parametrize("qt", QTS)
 @pytest.mark.parametrize("n", [1, 2, 3, 5, 8, 13, 32])
-def test_gemv_parity(qt, n):
+def test_gemv_parity(qt, n, path):
+    """Both streams of the f32 decode path (products on FMAs, or on
+    v_mfma_f32_4x4x1f32 with token groups of 4 or 8) at every n; the shapes
+    leave the last row group and the last unit iteration of a row ragged."""
     for si, (m, k) in enumerate(GEMV_SHAPES[qt]):
-        note(f"gemv {qt} m={m} k={k} n={n}")
+        note(f"gemv {path} {qt} m={m} k={k} n={n}")
         w = weights(qt, m, k, si)
         x = acts(n, k, si)
-        got = gpu_gemm(qt, w, x, m, "gemv")
-        check_full(qt, w, x, m, k, n, got, TAU_F32, f"gemv {qt} {m}x{k} n={n}")
+        got = gpu_gemm(qt, w, x, m, path)
+        check_full(qt, w, x, m, k, n, got, TAU_F32, f"{path} {qt} {m}x{k} n={n}")
+
+
+@pytest.mark.parametrize("qt", QTS)
+@pytest.mark.parametrize("n", [4, 8])
+def test_gemv_matrix_long_rows(qt, n):
+    """k = 8192: four staged rows take one work group per CU (8 waves);
+    eight do not fit, so n = 8 runs as two token groups of four."""
+    import gemv_prefill_decode_amd as qmm
+    k = 8192
+    for si, m in enumerate((37, 1030)):
+        note(f"gemv_matrix long rows {qt} m={m} k={k} n={n}")
+        assert qmm.gemm_plan(m, k, n, qt, "gemv_matrix")["tokens_per_pass"] == 4
+        w = weights(qt, m, k, 60 + si)
+        x = acts(n, k, 60 + si)
+        got = gpu_gemm(qt, w, x, m, "gemv_matrix")
+        check_full(qt, w, x, m, k, n, got, TAU_F32, f"gemv_matrix {qt} {m}x{k} n={n}")
+
+
+@pytest.mark.parametrize("mfma_min", ["0", "1", "4"])
+def test_moe_stream_choice(mfma_min):
+    """The MoE projections with each choice of the chunks that run on the
+    matrix-core stream (none; every chunk, also of one pair; chunks of four
+    pairs only), in a process of its own since the choice is read once per
+    process; every output against the oracle."""
+    import os
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    env = dict(os.environ, QMM_MOE_MFMA_MIN=mfma_min)
+    note(f"moe stream choice QMM_MOE_MFMA_MIN={mfma_min}")
+    r = subprocess.run([sys.executable, os.path.join(here, "moe_env_check.py")], env=env, capture_output=True,
+                       text=True, timeout=600)
+    sys.stderr.write(r.stdout[-2000:])
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert r.stdout.count("OK ") == 4
 
 
 MFMA_SHAPES = {
@@ -213,18 +252,19 @@ def test_lds_ring_identity_and_exact(qt, plan, monkeypatch):
     assert np.array_equal(got.astype(np.float64), r)
 
 
+@pytest.mark.parametrize("path", ["gemv_fma", "gemv_matrix"])
 @pytest.mark.parametrize("qt", QTS)
-def test_identity_windows_gemv(qt):
+def test_identity_windows_gemv(qt, path):
     """Sliding one-hot windows (n = 32 tokens, token j selects k index
-    c0 + j): dst[j, i] = f32(W[i, c0 + j]) exactly on the f32 path."""
+    c0 + j): dst[j, i] = f32(W[i, c0 + j]) exactly on both f32 streams."""
     m, k = 70, 512
-    note(f"identity gemv {qt}")
+    note(f"identity {path} {qt}")
     w = weights(qt, m, k, 22)
     W = formats.decode(qt, w, m, k)
     for c0 in range(0, k, 32):
         x = np.zeros((32, k), dtype=np.float32)
         x[np.arange(32), c0 + np.arange(32)] = 1.0
-        got = gpu_gemm(qt, w, x, m, "gemv")
+        got = gpu_gemm(qt, w, x, m, path)
         want = W[:, c0:c0 + 32].T.astype(np.float32)
         assert np.array_equal(got, want), c0
 
