@@ -44,8 +44,8 @@ __global__ __launch_bounds__(64 * WPG) void gemv_kernel(float* __restrict__ dst,
 }
 
 // The matrix-core stream: grid x = work groups, y = token groups of 4 * TT
-// rows, staged in LDS in the quad layout (qlds_floats(4 * TT, k, lm) floats,
-// row stride mld).
+// rows, staged in LDS in the quad layout (qlds_floats(4 * TT, k, lm,
+// MTraits::RUN) floats, row stride mld).
 template <int QT, int TT, int R, int D, int WPG = 4>
 __global__ __launch_bounds__(64 * WPG) void gemv_mfma_kernel(float* __restrict__ dst,
                                                              const uint8_t* __restrict__ w,
@@ -66,12 +66,9 @@ __global__ __launch_bounds__(64 * WPG) void gemv_mfma_kernel(float* __restrict__
         if (row < m && j < ntok) out[(int64_t)j * ldd + row] = v;
     };
     float* sx = qmm_dyn_lds;
-    XQuad<TT> xq;
-#pragma unroll
-    for (int t = 0; t < TT; ++t) xq.row[t] = sx + (4 * t + (int)(threadIdx.x & 3)) * mld;
-    xq.zero = sx + NTOK * mld;
+    const XQuad<TT> xq = make_xquad<TT>(sx, mld, k, ntok);
     mfma_stream<QT, TT, R, D>(g, blockIdx.x * WPG + wave, gridDim.x * WPG, n_rg, xq, store,
-                              make_qstage<NTOK, 64 * WPG>(sx, xr, xoff, k, mld));
+                              make_qstage<NTOK, MTraits<QT>::RUN, 64 * WPG>(sx, xr, xoff, k, mld, ntok));
 }
 
 // ------------------------------------------------------------------ load-only twin
@@ -206,7 +203,7 @@ static bool launch_gemv_mfma(float* dst, const uint8_t* w, const float* x, int64
                              int64_t rb, int64_t ldx, int64_t ldd, const GemvTuning& tune, hipStream_t st) {
     constexpr int R = 2, D = 2;
     const int lm = MTraits<QT>::LM;
-    const int64_t lds = (int64_t)qlds_floats(4 * TT, (int)k, lm) * 4;
+    const int64_t lds = (int64_t)qlds_floats(4 * TT, (int)k, lm, MTraits<QT>::RUN) * 4;
     if (lds > tune.lds_per_wg) return false;
     const int mld = qld((int)k, lm);
     const int64_t n_rg = (m + 4 * R - 1) / (4 * R);
@@ -232,8 +229,9 @@ int gemv_matrix_tokens(int64_t m, int64_t k, int64_t n, int qt, int kind, const 
     const bool use = kind == GEMV_MATRIX || (kind == GEMV_AUTO && tune.gemv_mfma_min > 0 && n >= tune.gemv_mfma_min);
     if (!use) return 0;
     const int lm = mtraits_lm(qt);
-    if (n > 4 && tune.gemv_mfma_tt >= 2 && (int64_t)qlds_floats(8, (int)k, lm) * 4 <= tune.lds_per_wg) return 8;
-    if ((int64_t)qlds_floats(4, (int)k, lm) * 4 <= tune.lds_per_wg) return 4;
+    const bool sums = qt_runs(qt);
+    if (n > 4 && tune.gemv_mfma_tt >= 2 && (int64_t)qlds_floats(8, (int)k, lm, sums) * 4 <= tune.lds_per_wg) return 8;
+    if ((int64_t)qlds_floats(4, (int)k, lm, sums) * 4 <= tune.lds_per_wg) return 4;
     return 0;
 }
 

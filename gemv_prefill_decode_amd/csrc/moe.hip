@@ -201,10 +201,9 @@ __device__ __forceinline__ void moe_mchunk(const MoeArgs& a, int e, const int* p
     for (int j = 0; j < NT; ++j) xoff[j] = ck.row[j] * (uint32_t)a.in_f * 4u;
     __syncthreads();  // the previous chunk's waves are done with the staged rows
     float* sx = qmm_dyn_lds;
-    XQuad<1> xq;
-    xq.row[0] = sx + (threadIdx.x & 3) * a.mld;
-    xq.zero = sx + NT * a.mld;
-    const auto st = make_qstage<NT>(sx, xr, xoff, a.in_f, a.mld);
+    const int nreal = cnt - c0 < NT ? cnt - c0 : NT;
+    const XQuad<1> xq = make_xquad<1>(sx, a.mld, a.in_f, nreal);
+    const auto st = make_qstage<NT, MTraits<QT>::RUN>(sx, xr, xoff, a.in_f, a.mld, nreal);
     const int first = blockIdx.x * 4 + wave, stride = gridDim.x * 4;
     if constexpr (MODE == MOE_ACT) {
         const StreamGeom g1{a.w1 + (int64_t)e * n_ff * a.rb, n_ff, a.rb, a.in_f, 4};
@@ -330,7 +329,7 @@ static void launch_moe_mode(MoeArgs a, int planes, const GemvTuning& tune, hipSt
         // one activation row (one token's pairs go to distinct experts), f32
         // activations, and MOE_MT staged rows within the LDS limit
         const int lm = mtraits_lm(QT);
-        const int64_t mbytes = (int64_t)qlds_floats(MOE_MT, a.in_f, lm) * 4;
+        const int64_t mbytes = (int64_t)qlds_floats(MOE_MT, a.in_f, lm, MTraits<QT>::RUN) * 4;
         const int64_t RGM = 4 * R;
         const int64_t n_rg_m = (a.n_ff + RGM - 1) / RGM;
         a.mt_min = !Q8 && a.t > 1 && mbytes <= MOE_MT_LDS_MAX ? tune.moe_mfma_min : 0;

@@ -39,8 +39,11 @@ __host__ __device__ constexpr int qld(int k, int lm) {
     return b + ((lm - b % 32) % 32 + 32) % 32;
 }
 constexpr int QZERO = 128;
-// LDS floats of nt staged rows and the zero block.
-__host__ __device__ constexpr int qlds_floats(int nt, int k, int lm) { return nt * qld(k, lm) + QZERO; }
+// LDS floats of nt staged rows, the zero block and, for the offset formats
+// (sums), the rows' run sums (k/16 per row, four rows interleaved).
+__host__ __device__ constexpr int qlds_floats(int nt, int k, int lm, bool sums) {
+    return nt * qld(k, lm) + QZERO + (sums ? nt * (k >> 4) : 0);
+}
 
 // Offset of k = e + rel from k = e in the padded layout.  Every unit starts
 // at e with e % 32 + rel % 32 + 4 <= 32 for the offsets it reads, so the
@@ -52,16 +55,24 @@ __host__ __device__ constexpr int qrel(int rel) { return rel + 4 * (rel >> 5); }
 // when its two halves carry different scale factors), EM1 (the second residue
 // e % 32 that units start at, besides 0), flush(s) (whether a run of one
 // scale factor, or the unit, ends with sub-unit s).
+// Q4_0 and Q4_K (w = A_r*q - B_r per run of 16, 4-bit q) stream q itself,
+// exact, and finish each run with A_r*sum(q*x) - B_r*sum(x) (RUN); q
+// converts through v_cvt_pk_f32_fp8 as the E4M3 codes 0..15, whose values
+// are exactly q * 2^-9, so QS = 2^9 goes into A_r.  Q6_K keeps w = q - 32
+// with its scale per run: its 6-bit q converts through ubyte_f32, whose
+// inline asm hides the register write from the compiler's hazard checks,
+// and a matrix-core operand must not be such a write (the subtract between
+// them is an ordinary VALU instruction).
 template <int QT> struct MTraits;
-template <> struct MTraits<QT_F32> { static constexpr int LM = 4, CH = 1, EM1 = 16; static constexpr bool flush(int s) { return s == 1; } };
-template <> struct MTraits<QT_Q4_0> { static constexpr int LM = 8, CH = 1, EM1 = 0; static constexpr bool flush(int s) { return s == 3; } };
-template <> struct MTraits<QT_Q8_0> { static constexpr int LM = 8, CH = 1, EM1 = 0; static constexpr bool flush(int s) { return s == 3; } };
-template <> struct MTraits<QT_Q4_K> { static constexpr int LM = 4, CH = 1, EM1 = 16; static constexpr bool flush(int s) { return s == 3; } };
+template <> struct MTraits<QT_F32> { static constexpr bool RUN = false; static constexpr float QS = 1.0f; static constexpr int LM = 4, CH = 1, EM1 = 16; static constexpr bool flush(int s) { return s == 1; } };
+template <> struct MTraits<QT_Q4_0> { static constexpr bool RUN = true; static constexpr float QS = 512.0f; static constexpr int LM = 8, CH = 1, EM1 = 0; static constexpr bool flush(int s) { return s == 3; } };
+template <> struct MTraits<QT_Q8_0> { static constexpr bool RUN = false; static constexpr float QS = 1.0f; static constexpr int LM = 8, CH = 1, EM1 = 0; static constexpr bool flush(int s) { return s == 3; } };
+template <> struct MTraits<QT_Q4_K> { static constexpr bool RUN = true; static constexpr float QS = 512.0f; static constexpr int LM = 4, CH = 1, EM1 = 16; static constexpr bool flush(int s) { return s == 3; } };
 // Q6_K: a scale factor per quarter (sub-units 2g, 2g + 1)
-template <> struct MTraits<QT_Q6_K> { static constexpr int LM = 4, CH = 1, EM1 = 16; static constexpr bool flush(int s) { return (s & 1) == 1; } };
+template <> struct MTraits<QT_Q6_K> { static constexpr bool RUN = false; static constexpr float QS = 1.0f; static constexpr int LM = 4, CH = 1, EM1 = 16; static constexpr bool flush(int s) { return (s & 1) == 1; } };
 // NVFP4: the two halves of a sub-unit belong to the unit's two scale groups
-template <> struct MTraits<QT_NVFP4> { static constexpr int LM = 8, CH = 2, EM1 = 0; static constexpr bool flush(int s) { return s == 3; } };
-template <> struct MTraits<QT_NVFP4_V2> { static constexpr int LM = 8, CH = 2, EM1 = 0; static constexpr bool flush(int s) { return s == 3; } };
+template <> struct MTraits<QT_NVFP4> { static constexpr bool RUN = false; static constexpr float QS = 1.0f; static constexpr int LM = 8, CH = 2, EM1 = 0; static constexpr bool flush(int s) { return s == 3; } };
+template <> struct MTraits<QT_NVFP4_V2> { static constexpr bool RUN = false; static constexpr float QS = 1.0f; static constexpr int LM = 8, CH = 2, EM1 = 0; static constexpr bool flush(int s) { return s == 3; } };
 
 // The four activations at e + rel .. e + rel + 3 are contiguous at
 // qpad(e) + qrel(rel) for every sub-unit offset and unit start residue.
@@ -83,6 +94,13 @@ static_assert(qrel_ok<QT_F32>() && qrel_ok<QT_Q4_0>() && qrel_ok<QT_Q8_0>() && q
                   qrel_ok<QT_Q6_K>() && qrel_ok<QT_NVFP4>() && qrel_ok<QT_NVFP4_V2>(),
               "a unit's activations cross the quad layout's padding");
 
+// The formats whose matrix-core stream needs the run sums (MTraits::RUN).
+inline bool qt_runs(int qt) { return qt == QT_Q4_0 || qt == QT_Q4_K; }
+static_assert(MTraits<QT_Q4_0>::RUN && MTraits<QT_Q4_K>::RUN && !MTraits<QT_Q6_K>::RUN && !MTraits<QT_F32>::RUN &&
+                  !MTraits<QT_Q8_0>::RUN && !MTraits<QT_NVFP4>::RUN && !MTraits<QT_NVFP4_V2>::RUN,
+              "qt_runs lists the formats with MTraits::RUN");
+static_assert(GUnit<QT_Q4_0>::RUNS > 0 && GUnit<QT_Q4_K>::RUNS > 0, "RUN formats have runs");
+
 inline int mtraits_lm(int qt) {
     switch (qt) {
         case QT_F32: return MTraits<QT_F32>::LM;
@@ -103,17 +121,21 @@ template <int TT>
 struct XQuad {
     const float* row[TT];
     const float* zero;
+    const float* sums[TT];  // offset formats: run sums of tile t, [k/16][4 tokens]
 };
 
-// Stage rows xoff[j] (j < NTOK) of x into LDS in the quad layout (two-phase,
-// as XStage), then clear the zero block.
-template <int NTOK, int TPB = 256>
+// Stage rows xoff[j] (j < nreal <= NTOK) of x into LDS in the quad layout
+// (two-phase, as XStage), clear the zero block and, with SUMS, write the run
+// sums of the staged rows: token j's sum over k = 16r .. 16r + 15 at
+// sums[((j >> 2) * (k >> 4) + r) * 4 + (j & 3)], added in a fixed order.
+// Rows j >= nreal are not staged: the lanes of absent tokens read row 0.
+template <int NTOK, bool SUMS, int TPB = 256>
 struct QStage {
     static constexpr int U = NTOK >= 8 ? 1 : 8 / NTOK;  // float4 columns per thread per batch
     float* sx;
     rsrc_t xr;
     uint32_t xoff[NTOK];
-    int k, ld;
+    int k, ld, nreal;
     f32x4 v[NTOK][U];
 
     __device__ __forceinline__ void load(int c0) {
@@ -123,7 +145,8 @@ struct QStage {
             const int c = c0 + TPB * u;
 #pragma unroll
             for (int j = 0; j < NTOK; ++j)
-                v[j][u] = __builtin_bit_cast(f32x4, ld128(xr, c < per ? xoff[j] + 16u * (uint32_t)c : OOB_OFF));
+                if (j < nreal)
+                    v[j][u] = __builtin_bit_cast(f32x4, ld128(xr, c < per ? xoff[j] + 16u * (uint32_t)c : OOB_OFF));
         }
     }
     __device__ __forceinline__ void store(int c0) {
@@ -133,7 +156,8 @@ struct QStage {
             const int c = c0 + TPB * u;
             if (c < per)
 #pragma unroll
-                for (int j = 0; j < NTOK; ++j) *(f32x4*)(sx + j * ld + qpad(4 * c)) = v[j][u];
+                for (int j = 0; j < NTOK; ++j)
+                    if (j < nreal) *(f32x4*)(sx + j * ld + qpad(4 * c)) = v[j][u];
         }
     }
     __device__ __forceinline__ void issue() { load((int)threadIdx.x); }
@@ -145,20 +169,52 @@ struct QStage {
         }
         for (int i = (int)threadIdx.x; i < QZERO; i += TPB) sx[NTOK * ld + i] = 0.0f;
         __syncthreads();
+        if constexpr (SUMS) {
+            const int nrun = k >> 4;
+            float* sums = sx + NTOK * ld + QZERO;
+            for (int t = threadIdx.x; t < nreal * nrun; t += TPB) {
+                const int j = t / nrun, r = t - j * nrun;
+                const float* p = sx + j * ld + qpad(16 * r);  // 16 contiguous floats
+                const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+                const f32x4 c = *(const f32x4*)(p + 8), d = *(const f32x4*)(p + 12);
+                const float sa = (a.x + a.y) + (a.z + a.w), sb = (b.x + b.y) + (b.z + b.w);
+                const float sc = (c.x + c.y) + (c.z + c.w), sd = (d.x + d.y) + (d.z + d.w);
+                sums[((j >> 2) * nrun + r) * 4 + (j & 3)] = (sa + sb) + (sc + sd);
+            }
+            __syncthreads();
+        }
     }
 };
 
-template <int NTOK, int TPB = 256>
-__device__ __forceinline__ QStage<NTOK, TPB> make_qstage(float* sx, rsrc_t xr, const uint32_t (&xoff)[NTOK], int k,
-                                                         int ld) {
-    QStage<NTOK, TPB> st;
+template <int NTOK, bool SUMS, int TPB = 256>
+__device__ __forceinline__ QStage<NTOK, SUMS, TPB> make_qstage(float* sx, rsrc_t xr, const uint32_t (&xoff)[NTOK],
+                                                               int k, int ld, int nreal) {
+    QStage<NTOK, SUMS, TPB> st;
     st.sx = sx;
     st.xr = xr;
 #pragma unroll
     for (int j = 0; j < NTOK; ++j) st.xoff[j] = xoff[j];
     st.k = k;
     st.ld = ld;
+    st.nreal = nreal;
     return st;
+}
+
+// The quad-layout view of NTOK = 4 TT staged rows at sx (row stride ld) for
+// this lane: tile t's token 4t + (lane & 3), row 0 for tokens >= nreal.
+template <int TT>
+__device__ __forceinline__ XQuad<TT> make_xquad(float* sx, int ld, int k, int nreal) {
+    XQuad<TT> xq;
+    const int i = (int)(threadIdx.x & 3);
+    xq.zero = sx + 4 * TT * ld;
+    const float* sums = xq.zero + QZERO;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        const int j = 4 * t + i;
+        xq.row[t] = sx + (j < nreal ? j : 0) * ld;
+        xq.sums[t] = sums + t * (k >> 4) * 4;
+    }
+    return xq;
 }
 
 // ------------------------------------------------------------------ core
@@ -233,6 +289,96 @@ __device__ __forceinline__ void msub_all(const GUnit<QT> (&un)[R], const float* 
     }
 }
 
+// Four nibbles (bytes 0..3 of lo) as floats q * 2^-9: v_cvt_pk_f32_fp8
+// reads each byte as an E4M3 code, and the codes 0..15 are the subnormals
+// m * 2^-9 (m < 8) and the normals (1 + m/8) * 2^-6 = (8 + m) * 2^-9.
+__device__ __forceinline__ void nib4_f32(uint32_t v, float* q) {
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v, false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v, true);
+    q[0] = a.x;
+    q[1] = a.y;
+    q[2] = b.x;
+    q[3] = b.y;
+}
+
+// q of sub-unit s of an offset format as exact floats times 1/QS, in the
+// order of GUnit::qsub (q[0..3] at rel0(s), q[4..7] at rel1(s)).
+template <int QT>
+__device__ __forceinline__ void mq(const GUnit<QT>& u, int s, float (&q)[8]) {
+    static_assert(QT == QT_Q4_0 || QT == QT_Q4_K, "4-bit q only");
+    uint32_t v;
+    if constexpr (QT == QT_Q4_0) v = shr64(u.r[s], u.r[s + 1], u.sh + 2u);
+    else v = s == 0 ? u.qs.x : (s == 1 ? u.qs.y : (s == 2 ? u.qs.z : u.qs.w));
+    nib4_f32(v & 0x0F0F0F0Fu, q);
+    nib4_f32((v >> 4) & 0x0F0F0F0Fu, q + 4);
+}
+
+// Sub-unit S_ of an offset format: the q*x products of each run accumulate
+// in P (slot r & 1); after the run's last sub-unit, acc += A_r*QS*P -
+// B_r*sum(x of the run), the sums of the lane's tile tokens read as one
+// float4 (sp[t]: the run sums at the unit's first k).
+template <int QT, int TT, int R, int S_>
+__device__ __forceinline__ void msub_runs(const GUnit<QT> (&un)[R], const float* const (&xp)[TT],
+                                          const float* const (&sp)[TT], f32x4 (&P)[R][TT][2],
+                                          f32x4 (&acc)[R][TT]) {
+    using UT = GUnit<QT>;
+    using MT = MTraits<QT>;
+    constexpr int r0 = UT::run0(S_), r1 = UT::run1(S_);
+    float q[R][8];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) mq<QT>(un[rr], S_, q[rr]);
+    f32x4 xa[TT], xb[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        xa[t] = *(const f32x4*)(xp[t] + qrel(UT::rel0(S_)));
+        xb[t] = *(const f32x4*)(xp[t] + qrel(UT::rel1(S_)));
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) {
+                P[rr][t][r0 & 1] = mfma4(xa[t][c], q[rr][c], P[rr][t][r0 & 1]);
+                if constexpr (r1 != r0) P[rr][t][r1 & 1] = mfma4(xb[t][c], q[rr][4 + c], P[rr][t][r1 & 1]);
+            }
+    if constexpr (r1 == r0)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+#pragma unroll
+                for (int rr = 0; rr < R; ++rr) P[rr][t][r0 & 1] = mfma4(xb[t][c], q[rr][4 + c], P[rr][t][r0 & 1]);
+    auto flush = [&](int r) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            const f32x4 sx = *(const f32x4*)(sp[t] + (UT::runrel(r) >> 4) * 4);
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) {
+                const float a = un[rr].runA(r) * MT::QS, b = un[rr].runB(r);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = __builtin_fmaf(a, P[rr][t][r & 1][i], acc[rr][t][i]);
+                    acc[rr][t][i] = __builtin_fmaf(-b, sx[i], v);
+                }
+                P[rr][t][r & 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    };
+    if constexpr (S_ == UT::lastsub(r0)) flush(r0);
+    if constexpr (r1 != r0 && S_ == UT::lastsub(r1)) flush(r1);
+}
+
+template <int QT, int TT, int R, int S_ = 0>
+__device__ __forceinline__ void msub_all_runs(const GUnit<QT> (&un)[R], const float* const (&xp)[TT],
+                                              const float* const (&sp)[TT], f32x4 (&P)[R][TT][2],
+                                              f32x4 (&acc)[R][TT]) {
+    if constexpr (S_ < GUnit<QT>::S) {
+        msub_runs<QT, TT, R, S_>(un, xp, sp, P, acc);
+        msub_all_runs<QT, TT, R, S_ + 1>(un, xp, sp, P, acc);
+    }
+}
+
 // One item: the unit at k = e of the lane's R rows against the lane's token
 // in each tile; valid = false (the quad's unit lies past the row's end; its
 // weights were loaded as zeros) reads the zero block instead.
@@ -245,6 +391,18 @@ __device__ __forceinline__ void mcompute_item(GUnit<QT> (&un)[R], const typename
     const int pe = qpad(e);
 #pragma unroll
     for (int t = 0; t < TT; ++t) xp[t] = valid ? xq.row[t] + pe : xq.zero;
+    if constexpr (MTraits<QT>::RUN) {
+        const float* sp[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) sp[t] = valid ? xq.sums[t] + (e >> 4) * 4 : xq.zero;
+        f32x4 P[R][TT][2];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int t = 0; t < TT; ++t) P[rr][t][0] = P[rr][t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        msub_all_runs<QT, TT, R>(un, xp, sp, P, acc);
+        return;
+    }
     f32x4 P[R][TT][MTraits<QT>::CH];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr)
