@@ -63,30 +63,64 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources; profiles/traffic.json is used only when it
-    was measured on the same sources."""
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "gemv_prefill_decode_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
+CSRC = os.path.join(ROOT, "gemv_prefill_decode_amd", "csrc")
+
+
+def tu_source_hashes() -> dict:
+    """Per kernel translation unit (csrc/*.hip), a hash of its source and of
+    every local header it includes, directly or not: the measured traffic of a
+    kernel is used only while its own translation unit hashes the same."""
+    def includes(path):
+        out = []
+        for ln in open(path):
+            ln = ln.strip()
+            if ln.startswith("#include \""):
+                out.append(ln.split("\"")[1])
+        return out
+
+    hashes = {}
+    for tu in sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")):
+        seen, todo = set(), [tu]
+        while todo:
+            f = todo.pop()
+            if f in seen or not os.path.exists(os.path.join(CSRC, f)):
+                continue
+            seen.add(f)
+            todo.extend(includes(os.path.join(CSRC, f)))
+        h = hashlib.sha256()
+        for f in sorted(seen):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+        hashes[tu] = h.hexdigest()[:16]
+    return hashes
+
+
+def kernel_tu(kernel: str):
+    """The translation unit that defines a kernel (by its unqualified name)."""
+    base = kernel.replace("qmm::", "").split("<")[0].split("@")[0].strip()
+    for tu in sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")):
+        src = open(os.path.join(CSRC, tu)).read()
+        if f" {base}(" in src and "__global__" in src:
+            return tu
+    return None
 
 
 def traffic_from_profiles(kernel: str):
     """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
-    calibration) from profiles/traffic.json, or None if absent or stale."""
+    calibration) from profiles/traffic.json, or None if absent or if the
+    kernel's translation unit has changed since it was measured."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             tab = json.load(f)
     except (OSError, ValueError):
         return None
-    if tab.get("source_hash") != kernel_source_hash():
-        return None
     ent = tab.get("kernels", {}).get(kernel)
-    return None if not ent else ent.get("bytes_per_launch")
+    if not ent or ent.get("tu") is None:
+        return None
+    if tab.get("tu_hashes", {}).get(ent["tu"]) != tu_source_hashes().get(ent["tu"]):
+        return None
+    return ent.get("bytes_per_launch")
 
 
 def plan_grid_size(plan, m, n):
@@ -709,21 +743,22 @@ def run_counter_workload():
         torch.cuda.empty_cache()
 
 
-STREAM_COUNTER_SET = ("SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES "
+STREAM_COUNTER_SET = ("SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_BUSY_CYCLES SQ_WAVE_CYCLES "
                       "SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU")
 
 
 def run_stream_counter_workload():
     """The streaming kernels three times each (synchronized, eager), for a
     rocprofv3 --pmc run: the n=1 GEMV and its load-only twin on 14336x4096
-    Q4_K and Q6_K, the NVFP4 MoE gate/up at t=1 and t=16 with its load-only
-    and math-only twins."""
+    Q4_K and Q6_K; the n=4 and n=16 Q4_K GEMV on its FMA and matrix-core
+    streams; the NVFP4 MoE gate/up at t=1 and t=16 with its load-only and
+    math-only twins.  Each tag line lists its arms in call order."""
     import numpy as np
     import torch
     import gemv_prefill_decode_amd as qmm
     from synth import gen
+    m, k = 14336, 4096
     for qt in ("q4_k", "q6_k"):
-        m, k = 14336, 4096
         w = to_dev(gen_weights(qt, m, k, 99))
         x = to_dev(gen.unit_f32(k, gen.SEED_X).reshape(1, k))
         out = torch.empty((1, m), dtype=torch.float32, device="cuda")
@@ -733,8 +768,21 @@ def run_stream_counter_workload():
             torch.cuda.synchronize()
             qmm.stream_loadonly(w, m, k, qt, sink)
             torch.cuda.synchronize()
-        print(json.dumps({"tag": f"gemv_n1_{qt}_{m}x{k}", "weights": m * k}), flush=True)
+        print(json.dumps({"tag": f"gemv_n1_{qt}_{m}x{k}", "weights": m * k,
+                          "arms": ["served", "load-only twin"]}), flush=True)
         del w, x, out, sink
+    w = to_dev(gen_weights("q4_k", m, k, 99))
+    for n in (4, 16):
+        x = to_dev(gen.unit_f32(n * k, gen.SEED_X).reshape(n, k))
+        out = torch.empty((n, m), dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            for path in ("gemv_fma", "gemv_matrix"):
+                qmm.gemm(w, x, m, "q4_k", out=out, path=path)
+                torch.cuda.synchronize()
+        print(json.dumps({"tag": f"gemv_n{n}_q4_k_{m}x{k}", "weights": m * k,
+                          "arms": ["FMA stream", "matrix-core stream"]}), flush=True)
+        del x, out
+    del w
     n_expert, in_f, n_ff, n_used = 64, 4096, 2048, 8
     wg = to_dev(np.concatenate([gen.nvfp4_rows(n_ff, in_f, gen.SEED_MOE_W + 2 * e) for e in range(n_expert)]))
     wu = to_dev(np.concatenate([gen.nvfp4_rows(n_ff, in_f, gen.SEED_MOE_W + 2 * e + 1) for e in range(n_expert)]))
@@ -750,8 +798,8 @@ def run_stream_counter_workload():
             torch.cuda.synchronize()
             qmm.moe_gateup_probe("mathonly", wg, wu, ids, sc, x, n_expert, n_ff)
             torch.cuda.synchronize()
-        print(json.dumps({"tag": f"moe_gateup_t{t}", "weights": 2 * len(np.unique(ids_h)) * n_ff * in_f}),
-              flush=True)
+        print(json.dumps({"tag": f"moe_gateup_t{t}", "weights": 2 * len(np.unique(ids_h)) * n_ff * in_f,
+                          "arms": ["served", "load-only twin", "math-only twin"]}), flush=True)
 
 
 def stream_counter_summary(tags_path, csv_path, out_path):
@@ -767,41 +815,37 @@ def stream_counter_summary(tags_path, csv_path, out_path):
     vals = collections.defaultdict(lambda: collections.defaultdict(list))
     for r in csv.DictReader(open(csv_path)):
         name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("qmm::", "").strip()
-        if not name.startswith(("gemv_kernel", "loadonly_kernel", "moe_kernel")):
+        if not name.startswith(("gemv_kernel", "gemv_mfma_kernel", "loadonly_kernel", "moe_kernel")):
             continue
         key = (name, int(r["Grid_Size"]))
         if key not in vals:
             order.append(key)
         vals[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
-    # kernels in call order: gemv q4_k (served, load-only), gemv q6_k, then per t the MoE served,
-    # load-only and math-only twins
-    groups = {"gemv": [t for t in tags if t["tag"].startswith("gemv")],
-              "moe": [t for t in tags if t["tag"].startswith("moe")]}
-    labels = []
-    for t in groups["gemv"]:
-        labels += [(t, "served"), (t, "load-only twin")]
-    for t in groups["moe"]:
-        labels += [(t, "served"), (t, "load-only twin"), (t, "math-only twin")]
+    # distinct (kernel, grid) pairs in first-call order match the tags' arms in call order
+    labels = [(t, arm) for t in tags for arm in t["arms"]]
     with open(out_path, "w") as f:
-        f.write("# Streaming-kernel counters: n=1 GEMV and NVFP4 MoE gate/up with their twins\n\n"
+        f.write("# Streaming-kernel counters: the GEMV (n=1 with its load-only twin; n=4, 16 on both streams) "
+                "and the NVFP4 MoE gate/up with its twins\n\n"
                 "Commands (on one MI355X, from the repository root):\n\n"
                 "```\ncd /tmp && export TMPDIR=/tmp && cd \"$GRAFT_REPO_ROOT\"\n"
                 "rocprofv3 --pmc " + STREAM_COUNTER_SET + " --output-format csv -d gpurun_out/sw -o run -- "
                 "python3 bench.py --stream-counter-workload > gpurun_out/sw_tags.txt\n"
                 "python3 bench.py --stream-summary gpurun_out/sw_tags.txt gpurun_out/sw/run_counter_collection.csv "
                 "profiles/stream_counters.md\n```\n\n"
-                "Wave instructions per weight streamed (x 64 lanes / weights); VALU issue per SIMD = "
-                "SQ_INSTS_VALU x 4 cycles / 1024 SIMDs at 2.4 GHz (the VALU time if nothing else ran); the last "
-                "two columns as shares of SQ_WAVE_CYCLES.\n\n")
-        f.write("| config | arm | kernel | grid | waves | VALU / weight | LDS / weight | SALU / weight | "
+                "Wave instructions per weight of the matrix (x 64 lanes / weights; the MoE's weights are those of "
+                "its distinct experts, the n = 16 GEMV streams its weights twice, once per token group of 8); VALU counts the matrix-core instructions, MFMA lists them apart; VALU "
+                "issue per SIMD = SQ_INSTS_VALU x 4 cycles / 1024 SIMDs at 2.4 GHz (the VALU time if nothing "
+                "else ran); the last two columns as shares of SQ_WAVE_CYCLES.\n\n")
+        f.write("| config | arm | kernel | grid | VALU / weight | MFMA / weight | LDS / weight | SALU / weight | "
                 "VALU issue per SIMD (us) | VALU-active / wave cycles | wait-inst / wave cycles |\n"
                 "|---|---|---|---:|---:|---:|---:|---:|---:|---:|---:|\n")
         for (t, arm), key in zip(labels, order):
             c = {k: statistics.mean(v) for k, v in vals[key].items()}
             wgt = t["weights"]
             valu = c.get("SQ_INSTS_VALU", float("nan"))
-            f.write(f"| {t['tag']} | {arm} | `{key[0]}` | {key[1]} | {c.get('SQ_WAVES', 0):.0f} | "
-                    f"{64 * valu / wgt:.2f} | {64 * c.get('SQ_INSTS_LDS', 0) / wgt:.3f} | "
+            f.write(f"| {t['tag']} | {arm} | `{key[0]}` | {key[1]} | "
+                    f"{64 * valu / wgt:.2f} | {64 * c.get('SQ_INSTS_MFMA', 0) / wgt:.3f} | "
+                    f"{64 * c.get('SQ_INSTS_LDS', 0) / wgt:.3f} | "
                     f"{64 * c.get('SQ_INSTS_SALU', 0) / wgt:.3f} | {valu * 4 / 1024 / 2.4e3:.2f} | "
                     f"{c.get('SQ_ACTIVE_INST_VALU', 0) / c.get('SQ_WAVE_CYCLES', 1):.3f} | "
                     f"{c.get('SQ_WAIT_INST_ANY', 0) / c.get('SQ_WAVE_CYCLES', 1):.3f} |\n")
@@ -917,8 +961,9 @@ def pmc_summary(fetch_csv, write_csv, out_path):
         w = statistics.mean(write[name]) * fac["write"]
         short = name.replace("qmm::", "")
         kernels[short] = {"fetch_bytes": round(f), "write_bytes": round(w),
-                          "bytes_per_launch": round(f + w), "dispatches": len(fetch[name])}
-    tab = {"source_hash": kernel_source_hash(),
+                          "bytes_per_launch": round(f + w), "dispatches": len(fetch[name]),
+                          "tu": kernel_tu(short)}
+    tab = {"tu_hashes": tu_source_hashes(),
            "calibration": {"copy_bytes": COPY_PROBE_BYTES, "fetch_scale": round(fac["fetch"], 4),
                            "write_scale": round(fac["write"], 4)},
            "kernels": kernels}
