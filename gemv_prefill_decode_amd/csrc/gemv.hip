@@ -43,15 +43,17 @@ __global__ __launch_bounds__(64 * WPG) void gemv_kernel(float* __restrict__ dst,
     }
 }
 
-// The matrix-core stream: grid x = work groups, y = token groups of 4 * TT
-// rows, staged in LDS in the quad layout (qlds_floats(4 * TT, k, lm,
-// MTraits::RUN) floats, row stride mld).
-template <int QT, int TT, int R, int D, int WPG = 4>
-__global__ __launch_bounds__(64 * WPG) void gemv_mfma_kernel(float* __restrict__ dst,
-                                                             const uint8_t* __restrict__ w,
+// The matrix-core stream: grid x = work groups of WPG waves, y = token
+// groups of 4 * TT rows, staged in LDS in the quad layout (qlds_floats(4 *
+// TT, k, lm, MTraits::RUN) floats, row stride mld), then the KW-wave partial
+// sums (2 * WPG * 16 R TT floats).  The work group's WPG / KW row-group
+// slots take row groups blockIdx.x * (WPG / KW) + slot + j * gridDim.x *
+// (WPG / KW).
+template <int QT, int TT, int R, int D, int KW, int WPG>
+__global__ __launch_bounds__(64 * WPG) void gemv_mfma_kernel(float* __restrict__ dst, const uint8_t* __restrict__ w,
                                                              const float* __restrict__ x, int m, int k, int n,
                                                              int rb, int n_rg, int ldx, int ldd, int mld) {
-    constexpr int NTOK = 4 * TT;
+    constexpr int NTOK = 4 * TT, S = WPG / KW;
     const int wave = wave_id();
     const int tok0 = blockIdx.y * NTOK;
     const int ntok = min(NTOK, n - tok0);
@@ -67,8 +69,11 @@ __global__ __launch_bounds__(64 * WPG) void gemv_mfma_kernel(float* __restrict__
     };
     float* sx = qmm_dyn_lds;
     const XQuad<TT> xq = make_xquad<TT>(sx, mld, k, ntok);
-    mfma_stream<QT, TT, R, D>(g, blockIdx.x * WPG + wave, gridDim.x * WPG, n_rg, xq, store,
-                              make_qstage<NTOK, MTraits<QT>::RUN, 64 * WPG>(sx, xr, xoff, k, mld, ntok));
+    float* red = sx + qlds_floats(NTOK, k, MTraits<QT>::LM, MTraits<QT>::RUN);
+    const int wg_first = (int)blockIdx.x * S, stride = (int)gridDim.x * S;
+    const int n_iter = wg_first < n_rg ? (n_rg - wg_first + stride - 1) / stride : 0;  // the same for every wave
+    mfma_stream<QT, TT, R, D, KW>(g, wg_first + wave / KW, stride, n_rg, n_iter, wave % KW, red, xq, store,
+                                  make_qstage<NTOK, MTraits<QT>::RUN, 64 * WPG>(sx, xr, xoff, k, mld, ntok));
 }
 
 // ------------------------------------------------------------------ load-only twin
@@ -197,28 +202,40 @@ static void launch_gemv_nt(float* dst, const uint8_t* w, const float* x, int64_t
 }
 
 // The matrix-core stream with token groups of 4 * TT rows; false if they do
-// not fit one work group's LDS.
+// not fit one work group's LDS.  With at least four row groups per CU, one
+// wave per row group (KW = 1), 8-wave work groups where the
+// LDS holds at most two per CU, else 4-wave ones.  With fewer row groups and
+// rows of at least 4 unit iterations, KW = 4 or 8 waves share a row group
+// (one row group per work group at KW = 8), which costs a barrier per row
+// group but fills the CUs: 1024x4608 Q4_0, n = 4: 17.7 -> 7.8 us; on
+// 14336x4096 and 4608x1024 the barriers made it slower than KW = 1.
 template <int QT, int TT>
 static bool launch_gemv_mfma(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k, int64_t n,
                              int64_t rb, int64_t ldx, int64_t ldd, const GemvTuning& tune, hipStream_t st) {
     constexpr int R = 2, D = 2;
     const int lm = MTraits<QT>::LM;
-    const int64_t lds = (int64_t)qlds_floats(4 * TT, (int)k, lm, MTraits<QT>::RUN) * 4;
+    const int64_t lds = ((int64_t)qlds_floats(4 * TT, (int)k, lm, MTraits<QT>::RUN) + 2 * 8 * 16 * R * TT) * 4;  // partial sums sized for 8 waves
     if (lds > tune.lds_per_wg) return false;
     const int mld = qld((int)k, lm);
     const int64_t n_rg = (m + 4 * R - 1) / (4 * R);
     const int64_t gy = (n + 4 * TT - 1) / (4 * TT);
     const GemvTuning lt = lds_limited(tune, lds);
-    if (lt.wg_per_cu <= 2) {
-        // one or two work groups per CU: 8 waves share the staged rows
-        const dim3 grid(stream_grid(n_rg, gy, lt, 8), (unsigned)gy);
-        gemv_mfma_kernel<QT, TT, R, D, 8><<<grid, 512, (size_t)lds, st>>>(
+    const int64_t units = (k + GUnit<QT>::UE - 1) / GUnit<QT>::UE;
+    const int64_t upl = (units + 15) / 16;
+    const int kw = n_rg >= 4 * (int64_t)lt.num_cu || upl < 4 ? 1 : (upl < 8 ? 4 : 8);
+    auto go = [&](auto KWc, auto WPGc) {
+        constexpr int KW = decltype(KWc)::value, WPG = decltype(WPGc)::value;
+        const dim3 grid(stream_grid(n_rg, gy, lt, WPG / KW), (unsigned)gy);
+        gemv_mfma_kernel<QT, TT, R, D, KW, WPG><<<grid, 64 * WPG, (size_t)lds, st>>>(
             dst, w, x, (int)m, (int)k, (int)n, (int)rb, (int)n_rg, (int)ldx, (int)ldd, mld);
-    } else {
-        const dim3 grid(stream_grid(n_rg, gy, lt), (unsigned)gy);
-        gemv_mfma_kernel<QT, TT, R, D><<<grid, 256, (size_t)lds, st>>>(
-            dst, w, x, (int)m, (int)k, (int)n, (int)rb, (int)n_rg, (int)ldx, (int)ldd, mld);
-    }
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I4 = std::integral_constant<int, 4>;
+    using I8 = std::integral_constant<int, 8>;
+    if (kw == 4) go(I4{}, I8{});
+    else if (kw == 8) go(I8{}, I8{});
+    else if (lt.wg_per_cu <= 2) go(I1{}, I8{});
+    else go(I1{}, I4{});
     return true;
 }
 
@@ -230,8 +247,10 @@ int gemv_matrix_tokens(int64_t m, int64_t k, int64_t n, int qt, int kind, const 
     if (!use) return 0;
     const int lm = mtraits_lm(qt);
     const bool sums = qt_runs(qt);
-    if (n > 4 && tune.gemv_mfma_tt >= 2 && (int64_t)qlds_floats(8, (int)k, lm, sums) * 4 <= tune.lds_per_wg) return 8;
-    if ((int64_t)qlds_floats(4, (int)k, lm, sums) * 4 <= tune.lds_per_wg) return 4;
+    // the staged rows and the partial sums of launch_gemv_mfma (R = 2)
+    auto lds = [&](int tt) { return ((int64_t)qlds_floats(4 * tt, (int)k, lm, sums) + 2 * 8 * 16 * 2 * tt) * 4; };
+    if (n > 4 && tune.gemv_mfma_tt >= 2 && lds(2) <= tune.lds_per_wg) return 8;
+    if (lds(1) <= tune.lds_per_wg) return 4;
     return 0;
 }
 

@@ -205,13 +205,14 @@ __device__ __forceinline__ void moe_mchunk(const MoeArgs& a, int e, const int* p
     const XQuad<1> xq = make_xquad<1>(sx, a.mld, a.in_f, nreal);
     const auto st = make_qstage<NT, MTraits<QT>::RUN>(sx, xr, xoff, a.in_f, a.mld, nreal);
     const int first = blockIdx.x * 4 + wave, stride = gridDim.x * 4;
+    const int n_iter = first < a.n_rg_m ? (a.n_rg_m - first + stride - 1) / stride : 0;
     if constexpr (MODE == MOE_ACT) {
         const StreamGeom g1{a.w1 + (int64_t)e * n_ff * a.rb, n_ff, a.rb, a.in_f, 4};
-        mfma_stream<QT, 1, R, D>(g0, first, stride, a.n_rg_m, xq, store_gate, st);
-        mfma_stream<QT, 1, R, D>(g1, first, stride, a.n_rg_m, xq, store_act);
+        mfma_stream<QT, 1, R, D, 1>(g0, first, stride, a.n_rg_m, n_iter, 0, nullptr, xq, store_gate, st);
+        mfma_stream<QT, 1, R, D, 1>(g1, first, stride, a.n_rg_m, n_iter, 0, nullptr, xq, store_act);
     } else {
-        mfma_stream<QT, 1, R, D, decltype(store), std::decay_t<decltype(st)>, ARM>(g0, first, stride, a.n_rg_m, xq,
-                                                                                  store, st);
+        mfma_stream<QT, 1, R, D, 1, decltype(store), std::decay_t<decltype(st)>, ARM>(
+            g0, first, stride, a.n_rg_m, n_iter, 0, nullptr, xq, store, st);
     }
 }
 

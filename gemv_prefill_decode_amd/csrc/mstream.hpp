@@ -414,16 +414,23 @@ __device__ __forceinline__ void mcompute_item(GUnit<QT> (&un)[R], const typename
 }
 
 // Row groups of 4R rows (lane l takes rows (l & 3) * R + rr of the group, and
-// units (l >> 2) + 16 uu of them); items numbered as in gemv_stream, a ring
-// of D items of loads in flight, pre.issue()/pre.finish() around the first
-// loads.  store(row, j, value) is called by lanes 0..3 for token j = 4t + i
-// of every row (rows >= m too).  The quad whose unit lies past the row's end
-// loads nothing (zeros) and reads the zero block, so it adds exact zeros.
+// units (l >> 2) + 16 uu of them).  KW waves share a row group: wave kq of
+// the KW takes the unit iterations uu = kq, kq + KW, ... (V = ceil(upl/KW)
+// items per row group, those past upl dead), and at the row group's end the
+// KW partial sums meet in LDS (red: 2 * waves per work group * 16 R TT
+// floats, alternate halves per row group) and the kq = 0 wave adds them in
+// the order kq = 0, 1, ... and stores.  A work group's waves all run the
+// same n_iter row-group iterations (row groups past n_rg are dead: no loads,
+// no stores), so its barriers match.  A ring of D items of loads is in
+// flight; pre.issue()/pre.finish() go around the first loads.  store(row, j,
+// value) is called by lanes 0..3 for token j = 4t + i of every row of a live
+// row group (rows >= m too).  A quad whose unit lies past the row's end loads
+// nothing (zeros) and reads the zero block, so it adds exact zeros.
 // ARM: the measurement twins as in gemv_stream (load-only: the raw words
 // XORed into acc[rr][0][0]; math-only: the first item's unit for every item).
-template <int QT, int TT, int R, int D, typename Store, typename Pre = NoPre, int ARM = STREAM_SERVED>
-__device__ __forceinline__ void mfma_stream(const StreamGeom& g, int first_rg, int rg_stride, int n_rg,
-                                            const XQuad<TT>& xq, Store store, Pre pre = {}) {
+template <int QT, int TT, int R, int D, int KW, typename Store, typename Pre = NoPre, int ARM = STREAM_SERVED>
+__device__ __forceinline__ void mfma_stream(const StreamGeom& g, int first_rg, int rg_stride, int n_rg, int n_iter,
+                                            int kq, float* red, const XQuad<TT>& xq, Store store, Pre pre = {}) {
     using UT = GUnit<QT>;
     constexpr int LPR = 16;
     const int lane = threadIdx.x & 63;
@@ -431,11 +438,13 @@ __device__ __forceinline__ void mfma_stream(const StreamGeom& g, int first_rg, i
     const int RG = 4 * R;
     const int U = (g.k + UT::UE - 1) / UT::UE;
     const int upl = (U + LPR - 1) / LPR;
-    const int n_items = first_rg < n_rg ? (n_rg - first_rg + rg_stride - 1) / rg_stride * upl : 0;
+    const int V = (upl + KW - 1) / KW;
+    const int n_items = n_iter * V;
     const typename UT::Lane ln = UT::lane(gl);
     const uint32_t lane_row_off = (uint32_t)(slot * R) * (uint32_t)g.rb;
     const int e_step = LPR * UT::UE;
     const StreamGeom g16{g.w, g.m, g.rb, g.k, 4};  // the unit step of 16-lane groups
+    auto rg_live = [&](int q) { return first_rg + q * rg_stride < n_rg; };
 
     f32x4 acc[R][TT];
 #pragma unroll
@@ -452,42 +461,70 @@ __device__ __forceinline__ void mfma_stream(const StreamGeom& g, int first_rg, i
                 for (int t = 0; t < TT; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[rr][t][i] += __shfl_xor(acc[rr][t][i], off, 64);
-        if (lane < 4) {
-            const int64_t r0 = (int64_t)(first_rg + q * rg_stride) * RG + slot * R;
+        const int64_t r0 = (int64_t)(first_rg + q * rg_stride) * RG + slot * R;
+        if constexpr (KW == 1) {
+            if (rg_live(q) && lane < 4)
 #pragma unroll
-            for (int rr = 0; rr < R; ++rr)
+                for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-                for (int t = 0; t < TT; ++t)
+                    for (int t = 0; t < TT; ++t)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) store(r0 + rr, 4 * t + i, acc[rr][t][i]);
+                        for (int i = 0; i < 4; ++i) store(r0 + rr, 4 * t + i, acc[rr][t][i]);
+        } else {
+            constexpr int PW = 16 * R * TT;  // floats per wave: lanes 0..3, R*TT*4 each
+            const int wave = wave_id();
+            float* half = red + (q & 1) * (int)(blockDim.x >> 6) * PW;
+            if (lane < 4)
+#pragma unroll
+                for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                    for (int t = 0; t < TT; ++t)
+                        *(f32x4*)(half + wave * PW + lane * (4 * R * TT) + (rr * TT + t) * 4) = acc[rr][t];
+            __syncthreads();
+            if (kq == 0 && rg_live(q) && lane < 4) {
+#pragma unroll
+                for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) {
+                        f32x4 v = *(const f32x4*)(half + wave * PW + lane * (4 * R * TT) + (rr * TT + t) * 4);
+#pragma unroll
+                        for (int w = 1; w < KW; ++w)
+                            v += *(const f32x4*)(half + (wave + w) * PW + lane * (4 * R * TT) + (rr * TT + t) * 4);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) store(r0 + rr, 4 * t + i, v[i]);
+                    }
+            }
         }
 #pragma unroll
         for (int rr = 0; rr < R; ++rr)
 #pragma unroll
             for (int t = 0; t < TT; ++t) acc[rr][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
-    // loads of item (q, uu): a quad whose unit is past the row's end loads zeros
-    auto issue = [&](UT (&slot_un)[R], int q, int uu, bool live) {
-        issue_item<QT, R>(slot_un, g16, RG, lane_row_off, ln, first_rg + q * rg_stride, uu,
-                          ln.e + uu * e_step, live, gl + LPR * uu < U);
+    // loads of item (row-group iteration q, iteration v of this wave): unit
+    // uu = kq + KW v; dead items (row group past n_rg, or uu >= upl) load
+    // nothing, and a quad whose unit is past the row's end loads zeros
+    auto issue = [&](UT (&slot_un)[R], int q, int v, bool exists) {
+        const int uu = kq + KW * v;
+        issue_item<QT, R>(slot_un, g16, RG, lane_row_off, ln, first_rg + q * rg_stride, uu, ln.e + uu * e_step,
+                          exists && rg_live(q) && uu < upl, gl + LPR * uu < U);
     };
 
     UT ring[D][R];
     pre.issue();
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        const int q = d / upl, uu = d - q * upl;
-        issue(ring[d], q, uu, d < n_items);
+        const int q = d / V, v = d - q * V;
+        issue(ring[d], q, v, d < n_items);
     }
     pre.finish();
-    ItemPos cur{0, 0}, nxt{D / upl, D - (D / upl) * upl};
+    ItemPos cur{0, 0}, nxt{D / V, D - (D / V) * V};
     for (int base = 0; base < n_items; base += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int it = base + d;
-            const bool live = it < n_items;  // wave-uniform
-            const int q = cur.q, uu = cur.uu;
-            if (live) {
+            const bool exists = it < n_items;  // wave-uniform, the same for every wave of the work group
+            const int q = cur.q, v = cur.uu, uu = kq + KW * v;
+            if (exists && rg_live(q) && uu < upl) {
                 if constexpr (ARM == STREAM_LOADONLY) {
 #pragma unroll
                     for (int rr = 0; rr < R; ++rr)
@@ -499,9 +536,9 @@ __device__ __forceinline__ void mfma_stream(const StreamGeom& g, int first_rg, i
             }
             if constexpr (ARM == STREAM_MATHONLY) issue(ring[d], 0, 0, it + D < n_items);
             else issue(ring[d], nxt.q, nxt.uu, it + D < n_items);
-            if (live && uu == upl - 1) finish(q);
-            cur.next(upl);
-            nxt.next(upl);
+            if (exists && v == V - 1) finish(q);
+            cur.next(V);
+            nxt.next(V);
         }
     }
 }

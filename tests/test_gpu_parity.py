@@ -47,13 +47,16 @@ def test_gemv_parity(qt, n, path):
 @pytest.mark.parametrize("qt", QTS)
 @pytest.mark.parametrize("n", [4, 8])
 def test_gemv_matrix_long_rows(qt, n):
-    """k = 8192: four staged rows take one work group per CU (8 waves);
-    eight do not fit, so n = 8 runs as two token groups of four."""
+    """Long rows with few row groups: k = 8192, where four staged rows take
+    one work group per CU and eight do not fit (n = 8 runs as two token
+    groups of four), k = 4608 and k = 2048; with so few row groups 8 (4 for
+    the 4 unit iterations of k = 2048 at 32 weights per unit) waves share each
+    row group and add their partial sums in LDS."""
     import gemv_prefill_decode_amd as qmm
-    k = 8192
-    for si, m in enumerate((37, 1030)):
+    for si, (m, k) in enumerate(((37, 8192), (1030, 8192), (600, 4608), (300, 2048))):
         note(f"gemv_matrix long rows {qt} m={m} k={k} n={n}")
-        assert qmm.gemm_plan(m, k, n, qt, "gemv_matrix")["tokens_per_pass"] == 4
+        if k == 8192:
+            assert qmm.gemm_plan(m, k, n, qt, "gemv_matrix")["tokens_per_pass"] == 4
         w = weights(qt, m, k, 60 + si)
         x = acts(n, k, 60 + si)
         got = gpu_gemm(qt, w, x, m, "gemv_matrix")
