@@ -51,6 +51,8 @@ PEAK_F16_TFLOPS = 2516.6   # MI355X dense f16 MFMA
 # this build disables; the roof of the code built is the unpacked rate
 PEAK_F32_TFLOPS = 78.6
 PEAK_F32_PACKED_TFLOPS = 157.3
+# MI355X f32 matrix cores (v_mfma_f32_*): the roof of the GEMV's matrix-core stream
+PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 SHAPES = [("ffn_gate", 4608, 1024), ("ffn_down", 1024, 4608), ("conv_in", 3072, 1024),
           ("attn_out", 1024, 1024)]
@@ -305,11 +307,16 @@ def run_decode(args):
                 t = time_graph(g, L, 5)
                 del g
                 alg = wbytes + 4 * n * k + 4 * n * m
+                stream = qmm.gemm_plan(m, k, n, qt, "gemv")["stream"]
+                roof = PEAK_F32_MFMA_TFLOPS if stream == "matrix" else PEAK_F32_TFLOPS
                 ent[f"n{n}"] = {"us": round(t * 1e6, 2),
                                 "GB/s": round(alg / t / 1e9, 1),
                                 "frac_hbm_peak": round(alg / t / 1e9 / PEAK_HBM_GBS, 4),
                                 "TFLOP/s": round(2.0 * m * k * n / t / 1e12, 2),
-                                "frac_f32_unpacked_peak": round(2.0 * m * k * n / t / 1e12 / PEAK_F32_TFLOPS, 4)}
+                                "stream": stream,
+                                # f32 products: unpacked FMA (78.6) or f32 matrix cores (157.3)
+                                "f32_roof_TFLOP/s": roof,
+                                "frac_f32_roof": round(2.0 * m * k * n / t / 1e12 / roof, 4)}
             sink = torch.empty(m, dtype=torch.int32, device="cuda")
             g = capture([(lambda w=ws[i % copies]: qmm.stream_loadonly(w, m, k, qt, sink=sink))
                          for i in range(L)])

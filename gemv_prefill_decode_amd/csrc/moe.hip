@@ -216,7 +216,10 @@ __device__ __forceinline__ void moe_mchunk(const MoeArgs& a, int e, const int* p
     }
 }
 
-template <int QT, int R, int D, bool Q8, int MODE>
+// SINGLE: every chunk is one pair on the FMA stream (the launch for one
+// token, whose pairs go to distinct experts): the kernel then holds only
+// that path's registers, and more of its waves fit a SIMD.
+template <int QT, int R, int D, bool Q8, int MODE, bool SINGLE>
 __global__ __launch_bounds__(256) void moe_kernel(MoeArgs a) {
     __shared__ int plist[MOE_CHUNK];
     __shared__ int tlist[MOE_CHUNK];
@@ -269,6 +272,13 @@ __global__ __launch_bounds__(256) void moe_kernel(MoeArgs a) {
         }
         const int cnt = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
         __syncthreads();
+        if constexpr (SINGLE) {
+            for (int c0 = 0; c0 < cnt; ++c0) {
+                if (Q8 || a.xl) moe_chunk<QT, 1, R, D, true, Q8, MODE>(a, e, plist, tlist, c0, cnt);
+                else if constexpr (!Q8) moe_chunk<QT, 1, R, 2, false, Q8, MODE>(a, e, plist, tlist, c0, cnt);
+            }
+            continue;
+        }
         for (int c0 = 0; c0 < cnt;) {
             const int left = cnt - c0;
             if constexpr (!Q8) {
@@ -322,8 +332,10 @@ static void launch_moe_mode(MoeArgs a, int planes, const GemvTuning& tune, hipSt
         unsigned gx = stream_grid(n_rg, active, mt);
         const unsigned need = (unsigned)((n_rg + 3) / 4);
         if (gx < MOE_MIN_WG) gx = need < MOE_MIN_WG ? need : MOE_MIN_WG;
-        int64_t xbytes = Q8 ? (int64_t)q8lds_bytes(MOE_NT, a.in_f)
-                            : (int64_t)xlds_floats(MOE_NT, a.in_f, GUnit<QT>::RUNS > 0) * 4;
+        // one token: single-pair chunks (the SINGLE kernel), one staged row
+        const int ntc = a.t == 1 ? 1 : MOE_NT;
+        int64_t xbytes = Q8 ? (int64_t)q8lds_bytes(ntc, a.in_f)
+                            : (int64_t)xlds_floats(ntc, a.in_f, GUnit<QT>::RUNS > 0) * 4;
         a.xl = Q8 || xbytes <= XLDS_MAX_BYTES;
         if (!a.xl) xbytes = 0;
         // chunks of several pairs on the matrix-core stream: with more than
@@ -345,7 +357,7 @@ static void launch_moe_mode(MoeArgs a, int planes, const GemvTuning& tune, hipSt
             // groups (fewer row groups each) until it fits
             a.gbuf_off = (int)((xbytes + 15) / 16 * 4);
             auto gbytes = [&](unsigned w) {
-                const int64_t fma = (n_rg + 4 * (int64_t)w - 1) / (4 * (int64_t)w) * 4 * RG * MOE_NT * 4;
+                const int64_t fma = (n_rg + 4 * (int64_t)w - 1) / (4 * (int64_t)w) * 4 * RG * ntc * 4;
                 const int64_t mat = a.mt_min > 0 ? (n_rg_m + 4 * (int64_t)w - 1) / (4 * (int64_t)w) * 4 * RGM * MOE_MT * 4 : 0;
                 return fma > mat ? fma : mat;
             };
@@ -355,7 +367,8 @@ static void launch_moe_mode(MoeArgs a, int planes, const GemvTuning& tune, hipSt
         a.lpr_log2 = l;
         a.n_rg = (int)n_rg;
         const dim3 grid(gx, (unsigned)n_pairs, (unsigned)(MODE == MOE_ACT ? 1 : planes));
-        moe_kernel<QT, R, D, Q8, MODE><<<grid, 256, (size_t)lds, st>>>(a);
+        if (a.t == 1) moe_kernel<QT, R, D, Q8, MODE, true><<<grid, 256, (size_t)lds, st>>>(a);
+        else moe_kernel<QT, R, D, Q8, MODE, false><<<grid, 256, (size_t)lds, st>>>(a);
     }
 }
 
