@@ -216,11 +216,19 @@ __device__ __forceinline__ void moe_mchunk(const MoeArgs& a, int e, const int* p
     }
 }
 
-// SINGLE: every chunk is one pair on the FMA stream (the launch for one
-// token, whose pairs go to distinct experts): the kernel then holds only
-// that path's registers, and more of its waves fit a SIMD.
-template <int QT, int R, int D, bool Q8, int MODE, bool SINGLE>
+// Chunk paths compiled into a kernel (its registers are those of its
+// heaviest path, so fewer paths fit more waves per SIMD):
+// MOE_K_SINGLE: every chunk is one pair on the FMA stream (the launch for one
+//   token, whose pairs go to distinct experts);
+// MOE_K_LEAN: chunks of two or more pairs on the matrix-core stream, single
+//   pairs on the FMA stream (QMM_MOE_MFMA_MIN 1 or 2);
+// MOE_K_FULL: chunks of 1..3 pairs on the FMA stream, or on Q8_1 codes, and
+//   the matrix-core chunks from a.mt_min pairs up when it is set.
+enum : int { MOE_K_SINGLE = 0, MOE_K_LEAN = 1, MOE_K_FULL = 2 };
+
+template <int QT, int R, int D, bool Q8, int MODE, int KIND>
 __global__ __launch_bounds__(256) void moe_kernel(MoeArgs a) {
+    constexpr bool SINGLE = KIND == MOE_K_SINGLE;
     __shared__ int plist[MOE_CHUNK];
     __shared__ int tlist[MOE_CHUNK];
     __shared__ int wcnt[4];
@@ -276,6 +284,19 @@ __global__ __launch_bounds__(256) void moe_kernel(MoeArgs a) {
             for (int c0 = 0; c0 < cnt; ++c0) {
                 if (Q8 || a.xl) moe_chunk<QT, 1, R, D, true, Q8, MODE>(a, e, plist, tlist, c0, cnt);
                 else if constexpr (!Q8) moe_chunk<QT, 1, R, 2, false, Q8, MODE>(a, e, plist, tlist, c0, cnt);
+            }
+            continue;
+        }
+        if constexpr (KIND == MOE_K_LEAN && !Q8) {
+            for (int c0 = 0; c0 < cnt;) {
+                if (cnt - c0 >= a.mt_min) {
+                    moe_mchunk<QT, R, D, MODE>(a, e, plist, tlist, c0, cnt);
+                    c0 += MOE_MT;
+                } else {
+                    if (a.xl) moe_chunk<QT, 1, R, D, true, Q8, MODE>(a, e, plist, tlist, c0, cnt);
+                    else moe_chunk<QT, 1, R, 2, false, Q8, MODE>(a, e, plist, tlist, c0, cnt);
+                    ++c0;
+                }
             }
             continue;
         }
@@ -367,8 +388,10 @@ static void launch_moe_mode(MoeArgs a, int planes, const GemvTuning& tune, hipSt
         a.lpr_log2 = l;
         a.n_rg = (int)n_rg;
         const dim3 grid(gx, (unsigned)n_pairs, (unsigned)(MODE == MOE_ACT ? 1 : planes));
-        if (a.t == 1) moe_kernel<QT, R, D, Q8, MODE, true><<<grid, 256, (size_t)lds, st>>>(a);
-        else moe_kernel<QT, R, D, Q8, MODE, false><<<grid, 256, (size_t)lds, st>>>(a);
+        if (a.t == 1) moe_kernel<QT, R, D, Q8, MODE, MOE_K_SINGLE><<<grid, 256, (size_t)lds, st>>>(a);
+        else if (!Q8 && (a.mt_min == 1 || a.mt_min == 2))
+            moe_kernel<QT, R, D, Q8, MODE, MOE_K_LEAN><<<grid, 256, (size_t)lds, st>>>(a);
+        else moe_kernel<QT, R, D, Q8, MODE, MOE_K_FULL><<<grid, 256, (size_t)lds, st>>>(a);
     }
 }
 
