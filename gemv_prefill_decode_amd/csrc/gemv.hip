@@ -241,9 +241,18 @@ static bool launch_gemv_mfma(float* dst, const uint8_t* w, const float* x, int64
 
 // Token groups of the matrix-core stream: 8 rows where they fit (half the
 // passes over the weights) and n > 4, else 4 where they fit, else 0.
+// GEMV_AUTO takes it from n = gemv_mfma_min; below n = 8 only where it
+// measured faster than the FMA stream: at least four row groups of 8 rows
+// per CU (14336x4096, n = 4: 19.2 against 20.0 us) or rows of at least 4
+// unit iterations, which several waves then share (1024x4608 Q4_0: 7.8
+// against 9.4 us); on short rows with few row groups the FMA stream stays
+// (4608x1024 Q4_K, n = 4: 5.8 against 6.2 us).
 int gemv_matrix_tokens(int64_t m, int64_t k, int64_t n, int qt, int kind, const GemvTuning& tune) {
-    (void)m;
-    const bool use = kind == GEMV_MATRIX || (kind == GEMV_AUTO && tune.gemv_mfma_min > 0 && n >= tune.gemv_mfma_min);
+    const int64_t n_rg = (m + 7) / 8;
+    const int64_t upl = ((k + unit_elems_of(qt) - 1) / unit_elems_of(qt) + 15) / 16;
+    const bool wide = n >= 8 || n_rg >= 4 * (int64_t)tune.num_cu || upl >= 4;
+    const bool use = kind == GEMV_MATRIX ||
+                     (kind == GEMV_AUTO && tune.gemv_mfma_min > 0 && n >= tune.gemv_mfma_min && wide);
     if (!use) return 0;
     const int lm = mtraits_lm(qt);
     const bool sums = qt_runs(qt);

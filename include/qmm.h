@@ -91,7 +91,11 @@ typedef enum {
 typedef enum {
     QMM_PATH_AUTO = 0,     /* n <= qmm_gemv_max_n() -> GEMV, else MFMA       */
     QMM_PATH_GEMV = 1,     /* the f32 decode path, any n: GEMV_FMA for n below
-                              QMM_GEMV_MFMA_MIN (3), else GEMV_MATRIX          */
+                              QMM_GEMV_MFMA_MIN (3), GEMV_MATRIX from n = 8,
+                              between them GEMV_MATRIX where the weights have
+                              at least 4 row groups of 8 rows per CU or rows
+                              of at least 64 blocks' units (k >= 2048 at 32
+                              weights per unit), else GEMV_FMA               */
     QMM_PATH_MFMA = 2,     /* f16 MFMA tiles, f32 accumulation, any n (prefill) */
     QMM_PATH_GEMV_FMA = 3, /* the f32 decode path on f32 FMAs                  */
     QMM_PATH_GEMV_MATRIX = 4 /* the f32 decode path with its products on

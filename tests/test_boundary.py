@@ -239,13 +239,18 @@ def test_gemm_ws_rejects_a_workspace_overlapping_an_operand():
 
 def test_gemm_plan_reports_kernels():
     """qmm_gemm_plan: GEMV below the crossover (its FMA stream at n < 3, the
-    matrix-core stream above, with 8 activation rows per pass where they fit
-    the LDS, which at k = 1024 they do on any device), MFMA above; without a
+    matrix-core stream from n = 8 and, below, where the rows or row groups are
+    many, with 8 activation rows per pass where they fit the LDS, which at
+    k = 1024 they do on any device), MFMA above; without a
     workspace never a pre-pass or a k split; bad arguments give a status."""
     import gemv_prefill_decode_amd as qmm
     _lib()
     assert qmm.gemm_plan(4096, 1024, 8, "q4_k") == {"path": "gemv", "stream": "matrix", "tokens_per_pass": 8}
-    assert qmm.gemm_plan(4096, 1024, 4, "q4_k") == {"path": "gemv", "stream": "matrix", "tokens_per_pass": 4}
+    # below n = 8 the matrix-core stream only with many row groups or long rows
+    # (the CPU build sees the default 256 CUs)
+    assert qmm.gemm_plan(4096, 1024, 4, "q4_k") == {"path": "gemv", "stream": "fma", "tokens_per_pass": 0}
+    assert qmm.gemm_plan(16384, 1024, 4, "q4_k")["stream"] == "matrix"
+    assert qmm.gemm_plan(1024, 2048, 4, "q4_k")["stream"] == "matrix"
     assert qmm.gemm_plan(4096, 1024, 2, "q4_k") == {"path": "gemv", "stream": "fma", "tokens_per_pass": 0}
     assert qmm.gemm_plan(4096, 1024, 8, "q4_k", "gemv_fma")["stream"] == "fma"
     assert qmm.gemm_plan(4096, 1024, 1, "q4_k", "gemv_matrix")["tokens_per_pass"] == 4
