@@ -524,6 +524,49 @@ def test_split_k_shared_workspace_growing_tile_count():
         check_full(qt, w, x, m, k, n, got.cpu().numpy(), TAU_F16, f"shared ws {m}x{k}x{n}")
 
 
+def test_split_k_graph_replays():
+    """A k-split call (the GEMM kernel, then the sum of its partials)
+    captured in a HIP graph: every replay equals the eager result bit for
+    bit, with eager calls of another shape on the same workspace between the
+    replays, and the eager result matches the oracle."""
+    import torch
+    import gemv_prefill_decode_amd as qmm
+    qt, m, k, n = "q4_0", 1024, 1024, 512
+    p = qmm.gemm_plan(m, k, n, qt, "mfma")
+    assert p["n_split"] > 1, p
+    m2, k2, n2 = 640, 2048, 300
+    assert qmm.gemm_plan(m2, k2, n2, qt, "mfma")["n_split"] > 1
+    note(f"split-k graph {qt} {m}x{k} n={n} {p}")
+    w, x = weights(qt, m, k, 81), acts(n, k, 81)
+    w2, x2 = weights(qt, m2, k2, 82), acts(n2, k2, 82)
+    wd, xd, wd2, xd2 = to_dev(w), to_dev(x), to_dev(w2), to_dev(x2)
+    nbytes = max(qmm.workspace_bytes(m, k, n, qt, "mfma"), qmm.workspace_bytes(m2, k2, n2, qt, "mfma"))
+    ws = torch.full((nbytes,), 0x5A, dtype=torch.uint8, device="cuda")
+    eager = qmm.gemm(wd, xd, m, qt, path="mfma", workspace=ws).clone()
+    eager2 = qmm.gemm(wd2, xd2, m2, qt, path="mfma", workspace=ws).clone()
+    out = torch.empty_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        qmm.gemm(wd, xd, m, qt, path="mfma", out=out, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        qmm.gemm(wd, xd, m, qt, path="mfma", out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r} differs from the eager call"
+        other = qmm.gemm(wd2, xd2, m2, qt, path="mfma", workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(other, eager2), f"eager call after replay {r} differs"
+    del g
+    check_full(qt, w, x, m, k, n, eager.cpu().numpy(), TAU_F16, "split-k graph")
+    check_full(qt, w2, x2, m2, k2, n2, eager2.cpu().numpy(), TAU_F16, "split-k graph, other shape")
+
+
 # Every prefill kernel family, forced through QMM_MFMA_PLAN on a ragged shape
 # (m, n not multiples of any tile; k with a partial split): x16, tile rows
 # (wm*64), k splits, k groups.
