@@ -5,7 +5,7 @@
 // so the ring can be deep, and the k loop is a single rolled step.
 //
 // One work group of 4 waves computes a BM x BNT tile of dst (BM = 4*WR
-// weight rows, BNT = 128 or 256 tokens).  Wave w owns weight rows
+// weight rows, BNT = 64, 128 or 256 tokens).  Wave w owns weight rows
 // [w*WR, w*WR + WR) and all the tile's tokens; 256-token tiles halve the
 // decode work per matrix-core op.  Per step it decodes its rows' packed bytes from the LDS
 // stage straight into the A operands of v_mfma_f32_16x16x32_f16 (no decoded
@@ -661,7 +661,7 @@ static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t 
         if (blocks > 8192) blocks = 8192;
         x16_slot_kernel<QT><<<dim3((unsigned)blocks), 256, 0, st>>>(x16, x, (int)n, (int)k, (int)kp, (int)ldx);
     }
-    const int bm = 64 * pl.wm, bn = pl.x16 == 3 ? 256 : 128;
+    const int bm = 64 * pl.wm, bn = pl.x16 == 3 ? 256 : (pl.x16 == 5 ? 64 : 128);
     const int n_mb = (int)((m + bm - 1) / bm), n_nb = (int)((n + bn - 1) / bn);
     const dim3 grid((unsigned)(n_mb * n_nb * pl.n_split));
     // Item order: with the weight tile fastest, every token tile's XCDs read
@@ -671,7 +671,7 @@ static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t 
     const double w_bytes = (double)m * (double)rb, x_bytes = (double)n * (double)kp * (xf ? 4.0 : 2.0);
     const int nb_fast = (double)(n_nb - 1) * w_bytes > (double)((n_mb < 8 ? n_mb : 8) - 1) * x_bytes;
     // only shapes lds_ring_fits() accepts are planned
-    const int bnt = pl.x16 == 3 ? 256 : 128, wr = pl.x16 == 3 ? 32 : 16 * pl.wm;
+    const int bnt = bn, wr = pl.x16 == 3 ? 32 : 16 * pl.wm;
 #define QMM_LDS_LAUNCH(WR_, BN_, KG_, XF_)                                                                      \
     if constexpr (lds_ring::Geo<QT, WR_, BN_, KG_, XF_>::OK) {                                                  \
         if (wr == WR_ && bnt == BN_ && pl.kg == KG_ && xf == XF_)                                               \
@@ -679,6 +679,8 @@ static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t 
                 dst, w, x16, x, (int)ldx, (int)m, (int)k, (int)n, (int)rb, (int)kp, n_mb, n_nb, pl.n_split,     \
                 pl.sps, part, (int)ldd, nb_fast);                                                               \
     }
+    QMM_LDS_LAUNCH(16, 64, 1, false)
+    QMM_LDS_LAUNCH(16, 64, 2, false)
     QMM_LDS_LAUNCH(16, 128, 1, false)
     QMM_LDS_LAUNCH(16, 128, 2, false)
     QMM_LDS_LAUNCH(16, 128, 1, true)
@@ -699,6 +701,8 @@ static int per_cu_qt(int wr, int bnt, int kg, bool xf) {
     using namespace lds_ring;
 #define QMM_LDS_PER_CU(WR_, BN_, KG_, XF_) \
     if (xf == XF_ && wr == WR_ && bnt == BN_ && kg == KG_) return Geo<QT, WR_, BN_, KG_, XF_>::OK ? Geo<QT, WR_, BN_, KG_, XF_>::PER_CU : 0;
+    QMM_LDS_PER_CU(16, 64, 1, false)
+    QMM_LDS_PER_CU(16, 64, 2, false)
     QMM_LDS_PER_CU(16, 128, 1, false)
     QMM_LDS_PER_CU(16, 128, 2, false)
     QMM_LDS_PER_CU(16, 128, 1, true)

@@ -302,7 +302,7 @@ struct FamCost {
     double step_shared_us;
     int per_cu;
 };
-constexpr int N_FAM = 13;
+constexpr int N_FAM = 15;
 constexpr FamCost FAM_COST[N_FAM] = {
     {0, 2, 1, 1.50, 1.04, 2},  // gemm_mfma_kernel, 128 x 128, f32 activations
     {0, 2, 2, 1.06, 1.60, 1},  // gemm_mfma_kernel with 2 k groups (time per step of the item)
@@ -324,7 +324,20 @@ constexpr FamCost FAM_COST[N_FAM] = {
     {2, 1, 2, 0.43, 0.40, 1},
     {4, 1, 1, 0.65, 0.45, 1},
     {4, 1, 2, 0.51, 0.42, 1},
+    // 64 x 64 tiles on f16 activations (four times the work groups of
+    // 128 x 128 tiles; the decode work per matrix-core op doubles against
+    // 64 x 128, priced by format below)
+    {5, 1, 1, 0.273, 0.25, 1},
+    {5, 1, 2, 0.212, 0.215, 1},
 };
+// 64 x 64 tiles: step time by format against Q4_0 (each decoded weight meets
+// 64 tokens instead of 128, so the decode is a larger share of the step);
+// fitted with the two families above to 64 forced-plan timings of the LFM2
+// shapes (9% rms; Q8_0 raised from 1.26, where its k-split ffn_down plans
+// measured slower than the 128-token ones)
+constexpr double lds64_factor(int qt) {
+    return qt == QT_Q4_0 ? 1.0 : qt == QT_Q8_0 ? 1.33 : qt == QT_Q4_K ? 1.365 : qt == QT_Q6_K ? 1.884 : 1.245;
+}
 // The LDS-ring kernel's step time by format: Q6_K's two-field 6-bit codes
 // take about a quarter longer to decode; with 256-token tiles the decode is
 // a smaller share of the step.
@@ -361,16 +374,20 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
         const int x16 = FAM_COST[fam].x16, wm = FAM_COST[fam].wm, kg = FAM_COST[fam].kg;
         if (kg == 2 && qt == QT_F32) continue;  // its two register rings of f32 weights exceed 256 VGPRs
         // the LDS ring: whole 64-k steps only, and f32 rows fit it with 128-row tiles only
-        if (x16 >= 2 && (k % 64 != 0 || !lds_ring_fits(qt, 64 * wm, x16 == 3 ? 256 : 128, kg, x16 == 4))) continue;
+        const int bn = x16 == 3 ? 256 : (x16 == 5 ? 64 : 128);
+        if (x16 >= 2 && (k % 64 != 0 || !lds_ring_fits(qt, 64 * wm, bn, kg, x16 == 4))) continue;
+        // 64 x 64 tiles for products with fewer 64 x 128 tiles than CUs (the
+        // cost model mis-prices them where two work groups share most CUs)
+        if (x16 == 5 && !force && ((m + 63) / 64) * ((n + 127) / 128) >= num_cu) continue;
         if (force && (force->x16 != x16 || force->wm != wm || force->kg != kg)) continue;
         const FamCost& fc0 = FAM_COST[fam];
-        const double fmul = x16 == 4 && qt == QT_F32 ? LDS_F32_XF_FACTOR
+        const double fmul = x16 == 5                   ? lds64_factor(qt)
+                            : x16 == 4 && qt == QT_F32 ? LDS_F32_XF_FACTOR
                             : x16 < 2 || qt != QT_Q6_K
                                 ? 1.0
                                 : (x16 == 3 ? LDS_Q6K_FACTOR_256 : (kg == 2 ? LDS_Q6K_FACTOR_128_KG2 : LDS_Q6K_FACTOR_128));
-        const int per_cu = x16 >= 2 ? lds_ring_per_cu(qt, 64 * wm, x16 == 3 ? 256 : 128, kg, x16 == 4) : fc0.per_cu;
+        const int per_cu = x16 >= 2 ? lds_ring_per_cu(qt, 64 * wm, bn, kg, x16 == 4) : fc0.per_cu;
         const FamCost fc{x16, wm, kg, fc0.step_alone_us * fmul, fc0.step_shared_us * fmul, per_cu};
-        const int bn = x16 == 3 ? 256 : 128;
         const int64_t T = ((m + 64 * wm - 1) / (64 * wm)) * ((n + bn - 1) / bn);
         for (int S = 1; S <= 16 && (S == 1 || S <= nk / 2); ++S) {
             const int sps = ((nk + S - 1) / S + 1) & ~1;
@@ -392,7 +409,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
                                           : 0.0;
             const double cost = (LAUNCH_US + rounds * sps * step_t +
                                  (se > 1 ? SPLIT_US + (2.0 * se + 1.0) * out_bytes / BYTES_PER_US : 0.0) +
-                                 (x16 == 2 || x16 == 3 ? x16_us : 0.0) + xf_us);
+                                 (x16 == 2 || x16 == 3 || x16 == 5 ? x16_us : 0.0) + xf_us);
             if (cost < best_cost) {
                 best_cost = cost;
                 best.x16 = x16;
@@ -403,7 +420,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
             }
         }
     }
-    best.ws_bytes = (best.x16 == 2 || best.x16 == 3 ? x16_bytes(n, k) : 0) +
+    best.ws_bytes = (best.x16 == 2 || best.x16 == 3 || best.x16 == 5 ? x16_bytes(n, k) : 0) +
                     (best.n_split > 1 ? (int64_t)best.n_split * splitk_stride(n, m) * 4 : 0);
     if (best.ws_bytes == 0) best.ws_bytes = 256;  // a plan that uses no workspace still takes one
     return best;

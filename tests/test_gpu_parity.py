@@ -524,7 +524,7 @@ def test_split_k_shared_workspace_growing_tile_count():
         check_full(qt, w, x, m, k, n, got.cpu().numpy(), TAU_F16, f"shared ws {m}x{k}x{n}")
 
 
-def test_split_k_graph_replays():
+def test_split_k_graph_replays(monkeypatch):
     """A k-split call (the GEMM kernel, then the sum of its partials)
     captured in a HIP graph: every replay equals the eager result bit for
     bit, with eager calls of another shape on the same workspace between the
@@ -532,10 +532,11 @@ def test_split_k_graph_replays():
     import torch
     import gemv_prefill_decode_amd as qmm
     qt, m, k, n = "q4_0", 1024, 1024, 512
+    monkeypatch.setenv("QMM_MFMA_PLAN", "2,1,4,2")   # the LDS ring, k split 4, 2 k groups
     p = qmm.gemm_plan(m, k, n, qt, "mfma")
     assert p["n_split"] > 1, p
     m2, k2, n2 = 640, 2048, 300
-    assert qmm.gemm_plan(m2, k2, n2, qt, "mfma")["n_split"] > 1
+    assert qmm.gemm_plan(m2, k2, n2, qt, "mfma")["n_split"] > 1   # 2048 / 64 / 4 steps per split
     note(f"split-k graph {qt} {m}x{k} n={n} {p}")
     w, x = weights(qt, m, k, 81), acts(n, k, 81)
     w2, x2 = weights(qt, m2, k2, 82), acts(n2, k2, 82)
@@ -568,11 +569,12 @@ def test_split_k_graph_replays():
 
 
 # Every prefill kernel family, forced through QMM_MFMA_PLAN on a ragged shape
-# (m, n not multiples of any tile; k with a partial split): x16, tile rows
-# (wm*64), k splits, k groups.
+# (m, n not multiples of any tile; k with a partial split): x16 (5: 64-token
+# tiles), tile rows (wm*64), k splits, k groups.
 FORCED_PLANS = ["0,2,1,1", "0,2,3,1", "0,2,1,2", "0,2,3,2",
                 "2,2,1", "2,2,3", "2,4,1", "2,4,3", "3,2,1", "3,2,3", "2,2,1,2", "2,2,3,2", "3,2,1,2", "3,2,3,2",
-                "4,2,1", "4,2,3", "4,2,1,2", "4,2,3,2", "2,1,1", "2,1,3", "2,1,1,2", "4,1,1", "4,1,3,2"]
+                "4,2,1", "4,2,3", "4,2,1,2", "4,2,3,2", "2,1,1", "2,1,3", "2,1,1,2", "4,1,1", "4,1,3,2",
+                "5,1,1", "5,1,3", "5,1,1,2", "5,1,3,2"]
 
 
 @pytest.mark.parametrize("plan", FORCED_PLANS)
