@@ -189,9 +189,9 @@ def plan_kernel_name(plan: dict, qtype) -> str:
     if plan["path"] == "gemv":
         return "gemv_mfma_kernel" if plan["stream"] == "matrix" else "gemv_kernel"
     if plan["x16"] >= 2:
-        cols = 256 if plan["x16"] == 3 else 64 if plan["x16"] == 5 else 128
+        cols = 256 if plan["x16"] == 3 else 64 if plan["x16"] in (5, 6) else 128
         return (f"gemm_lds_kernel<{qt}, {plan['tile_rows'] // 4}, {cols}, "
-                f"{plan['k_groups']}, {'true' if plan['x16'] == 4 else 'false'}>")
+                f"{plan['k_groups']}, {'true' if plan['x16'] in (4, 6) else 'false'}>")
     return f"gemm_mfma_kernel<{qt}, {plan['k_groups']}>"
 
 

@@ -80,9 +80,10 @@ template <int QT, int WR, int BNT, int KG, bool XF = false> struct Geo {
     static constexpr int XL = 2 * XC;                   // XF: its 16-byte f32 loads per step
     // runnable: a ring of at least 2 rounds, its waits within vmcnt's range,
     // (KG = 2) room for group 1's accumulators in the ring's LDS, and (XF)
-    // 128-token tiles with at most 3 rounds (the waits below assume them)
+    // 64- or 128-token tiles with at most 3 rounds (the waits below assume them)
     static constexpr bool OK = NR >= 2 && (NR - 2) * (DA + DB + XL) <= 63 &&
-                               (KG == 1 || NS * STAGE >= BM * BNT * 4) && (!XF || (BNT == 128 && NR <= 3));
+                               (KG == 1 || NS * STAGE >= BM * BNT * 4) &&
+                               (!XF || ((BNT == 128 || BNT == 64) && NR <= 3));
 };
 
 // k of slot s = 32*ks + 8*g + i of step kt (see the file comment).
@@ -652,7 +653,7 @@ template <int QT>
 static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k, int64_t n,
                           int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd, hipStream_t st) {
     const int64_t kp = x16_row_halves(k);
-    const bool xf = pl.x16 == 4;  // f32 activations straight into the ring: no pre-pass
+    const bool xf = pl.x16 == 4 || pl.x16 == 6;  // f32 activations straight into the ring: no pre-pass
     uint16_t* x16 = (uint16_t*)ws;
     float* part = xf ? (float*)ws : (float*)((uint8_t*)ws + x16_bytes(n, k));
     if (!xf) {
@@ -661,7 +662,7 @@ static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t 
         if (blocks > 8192) blocks = 8192;
         x16_slot_kernel<QT><<<dim3((unsigned)blocks), 256, 0, st>>>(x16, x, (int)n, (int)k, (int)kp, (int)ldx);
     }
-    const int bm = 64 * pl.wm, bn = pl.x16 == 3 ? 256 : (pl.x16 == 5 ? 64 : 128);
+    const int bm = 64 * pl.wm, bn = pl.x16 == 3 ? 256 : (pl.x16 == 5 || pl.x16 == 6 ? 64 : 128);
     const int n_mb = (int)((m + bm - 1) / bm), n_nb = (int)((n + bn - 1) / bn);
     const dim3 grid((unsigned)(n_mb * n_nb * pl.n_split));
     // Item order: with the weight tile fastest, every token tile's XCDs read
@@ -681,6 +682,8 @@ static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t 
     }
     QMM_LDS_LAUNCH(16, 64, 1, false)
     QMM_LDS_LAUNCH(16, 64, 2, false)
+    QMM_LDS_LAUNCH(16, 64, 1, true)
+    QMM_LDS_LAUNCH(16, 64, 2, true)
     QMM_LDS_LAUNCH(16, 128, 1, false)
     QMM_LDS_LAUNCH(16, 128, 2, false)
     QMM_LDS_LAUNCH(16, 128, 1, true)
@@ -703,6 +706,8 @@ static int per_cu_qt(int wr, int bnt, int kg, bool xf) {
     if (xf == XF_ && wr == WR_ && bnt == BN_ && kg == KG_) return Geo<QT, WR_, BN_, KG_, XF_>::OK ? Geo<QT, WR_, BN_, KG_, XF_>::PER_CU : 0;
     QMM_LDS_PER_CU(16, 64, 1, false)
     QMM_LDS_PER_CU(16, 64, 2, false)
+    QMM_LDS_PER_CU(16, 64, 1, true)
+    QMM_LDS_PER_CU(16, 64, 2, true)
     QMM_LDS_PER_CU(16, 128, 1, false)
     QMM_LDS_PER_CU(16, 128, 2, false)
     QMM_LDS_PER_CU(16, 128, 1, true)

@@ -302,7 +302,7 @@ struct FamCost {
     double step_shared_us;
     int per_cu;
 };
-constexpr int N_FAM = 15;
+constexpr int N_FAM = 17;
 constexpr FamCost FAM_COST[N_FAM] = {
     {0, 2, 1, 1.50, 1.04, 2},  // gemm_mfma_kernel, 128 x 128, f32 activations
     {0, 2, 2, 1.06, 1.60, 1},  // gemm_mfma_kernel with 2 k groups (time per step of the item)
@@ -329,7 +329,13 @@ constexpr FamCost FAM_COST[N_FAM] = {
     // 64 x 128, priced by format below)
     {5, 1, 1, 0.273, 0.25, 1},
     {5, 1, 2, 0.212, 0.215, 1},
+    // ... and on the f32 activations (no pre-pass; fitted to 55 more timings,
+    // 7% rms)
+    {6, 1, 1, 0.329, 0.224, 1},
+    {6, 1, 2, 0.233, 0.197, 1},
 };
+// f32 weights on the 64 x 64 f32-activation family, on top of lds64_factor
+constexpr double LDS64_F32_XF_FACTOR = 1.15;
 // 64 x 64 tiles: step time by format against Q4_0 (each decoded weight meets
 // 64 tokens instead of 128, so the decode is a larger share of the step);
 // fitted with the two families above to 64 forced-plan timings of the LFM2
@@ -374,19 +380,21 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
         const int x16 = FAM_COST[fam].x16, wm = FAM_COST[fam].wm, kg = FAM_COST[fam].kg;
         if (kg == 2 && qt == QT_F32) continue;  // its two register rings of f32 weights exceed 256 VGPRs
         // the LDS ring: whole 64-k steps only, and f32 rows fit it with 128-row tiles only
-        const int bn = x16 == 3 ? 256 : (x16 == 5 ? 64 : 128);
-        if (x16 >= 2 && (k % 64 != 0 || !lds_ring_fits(qt, 64 * wm, bn, kg, x16 == 4))) continue;
+        const int bn = x16 == 3 ? 256 : (x16 == 5 || x16 == 6 ? 64 : 128);
+        const bool xf = x16 == 4 || x16 == 6;
+        if (x16 >= 2 && (k % 64 != 0 || !lds_ring_fits(qt, 64 * wm, bn, kg, xf))) continue;
         // 64 x 64 tiles for products with fewer 64 x 128 tiles than CUs (the
         // cost model mis-prices them where two work groups share most CUs)
-        if (x16 == 5 && !force && ((m + 63) / 64) * ((n + 127) / 128) >= num_cu) continue;
+        if ((x16 == 5 || x16 == 6) && !force && ((m + 63) / 64) * ((n + 127) / 128) >= num_cu) continue;
         if (force && (force->x16 != x16 || force->wm != wm || force->kg != kg)) continue;
         const FamCost& fc0 = FAM_COST[fam];
         const double fmul = x16 == 5                   ? lds64_factor(qt)
+                            : x16 == 6                 ? lds64_factor(qt) * (qt == QT_F32 ? LDS64_F32_XF_FACTOR : 1.0)
                             : x16 == 4 && qt == QT_F32 ? LDS_F32_XF_FACTOR
                             : x16 < 2 || qt != QT_Q6_K
                                 ? 1.0
                                 : (x16 == 3 ? LDS_Q6K_FACTOR_256 : (kg == 2 ? LDS_Q6K_FACTOR_128_KG2 : LDS_Q6K_FACTOR_128));
-        const int per_cu = x16 >= 2 ? lds_ring_per_cu(qt, 64 * wm, bn, kg, x16 == 4) : fc0.per_cu;
+        const int per_cu = x16 >= 2 ? lds_ring_per_cu(qt, 64 * wm, bn, kg, xf) : fc0.per_cu;
         const FamCost fc{x16, wm, kg, fc0.step_alone_us * fmul, fc0.step_shared_us * fmul, per_cu};
         const int64_t T = ((m + 64 * wm - 1) / (64 * wm)) * ((n + bn - 1) / bn);
         for (int S = 1; S <= 16 && (S == 1 || S <= nk / 2); ++S) {
@@ -404,7 +412,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
             const double step_t = step > fc.step_alone_us ? step : fc.step_alone_us;
             double rounds = (double)items / (double)(num_cu * share);
             if (share == 1 || rounds < 1.0) rounds = (double)((items + num_cu * share - 1) / (num_cu * share));
-            const double xf_us = x16 == 4 && qt != QT_F32 ? 2.0 * (double)n * (double)k * (double)((m + 64 * wm - 1) / (64 * wm)) /
+            const double xf_us = xf && qt != QT_F32 ? 2.0 * (double)n * (double)k * (double)((m + 64 * wm - 1) / (64 * wm)) /
                                                  XF_L2_BYTES_PER_US
                                           : 0.0;
             const double cost = (LAUNCH_US + rounds * sps * step_t +

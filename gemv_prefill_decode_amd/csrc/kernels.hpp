@@ -48,7 +48,8 @@ int gemv_matrix_tokens(int64_t m, int64_t k, int64_t n, int qt, int kind, const 
 // its own pre-pass, weight bytes and activations streamed through an LDS
 // ring; k % 64 == 0 only); x16 = 3: the same kernel with 128 x 256 tiles
 // (wm = 2); x16 = 5: with 64 x 64 tiles (wm = 1: twice the work groups of
-// 64 x 128 tiles for products of few tiles).  x16 = 4: the same kernel with 128 x 128 tiles reading the f32
+// 64 x 128 tiles for products of few tiles); x16 = 6: 64 x 64 tiles on the
+// f32 activations (as x16 = 4).  x16 = 4: the same kernel with 128 x 128 tiles reading the f32
 // activations into its ring and rounding them as it reads (no pre-pass, no
 // f16 workspace).  kg = 2: two groups of 4 waves take alternate k steps of
 // each tile.  Any of them may split k into n_split ranges of sps steps (64 k

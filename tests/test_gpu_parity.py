@@ -569,12 +569,12 @@ def test_split_k_graph_replays(monkeypatch):
 
 
 # Every prefill kernel family, forced through QMM_MFMA_PLAN on a ragged shape
-# (m, n not multiples of any tile; k with a partial split): x16 (5: 64-token
+# (m, n not multiples of any tile; k with a partial split): x16 (5, 6: 64-token
 # tiles), tile rows (wm*64), k splits, k groups.
 FORCED_PLANS = ["0,2,1,1", "0,2,3,1", "0,2,1,2", "0,2,3,2",
                 "2,2,1", "2,2,3", "2,4,1", "2,4,3", "3,2,1", "3,2,3", "2,2,1,2", "2,2,3,2", "3,2,1,2", "3,2,3,2",
                 "4,2,1", "4,2,3", "4,2,1,2", "4,2,3,2", "2,1,1", "2,1,3", "2,1,1,2", "4,1,1", "4,1,3,2",
-                "5,1,1", "5,1,3", "5,1,1,2", "5,1,3,2"]
+                "5,1,1", "5,1,3", "5,1,1,2", "5,1,3,2", "6,1,1", "6,1,3", "6,1,1,2", "6,1,3,2"]
 
 
 @pytest.mark.parametrize("plan", FORCED_PLANS)
