@@ -383,9 +383,14 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
         const int bn = x16 == 3 ? 256 : (x16 == 5 || x16 == 6 ? 64 : 128);
         const bool xf = x16 == 4 || x16 == 6;
         if (x16 >= 2 && (k % 64 != 0 || !lds_ring_fits(qt, 64 * wm, bn, kg, xf))) continue;
-        // 64 x 64 tiles for products with fewer 64 x 128 tiles than CUs (the
-        // cost model mis-prices them where two work groups share most CUs)
-        if ((x16 == 5 || x16 == 6) && !force && ((m + 63) / 64) * ((n + 127) / 128) >= num_cu) continue;
+        // 64 x 64 tiles for products with fewer 64 x 128 tiles than CUs; with
+        // more (two work groups sharing most CUs) the cost model under-prices
+        // the two-k-group forms and the Q6_K and f32 rows, so there only the
+        // one-group f16-activation form, for the cheaper decodes (measured
+        // faster on LFM2 ffn_gate: Q4_0 19.5 -> 17.5 us, Q4_K 22.5 -> 20.6)
+        if ((x16 == 5 || x16 == 6) && !force && ((m + 63) / 64) * ((n + 127) / 128) >= num_cu &&
+            (x16 == 6 || kg != 1 || qt == QT_Q6_K || qt == QT_F32))
+            continue;
         if (force && (force->x16 != x16 || force->wm != wm || force->kg != kg)) continue;
         const FamCost& fc0 = FAM_COST[fam];
         const double fmul = x16 == 5                   ? lds64_factor(qt)
