@@ -667,7 +667,7 @@ PLAN_SHAPES = [("ffn_gate", 4608, 1024, 512), ("ffn_down", 1024, 4608, 512), ("c
                ("q4_0_1024_n64", 1024, 1024, 64)]
 # forced prefill plans compared with the planned one (QMM_MFMA_PLAN codes)
 PLAN_FAMILIES = ["0,2,1,2", "2,2,1", "2,2,1,2", "3,2,1", "3,2,1,2", "4,2,1,2", "2,1,1", "2,1,1,2", "4,1,1,2",
-                 "4,1,4,2"]
+                 "4,1,4,2", "5,1,1", "5,1,1,2", "6,1,1,2", "6,1,2,2"]
 
 
 def run_prefill_plans(families=None, shapes=None):
