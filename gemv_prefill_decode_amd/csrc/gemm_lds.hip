@@ -231,7 +231,32 @@ template <> struct Dec<QT_Q8_0> {
     }
 };
 
-// 8 weights D*q - M for the nibbles or bytes of q0 (elements 0..3) and q1 (4..7)
+// 8 weights D*q - M.  The codes come as f16 halves holding q itself, i.e.
+// the subnormal q * 2^-24 (exact): e0 = codes 0 and 2, o0 = codes 1 and 3,
+// e1, o1 the same for codes 4..7 (a mask cuts two codes out of four packed
+// bytes at once).  D24 = D * 2^24, so D24 * (q * 2^-24) = D * q exactly and
+// the multiply-add, one v_fma_mix*_f16 per weight reading its f16 half
+// directly, rounds once to f16.
+__device__ __forceinline__ f16x8 affine8h(uint32_t e0, uint32_t o0, uint32_t e1, uint32_t o1, float D24,
+                                          float Mneg) {
+    const f16x2 a = __builtin_bit_cast(f16x2, e0), b = __builtin_bit_cast(f16x2, o0);
+    const f16x2 c = __builtin_bit_cast(f16x2, e1), d = __builtin_bit_cast(f16x2, o1);
+    f16x8 r;
+    r[0] = (_Float16)__builtin_fmaf(D24, (float)a[0], Mneg);
+    r[1] = (_Float16)__builtin_fmaf(D24, (float)b[0], Mneg);
+    r[2] = (_Float16)__builtin_fmaf(D24, (float)a[1], Mneg);
+    r[3] = (_Float16)__builtin_fmaf(D24, (float)b[1], Mneg);
+    r[4] = (_Float16)__builtin_fmaf(D24, (float)c[0], Mneg);
+    r[5] = (_Float16)__builtin_fmaf(D24, (float)d[0], Mneg);
+    r[6] = (_Float16)__builtin_fmaf(D24, (float)c[1], Mneg);
+    r[7] = (_Float16)__builtin_fmaf(D24, (float)d[1], Mneg);
+    return r;
+}
+constexpr float TWO24 = 16777216.0f;
+
+// 8 weights D*q - M for the bytes of q0 (elements 0..3) and q1 (4..7), each
+// byte converted by v_cvt_f32_ubyteN (Q6_K's 6-bit codes: one instruction
+// per code, where cutting f16 halves out of the packed bytes costs as much)
 __device__ __forceinline__ f16x8 affine8(uint32_t q0, uint32_t q1, float D, float Mneg) {
     float v[8];
 #pragma unroll
@@ -253,20 +278,28 @@ template <> struct Dec<QT_Q4_K> {
         // A = sc[jj], B = sc[jj + 4], C = sc[jj + 8]: for j < 4 the scale is
         // A & 63 and the min B & 63; for j >= 4 the scale is
         // (C & 15) | (A >> 6) << 4 and the min (C >> 4) | (B >> 6) << 4.
-        const int c = kt & 3;
+        const int c = kt & 3;  // the same for the whole wave
         const uint32_t sh0 = 16u * (uint32_t)(c & 1);  // byte jj0 = 2(c & 1), jj1 = jj0 + 1
         const uint32_t A = hdr.y >> sh0, B = hdr.z >> sh0, C = hdr.w >> sh0;
-        // all ones for c < 2, else zero
-        const uint32_t lo = (uint32_t)(-(int)(c < 2));
-        auto blend = [lo](uint32_t a, uint32_t b) { return (a & lo) | (b & ~lo); };
-        const uint32_t s0 = blend(A & 63u, (C & 15u) | (((A >> 6) & 3u) << 4));
-        const uint32_t m0 = blend(B & 63u, ((C >> 4) & 15u) | (((B >> 6) & 3u) << 4));
-        const uint32_t s1 = blend((A >> 8) & 63u, ((C >> 8) & 15u) | (((A >> 14) & 3u) << 4));
-        const uint32_t m1 = blend((B >> 8) & 63u, ((C >> 12) & 15u) | (((B >> 14) & 3u) << 4));
-        const float D0 = d * (float)s0, M0 = dmin * (float)m0;
-        const float D1 = d * (float)s1, M1 = dmin * (float)m1;
-        a0 = affine8(q.x & 0x0F0F0F0Fu, q.y & 0x0F0F0F0Fu, D0, -M0);
-        a1 = affine8((q.x >> 4) & 0x0F0F0F0Fu, (q.y >> 4) & 0x0F0F0F0Fu, D1, -M1);
+        uint32_t s0, m0, s1, m1;
+        if (c < 2) {
+            s0 = A & 63u;
+            m0 = B & 63u;
+            s1 = (A >> 8) & 63u;
+            m1 = (B >> 8) & 63u;
+        } else {
+            s0 = (C & 15u) | (((A >> 6) & 3u) << 4);
+            m0 = ((C >> 4) & 15u) | (((B >> 6) & 3u) << 4);
+            s1 = ((C >> 8) & 15u) | (((A >> 14) & 3u) << 4);
+            m1 = ((C >> 12) & 15u) | (((B >> 14) & 3u) << 4);
+        }
+        const float d24 = d * TWO24;
+        const float D0 = d24 * (float)s0, M0 = dmin * (float)m0;
+        const float D1 = d24 * (float)s1, M1 = dmin * (float)m1;
+        // low nibbles: elements 0..7 of the step's first 32; high: of its second
+        constexpr uint32_t N2 = 0x000F000Fu;
+        a0 = affine8h(q.x & N2, (q.x >> 8) & N2, q.y & N2, (q.y >> 8) & N2, D0, -M0);
+        a1 = affine8h((q.x >> 4) & N2, (q.x >> 12) & N2, (q.y >> 4) & N2, (q.y >> 12) & N2, D1, -M1);
     }
 };
 
