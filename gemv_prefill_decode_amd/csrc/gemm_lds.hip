@@ -254,18 +254,9 @@ __device__ __forceinline__ f16x8 affine8h(uint32_t e0, uint32_t o0, uint32_t e1,
 }
 constexpr float TWO24 = 16777216.0f;
 
-// 8 weights D*q - M for the bytes of q0 (elements 0..3) and q1 (4..7), each
-// byte converted by v_cvt_f32_ubyteN (Q6_K's 6-bit codes: one instruction
-// per code, where cutting f16 halves out of the packed bytes costs as much)
-__device__ __forceinline__ f16x8 affine8(uint32_t q0, uint32_t q1, float D, float Mneg) {
-    float v[8];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        v[b] = __builtin_fmaf(D, ubyte_f32(q0, b), Mneg);
-        v[4 + b] = __builtin_fmaf(D, ubyte_f32(q1, b), Mneg);
-    }
-    return frag4(pack_f2h(v[0], v[1]), pack_f2h(v[2], v[3]), pack_f2h(v[4], v[5]), pack_f2h(v[6], v[7]));
-}
+// Bytes 1 and 3 of v as the low bytes of two halves (high bytes zero): one
+// v_perm_b32 (selector 0x0c gives a zero byte)
+__device__ __forceinline__ uint32_t odd_bytes(uint32_t v) { return __builtin_amdgcn_perm(0u, v, 0x0c030c01u); }
 
 template <> struct Dec<QT_Q4_K> {
     __device__ __forceinline__ static void run(const uint8_t* row, uint32_t, int kt, int g, int,
@@ -328,8 +319,10 @@ template <> struct Dec<QT_Q6_K> {
         const uint32_t ql1 = (l1 & 0x0F0F0F0Fu) | (((h1 >> hs) & 0x03030303u) << 4);
         const uint32_t qh0 = ((l0 >> 4) & 0x0F0F0F0Fu) | (((h0 >> (hs + 4)) & 0x03030303u) << 4);
         const uint32_t qh1 = ((l1 >> 4) & 0x0F0F0F0Fu) | (((h1 >> (hs + 4)) & 0x03030303u) << 4);
-        a0 = affine8(ql0, ql1, Dl, -32.0f * Dl);
-        a1 = affine8(qh0, qh1, Dh, -32.0f * Dh);
+        // one 6-bit code per byte: even bytes by a mask, odd ones by a permute
+        constexpr uint32_t B2 = 0x00FF00FFu;
+        a0 = affine8h(ql0 & B2, odd_bytes(ql0), ql1 & B2, odd_bytes(ql1), Dl * TWO24, -32.0f * Dl);
+        a1 = affine8h(qh0 & B2, odd_bytes(qh0), qh1 & B2, odd_bytes(qh1), Dh * TWO24, -32.0f * Dh);
     }
 };
 
