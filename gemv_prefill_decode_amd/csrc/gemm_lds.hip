@@ -519,15 +519,15 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
     auto bfrag = [&](const uint8_t* bt, int ks) -> f16x8 { return *(const f16x8*)(bt + (ks ? bsw ^ 64 : bsw)); };
     constexpr int BROW = 128;  // bytes of one token row of a stage
 
+#pragma unroll
+    for (int p = 0; p < NR - 1; ++p) issue(p, p);
     if constexpr (XF) {
-        // round 0's activations into stage 0 before any weight load, then
-        // round 1's in flight behind the first rounds' weight loads
+        // round 0's activations in flight with the first rounds' weights
+        // (their store waits for all of them), then round 1's
         xload(0);
         xstore(0);
         xload(1);
     }
-#pragma unroll
-    for (int p = 0; p < NR - 1; ++p) issue(p, p);
 
     const int nrounds = (nk - s0 + KG - 1) / KG;
     int cur = 0;
@@ -536,10 +536,11 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
         // flight), its LDS reads of round r-1 and writes of round r's
         // activations are done; then every wave's.  Loads issued after round
         // r's weights: rounds r+1 .. r+NR-2 of them, and (XF) the activations
-        // of rounds r+2 .. r+NR-1, except at r = 0, where round 1's
-        // activations went out before all weight loads.
+        // of rounds r+2 .. r+NR-1, except at r = 0, where the first rounds'
+        // weights and round 0's activations have landed before round 0's
+        // activation store.
         if (XF && r == 0)
-            lds_ring::waitcnt<(NR - 2) * DA, 0>();
+            lds_ring::waitcnt<G::XL, 0>();
         else
             lds_ring::waitcnt<(NR - 2) * (DA + DB + G::XL), 0>();
         asm volatile("" ::: "memory");
