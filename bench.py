@@ -129,8 +129,8 @@ def plan_grid_size(plan, m, n):
     """Work-items of the GEMM kernel a qmm_gemm_plan() result launches (the
     Grid_Size the profiler records for that dispatch)."""
     x16, rows, kg, split = plan["x16"], plan["tile_rows"], plan["k_groups"], plan["n_split"]
-    cols = 256 if x16 == 3 else 64 if x16 in (5, 6) else 128
-    threads = 256 * kg
+    cols = 256 if x16 in (3, 7) else 64 if x16 in (5, 6) else 128
+    threads = 512 if x16 == 7 else 256 * kg
     groups = -(-m // rows) * -(-n // cols) * split
     return groups * threads
 

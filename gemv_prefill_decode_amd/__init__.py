@@ -188,6 +188,8 @@ def plan_kernel_name(plan: dict, qtype) -> str:
     qt = _qt(qtype)
     if plan["path"] == "gemv":
         return "gemv_mfma_kernel" if plan["stream"] == "matrix" else "gemv_kernel"
+    if plan["x16"] == 7:
+        return f"gemm_lds_tg_kernel<{qt}, 64, 256>"
     if plan["x16"] >= 2:
         cols = 256 if plan["x16"] == 3 else 64 if plan["x16"] in (5, 6) else 128
         return (f"gemm_lds_kernel<{qt}, {plan['tile_rows'] // 4}, {cols}, "

@@ -386,21 +386,29 @@ __global__ __launch_bounds__(256) void x16_slot_kernel(uint16_t* __restrict__ x1
 // and after the round's barrier writes them, rounded to f16 (nearest even),
 // where the buffer-to-LDS loads would have put the pre-pass's rows: every
 // activation is converted once per work group and no pre-pass runs.
-template <int QT, int WR, int BNT, int KG, bool XF>
-__global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict__ dst, const uint8_t* __restrict__ w,
-                                                               const uint16_t* __restrict__ x16,
-                                                               const float* __restrict__ x, int ldx, int m, int k,
-                                                               int n, int rb, int kp, int n_mb, int n_nb, int n_split,
-                                                               int sps, float* __restrict__ partial, int ldd,
-                                                               int nb_fast) {
+// TG = 2 (8 waves, one k group): the two halves of the tile's tokens go to
+// two sets of 4 waves that share every stage; wave w of each set decodes the
+// same rows [w*WR, w*WR + WR) for its own BNT/2 tokens, and only the first
+// set issues the stage loads.  With 256-row tiles this halves the activation
+// bytes each weight row costs (LDS reads and L2 traffic) against 128-row
+// tiles, for twice the decode per matrix-core op.
+template <int QT, int WR, int BNT, int KG, bool XF, int TG>
+__device__ __forceinline__ void gemm_lds_body(float* __restrict__ dst, const uint8_t* __restrict__ w,
+                                              const uint16_t* __restrict__ x16, const float* __restrict__ x,
+                                              int ldx, int m, int k, int n, int rb, int kp, int n_mb, int n_nb,
+                                              int n_split, int sps, float* __restrict__ partial, int ldd,
+                                              int nb_fast) {
     using G = lds_ring::Geo<QT, WR, BNT, KG, XF>;
     static_assert(G::OK, "no LDS ring of this shape fits");
+    static_assert(TG == 1 || (TG == 2 && KG == 1 && !XF), "token groups: one k group, f16 activations");
     constexpr int BM = G::BM, BN = BNT, CPR = G::CPR, NR = G::NR, DA = G::DA, DB = G::DB;
-    constexpr int RI = WR / 16, NJ = BN / 16;  // 16-row and 16-token blocks per wave
+    constexpr int RI = WR / 16, NJ = BN / 16 / TG;  // 16-row and 16-token blocks per wave
     __shared__ __attribute__((aligned(1024))) uint8_t lds[G::NS * G::STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave_all = wave_id();
     const int grp = KG == 1 ? 0 : wave_all >> 2, wave = wave_all & 3;  // k group, wave in the group
+    const int tg = TG == 1 ? 0 : wave_all >> 2;                        // token group
+    const int jb = tg * NJ;                                            // its first token block
     const int r16 = lane & 15, g = lane >> 4;
 
     const int T = n_mb * n_nb, NI = T * n_split, L = blockIdx.x;
@@ -451,6 +459,7 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
                             16u * (uint32_t)((lane & 7) ^ ((lane >> 3) & 7));
     // round r: group grp's step s0 + KG*r + grp into stage KG*slot + grp
     auto issue = [&](int r, int slot) {
+        if (TG > 1 && tg != 0) return;  // the first token group loads the shared stages
         const int kt = s0 + KG * r + grp;
         uint8_t* sa = lds + (KG * slot + grp) * G::STAGE;
         uint8_t* sb = sa + G::A_STAGE;
@@ -565,7 +574,7 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
             f16x8 b0[8], b1[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const uint8_t* bt = sb + (16 * j + r16) * BROW;
+                const uint8_t* bt = sb + (16 * (jb + j) + r16) * BROW;
                 b0[j] = bfrag(bt, 0);
                 b1[j] = bfrag(bt, 1);
             }
@@ -599,7 +608,7 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
             f16x8 bq0[PF], bq1[PF];
 #pragma unroll
             for (int j = 0; j < PF; ++j) {
-                const uint8_t* bt = sb + (16 * j + r16) * BROW;
+                const uint8_t* bt = sb + (16 * (jb + j) + r16) * BROW;
                 bq0[j] = bfrag(bt, 0);
                 bq1[j] = bfrag(bt, 1);
             }
@@ -607,7 +616,7 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
             for (int j = 0; j < NJ; ++j) {
                 const f16x8 b0 = bq0[j % PF], b1 = bq1[j % PF];
                 if (j + PF < NJ) {
-                    const uint8_t* bt = sb + (16 * (j + PF) + r16) * BROW;
+                    const uint8_t* bt = sb + (16 * (jb + j + PF) + r16) * BROW;
                     bq0[j % PF] = bfrag(bt, 0);
                     bq1[j % PF] = bfrag(bt, 1);
                 }
@@ -660,7 +669,7 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int64_t mrow = m0 + wave * WR + i * 16 + g * 4;
-            const int64_t tok = n0 + j * 16 + r16;
+            const int64_t tok = n0 + (jb + j) * 16 + r16;
             if (tok < n) {
                 float* p = out + tok * ldo + mrow;
                 const f32x4 v = acc[i][j];
@@ -676,6 +685,27 @@ __global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict
     }
 }
 
+template <int QT, int WR, int BNT, int KG, bool XF>
+__global__ __launch_bounds__(256 * KG, 1) void gemm_lds_kernel(float* __restrict__ dst, const uint8_t* __restrict__ w,
+                                                               const uint16_t* __restrict__ x16,
+                                                               const float* __restrict__ x, int ldx, int m, int k,
+                                                               int n, int rb, int kp, int n_mb, int n_nb, int n_split,
+                                                               int sps, float* __restrict__ partial, int ldd,
+                                                               int nb_fast) {
+    gemm_lds_body<QT, WR, BNT, KG, XF, 1>(dst, w, x16, x, ldx, m, k, n, rb, kp, n_mb, n_nb, n_split, sps, partial,
+                                          ldd, nb_fast);
+}
+
+// 8 waves in two token groups (TG = 2 above) on f16 activations, one k group
+template <int QT, int WR, int BNT>
+__global__ __launch_bounds__(512, 1) void gemm_lds_tg_kernel(float* __restrict__ dst, const uint8_t* __restrict__ w,
+                                                             const uint16_t* __restrict__ x16, int m, int k, int n,
+                                                             int rb, int kp, int n_mb, int n_nb, int n_split, int sps,
+                                                             float* __restrict__ partial, int ldd, int nb_fast) {
+    gemm_lds_body<QT, WR, BNT, 1, false, 2>(dst, w, x16, nullptr, 0, m, k, n, rb, kp, n_mb, n_nb, n_split, sps,
+                                            partial, ldd, nb_fast);
+}
+
 template <int QT>
 static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k, int64_t n,
                           int64_t rb, const MfmaPlan& pl, void* ws, int64_t ldx, int64_t ldd, hipStream_t st) {
@@ -689,7 +719,7 @@ static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t 
         if (blocks > 8192) blocks = 8192;
         x16_slot_kernel<QT><<<dim3((unsigned)blocks), 256, 0, st>>>(x16, x, (int)n, (int)k, (int)kp, (int)ldx);
     }
-    const int bm = 64 * pl.wm, bn = pl.x16 == 3 ? 256 : (pl.x16 == 5 || pl.x16 == 6 ? 64 : 128);
+    const int bm = 64 * pl.wm, bn = pl.x16 == 3 || pl.x16 == 7 ? 256 : (pl.x16 == 5 || pl.x16 == 6 ? 64 : 128);
     const int n_mb = (int)((m + bm - 1) / bm), n_nb = (int)((n + bn - 1) / bn);
     const dim3 grid((unsigned)(n_mb * n_nb * pl.n_split));
     // Item order: with the weight tile fastest, every token tile's XCDs read
@@ -707,6 +737,13 @@ static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t 
                 dst, w, x16, x, (int)ldx, (int)m, (int)k, (int)n, (int)rb, (int)kp, n_mb, n_nb, pl.n_split,     \
                 pl.sps, part, (int)ldd, nb_fast);                                                               \
     }
+    if (pl.x16 == 7) {
+        // 256 x 256 tiles, two token groups of 4 waves
+        if constexpr (lds_ring::Geo<QT, 64, 256, 1, false>::OK)
+            gemm_lds_tg_kernel<QT, 64, 256><<<grid, 512, 0, st>>>(dst, w, x16, (int)m, (int)k, (int)n, (int)rb,
+                                                                 (int)kp, n_mb, n_nb, pl.n_split, pl.sps, part,
+                                                                 (int)ldd, nb_fast);
+    } else {
     QMM_LDS_LAUNCH(16, 64, 1, false)
     QMM_LDS_LAUNCH(16, 64, 2, false)
     QMM_LDS_LAUNCH(16, 64, 1, true)
@@ -722,6 +759,7 @@ static void launch_lds_qt(float* dst, const uint8_t* w, const float* x, int64_t 
     QMM_LDS_LAUNCH(32, 256, 2, false)
     QMM_LDS_LAUNCH(32, 128, 1, true)
     QMM_LDS_LAUNCH(32, 128, 2, true)
+    }
 #undef QMM_LDS_LAUNCH
     if (pl.n_split > 1) launch_splitk_sum(dst, part, n * m, splitk_stride(n, m), pl.n_split, m, ldd, st);
 }
@@ -744,6 +782,7 @@ static int per_cu_qt(int wr, int bnt, int kg, bool xf) {
     QMM_LDS_PER_CU(32, 256, 1, false)
     QMM_LDS_PER_CU(32, 128, 2, false)
     QMM_LDS_PER_CU(32, 256, 2, false)
+    QMM_LDS_PER_CU(64, 256, 1, false)
     QMM_LDS_PER_CU(32, 128, 1, true)
     QMM_LDS_PER_CU(32, 128, 2, true)
 #undef QMM_LDS_PER_CU

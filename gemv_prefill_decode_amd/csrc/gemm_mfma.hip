@@ -302,7 +302,7 @@ struct FamCost {
     double step_shared_us;
     int per_cu;
 };
-constexpr int N_FAM = 17;
+constexpr int N_FAM = 18;
 constexpr FamCost FAM_COST[N_FAM] = {
     {0, 2, 1, 1.50, 1.04, 2},  // gemm_mfma_kernel, 128 x 128, f32 activations
     {0, 2, 2, 1.06, 1.60, 1},  // gemm_mfma_kernel with 2 k groups (time per step of the item)
@@ -333,6 +333,10 @@ constexpr FamCost FAM_COST[N_FAM] = {
     // 7% rms)
     {6, 1, 1, 0.329, 0.224, 1},
     {6, 1, 2, 0.233, 0.197, 1},
+    // 256 x 256 tiles, two token groups of 4 waves (priced per step of four
+    // times the 128 x 128 work; one work group per CU; from 8B-class Q4_K
+    // and Q6_K timings, 14336 x 4096 x 2048)
+    {7, 4, 1, 2.08, 2.08, 1},
 };
 // f32 weights on the 64 x 64 f32-activation family, on top of lds64_factor
 constexpr double LDS64_F32_XF_FACTOR = 1.15;
@@ -347,7 +351,8 @@ constexpr double lds64_factor(int qt) {
 // The LDS-ring kernel's step time by format: Q6_K's two-field 6-bit codes
 // take about a quarter longer to decode; with 256-token tiles the decode is
 // a smaller share of the step.
-constexpr double LDS_Q6K_FACTOR_128 = 1.27, LDS_Q6K_FACTOR_128_KG2 = 1.31, LDS_Q6K_FACTOR_256 = 1.04;
+constexpr double LDS_Q6K_FACTOR_128 = 1.27, LDS_Q6K_FACTOR_128_KG2 = 1.31, LDS_Q6K_FACTOR_256 = 1.04,
+                 LDS_Q6K_FACTOR_TG = 1.24;
 // f32 weights on f32 activations: the activation rounding adds to the
 // largest weight stages
 constexpr double LDS_F32_XF_FACTOR = 1.29;
@@ -380,7 +385,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
         const int x16 = FAM_COST[fam].x16, wm = FAM_COST[fam].wm, kg = FAM_COST[fam].kg;
         if (kg == 2 && qt == QT_F32) continue;  // its two register rings of f32 weights exceed 256 VGPRs
         // the LDS ring: whole 64-k steps only, and f32 rows fit it with 128-row tiles only
-        const int bn = x16 == 3 ? 256 : (x16 == 5 || x16 == 6 ? 64 : 128);
+        const int bn = x16 == 3 || x16 == 7 ? 256 : (x16 == 5 || x16 == 6 ? 64 : 128);
         const bool xf = x16 == 4 || x16 == 6;
         if (x16 >= 2 && (k % 64 != 0 || !lds_ring_fits(qt, 64 * wm, bn, kg, xf))) continue;
         // 64 x 64 tiles for products with fewer 64 x 128 tiles than CUs; with
@@ -388,6 +393,9 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
         // the two-k-group forms and the Q6_K and f32 rows, so there only the
         // one-group f16-activation form, for the cheaper decodes (measured
         // faster on LFM2 ffn_gate: Q4_0 19.5 -> 17.5 us, Q4_K 22.5 -> 20.6)
+        // 256 x 256 tiles: measured faster than the 128-row ones for Q6_K only
+        // (8B-class 14336 x 4096 x 2048: 356 against 399 us; Q4_K 291 against 249)
+        if (x16 == 7 && !force && qt != QT_Q6_K) continue;
         if ((x16 == 5 || x16 == 6) && !force && ((m + 63) / 64) * ((n + 127) / 128) >= num_cu &&
             (x16 == 6 || kg != 1 || qt == QT_Q6_K || qt == QT_F32))
             continue;
@@ -396,6 +404,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
         const double fmul = x16 == 5                   ? lds64_factor(qt)
                             : x16 == 6                 ? lds64_factor(qt) * (qt == QT_F32 ? LDS64_F32_XF_FACTOR : 1.0)
                             : x16 == 4 && qt == QT_F32 ? LDS_F32_XF_FACTOR
+                            : x16 == 7                 ? (qt == QT_Q6_K ? LDS_Q6K_FACTOR_TG : 1.0)
                             : x16 < 2 || qt != QT_Q6_K
                                 ? 1.0
                                 : (x16 == 3 ? LDS_Q6K_FACTOR_256 : (kg == 2 ? LDS_Q6K_FACTOR_128_KG2 : LDS_Q6K_FACTOR_128));
@@ -422,7 +431,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
                                           : 0.0;
             const double cost = (LAUNCH_US + rounds * sps * step_t +
                                  (se > 1 ? SPLIT_US + (2.0 * se + 1.0) * out_bytes / BYTES_PER_US : 0.0) +
-                                 (x16 == 2 || x16 == 3 || x16 == 5 ? x16_us : 0.0) + xf_us);
+                                 (x16 == 2 || x16 == 3 || x16 == 5 || x16 == 7 ? x16_us : 0.0) + xf_us);
             if (cost < best_cost) {
                 best_cost = cost;
                 best.x16 = x16;
@@ -433,7 +442,7 @@ MfmaPlan plan_gemm_mfma(int64_t m, int64_t k, int64_t n, int qt, int num_cu, boo
             }
         }
     }
-    best.ws_bytes = (best.x16 == 2 || best.x16 == 3 || best.x16 == 5 ? x16_bytes(n, k) : 0) +
+    best.ws_bytes = (best.x16 == 2 || best.x16 == 3 || best.x16 == 5 || best.x16 == 7 ? x16_bytes(n, k) : 0) +
                     (best.n_split > 1 ? (int64_t)best.n_split * splitk_stride(n, m) * 4 : 0);
     if (best.ws_bytes == 0) best.ws_bytes = 256;  // a plan that uses no workspace still takes one
     return best;

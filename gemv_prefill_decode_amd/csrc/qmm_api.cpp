@@ -138,7 +138,8 @@ void parse_tune() {
 // a workspace (tuning and tests): x16 0 (f32-activation kernel, 128-row
 // tiles, kg k groups), 2 (the LDS ring, (64*wm)-row tiles), 3 (the LDS ring,
 // 128 x 256 tiles), 4 (the LDS ring on f32 activations, (64*wm)-row tiles)
-// 5 (the LDS ring, 64 x 64 tiles) or 6 (the same on f32 activations);
+// 5 (the LDS ring, 64 x 64 tiles), 6 (the same on f32 activations) or 7
+// (the LDS ring, 256 x 256 tiles in two token groups of 4 waves);
 // where the LDS ring cannot run, the unsplit default; unset: the cost model
 // chooses.  Malformed -> bad.
 struct MfmaForceState {
@@ -154,8 +155,9 @@ MfmaForceState parse_force() {
     int a = -1, b = -1, c = -1, d = 1;
     char tail = 0;
     const int got = std::sscanf(v, "%d,%d,%d,%d%c", &a, &b, &c, &d, &tail);
-    if ((got != 3 && got != 4) || a < 0 || a > 6 || a == 1 || (b != 1 && b != 2 && b != 4) || (b == 4 && a != 2) ||
-        (b == 1 && a != 2 && a != 4 && a != 5 && a != 6) || ((a == 5 || a == 6) && b != 1) ||
+    if ((got != 3 && got != 4) || a < 0 || a > 7 || a == 1 || (b != 1 && b != 2 && b != 4) ||
+        (b == 4 && a != 2 && a != 7) || (b == 1 && a != 2 && a != 4 && a != 5 && a != 6) ||
+        ((a == 5 || a == 6) && b != 1) || (a == 7 && (b != 4 || d != 1)) ||
         c < 1 || c > 16 || (d != 1 && d != 2)) {
         g_force.bad = true;
         return g_force;

@@ -162,7 +162,9 @@ int qmm_gemm_path(float* dst, const void* w, const float* x,
  *      f16 workspace), 64 or 128 weight rows x 128 tokens;
  *   5  the LDS ring with 64 x 64 tiles (four times the work groups of
  *      128 x 128 tiles, for products with fewer 64 x 128 tiles than CUs);
- *   6  the same 64 x 64 tiles on the f32 activations (as code 4).
+ *   6  the same 64 x 64 tiles on the f32 activations (as code 4);
+ *   7  the LDS ring with 256 x 256 tiles, eight waves in two token groups
+ *      sharing each stage (half the activation traffic per weight row).
  * (Code 1 is not used.)
  * Every family rounds each decoded weight and each activation to f16 once
  * (RNE) and accumulates in f32, so the tolerance is the one of qmm_gemm.
@@ -170,7 +172,7 @@ int qmm_gemm_path(float* dst, const void* w, const float* x,
  * compute-unit count; the environment variable
  * QMM_MFMA_PLAN="x16,wm,n_split[,kg]" forces it (tuning and tests only:
  * x16 0 with wm 2; 2 with wm 1, 2 or 4; 3 with wm 2; 4 with wm 1 or 2;
- * 5 or 6 with wm 1; kg 1 or 2;
+ * 5 or 6 with wm 1; 7 with wm 4 and kg 1; kg 1 or 2;
  * malformed -> QMM_ERR_RANGE; a family the format or k cannot run falls back
  * to family 0 unsplit).
  *   workspace        DEVICE memory, 256-byte aligned, of at least

@@ -570,11 +570,12 @@ def test_split_k_graph_replays(monkeypatch):
 
 # Every prefill kernel family, forced through QMM_MFMA_PLAN on a ragged shape
 # (m, n not multiples of any tile; k with a partial split): x16 (5, 6: 64-token
-# tiles), tile rows (wm*64), k splits, k groups.
+# tiles; 7: 256 x 256 tiles in two token groups), tile rows (wm*64), k splits,
+# k groups.
 FORCED_PLANS = ["0,2,1,1", "0,2,3,1", "0,2,1,2", "0,2,3,2",
                 "2,2,1", "2,2,3", "2,4,1", "2,4,3", "3,2,1", "3,2,3", "2,2,1,2", "2,2,3,2", "3,2,1,2", "3,2,3,2",
                 "4,2,1", "4,2,3", "4,2,1,2", "4,2,3,2", "2,1,1", "2,1,3", "2,1,1,2", "4,1,1", "4,1,3,2",
-                "5,1,1", "5,1,3", "5,1,1,2", "5,1,3,2", "6,1,1", "6,1,3", "6,1,1,2", "6,1,3,2"]
+                "5,1,1", "5,1,3", "5,1,1,2", "5,1,3,2", "6,1,1", "6,1,3", "6,1,1,2", "6,1,3,2", "7,4,1", "7,4,3"]
 
 
 @pytest.mark.parametrize("plan", FORCED_PLANS)
@@ -586,7 +587,7 @@ def test_forced_prefill_plans(plan, qt, monkeypatch):
     m, k, n = 300, 1536 if qt != "q6_k" else 1792, 270
     if qt == "f32" and (kg == 2 or (x16, wm) == (2, 4)):
         pytest.skip("not a plan the library runs for f32 weights")
-    if x16 == 3 and kg == 2 and qt in ("q6_k", "q8_0", "f32"):
+    if (x16 == 3 and kg == 2 and qt in ("q6_k", "q8_0", "f32")) or (x16 == 7 and qt == "f32"):
         pytest.skip("its LDS ring does not fit 160 KB")
     monkeypatch.setenv("QMM_MFMA_PLAN", plan)
     p = qmm.gemm_plan(m, k, n, qt, "mfma")
