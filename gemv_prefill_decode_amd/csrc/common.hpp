@@ -99,6 +99,27 @@ __device__ __forceinline__ float f16hi(uint32_t p) { return (float)__builtin_bit
 
 __device__ __forceinline__ uint32_t byte_of(uint32_t v, int b) { return (v >> (8 * b)) & 0xFFu; }
 
+// Bytes 1 and 3 of v as the low bytes of two halves (high bytes zero): one
+// v_perm_b32 (selector 0x0c gives a zero byte).  With v & 0x00FF00FF for
+// bytes 0 and 2, four byte-wide codes become the halves of two dwords.
+__device__ __forceinline__ uint32_t odd_bytes(uint32_t v) { return __builtin_amdgcn_perm(0u, v, 0x0c030c01u); }
+
+constexpr float TWO24 = 16777216.0f;
+
+// Four weights D*q - M as two packed f16 pairs (codes 0,1 and 2,3), the
+// codes given as f16 halves holding q itself (the subnormal q * 2^-24,
+// exact): e = codes 0 and 2, o = codes 1 and 3.  D24 = D * 2^24, so the
+// product D24 * (q * 2^-24) is D * q exactly and each weight, one
+// v_fma_mix*_f16 reading its half directly, is rounded once to f16.
+__device__ __forceinline__ void affine4h(uint32_t e, uint32_t o, float D24, float Mneg, uint32_t& p01,
+                                         uint32_t& p23) {
+    const f16x2 a = __builtin_bit_cast(f16x2, e), b = __builtin_bit_cast(f16x2, o);
+    const f16x2 lo = {(_Float16)__builtin_fmaf(D24, (float)a[0], Mneg), (_Float16)__builtin_fmaf(D24, (float)b[0], Mneg)};
+    const f16x2 hi = {(_Float16)__builtin_fmaf(D24, (float)a[1], Mneg), (_Float16)__builtin_fmaf(D24, (float)b[1], Mneg)};
+    p01 = __builtin_bit_cast(uint32_t, lo);
+    p23 = __builtin_bit_cast(uint32_t, hi);
+}
+
 // Byte B of v as f32: v_cvt_f32_ubyte{0..3}, select and convert in one
 // instruction.  There is no builtin for it, and the plain expression
 // (float)((v >> 8B) & 0xFF) on a nibble-masked v compiles to v_bfe_u32 plus

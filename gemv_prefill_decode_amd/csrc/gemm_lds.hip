@@ -231,32 +231,15 @@ template <> struct Dec<QT_Q8_0> {
     }
 };
 
-// 8 weights D*q - M.  The codes come as f16 halves holding q itself, i.e.
-// the subnormal q * 2^-24 (exact): e0 = codes 0 and 2, o0 = codes 1 and 3,
-// e1, o1 the same for codes 4..7 (a mask cuts two codes out of four packed
-// bytes at once).  D24 = D * 2^24, so D24 * (q * 2^-24) = D * q exactly and
-// the multiply-add, one v_fma_mix*_f16 per weight reading its f16 half
-// directly, rounds once to f16.
+// 8 weights D*q - M from codes held as f16 halves (affine4h): e0, o0 the
+// halves of codes 0..3, e1, o1 of codes 4..7; D24 = D * 2^24.
 __device__ __forceinline__ f16x8 affine8h(uint32_t e0, uint32_t o0, uint32_t e1, uint32_t o1, float D24,
                                           float Mneg) {
-    const f16x2 a = __builtin_bit_cast(f16x2, e0), b = __builtin_bit_cast(f16x2, o0);
-    const f16x2 c = __builtin_bit_cast(f16x2, e1), d = __builtin_bit_cast(f16x2, o1);
-    f16x8 r;
-    r[0] = (_Float16)__builtin_fmaf(D24, (float)a[0], Mneg);
-    r[1] = (_Float16)__builtin_fmaf(D24, (float)b[0], Mneg);
-    r[2] = (_Float16)__builtin_fmaf(D24, (float)a[1], Mneg);
-    r[3] = (_Float16)__builtin_fmaf(D24, (float)b[1], Mneg);
-    r[4] = (_Float16)__builtin_fmaf(D24, (float)c[0], Mneg);
-    r[5] = (_Float16)__builtin_fmaf(D24, (float)d[0], Mneg);
-    r[6] = (_Float16)__builtin_fmaf(D24, (float)c[1], Mneg);
-    r[7] = (_Float16)__builtin_fmaf(D24, (float)d[1], Mneg);
-    return r;
+    uint32_t p[4];
+    affine4h(e0, o0, D24, Mneg, p[0], p[1]);
+    affine4h(e1, o1, D24, Mneg, p[2], p[3]);
+    return frag4(p[0], p[1], p[2], p[3]);
 }
-constexpr float TWO24 = 16777216.0f;
-
-// Bytes 1 and 3 of v as the low bytes of two halves (high bytes zero): one
-// v_perm_b32 (selector 0x0c gives a zero byte)
-__device__ __forceinline__ uint32_t odd_bytes(uint32_t v) { return __builtin_amdgcn_perm(0u, v, 0x0c030c01u); }
 
 template <> struct Dec<QT_Q4_K> {
     __device__ __forceinline__ static void run(const uint8_t* row, uint32_t, int kt, int g, int,

@@ -137,22 +137,17 @@ template <> struct ALoad<QT_Q4_K> {
         const uint32_t m0 = blend(b4 & 63u, (b4 >> 4) | ((b0 >> 6) << 4));
         const uint32_t s1 = blend(b1 & 63u, (b5 & 15u) | ((bm1 >> 6) << 4));
         const uint32_t m1 = blend(b5 & 63u, (b5 >> 4) | ((b1 >> 6) << 4));
-        const float D0 = d * (float)s0, M0 = dmin * (float)m0;
-        const float D1 = d * (float)s1, M1 = dmin * (float)m1;
+        const float d24 = d * TWO24;
+        const float D0 = d24 * (float)s0, M0 = dmin * (float)m0;
+        const float D1 = d24 * (float)s1, M1 = dmin * (float)m1;
+        // the nibbles as f16 halves: low nibbles of bytes 0, 2 and 1, 3, then
+        // the high ones
+        constexpr uint32_t N2 = 0x000F000Fu;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const uint32_t q = u == 0 ? qs.x : (u == 1 ? qs.y : (u == 2 ? qs.z : qs.w));
-            float lo[4], hi[4];
-            const uint32_t ql = q & 0x0F0F0F0Fu, qh = (q >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                lo[b] = __builtin_fmaf(D0, ubyte_f32(ql, b), -M0);
-                hi[b] = __builtin_fmaf(D1, ubyte_f32(qh, b), -M1);
-            }
-            o[4 * u + 0] = pack_f2h(lo[0], lo[1]);
-            o[4 * u + 1] = pack_f2h(lo[2], lo[3]);
-            o[4 * u + 2] = pack_f2h(hi[0], hi[1]);
-            o[4 * u + 3] = pack_f2h(hi[2], hi[3]);
+            affine4h(q & N2, (q >> 8) & N2, D0, -M0, o[4 * u + 0], o[4 * u + 1]);
+            affine4h((q >> 4) & N2, (q >> 12) & N2, D1, -M1, o[4 * u + 2], o[4 * u + 3]);
         }
     }
 };
@@ -191,16 +186,9 @@ template <> struct ALoad<QT_Q6_K> {
             const uint32_t H = shr64(rh[u], rh[u + 1], sh);
             const uint32_t ql = (L & 0x0F0F0F0Fu) | (((H >> hs) & 0x03030303u) << 4);
             const uint32_t qhv = ((L >> 4) & 0x0F0F0F0Fu) | (((H >> (hs + 4)) & 0x03030303u) << 4);
-            float lo[4], hi[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                lo[b] = __builtin_fmaf(Dl, ubyte_f32(ql, b), Dl32);
-                hi[b] = __builtin_fmaf(Dh, ubyte_f32(qhv, b), Dh32);
-            }
-            o[4 * u + 0] = pack_f2h(lo[0], lo[1]);
-            o[4 * u + 1] = pack_f2h(lo[2], lo[3]);
-            o[4 * u + 2] = pack_f2h(hi[0], hi[1]);
-            o[4 * u + 3] = pack_f2h(hi[2], hi[3]);
+            // one 6-bit code per byte: even bytes by a mask, odd ones by a permute
+            affine4h(ql & 0x00FF00FFu, odd_bytes(ql), Dl * TWO24, Dl32, o[4 * u + 0], o[4 * u + 1]);
+            affine4h(qhv & 0x00FF00FFu, odd_bytes(qhv), Dh * TWO24, Dh32, o[4 * u + 2], o[4 * u + 3]);
         }
     }
 };
