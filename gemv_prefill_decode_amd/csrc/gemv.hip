@@ -201,18 +201,18 @@ static void launch_gemv_nt(float* dst, const uint8_t* w, const float* x, int64_t
     });
 }
 
-// The matrix-core stream with token groups of 4 * TT rows; false if they do
-// not fit one work group's LDS.  With at least four row groups per CU, one
-// wave per row group (KW = 1), 8-wave work groups where the
-// LDS holds at most two per CU, else 4-wave ones.  With fewer row groups and
-// rows of at least 4 unit iterations, KW = 4 or 8 waves share a row group
-// (one row group per work group at KW = 8), which costs a barrier per row
-// group but fills the CUs: 1024x4608 Q4_0, n = 4: 17.7 -> 7.8 us; on
+// The matrix-core stream with token groups of 4 * TT rows and R rows per
+// lane; false if they do not fit one work group's LDS.  With at least four
+// row groups per CU, one wave per row group (KW = 1), 8-wave work groups
+// where the LDS holds at most two per CU, else 4-wave ones.  With fewer row
+// groups and rows of at least 4 unit iterations, KW = 4 or 8 waves share a
+// row group (one row group per work group at KW = 8), which costs a barrier
+// per row group but fills the CUs: 1024x4608 Q4_0, n = 4: 17.7 -> 7.8 us; on
 // 14336x4096 and 4608x1024 the barriers made it slower than KW = 1.
-template <int QT, int TT>
-static bool launch_gemv_mfma(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k, int64_t n,
+template <int QT, int TT, int R>
+static bool launch_gemv_mfma_r(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k, int64_t n,
                              int64_t rb, int64_t ldx, int64_t ldd, const GemvTuning& tune, hipStream_t st) {
-    constexpr int R = 2, D = 2;
+    constexpr int D = 2;
     const int lm = MTraits<QT>::LM;
     const int64_t lds = ((int64_t)qlds_floats(4 * TT, (int)k, lm, MTraits<QT>::RUN) + 2 * 8 * 16 * R * TT) * 4;  // partial sums sized for 8 waves
     if (lds > tune.lds_per_wg) return false;
@@ -237,6 +237,22 @@ static bool launch_gemv_mfma(float* dst, const uint8_t* w, const float* x, int64
     else if (lt.wg_per_cu <= 2) go(I1{}, I8{});
     else go(I1{}, I4{});
     return true;
+}
+
+// Rows per lane R: one (row groups of 4 rows, twice as many waves with work)
+// for Q6_K, whose scaled sub-units keep more registers per row, and for the
+// other quantized formats where two-row groups would leave fewer than four
+// row groups per CU; else two.  Measured (graph replays): 14336x4096 Q6_K
+// n = 8 / 32: 30.6 -> 29.1 / 90.1 -> 76.5 us; 4608x1024 Q4_K n = 16:
+// 10.4 -> 9.0 us; 1024x4608 Q4_0 n = 4: 7.8 -> 6.3 us; but 14336x4096 Q4_K
+// n = 16 46.8 against 55.4 us and f32 3072x1024 n = 32 12.6 against 18.6
+// with one row.
+template <int QT, int TT>
+static bool launch_gemv_mfma(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k, int64_t n,
+                             int64_t rb, int64_t ldx, int64_t ldd, const GemvTuning& tune, hipStream_t st) {
+    const bool one = QT == QT_Q6_K || (QT != QT_F32 && (m + 7) / 8 < 4 * (int64_t)tune.num_cu);
+    if (one) return launch_gemv_mfma_r<QT, TT, 1>(dst, w, x, m, k, n, rb, ldx, ldd, tune, st);
+    return launch_gemv_mfma_r<QT, TT, 2>(dst, w, x, m, k, n, rb, ldx, ldd, tune, st);
 }
 
 // Token groups of the matrix-core stream: 8 rows where they fit (half the
