@@ -201,58 +201,84 @@ static void launch_gemv_nt(float* dst, const uint8_t* w, const float* x, int64_t
     });
 }
 
-// The matrix-core stream with token groups of 4 * TT rows and R rows per
-// lane; false if they do not fit one work group's LDS.  With at least four
-// row groups per CU, one wave per row group (KW = 1), 8-wave work groups
-// where the LDS holds at most two per CU, else 4-wave ones.  With fewer row
-// groups and rows of at least 4 unit iterations, KW = 4 or 8 waves share a
-// row group (one row group per work group at KW = 8), which costs a barrier
-// per row group but fills the CUs: 1024x4608 Q4_0, n = 4: 17.7 -> 7.8 us; on
-// 14336x4096 and 4608x1024 the barriers made it slower than KW = 1.
+// Launch shape of the matrix-core stream with token groups of 4 * TT rows
+// and R rows per lane.  With at least four row groups per CU, one wave per
+// row group (KW = 1), 8-wave work groups where the LDS holds at most two per
+// CU, else 4-wave ones.  With fewer row groups and rows of at least 4 unit
+// iterations, KW = 4 or 8 waves share a row group (one row group per work
+// group at KW = 8), which costs a barrier per row group but fills the CUs:
+// 1024x4608 Q4_0, n = 4: 17.7 -> 7.8 us; on 14336x4096 and 4608x1024 the
+// barriers made it slower than KW = 1.  iters: row-group passes of the
+// busiest work group.
+struct MStreamLaunch {
+    int64_t lds, n_rg, gy, iters;
+    int kw, wpg, mld;
+    unsigned grid;
+};
+
 template <int QT, int TT, int R>
-static bool launch_gemv_mfma_r(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k, int64_t n,
-                             int64_t rb, int64_t ldx, int64_t ldd, const GemvTuning& tune, hipStream_t st) {
-    constexpr int D = 2;
+static MStreamLaunch mstream_launch(int64_t m, int64_t k, int64_t n, const GemvTuning& tune) {
+    MStreamLaunch p{};
     const int lm = MTraits<QT>::LM;
-    const int64_t lds = ((int64_t)qlds_floats(4 * TT, (int)k, lm, MTraits<QT>::RUN) + 2 * 8 * 16 * R * TT) * 4;  // partial sums sized for 8 waves
-    if (lds > tune.lds_per_wg) return false;
-    const int mld = qld((int)k, lm);
-    const int64_t n_rg = (m + 4 * R - 1) / (4 * R);
-    const int64_t gy = (n + 4 * TT - 1) / (4 * TT);
-    const GemvTuning lt = lds_limited(tune, lds);
+    p.lds = ((int64_t)qlds_floats(4 * TT, (int)k, lm, MTraits<QT>::RUN) + 2 * 8 * 16 * R * TT) * 4;  // partial sums sized for 8 waves
+    p.mld = qld((int)k, lm);
+    p.n_rg = (m + 4 * R - 1) / (4 * R);
+    p.gy = (n + 4 * TT - 1) / (4 * TT);
+    const GemvTuning lt = lds_limited(tune, p.lds);
     const int64_t units = (k + GUnit<QT>::UE - 1) / GUnit<QT>::UE;
     const int64_t upl = (units + 15) / 16;
-    const int kw = n_rg >= 4 * (int64_t)lt.num_cu || upl < 4 ? 1 : (upl < 8 ? 4 : 8);
+    p.kw = p.n_rg >= 4 * (int64_t)lt.num_cu || upl < 4 ? 1 : (upl < 8 ? 4 : 8);
+    p.wpg = p.kw > 1 || lt.wg_per_cu <= 2 ? 8 : 4;
+    const int64_t slots = p.wpg / p.kw;
+    p.grid = stream_grid(p.n_rg, p.gy, lt, (int)slots);
+    p.iters = (p.n_rg + (int64_t)p.grid * slots - 1) / ((int64_t)p.grid * slots);
+    return p;
+}
+
+// false if the launch does not fit one work group's LDS
+template <int QT, int TT, int R>
+static bool launch_gemv_mfma_r(const MStreamLaunch& p, float* dst, const uint8_t* w, const float* x, int64_t m,
+                               int64_t k, int64_t n, int64_t rb, int64_t ldx, int64_t ldd, const GemvTuning& tune,
+                               hipStream_t st) {
+    constexpr int D = 2;
+    if (p.lds > tune.lds_per_wg) return false;
     auto go = [&](auto KWc, auto WPGc) {
         constexpr int KW = decltype(KWc)::value, WPG = decltype(WPGc)::value;
-        const dim3 grid(stream_grid(n_rg, gy, lt, WPG / KW), (unsigned)gy);
-        gemv_mfma_kernel<QT, TT, R, D, KW, WPG><<<grid, 64 * WPG, (size_t)lds, st>>>(
-            dst, w, x, (int)m, (int)k, (int)n, (int)rb, (int)n_rg, (int)ldx, (int)ldd, mld);
+        gemv_mfma_kernel<QT, TT, R, D, KW, WPG><<<dim3(p.grid, (unsigned)p.gy), 64 * WPG, (size_t)p.lds, st>>>(
+            dst, w, x, (int)m, (int)k, (int)n, (int)rb, (int)p.n_rg, (int)ldx, (int)ldd, p.mld);
     };
     using I1 = std::integral_constant<int, 1>;
     using I4 = std::integral_constant<int, 4>;
     using I8 = std::integral_constant<int, 8>;
-    if (kw == 4) go(I4{}, I8{});
-    else if (kw == 8) go(I8{}, I8{});
-    else if (lt.wg_per_cu <= 2) go(I1{}, I8{});
+    if (p.kw == 4) go(I4{}, I8{});
+    else if (p.kw == 8) go(I8{}, I8{});
+    else if (p.wpg == 8) go(I1{}, I8{});
     else go(I1{}, I4{});
     return true;
 }
 
-// Rows per lane R: one (row groups of 4 rows, twice as many waves with work)
-// for Q6_K, whose scaled sub-units keep more registers per row, and for the
-// other quantized formats where two-row groups would leave fewer than four
-// row groups per CU; else two.  Measured (graph replays): 14336x4096 Q6_K
-// n = 8 / 32: 30.6 -> 29.1 / 90.1 -> 76.5 us; 4608x1024 Q4_K n = 16:
-// 10.4 -> 9.0 us; 1024x4608 Q4_0 n = 4: 7.8 -> 6.3 us; but 14336x4096 Q4_K
-// n = 16 46.8 against 55.4 us and f32 3072x1024 n = 32 12.6 against 18.6
-// with one row.
+// Rows per lane R, from the rows the busiest wave streams (iters * R): one
+// row (row groups of 4 rows, twice the work groups) where that is fewer than
+// three quarters of the two-row figure, for Q6_K where it is no more (its
+// scaled sub-units keep more registers per row); f32 rows and the quantized
+// formats with four or more row groups of 8 rows per CU keep two.  Measured
+// (graph replays, one row against two): 14336x4096 Q6_K n = 8 / 32: 28.4 /
+// 75.7 against 30.3 / 89.1 us; 4608x1024 Q4_K n = 16: 9.0 against 10.4;
+// 1024x4608 Q4_0 n = 4: 6.4 against 7.8, but n = 8 / 32 (the same number of
+// passes): 8.1 / 18.7 against 7.8 / 16.5; 4608x1024 Q4_K n = 24 (two passes
+// against one): 13.4 against 10.5; 14336x4096 Q4_K n = 16 55.4 against 46.8;
+// f32 3072x1024 n = 32 18.6 against 12.6.
 template <int QT, int TT>
 static bool launch_gemv_mfma(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k, int64_t n,
                              int64_t rb, int64_t ldx, int64_t ldd, const GemvTuning& tune, hipStream_t st) {
-    const bool one = QT == QT_Q6_K || (QT != QT_F32 && (m + 7) / 8 < 4 * (int64_t)tune.num_cu);
-    if (one) return launch_gemv_mfma_r<QT, TT, 1>(dst, w, x, m, k, n, rb, ldx, ldd, tune, st);
-    return launch_gemv_mfma_r<QT, TT, 2>(dst, w, x, m, k, n, rb, ldx, ldd, tune, st);
+    const MStreamLaunch p1 = mstream_launch<QT, TT, 1>(m, k, n, tune);
+    const MStreamLaunch p2 = mstream_launch<QT, TT, 2>(m, k, n, tune);
+    const int64_t c1 = p1.iters, c2 = 2 * p2.iters;
+    bool one = false;
+    if (QT == QT_Q6_K) one = c1 <= c2;
+    else if (QT != QT_F32) one = (m + 7) / 8 < 4 * (int64_t)tune.num_cu && 4 * c1 < 3 * c2;
+    if (one) return launch_gemv_mfma_r<QT, TT, 1>(p1, dst, w, x, m, k, n, rb, ldx, ldd, tune, st);
+    return launch_gemv_mfma_r<QT, TT, 2>(p2, dst, w, x, m, k, n, rb, ldx, ldd, tune, st);
 }
 
 // Token groups of the matrix-core stream: 8 rows where they fit (half the
