@@ -257,28 +257,32 @@ static bool launch_gemv_mfma_r(const MStreamLaunch& p, float* dst, const uint8_t
     return true;
 }
 
-// Rows per lane R, from the rows the busiest wave streams (iters * R): one
-// row (row groups of 4 rows, twice the work groups) where that is fewer than
-// three quarters of the two-row figure, for Q6_K where it is no more (its
-// scaled sub-units keep more registers per row); f32 rows and the quantized
-// formats with four or more row groups of 8 rows per CU keep two.  Measured
-// (graph replays, one row against two): 14336x4096 Q6_K n = 8 / 32: 28.4 /
-// 75.7 against 30.3 / 89.1 us; 4608x1024 Q4_K n = 16: 9.0 against 10.4;
-// 1024x4608 Q4_0 n = 4: 6.4 against 7.8, but n = 8 / 32 (the same number of
-// passes): 8.1 / 18.7 against 7.8 / 16.5; 4608x1024 Q4_K n = 24 (two passes
-// against one): 13.4 against 10.5; 14336x4096 Q4_K n = 16 55.4 against 46.8;
-// f32 3072x1024 n = 32 18.6 against 12.6.
+// Rows per lane R: one for Q6_K (row groups of 4 rows: twice the work
+// groups, and its scaled sub-units keep more registers per row), two for f32
+// rows.  For the other formats one row only where it shortens the rows the
+// busiest wave streams (its row-group passes times R) to under three
+// quarters of the two-row figure, and never with four or more row groups of
+// 8 rows per CU.  Measured (graph replays, one row against two): 14336x4096
+// Q6_K n = 8 / 32: 28.4 / 75.7 against 30.3 / 89.1 us; 4608x1024 Q4_K
+// n = 16: 9.0 against 10.4; 1024x4608 Q4_0 n = 4: 6.4 against 7.8, but
+// n = 8 / 32, with as many passes: 8.1 / 18.7 against 7.8 / 16.5; 4608x1024
+// Q4_K n = 24, two passes against one: 13.4 against 10.5; 14336x4096 Q4_K
+// n = 16: 55.4 against 46.8; f32 3072x1024 n = 32: 18.6 against 12.6.
 template <int QT, int TT>
 static bool launch_gemv_mfma(float* dst, const uint8_t* w, const float* x, int64_t m, int64_t k, int64_t n,
                              int64_t rb, int64_t ldx, int64_t ldd, const GemvTuning& tune, hipStream_t st) {
-    const MStreamLaunch p1 = mstream_launch<QT, TT, 1>(m, k, n, tune);
-    const MStreamLaunch p2 = mstream_launch<QT, TT, 2>(m, k, n, tune);
-    const int64_t c1 = p1.iters, c2 = 2 * p2.iters;
-    bool one = false;
-    if (QT == QT_Q6_K) one = c1 <= c2;
-    else if (QT != QT_F32) one = (m + 7) / 8 < 4 * (int64_t)tune.num_cu && 4 * c1 < 3 * c2;
-    if (one) return launch_gemv_mfma_r<QT, TT, 1>(p1, dst, w, x, m, k, n, rb, ldx, ldd, tune, st);
-    return launch_gemv_mfma_r<QT, TT, 2>(p2, dst, w, x, m, k, n, rb, ldx, ldd, tune, st);
+    if constexpr (QT == QT_Q6_K) {
+        const MStreamLaunch p1 = mstream_launch<QT, TT, 1>(m, k, n, tune);
+        return launch_gemv_mfma_r<QT, TT, 1>(p1, dst, w, x, m, k, n, rb, ldx, ldd, tune, st);
+    } else {
+        const MStreamLaunch p2 = mstream_launch<QT, TT, 2>(m, k, n, tune);
+        if constexpr (QT != QT_F32) {
+            const MStreamLaunch p1 = mstream_launch<QT, TT, 1>(m, k, n, tune);
+            if ((m + 7) / 8 < 4 * (int64_t)tune.num_cu && 4 * p1.iters < 3 * 2 * p2.iters)
+                return launch_gemv_mfma_r<QT, TT, 1>(p1, dst, w, x, m, k, n, rb, ldx, ldd, tune, st);
+        }
+        return launch_gemv_mfma_r<QT, TT, 2>(p2, dst, w, x, m, k, n, rb, ldx, ldd, tune, st);
+    }
 }
 
 // Token groups of the matrix-core stream: 8 rows where they fit (half the
