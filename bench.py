@@ -213,25 +213,45 @@ def run_prefill(args, n):
         for qt in QTS:
             graphs[qt].replay()
     torch.cuda.synchronize()
-    ev = [{qt: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for qt in QTS} for _ in range(args.steps)]
-    # timed region: K steps, each the five per-format graphs on the current stream
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        for qt in QTS:
-            ev[s][qt][0].record()
-            graphs[qt].replay()
-            ev[s][qt][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    # per-format times (before the timed region): each format's graph between
+    # two events, as many rounds as timed steps
     per_qt = {}
     for qt in QTS:
-        sec = [ev[s][qt][0].elapsed_time(ev[s][qt][1]) * 1e-3 for s in range(args.steps)]
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for s in range(args.steps):
+            ev[s][0].record()
+            graphs[qt].replay()
+            ev[s][1].record()
+        torch.cuda.synchronize()
+        sec = [a.elapsed_time(b) * 1e-3 for (a, b) in ev]
         mean = sum(sec) / len(sec)
         per_qt[qt] = {"us_per_step": round(mean * 1e6, 2),
                       "TFLOP/s": round(flops[qt] / mean / 1e12, 1),
                       "frac_mfma_peak": round(flops[qt] / mean / 1e12 / PEAK_F16_TFLOPS, 4)}
+    # the dominant format (the largest time per step); its four calls, each a
+    # GEMM kernel (plus the f16 pre-pass and the k-split sum where planned)
+    dom = max(QTS, key=lambda q: per_qt[q]["us_per_step"])
+    # A timed step: the other formats' 16 calls as one graph, then the
+    # dominant format's graph between two events (its time per call for the
+    # roofline).  Every event recorded between graphs costs the stream a few
+    # microseconds, so the step records only these two.
+    rest = capture([call(b) for b in bufs if b[0] != dom])
+    for _ in range(args.warmup):
+        rest.replay()
+        graphs[dom].replay()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        rest.replay()
+        ev[s][0].record()
+        graphs[dom].replay()
+        ev[s][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dom_sec = sum(a.elapsed_time(b) * 1e-3 for (a, b) in ev) / args.steps
+    del rest
     # per-shape times (outside the timed region): each launch graph-replayed alone
     kern = {}
     for (qt, label, m, k, w) in bufs:
@@ -243,12 +263,9 @@ def run_prefill(args, n):
             "us": round(t * 1e6, 2), "TFLOP/s": round(2.0 * m * k * n / t / 1e12, 1),
             "kernel": kern[(qt, label)][0], "grid": kern[(qt, label)][1], "k_split": plan["n_split"]}
         del g
-    # the dominant format (the largest time per step); its four calls, each a
-    # GEMM kernel (plus the f16 pre-pass and the k-split sum where planned)
-    dom = max(QTS, key=lambda q: per_qt[q]["us_per_step"])
     calls = [b for b in bufs if b[0] == dom]
     launches = len(calls)
-    avg_launch = per_qt[dom]["us_per_step"] * 1e-6 / launches
+    avg_launch = dom_sec / launches
     fpl = flops[dom] / launches
     ach = fpl / avg_launch / 1e12
     names = [kern[(dom, label)] for (_, label, _, _, _) in calls]
