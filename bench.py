@@ -851,11 +851,10 @@ def stream_counter_summary(tags_path, csv_path, out_path):
         f.write("# Streaming-kernel counters: the GEMV (n=1 with its load-only twin; n=4, 16 on both streams) "
                 "and the NVFP4 MoE gate/up with its twins\n\n"
                 "Commands (on one MI355X, from the repository root):\n\n"
-                "```\ncd /tmp && export TMPDIR=/tmp && cd \"$GRAFT_REPO_ROOT\"\n"
-                "rocprofv3 --pmc " + STREAM_COUNTER_SET + " --output-format csv -d gpurun_out/sw -o run -- "
-                "python3 bench.py --stream-counter-workload > gpurun_out/sw_tags.txt\n"
-                "python3 bench.py --stream-summary gpurun_out/sw_tags.txt gpurun_out/sw/run_counter_collection.csv "
-                "profiles/stream_counters.md\n```\n\n"
+                "```\ncd /tmp && export TMPDIR=/tmp && cd -\n"
+                f"rocprofv3 --pmc {STREAM_COUNTER_SET} --output-format csv -d {os.path.dirname(csv_path)} -o run -- "
+                f"python3 bench.py --stream-counter-workload > {tags_path}\n"
+                f"python3 bench.py --stream-summary {tags_path} {csv_path} {out_path}\n```\n\n"
                 "Wave instructions per weight of the matrix (x 64 lanes / weights; the MoE's weights are those of "
                 "its distinct experts, the n = 16 GEMV streams its weights twice, once per token group of 8); VALU counts the matrix-core instructions, MFMA lists them apart; VALU "
                 "issue per SIMD = SQ_INSTS_VALU x 4 cycles / 1024 SIMDs at 2.4 GHz (the VALU time if nothing "
@@ -911,13 +910,11 @@ def mfma_counter_summary(tags_path, csv_paths, out_path):
     with open(out_path, "w") as f:
         f.write("# Matrix-core counters of the prefill GEMM kernels (current sources)\n\n"
                 "Commands (on one MI355X, from the repository root; two counter passes, then the table):\n\n"
-                "```\ncd /tmp && export TMPDIR=/tmp && cd \"$GRAFT_REPO_ROOT\"\n"
-                "rocprofv3 --pmc " + COUNTER_SETS[0] + " --output-format csv -d gpurun_out/cw0 -o run -- "
-                "python3 bench.py --counter-workload > gpurun_out/cw_tags.txt\n"
-                "rocprofv3 --pmc " + COUNTER_SETS[1] + " --output-format csv -d gpurun_out/cw1 -o run -- "
-                "python3 bench.py --counter-workload > gpurun_out/cw_tags1.txt\n"
-                "python3 bench.py --mfma-summary gpurun_out/cw_tags.txt profiles/mfma_counters_prefill.md "
-                "gpurun_out/cw0/run_counter_collection.csv gpurun_out/cw1/run_counter_collection.csv\n```\n\n"
+                "```\ncd /tmp && export TMPDIR=/tmp && cd -\n" +
+                "".join(f"rocprofv3 --pmc {cs} --output-format csv -d {os.path.dirname(cp)} -o run -- "
+                        f"python3 bench.py --counter-workload > {tags_path if i == 0 else os.devnull}\n"
+                        for i, (cs, cp) in enumerate(zip(COUNTER_SETS, csv_paths))) +
+                f"python3 bench.py --mfma-summary {tags_path} {out_path} {' '.join(csv_paths)}\n```\n\n"
                 "Per GEMM call of each headline configuration (the planned kernel at its grid, mean of 3 "
                 "dispatches): MFMA flops from SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 against 2mkn; matrix cores busy = "
                 "SQ_VALU_MFMA_BUSY_CYCLES / (SQ_BUSY_CYCLES x 32); VALU / MFMA counts the matrix-core "
