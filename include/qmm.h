@@ -19,7 +19,8 @@
  *    cached device properties (compute units, LDS sizes) and the parsed
  *    tuning variables (QMM_GEMV_MAX_N below; QMM_GEMV_WG_PER_CU and
  *    QMM_MOE_WG_PER_CU 1..64, QMM_GEMV_ROWS 1..2, QMM_GEMV_DEPTH 2/4/8,
- *    QMM_MOE_LPR_LOG2 3..6 (log2 of the MoE streams' lanes per row) for the
+ *    QMM_MOE_LPR_LOG2 3..6 (log2 of the MoE streams' largest lane group per
+ *    row; rows of few units take smaller groups, down to 8 lanes) for the
  *    streaming kernels' launch shape; QMM_GEMV_MFMA_MIN 0..64 (default 3:
  *    the smallest n that QMM_PATH_GEMV runs on its matrix-core stream, 0 =
  *    never), QMM_GEMV_MFMA_TT 1..2 (that stream's activation rows per pass
